@@ -1,0 +1,102 @@
+"""Seeded synthetic inputs for the GDN streaming core.
+
+This module only draws random numbers and rounds them to the storage dtype; it
+holds none of the method's arithmetic (no normalisation, no scan), so both the
+GPU tests and the CPU oracle can take their inputs from it.
+
+Workload shapes follow the SANA-Streaming pages: 1280x704 frames through the
+DCAE-V F32T4C32 autoencoder give 22 x 40 = 880 latent tokens per latent frame
+(SANA-Video blog, section 3.2, and the Chinese summary's "Motivation"), a
+streaming chunk is 3 latent frames (Chinese summary, "Method steps" step 2),
+the head dimension is 112 (SANA-Video blog, section 3.1 table), and the hybrid
+DiT has 15 GDN blocks (Chinese summary, "Core method").
+
+Distributions (per token and head):
+  q, k, v ~ N(0, 1), rounded to bf16 (round-to-nearest-even) unless io="f32";
+  a = exp(-0.1 * softplus(z_a)), beta = sigmoid(z_b), z ~ N(0, 1), kept in fp32;
+  S0 ~ N(0, 0.1^2) in fp32 where a carried state is needed.
+q and k are drawn raw: the per-token L2 normalisation is part of the path.
+Seeds: numpy SeedSequence([cfg, stream, layer, chunk, step]) -> PCG64; draw order
+q, k, v, z_a, z_b, then S0.  The tiny fp32 case uses default_rng(0).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+TOKENS_PER_FRAME = 22 * 40          # 1280x704 at 32x spatial compression
+FRAMES_PER_CHUNK = 3
+CHUNK_TOKENS = TOKENS_PER_FRAME * FRAMES_PER_CHUNK   # 2640
+HEAD_DIM = 112
+HEADS = 20
+GDN_LAYERS = 15
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bf16 value (ties to even); returns float32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) & 0xFFFF0000).astype(np.uint32)
+    out = r.view(np.float32).copy()
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = np.nan
+    return out
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Upper 16 bits of bf16-exact float32 values (the bf16 storage pattern)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _softplus(z):
+    return np.logaddexp(0.0, z)
+
+
+def _sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def draw(rng: np.random.Generator, T: int, H: int, Dk: int, Dv: int, *, io: str = "bf16",
+         with_state: bool = False, gates: str = "default"):
+    """Draw one stream's chunk: q, k [T, H, Dk], v [T, H, Dv], a, beta [T, H] (+ S0 [H, Dv, Dk])."""
+    q = rng.standard_normal((T, H, Dk)).astype(np.float32)
+    k = rng.standard_normal((T, H, Dk)).astype(np.float32)
+    v = rng.standard_normal((T, H, Dv)).astype(np.float32)
+    za = rng.standard_normal((T, H))
+    zb = rng.standard_normal((T, H))
+    if io == "bf16":
+        q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
+    elif io != "f32":
+        raise ValueError(f"unknown io dtype {io!r}")
+    if gates == "default":
+        a = np.exp(-0.1 * _softplus(za)).astype(np.float32)
+    elif gates == "stress":           # slow forgetting: the carried state matters for a whole chunk
+        a = np.full((T, H), 1.0 - 1e-3, dtype=np.float32)
+    else:
+        raise ValueError(f"unknown gate recipe {gates!r}")
+    beta = _sigmoid(zb).astype(np.float32)
+    out = dict(q=q, k=k, v=v, a=a, beta=beta)
+    if with_state:
+        out["S0"] = (0.1 * rng.standard_normal((H, Dv, Dk))).astype(np.float32)
+    return out
+
+
+def rng_for(cfg: int, stream: int = 0, layer: int = 0, chunk: int = 0, step: int = 0):
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg, stream, layer, chunk, step])))
+
+
+def batch(cfg: int, B: int, T: int, H: int, D: int, *, layer: int = 0, chunk: int = 0, step: int = 0,
+          io: str = "bf16", with_state: bool = False, gates: str = "default", stream0: int = 0):
+    """Stack B independent streams along a leading batch axis: q [B, T, H, D], ..., S0 [B, H, D, D]."""
+    parts = [draw(rng_for(cfg, stream0 + b, layer, chunk, step), T, H, D, D, io=io,
+                  with_state=with_state, gates=gates) for b in range(B)]
+    return {key: np.stack([p[key] for p in parts]) for key in parts[0]}
+
+
+def tiny_fp32():
+    """16-dim single-head 64-token fp32 case (zero initial state), seed 0."""
+    rng = np.random.default_rng(0)
+    d = draw(rng, 64, 1, 16, 16, io="f32")
+    return {key: val[None] for key, val in d.items()}
