@@ -1,0 +1,222 @@
+"""ctypes binding of ``libgdn_stream.so`` (C ABI in include/gdn_stream.h).
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream; every step of the computation runs in the library's kernels.  The
+functions carry the C names; ``Stream`` is a small convenience wrapper.
+There is no fallback: if the library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(PKG, "libgdn_stream.so")
+
+GDN_OK = 0
+GDN_E_INVAL, GDN_E_SHAPE, GDN_E_DTYPE, GDN_E_NOMEM, GDN_E_HIP = -1, -2, -3, -4, -5
+GDN_BF16, GDN_F32 = 0, 1
+GDN_L2NORM_QK = 1 << 0
+GDN_NO_COMMIT = 1 << 0
+GDN_SEQUENTIAL = 1 << 1
+GDN_KERNEL_PREP, GDN_KERNEL_SCAN, GDN_KERNEL_SEQ, GDN_KERNEL_COUNT = 0, 1, 2, 3
+KERNEL_NAMES = ("prep", "scan", "sequential")
+
+
+class GdnConfig(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("d_k", ctypes.c_int32),
+                ("d_v", ctypes.c_int32), ("max_tokens", ctypes.c_int64), ("subchunk", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32), ("l2_eps", ctypes.c_float),
+                ("scale", ctypes.c_float)]
+
+
+_Strides = ctypes.c_int64 * 3
+
+
+class GdnIo(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("o", ctypes.c_void_p), ("a", ctypes.c_void_p), ("beta", ctypes.c_void_p),
+                ("q_strides", _Strides), ("k_strides", _Strides), ("v_strides", _Strides),
+                ("o_strides", _Strides), ("g_strides", _Strides)]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"gdn error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load the in-tree library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m gated_deltanet_streaming_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i64, u32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_int
+    sigs = {
+        "gdn_stream_init": ([ctypes.POINTER(GdnConfig), i32, ctypes.POINTER(vp)], i32),
+        "gdn_stream_destroy": ([vp], i32),
+        "gdn_chunk_forward": ([vp, ctypes.POINTER(GdnIo), i64, u32, vp, vp], i32),
+        "gdn_chunk_reverse": ([vp, ctypes.POINTER(GdnIo), i64, u32, vp, vp], i32),
+        "gdn_chunk_bidir": ([vp, ctypes.POINTER(GdnIo), vp, i64, u32, vp, vp], i32),
+        "gdn_state_get": ([vp, vp, vp], i32),
+        "gdn_state_set": ([vp, vp, vp], i32),
+        "gdn_profile": ([vp, i32], i32),
+        "gdn_profile_read": ([vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), i32], i32),
+        "gdn_last_error": ([], ctypes.c_char_p),
+    }
+    for name, (args, res) in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def gdn_last_error() -> str:
+    return load_library().gdn_last_error().decode()
+
+
+def _check(rc):
+    if rc != GDN_OK:
+        raise GdnError(rc, gdn_last_error())
+
+
+def _stream_ptr(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _strides3(t):
+    st = t.stride()
+    return _Strides(st[0], st[1], st[2])
+
+
+def _make_io(q, k, v, o, a, beta):
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        if t.dim() != 4 or t.stride(-1) != 1:
+            raise ValueError(f"{name} must be [B, T, H, D] with a contiguous last dimension")
+    for name, t in (("a", a), ("beta", beta)):
+        if t.dim() != 3:
+            raise ValueError(f"{name} must be [B, T, H]")
+    if a.stride() != beta.stride():
+        raise ValueError("a and beta must share strides")
+    io = GdnIo()
+    io.q, io.k, io.v, io.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()
+    io.a, io.beta = a.data_ptr(), beta.data_ptr()
+    io.q_strides, io.k_strides, io.v_strides = _strides3(q), _strides3(k), _strides3(v)
+    io.o_strides, io.g_strides = _strides3(o), _strides3(a)
+    return io
+
+
+def gdn_stream_init(batch, heads, d_k, d_v, max_tokens, *, subchunk=0, io_dtype=GDN_BF16,
+                    l2norm=True, l2_eps=1e-6, scale=1.0, device=0):
+    """Create a handle; returns the opaque pointer (int)."""
+    lib = load_library()
+    cfg = GdnConfig(batch, heads, d_k, d_v, max_tokens, subchunk, io_dtype,
+                    GDN_L2NORM_QK if l2norm else 0, l2_eps, scale)
+    h = ctypes.c_void_p()
+    _check(lib.gdn_stream_init(ctypes.byref(cfg), int(device), ctypes.byref(h)))
+    return h.value
+
+
+def gdn_stream_destroy(handle):
+    _check(load_library().gdn_stream_destroy(ctypes.c_void_p(handle)))
+
+
+def gdn_chunk_forward(handle, q, k, v, a, beta, o, *, flags=0, state_out=None, stream=None):
+    io = _make_io(q, k, v, o, a, beta)
+    _check(load_library().gdn_chunk_forward(ctypes.c_void_p(handle), ctypes.byref(io), q.shape[1], flags,
+                                            _ptr(state_out), _stream_ptr(stream, q.device)))
+
+
+def gdn_chunk_reverse(handle, q, k, v, a, beta, o, *, flags=0, state_out=None, stream=None):
+    io = _make_io(q, k, v, o, a, beta)
+    _check(load_library().gdn_chunk_reverse(ctypes.c_void_p(handle), ctypes.byref(io), q.shape[1], flags,
+                                            _ptr(state_out), _stream_ptr(stream, q.device)))
+
+
+def gdn_chunk_bidir(handle, q, k, v, a, beta, o, o_rev, *, flags=0, state_out=None, stream=None):
+    if o_rev.stride() != o.stride():
+        raise ValueError("o_rev must have o's strides")
+    io = _make_io(q, k, v, o, a, beta)
+    _check(load_library().gdn_chunk_bidir(ctypes.c_void_p(handle), ctypes.byref(io), _ptr(o_rev), q.shape[1],
+                                          flags, _ptr(state_out), _stream_ptr(stream, q.device)))
+
+
+def gdn_state_get(handle, dst, *, stream=None):
+    _check(load_library().gdn_state_get(ctypes.c_void_p(handle), _ptr(dst), _stream_ptr(stream, dst.device)))
+
+
+def gdn_state_set(handle, src, *, stream=None, device=None):
+    dev = src.device if src is not None else device
+    _check(load_library().gdn_state_set(ctypes.c_void_p(handle), _ptr(src), _stream_ptr(stream, dev)))
+
+
+def gdn_profile(handle, enable=True):
+    _check(load_library().gdn_profile(ctypes.c_void_p(handle), int(bool(enable))))
+
+
+def gdn_profile_read(handle, reset=True):
+    """{kernel name: (total ms, launches)} for the timed launches since the last reset."""
+    ms = (ctypes.c_double * GDN_KERNEL_COUNT)()
+    n = (ctypes.c_int64 * GDN_KERNEL_COUNT)()
+    _check(load_library().gdn_profile_read(ctypes.c_void_p(handle), ms, n, int(bool(reset))))
+    return {KERNEL_NAMES[i]: (ms[i], n[i]) for i in range(GDN_KERNEL_COUNT)}
+
+
+class Stream:
+    """One handle: B streams x H heads of carried state on one device."""
+
+    def __init__(self, batch, heads, d_k, d_v, max_tokens, *, subchunk=0, io_dtype="bf16", l2norm=True,
+                 l2_eps=1e-6, scale=1.0, device=0):
+        self.shape = (batch, heads, d_v, d_k)
+        self.device = device
+        self.handle = gdn_stream_init(batch, heads, d_k, d_v, max_tokens, subchunk=subchunk,
+                                      io_dtype=GDN_F32 if io_dtype == "f32" else GDN_BF16, l2norm=l2norm,
+                                      l2_eps=l2_eps, scale=scale, device=device)
+
+    def forward(self, q, k, v, a, beta, o, **kw):
+        gdn_chunk_forward(self.handle, q, k, v, a, beta, o, **kw)
+
+    def reverse(self, q, k, v, a, beta, o, **kw):
+        gdn_chunk_reverse(self.handle, q, k, v, a, beta, o, **kw)
+
+    def bidir(self, q, k, v, a, beta, o, o_rev, **kw):
+        gdn_chunk_bidir(self.handle, q, k, v, a, beta, o, o_rev, **kw)
+
+    def state_get(self, dst=None, **kw):
+        import torch
+        if dst is None:
+            dst = torch.empty(self.shape, dtype=torch.float32, device=f"cuda:{self.device}")
+        gdn_state_get(self.handle, dst, **kw)
+        return dst
+
+    def state_set(self, src, **kw):
+        gdn_state_set(self.handle, src, device=f"cuda:{self.device}", **kw)
+
+    def close(self):
+        if self.handle:
+            gdn_stream_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

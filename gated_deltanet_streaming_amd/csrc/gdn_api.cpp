@@ -1,0 +1,408 @@
+// gdn_api.cpp -- C ABI of the Gated DeltaNet streaming core (include/gdn_stream.h).
+//
+// Owns the per-handle state cache (one d_v x d_k fp32 state per stream and
+// head: the pages' compact recurrent state, Chinese summary "Core method") and
+// a workspace fixed at init, so memory stays constant however long the stream
+// runs (the pages' constant-memory streaming, Chinese summary "Prerequisites",
+// "Streaming generation").  Every argument is validated before anything is
+// enqueued; on error the cache is untouched and nothing runs.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "gdn_internal.h"
+#include "gdn_stream.h"
+
+struct gdn_stream {
+    gdn_config cfg;
+    int device;
+    int C;                // sub-chunk of the chunked kernels
+    bool chunked_ok;      // chunked kernels exist for this shape and dtype
+    float* state;         // [B, H, d_v, d_k]
+    int64_t state_elems;
+    char* ws;             // chunked workspace: [2 directions][B][H][nsub_max] items
+    int64_t item_bytes;
+    int nsub_max;
+    // optional per-kernel timing
+    bool profile;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> pend;
+    std::vector<int> pend_kind;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> spare;
+    double acc_ms[gdn::KCOUNT];
+    int64_t acc_n[gdn::KCOUNT];
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok() {
+    g_err.clear();
+    return GDN_OK;
+}
+
+// Makes the handle's device current for the duration of a call.
+struct DeviceGuard {
+    int prev = -1;
+    bool changed = false;
+    hipError_t err = hipSuccess;
+    explicit DeviceGuard(int dev) {
+        err = hipGetDevice(&prev);
+        if (err == hipSuccess && prev != dev) {
+            err = hipSetDevice(dev);
+            changed = err == hipSuccess;
+        }
+    }
+    ~DeviceGuard() {
+        if (changed) (void)hipSetDevice(prev);
+    }
+};
+
+bool is_mult16(int x) { return x >= 16 && x <= 128 && x % 16 == 0; }
+
+int elem_size(const gdn_config& c) { return c.io_dtype == GDN_F32 ? 4 : 2; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_tensor(const char* name, const void* ptr, const int64_t* st, int esz) {
+    if (!ptr) return fail(GDN_E_INVAL, "%s is NULL", name);
+    if (!aligned16(ptr)) return fail(GDN_E_INVAL, "%s is not 16-byte aligned", name);
+    for (int i = 0; i < 3; ++i) {
+        if (st[i] < 0) return fail(GDN_E_INVAL, "%s stride %d is negative", name, i);
+        if ((st[i] * esz) % 16 != 0)
+            return fail(GDN_E_INVAL, "%s stride %d (%lld elements) is not a multiple of 16 bytes", name, i,
+                        (long long)st[i]);
+    }
+    return GDN_OK;
+}
+
+int check_call(gdn_stream* s, const gdn_io* io, int64_t T, uint32_t flags, const void* o_rev, bool need_rev) {
+    if (!s) return fail(GDN_E_INVAL, "handle is NULL");
+    if (!io) return fail(GDN_E_INVAL, "io is NULL");
+    if (flags & ~(uint32_t)(GDN_NO_COMMIT | GDN_SEQUENTIAL)) return fail(GDN_E_INVAL, "unknown flag bits 0x%x", flags);
+    if (T < 0 || T > s->cfg.max_tokens)
+        return fail(GDN_E_SHAPE, "T = %lld outside [0, max_tokens = %lld]", (long long)T, (long long)s->cfg.max_tokens);
+    if (T == 0) return GDN_OK;
+    const int esz = elem_size(s->cfg);
+    int rc;
+    if ((rc = check_tensor("q", io->q, io->q_strides, esz)) != GDN_OK) return rc;
+    if ((rc = check_tensor("k", io->k, io->k_strides, esz)) != GDN_OK) return rc;
+    if ((rc = check_tensor("v", io->v, io->v_strides, esz)) != GDN_OK) return rc;
+    if ((rc = check_tensor("o", io->o, io->o_strides, esz)) != GDN_OK) return rc;
+    if (need_rev && (rc = check_tensor("o_rev", o_rev, io->o_strides, esz)) != GDN_OK) return rc;
+    if (!io->a) return fail(GDN_E_INVAL, "a is NULL");
+    if (!io->beta) return fail(GDN_E_INVAL, "beta is NULL");
+    for (int i = 0; i < 3; ++i)
+        if (io->g_strides[i] < 0) return fail(GDN_E_INVAL, "gate stride %d is negative", i);
+    if (!(flags & GDN_SEQUENTIAL) && !s->chunked_ok)
+        return fail(GDN_E_SHAPE,
+                    "no chunked kernel for d_k=%d d_v=%d subchunk=%d io_dtype=%d; pass GDN_SEQUENTIAL",
+                    s->cfg.d_k, s->cfg.d_v, s->C, s->cfg.io_dtype);
+    return GDN_OK;
+}
+
+gdn::Params base_params(gdn_stream* s, const gdn_io* io, int64_t T) {
+    gdn::Params p;
+    std::memset(&p, 0, sizeof p);
+    p.q = io->q;
+    p.k = io->k;
+    p.v = io->v;
+    p.o[0] = p.o[1] = io->o;
+    p.a = io->a;
+    p.beta = io->beta;
+    for (int i = 0; i < 3; ++i) {
+        p.qs[i] = io->q_strides[i];
+        p.ks[i] = io->k_strides[i];
+        p.vs[i] = io->v_strides[i];
+        p.os[i] = io->o_strides[i];
+        p.gs[i] = io->g_strides[i];
+    }
+    p.T = T;
+    p.B = s->cfg.batch;
+    p.H = s->cfg.heads;
+    p.Dk = s->cfg.d_k;
+    p.Dv = s->cfg.d_v;
+    p.io_f32 = s->cfg.io_dtype == GDN_F32;
+    p.l2norm = (s->cfg.flags & GDN_L2NORM_QK) != 0;
+    p.eps = s->cfg.l2_eps;
+    p.scale = s->cfg.scale;
+    p.ws = s->ws;
+    p.ws_item_bytes = s->item_bytes;
+    p.nsub_max = s->nsub_max;
+    p.C = s->C;
+    return p;
+}
+
+// Fold finished timing events into the per-kernel totals.
+void drain_profile(gdn_stream* s) {
+    for (size_t i = 0; i < s->pend.size(); ++i) {
+        float ms = 0.f;
+        if (hipEventSynchronize(s->pend[i].second) == hipSuccess &&
+            hipEventElapsedTime(&ms, s->pend[i].first, s->pend[i].second) == hipSuccess) {
+            s->acc_ms[s->pend_kind[i]] += ms;
+            s->acc_n[s->pend_kind[i]] += 1;
+        }
+        s->spare.push_back(s->pend[i]);
+    }
+    s->pend.clear();
+    s->pend_kind.clear();
+}
+
+int run(gdn_stream* s, gdn::Params& p, uint32_t flags, hipStream_t st) {
+    DeviceGuard dg(s->device);
+    if (dg.err != hipSuccess) return fail(GDN_E_HIP, "hipSetDevice(%d): %s", s->device, hipGetErrorString(dg.err));
+    hipError_t prior = hipPeekAtLastError();
+    if (prior != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(GDN_E_HIP, "earlier HIP error: %s", hipGetErrorString(prior));
+    }
+    hipEvent_t evs[8];
+    int kinds[4];
+    gdn::Timing tm{nullptr, kinds, 4, 0};
+    if (s->profile) {
+        for (int i = 0; i < 4; ++i) {
+            std::pair<hipEvent_t, hipEvent_t> pr;
+            if (!s->spare.empty()) {
+                pr = s->spare.back();
+                s->spare.pop_back();
+            } else if (hipEventCreate(&pr.first) != hipSuccess || hipEventCreate(&pr.second) != hipSuccess) {
+                return fail(GDN_E_HIP, "hipEventCreate failed");
+            }
+            evs[2 * i] = pr.first;
+            evs[2 * i + 1] = pr.second;
+        }
+        tm.ev = evs;
+    }
+    hipError_t e = (flags & GDN_SEQUENTIAL) ? gdn::launch_sequential(p, st, &tm) : gdn::launch_chunked(p, st, &tm);
+    if (s->profile) {
+        for (int i = 0; i < 4; ++i) {
+            auto pr = std::make_pair(evs[2 * i], evs[2 * i + 1]);
+            if (i < tm.n) {
+                s->pend.push_back(pr);
+                s->pend_kind.push_back(kinds[i]);
+            } else {
+                s->spare.push_back(pr);
+            }
+        }
+    }
+    if (e != hipSuccess) return fail(GDN_E_HIP, "kernel launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+GDN_API int gdn_stream_init(const gdn_config* cfg, int device, gdn_stream** out) {
+    if (!cfg || !out) return fail(GDN_E_INVAL, "cfg and out must be non-NULL");
+    *out = nullptr;
+    const gdn_config c = *cfg;
+    if (c.batch < 1 || c.heads < 1) return fail(GDN_E_SHAPE, "batch and heads must be >= 1");
+    if (!is_mult16(c.d_k) || !is_mult16(c.d_v))
+        return fail(GDN_E_SHAPE, "d_k=%d d_v=%d must be multiples of 16 in [16, 128]", c.d_k, c.d_v);
+    if (c.max_tokens < 1) return fail(GDN_E_SHAPE, "max_tokens must be >= 1");
+    const int C = c.subchunk == 0 ? 64 : c.subchunk;
+    if (!(C == 16 || C == 32 || C == 64)) return fail(GDN_E_SHAPE, "subchunk %d not in {0, 16, 32, 64}", c.subchunk);
+    if (c.io_dtype != GDN_BF16 && c.io_dtype != GDN_F32) return fail(GDN_E_DTYPE, "unknown io_dtype %d", c.io_dtype);
+    if (c.flags & ~(uint32_t)GDN_L2NORM_QK) return fail(GDN_E_INVAL, "unknown config flag bits 0x%x", c.flags);
+    if (!std::isfinite(c.l2_eps) || c.l2_eps < 0.f) return fail(GDN_E_INVAL, "l2_eps must be finite and >= 0");
+    if (!std::isfinite(c.scale)) return fail(GDN_E_INVAL, "scale must be finite");
+
+    int ndev = 0;
+    hipError_t e = hipGetDeviceCount(&ndev);
+    if (e != hipSuccess) return fail(GDN_E_HIP, "hipGetDeviceCount: %s", hipGetErrorString(e));
+    if (device < 0 || device >= ndev) return fail(GDN_E_HIP, "device %d not present (%d devices)", device, ndev);
+    DeviceGuard dg(device);
+    if (dg.err != hipSuccess) return fail(GDN_E_HIP, "hipSetDevice(%d): %s", device, hipGetErrorString(dg.err));
+
+    gdn_stream* s = new (std::nothrow) gdn_stream();
+    if (!s) return fail(GDN_E_NOMEM, "host allocation failed");
+    s->cfg = c;
+    s->device = device;
+    s->C = C;
+    s->chunked_ok = gdn::chunked_supported(C, c.d_k, c.d_v, c.io_dtype == GDN_F32);
+    s->state_elems = (int64_t)c.batch * c.heads * c.d_v * c.d_k;
+    s->profile = false;
+    for (int i = 0; i < gdn::KCOUNT; ++i) {
+        s->acc_ms[i] = 0.0;
+        s->acc_n[i] = 0;
+    }
+    e = hipMalloc(&s->state, s->state_elems * sizeof(float));
+    if (e != hipSuccess) {
+        delete s;
+        return fail(GDN_E_NOMEM, "state cache allocation: %s", hipGetErrorString(e));
+    }
+    e = hipMemset(s->state, 0, s->state_elems * sizeof(float));
+    s->ws = nullptr;
+    s->item_bytes = 0;
+    s->nsub_max = 0;
+    if (e == hipSuccess && s->chunked_ok) {
+        s->item_bytes = gdn::chunk_item_bytes(C);
+        s->nsub_max = (int)((c.max_tokens + C - 1) / C);
+        const int64_t bytes = 2 * (int64_t)c.batch * c.heads * s->nsub_max * s->item_bytes;
+        e = hipMalloc(&s->ws, bytes);
+        if (e != hipSuccess) {
+            (void)hipFree(s->state);
+            delete s;
+            return fail(GDN_E_NOMEM, "workspace allocation (%lld bytes): %s", (long long)bytes, hipGetErrorString(e));
+        }
+    }
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        (void)hipFree(s->state);
+        if (s->ws) (void)hipFree(s->ws);
+        delete s;
+        return fail(GDN_E_HIP, "init: %s", hipGetErrorString(e));
+    }
+    *out = s;
+    return ok();
+}
+
+GDN_API int gdn_stream_destroy(gdn_stream* s) {
+    if (!s) return ok();
+    DeviceGuard dg(s->device);
+    hipError_t e = hipDeviceSynchronize();
+    for (auto& pr : s->pend) {
+        (void)hipEventDestroy(pr.first);
+        (void)hipEventDestroy(pr.second);
+    }
+    for (auto& pr : s->spare) {
+        (void)hipEventDestroy(pr.first);
+        (void)hipEventDestroy(pr.second);
+    }
+    (void)hipFree(s->state);
+    if (s->ws) (void)hipFree(s->ws);
+    delete s;
+    if (e != hipSuccess) return fail(GDN_E_HIP, "destroy: %s", hipGetErrorString(e));
+    return ok();
+}
+
+GDN_API int gdn_chunk_forward(gdn_stream* s, const gdn_io* io, int64_t T, uint32_t flags, float* state_out,
+                              void* hip_stream) {
+    int rc = check_call(s, io, T, flags, nullptr, false);
+    if (rc != GDN_OK) return rc;
+    hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+    const bool commit = !(flags & GDN_NO_COMMIT);
+    if (T == 0) {
+        if (!commit && state_out) {
+            DeviceGuard dg(s->device);
+            hipError_t e = hipMemcpyAsync(state_out, s->state, s->state_elems * sizeof(float),
+                                          hipMemcpyDeviceToDevice, st);
+            if (e != hipSuccess) return fail(GDN_E_HIP, "state copy: %s", hipGetErrorString(e));
+        }
+        return ok();
+    }
+    gdn::Params p = base_params(s, io, T);
+    p.S_in = s->state;
+    p.S_out[0] = commit ? s->state : state_out;
+    p.dir0 = 0;
+    p.ndirs = 1;
+    return run(s, p, flags, st);
+}
+
+GDN_API int gdn_chunk_reverse(gdn_stream* s, const gdn_io* io, int64_t T, uint32_t flags, float* state_out,
+                              void* hip_stream) {
+    int rc = check_call(s, io, T, flags, nullptr, false);
+    if (rc != GDN_OK) return rc;
+    hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+    if (T == 0) {
+        if (state_out) {
+            DeviceGuard dg(s->device);
+            hipError_t e = gdn::launch_zero(state_out, s->state_elems, st);
+            if (e != hipSuccess) return fail(GDN_E_HIP, "state zero: %s", hipGetErrorString(e));
+        }
+        return ok();
+    }
+    gdn::Params p = base_params(s, io, T);
+    p.S_in = nullptr;
+    p.S_out[1] = state_out;
+    p.dir0 = 1;
+    p.ndirs = 1;
+    return run(s, p, flags, st);
+}
+
+GDN_API int gdn_chunk_bidir(gdn_stream* s, const gdn_io* io, void* o_rev, int64_t T, uint32_t flags,
+                            float* state_out, void* hip_stream) {
+    int rc = check_call(s, io, T, flags, o_rev, T > 0);
+    if (rc != GDN_OK) return rc;
+    hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+    const bool commit = !(flags & GDN_NO_COMMIT);
+    if (T == 0) {
+        if (!commit && state_out) {
+            DeviceGuard dg(s->device);
+            hipError_t e = hipMemcpyAsync(state_out, s->state, s->state_elems * sizeof(float),
+                                          hipMemcpyDeviceToDevice, st);
+            if (e != hipSuccess) return fail(GDN_E_HIP, "state copy: %s", hipGetErrorString(e));
+        }
+        return ok();
+    }
+    gdn::Params p = base_params(s, io, T);
+    p.o[1] = o_rev;
+    p.S_in = s->state;
+    p.S_out[0] = commit ? s->state : state_out;
+    p.S_out[1] = nullptr;
+    p.dir0 = 0;
+    p.ndirs = 2;
+    return run(s, p, flags, st);
+}
+
+GDN_API int gdn_state_get(gdn_stream* s, float* dst, void* hip_stream) {
+    if (!s || !dst) return fail(GDN_E_INVAL, "handle and dst must be non-NULL");
+    DeviceGuard dg(s->device);
+    hipError_t e = hipMemcpyAsync(dst, s->state, s->state_elems * sizeof(float), hipMemcpyDeviceToDevice,
+                                  reinterpret_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(GDN_E_HIP, "state_get: %s", hipGetErrorString(e));
+    return ok();
+}
+
+GDN_API int gdn_state_set(gdn_stream* s, const float* src, void* hip_stream) {
+    if (!s) return fail(GDN_E_INVAL, "handle is NULL");
+    DeviceGuard dg(s->device);
+    hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+    hipError_t e = src ? hipMemcpyAsync(s->state, src, s->state_elems * sizeof(float), hipMemcpyDeviceToDevice, st)
+                       : gdn::launch_zero(s->state, s->state_elems, st);
+    if (e != hipSuccess) return fail(GDN_E_HIP, "state_set: %s", hipGetErrorString(e));
+    return ok();
+}
+
+GDN_API int gdn_profile(gdn_stream* s, int enable) {
+    if (!s) return fail(GDN_E_INVAL, "handle is NULL");
+    s->profile = enable != 0;
+    return ok();
+}
+
+GDN_API int gdn_profile_read(gdn_stream* s, double* ms, int64_t* launches, int reset) {
+    if (!s) return fail(GDN_E_INVAL, "handle is NULL");
+    DeviceGuard dg(s->device);
+    drain_profile(s);
+    for (int i = 0; i < gdn::KCOUNT; ++i) {
+        if (ms) ms[i] = s->acc_ms[i];
+        if (launches) launches[i] = s->acc_n[i];
+        if (reset) {
+            s->acc_ms[i] = 0.0;
+            s->acc_n[i] = 0;
+        }
+    }
+    return ok();
+}
+
+GDN_API const char* gdn_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

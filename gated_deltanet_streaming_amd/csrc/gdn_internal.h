@@ -1,0 +1,56 @@
+// Internal interface between the C ABI (gdn_api.cpp) and the gfx950 kernels
+// (gdn_kernels.hip).  Not installed; the public surface is include/gdn_stream.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+enum KernelKind { KPREP = 0, KSCAN = 1, KSEQ = 2, KCOUNT = 3 };
+
+// Everything one launch needs.  Directions: 0 = forward (t ascending, starts
+// from S_in), 1 = reverse (t descending, starts from zero).
+struct Params {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o[2];            // output per direction
+    const float* a;
+    const float* beta;
+    int64_t qs[3], ks[3], vs[3], os[3], gs[3];   // (b, t, h) strides, elements
+    int64_t T;
+    int B, H, Dk, Dv;
+    int io_f32;            // 0 = bf16, 1 = fp32 for q, k, v, o
+    int l2norm;
+    float eps, scale;
+    const float* S_in;     // forward start state [B, H, Dv, Dk], or null (zero)
+    float* S_out[2];       // final state per direction, or null
+    int dir0, ndirs;       // directions dir0 .. dir0 + ndirs - 1
+    // chunked path workspace: one item per (dir, b, h, sub-chunk)
+    char* ws;
+    int64_t ws_item_bytes;
+    int nsub_max;
+    int C;                 // sub-chunk length
+};
+
+// Bytes of one workspace item for sub-chunk C (multiple of 16, 16..64).
+int64_t chunk_item_bytes(int C);
+
+// Which (C, D) pairs the chunked kernels are built for.
+bool chunked_supported(int C, int Dk, int Dv, int io_f32);
+
+// Optional per-kernel timing: when `ev` is non-null, ev[2*i] / ev[2*i+1] are
+// recorded around launch i and *nlaunch receives the count (<= 4).
+struct Timing {
+    hipEvent_t* ev;
+    int* kinds;
+    int cap;
+    int n;
+};
+
+hipError_t launch_zero(float* x, int64_t n, hipStream_t s);
+hipError_t launch_sequential(const Params& p, hipStream_t s, Timing* tm);
+hipError_t launch_chunked(const Params& p, hipStream_t s, Timing* tm);
+
+}  // namespace gdn

@@ -1,0 +1,154 @@
+/*
+ * gdn_stream.h -- C ABI of the MI355X (gfx950) Gated DeltaNet streaming core.
+ *
+ * The operation (SANA-Streaming pages: the Korean review, section 1 "Key
+ * Terms", GDN entry -- a fixed-size state updated recursively from the previous
+ * one; the Chinese summary, "Core method" -- GDN blocks carry global
+ * information in a compact recurrent state; "Method steps" step 2 -- a chunk is
+ * 3 latent frames, the streaming model runs a forward scan that starts from the
+ * previous chunk's cache plus a backward scan inside the chunk).  The per-token
+ * update is the published Gated DeltaNet rule, which the pages name but do not
+ * print.  Per stream b and head h, with state S in R^{d_v x d_k}:
+ *
+ *     k^_t = k_t / sqrt(|k_t|^2 + eps),  q^_t likewise     (GDN_L2NORM_QK)
+ *     S_t  = a_t S_{t-1} (I - beta_t k^_t k^_t^T) + beta_t v_t k^_t^T
+ *     o_t  = scale * S_t q^_t
+ *
+ * gdn_chunk_forward runs t = 0..T-1 from the cached state of the handle and
+ * (by default) stores S_{T-1} back into the cache, so consecutive calls stream
+ * one long sequence in constant memory.  gdn_chunk_reverse runs t = T-1..0 from
+ * a zero state (the future chunk does not exist yet) and never touches the
+ * cache; o_t is stored at the token's own position.
+ *
+ * Conventions shared by every entry point
+ *  - Return GDN_OK (0) or a negative GDN_E_* code.  On any error nothing has
+ *    been enqueued and the cache is unchanged; gdn_last_error() gives a message
+ *    (thread-local, valid until the next call from the same thread).
+ *  - Device pointers are caller-owned, must live on the handle's device, and
+ *    are not retained after the call returns.  Work is enqueued asynchronously
+ *    on `hip_stream` (a hipStream_t; NULL = the null stream); the caller
+ *    synchronises.  A fault inside a kernel surfaces as GDN_E_HIP on a later
+ *    call or at the caller's synchronisation.
+ *  - One handle is one logical sequence: calls on a handle must not overlap in
+ *    time (use one stream per handle).  Different handles are independent.
+ *  - Strides are in elements, in the order (b, t, h); the feature dimension is
+ *    contiguous.  q/k/v/o rows must be 16-byte aligned.
+ */
+#ifndef GDN_STREAM_H
+#define GDN_STREAM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_API __attribute__((visibility("default")))
+
+/* return codes */
+#define GDN_OK        0
+#define GDN_E_INVAL  -1   /* NULL handle/pointer, bad flag, bad alignment      */
+#define GDN_E_SHAPE  -2   /* unsupported sizes, T outside [0, max_tokens]       */
+#define GDN_E_DTYPE  -3   /* unknown io_dtype                                   */
+#define GDN_E_NOMEM  -4   /* device allocation failed at init                   */
+#define GDN_E_HIP    -5   /* a HIP runtime call failed (incl. earlier faults)   */
+
+/* gdn_config.io_dtype: element type of q, k, v and o */
+#define GDN_BF16 0
+#define GDN_F32  1
+
+/* gdn_config.flags */
+#define GDN_L2NORM_QK (1u << 0)   /* normalise q and k per token (default on) */
+
+/* per-call flags */
+#define GDN_NO_COMMIT  (1u << 0)  /* forward: leave the cache unchanged; the final
+                                     state goes to state_out (when non-NULL)      */
+#define GDN_SEQUENTIAL (1u << 1)  /* use the token-sequential fp32 kernel instead
+                                     of the chunked MFMA kernels                 */
+
+typedef struct gdn_config {
+    int32_t batch;       /* B independent streams, >= 1                          */
+    int32_t heads;       /* H heads per stream, >= 1                             */
+    int32_t d_k;         /* key/query width: multiple of 16, 16..128             */
+    int32_t d_v;         /* value width (state rows): multiple of 16, 16..128;   */
+                         /* the chunked kernels need d_v == d_k (16, 32, 64, 112, 128) */
+    int64_t max_tokens;  /* largest T of any call; sizes the fixed workspace     */
+    int32_t subchunk;    /* chunked-kernel sub-chunk C: 0 (= 64), 16, 32 or 64  */
+    int32_t io_dtype;    /* GDN_BF16 or GDN_F32                                  */
+    uint32_t flags;      /* GDN_L2NORM_QK                                        */
+    float l2_eps;        /* eps inside the L2 norm (1e-6 is the usual value)     */
+    float scale;         /* output scale (1.0 when q is unit-norm)               */
+} gdn_config;
+
+typedef struct gdn_io {
+    const void* q;        /* [B, T, H, d_k] io_dtype                           */
+    const void* k;        /* [B, T, H, d_k] io_dtype                           */
+    const void* v;        /* [B, T, H, d_v] io_dtype                           */
+    void* o;              /* [B, T, H, d_v] io_dtype, written                  */
+    const float* a;       /* [B, T, H] decay a_t in (0, 1]; log-domain inside  */
+    const float* beta;    /* [B, T, H] write strength beta_t                    */
+    int64_t q_strides[3]; /* (b, t, h) strides of q, in elements                */
+    int64_t k_strides[3];
+    int64_t v_strides[3];
+    int64_t o_strides[3];
+    int64_t g_strides[3]; /* shared by a and beta                               */
+} gdn_io;
+
+typedef struct gdn_stream gdn_stream;
+
+/* Create a handle on `device`: allocates the state cache [B, H, d_v, d_k] fp32
+ * (zeroed) plus a workspace sized by max_tokens.  Memory is fixed here and never
+ * grows with the length of the stream.  Errors: GDN_E_INVAL (NULL cfg/out, bad
+ * flags), GDN_E_SHAPE, GDN_E_DTYPE, GDN_E_NOMEM, GDN_E_HIP (bad device). */
+GDN_API int gdn_stream_init(const gdn_config* cfg, int device, gdn_stream** out);
+
+/* Free every allocation of the handle (waits for its device to go idle).
+ * NULL is a no-op. */
+GDN_API int gdn_stream_destroy(gdn_stream* s);
+
+/* Causal forward scan of T tokens (0 <= T <= max_tokens) from the cached state;
+ * writes o for every token.  Without GDN_NO_COMMIT the final state replaces the
+ * cache; with it the cache is untouched and the final state goes to state_out
+ * ([B, H, d_v, d_k] fp32 device memory, may be NULL).  T = 0 leaves everything
+ * as it is (state_out, if given, receives the cached state). */
+GDN_API int gdn_chunk_forward(gdn_stream* s, const gdn_io* io, int64_t T, uint32_t flags,
+                              float* state_out, void* hip_stream);
+
+/* Backward scan inside the chunk: t = T-1 .. 0 from a zero state, each token
+ * with its own a_t and beta_t.  Writes o; never reads or writes the cache.
+ * state_out (may be NULL) receives the state after absorbing token 0. */
+GDN_API int gdn_chunk_reverse(gdn_stream* s, const gdn_io* io, int64_t T, uint32_t flags,
+                              float* state_out, void* hip_stream);
+
+/* Both scans of one chunk in one pass (the pair the streaming model runs per
+ * chunk): forward from the cache into o_fwd (committing unless GDN_NO_COMMIT,
+ * then the final forward state goes to state_out) and reverse into o_rev.
+ * `io->o` is o_fwd; o_rev has o's strides. */
+GDN_API int gdn_chunk_bidir(gdn_stream* s, const gdn_io* io, void* o_rev, int64_t T,
+                            uint32_t flags, float* state_out, void* hip_stream);
+
+/* Asynchronous device-to-device copy of the cache [B, H, d_v, d_k] fp32 into
+ * dst / from src (src NULL = zero the cache).  Checkpoint, resume and replay. */
+GDN_API int gdn_state_get(gdn_stream* s, float* dst, void* hip_stream);
+GDN_API int gdn_state_set(gdn_stream* s, const float* src, void* hip_stream);
+
+/* Per-kernel timing for measurement.  While enabled, every launch of the handle
+ * is bracketed by hipEvents recorded on the launch stream; gdn_profile_read
+ * waits for them and returns, per kernel kind (GDN_KERNEL_*), the summed
+ * duration in milliseconds and the launch count (arrays of GDN_KERNEL_COUNT;
+ * either may be NULL), then clears the totals when `reset` is non-zero. */
+#define GDN_KERNEL_PREP  0   /* chunk preparation (norms, gates, Gram, UT inverse) */
+#define GDN_KERNEL_SCAN  1   /* chunk scan (state recurrence and outputs)          */
+#define GDN_KERNEL_SEQ   2   /* token-sequential kernel                            */
+#define GDN_KERNEL_COUNT 3
+GDN_API int gdn_profile(gdn_stream* s, int enable);
+GDN_API int gdn_profile_read(gdn_stream* s, double* ms, int64_t* launches, int reset);
+
+/* Message for the last failing call on this thread ("" when none). */
+GDN_API const char* gdn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_STREAM_H */

@@ -1,0 +1,80 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_deltanet_streaming_amd import binding
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "gdn_stream.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"GDN_API\s+[\w\s\*]+?\b(gdn_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = declared_symbols()
+    for required in ("gdn_stream_init", "gdn_stream_destroy", "gdn_chunk_forward", "gdn_chunk_reverse",
+                     "gdn_state_get", "gdn_state_set", "gdn_last_error"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    missing = [n for n in declared_symbols() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_only_declared_symbols_are_exported():
+    out = os.popen(f"nm -D --defined-only {binding.library_path()}").read()
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    gdn = {n for n in exported if n.startswith("gdn_")}
+    assert gdn == set(declared_symbols())
+
+
+def _cfg(**kw):
+    base = dict(batch=1, heads=2, d_k=112, d_v=112, max_tokens=2640, subchunk=0, io_dtype=binding.GDN_BF16,
+                flags=binding.GDN_L2NORM_QK, l2_eps=1e-6, scale=1.0)
+    base.update(kw)
+    return binding.GdnConfig(**base)
+
+
+@pytest.mark.parametrize("bad, code", [
+    (dict(batch=0), binding.GDN_E_SHAPE),
+    (dict(heads=-1), binding.GDN_E_SHAPE),
+    (dict(d_k=100), binding.GDN_E_SHAPE),
+    (dict(d_v=144), binding.GDN_E_SHAPE),
+    (dict(max_tokens=0), binding.GDN_E_SHAPE),
+    (dict(subchunk=48), binding.GDN_E_SHAPE),
+    (dict(io_dtype=7), binding.GDN_E_DTYPE),
+    (dict(flags=0x80), binding.GDN_E_INVAL),
+    (dict(l2_eps=-1.0), binding.GDN_E_INVAL),
+    (dict(scale=float("nan")), binding.GDN_E_INVAL),
+])
+def test_init_rejects_bad_config(lib, bad, code):
+    h = ctypes.c_void_p(123)
+    rc = lib.gdn_stream_init(ctypes.byref(_cfg(**bad)), 0, ctypes.byref(h))
+    assert rc == code
+    assert h.value is None
+    assert binding.gdn_last_error()
+
+
+def test_null_arguments_are_rejected(lib):
+    h = ctypes.c_void_p()
+    assert lib.gdn_stream_init(None, 0, ctypes.byref(h)) == binding.GDN_E_INVAL
+    io = binding.GdnIo()
+    for fn in (lib.gdn_chunk_forward, lib.gdn_chunk_reverse):
+        assert fn(None, ctypes.byref(io), 1, 0, None, None) == binding.GDN_E_INVAL
+        assert "handle" in binding.gdn_last_error()
+    assert lib.gdn_chunk_bidir(None, ctypes.byref(io), None, 1, 0, None, None) == binding.GDN_E_INVAL
+    assert lib.gdn_state_get(None, None, None) == binding.GDN_E_INVAL
+    assert lib.gdn_state_set(None, None, None) == binding.GDN_E_INVAL
+    assert lib.gdn_stream_destroy(None) == binding.GDN_OK
