@@ -1,0 +1,227 @@
+"""Throughput of the GDN streaming core on one MI355X.
+
+Workload: one GDN layer on one 720p streaming chunk -- B=1 stream, H=20 heads,
+d_k = d_v = 112, T = 2640 tokens (3 latent frames x 22 x 40 tokens), bf16
+q/k/v/o, fp32 gates and state.  One step = the forward scan from the carried
+state (committed back to the cache) plus the reverse scan inside the chunk.
+Inputs are synthetic (seeded) and already resident in HBM; by default they
+rotate over enough buffer sets that the live set exceeds the 256 MB MALL, so
+every step streams from HBM.
+
+Prints one JSON line.  `value` is tokens per second per layer (T / step time).
+`roofline` is for the dominant kernel (the chunk scan): algorithmic bytes per
+launch (904 B per token-head per scan + the state read and write) over its
+average duration from HIP events recorded on its launch stream.
+`cpu_baseline` times the fp64 CPU oracle on the host cores over the same
+workload (the oracle is a test reference, not a tuned CPU implementation).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN tokens/s per layer at 2640-token 720p chunk; % of MFMA/HBM roofline"
+B, H, D, T = 1, 20, 112, 2640
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16
+BYTES_PER_TOKEN_HEAD = 4 * D * 2 + 2 * 4     # q, k, v, o in bf16 + a, beta in fp32
+STATE_BYTES = B * H * D * D * 4
+FLOPS_PER_TOKEN_HEAD = 6 * D * D             # S k, rank-1 update, S q
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_scan_720p.json")
+KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_streaming_amd", "csrc", "gdn_kernels.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def algorithmic_bytes(mode: str) -> int:
+    per_scan = B * T * H * BYTES_PER_TOKEN_HEAD
+    fwd = per_scan + 2 * STATE_BYTES
+    return fwd + per_scan if mode in ("bidir", "separate") else fwd
+
+
+def load_traffic():
+    """HBM bytes per scan launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(d, threads):
+    import oracle
+    oracle.build(force=False)
+    reps, t0 = 0, time.perf_counter()
+    while reps < 20 and (reps < 2 or time.perf_counter() - t0 < 10.0):
+        oracle.forward(d["q"], d["k"], d["v"], d["a"], d["beta"], d["S0"], threads=threads)
+        oracle.reverse(d["q"], d["k"], d["v"], d["a"], d["beta"], threads=threads)
+        reps += 1
+    dt = (time.perf_counter() - t0) / reps
+    return {"value": round(T / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the full workload, {reps} repeats: forward + reverse fp64 scans of B={B} H={H} "
+                      f"d={D} T={T} ({dt:.3f} s per step)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--mode", choices=["bidir", "separate"], default="bidir",
+                    help="bidir: one gdn_chunk_bidir call per step; separate: forward then reverse calls")
+    ap.add_argument("--sets", type=int, default=6, help="rotating input/output buffer sets (1 = warm)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a 256 MiB device copy (reference for counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path needs no "
+              "multi-GPU exchange; see the sharding notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gdn_inputs
+    from gated_deltanet_streaming_amd import binding as gb
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = gdn_inputs.batch(1, B, T, H, D, with_state=True)
+
+    sets = []
+    for i in range(args.sets):
+        # distinct values per set (the first set is the seeded workload itself)
+        di = d if i == 0 else gdn_inputs.batch(1, B, T, H, D, chunk=i)
+        qi = {k: torch.from_numpy(di[k]).to(dev, torch.bfloat16) for k in ("q", "k", "v")}
+        qi["a"] = torch.from_numpy(di["a"]).to(dev)
+        qi["beta"] = torch.from_numpy(di["beta"]).to(dev)
+        qi["o"] = torch.empty_like(qi["v"])
+        qi["o_rev"] = torch.empty_like(qi["v"])
+        sets.append(qi)
+
+    s = gb.Stream(B, H, D, D, T, device=0)
+    s.state_set(torch.from_numpy(d["S0"]).to(dev))
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        x = sets[i % len(sets)]
+        if args.mode == "bidir":
+            s.bidir(x["q"], x["k"], x["v"], x["a"], x["beta"], x["o"], x["o_rev"], stream=stream)
+        else:
+            s.forward(x["q"], x["k"], x["v"], x["a"], x["beta"], x["o"], stream=stream)
+            s.reverse(x["q"], x["k"], x["v"], x["a"], x["beta"], x["o_rev"], stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, no per-kernel events
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_events = e0.elapsed_time(e1)
+    ms_per_step = wall * 1e3 / args.steps
+    print(f"# timed {args.steps} steps: wall {wall * 1e3:.3f} ms, events {ms_events:.3f} ms", file=sys.stderr,
+          flush=True)
+
+    # second pass over the same steps with per-kernel HIP events on the launch stream
+    gb.gdn_profile(s.handle, True)
+    gb.gdn_profile_read(s.handle, reset=True)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    prof = gb.gdn_profile_read(s.handle, reset=True)
+    gb.gdn_profile(s.handle, False)
+    scan_ms, scan_n = prof["scan"]
+    prep_ms, prep_n = prof["prep"]
+    scan_avg_ms = scan_ms / max(scan_n, 1)
+    prep_avg_ms = prep_ms / max(prep_n, 1)
+
+    if args.copy_probe:
+        src = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    alg_bytes = algorithmic_bytes(args.mode)
+    launches_per_step = scan_n / args.steps
+    bytes_per_scan_launch = alg_bytes / launches_per_step
+    achieved_gbs = bytes_per_scan_launch / (scan_avg_ms * 1e-3) / 1e9
+    step_gbs = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    flops = 2 * B * T * H * FLOPS_PER_TOKEN_HEAD
+    traffic = load_traffic()
+
+    out = {
+        "metric": METRIC,
+        "value": round(T / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "720p streaming chunk, one GDN layer: forward scan from the carried state + "
+                        "intra-chunk reverse scan",
+            "B": B, "H": H, "d_k": D, "d_v": D, "T": T, "subchunk": 64,
+            "call": "gdn_chunk_bidir" if args.mode == "bidir" else "gdn_chunk_forward + gdn_chunk_reverse",
+            "buffers": f"{args.sets} rotating sets ({'cold: live set > 256 MB MALL' if args.sets >= 6 else 'warm'})",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "gdn_scan_kernel",
+            "kernel_avg_us": round(scan_avg_ms * 1e3, 3),
+            "algorithmic_bytes_per_launch": int(bytes_per_scan_launch),
+        },
+        "step_roofline": {
+            "algorithmic_bytes_per_step": alg_bytes,
+            "achieved_GBs": round(step_gbs, 1),
+            "hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+            "mfma_bf16_frac": round(flops / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
+            "prep_avg_us": round(prep_avg_ms * 1e3, 3),
+            "scan_avg_us": round(scan_avg_ms * 1e3, 3),
+            "event_ms_per_step": round(ms_events / args.steps, 5),
+        },
+    }
+    if not args.no_cpu:
+        # the host share of one GPU: OMP_NUM_THREADS when set (16 on the GPU machines), else the affinity mask
+        threads = min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS", "0")) or 1 << 30)
+        out["cpu_baseline"] = cpu_baseline(d, threads)
+    s.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

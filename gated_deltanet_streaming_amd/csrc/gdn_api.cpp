@@ -81,7 +81,10 @@ int elem_size(const gdn_config& c) { return c.io_dtype == GDN_F32 ? 4 : 2; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int check_tensor(const char* name, const void* ptr, const int64_t* st, int esz) {
+// Rows of one (stream, head) are addressed with 32-bit byte offsets from a
+// per-(b, h) base, and rows past the end of the sequence must not overlap real
+// rows (they read as zero): token stride >= row width, extent < 2 GiB.
+int check_tensor(const char* name, const void* ptr, const int64_t* st, int esz, int width, int64_t T) {
     if (!ptr) return fail(GDN_E_INVAL, "%s is NULL", name);
     if (!aligned16(ptr)) return fail(GDN_E_INVAL, "%s is not 16-byte aligned", name);
     for (int i = 0; i < 3; ++i) {
@@ -90,6 +93,10 @@ int check_tensor(const char* name, const void* ptr, const int64_t* st, int esz) 
             return fail(GDN_E_INVAL, "%s stride %d (%lld elements) is not a multiple of 16 bytes", name, i,
                         (long long)st[i]);
     }
+    if (st[1] < width)
+        return fail(GDN_E_INVAL, "%s token stride %lld is smaller than the row width %d", name, (long long)st[1], width);
+    if ((T + 64) * st[1] * esz >= ((int64_t)1 << 31))
+        return fail(GDN_E_SHAPE, "%s: T * token stride exceeds the 2 GiB per-(stream, head) extent", name);
     return GDN_OK;
 }
 
@@ -102,11 +109,12 @@ int check_call(gdn_stream* s, const gdn_io* io, int64_t T, uint32_t flags, const
     if (T == 0) return GDN_OK;
     const int esz = elem_size(s->cfg);
     int rc;
-    if ((rc = check_tensor("q", io->q, io->q_strides, esz)) != GDN_OK) return rc;
-    if ((rc = check_tensor("k", io->k, io->k_strides, esz)) != GDN_OK) return rc;
-    if ((rc = check_tensor("v", io->v, io->v_strides, esz)) != GDN_OK) return rc;
-    if ((rc = check_tensor("o", io->o, io->o_strides, esz)) != GDN_OK) return rc;
-    if (need_rev && (rc = check_tensor("o_rev", o_rev, io->o_strides, esz)) != GDN_OK) return rc;
+    const int dk = s->cfg.d_k, dv = s->cfg.d_v;
+    if ((rc = check_tensor("q", io->q, io->q_strides, esz, dk, T)) != GDN_OK) return rc;
+    if ((rc = check_tensor("k", io->k, io->k_strides, esz, dk, T)) != GDN_OK) return rc;
+    if ((rc = check_tensor("v", io->v, io->v_strides, esz, dv, T)) != GDN_OK) return rc;
+    if ((rc = check_tensor("o", io->o, io->o_strides, esz, dv, T)) != GDN_OK) return rc;
+    if (need_rev && (rc = check_tensor("o_rev", o_rev, io->o_strides, esz, dv, T)) != GDN_OK) return rc;
     if (!io->a) return fail(GDN_E_INVAL, "a is NULL");
     if (!io->beta) return fail(GDN_E_INVAL, "beta is NULL");
     for (int i = 0; i < 3; ++i)
