@@ -262,7 +262,7 @@ GDN_API int gdn_stream_init(const gdn_config* cfg, int device, gdn_stream** out)
     s->item_bytes = 0;
     s->nsub_max = 0;
     if (e == hipSuccess && s->chunked_ok) {
-        s->item_bytes = gdn::chunk_item_bytes(C);
+        s->item_bytes = gdn::chunk_item_bytes(C, c.d_k);
         s->nsub_max = (int)((c.max_tokens + C - 1) / C);
         const int64_t bytes = 2 * (int64_t)c.batch * c.heads * s->nsub_max * s->item_bytes;
         e = hipMalloc(&s->ws, bytes);

@@ -35,7 +35,7 @@ struct Params {
 };
 
 // Bytes of one workspace item for sub-chunk C (multiple of 16, 16..64).
-int64_t chunk_item_bytes(int C);
+int64_t chunk_item_bytes(int C, int D);
 
 // Which (C, D) pairs the chunked kernels are built for.
 bool chunked_supported(int C, int Dk, int Dv, int io_f32);

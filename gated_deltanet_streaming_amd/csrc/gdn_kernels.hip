@@ -10,18 +10,22 @@
 //  * gdn_seq_kernel -- token-sequential fp32 recurrence, one 64-lane workgroup
 //    per (direction, stream, head, 16 state rows).  Plain and exact; the anchor.
 //  * chunked path -- the pages' fused kernel works in stages (frame summaries,
-//    recurrent scan, apply state; Chinese summary "Method steps" step 4).  Here:
-//      gdn_prep_kernel  (parallel over sub-chunks of C tokens): per-token L2
-//        norms, in-chunk log-gate prefix g, the Gram products K K^T and Q K^T on
-//        bf16 MFMA, the decay-masked in-chunk attention A, and the UT transform
-//        T = (I + L)^{-1} with L[t,s] = beta_t e^{g_t-g_s} k^_t.k^_s (s < t).
-//      gdn_scan_kernel  (serial over sub-chunks): one wavefront owns 16 rows of
-//        one head's state, kept in MFMA accumulators for the whole call, and per
-//        sub-chunk computes  X = K S^T, U = T (diag(beta) V - diag(beta e^g) X),
-//        O = diag(e^g) Q S^T + A U,  S <- e^{g_C} S + U^T diag(e^{g_C-g}) K^.
+//    recurrent scan, apply state; Chinese summary "Method steps" step 4).  Here
+//    a sequence is cut into processing steps of C tokens and:
+//      gdn_prep_kernel  (parallel over steps): per-token L2 norms, the in-step
+//        log-gate prefix g, the Gram products K K^T and Q K^T on bf16 MFMA, the
+//        UT transform T = (I + L)^{-1} with L[t,s] = beta_t e^{g_t-g_s} k^_t.k^_s
+//        (s < t), and from them two step operators that do not depend on the
+//        state: E = A T (A = decay-masked in-step attention) and
+//        Z = T^T diag(e^{g_C-g}) K^.
+//      gdn_scan_kernel  (serial over steps): per (direction, stream, head, 16
+//        state rows) one wavefront keeps its state slice in MFMA accumulators
+//        for the whole call and per step computes X = K S^T,
+//        R = diag(beta) V - diag(beta e^g / |k|) X and S^T <- e^{g_C} S^T + Z^T R;
+//        a second wavefront forms O = diag(scale e^g / |q|) Q S^T + E R.
 //    The raw bf16 q/k enter the MFMAs unrounded (norms are applied as row
-//    scales); the bounded in-chunk operands T, A, R, U, K^ use fp16 (11-bit
-//    significand), the state enters its two products as bf16, everything
+//    scales); the bounded in-step operands E, Z, R use fp16 (11-bit
+//    significand), the state enters its products as bf16, everything
 //    accumulates in fp32.
 //
 // MFMA lane layouts (16x16 output tiles, 64 lanes, l = lane, g = l / 16):
@@ -46,6 +50,7 @@ typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef f16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // decays below e^-80 are treated as e^-80 (the state is forgotten either way)
 #define GDN_MIN_LOG_DECAY (-80.0f)
@@ -64,11 +69,6 @@ __device__ __forceinline__ f32x4 mma_bf16_k16(bf16x4 a, bf16x4 b, f32x4 c) {
 }
 __device__ __forceinline__ f32x4 mma_f16_k32(f16x8 a, f16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mma_f16_k16(f16x4 a, f16x4 b, f32x4 c) {
-    const f16 z = (f16)0.f;
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(f16x8{a[0], a[1], a[2], a[3], z, z, z, z},
-                                                  f16x8{b[0], b[1], b[2], b[3], z, z, z, z}, c, 0, 0, 0);
 }
 
 // Keeps a value in its registers up to this point.  An MFMA may start executing
@@ -112,18 +112,44 @@ struct Blocks {
     static constexpr int TOTAL = offset(NB);
 };
 
-// workspace item: [T fragments][A fragments][scalars 5*C][gamma_C], 1 KB per fragment block
-template <int NB>
+// Order of the state index d in the scan.  The scan keeps S^T in MFMA output tiles
+// m = 0..ND-1 (rows j = 0..15); row j of tile m holds d = dperm(m, j).  Within each
+// 32-wide block, tile 2c takes d = 32c + 8(j/4) + j%4 and tile 2c+1 takes
+// d = 32c + 8(j/4) + 4 + j%4, so that the 8 k-slots a lane group contributes to a
+// product over d are 8 consecutive d (one 16-byte load of a bf16 row).  A trailing
+// single tile (odd ND) keeps d = 16m + j.
+template <int ND>
+__host__ __device__ constexpr int dperm(int m, int j) {
+    return (m < (ND & ~1)) ? 32 * (m >> 1) + 8 * (j >> 2) + 4 * (m & 1) + (j & 3) : 16 * m + j;
+}
+
+// workspace item of one processing step: [E fragments: TOTAL blocks][Z^T fragments:
+// ND x NKT blocks][scalars: c1, c2 (C floats each), gamma_C], 1 KB per fragment
+// block (64 lanes x 16 bytes)
+template <int NB, int ND>
 __host__ __device__ constexpr int64_t item_bytes_t() {
-    int64_t b = 2 * 1024 * (int64_t)Blocks<NB>::TOTAL + 4 * (5 * 16 * NB + 4);
+    constexpr int NKT = Blocks<NB>::NFULL + (Blocks<NB>::HALF ? 1 : 0);
+    int64_t b = 1024 * (int64_t)(Blocks<NB>::TOTAL + ND * NKT) + 4 * (2 * 16 * NB + 4);
     return (b + 255) / 256 * 256;
 }
 
-int64_t chunk_item_bytes(int C) {
+template <int NB>
+static int64_t item_bytes_d(int D) {
+    switch (D) {
+        case 16: return item_bytes_t<NB, 1>();
+        case 32: return item_bytes_t<NB, 2>();
+        case 64: return item_bytes_t<NB, 4>();
+        case 112: return item_bytes_t<NB, 7>();
+        case 128: return item_bytes_t<NB, 8>();
+        default: return -1;
+    }
+}
+
+int64_t chunk_item_bytes(int C, int D) {
     switch (C) {
-        case 16: return item_bytes_t<1>();
-        case 32: return item_bytes_t<2>();
-        case 64: return item_bytes_t<4>();
+        case 16: return item_bytes_d<1>(D);
+        case 32: return item_bytes_d<2>(D);
+        case 64: return item_bytes_d<4>(D);
         default: return -1;
     }
 }
@@ -240,31 +266,42 @@ struct TokMap {
     __device__ __forceinline__ int operator()(int n, int C, int t) const { return base + sgn * (n * C + t); }
 };
 
-__device__ __forceinline__ f16x4 u2_to_f16x4(uint2 u) { return __builtin_bit_cast(f16x4, u); }
-__device__ __forceinline__ bf16x4 u2_to_bf16x4(uint2 u) { return __builtin_bit_cast(bf16x4, u); }
 
 // ---------------------------------------------------------------------------
 // Chunk preparation: one workgroup (NB wavefronts) per (direction, b, h,
-// processing step n).  Rows are stored in processing order.
+// processing step n).  Rows are in processing order.  For the C tokens of the
+// step, with k^ = k/|k|, q^ = q/|q|, g = prefix of log a, gamma = e^g:
+//   L[t,s] = beta_t e^{g_t-g_s} k^_t.k^_s (s < t),   T = (I + L)^{-1}
+//   A[t,s] = scale e^{g_t-g_s} q^_t.k^_s (s <= t)
+//   E = A T diag(beta)                  (output:  O = diag(c2) Q S^T + E R)
+//   Z = diag(beta) T^T diag(e^{g_C-g}/|k|) K  (state: S^T <- gamma_C S^T + Z^T R)
+// with R = V - diag(c1) K S^T, c1 = gamma/|k|, c2 = scale gamma/|q|.  (The gate
+// beta is folded into E and Z, so the serial scan needs one scale per token.)
+// E and Z^T are stored as fp16 MFMA fragments for the scan; the state dimension
+// d of Z^T follows the scan's state order (see dperm).
 // ---------------------------------------------------------------------------
 template <int NB, int ND>
 __global__ __launch_bounds__(64 * NB) void gdn_prep_kernel(Params p) {
     constexpr int C = 16 * NB, D = 16 * ND;
-    constexpr int LDR = D + 8;   // bf16 row stride of the staged K and Q rows
-    constexpr int LDM = C + 4;   // fp32 row stride of L^T, T, A
+    constexpr int LDR = D + 8;   // bf16 row stride of the staged K and Q rows (8-byte aligned rows)
+    constexpr int LDM = C + 4;   // fp32 row stride of L^T, T^T, A (16-byte aligned rows)
     constexpr int NT = 64 * NB;
     constexpr int CH = D / 8;    // 16-byte chunks per row
     using BK = Blocks<NB>;
+    constexpr int NFT = BK::NFULL;
+    constexpr bool HT = BK::HALF;
+    constexpr int NKT = NFT + (HT ? 1 : 0);
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-    // K and Q rows (bf16) share storage with T (fp32), which is built after the Gram products
-    constexpr int KQ_BYTES = 2 * C * LDR * 2, T_BYTES = C * LDM * 4;
-    __shared__ __align__(16) char KQT[KQ_BYTES > T_BYTES ? KQ_BYTES : T_BYTES];
+    // Q rows (bf16) share storage with T^T (fp32), which is built after the Gram products
+    constexpr int Q_BYTES = C * LDR * 2, T_BYTES = C * LDM * 4;
+    __shared__ __align__(16) bf16 Ks[C * LDR];
+    __shared__ __align__(16) char QT[Q_BYTES > T_BYTES ? Q_BYTES : T_BYTES];
     __shared__ __align__(16) float Lt[C * LDM];   // L transposed: Lt[s][t] = L[t][s], s < t
-    __shared__ __align__(16) float Am[C * LDM];
-    __shared__ float sc[4][C];   // 0: log a then g, 1: beta, 2: 1/|k|, 3: 1/|q|
-    bf16* Ks = reinterpret_cast<bf16*>(KQT);
-    bf16* Qs = Ks + C * LDR;
-    float* Tm = reinterpret_cast<float*>(KQT);
+    __shared__ __align__(16) float Am[C * LDM];   // A[t][s]
+    __shared__ __align__(16) float sc[5][C];      // 0: log a then g, 1: beta, 2: 1/|k|, 3: 1/|q|, 4: e^{g_C-g}/|k|
+    bf16* Qs = reinterpret_cast<bf16*>(QT);
+    float* Tt = reinterpret_cast<float*>(QT);     // T transposed: Tt[u][s] = T[s][u]
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, r = lane & 15;
@@ -334,8 +371,9 @@ __global__ __launch_bounds__(64 * NB) void gdn_prep_kernel(Params p) {
         if (lane < C) sc[0][lane] = x;
     }
     __syncthreads();
+    if (tid < C) sc[4][tid] = __expf(sc[0][C - 1] - sc[0][tid]) * sc[2][tid];
 
-    // Gram tiles on MFMA: K K^T -> L (strictly lower), Q K^T -> A (lower incl. diagonal)
+    // Gram tiles on MFMA: K K^T -> L (strictly lower, stored transposed), Q K^T -> A (lower incl. diagonal)
     {
         constexpr int NTILE = NB * (NB + 1) / 2;
         for (int tt = w; tt < 2 * NTILE; tt += NB) {
@@ -357,19 +395,24 @@ __global__ __launch_bounds__(64 * NB) void gdn_prep_kernel(Params p) {
                 aoh = ld_bf16x4(arow + 32 * (ND / 2) + 4 * g);
                 boh = ld_bf16x4(brow + 32 * (ND / 2) + 4 * g);
             }
+            // per-row (t = 16 mt + 4 g + i) and per-column (s = 16 nt + r) scalars
+            const int s = 16 * nt + r, t0 = 16 * mt + 4 * g;
+            const f32x4 gt = *reinterpret_cast<const f32x4*>(&sc[0][t0]);
+            const f32x4 bt = *reinterpret_cast<const f32x4*>(&sc[1][t0]);
+            const f32x4 rt = *reinterpret_cast<const f32x4*>(&sc[isq ? 3 : 2][t0]);
+            const float gs = sc[0][s], rs = sc[2][s];
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < ND / 2; ++ks) acc = mma_bf16_k32(aop[ks], bop[ks], acc);
             if constexpr (ND % 2) acc = mma_bf16_k16(aoh, boh, acc);
-            const int s = 16 * nt + r;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int t = 16 * mt + 4 * g + i;
-                const float dec = (s <= t) ? __expf(sc[0][t] - sc[0][s]) : 0.f;
+                const int t = t0 + i;
+                const float dec = (s <= t) ? __expf(gt[i] - gs) : 0.f;
                 if (!isq)
-                    Lt[s * LDM + t] = (s < t) ? sc[1][t] * dec * sc[2][t] * sc[2][s] * acc[i] : 0.f;
+                    Lt[s * LDM + t] = (s < t) ? bt[i] * dec * rt[i] * rs * acc[i] : 0.f;
                 else
-                    Am[t * LDM + s] = (s <= t) ? p.scale * dec * sc[3][t] * sc[2][s] * acc[i] : 0.f;
+                    Am[t * LDM + s] = (s <= t) ? p.scale * dec * rt[i] * rs * acc[i] : 0.f;
             }
 #pragma unroll
             for (int ks = 0; ks < ND / 2; ++ks) {
@@ -384,8 +427,9 @@ __global__ __launch_bounds__(64 * NB) void gdn_prep_kernel(Params p) {
     }
     __syncthreads();
 
-    // T = (I + L)^{-1}.  16x16 diagonal blocks: one lane per (block, column),
-    // right-looking forward substitution.
+    // T = (I + L)^{-1}, built transposed.  16x16 diagonal blocks: one lane per
+    // (block, column j), right-looking forward substitution; column j of T_bb is
+    // row j of Tt.
     if (tid < C) {
         const int o = 16 * (tid >> 4), j = tid & 15;
         float x[16];
@@ -394,15 +438,24 @@ __global__ __launch_bounds__(64 * NB) void gdn_prep_kernel(Params p) {
 #pragma unroll
         for (int k = 0; k < 15; ++k) {
             const float* lcol = Lt + (o + k) * LDM + o;   // L[o + i][o + k] for i > k
+            float lv[16];
 #pragma unroll
-            for (int i = k + 1; i < 16; ++i) x[i] -= lcol[i] * x[k];
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const f32x4 v4 = *reinterpret_cast<const f32x4*>(lcol + 4 * i4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) lv[4 * i4 + e] = v4[e];
+            }
+#pragma unroll
+            for (int i = k + 1; i < 16; ++i) x[i] -= lv[i] * x[k];
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) Tm[(o + i) * LDM + o + j] = x[i];
+        for (int i4 = 0; i4 < 4; ++i4)
+            *reinterpret_cast<f32x4*>(Tt + (o + j) * LDM + o + 4 * i4) =
+                f32x4{x[4 * i4], x[4 * i4 + 1], x[4 * i4 + 2], x[4 * i4 + 3]};
     }
     __syncthreads();
-    // off-diagonal blocks, by distance d from the diagonal, on fp32 MFMA:
-    // T_ij = -T_ii sum_{k=j}^{i-1} L_ik T_kj  (one wavefront per block)
+    // off-diagonal blocks, by distance d from the diagonal, on fp32 MFMA (one wavefront per block):
+    //   T_ij = -T_ii sum_{k=j}^{i-1} L_ik T_kj
     for (int d = 1; d < NB; ++d) {
         if (w < NB - d) {
             const int ib = w + d, jb = w;
@@ -412,12 +465,11 @@ __global__ __launch_bounds__(64 * NB) void gdn_prep_kernel(Params p) {
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
                     const int k = 16 * kb + 4 * kk + g;
-                    la[kk] = Lt[k * LDM + 16 * ib + r];
-                    tb[kk] = Tm[k * LDM + 16 * jb + r];
+                    la[kk] = Lt[k * LDM + 16 * ib + r];      // L[16 ib + r][k]
+                    tb[kk] = Tt[(16 * jb + r) * LDM + k];     // T[k][16 jb + r]
                 }
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) z = __builtin_amdgcn_mfma_f32_16x16x4f32(la[kk], tb[kk], z, 0, 0, 0);
-                // z is consumed by the next block product or below; keep its operands until then
                 const float zs = z[0];
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
@@ -426,75 +478,169 @@ __global__ __launch_bounds__(64 * NB) void gdn_prep_kernel(Params p) {
                 }
                 keep_alive(zs);
             }
-            // z: lane (column r, group g) holds Z[4g + e][r]; use it as the B operand with k = 4g + kk
+            // z: lane (column r, group g) holds Z[4g + e][r]; B operand with k = 4g + kk
             float ta[4];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) ta[kk] = Tm[(16 * ib + r) * LDM + 16 * ib + 4 * g + kk];
+            for (int kk = 0; kk < 4; ++kk) ta[kk] = Tt[(16 * ib + 4 * g + kk) * LDM + 16 * ib + r];   // T[16 ib + r][16 ib + 4g + kk]
             f32x4 t4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) t4 = __builtin_amdgcn_mfma_f32_16x16x4f32(ta[kk], z[kk], t4, 0, 0, 0);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Tm[(16 * ib + 4 * g + e) * LDM + 16 * jb + r] = -t4[e];
+            // T[16 ib + 4g + e][16 jb + r] -> Tt[16 jb + r][16 ib + 4g + e]
+            *reinterpret_cast<f32x4*>(Tt + (16 * jb + r) * LDM + 16 * ib + 4 * g) = -t4;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) keep_alive(ta[kk]);
         }
         __syncthreads();
     }
 
-    // store T and A as fp16 MFMA A-operand fragments, then the per-token scalars
     char* item = p.ws + ((((int64_t)dir * p.B + b) * p.H + h) * p.nsub_max + n) * p.ws_item_bytes;
-    f16* Tsw = reinterpret_cast<f16*>(item);
-    f16* Asw = Tsw + BK::TOTAL * 512;
-    float* scw = reinterpret_cast<float*>(item + 2 * 1024 * BK::TOTAL);
+    uint4* Efr = reinterpret_cast<uint4*>(item);                          // BK::TOTAL blocks
+    uint4* Zfr = Efr + BK::TOTAL * 64;                                    // ND x NKT blocks
+    float* scw = reinterpret_cast<float*>(item + 1024 * (BK::TOTAL + ND * NKT));
+
+    // E^T = T^T A^T, tile (ut, tt) = sum_s Tt[u][s] A[t][s] over s in [16 ut, 16 tt + 16); the
+    // output tiles (2ks, mt) and (2ks + 1, mt) form the O-product A fragment (mt, ks) directly.
     for (int blk = w; blk < BK::TOTAL; blk += NB) {
         int mt = 0;
         while (BK::offset(mt + 1) <= blk) ++mt;
-        const int idx = blk - BK::offset(mt);
-        const int row = 16 * mt + r;
-        f16x8 tv, av;
-        if (idx < BK::nfull_for(mt)) {
+        const int ks = blk - BK::offset(mt);
+        f32x4 et[2];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int col = 32 * idx + 16 * (i >> 2) + 4 * g + (i & 3);
-                tv[i] = (col <= row) ? (f16)Tm[row * LDM + col] : (f16)0.f;
-                av[i] = (col <= row) ? (f16)Am[row * LDM + col] : (f16)0.f;
-            }
-        } else {
+        for (int hh = 0; hh < 2; ++hh) {
+            const int ut = 2 * ks + hh;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (ut <= mt) {
+                // contraction over s in 32-wide steps (zero outside the triangle)
+                for (int ss = (16 * ut) / 32; ss * 32 < 16 * (mt + 1); ++ss) {
+                    const float* ta = Tt + (16 * ut + r) * LDM + 32 * ss + 8 * g;
+                    const float* aa = Am + (16 * mt + r) * LDM + 32 * ss + 8 * g;
+                    f16x8 ao, bo;
+                    const int sb = 2 * ss + (g >> 1);   // 16-wide block of this lane's s
+                    if (32 * ss + 8 * g < C && sb >= ut && sb <= mt) {
+                        const f32x4 t0v = *reinterpret_cast<const f32x4*>(ta), t1v = *reinterpret_cast<const f32x4*>(ta + 4);
+                        const f32x4 a0v = *reinterpret_cast<const f32x4*>(aa), a1v = *reinterpret_cast<const f32x4*>(aa + 4);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int col = 32 * BK::NFULL + 4 * g + (i & 3);
-                tv[i] = (i < 4 && col <= row) ? (f16)Tm[row * LDM + col] : (f16)0.f;
-                av[i] = (i < 4 && col <= row) ? (f16)Am[row * LDM + col] : (f16)0.f;
+                        for (int e = 0; e < 4; ++e) {
+                            ao[e] = (f16)t0v[e];
+                            ao[4 + e] = (f16)t1v[e];
+                            bo[e] = (f16)a0v[e];
+                            bo[4 + e] = (f16)a1v[e];
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) ao[e] = bo[e] = (f16)0.f;
+                    }
+                    acc = mma_f16_k32(ao, bo, acc);
+                    const float accs = acc[0];
+                    keep_alive(ao);
+                    keep_alive(bo);
+                    keep_alive(accs);
+                }
             }
+            // column beta_u of T diag(beta): rows u = 16 ut + 4 g + i of this E^T tile
+            const f32x4 bu = (ut < NB) ? *reinterpret_cast<const f32x4*>(&sc[1][16 * ut + 4 * g])
+                                       : f32x4{0.f, 0.f, 0.f, 0.f};
+            et[hh] = acc * bu;
         }
-        *reinterpret_cast<f16x8*>(Tsw + blk * 512 + lane * 8) = tv;
-        *reinterpret_cast<f16x8*>(Asw + blk * 512 + lane * 8) = av;
+        f16x8 fr;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            fr[e] = (f16)et[0][e];
+            fr[4 + e] = (f16)et[1][e];
+        }
+        Efr[blk * 64 + lane] = __builtin_bit_cast(uint4, fr);
     }
+
+    // Z = diag(beta) T^T diag(e^{g_C-g}/|k|) K: A operand rows t, k = s (slots 16 (i/4) + 4g
+    // + i%4 of each 32-wide step) as a bf16 high/low pair; B operand = raw K rows read
+    // transposed, column r of tile m being state index dperm(m, r).  Output tiles (2ks, m)
+    // and (2ks + 1, m) form the state-update fragment (m, ks).
+    for (int job = w; job < ND * NKT; job += NB) {
+        const int m = job / NKT, ks = job - m * NKT;
+        f32x4 zt[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int mt = 2 * ks + hh;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (mt < NB) {
+                for (int ss = mt / 2; ss < NKT; ++ss) {
+                    // A: Tt[t][s] * wk[s], s = 32 ss + 16 (i/4) + 4 g + i%4
+                    const float* ta = Tt + (16 * mt + r) * LDM + 32 * ss + 4 * g;
+                    bf16x8 ahi, alo;
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const int s0 = 32 * ss + 16 * hf + 4 * g;
+                        f32x4 tv = {0.f, 0.f, 0.f, 0.f}, wv = {0.f, 0.f, 0.f, 0.f};
+                        if (s0 < C && 2 * ss + hf >= mt) {   // T[s][t] = 0 for s < t
+                            tv = *reinterpret_cast<const f32x4*>(ta + 16 * hf);
+                            wv = *reinterpret_cast<const f32x4*>(&sc[4][s0]);
+                        }
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float v = tv[e] * wv[e];
+                            const bf16 hi = (bf16)v;
+                            ahi[4 * hf + e] = hi;
+                            alo[4 * hf + e] = (bf16)(v - (float)hi);
+                        }
+                    }
+                    // B: K[s][16 m + r] with the same slot -> s map, via transposing LDS reads
+                    const int t0 = 32 * ss + 4 * g + (r >> 2);
+                    const int d0 = dperm<ND>(m, 4 * (r & 3));   // 4 consecutive d per lane quad
+                    s16x4 lo = {0, 0, 0, 0}, hi4 = {0, 0, 0, 0};
+                    if (32 * ss < C)
+                        lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(Ks + t0 * LDR + d0));
+                    if (32 * ss + 16 < C)
+                        hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) s16x4*)(Ks + (t0 + 16) * LDR + d0));
+                    const bf16x8 bk = cat(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi4));
+                    acc = mma_bf16_k32(ahi, bk, acc);
+                    acc = mma_bf16_k32(alo, bk, acc);
+                    const float accs = acc[0];
+                    keep_alive(ahi);
+                    keep_alive(alo);
+                    keep_alive(bk);
+                    keep_alive(accs);
+                }
+            }
+            const f32x4 bt4 = (mt < NB) ? *reinterpret_cast<const f32x4*>(&sc[1][16 * mt + 4 * g])
+                                        : f32x4{0.f, 0.f, 0.f, 0.f};
+            zt[hh] = acc * bt4;
+        }
+        f16x8 fr;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            fr[e] = (f16)zt[0][e];
+            fr[4 + e] = (f16)zt[1][e];
+        }
+        Zfr[job * 64 + lane] = __builtin_bit_cast(uint4, fr);
+    }
+
+    // scalars: c1 in token order; c2 with token 16 mt + r at r * NB + mt (one vector load
+    // per lane of the scan's output wavefront); gamma_C
     if (tid < C) {
-        const float gt = sc[0][tid], gC = sc[0][C - 1];
-        const float gam = __expf(gt), bt = sc[1][tid], rk = sc[2][tid];
-        scw[0 * C + tid] = bt;                          // beta
-        scw[1 * C + tid] = bt * gam * rk;               // scales K S^T inside R
-        scw[2 * C + tid] = p.scale * gam * sc[3][tid];  // scales Q S^T inside O
-        scw[3 * C + tid] = __expf(gC - gt) * rk;        // decay to the end of the step, over |k|
-        scw[4 * C + tid] = rk;                          // 1/|k|
-        if (tid == 0) scw[5 * C] = __expf(gC);          // decay over the whole step
+        const float gam = __expf(sc[0][tid]);
+        scw[tid] = gam * sc[2][tid];
+        scw[C + (tid & 15) * NB + (tid >> 4)] = p.scale * gam * sc[3][tid];
+        if (tid == 0) scw[2 * C] = __expf(sc[0][C - 1]);
     }
 }
 
 // ---------------------------------------------------------------------------
 // Chunk scan: one workgroup of two wavefronts per (direction, b, h, 16 state
-// rows), serial over the sub-chunks.
-//   wave 0 (chain):  X = K S^T, R, U = T R, publishes (S as bf16, U as fp16)
-//                    to LDS, then S <- e^{g_C} S + K^T W with
-//                    W = diag(e^{g_C-g}/|k|) U carried as a bf16 high/low pair.
-//                    The state slice lives in its MFMA accumulators.
-//   wave 1 (output): O = diag(scale e^g/|q|) Q S^T + A U from the published
-//                    fragments, stored as bf16.
-// One LDS barrier per sub-chunk; LDS slots are double-buffered, so wave 1
-// works on step n while wave 0 runs the state update of step n and the first
-// half of step n+1.  Each wavefront reloads an operand for step n+1 right
-// after its last use in step n, so the loads overlap the rest of the step.
+// rows), serial over the processing steps.
+//   wave 0 (chain):  X = K S^T, R = V - diag(c1) X; publishes the step's state
+//                    (bf16) and R (fp16) to an LDS ring, then
+//                    S^T <- gamma_C S^T + Z^T R.  The state slice lives in its
+//                    MFMA accumulators for the whole call.
+//   wave 1 (output): O^T = S Q^T diag(c2) + R^T E^T from the published
+//                    fragments (the transposed products put 4 consecutive
+//                    state rows of one token in each lane), stored as bf16.
+// The wavefronts are coupled only through the ring (GDN_RING slots, LDS
+// counters with bounded spins), so the output wavefront may trail the chain by
+// up to GDN_RING - 1 steps.  Per-step operands are prefetched two steps ahead
+// with few, wide loads (the hardware tracks at most 63 outstanding vector
+// memory instructions per wavefront); an operand register of an MFMA is
+// refilled only after a result depending on that MFMA has been consumed.
 //
 // Row addressing: the buffer resource of a step starts at the lowest token of
 // the step and ends after the last real token, so a row's byte offset is a
@@ -502,23 +648,28 @@ __global__ __launch_bounds__(64 * NB) void gdn_prep_kernel(Params p) {
 // are not stored).
 // ---------------------------------------------------------------------------
 template <int NB, int ND>
-struct KRows {                                   // K or Q rows (bf16) as MFMA A operands
-    uint2 op[NB][ND / 2 > 0 ? ND / 2 : 1][2];    // [mt][ks][low/high 4 elements]
-    uint2 h[NB];                                 // trailing 16-wide d-step (odd ND)
+struct KRows {                   // K or Q rows of one step (lane = row) as MFMA operands
+    uint4 op[NB][(ND + 1) / 2];  // [mt][ks]: 8 consecutive d; a trailing single tile holds 4 and zeros
 };
 
 template <int NB, int ND>
-struct ChainIn {
-    uint4 tfr[Blocks<NB>::TOTAL];
-    uint32_t vv[NB][4];                          // V[t][row]: bf16 bits
-    f32x4 bet[NB], c1[NB], w[NB];
+struct ChainIn {                 // chain operands of one step
+    KRows<NB, ND> k;
+    uint4 v[2];                  // V row of one token, columns row0 .. row0 + 15 (bf16)
+    f32x4 c1[NB];
+};
+
+template <int NB, int ND>
+struct ZIn {                     // state-update operands of one step
+    uint4 zfr[ND][Blocks<NB>::NFULL + (Blocks<NB>::HALF ? 1 : 0)];
     float gC;
 };
 
 template <int NB, int ND>
-struct OutIn {
-    uint4 afr[Blocks<NB>::TOTAL];
-    f32x4 c2[NB];
+struct OutIn {                   // output operands of one step
+    KRows<NB, ND> q;
+    uint4 efr[Blocks<NB>::TOTAL];
+    float c2[NB];
 };
 
 // Buffer resource over the rows of processing step n: base at the step's lowest
@@ -536,26 +687,59 @@ struct StepRows {
     __device__ __forceinline__ int row(int t) const { return (dir ? (C - 1 - t) : t) * (int)tstride; }
 };
 
+// Rows 16 mt + r of a step as operands: k-step ks < ND/2 takes d = 32 ks + 8 g .. +7
+// (one 16-byte load at byte 64 ks + 16 g), a trailing single tile d = 16 (ND-1) + 4 g .. +3.
+template <int NB, int ND>
+__device__ __forceinline__ void load_rows(KRows<NB, ND>& kk, __amdgpu_buffer_rsrc_t rs, const int (&row)[NB], int g) {
+#pragma unroll
+    for (int mt = 0; mt < NB; ++mt) {
+#pragma unroll
+        for (int ks = 0; ks < ND / 2; ++ks)
+            kk.op[mt][ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, row[mt] + 16 * g, 64 * ks, 0));
+        if constexpr (ND % 2) {
+            const uint2 t = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, row[mt] + 8 * g, 32 * (ND - 1), 0));
+            kk.op[mt][ND / 2] = uint4{t.x, t.y, 0u, 0u};
+        }
+    }
+}
+
+#define GDN_RING 4
+#define GDN_SPIN_LIMIT (1 << 22)
+
+// Wait until an LDS counter written by the other wavefront reaches `target`.
+// Bounded, so a wavefront can never hang here.
+__device__ __forceinline__ void wait_counter(int* cnt, int target) {
+    for (int it = 0; it < GDN_SPIN_LIMIT; ++it) {
+        if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+// Make this wavefront's LDS writes (or completed LDS reads) visible, then set the counter.
+__device__ __forceinline__ void signal_counter(int* cnt, int value) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __hip_atomic_store(cnt, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
 template <int NB, int ND>
 __global__ __launch_bounds__(128) void gdn_scan_kernel(Params p, int ngroups) {
     constexpr int C = 16 * NB, D = 16 * ND;
-    constexpr int NFK = ND / 2;            // 32-wide steps over d
-    constexpr bool HK = (ND % 2) != 0;     // trailing 16-wide step over d
-    constexpr int NKD = NFK + (HK ? 1 : 0);
+    constexpr int NKD = (ND + 1) / 2;      // k-steps over d (the last one half-filled for odd ND)
     using BK = Blocks<NB>;
     constexpr int NFT = BK::NFULL;         // 32-wide steps over tokens
     constexpr bool HT = BK::HALF;
     constexpr int NKT = NFT + (HT ? 1 : 0);
-    constexpr int LDK = D + 32;            // bf16 row stride of the staged K rows (8-byte aligned rows)
+    constexpr int SCAL_OFF = 1024 * (BK::TOTAL + ND * NKT);   // scalars of an item
     typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-    __shared__ __align__(16) bf16 Kh[C * LDK];
-    __shared__ __align__(16) uint4 pubP[2][NKD][64];
-    __shared__ __align__(16) uint4 pubU[2][NKT][64];
+    __shared__ __align__(16) uint4 ringP[GDN_RING][NKD][64];
+    __shared__ __align__(16) uint4 ringR[GDN_RING][NKT][64];
+    __shared__ __align__(16) bf16 Vs[64 * 16];   // V rows of the chain's current step
+    __shared__ int ready, done;
 
     const int lane = threadIdx.x & 63;
     // the role of a wavefront is wave-uniform: keep it in a scalar register so both
-    // roles are whole-wavefront branches (each role runs its own barrier sequence)
+    // roles are whole-wavefront branches
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, g = lane >> 4;
     // Workgroups are spread over the 8 XCDs round-robin (id % 8); keep the ND
@@ -573,6 +757,12 @@ __global__ __launch_bounds__(128) void gdn_scan_kernel(Params p, int ngroups) {
     const char* item0 = p.ws + (((int64_t)dir * p.B + b) * p.H + h) * p.nsub_max * p.ws_item_bytes;
     const int64_t ib = p.ws_item_bytes;
 
+    if (threadIdx.x == 0) {
+        ready = 0;
+        done = 0;
+    }
+    __syncthreads();
+
     if (wave == 0) {
         // ------------------------------ chain wavefront ------------------------------
         const StepRows kr{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.k) + (int64_t)b * p.ks[0] +
@@ -581,239 +771,138 @@ __global__ __launch_bounds__(128) void gdn_scan_kernel(Params p, int ngroups) {
         const StepRows vr{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.v) + (int64_t)b * p.vs[0] +
                                                         (int64_t)h * p.vs[2]),
                           p.vs[1] * 2, T, C, N, dir, 2 * D};
-        int koff[NB], voff[NB][4];
+        int krow[NB];
 #pragma unroll
-        for (int mt = 0; mt < NB; ++mt) {
-            koff[mt] = kr.row(16 * mt + r) + 8 * g;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) voff[mt][i] = vr.row(16 * mt + 4 * g + i) + 2 * (row0 + r);
-        }
+        for (int mt = 0; mt < NB; ++mt) krow[mt] = kr.row(16 * mt + r);
+        // each lane stages the V row of token `lane` (rows >= C duplicate real ones, unused)
+        const int voff = vr.row(lane & (C - 1)) + 2 * row0;
 
-        ChainIn<NB, ND> in;
-        KRows<NB, ND> kA, kB;
-        auto load_k = [&](KRows<NB, ND>& kk, int n) {
-            const auto rs = kr.rsrc(n);
-#pragma unroll
-            for (int mt = 0; mt < NB; ++mt) {
-#pragma unroll
-                for (int ks = 0; ks < NFK; ++ks) {
-                    kk.op[mt][ks][0] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, koff[mt], 64 * ks, 0));
-                    kk.op[mt][ks][1] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, koff[mt], 64 * ks + 32, 0));
-                }
-                if constexpr (HK)
-                    kk.h[mt] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, koff[mt], 64 * NFK, 0));
-            }
-        };
-        auto load_rest = [&](int n) {
-            const char* item = item0 + n * ib;
+        ChainIn<NB, ND> cA, cB;
+        ZIn<NB, ND> zi;
+        auto load_chain = [&](ChainIn<NB, ND>& c, int n) {
+            load_rows(c.k, kr.rsrc(n), krow, g);
             const auto rs = vr.rsrc(n);
+            c.v[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
+            c.v[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 16, 0));
+            const float* scg = reinterpret_cast<const float*>(item0 + n * ib + SCAL_OFF);
 #pragma unroll
-            for (int mt = 0; mt < NB; ++mt)
+            for (int mt = 0; mt < NB; ++mt) c.c1[mt] = *reinterpret_cast<const f32x4*>(scg + 16 * mt + 4 * g);
+        };
+        auto load_z = [&](int n) {
+            const char* item = item0 + n * ib;
+            const uint4* zsw = reinterpret_cast<const uint4*>(item) + BK::TOTAL * 64;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) in.vv[mt][i] = __builtin_amdgcn_raw_buffer_load_b16(rs, voff[mt][i], 0, 0);
-            const uint4* tsw = reinterpret_cast<const uint4*>(item);
+            for (int m = 0; m < ND; ++m)
 #pragma unroll
-            for (int blk = 0; blk < BK::TOTAL; ++blk) in.tfr[blk] = tsw[blk * 64 + lane];
-            const float* scg = reinterpret_cast<const float*>(item + 2 * 1024 * BK::TOTAL);
-#pragma unroll
-            for (int mt = 0; mt < NB; ++mt) {
-                in.bet[mt] = *reinterpret_cast<const f32x4*>(scg + 0 * C + 16 * mt + 4 * g);
-                in.c1[mt] = *reinterpret_cast<const f32x4*>(scg + 1 * C + 16 * mt + 4 * g);
-                in.w[mt] = *reinterpret_cast<const f32x4*>(scg + 3 * C + 16 * mt + 4 * g);
-            }
-            in.gC = scg[5 * C];
+                for (int ks = 0; ks < NKT; ++ks) zi.zfr[m][ks] = zsw[(m * NKT + ks) * 64 + lane];
+            zi.gC = reinterpret_cast<const float*>(item + SCAL_OFF)[2 * C];
         };
 
-        // state slice, transposed: P[m][i] = S[row0 + r][16 m + 4 g + i]
+        // state slice, transposed: P[m][i] = S[row0 + r][dperm(m, 4 g + i)]
         f32x4 P[ND];
         const float* Sin = (dir == 0) ? p.S_in : nullptr;
         const int64_t sbase = ((int64_t)b * p.H + h) * D * D + (int64_t)(row0 + r) * D;
 #pragma unroll
         for (int m = 0; m < ND; ++m) {
-            if (Sin) P[m] = *reinterpret_cast<const f32x4*>(Sin + sbase + 16 * m + 4 * g);
+            if (Sin) P[m] = *reinterpret_cast<const f32x4*>(Sin + sbase + dperm<ND>(m, 4 * g));
             else P[m] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 
-        load_k(kA, 0);
-        if (N > 1) load_k(kB, 1);
-        load_rest(0);
-        auto chain_step = [&](KRows<NB, ND>& kc, int n) {
-            const int sl = n & 1;
-            // state as bf16 B operand: slot i of group g <-> d = 32 ks + 16 (i/4) + 4 g + i%4
+        load_chain(cA, 0);
+        load_chain(cB, N > 1 ? 1 : 0);
+        load_z(0);
+        auto chain_step = [&](ChainIn<NB, ND>& c, int n) {
+            const int sl = n % GDN_RING;
+            // state as bf16 operand: k-slot e of lane group g <-> d = dperm(2 ks + e/4, 4 g + e%4)
             bf16x8 Pb[NKD];
 #pragma unroll
-            for (int ks = 0; ks < NFK; ++ks)
+            for (int ks = 0; ks < ND / 2; ++ks)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     Pb[ks][i] = (bf16)P[2 * ks][i];
                     Pb[ks][4 + i] = (bf16)P[2 * ks + 1][i];
                 }
-            if constexpr (HK) {
+            if constexpr (ND % 2) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    Pb[NFK][i] = (bf16)P[ND - 1][i];
-                    Pb[NFK][4 + i] = (bf16)0.f;
+                    Pb[NKD - 1][i] = (bf16)P[ND - 1][i];
+                    Pb[NKD - 1][4 + i] = (bf16)0.f;
                 }
             }
-            // X = K S^T (rows: tokens), independent accumulators interleaved; the raw bf16
-            // K rows also go to LDS for the state update
+            // X = K S^T (rows: tokens 16 mt + 4 g + i, column r)
             f32x4 X[NB];
 #pragma unroll
             for (int mt = 0; mt < NB; ++mt) X[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < NFK; ++ks)
+            for (int ks = 0; ks < NKD; ++ks)
 #pragma unroll
                 for (int mt = 0; mt < NB; ++mt)
-                    X[mt] = mma_bf16_k32(cat(u2_to_bf16x4(kc.op[mt][ks][0]), u2_to_bf16x4(kc.op[mt][ks][1])), Pb[ks], X[mt]);
-            if constexpr (HK) {
-                const bf16x4 pbh = {Pb[NFK][0], Pb[NFK][1], Pb[NFK][2], Pb[NFK][3]};
+                    X[mt] = mma_bf16_k32(__builtin_bit_cast(bf16x8, c.k.op[mt][ks]), Pb[ks], X[mt]);
+            // V in the same layout: stage the rows in LDS, read them back transposed
+            // (lane quad c of group g supplies row 16 mt + 4 g + i, columns 4c .. 4c+3)
+            *reinterpret_cast<uint4*>(Vs + 16 * lane) = c.v[0];
+            *reinterpret_cast<uint4*>(Vs + 16 * lane + 8) = c.v[1];
+            bf16x4 vt[NB];
 #pragma unroll
-                for (int mt = 0; mt < NB; ++mt) X[mt] = mma_bf16_k16(u2_to_bf16x4(kc.h[mt]), pbh, X[mt]);
-            }
-#pragma unroll
-            for (int mt = 0; mt < NB; ++mt) {
-                const int t = 16 * mt + r;
-#pragma unroll
-                for (int ks = 0; ks < NFK; ++ks) {
-                    *reinterpret_cast<uint2*>(Kh + t * LDK + 32 * ks + 4 * g) = kc.op[mt][ks][0];
-                    *reinterpret_cast<uint2*>(Kh + t * LDK + 32 * ks + 16 + 4 * g) = kc.op[mt][ks][1];
-                }
-                if constexpr (HK) *reinterpret_cast<uint2*>(Kh + t * LDK + 32 * NFK + 4 * g) = kc.h[mt];
-            }
-            // R = diag(beta) V - diag(beta e^g / |k|) X, as fp16 B operand (k = token)
+            for (int mt = 0; mt < NB; ++mt)
+                vt[mt] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                        (__attribute__((address_space(3))) s16x4*)(
+                                                            Vs + 16 * (16 * mt + 4 * g + (r >> 2)) + 4 * (r & 3))));
+            // R = V - diag(e^g / |k|) X, as fp16 B operand (k = token)
             f16x8 Rb[NKT];
 #pragma unroll
             for (int mt = 0; mt < NB; ++mt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float vv = __builtin_bit_cast(float, in.vv[mt][i] << 16);
-                    Rb[mt >> 1][4 * (mt & 1) + i] = (f16)(in.bet[mt][i] * vv - in.c1[mt][i] * X[mt][i]);
-                }
+                for (int i = 0; i < 4; ++i)
+                    Rb[mt >> 1][4 * (mt & 1) + i] = (f16)((float)vt[mt][i] - c.c1[mt][i] * X[mt][i]);
             if constexpr (HT) {
 #pragma unroll
                 for (int i = 4; i < 8; ++i) Rb[NFT][i] = (f16)0.f;
             }
-            // X has been consumed (R is formed here), so its operands are free: the K-row
-            // registers are refilled for step n + 2
+            // X is consumed: the operands of step n + 2 may now be loaded into c
 #pragma unroll
             for (int ks = 0; ks < NKT; ++ks) keep_alive(Rb[ks]);
 #pragma unroll
             for (int ks = 0; ks < NKD; ++ks) keep_alive(Pb[ks]);
-            __builtin_amdgcn_sched_barrier(0);   // no refill above the consumers of X
-            if (n + 2 < N) load_k(kc, n + 2);
-            // U = T R (k-step outer, row tiles inner: consecutive MFMAs are independent)
-            f32x4 U[NB];
+            __builtin_amdgcn_sched_barrier(0);
+            load_chain(c, n + 2 < N ? n + 2 : N - 1);
+            // publish the step's state and R once the output wavefront has released the slot
+            wait_counter(&done, n + 1 - GDN_RING);
 #pragma unroll
-            for (int mt = 0; mt < NB; ++mt) U[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int ks = 0; ks < NKD; ++ks) ringP[sl][ks][lane] = __builtin_bit_cast(uint4, Pb[ks]);
 #pragma unroll
-            for (int idx = 0; idx < NKT; ++idx)
+            for (int ks = 0; ks < NKT; ++ks) ringR[sl][ks][lane] = __builtin_bit_cast(uint4, Rb[ks]);
+            signal_counter(&ready, n + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            // S^T <- gamma_C S^T + Z^T R  (rows d, columns r); a trailing 16-token step has
+            // zero upper slots in both operands
 #pragma unroll
-                for (int mt = 0; mt < NB; ++mt) {
-                    if (idx >= BK::count(mt)) continue;
-                    const uint4 tf = in.tfr[BK::offset(mt) + idx];
-                    if (idx < BK::nfull_for(mt)) {
-                        U[mt] = mma_f16_k32(__builtin_bit_cast(f16x8, tf), Rb[idx], U[mt]);
-                    } else {
-                        const f16x4 rb = {Rb[NFT][0], Rb[NFT][1], Rb[NFT][2], Rb[NFT][3]};
-                        U[mt] = mma_f16_k16(u2_to_f16x4(uint2{tf.x, tf.y}), rb, U[mt]);
-                    }
-                }
-            // publish the state at the start of this step and U for the output wavefront;
-            // W = diag(e^{g_C-g}/|k|) U as a bf16 pair (high part + rounded remainder)
-            f16x8 Ub[NKT];
-            bf16x8 Wh[NKT], Wl[NKT];
-#pragma unroll
-            for (int mt = 0; mt < NB; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int si = 4 * (mt & 1) + i;
-                    Ub[mt >> 1][si] = (f16)U[mt][i];
-                    const float wv = in.w[mt][i] * U[mt][i];
-                    const bf16 hi = (bf16)wv;
-                    Wh[mt >> 1][si] = hi;
-                    Wl[mt >> 1][si] = (bf16)(wv - (float)hi);
-                }
-            if constexpr (HT) {
-#pragma unroll
-                for (int i = 4; i < 8; ++i) {
-                    Ub[NFT][i] = (f16)0.f;
-                    Wh[NFT][i] = (bf16)0.f;
-                    Wl[NFT][i] = (bf16)0.f;
-                }
-            }
-            const float gC = in.gC;
-            // U has been consumed (Ub, W are formed here): its operands are free
-#pragma unroll
-            for (int ks = 0; ks < NKT; ++ks) {
-                keep_alive(Ub[ks]);
-                keep_alive(Wh[ks]);
-                keep_alive(Wl[ks]);
-                keep_alive(Rb[ks]);
-            }
-            __builtin_amdgcn_sched_barrier(0);   // no refill above the consumers of U
-            if (n + 1 < N) load_rest(n + 1);
-#pragma unroll
-            for (int ks = 0; ks < NKD; ++ks) pubP[sl][ks][lane] = __builtin_bit_cast(uint4, Pb[ks]);
-#pragma unroll
-            for (int ks = 0; ks < NKT; ++ks) pubU[sl][ks][lane] = __builtin_bit_cast(uint4, Ub[ks]);
-            lds_barrier();
-            // S <- e^{g_C} S + K^T W, computed transposed (rows d, columns r): the A operand
-            // (rows d, k = token) comes from the K rows with transposing LDS reads, all issued
-            // before the MFMAs; the ND accumulators are interleaved.
-            bf16x8 KT[ND][NKT];
-#pragma unroll
-            for (int m = 0; m < ND; ++m)
-#pragma unroll
-                for (int ks = 0; ks < NKT; ++ks) {
-                    const int t0 = 32 * ks + 4 * g + (r >> 2);
-                    const int d0 = 16 * m + 4 * (r & 3);
-                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) s16x4*)(Kh + t0 * LDK + d0));
-                    s16x4 hi = {0, 0, 0, 0};
-                    if (ks < NFT)
-                        hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) s16x4*)(Kh + (t0 + 16) * LDK + d0));
-                    KT[m][ks] = cat(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi));
-                }
-#pragma unroll
-            for (int m = 0; m < ND; ++m) P[m] = P[m] * gC;
+            for (int m = 0; m < ND; ++m) P[m] = P[m] * zi.gC;
 #pragma unroll
             for (int ks = 0; ks < NKT; ++ks)
 #pragma unroll
-                for (int hl = 0; hl < 2; ++hl)
-#pragma unroll
-                    for (int m = 0; m < ND; ++m) {
-                        const bf16x8 wv = hl ? Wl[ks] : Wh[ks];
-                        if (ks < NFT) {
-                            P[m] = mma_bf16_k32(KT[m][ks], wv, P[m]);
-                        } else {
-                            const bf16x4 a = {KT[m][ks][0], KT[m][ks][1], KT[m][ks][2], KT[m][ks][3]};
-                            const bf16x4 w4 = {wv[0], wv[1], wv[2], wv[3]};
-                            P[m] = mma_bf16_k16(a, w4, P[m]);
-                        }
-                    }
-            // P is read here, so every state-update MFMA has finished before its operands go
+                for (int m = 0; m < ND; ++m) P[m] = mma_f16_k32(__builtin_bit_cast(f16x8, zi.zfr[m][ks]), Rb[ks], P[m]);
+            // every state-update MFMA has finished once P is read: its Z operands may go
 #pragma unroll
             for (int m = 0; m < ND; ++m) {
                 const float pm = P[m][0];
                 keep_alive(pm);
-#pragma unroll
-                for (int ks = 0; ks < NKT; ++ks) keep_alive(KT[m][ks]);
             }
-#pragma unroll
-            for (int ks = 0; ks < NKT; ++ks) {
-                keep_alive(Wh[ks]);
-                keep_alive(Wl[ks]);
-            }
+            __builtin_amdgcn_sched_barrier(0);
+            load_z(n + 1 < N ? n + 1 : N - 1);
         };
-        for (int n = 0; n < N; n += 2) {
-            chain_step(kA, n);
-            if (n + 1 < N) chain_step(kB, n + 1);
+        // The prefetches are unconditional (the last steps reload step N-1) so that
+        // every path through the loop has the same loads in flight.
+        int n = 0;
+        for (; n + 1 < N; n += 2) {
+            chain_step(cA, n);
+            chain_step(cB, n + 1);
         }
+        if (n < N) chain_step(cA, n);
         float* Sout = p.S_out[dir];
         if (Sout) {
 #pragma unroll
-            for (int m = 0; m < ND; ++m) *reinterpret_cast<f32x4*>(Sout + sbase + 16 * m + 4 * g) = P[m];
+            for (int m = 0; m < ND; ++m) *reinterpret_cast<f32x4*>(Sout + sbase + dperm<ND>(m, 4 * g)) = P[m];
         }
     } else {
         // ------------------------------ output wavefront ------------------------------
@@ -823,115 +912,84 @@ __global__ __launch_bounds__(128) void gdn_scan_kernel(Params p, int ngroups) {
         const StepRows orow{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.o[dir]) + (int64_t)b * p.os[0] +
                                                           (int64_t)h * p.os[2]),
                             p.os[1] * 2, T, C, N, dir, 2 * D};
-        int qoff[NB], ooff[NB][4];
+        int qrow[NB], ooff[NB];
 #pragma unroll
         for (int mt = 0; mt < NB; ++mt) {
-            qoff[mt] = qr.row(16 * mt + r) + 8 * g;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ooff[mt][i] = orow.row(16 * mt + 4 * g + i) + 2 * (row0 + r);
+            qrow[mt] = qr.row(16 * mt + r);
+            ooff[mt] = orow.row(16 * mt + r) + 2 * (row0 + 4 * g);   // token 16 mt + r, state rows row0 + 4g ..
         }
 
-        OutIn<NB, ND> in;
-        KRows<NB, ND> qA, qB;
-        auto load_q = [&](KRows<NB, ND>& qq, int n) {
-            const auto rs = qr.rsrc(n);
-#pragma unroll
-            for (int mt = 0; mt < NB; ++mt) {
-#pragma unroll
-                for (int ks = 0; ks < NFK; ++ks) {
-                    qq.op[mt][ks][0] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, qoff[mt], 64 * ks, 0));
-                    qq.op[mt][ks][1] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, qoff[mt], 64 * ks + 32, 0));
-                }
-                if constexpr (HK)
-                    qq.h[mt] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, qoff[mt], 64 * NFK, 0));
-            }
-        };
-        auto load_rest = [&](int n) {
+        OutIn<NB, ND> oA, oB;
+        auto load_out = [&](OutIn<NB, ND>& o, int n) {
+            load_rows(o.q, qr.rsrc(n), qrow, g);
             const char* item = item0 + n * ib;
-            const uint4* asw = reinterpret_cast<const uint4*>(item) + BK::TOTAL * 64;
+            const uint4* esw = reinterpret_cast<const uint4*>(item);
 #pragma unroll
-            for (int blk = 0; blk < BK::TOTAL; ++blk) in.afr[blk] = asw[blk * 64 + lane];
-            const float* scg = reinterpret_cast<const float*>(item + 2 * 1024 * BK::TOTAL);
+            for (int blk = 0; blk < BK::TOTAL; ++blk) o.efr[blk] = esw[blk * 64 + lane];
+            const float* scg = reinterpret_cast<const float*>(item + SCAL_OFF) + C + NB * r;
 #pragma unroll
-            for (int mt = 0; mt < NB; ++mt) in.c2[mt] = *reinterpret_cast<const f32x4*>(scg + 2 * C + 16 * mt + 4 * g);
+            for (int mt = 0; mt < NB; ++mt) o.c2[mt] = scg[mt];
         };
 
-        load_q(qA, 0);
-        if (N > 1) load_q(qB, 1);
-        load_rest(0);
-        auto out_step = [&](KRows<NB, ND>& qc, int n) {
-            const int sl = n & 1;
-            const auto ors = orow.rsrc(n);
-            lds_barrier();
+        load_out(oA, 0);
+        load_out(oB, N > 1 ? 1 : 0);
+        auto out_step = [&](OutIn<NB, ND>& o, int n) {
+            const int sl = n % GDN_RING;
+            wait_counter(&ready, n + 1);
             bf16x8 Pb[NKD];
-            f16x8 Ub[NKT];
+            f16x8 Rb[NKT];
 #pragma unroll
-            for (int ks = 0; ks < NKD; ++ks) Pb[ks] = __builtin_bit_cast(bf16x8, pubP[sl][ks][lane]);
+            for (int ks = 0; ks < NKD; ++ks) Pb[ks] = __builtin_bit_cast(bf16x8, ringP[sl][ks][lane]);
 #pragma unroll
-            for (int ks = 0; ks < NKT; ++ks) Ub[ks] = __builtin_bit_cast(f16x8, pubU[sl][ks][lane]);
-            f32x4 Y[NB];
-#pragma unroll
-            for (int mt = 0; mt < NB; ++mt) Y[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < NFK; ++ks)
-#pragma unroll
-                for (int mt = 0; mt < NB; ++mt)
-                    Y[mt] = mma_bf16_k32(cat(u2_to_bf16x4(qc.op[mt][ks][0]), u2_to_bf16x4(qc.op[mt][ks][1])), Pb[ks], Y[mt]);
-            if constexpr (HK) {
-                const bf16x4 pbh = {Pb[NFK][0], Pb[NFK][1], Pb[NFK][2], Pb[NFK][3]};
-#pragma unroll
-                for (int mt = 0; mt < NB; ++mt) Y[mt] = mma_bf16_k16(u2_to_bf16x4(qc.h[mt]), pbh, Y[mt]);
-            }
-            f32x4 O[NB];
-#pragma unroll
-            for (int mt = 0; mt < NB; ++mt) O[mt] = in.c2[mt] * Y[mt];
-            // Y has been consumed (O is started here): the state fragments may go and the Q
-            // registers may be refilled
-#pragma unroll
-            for (int mt = 0; mt < NB; ++mt) keep_alive(O[mt]);
+            for (int ks = 0; ks < NKT; ++ks) Rb[ks] = __builtin_bit_cast(f16x8, ringR[sl][ks][lane]);
+            // the slot is free once its fragments are in registers
 #pragma unroll
             for (int ks = 0; ks < NKD; ++ks) keep_alive(Pb[ks]);
-            __builtin_amdgcn_sched_barrier(0);   // no refill above the consumers of Y
-            if (n + 2 < N) load_q(qc, n + 2);
+#pragma unroll
+            for (int ks = 0; ks < NKT; ++ks) keep_alive(Rb[ks]);
+            signal_counter(&done, n + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            // Y^T = S Q^T: rows = state rows 4 g + i, column = token 16 mt + r
+            f32x4 O[NB];
+#pragma unroll
+            for (int mt = 0; mt < NB; ++mt) O[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKD; ++ks)
+#pragma unroll
+                for (int mt = 0; mt < NB; ++mt)
+                    O[mt] = mma_bf16_k32(Pb[ks], __builtin_bit_cast(bf16x8, o.q.op[mt][ks]), O[mt]);
+#pragma unroll
+            for (int mt = 0; mt < NB; ++mt) O[mt] = O[mt] * o.c2[mt];
+            // + R^T E^T (a trailing 16-token step has zero upper slots in both operands)
 #pragma unroll
             for (int idx = 0; idx < NKT; ++idx)
 #pragma unroll
                 for (int mt = 0; mt < NB; ++mt) {
                     if (idx >= BK::count(mt)) continue;
-                    const uint4 af = in.afr[BK::offset(mt) + idx];
-                    if (idx < BK::nfull_for(mt)) {
-                        O[mt] = mma_f16_k32(__builtin_bit_cast(f16x8, af), Ub[idx], O[mt]);
-                    } else {
-                        const f16x4 ub = {Ub[NFT][0], Ub[NFT][1], Ub[NFT][2], Ub[NFT][3]};
-                        O[mt] = mma_f16_k16(u2_to_f16x4(uint2{af.x, af.y}), ub, O[mt]);
-                    }
+                    O[mt] = mma_f16_k32(Rb[idx], __builtin_bit_cast(f16x8, o.efr[BK::offset(mt) + idx]), O[mt]);
                 }
-            bf16 ov[NB][4];
+            uint2 ov[NB];
+#pragma unroll
+            for (int mt = 0; mt < NB; ++mt) {
+                const bf16x4 b4 = {(bf16)O[mt][0], (bf16)O[mt][1], (bf16)O[mt][2], (bf16)O[mt][3]};
+                ov[mt] = __builtin_bit_cast(uint2, b4);
+            }
+            // O is consumed: the operands of step n + 2 may now be loaded into o
+#pragma unroll
+            for (int mt = 0; mt < NB; ++mt) keep_alive(ov[mt]);
+            __builtin_amdgcn_sched_barrier(0);
+            load_out(o, n + 2 < N ? n + 2 : N - 1);
+            const auto ors = orow.rsrc(n);
 #pragma unroll
             for (int mt = 0; mt < NB; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ov[mt][i] = (bf16)O[mt][i];
-            // O has been consumed (converted here): the U fragments may go and the A fragments
-            // may be refilled
-#pragma unroll
-            for (int mt = 0; mt < NB; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) keep_alive(ov[mt][i]);
-#pragma unroll
-            for (int ks = 0; ks < NKT; ++ks) keep_alive(Ub[ks]);
-            __builtin_amdgcn_sched_barrier(0);   // no refill above the consumers of O
-            if (n + 1 < N) load_rest(n + 1);
-#pragma unroll
-            for (int mt = 0; mt < NB; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, ov[mt][i]), ors,
-                                                          ooff[mt][i], 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ov[mt]), ors, ooff[mt], 0, 0);
         };
-        for (int n = 0; n < N; n += 2) {
-            out_step(qA, n);
-            if (n + 1 < N) out_step(qB, n + 1);
+        int n = 0;
+        for (; n + 1 < N; n += 2) {
+            out_step(oA, n);
+            out_step(oB, n + 1);
         }
+        if (n < N) out_step(oA, n);
     }
 }
 
