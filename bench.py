@@ -9,9 +9,12 @@ rotate over enough buffer sets that the live set exceeds the 256 MB MALL, so
 every step streams from HBM.
 
 Prints one JSON line.  `value` is tokens per second per layer (T / step time).
-`roofline` is for the dominant kernel (the chunk scan): algorithmic bytes per
-launch (904 B per token-head per scan + the state read and write) over its
-average duration from HIP events recorded on its launch stream.
+`roofline` is for the dominant kernel (the chunk scan): the algorithmic bytes of
+the call it serves over its average duration from HIP events recorded on its
+launch stream.  Algorithmic bytes per token-head: q, k, v read once and o
+written (224 B each in bf16) plus the two fp32 gates; a bidirectional call also
+writes o_rev; the forward scan reads and writes the 112x112 fp32 state of each
+head once.
 `cpu_baseline` times the fp64 CPU oracle on the host cores over the same
 workload (the oracle is a test reference, not a tuned CPU implementation).
 """
@@ -31,7 +34,8 @@ METRIC = "GDN tokens/s per layer at 2640-token 720p chunk; % of MFMA/HBM rooflin
 B, H, D, T = 1, 20, 112, 2640
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16
-BYTES_PER_TOKEN_HEAD = 4 * D * 2 + 2 * 4     # q, k, v, o in bf16 + a, beta in fp32
+BYTES_PER_TOKEN_HEAD = 4 * D * 2 + 2 * 4     # one scan: q, k, v, o in bf16 + a, beta in fp32
+BIDIR_BYTES_PER_TOKEN_HEAD = 5 * D * 2 + 2 * 4   # both scans in one call: q, k, v once, o and o_rev
 STATE_BYTES = B * H * D * D * 4
 FLOPS_PER_TOKEN_HEAD = 6 * D * D             # S k, rank-1 update, S q
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_scan_720p.json")
@@ -44,9 +48,11 @@ def kernel_source_hash() -> str:
 
 
 def algorithmic_bytes(mode: str) -> int:
+    """Bytes a whole step (forward with carried state + reverse) must move at least."""
+    if mode == "bidir":
+        return B * T * H * BIDIR_BYTES_PER_TOKEN_HEAD + 2 * STATE_BYTES
     per_scan = B * T * H * BYTES_PER_TOKEN_HEAD
-    fwd = per_scan + 2 * STATE_BYTES
-    return fwd + per_scan if mode in ("bidir", "separate") else fwd
+    return 2 * per_scan + 2 * STATE_BYTES
 
 
 def load_traffic():
@@ -66,7 +72,7 @@ def cpu_baseline(d, threads):
     import oracle
     oracle.build(force=False)
     reps, t0 = 0, time.perf_counter()
-    while reps < 20 and (reps < 2 or time.perf_counter() - t0 < 10.0):
+    while reps < 500 and (reps < 2 or time.perf_counter() - t0 < 12.0):
         oracle.forward(d["q"], d["k"], d["v"], d["a"], d["beta"], d["S0"], threads=threads)
         oracle.reverse(d["q"], d["k"], d["v"], d["a"], d["beta"], threads=threads)
         reps += 1
@@ -146,6 +152,25 @@ def main():
     print(f"# timed {args.steps} steps: wall {wall * 1e3:.3f} ms, events {ms_events:.3f} ms", file=sys.stderr,
           flush=True)
 
+    # per-call distribution: events around every step (a separate pass, so the timed
+    # region above carries no per-step events)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    per_call = np.array([a.elapsed_time(b) for a, b in evs])
+    p10, p50, p90 = (float(x) for x in np.percentile(per_call, [10, 50, 90]))
+
+    # warm: the same buffer set every step
+    torch.cuda.synchronize()
+    w1 = time.perf_counter()
+    for i in range(args.steps):
+        step(0)
+    torch.cuda.synchronize()
+    warm_ms = (time.perf_counter() - w1) * 1e3 / args.steps
+
     # second pass over the same steps with per-kernel HIP events on the launch stream
     gb.gdn_profile(s.handle, True)
     gb.gdn_profile_read(s.handle, reset=True)
@@ -213,6 +238,9 @@ def main():
             "prep_avg_us": round(prep_avg_ms * 1e3, 3),
             "scan_avg_us": round(scan_avg_ms * 1e3, 3),
             "event_ms_per_step": round(ms_events / args.steps, 5),
+            "per_call_ms_p10_p50_p90": [round(p10, 5), round(p50, 5), round(p90, 5)],
+            "warm_ms_per_step": round(warm_ms, 5),
+            "target_tokens_per_s": 108e6,
         },
     }
     if not args.no_cpu:
