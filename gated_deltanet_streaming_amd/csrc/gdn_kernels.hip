@@ -626,50 +626,48 @@ __global__ __launch_bounds__(64 * NB) void gdn_prep_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------------------
-// Chunk scan: one workgroup of two wavefronts per (direction, b, h, 16 state
-// rows), serial over the processing steps.
-//   wave 0 (chain):  X = K S^T, R = V - diag(c1) X; publishes the step's state
-//                    (bf16) and R (fp16) to an LDS ring, then
-//                    S^T <- gamma_C S^T + Z^T R.  The state slice lives in its
-//                    MFMA accumulators for the whole call.
-//   wave 1 (output): O^T = S Q^T diag(c2) + R^T E^T from the published
-//                    fragments (the transposed products put 4 consecutive
-//                    state rows of one token in each lane), stored as bf16.
+// Chunk scan: one workgroup per (direction, b, h, slice of 32 state rows),
+// serial over the processing steps.  Rows of S evolve independently, so the
+// slices of a head need no exchange.  Each MFMA operand fragment loaded for a
+// step (K, Z, Q, E) feeds the two 16-row column tiles of the slice.
+//   wave 0 (chain):   X = K S^T, R = V - diag(c1) X; publishes the step's state
+//                     (bf16) and R (fp16) to an LDS ring, then
+//                     S^T <- gamma_C S^T + Z^T R.  The state slice lives in its
+//                     MFMA accumulators for the whole call.
+//   waves 1.. (output, one per half of the step's token tiles):
+//                     O^T = S Q^T diag(c2) + R^T E^T from the published
+//                     fragments (each lane stores 4 consecutive state rows of
+//                     one token).
 // The wavefronts are coupled only through the ring (GDN_RING slots, LDS
-// counters with bounded spins), so the output wavefront may trail the chain by
-// up to GDN_RING - 1 steps.  Per-step operands are prefetched two steps ahead
-// with few, wide loads (the hardware tracks at most 63 outstanding vector
-// memory instructions per wavefront); an operand register of an MFMA is
-// refilled only after a result depending on that MFMA has been consumed.
+// counters with bounded spins), so the output wavefronts may trail the chain
+// by up to GDN_RING - 1 steps.  Operands are prefetched with 16-byte loads as
+// soon as their registers are free (K two steps ahead, V and the scales one
+// step ahead, Z at the start of its step); the register file and the 63
+// vector memory instructions the hardware tracks per wavefront bound the
+// buffering.  An
+// operand register of an MFMA is refilled only after a result depending on
+// that MFMA has been consumed.
 //
 // Row addressing: the buffer resource of a step starts at the lowest token of
 // the step and ends after the last real token, so a row's byte offset is a
 // per-lane constant and rows past the end of the sequence read as zero (and
-// are not stored).
+// are not stored).  State rows past d_v (the last slice when d_v is not a
+// multiple of 32) are computed from zero inputs and never stored.
 // ---------------------------------------------------------------------------
-template <int NB, int ND>
-struct KRows {                   // K or Q rows of one step (lane = row) as MFMA operands
-    uint4 op[NB][(ND + 1) / 2];  // [mt][ks]: 8 consecutive d; a trailing single tile holds 4 and zeros
+#define GDN_COLS 2       // 16-row column tiles of the state per workgroup
+#define GDN_RING 4
+#define GDN_SPIN_LIMIT (1 << 22)
+
+template <int NT, int ND>
+struct Rows {                    // NT row tiles of K or Q (lane = row) as MFMA operands
+    uint4 op[NT][(ND + 1) / 2];  // [tile][ks]: 8 consecutive d; a trailing single tile holds 4 and zeros
 };
 
-template <int NB, int ND>
-struct ChainIn {                 // chain operands of one step
-    KRows<NB, ND> k;
-    uint4 v[2];                  // V row of one token, columns row0 .. row0 + 15 (bf16)
+template <int NB>
+struct VIn {                     // chain operands of one step used right after X
+    uint4 v[GDN_COLS][2];        // V row of one token, columns row0 + 16c .. +15 (bf16)
     f32x4 c1[NB];
-};
-
-template <int NB, int ND>
-struct ZIn {                     // state-update operands of one step
-    uint4 zfr[ND][Blocks<NB>::NFULL + (Blocks<NB>::HALF ? 1 : 0)];
     float gC;
-};
-
-template <int NB, int ND>
-struct OutIn {                   // output operands of one step
-    KRows<NB, ND> q;
-    uint4 efr[Blocks<NB>::TOTAL];
-    float c2[NB];
 };
 
 // Buffer resource over the rows of processing step n: base at the step's lowest
@@ -689,10 +687,10 @@ struct StepRows {
 
 // Rows 16 mt + r of a step as operands: k-step ks < ND/2 takes d = 32 ks + 8 g .. +7
 // (one 16-byte load at byte 64 ks + 16 g), a trailing single tile d = 16 (ND-1) + 4 g .. +3.
-template <int NB, int ND>
-__device__ __forceinline__ void load_rows(KRows<NB, ND>& kk, __amdgpu_buffer_rsrc_t rs, const int (&row)[NB], int g) {
+template <int NT, int ND>
+__device__ __forceinline__ void load_rows(Rows<NT, ND>& kk, __amdgpu_buffer_rsrc_t rs, const int (&row)[NT], int g) {
 #pragma unroll
-    for (int mt = 0; mt < NB; ++mt) {
+    for (int mt = 0; mt < NT; ++mt) {
 #pragma unroll
         for (int ks = 0; ks < ND / 2; ++ks)
             kk.op[mt][ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, row[mt] + 16 * g, 64 * ks, 0));
@@ -703,10 +701,7 @@ __device__ __forceinline__ void load_rows(KRows<NB, ND>& kk, __amdgpu_buffer_rsr
     }
 }
 
-#define GDN_RING 4
-#define GDN_SPIN_LIMIT (1 << 22)
-
-// Wait until an LDS counter written by the other wavefront reaches `target`.
+// Wait until an LDS counter written by another wavefront reaches `target`.
 // Bounded, so a wavefront can never hang here.
 __device__ __forceinline__ void wait_counter(int* cnt, int target) {
     for (int it = 0; it < GDN_SPIN_LIMIT; ++it) {
@@ -721,31 +716,185 @@ __device__ __forceinline__ void signal_counter(int* cnt, int value) {
     __hip_atomic_store(cnt, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
+template <int NB>
+struct ScanShape {
+    static constexpr int NOUT = NB >= 2 ? 2 : 1;   // output wavefronts
+    static constexpr int TPO = NB / NOUT;          // token tiles per output wavefront
+    static constexpr int THREADS = 64 * (1 + NOUT);
+};
+
 template <int NB, int ND>
-__global__ __launch_bounds__(128) void gdn_scan_kernel(Params p, int ngroups) {
+struct ScanLds {
+    static constexpr int NKD = (ND + 1) / 2;
+    static constexpr int NKT = Blocks<NB>::NFULL + (Blocks<NB>::HALF ? 1 : 0);
+    uint4 ringP[GDN_RING][NKD][GDN_COLS][64];
+    uint4 ringR[GDN_RING][NKT][GDN_COLS][64];
+    bf16 Vs[64 * 40];            // V rows of the chain's current step (80-byte rows)
+    int ready;
+    int done[ScanShape<NB>::NOUT];
+};
+
+// Output wavefront `O`: token tiles [O * TPO, (O + 1) * TPO) of every step.
+template <int NB, int ND, int O>
+__device__ __forceinline__ void scan_output(const Params& p, ScanLds<NB, ND>& L, int lane, int b, int h, int dir, int T,
+                                            int N, int row0, const char* item0, int64_t ib) {
+    constexpr int C = 16 * NB, D = 16 * ND;
+    constexpr int NKD = (ND + 1) / 2;
+    using BK = Blocks<NB>;
+    constexpr int NKT = BK::NFULL + (BK::HALF ? 1 : 0);
+    constexpr int TPO = ScanShape<NB>::TPO;
+    constexpr int MT0 = O * TPO;
+    constexpr int EB0 = BK::offset(MT0), EB = BK::offset(MT0 + TPO) - EB0;   // E blocks of these tiles
+    constexpr int SCAL_OFF = 1024 * (BK::TOTAL + ND * NKT);
+    const int r = lane & 15, g = lane >> 4;
+    struct OutIn {
+        Rows<TPO, ND> q;
+        uint4 efr[EB];
+        float c2[TPO];
+    };
+
+    const StepRows qr{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.q) + (int64_t)b * p.qs[0] +
+                                                    (int64_t)h * p.qs[2]),
+                      p.qs[1] * 2, T, C, N, dir, 2 * D};
+    const StepRows orow{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.o[dir]) + (int64_t)b * p.os[0] +
+                                                      (int64_t)h * p.os[2]),
+                        p.os[1] * 2, T, C, N, dir, 2 * D};
+    int qrow[TPO], ooff[TPO];
+#pragma unroll
+    for (int tt = 0; tt < TPO; ++tt) {
+        qrow[tt] = qr.row(16 * (MT0 + tt) + r);
+        ooff[tt] = orow.row(16 * (MT0 + tt) + r) + 2 * (row0 + 4 * g);   // token, state rows row0 + 4g ..
+    }
+    bool col_ok[GDN_COLS];
+#pragma unroll
+    for (int c = 0; c < GDN_COLS; ++c) col_ok[c] = row0 + 16 * c < p.Dv;
+
+    OutIn oA, oB;
+    const auto irs = make_rsrc(item0, (uint32_t)(N * ib));
+    auto load_out = [&](OutIn& o, int n) {
+        load_rows(o.q, qr.rsrc(n), qrow, g);
+        const int ioff = n * (int)ib;
+#pragma unroll
+        for (int e = 0; e < EB; ++e)
+            o.efr[e] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(irs, 16 * lane, ioff + 1024 * (EB0 + e), 0));
+        // c2 of tokens 16 mt + r, mt = MT0 .. MT0 + TPO - 1 (lane-major scalars)
+#pragma unroll
+        for (int tt = 0; tt < TPO; ++tt)
+            o.c2[tt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(irs, 4 * (NB * r + MT0 + tt),
+                                                                                      ioff + SCAL_OFF + 4 * C, 0));
+    };
+
+    load_out(oA, 0);
+    load_out(oB, N > 1 ? 1 : 0);
+    auto out_step = [&](OutIn& o, int n) {
+        const int sl = n % GDN_RING;
+        wait_counter(&L.ready, n + 1);
+        bf16x8 Pb[NKD][GDN_COLS];
+        f16x8 Rb[NKT][GDN_COLS];
+#pragma unroll
+        for (int ks = 0; ks < NKD; ++ks)
+#pragma unroll
+            for (int c = 0; c < GDN_COLS; ++c) Pb[ks][c] = __builtin_bit_cast(bf16x8, L.ringP[sl][ks][c][lane]);
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int c = 0; c < GDN_COLS; ++c) Rb[kt][c] = __builtin_bit_cast(f16x8, L.ringR[sl][kt][c][lane]);
+        // the slot is free once its fragments are in registers
+#pragma unroll
+        for (int ks = 0; ks < NKD; ++ks)
+#pragma unroll
+            for (int c = 0; c < GDN_COLS; ++c) keep_alive(Pb[ks][c]);
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int c = 0; c < GDN_COLS; ++c) keep_alive(Rb[kt][c]);
+        signal_counter(&L.done[O], n + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        // Y^T = S Q^T: rows = state rows 16 c + 4 g + i, column = token 16 mt + r
+        f32x4 Ot[TPO][GDN_COLS];
+#pragma unroll
+        for (int tt = 0; tt < TPO; ++tt)
+#pragma unroll
+            for (int c = 0; c < GDN_COLS; ++c) Ot[tt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKD; ++ks)
+#pragma unroll
+            for (int tt = 0; tt < TPO; ++tt)
+#pragma unroll
+                for (int c = 0; c < GDN_COLS; ++c)
+                    Ot[tt][c] = mma_bf16_k32(Pb[ks][c], __builtin_bit_cast(bf16x8, o.q.op[tt][ks]), Ot[tt][c]);
+#pragma unroll
+        for (int tt = 0; tt < TPO; ++tt)
+#pragma unroll
+            for (int c = 0; c < GDN_COLS; ++c) Ot[tt][c] = Ot[tt][c] * o.c2[tt];
+        // + R^T E^T (a trailing 16-token step has zero upper slots in both operands)
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int tt = 0; tt < TPO; ++tt) {
+                if (kt >= BK::count(MT0 + tt)) continue;
+                const f16x8 ef = __builtin_bit_cast(f16x8, o.efr[BK::offset(MT0 + tt) - EB0 + kt]);
+#pragma unroll
+                for (int c = 0; c < GDN_COLS; ++c) Ot[tt][c] = mma_f16_k32(Rb[kt][c], ef, Ot[tt][c]);
+            }
+        uint2 ov[TPO][GDN_COLS];
+#pragma unroll
+        for (int tt = 0; tt < TPO; ++tt)
+#pragma unroll
+            for (int c = 0; c < GDN_COLS; ++c) {
+                const bf16x4 b4 = {(bf16)Ot[tt][c][0], (bf16)Ot[tt][c][1], (bf16)Ot[tt][c][2], (bf16)Ot[tt][c][3]};
+                ov[tt][c] = __builtin_bit_cast(uint2, b4);
+            }
+        // O is consumed: the operands of step n + 2 may now be loaded into o
+#pragma unroll
+        for (int tt = 0; tt < TPO; ++tt)
+#pragma unroll
+            for (int c = 0; c < GDN_COLS; ++c) keep_alive(ov[tt][c]);
+        __builtin_amdgcn_sched_barrier(0);
+        load_out(o, n + 2 < N ? n + 2 : N - 1);
+        const auto ors = orow.rsrc(n);
+#pragma unroll
+        for (int c = 0; c < GDN_COLS; ++c)
+            if (col_ok[c]) {
+#pragma unroll
+                for (int tt = 0; tt < TPO; ++tt)
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ov[tt][c]), ors, ooff[tt] + 32 * c, 0, 0);
+            }
+    };
+    // The prefetches are unconditional (the last steps reload step N-1) so that
+    // every path through the loop has the same loads in flight.
+    int n = 0;
+    for (; n + 1 < N; n += 2) {
+        out_step(oA, n);
+        out_step(oB, n + 1);
+    }
+    if (n < N) out_step(oA, n);
+}
+
+template <int NB, int ND>
+__global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params p, int ngroups) {
     constexpr int C = 16 * NB, D = 16 * ND;
     constexpr int NKD = (ND + 1) / 2;      // k-steps over d (the last one half-filled for odd ND)
+    constexpr int NS = (ND + GDN_COLS - 1) / GDN_COLS;   // slices per head
     using BK = Blocks<NB>;
     constexpr int NFT = BK::NFULL;         // 32-wide steps over tokens
     constexpr bool HT = BK::HALF;
     constexpr int NKT = NFT + (HT ? 1 : 0);
     constexpr int SCAL_OFF = 1024 * (BK::TOTAL + ND * NKT);   // scalars of an item
+    constexpr int NOUT = ScanShape<NB>::NOUT;
     typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-    __shared__ __align__(16) uint4 ringP[GDN_RING][NKD][64];
-    __shared__ __align__(16) uint4 ringR[GDN_RING][NKT][64];
-    __shared__ __align__(16) bf16 Vs[64 * 16];   // V rows of the chain's current step
-    __shared__ int ready, done;
+    __shared__ __align__(16) ScanLds<NB, ND> L;
 
     const int lane = threadIdx.x & 63;
-    // the role of a wavefront is wave-uniform: keep it in a scalar register so both
-    // roles are whole-wavefront branches
+    // the role of a wavefront is wave-uniform: keep it in a scalar register so every
+    // role is a whole-wavefront branch
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, g = lane >> 4;
-    // Workgroups are spread over the 8 XCDs round-robin (id % 8); keep the ND
-    // row slices of one (direction, b, h) on one XCD so they share its L2.
+    // Workgroups are spread over the 8 XCDs round-robin (id % 8); keep the NS
+    // slices of one (direction, b, h) on one XCD so they share its L2.
     const int id = blockIdx.x, xcd = id & 7, slot = id >> 3;
-    const int group = (slot / ND) * 8 + xcd, j = slot - (slot / ND) * ND;
+    const int group = (slot / NS) * 8 + xcd, j = slot - (slot / NS) * NS;
     if (group >= ngroups) return;
     int gg = group;
     const int h = gg % p.H; gg /= p.H;
@@ -753,243 +902,224 @@ __global__ __launch_bounds__(128) void gdn_scan_kernel(Params p, int ngroups) {
     const int dir = p.dir0 + gg;
     const int T = (int)p.T;
     const int N = (T + C - 1) / C;
-    const int row0 = 16 * j;
+    const int row0 = 16 * GDN_COLS * j;
     const char* item0 = p.ws + (((int64_t)dir * p.B + b) * p.H + h) * p.nsub_max * p.ws_item_bytes;
     const int64_t ib = p.ws_item_bytes;
 
     if (threadIdx.x == 0) {
-        ready = 0;
-        done = 0;
+        L.ready = 0;
+#pragma unroll
+        for (int o = 0; o < NOUT; ++o) L.done[o] = 0;
     }
     __syncthreads();
 
-    if (wave == 0) {
-        // ------------------------------ chain wavefront ------------------------------
-        const StepRows kr{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.k) + (int64_t)b * p.ks[0] +
-                                                        (int64_t)h * p.ks[2]),
-                          p.ks[1] * 2, T, C, N, dir, 2 * D};
-        const StepRows vr{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.v) + (int64_t)b * p.vs[0] +
-                                                        (int64_t)h * p.vs[2]),
-                          p.vs[1] * 2, T, C, N, dir, 2 * D};
-        int krow[NB];
-#pragma unroll
-        for (int mt = 0; mt < NB; ++mt) krow[mt] = kr.row(16 * mt + r);
-        // each lane stages the V row of token `lane` (rows >= C duplicate real ones, unused)
-        const int voff = vr.row(lane & (C - 1)) + 2 * row0;
+    if (wave == 1) {
+        scan_output<NB, ND, 0>(p, L, lane, b, h, dir, T, N, row0, item0, ib);
+        return;
+    }
+    if constexpr (NOUT > 1) {
+        if (wave == 2) {
+            scan_output<NB, ND, 1>(p, L, lane, b, h, dir, T, N, row0, item0, ib);
+            return;
+        }
+    }
 
-        ChainIn<NB, ND> cA, cB;
-        ZIn<NB, ND> zi;
-        auto load_chain = [&](ChainIn<NB, ND>& c, int n) {
-            load_rows(c.k, kr.rsrc(n), krow, g);
-            const auto rs = vr.rsrc(n);
-            c.v[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
-            c.v[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 16, 0));
-            const float* scg = reinterpret_cast<const float*>(item0 + n * ib + SCAL_OFF);
+    // ------------------------------ chain wavefront ------------------------------
+    // Per step n the chain runs: Pb = bf16(S); Z(n) loads; X = K S^T on MFMA while the
+    // VALU scales S by gamma_C and stages V; R = V - c1 X; V, c1, gamma_C of step n+1
+    // load; the state and R go to the ring; K of step n+2 loads; S^T += Z^T R on MFMA.
+    // Each load reuses registers whose last reader has completed (K after R, which
+    // depends on every X MFMA; Z after the Pb conversion, which depends on every
+    // state-update MFMA; V and the scales after R).
+    const StepRows kr{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.k) + (int64_t)b * p.ks[0] +
+                                                    (int64_t)h * p.ks[2]),
+                      p.ks[1] * 2, T, C, N, dir, 2 * D};
+    const StepRows vr{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.v) + (int64_t)b * p.vs[0] +
+                                                    (int64_t)h * p.vs[2]),
+                      p.vs[1] * 2, T, C, N, dir, 2 * D};
+    int krow[NB];
 #pragma unroll
-            for (int mt = 0; mt < NB; ++mt) c.c1[mt] = *reinterpret_cast<const f32x4*>(scg + 16 * mt + 4 * g);
-        };
-        auto load_z = [&](int n) {
-            const char* item = item0 + n * ib;
-            const uint4* zsw = reinterpret_cast<const uint4*>(item) + BK::TOTAL * 64;
+    for (int mt = 0; mt < NB; ++mt) krow[mt] = kr.row(16 * mt + r);
+    bool col_ok[GDN_COLS];
 #pragma unroll
-            for (int m = 0; m < ND; ++m)
-#pragma unroll
-                for (int ks = 0; ks < NKT; ++ks) zi.zfr[m][ks] = zsw[(m * NKT + ks) * 64 + lane];
-            zi.gC = reinterpret_cast<const float*>(item + SCAL_OFF)[2 * C];
-        };
+    for (int c = 0; c < GDN_COLS; ++c) col_ok[c] = row0 + 16 * c < p.Dv;
+    // each lane stages the V row of token `lane` (rows >= C duplicate real ones, unused)
+    const int voff = vr.row(lane & (C - 1)) + 2 * row0;
 
-        // state slice, transposed: P[m][i] = S[row0 + r][dperm(m, 4 g + i)]
-        f32x4 P[ND];
-        const float* Sin = (dir == 0) ? p.S_in : nullptr;
-        const int64_t sbase = ((int64_t)b * p.H + h) * D * D + (int64_t)(row0 + r) * D;
+    Rows<NB, ND> kA, kB;
+    VIn<NB> vi;
+    uint4 zfr[ND][NKT];
+    // the items of this (direction, b, h), addressed with lane-constant offsets
+    const auto irs = make_rsrc(item0, (uint32_t)(N * ib));
+    auto load_v = [&](int n) {   // V rows and scales of step n
+        const auto rs = vr.rsrc(n);
 #pragma unroll
-        for (int m = 0; m < ND; ++m) {
-            if (Sin) P[m] = *reinterpret_cast<const f32x4*>(Sin + sbase + dperm<ND>(m, 4 * g));
-            else P[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int cc = 0; cc < GDN_COLS; ++cc) {
+            if (col_ok[cc]) {
+                vi.v[cc][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 32 * cc, 0));
+                vi.v[cc][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 32 * cc + 16, 0));
+            } else {
+                vi.v[cc][0] = vi.v[cc][1] = uint4{0u, 0u, 0u, 0u};
+            }
+        }
+        const int ioff = n * (int)ib;
+#pragma unroll
+        for (int mt = 0; mt < NB; ++mt)
+            vi.c1[mt] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(irs, 64 * mt + 16 * g,
+                                                                                         ioff + SCAL_OFF, 0));
+        vi.gC = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(irs, 0, ioff + SCAL_OFF + 8 * C, 0));
+    };
+    auto load_z = [&](int n) {   // state-update operator of step n
+        const int ioff = n * (int)ib;
+#pragma unroll
+        for (int m = 0; m < ND; ++m)
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+                zfr[m][kt] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                           irs, 16 * lane, ioff + 1024 * (BK::TOTAL + m * NKT + kt), 0));
+    };
+
+    // state slice, transposed: P[m][c][i] = S[row0 + 16 c + r][dperm(m, 4 g + i)]
+    f32x4 P[ND][GDN_COLS];
+    const float* Sin = (dir == 0) ? p.S_in : nullptr;
+    const int64_t hbase = ((int64_t)b * p.H + h) * D * D;
+#pragma unroll
+    for (int m = 0; m < ND; ++m)
+#pragma unroll
+        for (int c = 0; c < GDN_COLS; ++c) {
+            if (Sin && col_ok[c])
+                P[m][c] = *reinterpret_cast<const f32x4*>(Sin + hbase + (int64_t)(row0 + 16 * c + r) * D + dperm<ND>(m, 4 * g));
+            else
+                P[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 
-        load_chain(cA, 0);
-        load_chain(cB, N > 1 ? 1 : 0);
-        load_z(0);
-        auto chain_step = [&](ChainIn<NB, ND>& c, int n) {
-            const int sl = n % GDN_RING;
-            // state as bf16 operand: k-slot e of lane group g <-> d = dperm(2 ks + e/4, 4 g + e%4)
-            bf16x8 Pb[NKD];
+    load_v(0);
+    load_rows(kA, kr.rsrc(0), krow, g);
+    load_rows(kB, kr.rsrc(N > 1 ? 1 : 0), krow, g);
+    auto chain_step = [&](Rows<NB, ND>& kc, int n) {
+        const int sl = n % GDN_RING;
+        // state as bf16 operand: k-slot e of lane group g <-> d = dperm(2 ks + e/4, 4 g + e%4)
+        bf16x8 Pb[NKD][GDN_COLS];
+#pragma unroll
+        for (int cc = 0; cc < GDN_COLS; ++cc) {
 #pragma unroll
             for (int ks = 0; ks < ND / 2; ++ks)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    Pb[ks][i] = (bf16)P[2 * ks][i];
-                    Pb[ks][4 + i] = (bf16)P[2 * ks + 1][i];
+                    Pb[ks][cc][i] = (bf16)P[2 * ks][cc][i];
+                    Pb[ks][cc][4 + i] = (bf16)P[2 * ks + 1][cc][i];
                 }
             if constexpr (ND % 2) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    Pb[NKD - 1][i] = (bf16)P[ND - 1][i];
-                    Pb[NKD - 1][4 + i] = (bf16)0.f;
+                    Pb[NKD - 1][cc][i] = (bf16)P[ND - 1][cc][i];
+                    Pb[NKD - 1][cc][4 + i] = (bf16)0.f;
                 }
             }
-            // X = K S^T (rows: tokens 16 mt + 4 g + i, column r)
-            f32x4 X[NB];
-#pragma unroll
-            for (int mt = 0; mt < NB; ++mt) X[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < NKD; ++ks)
-#pragma unroll
-                for (int mt = 0; mt < NB; ++mt)
-                    X[mt] = mma_bf16_k32(__builtin_bit_cast(bf16x8, c.k.op[mt][ks]), Pb[ks], X[mt]);
-            // V in the same layout: stage the rows in LDS, read them back transposed
-            // (lane quad c of group g supplies row 16 mt + 4 g + i, columns 4c .. 4c+3)
-            *reinterpret_cast<uint4*>(Vs + 16 * lane) = c.v[0];
-            *reinterpret_cast<uint4*>(Vs + 16 * lane + 8) = c.v[1];
-            bf16x4 vt[NB];
-#pragma unroll
-            for (int mt = 0; mt < NB; ++mt)
-                vt[mt] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                                        (__attribute__((address_space(3))) s16x4*)(
-                                                            Vs + 16 * (16 * mt + 4 * g + (r >> 2)) + 4 * (r & 3))));
-            // R = V - diag(e^g / |k|) X, as fp16 B operand (k = token)
-            f16x8 Rb[NKT];
-#pragma unroll
-            for (int mt = 0; mt < NB; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    Rb[mt >> 1][4 * (mt & 1) + i] = (f16)((float)vt[mt][i] - c.c1[mt][i] * X[mt][i]);
-            if constexpr (HT) {
-#pragma unroll
-                for (int i = 4; i < 8; ++i) Rb[NFT][i] = (f16)0.f;
-            }
-            // X is consumed: the operands of step n + 2 may now be loaded into c
-#pragma unroll
-            for (int ks = 0; ks < NKT; ++ks) keep_alive(Rb[ks]);
-#pragma unroll
-            for (int ks = 0; ks < NKD; ++ks) keep_alive(Pb[ks]);
-            __builtin_amdgcn_sched_barrier(0);
-            load_chain(c, n + 2 < N ? n + 2 : N - 1);
-            // publish the step's state and R once the output wavefront has released the slot
-            wait_counter(&done, n + 1 - GDN_RING);
-#pragma unroll
-            for (int ks = 0; ks < NKD; ++ks) ringP[sl][ks][lane] = __builtin_bit_cast(uint4, Pb[ks]);
-#pragma unroll
-            for (int ks = 0; ks < NKT; ++ks) ringR[sl][ks][lane] = __builtin_bit_cast(uint4, Rb[ks]);
-            signal_counter(&ready, n + 1);
-            __builtin_amdgcn_sched_barrier(0);
-            // S^T <- gamma_C S^T + Z^T R  (rows d, columns r); a trailing 16-token step has
-            // zero upper slots in both operands
-#pragma unroll
-            for (int m = 0; m < ND; ++m) P[m] = P[m] * zi.gC;
-#pragma unroll
-            for (int ks = 0; ks < NKT; ++ks)
-#pragma unroll
-                for (int m = 0; m < ND; ++m) P[m] = mma_f16_k32(__builtin_bit_cast(f16x8, zi.zfr[m][ks]), Rb[ks], P[m]);
-            // every state-update MFMA has finished once P is read: its Z operands may go
-#pragma unroll
-            for (int m = 0; m < ND; ++m) {
-                const float pm = P[m][0];
-                keep_alive(pm);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            load_z(n + 1 < N ? n + 1 : N - 1);
-        };
-        // The prefetches are unconditional (the last steps reload step N-1) so that
-        // every path through the loop has the same loads in flight.
-        int n = 0;
-        for (; n + 1 < N; n += 2) {
-            chain_step(cA, n);
-            chain_step(cB, n + 1);
         }
-        if (n < N) chain_step(cA, n);
-        float* Sout = p.S_out[dir];
-        if (Sout) {
+        // Pb depends on every state-update MFMA of the previous step: Z may be reloaded
 #pragma unroll
-            for (int m = 0; m < ND; ++m) *reinterpret_cast<f32x4*>(Sout + sbase + dperm<ND>(m, 4 * g)) = P[m];
-        }
-    } else {
-        // ------------------------------ output wavefront ------------------------------
-        const StepRows qr{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.q) + (int64_t)b * p.qs[0] +
-                                                        (int64_t)h * p.qs[2]),
-                          p.qs[1] * 2, T, C, N, dir, 2 * D};
-        const StepRows orow{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.o[dir]) + (int64_t)b * p.os[0] +
-                                                          (int64_t)h * p.os[2]),
-                            p.os[1] * 2, T, C, N, dir, 2 * D};
-        int qrow[NB], ooff[NB];
+        for (int ks = 0; ks < NKD; ++ks)
 #pragma unroll
-        for (int mt = 0; mt < NB; ++mt) {
-            qrow[mt] = qr.row(16 * mt + r);
-            ooff[mt] = orow.row(16 * mt + r) + 2 * (row0 + 4 * g);   // token 16 mt + r, state rows row0 + 4g ..
-        }
-
-        OutIn<NB, ND> oA, oB;
-        auto load_out = [&](OutIn<NB, ND>& o, int n) {
-            load_rows(o.q, qr.rsrc(n), qrow, g);
-            const char* item = item0 + n * ib;
-            const uint4* esw = reinterpret_cast<const uint4*>(item);
+            for (int cc = 0; cc < GDN_COLS; ++cc) keep_alive(Pb[ks][cc]);
+        __builtin_amdgcn_sched_barrier(0);
+        load_z(n);
+        // X = K S^T (rows: tokens 16 mt + 4 g + i, column: state row 16 cc + r)
+        f32x4 X[NB][GDN_COLS];
 #pragma unroll
-            for (int blk = 0; blk < BK::TOTAL; ++blk) o.efr[blk] = esw[blk * 64 + lane];
-            const float* scg = reinterpret_cast<const float*>(item + SCAL_OFF) + C + NB * r;
+        for (int mt = 0; mt < NB; ++mt)
 #pragma unroll
-            for (int mt = 0; mt < NB; ++mt) o.c2[mt] = scg[mt];
-        };
-
-        load_out(oA, 0);
-        load_out(oB, N > 1 ? 1 : 0);
-        auto out_step = [&](OutIn<NB, ND>& o, int n) {
-            const int sl = n % GDN_RING;
-            wait_counter(&ready, n + 1);
-            bf16x8 Pb[NKD];
-            f16x8 Rb[NKT];
+            for (int cc = 0; cc < GDN_COLS; ++cc) X[mt][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < NKD; ++ks) Pb[ks] = __builtin_bit_cast(bf16x8, ringP[sl][ks][lane]);
-#pragma unroll
-            for (int ks = 0; ks < NKT; ++ks) Rb[ks] = __builtin_bit_cast(f16x8, ringR[sl][ks][lane]);
-            // the slot is free once its fragments are in registers
-#pragma unroll
-            for (int ks = 0; ks < NKD; ++ks) keep_alive(Pb[ks]);
-#pragma unroll
-            for (int ks = 0; ks < NKT; ++ks) keep_alive(Rb[ks]);
-            signal_counter(&done, n + 1);
-            __builtin_amdgcn_sched_barrier(0);
-            // Y^T = S Q^T: rows = state rows 4 g + i, column = token 16 mt + r
-            f32x4 O[NB];
-#pragma unroll
-            for (int mt = 0; mt < NB; ++mt) O[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < NKD; ++ks)
-#pragma unroll
-                for (int mt = 0; mt < NB; ++mt)
-                    O[mt] = mma_bf16_k32(Pb[ks], __builtin_bit_cast(bf16x8, o.q.op[mt][ks]), O[mt]);
-#pragma unroll
-            for (int mt = 0; mt < NB; ++mt) O[mt] = O[mt] * o.c2[mt];
-            // + R^T E^T (a trailing 16-token step has zero upper slots in both operands)
-#pragma unroll
-            for (int idx = 0; idx < NKT; ++idx)
-#pragma unroll
-                for (int mt = 0; mt < NB; ++mt) {
-                    if (idx >= BK::count(mt)) continue;
-                    O[mt] = mma_f16_k32(Rb[idx], __builtin_bit_cast(f16x8, o.efr[BK::offset(mt) + idx]), O[mt]);
-                }
-            uint2 ov[NB];
+        for (int ks = 0; ks < NKD; ++ks)
 #pragma unroll
             for (int mt = 0; mt < NB; ++mt) {
-                const bf16x4 b4 = {(bf16)O[mt][0], (bf16)O[mt][1], (bf16)O[mt][2], (bf16)O[mt][3]};
-                ov[mt] = __builtin_bit_cast(uint2, b4);
+                const bf16x8 ka = __builtin_bit_cast(bf16x8, kc.op[mt][ks]);
+#pragma unroll
+                for (int cc = 0; cc < GDN_COLS; ++cc) X[mt][cc] = mma_bf16_k32(ka, Pb[ks][cc], X[mt][cc]);
             }
-            // O is consumed: the operands of step n + 2 may now be loaded into o
+        // meanwhile: decay the state, stage V in LDS and read it back transposed
+        // (lane quad q of group g supplies row 16 mt + 4 g + i, columns 16 cc + 4q .. +3)
 #pragma unroll
-            for (int mt = 0; mt < NB; ++mt) keep_alive(ov[mt]);
-            __builtin_amdgcn_sched_barrier(0);
-            load_out(o, n + 2 < N ? n + 2 : N - 1);
-            const auto ors = orow.rsrc(n);
+        for (int m = 0; m < ND; ++m)
 #pragma unroll
-            for (int mt = 0; mt < NB; ++mt)
-                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ov[mt]), ors, ooff[mt], 0, 0);
-        };
-        int n = 0;
-        for (; n + 1 < N; n += 2) {
-            out_step(oA, n);
-            out_step(oB, n + 1);
+            for (int cc = 0; cc < GDN_COLS; ++cc) P[m][cc] = P[m][cc] * vi.gC;
+#pragma unroll
+        for (int cc = 0; cc < GDN_COLS; ++cc) {
+            *reinterpret_cast<uint4*>(L.Vs + 40 * lane + 16 * cc) = vi.v[cc][0];
+            *reinterpret_cast<uint4*>(L.Vs + 40 * lane + 16 * cc + 8) = vi.v[cc][1];
         }
-        if (n < N) out_step(oA, n);
+        bf16x4 vt[NB][GDN_COLS];
+#pragma unroll
+        for (int mt = 0; mt < NB; ++mt)
+#pragma unroll
+            for (int cc = 0; cc < GDN_COLS; ++cc)
+                vt[mt][cc] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                            (__attribute__((address_space(3))) s16x4*)(
+                                                                L.Vs + 40 * (16 * mt + 4 * g + (r >> 2)) + 16 * cc + 4 * (r & 3))));
+        // R = V - diag(e^g / |k|) X, as fp16 B operand (k = token)
+        f16x8 Rb[NKT][GDN_COLS];
+#pragma unroll
+        for (int mt = 0; mt < NB; ++mt)
+#pragma unroll
+            for (int cc = 0; cc < GDN_COLS; ++cc)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    Rb[mt >> 1][cc][4 * (mt & 1) + i] = (f16)((float)vt[mt][cc][i] - vi.c1[mt][i] * X[mt][cc][i]);
+        if constexpr (HT) {
+#pragma unroll
+            for (int cc = 0; cc < GDN_COLS; ++cc)
+#pragma unroll
+                for (int i = 4; i < 8; ++i) Rb[NFT][cc][i] = (f16)0.f;
+        }
+        // R depends on every X MFMA and on V and c1 of this step: those registers are free
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int cc = 0; cc < GDN_COLS; ++cc) keep_alive(Rb[kt][cc]);
+        __builtin_amdgcn_sched_barrier(0);
+        load_v(n + 1 < N ? n + 1 : N - 1);
+        // publish the step's state and R once every output wavefront has released the slot
+#pragma unroll
+        for (int o = 0; o < NOUT; ++o) wait_counter(&L.done[o], n + 1 - GDN_RING);
+#pragma unroll
+        for (int ks = 0; ks < NKD; ++ks)
+#pragma unroll
+            for (int cc = 0; cc < GDN_COLS; ++cc) L.ringP[sl][ks][cc][lane] = __builtin_bit_cast(uint4, Pb[ks][cc]);
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int cc = 0; cc < GDN_COLS; ++cc) L.ringR[sl][kt][cc][lane] = __builtin_bit_cast(uint4, Rb[kt][cc]);
+        signal_counter(&L.ready, n + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_rows(kc, kr.rsrc(n + 2 < N ? n + 2 : N - 1), krow, g);
+        // S^T <- gamma_C S^T + Z^T R  (rows d, columns: state rows); a trailing 16-token
+        // step has zero upper slots in both operands
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int m = 0; m < ND; ++m) {
+                const f16x8 za = __builtin_bit_cast(f16x8, zfr[m][kt]);
+#pragma unroll
+                for (int cc = 0; cc < GDN_COLS; ++cc) P[m][cc] = mma_f16_k32(za, Rb[kt][cc], P[m][cc]);
+            }
+    };
+    // The prefetches are unconditional (the last steps reload step N-1) so that
+    // every path through the loop has the same loads in flight.
+    int n = 0;
+    for (; n + 1 < N; n += 2) {
+        chain_step(kA, n);
+        chain_step(kB, n + 1);
+    }
+    if (n < N) chain_step(kA, n);
+    float* Sout = p.S_out[dir];
+    if (Sout) {
+#pragma unroll
+        for (int m = 0; m < ND; ++m)
+#pragma unroll
+            for (int c = 0; c < GDN_COLS; ++c)
+                if (col_ok[c])
+                    *reinterpret_cast<f32x4*>(Sout + hbase + (int64_t)(row0 + 16 * c + r) * D + dperm<ND>(m, 4 * g)) = P[m][c];
     }
 }
 
@@ -1041,9 +1171,9 @@ static hipError_t run_chunked(const Params& p, hipStream_t s, Timing* tm) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int ngroups = p.ndirs * p.B * p.H;
-    const int grid = (ngroups + 7) / 8 * 8 * ND;
+    const int grid = (ngroups + 7) / 8 * 8 * ((ND + GDN_COLS - 1) / GDN_COLS);
     tm_begin(tm, s, KSCAN);
-    hipLaunchKernelGGL((gdn_scan_kernel<NB, ND>), dim3(grid), dim3(128), 0, s, p, ngroups);
+    hipLaunchKernelGGL((gdn_scan_kernel<NB, ND>), dim3(grid), dim3(ScanShape<NB>::THREADS), 0, s, p, ngroups);
     tm_end(tm, s);
     return hipGetLastError();
 }
