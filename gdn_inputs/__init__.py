@@ -34,10 +34,10 @@ GDN_LAYERS = 15
 def round_bf16(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bf16 value (ties to even); returns float32."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) & 0xFFFF0000).astype(np.uint32)
-    out = r.view(np.float32).copy()
+    u = x.view(np.uint32)
+    # finite inputs cannot wrap: the largest finite pattern plus 0x8000 stays below 2^32
+    r = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) & np.uint32(0xFFFF0000)
+    out = r.view(np.float32)
     nan = np.isnan(x)
     if nan.any():
         out[nan] = np.nan
@@ -100,3 +100,25 @@ def tiny_fp32():
     rng = np.random.default_rng(0)
     d = draw(rng, 64, 1, 16, 16, io="f32")
     return {key: val[None] for key, val in d.items()}
+
+
+def stream_chunk_torch(cfg: int, chunk: int, B: int, T: int, H: int, D: int, *, device="cuda",
+                       with_state: bool = False, stream0: int = 0):
+    """Same distributions as `batch`, drawn on the device with torch's generator (for long
+    streams whose host-side generation would dominate a test).  Seed: the first word of
+    SeedSequence([cfg, stream0, 0, chunk, 0]).  Returns bf16 q, k, v [B, T, H, D], fp32 a, beta
+    [B, T, H] and, if asked, an fp32 S0 [B, H, D, D], all on `device`."""
+    import torch
+    seed = int(np.random.SeedSequence([cfg, stream0, 0, chunk, 0]).generate_state(1)[0])
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    out = {}
+    for key in ("q", "k", "v"):
+        out[key] = torch.randn((B, T, H, D), generator=gen, device=device).to(torch.bfloat16)
+    za = torch.randn((B, T, H), generator=gen, device=device)
+    zb = torch.randn((B, T, H), generator=gen, device=device)
+    out["a"] = torch.exp(-0.1 * torch.nn.functional.softplus(za))
+    out["beta"] = torch.sigmoid(zb)
+    if with_state:
+        out["S0"] = 0.1 * torch.randn((B, H, D, D), generator=gen, device=device)
+    return out
