@@ -28,6 +28,7 @@ struct gdn_stream {
     float* state;         // [B, H, d_v, d_k]
     int64_t state_elems;
     char* ws;             // chunked workspace: [2 directions][B][H][nsub_max] items
+    __bf16* conv;         // fp32 I/O with the chunked kernels: bf16 staging of q, k, v
     int64_t item_bytes;
     int nsub_max;
     // optional per-kernel timing
@@ -155,6 +156,7 @@ gdn::Params base_params(gdn_stream* s, const gdn_io* io, int64_t T) {
     p.ws_item_bytes = s->item_bytes;
     p.nsub_max = s->nsub_max;
     p.C = s->C;
+    p.conv = s->conv;
     return p;
 }
 
@@ -259,6 +261,7 @@ GDN_API int gdn_stream_init(const gdn_config* cfg, int device, gdn_stream** out)
     }
     e = hipMemset(s->state, 0, s->state_elems * sizeof(float));
     s->ws = nullptr;
+    s->conv = nullptr;
     s->item_bytes = 0;
     s->nsub_max = 0;
     if (e == hipSuccess && s->chunked_ok) {
@@ -271,11 +274,23 @@ GDN_API int gdn_stream_init(const gdn_config* cfg, int device, gdn_stream** out)
             delete s;
             return fail(GDN_E_NOMEM, "workspace allocation (%lld bytes): %s", (long long)bytes, hipGetErrorString(e));
         }
+        if (c.io_dtype == GDN_F32) {
+            const int64_t cb = 3 * (int64_t)c.batch * c.max_tokens * c.heads * c.d_k * 2;
+            e = hipMalloc(&s->conv, cb);
+            if (e != hipSuccess) {
+                (void)hipFree(s->state);
+                (void)hipFree(s->ws);
+                delete s;
+                return fail(GDN_E_NOMEM, "bf16 staging allocation (%lld bytes): %s", (long long)cb,
+                            hipGetErrorString(e));
+            }
+        }
     }
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
         (void)hipFree(s->state);
         if (s->ws) (void)hipFree(s->ws);
+        if (s->conv) (void)hipFree(s->conv);
         delete s;
         return fail(GDN_E_HIP, "init: %s", hipGetErrorString(e));
     }
@@ -297,6 +312,7 @@ GDN_API int gdn_stream_destroy(gdn_stream* s) {
     }
     (void)hipFree(s->state);
     if (s->ws) (void)hipFree(s->ws);
+    if (s->conv) (void)hipFree(s->conv);
     delete s;
     if (e != hipSuccess) return fail(GDN_E_HIP, "destroy: %s", hipGetErrorString(e));
     return ok();

@@ -32,6 +32,7 @@ struct Params {
     int64_t ws_item_bytes;
     int nsub_max;
     int C;                 // sub-chunk length
+    __bf16* conv;          // fp32 I/O only: bf16 copies of q, k, v ([3][B][T][H][D])
 };
 
 // Bytes of one workspace item for sub-chunk C (multiple of 16, 16..64).

@@ -51,6 +51,7 @@ typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef f16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // decays below e^-80 are treated as e^-80 (the state is forgotten either way)
 #define GDN_MIN_LOG_DECAY (-80.0f)
@@ -756,14 +757,15 @@ __device__ __forceinline__ void scan_output(const Params& p, ScanLds<NB, ND>& L,
     const StepRows qr{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.q) + (int64_t)b * p.qs[0] +
                                                     (int64_t)h * p.qs[2]),
                       p.qs[1] * 2, T, C, N, dir, 2 * D};
-    const StepRows orow{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.o[dir]) + (int64_t)b * p.os[0] +
-                                                      (int64_t)h * p.os[2]),
-                        p.os[1] * 2, T, C, N, dir, 2 * D};
+    // o is bf16, or fp32 when the call's I/O is fp32 (its q, k, v were staged as bf16)
+    const int oesz = p.io_f32 ? 4 : 2;
+    const StepRows orow{reinterpret_cast<const char*>(p.o[dir]) + ((int64_t)b * p.os[0] + (int64_t)h * p.os[2]) * oesz,
+                        p.os[1] * oesz, T, C, N, dir, oesz * D};
     int qrow[TPO], ooff[TPO];
 #pragma unroll
     for (int tt = 0; tt < TPO; ++tt) {
         qrow[tt] = qr.row(16 * (MT0 + tt) + r);
-        ooff[tt] = orow.row(16 * (MT0 + tt) + r) + 2 * (row0 + 4 * g);   // token, state rows row0 + 4g ..
+        ooff[tt] = orow.row(16 * (MT0 + tt) + r) + oesz * (row0 + 4 * g);   // token, state rows row0 + 4g ..
     }
     bool col_ok[GDN_COLS];
 #pragma unroll
@@ -857,8 +859,12 @@ __device__ __forceinline__ void scan_output(const Params& p, ScanLds<NB, ND>& L,
         for (int c = 0; c < GDN_COLS; ++c)
             if (col_ok[c]) {
 #pragma unroll
-                for (int tt = 0; tt < TPO; ++tt)
-                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ov[tt][c]), ors, ooff[tt] + 32 * c, 0, 0);
+                for (int tt = 0; tt < TPO; ++tt) {
+                    if (oesz == 2)
+                        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ov[tt][c]), ors, ooff[tt] + 32 * c, 0, 0);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, Ot[tt][c]), ors, ooff[tt] + 64 * c, 0, 0);
+                }
             }
     };
     // The prefetches are unconditional (the last steps reload step N-1) so that
@@ -1123,6 +1129,20 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
     }
 }
 
+// fp32 q, k, v (caller strides) -> bf16 copies in `dst` ([3][B][T][H][D], contiguous), rounded to
+// nearest even: the chunked kernels take their MFMA operands in bf16.
+__global__ void gdn_to_bf16_kernel(Params p, bf16* dst) {
+    const int64_t D = p.Dk, rows = (int64_t)p.B * p.T * p.H, per = rows * D;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < 3 * per; i += (int64_t)gridDim.x * blockDim.x) {
+        const int w = (int)(i / per);
+        const int64_t j = i - w * per, row = j / D, d = j - row * D;
+        const int64_t hh = row % p.H, tt = (row / p.H) % p.T, bb = row / ((int64_t)p.H * p.T);
+        const float* src = static_cast<const float*>(w == 0 ? p.q : w == 1 ? p.k : p.v);
+        const int64_t* st = w == 0 ? p.qs : w == 1 ? p.ks : p.vs;
+        dst[i] = (bf16)src[bb * st[0] + tt * st[1] + hh * st[2] + d];
+    }
+}
+
 // Zero a float buffer (used instead of a memset node so callers may capture it in a graph).
 __global__ void gdn_zero_kernel(float* x, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
@@ -1191,13 +1211,28 @@ static hipError_t run_chunked_d(const Params& p, hipStream_t s, Timing* tm) {
 }
 
 bool chunked_supported(int C, int Dk, int Dv, int io_f32) {
-    if (io_f32) return false;
+    (void)io_f32;   // fp32 q, k, v are staged as bf16 (gdn_to_bf16_kernel), o is stored in fp32
     if (Dk != Dv) return false;
     if (!(Dk == 16 || Dk == 32 || Dk == 64 || Dk == 112 || Dk == 128)) return false;
     return C == 16 || C == 32 || C == 64;
 }
 
-hipError_t launch_chunked(const Params& p, hipStream_t s, Timing* tm) {
+hipError_t launch_chunked(const Params& p0, hipStream_t s, Timing* tm) {
+    Params p = p0;
+    if (p.io_f32) {
+        if (!p.conv) return hipErrorInvalidValue;
+        const int64_t per = (int64_t)p.B * p.T * p.H * p.Dk;
+        int64_t blocks = (3 * per + 255) / 256;
+        if (blocks > 8192) blocks = 8192;
+        hipLaunchKernelGGL(gdn_to_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p0, p.conv);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        p.q = p.conv;
+        p.k = p.conv + per;
+        p.v = p.conv + 2 * per;
+        const int64_t st[3] = {p.T * p.H * p.Dk, (int64_t)p.H * p.Dk, p.Dk};
+        for (int i = 0; i < 3; ++i) p.qs[i] = p.ks[i] = p.vs[i] = st[i];
+    }
     switch (p.C) {
         case 16: return run_chunked_d<1>(p, s, tm);
         case 32: return run_chunked_d<2>(p, s, tm);

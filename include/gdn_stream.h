@@ -74,7 +74,11 @@ typedef struct gdn_config {
                          /* the chunked kernels need d_v == d_k (16, 32, 64, 112, 128) */
     int64_t max_tokens;  /* largest T of any call; sizes the fixed workspace     */
     int32_t subchunk;    /* chunked-kernel sub-chunk C: 0 (= 64), 16, 32 or 64  */
-    int32_t io_dtype;    /* GDN_BF16 or GDN_F32                                  */
+    int32_t io_dtype;    /* GDN_BF16 or GDN_F32.  With GDN_F32 the chunked       */
+                         /* kernels stage q, k, v as bf16 (round to nearest    */
+                         /* even; a workspace of 3*B*max_tokens*H*d_k*2 bytes   */
+                         /* is added at init) and store o in fp32; the          */
+                         /* sequential kernel stays in fp32 throughout          */
     uint32_t flags;      /* GDN_L2NORM_QK                                        */
     float l2_eps;        /* eps inside the L2 norm (1e-6 is the usual value)     */
     float scale;         /* output scale (1.0 when q is unit-norm)               */

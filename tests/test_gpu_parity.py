@@ -96,6 +96,29 @@ def test_tiny_fp32_sequential():
     assert_close("state", S, Sf, rel_f=1e-5)
 
 
+def test_tiny_fp32_chunked():
+    """The tiny configuration (B=1, H=1, d=16, T=64, sub-chunk 16, fp32, zero initial state,
+    seed 0) through the chunked kernels: q, k, v are staged as bf16, o is stored in fp32."""
+    d = gdn_inputs.tiny_fp32()
+    of, orv, Sf = _oracle_pair(d, state=False)
+    o_f, o_r, S = _run_pair(d, 16, 64, C=16, io="f32", state=False)
+    assert o_f.dtype == torch.float32
+    assert_close("o_fwd", o_f, of)
+    assert_close("o_rev", o_r, orv)
+    assert_close("state", S, Sf)
+
+
+@pytest.mark.parametrize("C", [16, 64])
+def test_fp32_io_chunked(C):
+    """fp32 I/O through the chunked kernels at d = 112 with a carried state and a ragged tail."""
+    d = gdn_inputs.batch(63, 2, 700, 3, 112, io="f32", with_state=True)
+    of, orv, Sf = _oracle_pair(d)
+    o_f, o_r, S = _run_pair(d, 112, 700, C=C, io="f32", bidir=True)
+    assert_close("o_fwd", o_f, of)
+    assert_close("o_rev", o_r, orv)
+    assert_close("state", S, Sf)
+
+
 def test_bidir_equals_separate_calls_bitwise():
     d = gdn_inputs.batch(61, 2, 300, 4, 112, with_state=True)
     a = _run_pair(d, 112, 300)
