@@ -269,7 +269,7 @@ struct TokMap {
 
 
 // ---------------------------------------------------------------------------
-// Chunk preparation: one workgroup (NB wavefronts) per (direction, b, h,
+// Chunk preparation: one workgroup (2 NB wavefronts) per (direction, b, h,
 // processing step n).  Rows are in processing order.  For the C tokens of the
 // step, with k^ = k/|k|, q^ = q/|q|, g = prefix of log a, gamma = e^g:
 //   L[t,s] = beta_t e^{g_t-g_s} k^_t.k^_s (s < t),   T = (I + L)^{-1}
@@ -282,11 +282,13 @@ struct TokMap {
 // d of Z^T follows the scan's state order (see dperm).
 // ---------------------------------------------------------------------------
 template <int NB, int ND>
-__global__ __launch_bounds__(64 * NB) void gdn_prep_kernel(Params p) {
+__global__ __launch_bounds__(128 * NB) void gdn_prep_kernel(Params p) {
     constexpr int C = 16 * NB, D = 16 * ND;
     constexpr int LDR = D + 8;   // bf16 row stride of the staged K and Q rows (8-byte aligned rows)
-    constexpr int LDM = C + 4;   // fp32 row stride of L^T, T^T, A (16-byte aligned rows)
-    constexpr int NT = 64 * NB;
+    constexpr int LDM = C + 4;   // fp32 row stride of L^T, T^T (16-byte aligned rows)
+    constexpr int LDA = C + 8;   // fp16 row stride of A (16-byte aligned rows)
+    constexpr int NW = 2 * NB;   // wavefronts
+    constexpr int NT = 64 * NW;
     constexpr int CH = D / 8;    // 16-byte chunks per row
     using BK = Blocks<NB>;
     constexpr int NFT = BK::NFULL;
@@ -299,7 +301,7 @@ __global__ __launch_bounds__(64 * NB) void gdn_prep_kernel(Params p) {
     __shared__ __align__(16) bf16 Ks[C * LDR];
     __shared__ __align__(16) char QT[Q_BYTES > T_BYTES ? Q_BYTES : T_BYTES];
     __shared__ __align__(16) float Lt[C * LDM];   // L transposed: Lt[s][t] = L[t][s], s < t
-    __shared__ __align__(16) float Am[C * LDM];   // A[t][s]
+    __shared__ __align__(16) f16 Am[C * LDA];     // A[t][s] (an fp16 operand of E only)
     __shared__ __align__(16) float sc[5][C];      // 0: log a then g, 1: beta, 2: 1/|k|, 3: 1/|q|, 4: e^{g_C-g}/|k|
     bf16* Qs = reinterpret_cast<bf16*>(QT);
     float* Tt = reinterpret_cast<float*>(QT);     // T transposed: Tt[u][s] = T[s][u]
@@ -340,26 +342,23 @@ __global__ __launch_bounds__(64 * NB) void gdn_prep_kernel(Params p) {
     }
     __syncthreads();
 
-    // per-token inverse norms: 4 lanes per row, 16 rows per wavefront
+    // per-token inverse norms: 4 lanes per row, 16 rows per wavefront; waves < NB take the
+    // K rows, the others the Q rows
     {
-        const int t = 16 * w + (lane >> 2), part = lane & 3;
-        float sk = 0.f, sq = 0.f;
+        const bool isk = w < NB;
+        const int t = 16 * (isk ? w : w - NB) + (lane >> 2), part = lane & 3;
+        const bf16* rowp = (isk ? Ks : Qs) + t * LDR;
+        float ss = 0.f;
         for (int c = part; c < CH; c += 4) {
-            const bf16x8 kv = ld_bf16x8(Ks + t * LDR + 8 * c);
-            const bf16x8 qv = ld_bf16x8(Qs + t * LDR + 8 * c);
+            const bf16x8 xv = ld_bf16x8(rowp + 8 * c);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float kf = (float)kv[e], qf = (float)qv[e];
-                sk += kf * kf;
-                sq += qf * qf;
+                const float xf = (float)xv[e];
+                ss += xf * xf;
             }
         }
-        sk = sum4(sk);
-        sq = sum4(sq);
-        if (part == 0) {
-            sc[2][t] = p.l2norm ? 1.f / sqrtf(sk + p.eps) : 1.f;
-            sc[3][t] = p.l2norm ? 1.f / sqrtf(sq + p.eps) : 1.f;
-        }
+        ss = sum4(ss);
+        if (part == 0) sc[isk ? 2 : 3][t] = p.l2norm ? 1.f / sqrtf(ss + p.eps) : 1.f;
     }
     // inclusive prefix of log a along the processing order (C <= 64: one wavefront)
     if (w == 0) {
@@ -377,7 +376,7 @@ __global__ __launch_bounds__(64 * NB) void gdn_prep_kernel(Params p) {
     // Gram tiles on MFMA: K K^T -> L (strictly lower, stored transposed), Q K^T -> A (lower incl. diagonal)
     {
         constexpr int NTILE = NB * (NB + 1) / 2;
-        for (int tt = w; tt < 2 * NTILE; tt += NB) {
+        for (int tt = w; tt < 2 * NTILE; tt += NW) {
             const bool isq = tt >= NTILE;
             const int ti = isq ? tt - NTILE : tt;
             int mt = 0;
@@ -413,7 +412,7 @@ __global__ __launch_bounds__(64 * NB) void gdn_prep_kernel(Params p) {
                 if (!isq)
                     Lt[s * LDM + t] = (s < t) ? bt[i] * dec * rt[i] * rs * acc[i] : 0.f;
                 else
-                    Am[t * LDM + s] = (s <= t) ? p.scale * dec * rt[i] * rs * acc[i] : 0.f;
+                    Am[t * LDA + s] = (f16)((s <= t) ? p.scale * dec * rt[i] * rs * acc[i] : 0.f);
             }
 #pragma unroll
             for (int ks = 0; ks < ND / 2; ++ks) {
@@ -501,7 +500,7 @@ __global__ __launch_bounds__(64 * NB) void gdn_prep_kernel(Params p) {
 
     // E^T = T^T A^T, tile (ut, tt) = sum_s Tt[u][s] A[t][s] over s in [16 ut, 16 tt + 16); the
     // output tiles (2ks, mt) and (2ks + 1, mt) form the O-product A fragment (mt, ks) directly.
-    for (int blk = w; blk < BK::TOTAL; blk += NB) {
+    for (int blk = w; blk < BK::TOTAL; blk += NW) {
         int mt = 0;
         while (BK::offset(mt + 1) <= blk) ++mt;
         const int ks = blk - BK::offset(mt);
@@ -514,18 +513,16 @@ __global__ __launch_bounds__(64 * NB) void gdn_prep_kernel(Params p) {
                 // contraction over s in 32-wide steps (zero outside the triangle)
                 for (int ss = (16 * ut) / 32; ss * 32 < 16 * (mt + 1); ++ss) {
                     const float* ta = Tt + (16 * ut + r) * LDM + 32 * ss + 8 * g;
-                    const float* aa = Am + (16 * mt + r) * LDM + 32 * ss + 8 * g;
+                    const f16* aa = Am + (16 * mt + r) * LDA + 32 * ss + 8 * g;
                     f16x8 ao, bo;
                     const int sb = 2 * ss + (g >> 1);   // 16-wide block of this lane's s
                     if (32 * ss + 8 * g < C && sb >= ut && sb <= mt) {
                         const f32x4 t0v = *reinterpret_cast<const f32x4*>(ta), t1v = *reinterpret_cast<const f32x4*>(ta + 4);
-                        const f32x4 a0v = *reinterpret_cast<const f32x4*>(aa), a1v = *reinterpret_cast<const f32x4*>(aa + 4);
+                        bo = *reinterpret_cast<const f16x8*>(aa);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             ao[e] = (f16)t0v[e];
                             ao[4 + e] = (f16)t1v[e];
-                            bo[e] = (f16)a0v[e];
-                            bo[4 + e] = (f16)a1v[e];
                         }
                     } else {
 #pragma unroll
@@ -556,7 +553,7 @@ __global__ __launch_bounds__(64 * NB) void gdn_prep_kernel(Params p) {
     // + i%4 of each 32-wide step) as a bf16 high/low pair; B operand = raw K rows read
     // transposed, column r of tile m being state index dperm(m, r).  Output tiles (2ks, m)
     // and (2ks + 1, m) form the state-update fragment (m, ks).
-    for (int job = w; job < ND * NKT; job += NB) {
+    for (int job = w; job < ND * NKT; job += NW) {
         const int m = job / NKT, ks = job - m * NKT;
         f32x4 zt[2];
 #pragma unroll
@@ -656,7 +653,8 @@ __global__ __launch_bounds__(64 * NB) void gdn_prep_kernel(Params p) {
 // multiple of 32) are computed from zero inputs and never stored.
 // ---------------------------------------------------------------------------
 #define GDN_COLS 2       // 16-row column tiles of the state per workgroup
-#define GDN_RING 4
+#define GDN_RING 3        // output ring slots
+#define GDN_OPS 3         // operand ring slots (the loader runs up to two steps ahead)
 #define GDN_SPIN_LIMIT (1 << 22)
 
 template <int NT, int ND>
@@ -721,7 +719,21 @@ template <int NB>
 struct ScanShape {
     static constexpr int NOUT = NB >= 2 ? 2 : 1;   // output wavefronts
     static constexpr int TPO = NB / NOUT;          // token tiles per output wavefront
-    static constexpr int THREADS = 64 * (1 + NOUT);
+    static constexpr int THREADS = 64 * (GDN_COLS + NOUT + 2);   // + chain wavefronts + two loaders
+};
+
+// One step's chain operands as the loader wavefront deposits them (direct
+// global-to-LDS loads: lane l of a 16-byte load lands at byte 16 l of its block),
+// so each block is one MFMA operand fragment read back with one 16-byte LDS read.
+template <int NB, int ND>
+struct ScanOps {
+    static constexpr int NKF = ND / 2;   // full 32-wide k-steps over d
+    static constexpr int NKT = Blocks<NB>::NFULL + (Blocks<NB>::HALF ? 1 : 0);
+    uint4 k[NB][NKF > 0 ? NKF : 1][64];  // K rows 16 mt + r, d = 32 ks + 8 g .. +7
+    uint4 kh[(ND % 2) ? NB : 1][64];     // odd ND: d = 16 (ND-1) + 4 g .. +3 (low 8 bytes)
+    uint4 z[ND][NKT][64];                // state-update fragments of the item
+    uint4 v[2 * GDN_COLS][64];           // 16-byte chunk j of token `lane`'s V row slice
+    uint4 sc[64];                        // lanes 0..15: c1 (64 floats); lane 16: gamma_C
 };
 
 template <int NB, int ND>
@@ -730,14 +742,42 @@ struct ScanLds {
     static constexpr int NKT = Blocks<NB>::NFULL + (Blocks<NB>::HALF ? 1 : 0);
     uint4 ringP[GDN_RING][NKD][GDN_COLS][64];
     uint4 ringR[GDN_RING][NKT][GDN_COLS][64];
-    bf16 Vs[64 * 40];            // V rows of the chain's current step (80-byte rows)
-    int ready;
-    int done[ScanShape<NB>::NOUT];
+    ScanOps<NB, ND> ops[GDN_OPS];
 };
+
+// Progress counters of the scan's wavefronts.  A separate LDS object from the
+// operand slots, so that the compiler need not order the counters behind the
+// direct global-to-LDS loads in flight.
+template <int NB>
+struct ScanCtr {
+    int ready[GDN_COLS];                 // steps each chain wavefront has published to the output ring
+    int done[ScanShape<NB>::NOUT];       // steps each output wavefront has taken from the ring
+    int loaded[2];                       // steps whose operands each loader has landed in the slots
+    int released[GDN_COLS];              // steps whose operands each chain wavefront has read
+};
+
+// Direct global-to-LDS load of 16 bytes per lane into a wave-uniform LDS block.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void* lds, int voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+// Store a progress counter to LDS.  Written as an instruction of its own so that the
+// compiler does not hold it behind every direct global-to-LDS load in flight (it
+// cannot tell the counter from the loads' destinations); the caller orders it
+// after the loads it publishes with wait_vmcnt.
+__device__ __forceinline__ void publish_loaded(int* cnt, int value) {
+    const unsigned addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) int*)cnt;
+    asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(value) : "memory");
+}
+// s_waitcnt on the vector memory counter only (gfx9 encoding: expcnt and lgkmcnt at their maxima)
+template <int V>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(V >= 0 && V < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((V & 15) | (7 << 4) | (15 << 8) | ((V >> 4) << 14));
+}
 
 // Output wavefront `O`: token tiles [O * TPO, (O + 1) * TPO) of every step.
 template <int NB, int ND, int O>
-__device__ __forceinline__ void scan_output(const Params& p, ScanLds<NB, ND>& L, int lane, int b, int h, int dir, int T,
+__device__ __forceinline__ void scan_output(const Params& p, ScanLds<NB, ND>& L, ScanCtr<NB>& K, int lane, int b, int h, int dir, int T,
                                             int N, int row0, const char* item0, int64_t ib) {
     constexpr int C = 16 * NB, D = 16 * ND;
     constexpr int NKD = (ND + 1) / 2;
@@ -790,7 +830,8 @@ __device__ __forceinline__ void scan_output(const Params& p, ScanLds<NB, ND>& L,
     load_out(oB, N > 1 ? 1 : 0);
     auto out_step = [&](OutIn& o, int n) {
         const int sl = n % GDN_RING;
-        wait_counter(&L.ready, n + 1);
+#pragma unroll
+        for (int c = 0; c < GDN_COLS; ++c) wait_counter(&K.ready[c], n + 1);
         bf16x8 Pb[NKD][GDN_COLS];
         f16x8 Rb[NKT][GDN_COLS];
 #pragma unroll
@@ -810,7 +851,7 @@ __device__ __forceinline__ void scan_output(const Params& p, ScanLds<NB, ND>& L,
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
             for (int c = 0; c < GDN_COLS; ++c) keep_alive(Rb[kt][c]);
-        signal_counter(&L.done[O], n + 1);
+        signal_counter(&K.done[O], n + 1);
         __builtin_amdgcn_sched_barrier(0);
         // Y^T = S Q^T: rows = state rows 16 c + 4 g + i, column = token 16 mt + r
         f32x4 Ot[TPO][GDN_COLS];
@@ -881,6 +922,7 @@ template <int NB, int ND>
 __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params p, int ngroups) {
     constexpr int C = 16 * NB, D = 16 * ND;
     constexpr int NKD = (ND + 1) / 2;      // k-steps over d (the last one half-filled for odd ND)
+    constexpr int NKF = ND / 2;            // full k-steps over d
     constexpr int NS = (ND + GDN_COLS - 1) / GDN_COLS;   // slices per head
     using BK = Blocks<NB>;
     constexpr int NFT = BK::NFULL;         // 32-wide steps over tokens
@@ -888,9 +930,13 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
     constexpr int NKT = NFT + (HT ? 1 : 0);
     constexpr int SCAL_OFF = 1024 * (BK::TOTAL + ND * NKT);   // scalars of an item
     constexpr int NOUT = ScanShape<NB>::NOUT;
+    // loads the loader wavefronts issue per step: K, V and the scales; Z
+    constexpr int NDMA0 = NB * NKF + ((ND % 2) ? NB : 0) + 2 * GDN_COLS + 1;
+    constexpr int NDMA1 = ND * NKT;
     typedef short s16x4 __attribute__((ext_vector_type(4)));
 
     __shared__ __align__(16) ScanLds<NB, ND> L;
+    __shared__ ScanCtr<NB> K;
 
     const int lane = threadIdx.x & 63;
     // the role of a wavefront is wave-uniform: keep it in a scalar register so every
@@ -911,221 +957,218 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
     const int row0 = 16 * GDN_COLS * j;
     const char* item0 = p.ws + (((int64_t)dir * p.B + b) * p.H + h) * p.nsub_max * p.ws_item_bytes;
     const int64_t ib = p.ws_item_bytes;
+    bool col_ok[GDN_COLS];
+#pragma unroll
+    for (int c = 0; c < GDN_COLS; ++c) col_ok[c] = row0 + 16 * c < p.Dv;
 
     if (threadIdx.x == 0) {
-        L.ready = 0;
 #pragma unroll
-        for (int o = 0; o < NOUT; ++o) L.done[o] = 0;
+        for (int c = 0; c < GDN_COLS; ++c) K.ready[c] = K.released[c] = 0;
+#pragma unroll
+        for (int o = 0; o < NOUT; ++o) K.done[o] = 0;
+        K.loaded[0] = K.loaded[1] = 0;
     }
     __syncthreads();
 
-    if (wave == 1) {
-        scan_output<NB, ND, 0>(p, L, lane, b, h, dir, T, N, row0, item0, ib);
-        return;
-    }
-    if constexpr (NOUT > 1) {
-        if (wave == 2) {
-            scan_output<NB, ND, 1>(p, L, lane, b, h, dir, T, N, row0, item0, ib);
-            return;
-        }
-    }
-
-    // ------------------------------ chain wavefront ------------------------------
-    // Per step n the chain runs: Pb = bf16(S); Z(n) loads; X = K S^T on MFMA while the
-    // VALU scales S by gamma_C and stages V; R = V - c1 X; V, c1, gamma_C of step n+1
-    // load; the state and R go to the ring; K of step n+2 loads; S^T += Z^T R on MFMA.
-    // Each load reuses registers whose last reader has completed (K after R, which
-    // depends on every X MFMA; Z after the Pb conversion, which depends on every
-    // state-update MFMA; V and the scales after R).
     const StepRows kr{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.k) + (int64_t)b * p.ks[0] +
                                                     (int64_t)h * p.ks[2]),
                       p.ks[1] * 2, T, C, N, dir, 2 * D};
     const StepRows vr{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.v) + (int64_t)b * p.vs[0] +
                                                     (int64_t)h * p.vs[2]),
                       p.vs[1] * 2, T, C, N, dir, 2 * D};
-    int krow[NB];
-#pragma unroll
-    for (int mt = 0; mt < NB; ++mt) krow[mt] = kr.row(16 * mt + r);
-    bool col_ok[GDN_COLS];
-#pragma unroll
-    for (int c = 0; c < GDN_COLS; ++c) col_ok[c] = row0 + 16 * c < p.Dv;
-    // each lane stages the V row of token `lane` (rows >= C duplicate real ones, unused)
-    const int voff = vr.row(lane & (C - 1)) + 2 * row0;
-
-    Rows<NB, ND> kA, kB;
-    VIn<NB> vi;
-    uint4 zfr[ND][NKT];
     // the items of this (direction, b, h), addressed with lane-constant offsets
     const auto irs = make_rsrc(item0, (uint32_t)(N * ib));
-    auto load_v = [&](int n) {   // V rows and scales of step n
-        const auto rs = vr.rsrc(n);
-#pragma unroll
-        for (int cc = 0; cc < GDN_COLS; ++cc) {
-            if (col_ok[cc]) {
-                vi.v[cc][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 32 * cc, 0));
-                vi.v[cc][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 32 * cc + 16, 0));
-            } else {
-                vi.v[cc][0] = vi.v[cc][1] = uint4{0u, 0u, 0u, 0u};
-            }
-        }
-        const int ioff = n * (int)ib;
-#pragma unroll
-        for (int mt = 0; mt < NB; ++mt)
-            vi.c1[mt] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(irs, 64 * mt + 16 * g,
-                                                                                         ioff + SCAL_OFF, 0));
-        vi.gC = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(irs, 0, ioff + SCAL_OFF + 8 * C, 0));
-    };
-    auto load_z = [&](int n) {   // state-update operator of step n
-        const int ioff = n * (int)ib;
-#pragma unroll
-        for (int m = 0; m < ND; ++m)
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt)
-                zfr[m][kt] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                           irs, 16 * lane, ioff + 1024 * (BK::TOTAL + m * NKT + kt), 0));
-    };
 
-    // state slice, transposed: P[m][c][i] = S[row0 + 16 c + r][dperm(m, 4 g + i)]
-    f32x4 P[ND][GDN_COLS];
-    const float* Sin = (dir == 0) ? p.S_in : nullptr;
-    const int64_t hbase = ((int64_t)b * p.H + h) * D * D;
+    // roles: waves 0 .. GDN_COLS-1 chain, then the output wavefronts, then the two
+    // loaders (which share SIMDs with the chain wavefronts and move data without VGPRs)
+    if (wave >= GDN_COLS + NOUT) {
+        // ------------------------------ loader wavefronts ------------------------------
+        // Deposit the chain's operands of step n in slot n % GDN_OPS once both chain
+        // wavefronts have released that slot, with direct global-to-LDS loads, and publish
+        // a step once its loads have landed (each keeps the next step's loads in flight).
+        // Loader 0 moves K, V and the scales, loader 1 the state-update fragments Z.
+        const int part = wave - (GDN_COLS + NOUT);
+        int krow[NB];
 #pragma unroll
-    for (int m = 0; m < ND; ++m)
-#pragma unroll
-        for (int c = 0; c < GDN_COLS; ++c) {
-            if (Sin && col_ok[c])
-                P[m][c] = *reinterpret_cast<const f32x4*>(Sin + hbase + (int64_t)(row0 + 16 * c + r) * D + dperm<ND>(m, 4 * g));
-            else
-                P[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-
-    load_v(0);
-    load_rows(kA, kr.rsrc(0), krow, g);
-    load_rows(kB, kr.rsrc(N > 1 ? 1 : 0), krow, g);
-    auto chain_step = [&](Rows<NB, ND>& kc, int n) {
-        const int sl = n % GDN_RING;
-        // state as bf16 operand: k-slot e of lane group g <-> d = dperm(2 ks + e/4, 4 g + e%4)
-        bf16x8 Pb[NKD][GDN_COLS];
-#pragma unroll
-        for (int cc = 0; cc < GDN_COLS; ++cc) {
-#pragma unroll
-            for (int ks = 0; ks < ND / 2; ++ks)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    Pb[ks][cc][i] = (bf16)P[2 * ks][cc][i];
-                    Pb[ks][cc][4 + i] = (bf16)P[2 * ks + 1][cc][i];
-                }
-            if constexpr (ND % 2) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    Pb[NKD - 1][cc][i] = (bf16)P[ND - 1][cc][i];
-                    Pb[NKD - 1][cc][4 + i] = (bf16)0.f;
-                }
-            }
-        }
-        // Pb depends on every state-update MFMA of the previous step: Z may be reloaded
-#pragma unroll
-        for (int ks = 0; ks < NKD; ++ks)
-#pragma unroll
-            for (int cc = 0; cc < GDN_COLS; ++cc) keep_alive(Pb[ks][cc]);
-        __builtin_amdgcn_sched_barrier(0);
-        load_z(n);
-        // X = K S^T (rows: tokens 16 mt + 4 g + i, column: state row 16 cc + r)
-        f32x4 X[NB][GDN_COLS];
-#pragma unroll
-        for (int mt = 0; mt < NB; ++mt)
-#pragma unroll
-            for (int cc = 0; cc < GDN_COLS; ++cc) X[mt][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < NKD; ++ks)
+        for (int mt = 0; mt < NB; ++mt) krow[mt] = kr.row(16 * mt + r);
+        const int voff = vr.row(lane & (C - 1)) + 2 * row0;   // rows >= C duplicate real ones, unused
+        const int scoff = lane < 16 ? 16 * lane : (lane == 16 ? 8 * C : 0);
+        auto issue0 = [&](int n) {
+            ScanOps<NB, ND>& op = L.ops[n % GDN_OPS];
+            const auto krs = kr.rsrc(n);
 #pragma unroll
             for (int mt = 0; mt < NB; ++mt) {
-                const bf16x8 ka = __builtin_bit_cast(bf16x8, kc.op[mt][ks]);
 #pragma unroll
-                for (int cc = 0; cc < GDN_COLS; ++cc) X[mt][cc] = mma_bf16_k32(ka, Pb[ks][cc], X[mt][cc]);
+                for (int ks = 0; ks < NKF; ++ks) dma16(krs, &op.k[mt][ks][0], krow[mt] + 16 * g, 64 * ks);
+                // the trailing tile needs 8 bytes per lane; the upper 8 are not used (and read
+                // the next row, or zero past the end of the tensor)
+                if constexpr (ND % 2) dma16(krs, &op.kh[mt][0], krow[mt] + 8 * g, 32 * (ND - 1));
             }
-        // meanwhile: decay the state, stage V in LDS and read it back transposed
-        // (lane quad q of group g supplies row 16 mt + 4 g + i, columns 16 cc + 4q .. +3)
+            const auto vrs = vr.rsrc(n);
+#pragma unroll
+            for (int jj = 0; jj < 2 * GDN_COLS; ++jj)
+                // a column tile past d_v reads as zero (empty resource)
+                dma16(col_ok[jj / 2] ? vrs : make_rsrc(vr.base, 0u), &op.v[jj][0], voff, 16 * jj);
+            dma16(irs, &op.sc[0], scoff, n * (int)ib + SCAL_OFF);
+        };
+        auto issue1 = [&](int n) {
+            ScanOps<NB, ND>& op = L.ops[n % GDN_OPS];
+            const int ioff = n * (int)ib;
+#pragma unroll
+            for (int m = 0; m < ND; ++m)
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt)
+                    dma16(irs, &op.z[m][kt][0], 16 * lane, ioff + 1024 * (BK::TOTAL + m * NKT + kt));
+        };
+        // The direct loads complete in order and count on the vector memory counter;
+        // once it has dropped to this step's count, the previous step's data is in LDS.
+        for (int n = 0; n < N; ++n) {
+#pragma unroll
+            for (int c = 0; c < GDN_COLS; ++c) wait_counter(&K.released[c], n + 1 - GDN_OPS);
+            if (part == 0) {
+                issue0(n);
+                if (n > 0) wait_vmcnt<(NDMA0 < 63 ? NDMA0 : 63)>();   // step n - 1 has landed
+            } else {
+                issue1(n);
+                if (n > 0) wait_vmcnt<(NDMA1 < 63 ? NDMA1 : 63)>();
+            }
+            if (n > 0) publish_loaded(&K.loaded[part], n);
+        }
+        wait_vmcnt<0>();
+        publish_loaded(&K.loaded[part], N);
+        return;
+    }
+    if (wave == GDN_COLS) {
+        scan_output<NB, ND, 0>(p, L, K, lane, b, h, dir, T, N, row0, item0, ib);
+        return;
+    }
+    if constexpr (NOUT > 1) {
+        if (wave == GDN_COLS + 1) {
+            scan_output<NB, ND, 1>(p, L, K, lane, b, h, dir, T, N, row0, item0, ib);
+            return;
+        }
+    }
+
+    // ------------------------------ chain wavefronts ------------------------------
+    // Chain wavefront cc owns state rows row0 + 16 cc .. +15.  Per step n: wait for the
+    // step's operands; Pb = bf16(S); read K, the scales and Z from the operand slot;
+    // X = K S^T on MFMA while the VALU decays the state and reads V back transposed;
+    // R = V - c1 X; release the slot; publish the state and R to the output ring;
+    // S^T += Z^T R on MFMA.
+    const int cc = wave;
+    const bool tile_ok = row0 + 16 * cc < p.Dv;
+    f32x4 P[ND];   // P[m][i] = S[row0 + 16 cc + r][dperm(m, 4 g + i)]
+    const float* Sin = (dir == 0) ? p.S_in : nullptr;
+    const int64_t hbase = ((int64_t)b * p.H + h) * D * D;
+    const int64_t srow = hbase + (int64_t)(row0 + 16 * cc + r) * D;
+#pragma unroll
+    for (int m = 0; m < ND; ++m) {
+        if (Sin && tile_ok)
+            P[m] = *reinterpret_cast<const f32x4*>(Sin + srow + dperm<ND>(m, 4 * g));
+        else
+            P[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+#pragma unroll 1
+    for (int n = 0; n < N; ++n) {
+        const int sl = n % GDN_RING;
+        wait_counter(&K.loaded[0], n + 1);
+        wait_counter(&K.loaded[1], n + 1);
+        const ScanOps<NB, ND>& op = L.ops[n % GDN_OPS];
+        // state as bf16 operand: k-slot e of lane group g <-> d = dperm(2 ks + e/4, 4 g + e%4)
+        bf16x8 Pb[NKD];
+#pragma unroll
+        for (int ks = 0; ks < NKF; ++ks)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                Pb[ks][i] = (bf16)P[2 * ks][i];
+                Pb[ks][4 + i] = (bf16)P[2 * ks + 1][i];
+            }
+        if constexpr (ND % 2) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                Pb[NKD - 1][i] = (bf16)P[ND - 1][i];
+                Pb[NKD - 1][4 + i] = (bf16)0.f;
+            }
+        }
+        // operands of the step (in order of use)
+        uint4 kf[NB][NKD];
+#pragma unroll
+        for (int mt = 0; mt < NB; ++mt) {
+#pragma unroll
+            for (int ks = 0; ks < NKF; ++ks) kf[mt][ks] = op.k[mt][ks][lane];
+            if constexpr (ND % 2) {
+                const uint4 t4 = op.kh[mt][lane];
+                kf[mt][NKF] = uint4{t4.x, t4.y, 0u, 0u};
+            }
+        }
+        f32x4 c1[NB];
+#pragma unroll
+        for (int mt = 0; mt < NB; ++mt) c1[mt] = __builtin_bit_cast(f32x4, op.sc[4 * mt + g]);
+        const float gC = __builtin_bit_cast(f32x4, op.sc[16]).x;
+        uint4 zfr[ND][NKT];
 #pragma unroll
         for (int m = 0; m < ND; ++m)
 #pragma unroll
-            for (int cc = 0; cc < GDN_COLS; ++cc) P[m][cc] = P[m][cc] * vi.gC;
+            for (int kt = 0; kt < NKT; ++kt) zfr[m][kt] = op.z[m][kt][lane];
+        // X = K S^T (rows: tokens 16 mt + 4 g + i, column: state row 16 cc + r)
+        f32x4 X[NB];
 #pragma unroll
-        for (int cc = 0; cc < GDN_COLS; ++cc) {
-            *reinterpret_cast<uint4*>(L.Vs + 40 * lane + 16 * cc) = vi.v[cc][0];
-            *reinterpret_cast<uint4*>(L.Vs + 40 * lane + 16 * cc + 8) = vi.v[cc][1];
-        }
-        bf16x4 vt[NB][GDN_COLS];
-#pragma unroll
-        for (int mt = 0; mt < NB; ++mt)
-#pragma unroll
-            for (int cc = 0; cc < GDN_COLS; ++cc)
-                vt[mt][cc] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                                            (__attribute__((address_space(3))) s16x4*)(
-                                                                L.Vs + 40 * (16 * mt + 4 * g + (r >> 2)) + 16 * cc + 4 * (r & 3))));
-        // R = V - diag(e^g / |k|) X, as fp16 B operand (k = token)
-        f16x8 Rb[NKT][GDN_COLS];
-#pragma unroll
-        for (int mt = 0; mt < NB; ++mt)
-#pragma unroll
-            for (int cc = 0; cc < GDN_COLS; ++cc)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    Rb[mt >> 1][cc][4 * (mt & 1) + i] = (f16)((float)vt[mt][cc][i] - vi.c1[mt][i] * X[mt][cc][i]);
-        if constexpr (HT) {
-#pragma unroll
-            for (int cc = 0; cc < GDN_COLS; ++cc)
-#pragma unroll
-                for (int i = 4; i < 8; ++i) Rb[NFT][cc][i] = (f16)0.f;
-        }
-        // R depends on every X MFMA and on V and c1 of this step: those registers are free
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-            for (int cc = 0; cc < GDN_COLS; ++cc) keep_alive(Rb[kt][cc]);
-        __builtin_amdgcn_sched_barrier(0);
-        load_v(n + 1 < N ? n + 1 : N - 1);
-        // publish the step's state and R once every output wavefront has released the slot
-#pragma unroll
-        for (int o = 0; o < NOUT; ++o) wait_counter(&L.done[o], n + 1 - GDN_RING);
+        for (int mt = 0; mt < NB; ++mt) X[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < NKD; ++ks)
 #pragma unroll
-            for (int cc = 0; cc < GDN_COLS; ++cc) L.ringP[sl][ks][cc][lane] = __builtin_bit_cast(uint4, Pb[ks][cc]);
+            for (int mt = 0; mt < NB; ++mt) X[mt] = mma_bf16_k32(__builtin_bit_cast(bf16x8, kf[mt][ks]), Pb[ks], X[mt]);
+        // meanwhile: decay the state; read V back transposed (lane quad q of group g
+        // supplies row 16 mt + 4 g + i, columns 16 cc + 4 q .. +3 of the deposited rows)
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
+        for (int m = 0; m < ND; ++m) P[m] = P[m] * gC;
+        bf16x4 vt[NB];
 #pragma unroll
-            for (int cc = 0; cc < GDN_COLS; ++cc) L.ringR[sl][kt][cc][lane] = __builtin_bit_cast(uint4, Rb[kt][cc]);
-        signal_counter(&L.ready, n + 1);
+        for (int mt = 0; mt < NB; ++mt) {
+            const int q = r & 3, t = 16 * mt + 4 * g + (r >> 2);
+            const char* vp = reinterpret_cast<const char*>(&op.v[2 * cc + (q >> 1)][0]) + 16 * t + 8 * (q & 1);
+            vt[mt] = __builtin_bit_cast(
+                bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)vp));
+        }
+        // R = V - diag(e^g / |k|) X, as fp16 B operand (k = token)
+        f16x8 Rb[NKT];
+#pragma unroll
+        for (int mt = 0; mt < NB; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Rb[mt >> 1][4 * (mt & 1) + i] = (f16)((float)vt[mt][i] - c1[mt][i] * X[mt][i]);
+        if constexpr (HT) {
+#pragma unroll
+            for (int i = 4; i < 8; ++i) Rb[NFT][i] = (f16)0.f;
+        }
+        // every read of the operand slot has completed: release it to the loader
+#pragma unroll
+        for (int m = 0; m < ND; ++m)
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) keep_alive(__builtin_bit_cast(u32x4, zfr[m][kt]));
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) keep_alive(Rb[kt]);
+        signal_counter(&K.released[cc], n + 1);
+        // publish the step's state and R once every output wavefront has released the slot
+#pragma unroll
+        for (int o = 0; o < NOUT; ++o) wait_counter(&K.done[o], n + 1 - GDN_RING);
+#pragma unroll
+        for (int ks = 0; ks < NKD; ++ks) L.ringP[sl][ks][cc][lane] = __builtin_bit_cast(uint4, Pb[ks]);
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) L.ringR[sl][kt][cc][lane] = __builtin_bit_cast(uint4, Rb[kt]);
+        signal_counter(&K.ready[cc], n + 1);
         __builtin_amdgcn_sched_barrier(0);
-        load_rows(kc, kr.rsrc(n + 2 < N ? n + 2 : N - 1), krow, g);
         // S^T <- gamma_C S^T + Z^T R  (rows d, columns: state rows); a trailing 16-token
         // step has zero upper slots in both operands
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-            for (int m = 0; m < ND; ++m) {
-                const f16x8 za = __builtin_bit_cast(f16x8, zfr[m][kt]);
-#pragma unroll
-                for (int cc = 0; cc < GDN_COLS; ++cc) P[m][cc] = mma_f16_k32(za, Rb[kt][cc], P[m][cc]);
-            }
-    };
-    // The prefetches are unconditional (the last steps reload step N-1) so that
-    // every path through the loop has the same loads in flight.
-    int n = 0;
-    for (; n + 1 < N; n += 2) {
-        chain_step(kA, n);
-        chain_step(kB, n + 1);
+            for (int m = 0; m < ND; ++m) P[m] = mma_f16_k32(__builtin_bit_cast(f16x8, zfr[m][kt]), Rb[kt], P[m]);
     }
-    if (n < N) chain_step(kA, n);
     float* Sout = p.S_out[dir];
-    if (Sout) {
+    if (Sout && tile_ok) {
 #pragma unroll
-        for (int m = 0; m < ND; ++m)
-#pragma unroll
-            for (int c = 0; c < GDN_COLS; ++c)
-                if (col_ok[c])
-                    *reinterpret_cast<f32x4*>(Sout + hbase + (int64_t)(row0 + 16 * c + r) * D + dperm<ND>(m, 4 * g)) = P[m][c];
+        for (int m = 0; m < ND; ++m) *reinterpret_cast<f32x4*>(Sout + srow + dperm<ND>(m, 4 * g)) = P[m];
     }
 }
 
@@ -1186,7 +1229,7 @@ template <int NB, int ND>
 static hipError_t run_chunked(const Params& p, hipStream_t s, Timing* tm) {
     const int nsub = (int)((p.T + 16 * NB - 1) / (16 * NB));
     tm_begin(tm, s, KPREP);
-    hipLaunchKernelGGL((gdn_prep_kernel<NB, ND>), dim3(nsub, p.B * p.H, p.ndirs), dim3(64 * NB), 0, s, p);
+    hipLaunchKernelGGL((gdn_prep_kernel<NB, ND>), dim3(nsub, p.B * p.H, p.ndirs), dim3(128 * NB), 0, s, p);
     tm_end(tm, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
