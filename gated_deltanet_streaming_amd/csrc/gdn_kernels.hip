@@ -268,6 +268,25 @@ struct TokMap {
 };
 
 
+// Compact LDS storage of the C x C matrices of a step by 16x16 blocks: only the
+// blocks on one side of the diagonal are kept (rows padded to 16-byte multiples).
+template <int NB, int LD_>
+struct UpperF32 {   // fp32 blocks (a, b) with a <= b (L^T and T^T), rows of LD_ floats
+    static constexpr int LD = LD_, COUNT = NB * (NB + 1) / 2, FLOATS = COUNT * 16 * LD;
+    __device__ static int at(int row, int col) {
+        const int a = row >> 4, b = col >> 4;
+        return (a * NB - (a * (a - 1)) / 2 + (b - a)) * (16 * LD) + (row & 15) * LD + (col & 15);
+    }
+};
+template <int NB>
+struct LowerF16 {   // fp16 blocks (a, b) with a >= b (A), rows of 24 halves
+    static constexpr int LD = 24, COUNT = NB * (NB + 1) / 2, HALVES = COUNT * 16 * LD;
+    __device__ static int at(int row, int col) {
+        const int a = row >> 4, b = col >> 4;
+        return ((a * (a + 1)) / 2 + b) * (16 * LD) + (row & 15) * LD + (col & 15);
+    }
+};
+
 // ---------------------------------------------------------------------------
 // Chunk preparation: one workgroup (2 NB wavefronts) per (direction, b, h,
 // processing step n).  Rows are in processing order.  For the C tokens of the
@@ -282,11 +301,12 @@ struct TokMap {
 // d of Z^T follows the scan's state order (see dperm).
 // ---------------------------------------------------------------------------
 template <int NB, int ND>
-__global__ __launch_bounds__(128 * NB) void gdn_prep_kernel(Params p) {
+__global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(6))) void gdn_prep_kernel(Params p) {
     constexpr int C = 16 * NB, D = 16 * ND;
     constexpr int LDR = D + 8;   // bf16 row stride of the staged K and Q rows (8-byte aligned rows)
-    constexpr int LDM = C + 4;   // fp32 row stride of L^T, T^T (16-byte aligned rows)
-    constexpr int LDA = C + 8;   // fp16 row stride of A (16-byte aligned rows)
+    using UL = UpperF32<NB, 16>; // L^T (read by rows or 64 consecutive floats)
+    using UB = UpperF32<NB, 20>; // T^T (also read down columns: padded rows)
+    using LB = LowerF16<NB>;     // A
     constexpr int NW = 2 * NB;   // wavefronts
     constexpr int NT = 64 * NW;
     constexpr int CH = D / 8;    // 16-byte chunks per row
@@ -297,11 +317,11 @@ __global__ __launch_bounds__(128 * NB) void gdn_prep_kernel(Params p) {
     typedef short s16x4 __attribute__((ext_vector_type(4)));
 
     // Q rows (bf16) share storage with T^T (fp32), which is built after the Gram products
-    constexpr int Q_BYTES = C * LDR * 2, T_BYTES = C * LDM * 4;
+    constexpr int Q_BYTES = C * LDR * 2, T_BYTES = UB::FLOATS * 4;
     __shared__ __align__(16) bf16 Ks[C * LDR];
     __shared__ __align__(16) char QT[Q_BYTES > T_BYTES ? Q_BYTES : T_BYTES];
-    __shared__ __align__(16) float Lt[C * LDM];   // L transposed: Lt[s][t] = L[t][s], s < t
-    __shared__ __align__(16) f16 Am[C * LDA];     // A[t][s] (an fp16 operand of E only)
+    __shared__ __align__(16) float Lt[UL::FLOATS];   // L transposed: Lt[s][t] = L[t][s], s < t
+    __shared__ __align__(16) f16 Am[LB::HALVES];     // A[t][s], s <= t (an fp16 operand of E only)
     __shared__ __align__(16) float sc[5][C];      // 0: log a then g, 1: beta, 2: 1/|k|, 3: 1/|q|, 4: e^{g_C-g}/|k|
     bf16* Qs = reinterpret_cast<bf16*>(QT);
     float* Tt = reinterpret_cast<float*>(QT);     // T transposed: Tt[u][s] = T[s][u]
@@ -410,9 +430,9 @@ __global__ __launch_bounds__(128 * NB) void gdn_prep_kernel(Params p) {
                 const int t = t0 + i;
                 const float dec = (s <= t) ? __expf(gt[i] - gs) : 0.f;
                 if (!isq)
-                    Lt[s * LDM + t] = (s < t) ? bt[i] * dec * rt[i] * rs * acc[i] : 0.f;
+                    Lt[UL::at(s, t)] = (s < t) ? bt[i] * dec * rt[i] * rs * acc[i] : 0.f;
                 else
-                    Am[t * LDA + s] = (f16)((s <= t) ? p.scale * dec * rt[i] * rs * acc[i] : 0.f);
+                    Am[LB::at(t, s)] = (f16)((s <= t) ? p.scale * dec * rt[i] * rs * acc[i] : 0.f);
             }
 #pragma unroll
             for (int ks = 0; ks < ND / 2; ++ks) {
@@ -437,7 +457,7 @@ __global__ __launch_bounds__(128 * NB) void gdn_prep_kernel(Params p) {
         for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
 #pragma unroll
         for (int k = 0; k < 15; ++k) {
-            const float* lcol = Lt + (o + k) * LDM + o;   // L[o + i][o + k] for i > k
+            const float* lcol = Lt + UL::at(o + k, o);   // L[o + i][o + k] for i > k
             float lv[16];
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
@@ -450,7 +470,7 @@ __global__ __launch_bounds__(128 * NB) void gdn_prep_kernel(Params p) {
         }
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4)
-            *reinterpret_cast<f32x4*>(Tt + (o + j) * LDM + o + 4 * i4) =
+            *reinterpret_cast<f32x4*>(Tt + UB::at(o + j, o) + 4 * i4) =
                 f32x4{x[4 * i4], x[4 * i4 + 1], x[4 * i4 + 2], x[4 * i4 + 3]};
     }
     __syncthreads();
@@ -465,8 +485,8 @@ __global__ __launch_bounds__(128 * NB) void gdn_prep_kernel(Params p) {
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
                     const int k = 16 * kb + 4 * kk + g;
-                    la[kk] = Lt[k * LDM + 16 * ib + r];      // L[16 ib + r][k]
-                    tb[kk] = Tt[(16 * jb + r) * LDM + k];     // T[k][16 jb + r]
+                    la[kk] = Lt[UL::at(k, 16 * ib + r)];      // L[16 ib + r][k]
+                    tb[kk] = Tt[UB::at(16 * jb + r, k)];      // T[k][16 jb + r]
                 }
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) z = __builtin_amdgcn_mfma_f32_16x16x4f32(la[kk], tb[kk], z, 0, 0, 0);
@@ -481,12 +501,12 @@ __global__ __launch_bounds__(128 * NB) void gdn_prep_kernel(Params p) {
             // z: lane (column r, group g) holds Z[4g + e][r]; B operand with k = 4g + kk
             float ta[4];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) ta[kk] = Tt[(16 * ib + 4 * g + kk) * LDM + 16 * ib + r];   // T[16 ib + r][16 ib + 4g + kk]
+            for (int kk = 0; kk < 4; ++kk) ta[kk] = Tt[UB::at(16 * ib + 4 * g + kk, 16 * ib + r)];   // T[16 ib + r][16 ib + 4g + kk]
             f32x4 t4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) t4 = __builtin_amdgcn_mfma_f32_16x16x4f32(ta[kk], z[kk], t4, 0, 0, 0);
             // T[16 ib + 4g + e][16 jb + r] -> Tt[16 jb + r][16 ib + 4g + e]
-            *reinterpret_cast<f32x4*>(Tt + (16 * jb + r) * LDM + 16 * ib + 4 * g) = -t4;
+            *reinterpret_cast<f32x4*>(Tt + UB::at(16 * jb + r, 16 * ib + 4 * g)) = -t4;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) keep_alive(ta[kk]);
         }
@@ -512,8 +532,8 @@ __global__ __launch_bounds__(128 * NB) void gdn_prep_kernel(Params p) {
             if (ut <= mt) {
                 // contraction over s in 32-wide steps (zero outside the triangle)
                 for (int ss = (16 * ut) / 32; ss * 32 < 16 * (mt + 1); ++ss) {
-                    const float* ta = Tt + (16 * ut + r) * LDM + 32 * ss + 8 * g;
-                    const f16* aa = Am + (16 * mt + r) * LDA + 32 * ss + 8 * g;
+                    const float* ta = Tt + UB::at(16 * ut + r, 32 * ss + 8 * g);
+                    const f16* aa = Am + LB::at(16 * mt + r, 32 * ss + 8 * g);
                     f16x8 ao, bo;
                     const int sb = 2 * ss + (g >> 1);   // 16-wide block of this lane's s
                     if (32 * ss + 8 * g < C && sb >= ut && sb <= mt) {
@@ -563,14 +583,13 @@ __global__ __launch_bounds__(128 * NB) void gdn_prep_kernel(Params p) {
             if (mt < NB) {
                 for (int ss = mt / 2; ss < NKT; ++ss) {
                     // A: Tt[t][s] * wk[s], s = 32 ss + 16 (i/4) + 4 g + i%4
-                    const float* ta = Tt + (16 * mt + r) * LDM + 32 * ss + 4 * g;
                     bf16x8 ahi, alo;
 #pragma unroll
                     for (int hf = 0; hf < 2; ++hf) {
                         const int s0 = 32 * ss + 16 * hf + 4 * g;
                         f32x4 tv = {0.f, 0.f, 0.f, 0.f}, wv = {0.f, 0.f, 0.f, 0.f};
                         if (s0 < C && 2 * ss + hf >= mt) {   // T[s][t] = 0 for s < t
-                            tv = *reinterpret_cast<const f32x4*>(ta + 16 * hf);
+                            tv = *reinterpret_cast<const f32x4*>(Tt + UB::at(16 * mt + r, s0));
                             wv = *reinterpret_cast<const f32x4*>(&sc[4][s0]);
                         }
 #pragma unroll
@@ -750,10 +769,10 @@ struct ScanLds {
 // direct global-to-LDS loads in flight.
 template <int NB>
 struct ScanCtr {
-    int ready[GDN_COLS];                 // steps each chain wavefront has published to the output ring
+    int ready[GDN_COLS];                 // steps each chain wavefront has published to the output
+                                         // ring (and so finished reading from the operand slots)
     int done[ScanShape<NB>::NOUT];       // steps each output wavefront has taken from the ring
-    int loaded[2];                       // steps whose operands each loader has landed in the slots
-    int released[GDN_COLS];              // steps whose operands each chain wavefront has read
+    int loaded[2];                       // steps whose operands loader 0 / both loaders have landed
 };
 
 // Direct global-to-LDS load of 16 bytes per lane into a wave-uniform LDS block.
@@ -963,7 +982,7 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
 
     if (threadIdx.x == 0) {
 #pragma unroll
-        for (int c = 0; c < GDN_COLS; ++c) K.ready[c] = K.released[c] = 0;
+        for (int c = 0; c < GDN_COLS; ++c) K.ready[c] = 0;
 #pragma unroll
         for (int o = 0; o < NOUT; ++o) K.done[o] = 0;
         K.loaded[0] = K.loaded[1] = 0;
@@ -984,9 +1003,10 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
     if (wave >= GDN_COLS + NOUT) {
         // ------------------------------ loader wavefronts ------------------------------
         // Deposit the chain's operands of step n in slot n % GDN_OPS once both chain
-        // wavefronts have released that slot, with direct global-to-LDS loads, and publish
+        // wavefronts are done with that slot, with direct global-to-LDS loads, and publish
         // a step once its loads have landed (each keeps the next step's loads in flight).
-        // Loader 0 moves K, V and the scales, loader 1 the state-update fragments Z.
+        // Loader 0 moves K, V and the scales, loader 1 the state-update fragments Z;
+        // loader 1 publishes a step for the chain only once loader 0 has landed it too.
         const int part = wave - (GDN_COLS + NOUT);
         int krow[NB];
 #pragma unroll
@@ -1024,17 +1044,24 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
         // once it has dropped to this step's count, the previous step's data is in LDS.
         for (int n = 0; n < N; ++n) {
 #pragma unroll
-            for (int c = 0; c < GDN_COLS; ++c) wait_counter(&K.released[c], n + 1 - GDN_OPS);
+            for (int c = 0; c < GDN_COLS; ++c) wait_counter(&K.ready[c], n + 1 - GDN_OPS);
             if (part == 0) {
                 issue0(n);
-                if (n > 0) wait_vmcnt<(NDMA0 < 63 ? NDMA0 : 63)>();   // step n - 1 has landed
+                if (n > 0) {
+                    wait_vmcnt<(NDMA0 < 63 ? NDMA0 : 63)>();   // step n - 1 has landed
+                    publish_loaded(&K.loaded[0], n);
+                }
             } else {
                 issue1(n);
-                if (n > 0) wait_vmcnt<(NDMA1 < 63 ? NDMA1 : 63)>();
+                if (n > 0) {
+                    wait_vmcnt<(NDMA1 < 63 ? NDMA1 : 63)>();
+                    wait_counter(&K.loaded[0], n);
+                    publish_loaded(&K.loaded[1], n);
+                }
             }
-            if (n > 0) publish_loaded(&K.loaded[part], n);
         }
         wait_vmcnt<0>();
+        if (part == 1) wait_counter(&K.loaded[0], N);
         publish_loaded(&K.loaded[part], N);
         return;
     }
@@ -1069,10 +1096,12 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
             P[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
+    int done_seen[NOUT];
+#pragma unroll
+    for (int o = 0; o < NOUT; ++o) done_seen[o] = 0;
 #pragma unroll 1
     for (int n = 0; n < N; ++n) {
         const int sl = n % GDN_RING;
-        wait_counter(&K.loaded[0], n + 1);
         wait_counter(&K.loaded[1], n + 1);
         const ScanOps<NB, ND>& op = L.ops[n % GDN_OPS];
         // state as bf16 operand: k-slot e of lane group g <-> d = dperm(2 ks + e/4, 4 g + e%4)
@@ -1141,17 +1170,22 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
 #pragma unroll
             for (int i = 4; i < 8; ++i) Rb[NFT][i] = (f16)0.f;
         }
-        // every read of the operand slot has completed: release it to the loader
+        // every read of the operand slot has completed (the signal below also releases it
+        // to the loaders)
 #pragma unroll
         for (int m = 0; m < ND; ++m)
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt) keep_alive(__builtin_bit_cast(u32x4, zfr[m][kt]));
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) keep_alive(Rb[kt]);
-        signal_counter(&K.released[cc], n + 1);
         // publish the step's state and R once every output wavefront has released the slot
+        // (the last counts seen are kept, so the counters are read only when needed)
 #pragma unroll
-        for (int o = 0; o < NOUT; ++o) wait_counter(&K.done[o], n + 1 - GDN_RING);
+        for (int o = 0; o < NOUT; ++o)
+            if (done_seen[o] < n + 1 - GDN_RING) {
+                wait_counter(&K.done[o], n + 1 - GDN_RING);
+                done_seen[o] = __hip_atomic_load(&K.done[o], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
 #pragma unroll
         for (int ks = 0; ks < NKD; ++ks) L.ringP[sl][ks][cc][lane] = __builtin_bit_cast(uint4, Pb[ks]);
 #pragma unroll
