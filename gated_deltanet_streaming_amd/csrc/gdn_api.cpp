@@ -27,10 +27,13 @@ struct gdn_stream {
     bool chunked_ok;      // chunked kernels exist for this shape and dtype
     float* state;         // [B, H, d_v, d_k]
     int64_t state_elems;
-    char* ws;             // chunked workspace: [2 directions][B][H][nsub_max] items
+    char* ws;             // chunked workspace: [2 directions][B][H][nsub_max] items, then the
+                          // K / Q fragment area
     __bf16* conv;         // fp32 I/O with the chunked kernels: bf16 staging of q, k, v
     int64_t item_bytes;
     int nsub_max;
+    int64_t items_total;  // bytes of the items (the fragment area follows)
+    int ntile_max;
     // optional per-kernel timing
     bool profile;
     std::vector<std::pair<hipEvent_t, hipEvent_t>> pend;
@@ -157,6 +160,8 @@ gdn::Params base_params(gdn_stream* s, const gdn_io* io, int64_t T) {
     p.nsub_max = s->nsub_max;
     p.C = s->C;
     p.conv = s->conv;
+    p.frag = s->ws ? s->ws + s->items_total : nullptr;
+    p.ntile_max = s->ntile_max;
     return p;
 }
 
@@ -264,10 +269,14 @@ GDN_API int gdn_stream_init(const gdn_config* cfg, int device, gdn_stream** out)
     s->conv = nullptr;
     s->item_bytes = 0;
     s->nsub_max = 0;
+    s->items_total = 0;
+    s->ntile_max = 0;
     if (e == hipSuccess && s->chunked_ok) {
         s->item_bytes = gdn::chunk_item_bytes(C, c.d_k);
         s->nsub_max = (int)((c.max_tokens + C - 1) / C);
-        const int64_t bytes = 2 * (int64_t)c.batch * c.heads * s->nsub_max * s->item_bytes;
+        s->ntile_max = (int)((c.max_tokens + 15) / 16);
+        s->items_total = 2 * (int64_t)c.batch * c.heads * s->nsub_max * s->item_bytes;
+        const int64_t bytes = s->items_total + gdn::chunk_frag_bytes(c.d_k, c.max_tokens, c.batch, c.heads);
         e = hipMalloc(&s->ws, bytes);
         if (e != hipSuccess) {
             (void)hipFree(s->state);

@@ -33,10 +33,16 @@ struct Params {
     int nsub_max;
     int C;                 // sub-chunk length
     __bf16* conv;          // fp32 I/O only: bf16 copies of q, k, v ([3][B][T][H][D])
+    // K and Q rows as MFMA operand fragments, by 16-token tile in token order (shared by
+    // both directions): [2 (K, Q)][B][H][ntile_max][(D/16 + 1)/2 k-steps][64 lanes][16 B]
+    char* frag;
+    int ntile_max;
 };
 
 // Bytes of one workspace item for sub-chunk C (multiple of 16, 16..64).
 int64_t chunk_item_bytes(int C, int D);
+// Bytes of the fragment area for B streams, H heads and up to max_tokens tokens.
+int64_t chunk_frag_bytes(int D, int64_t max_tokens, int B, int H);
 
 // Which (C, D) pairs the chunked kernels are built for.
 bool chunked_supported(int C, int Dk, int Dv, int io_f32);

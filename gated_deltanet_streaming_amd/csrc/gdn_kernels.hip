@@ -155,6 +155,11 @@ int64_t chunk_item_bytes(int C, int D) {
     }
 }
 
+int64_t chunk_frag_bytes(int D, int64_t max_tokens, int B, int H) {
+    const int64_t nkd = (D / 16 + 1) / 2;
+    return 2 * (int64_t)B * H * ((max_tokens + 15) / 16) * nkd * 1024;
+}
+
 // ---------------------------------------------------------------------------
 // Token-sequential fp32 kernel.  Lane l owns state row 16*rb + l/4 and the
 // columns c = l%4 + 4i; row sums are reduced across the 4 lanes of a row.
@@ -268,6 +273,19 @@ struct TokMap {
 };
 
 
+// K and Q operand fragments by 16-token tile (token order).  Block (tile, ks) holds, for
+// lane r + 16 g, row 16 tile + r at d = 32 ks + 8 g .. +7 (16 bytes); a trailing single
+// tile of d (odd D/16) holds d = 16 (ND-1) + 4 g .. +3 and 8 zero bytes.  Processing tile mt
+// of step n is token tile frag_tile(); the reverse direction takes the tile's rows in
+// reverse order (processing row r is the tile's row 15 - r).
+__device__ __forceinline__ int frag_tile(int dir, int N, int NB, int n, int mt) {
+    return dir ? N * NB - 1 - NB * n - mt : NB * n + mt;
+}
+// fragments of (kind 0 = K / 1 = Q, b, h): base and bytes of the tiles that hold tokens
+__device__ __forceinline__ const char* frag_base(const Params& p, int kind, int b, int h, int nkd) {
+    return p.frag + (((int64_t)kind * p.B + b) * p.H + h) * p.ntile_max * nkd * 1024;
+}
+
 // Compact LDS storage of the C x C matrices of a step by 16x16 blocks: only the
 // blocks on one side of the diagonal are kept (rows padded to 16-byte multiples).
 template <int NB, int LD_>
@@ -361,6 +379,27 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(6))) v
         sc[1][tid] = bt;
     }
     __syncthreads();
+
+    // the operand fragments of this step's token tiles (written by one direction only)
+    if (dir == p.dir0) {
+        constexpr int NKD = (ND + 1) / 2, NKF = ND / 2;
+        const int ntile = (T + 15) / 16;
+        for (int job = w; job < 2 * NB * NKD; job += NW) {
+            const int kind = job / (NB * NKD), mt = (job / NKD) % NB, ks = job % NKD;
+            const int tile = frag_tile(dir, N, NB, n, mt);
+            if (tile >= ntile) continue;
+            const bf16* row = (kind ? Qs : Ks) + (16 * mt + (dir ? 15 - r : r)) * LDR;
+            uint4 v;
+            if (ks < NKF) {
+                v = *reinterpret_cast<const uint4*>(row + 32 * ks + 8 * g);
+            } else {
+                const uint2 hv = *reinterpret_cast<const uint2*>(row + 16 * (ND - 1) + 4 * g);
+                v = uint4{hv.x, hv.y, 0u, 0u};
+            }
+            char* dst = const_cast<char*>(frag_base(p, kind, b, h, NKD)) + ((int64_t)tile * NKD + ks) * 1024;
+            reinterpret_cast<uint4*>(dst)[lane] = v;
+        }
+    }
 
     // per-token inverse norms: 4 lanes per row, 16 rows per wavefront; waves < NB take the
     // K rows, the others the Q rows
@@ -677,7 +716,7 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(6))) v
 #define GDN_SPIN_LIMIT (1 << 22)
 
 template <int NT, int ND>
-struct Rows {                    // NT row tiles of K or Q (lane = row) as MFMA operands
+struct Rows {                    // NT row tiles of Q (lane = row) as MFMA operands
     uint4 op[NT][(ND + 1) / 2];  // [tile][ks]: 8 consecutive d; a trailing single tile holds 4 and zeros
 };
 
@@ -702,22 +741,6 @@ struct StepRows {
     // offset of local row t (processing order) from the step's lowest token
     __device__ __forceinline__ int row(int t) const { return (dir ? (C - 1 - t) : t) * (int)tstride; }
 };
-
-// Rows 16 mt + r of a step as operands: k-step ks < ND/2 takes d = 32 ks + 8 g .. +7
-// (one 16-byte load at byte 64 ks + 16 g), a trailing single tile d = 16 (ND-1) + 4 g .. +3.
-template <int NT, int ND>
-__device__ __forceinline__ void load_rows(Rows<NT, ND>& kk, __amdgpu_buffer_rsrc_t rs, const int (&row)[NT], int g) {
-#pragma unroll
-    for (int mt = 0; mt < NT; ++mt) {
-#pragma unroll
-        for (int ks = 0; ks < ND / 2; ++ks)
-            kk.op[mt][ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, row[mt] + 16 * g, 64 * ks, 0));
-        if constexpr (ND % 2) {
-            const uint2 t = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, row[mt] + 8 * g, 32 * (ND - 1), 0));
-            kk.op[mt][ND / 2] = uint4{t.x, t.y, 0u, 0u};
-        }
-    }
-}
 
 // Wait until an LDS counter written by another wavefront reaches `target`.
 // Bounded, so a wavefront can never hang here.
@@ -746,10 +769,9 @@ struct ScanShape {
 // so each block is one MFMA operand fragment read back with one 16-byte LDS read.
 template <int NB, int ND>
 struct ScanOps {
-    static constexpr int NKF = ND / 2;   // full 32-wide k-steps over d
+    static constexpr int NKD = (ND + 1) / 2;   // 32-wide k-steps over d (the last half-filled for odd ND)
     static constexpr int NKT = Blocks<NB>::NFULL + (Blocks<NB>::HALF ? 1 : 0);
-    uint4 k[NB][NKF > 0 ? NKF : 1][64];  // K rows 16 mt + r, d = 32 ks + 8 g .. +7
-    uint4 kh[(ND % 2) ? NB : 1][64];     // odd ND: d = 16 (ND-1) + 4 g .. +3 (low 8 bytes)
+    uint4 k[NB][NKD][64];                // K fragments of processing tile mt (as stored by the prep)
     uint4 z[ND][NKT][64];                // state-update fragments of the item
     uint4 v[2 * GDN_COLS][64];           // 16-byte chunk j of token `lane`'s V row slice
     uint4 sc[64];                        // lanes 0..15: c1 (64 floats); lane 16: gamma_C
@@ -813,19 +835,16 @@ __device__ __forceinline__ void scan_output(const Params& p, ScanLds<NB, ND>& L,
         float c2[TPO];
     };
 
-    const StepRows qr{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.q) + (int64_t)b * p.qs[0] +
-                                                    (int64_t)h * p.qs[2]),
-                      p.qs[1] * 2, T, C, N, dir, 2 * D};
+    // Q fragments (16 bytes per lane, the rows of a tile reversed for the reverse direction)
+    const auto qfr = make_rsrc(frag_base(p, 1, b, h, NKD), (uint32_t)(((T + 15) / 16) * NKD * 1024));
+    const int qfl = 16 * ((dir ? 15 - r : r) + 16 * g);
     // o is bf16, or fp32 when the call's I/O is fp32 (its q, k, v were staged as bf16)
     const int oesz = p.io_f32 ? 4 : 2;
     const StepRows orow{reinterpret_cast<const char*>(p.o[dir]) + ((int64_t)b * p.os[0] + (int64_t)h * p.os[2]) * oesz,
                         p.os[1] * oesz, T, C, N, dir, oesz * D};
-    int qrow[TPO], ooff[TPO];
+    int ooff[TPO];
 #pragma unroll
-    for (int tt = 0; tt < TPO; ++tt) {
-        qrow[tt] = qr.row(16 * (MT0 + tt) + r);
-        ooff[tt] = orow.row(16 * (MT0 + tt) + r) + oesz * (row0 + 4 * g);   // token, state rows row0 + 4g ..
-    }
+    for (int tt = 0; tt < TPO; ++tt) ooff[tt] = orow.row(16 * (MT0 + tt) + r) + oesz * (row0 + 4 * g);   // token, state rows row0 + 4g ..
     bool col_ok[GDN_COLS];
 #pragma unroll
     for (int c = 0; c < GDN_COLS; ++c) col_ok[c] = row0 + 16 * c < p.Dv;
@@ -833,7 +852,13 @@ __device__ __forceinline__ void scan_output(const Params& p, ScanLds<NB, ND>& L,
     OutIn oA, oB;
     const auto irs = make_rsrc(item0, (uint32_t)(N * ib));
     auto load_out = [&](OutIn& o, int n) {
-        load_rows(o.q, qr.rsrc(n), qrow, g);
+#pragma unroll
+        for (int tt = 0; tt < TPO; ++tt) {
+            const int tile = frag_tile(dir, N, NB, n, MT0 + tt);   // past the last token: zero
+#pragma unroll
+            for (int ks = 0; ks < NKD; ++ks)
+                o.q.op[tt][ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(qfr, qfl, (tile * NKD + ks) * 1024, 0));
+        }
         const int ioff = n * (int)ib;
 #pragma unroll
         for (int e = 0; e < EB; ++e)
@@ -950,7 +975,7 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
     constexpr int SCAL_OFF = 1024 * (BK::TOTAL + ND * NKT);   // scalars of an item
     constexpr int NOUT = ScanShape<NB>::NOUT;
     // loads the loader wavefronts issue per step: K, V and the scales; Z
-    constexpr int NDMA0 = NB * NKF + ((ND % 2) ? NB : 0) + 2 * GDN_COLS + 1;
+    constexpr int NDMA0 = NB * NKD + 2 * GDN_COLS + 1;
     constexpr int NDMA1 = ND * NKT;
     typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -989,9 +1014,6 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
     }
     __syncthreads();
 
-    const StepRows kr{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.k) + (int64_t)b * p.ks[0] +
-                                                    (int64_t)h * p.ks[2]),
-                      p.ks[1] * 2, T, C, N, dir, 2 * D};
     const StepRows vr{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.v) + (int64_t)b * p.vs[0] +
                                                     (int64_t)h * p.vs[2]),
                       p.vs[1] * 2, T, C, N, dir, 2 * D};
@@ -1008,21 +1030,19 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
         // Loader 0 moves K, V and the scales, loader 1 the state-update fragments Z;
         // loader 1 publishes a step for the chain only once loader 0 has landed it too.
         const int part = wave - (GDN_COLS + NOUT);
-        int krow[NB];
-#pragma unroll
-        for (int mt = 0; mt < NB; ++mt) krow[mt] = kr.row(16 * mt + r);
+        // K fragments: 16 bytes per lane, the rows of a tile reversed for the reverse direction
+        const auto kfr = make_rsrc(frag_base(p, 0, b, h, NKD), (uint32_t)(((T + 15) / 16) * NKD * 1024));
+        const int kfl = 16 * ((dir ? 15 - r : r) + 16 * g);
         const int voff = vr.row(lane & (C - 1)) + 2 * row0;   // rows >= C duplicate real ones, unused
         const int scoff = lane < 16 ? 16 * lane : (lane == 16 ? 8 * C : 0);
         auto issue0 = [&](int n) {
             ScanOps<NB, ND>& op = L.ops[n % GDN_OPS];
-            const auto krs = kr.rsrc(n);
 #pragma unroll
             for (int mt = 0; mt < NB; ++mt) {
+                // tiles past the last token read as zero (outside the resource)
+                const int tile = frag_tile(dir, N, NB, n, mt);
 #pragma unroll
-                for (int ks = 0; ks < NKF; ++ks) dma16(krs, &op.k[mt][ks][0], krow[mt] + 16 * g, 64 * ks);
-                // the trailing tile needs 8 bytes per lane; the upper 8 are not used (and read
-                // the next row, or zero past the end of the tensor)
-                if constexpr (ND % 2) dma16(krs, &op.kh[mt][0], krow[mt] + 8 * g, 32 * (ND - 1));
+                for (int ks = 0; ks < NKD; ++ks) dma16(kfr, &op.k[mt][ks][0], kfl, (tile * NKD + ks) * 1024);
             }
             const auto vrs = vr.rsrc(n);
 #pragma unroll
@@ -1099,11 +1119,29 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
     int done_seen[NOUT];
 #pragma unroll
     for (int o = 0; o < NOUT; ++o) done_seen[o] = 0;
+    // K fragments of a step, read one step ahead (while the state update runs); a trailing
+    // half k-step (odd ND) has zero upper slots
+    uint4 kf[NB][NKD];
+    auto read_k = [&](const ScanOps<NB, ND>& op) {
+#pragma unroll
+        for (int ks = 0; ks < NKD; ++ks)
+#pragma unroll
+            for (int mt = 0; mt < NB; ++mt) kf[mt][ks] = op.k[mt][ks][lane];
+    };
+    wait_counter(&K.loaded[1], 1);
+    read_k(L.ops[0]);
 #pragma unroll 1
     for (int n = 0; n < N; ++n) {
         const int sl = n % GDN_RING;
-        wait_counter(&K.loaded[1], n + 1);
         const ScanOps<NB, ND>& op = L.ops[n % GDN_OPS];
+        // the output ring slot of this step must have been released by every output
+        // wavefront (the last counts seen are kept, so the counters are read only when needed)
+#pragma unroll
+        for (int o = 0; o < NOUT; ++o)
+            if (done_seen[o] < n + 1 - GDN_RING) {
+                wait_counter(&K.done[o], n + 1 - GDN_RING);
+                done_seen[o] = __hip_atomic_load(&K.done[o], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
         // state as bf16 operand: k-slot e of lane group g <-> d = dperm(2 ks + e/4, 4 g + e%4)
         bf16x8 Pb[NKD];
 #pragma unroll
@@ -1120,38 +1158,22 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
                 Pb[NKD - 1][4 + i] = (bf16)0.f;
             }
         }
-        // operands of the step (in order of use)
-        uint4 kf[NB][NKD];
+        // The Z fragments are read into the registers the previous state update took its
+        // operands from: their LDS addresses depend on Pb (through an empty asm), and Pb
+        // on every result of that update, so the reads issue only once it has finished.
+        int zdep = 0;
 #pragma unroll
-        for (int mt = 0; mt < NB; ++mt) {
+        for (int ks = 0; ks < NKD; ++ks) asm volatile("" : "+v"(zdep) : "v"(Pb[ks]));
+        // publish the state to the output ring right away
 #pragma unroll
-            for (int ks = 0; ks < NKF; ++ks) kf[mt][ks] = op.k[mt][ks][lane];
-            if constexpr (ND % 2) {
-                const uint4 t4 = op.kh[mt][lane];
-                kf[mt][NKF] = uint4{t4.x, t4.y, 0u, 0u};
-            }
-        }
+        for (int ks = 0; ks < NKD; ++ks) L.ringP[sl][ks][cc][lane] = __builtin_bit_cast(uint4, Pb[ks]);
+        // the step's remaining operands, in order of use: the scales and V (read back
+        // transposed: lane quad q of group g supplies row 16 mt + 4 g + i, columns
+        // 16 cc + 4 q .. +3 of the deposited rows), then Z
         f32x4 c1[NB];
 #pragma unroll
         for (int mt = 0; mt < NB; ++mt) c1[mt] = __builtin_bit_cast(f32x4, op.sc[4 * mt + g]);
         const float gC = __builtin_bit_cast(f32x4, op.sc[16]).x;
-        uint4 zfr[ND][NKT];
-#pragma unroll
-        for (int m = 0; m < ND; ++m)
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) zfr[m][kt] = op.z[m][kt][lane];
-        // X = K S^T (rows: tokens 16 mt + 4 g + i, column: state row 16 cc + r)
-        f32x4 X[NB];
-#pragma unroll
-        for (int mt = 0; mt < NB; ++mt) X[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < NKD; ++ks)
-#pragma unroll
-            for (int mt = 0; mt < NB; ++mt) X[mt] = mma_bf16_k32(__builtin_bit_cast(bf16x8, kf[mt][ks]), Pb[ks], X[mt]);
-        // meanwhile: decay the state; read V back transposed (lane quad q of group g
-        // supplies row 16 mt + 4 g + i, columns 16 cc + 4 q .. +3 of the deposited rows)
-#pragma unroll
-        for (int m = 0; m < ND; ++m) P[m] = P[m] * gC;
         bf16x4 vt[NB];
 #pragma unroll
         for (int mt = 0; mt < NB; ++mt) {
@@ -1160,6 +1182,22 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
             vt[mt] = __builtin_bit_cast(
                 bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)vp));
         }
+        uint4 zfr[ND][NKT];
+#pragma unroll
+        for (int m = 0; m < ND; ++m)
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) zfr[m][kt] = op.z[m][kt][lane + zdep];
+        // X = K S^T (rows: tokens 16 mt + 4 g + i, column: state row 16 cc + r)
+        f32x4 X[NB];
+#pragma unroll
+        for (int mt = 0; mt < NB; ++mt) X[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKD; ++ks)
+#pragma unroll
+            for (int mt = 0; mt < NB; ++mt) X[mt] = mma_bf16_k32(__builtin_bit_cast(bf16x8, kf[mt][ks]), Pb[ks], X[mt]);
+        // meanwhile: decay the state
+#pragma unroll
+        for (int m = 0; m < ND; ++m) P[m] = P[m] * gC;
         // R = V - diag(e^g / |k|) X, as fp16 B operand (k = token)
         f16x8 Rb[NKT];
 #pragma unroll
@@ -1170,34 +1208,28 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
 #pragma unroll
             for (int i = 4; i < 8; ++i) Rb[NFT][i] = (f16)0.f;
         }
-        // every read of the operand slot has completed (the signal below also releases it
-        // to the loaders)
-#pragma unroll
-        for (int m = 0; m < ND; ++m)
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) keep_alive(__builtin_bit_cast(u32x4, zfr[m][kt]));
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) keep_alive(Rb[kt]);
-        // publish the step's state and R once every output wavefront has released the slot
-        // (the last counts seen are kept, so the counters are read only when needed)
-#pragma unroll
-        for (int o = 0; o < NOUT; ++o)
-            if (done_seen[o] < n + 1 - GDN_RING) {
-                wait_counter(&K.done[o], n + 1 - GDN_RING);
-                done_seen[o] = __hip_atomic_load(&K.done[o], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            }
-#pragma unroll
-        for (int ks = 0; ks < NKD; ++ks) L.ringP[sl][ks][cc][lane] = __builtin_bit_cast(uint4, Pb[ks]);
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) L.ringR[sl][kt][cc][lane] = __builtin_bit_cast(uint4, Rb[kt]);
+        // issue order of the step: the conversions and ring writes of Pb, then each X
+        // MFMA followed by two of the operand reads, then the arithmetic of R
+        __builtin_amdgcn_sched_group_barrier(0x002, 2 * NKD, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, NKD, 0);
+#pragma unroll
+        for (int i = 0; i < NB * NKD; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
         signal_counter(&K.ready[cc], n + 1);
+        // the next step's operands must have landed before its K is read below
+        if (n + 1 < N) wait_counter(&K.loaded[1], n + 2);
         __builtin_amdgcn_sched_barrier(0);
         // S^T <- gamma_C S^T + Z^T R  (rows d, columns: state rows); a trailing 16-token
-        // step has zero upper slots in both operands
+        // step has zero upper slots in both operands.  The next step's K is read meanwhile.
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
             for (int m = 0; m < ND; ++m) P[m] = mma_f16_k32(__builtin_bit_cast(f16x8, zfr[m][kt]), Rb[kt], P[m]);
+        if (n + 1 < N) read_k(L.ops[(n + 1) % GDN_OPS]);
     }
     float* Sout = p.S_out[dir];
     if (Sout && tile_ok) {
