@@ -773,7 +773,7 @@ struct ScanOps {
     static constexpr int NKT = Blocks<NB>::NFULL + (Blocks<NB>::HALF ? 1 : 0);
     uint4 k[NB][NKD][64];                // K fragments of processing tile mt (as stored by the prep)
     uint4 z[ND][NKT][64];                // state-update fragments of the item
-    uint4 v[2 * GDN_COLS][64];           // 16-byte chunk j of token `lane`'s V row slice
+    uint4 v[NB][64];                     // V row slices, [token][4 chunks of 16 bytes] (see vslot)
     uint4 sc[64];                        // lanes 0..15: c1 (64 floats); lane 16: gamma_C
 };
 
@@ -784,7 +784,14 @@ struct ScanLds {
     uint4 ringP[GDN_RING][NKD][GDN_COLS][64];
     uint4 ringR[GDN_RING][NKT][GDN_COLS][64];
     ScanOps<NB, ND> ops[GDN_OPS];
+    uint4 ostage[ScanShape<NB>::NOUT][ScanShape<NB>::TPO][64];   // bf16 output tiles on their way out
 };
+
+// A token's 64-byte slice (32 state rows, bf16) in LDS holds its 16-byte chunk j at position
+// j ^ vswz(t): tokens 4 apart land on different banks for the chain's transposing reads
+// and the output tiles' writes, while each lane quad moves one token's 64 contiguous bytes.
+__device__ __forceinline__ int vswz(int t) { return 2 * ((t >> 2) & 1); }
+__device__ __forceinline__ int oswz(int t) { return (t >> 2) & 3; }
 
 // Progress counters of the scan's wavefronts.  A separate LDS object from the
 // operand slots, so that the compiler need not order the counters behind the
@@ -845,6 +852,13 @@ __device__ __forceinline__ void scan_output(const Params& p, ScanLds<NB, ND>& L,
     int ooff[TPO];
 #pragma unroll
     for (int tt = 0; tt < TPO; ++tt) ooff[tt] = orow.row(16 * (MT0 + tt) + r) + oesz * (row0 + 4 * g);   // token, state rows row0 + 4g ..
+    // bf16: the tiles go out through LDS, lane quad l/4 storing token l/4's 64-byte slice
+    // (chunks past d_v are stored outside the resource, i.e. dropped)
+    const int st = lane >> 2, sj = (lane & 3) ^ oswz(lane >> 2);
+    int soff[TPO];
+#pragma unroll
+    for (int tt = 0; tt < TPO; ++tt)
+        soff[tt] = (row0 + 16 * (sj >> 1) < p.Dv) ? orow.row(16 * (MT0 + tt) + st) + 2 * row0 + 16 * sj : (int)0x80000000;
     bool col_ok[GDN_COLS];
 #pragma unroll
     for (int c = 0; c < GDN_COLS; ++c) col_ok[c] = row0 + 16 * c < p.Dv;
@@ -940,17 +954,29 @@ __device__ __forceinline__ void scan_output(const Params& p, ScanLds<NB, ND>& L,
         __builtin_amdgcn_sched_barrier(0);
         load_out(o, n + 2 < N ? n + 2 : N - 1);
         const auto ors = orow.rsrc(n);
+        if (oesz == 2) {
+            // token r's rows 16 c + 4 g .. +3 (8 bytes) to chunk 2 c + g/2, half g%2
 #pragma unroll
-        for (int c = 0; c < GDN_COLS; ++c)
-            if (col_ok[c]) {
+            for (int tt = 0; tt < TPO; ++tt)
 #pragma unroll
-                for (int tt = 0; tt < TPO; ++tt) {
-                    if (oesz == 2)
-                        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ov[tt][c]), ors, ooff[tt] + 32 * c, 0, 0);
-                    else
+                for (int c = 0; c < GDN_COLS; ++c) {
+                    char* sp = reinterpret_cast<char*>(&L.ostage[O][tt][0]) + 64 * r + 16 * ((2 * c + (g >> 1)) ^ oswz(r)) + 8 * (g & 1);
+                    *reinterpret_cast<uint2*>(sp) = ov[tt][c];
+                }
+#pragma unroll
+            for (int tt = 0; tt < TPO; ++tt) {
+                const uint4 v = L.ostage[O][tt][lane];
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ors, soff[tt], 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < GDN_COLS; ++c)
+                if (col_ok[c]) {
+#pragma unroll
+                    for (int tt = 0; tt < TPO; ++tt)
                         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, Ot[tt][c]), ors, ooff[tt] + 64 * c, 0, 0);
                 }
-            }
+        }
     };
     // The prefetches are unconditional (the last steps reload step N-1) so that
     // every path through the loop has the same loads in flight.
@@ -975,7 +1001,7 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
     constexpr int SCAL_OFF = 1024 * (BK::TOTAL + ND * NKT);   // scalars of an item
     constexpr int NOUT = ScanShape<NB>::NOUT;
     // loads the loader wavefronts issue per step: K, V and the scales; Z
-    constexpr int NDMA0 = NB * NKD + 2 * GDN_COLS + 1;
+    constexpr int NDMA0 = NB * NKD + NB + 1;
     constexpr int NDMA1 = ND * NKT;
     typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -1033,7 +1059,15 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
         // K fragments: 16 bytes per lane, the rows of a tile reversed for the reverse direction
         const auto kfr = make_rsrc(frag_base(p, 0, b, h, NKD), (uint32_t)(((T + 15) / 16) * NKD * 1024));
         const int kfl = 16 * ((dir ? 15 - r : r) + 16 * g);
-        const int voff = vr.row(lane & (C - 1)) + 2 * row0;   // rows >= C duplicate real ones, unused
+        // V: lane quad l/4 moves token 16 jj + l/4's slice, lane l%4 its chunk at position l%4;
+        // chunks of column tiles past d_v are read from outside the resource (zero)
+        static_assert(GDN_COLS == 2, "V slices are 64 bytes");
+        int voff[NB];
+#pragma unroll
+        for (int jj = 0; jj < NB; ++jj) {
+            const int t = 16 * jj + (lane >> 2), j = (lane & 3) ^ vswz(t);
+            voff[jj] = (row0 + 16 * (j >> 1) < p.Dv) ? vr.row(t) + 2 * row0 + 16 * j : (int)0x80000000;
+        }
         const int scoff = lane < 16 ? 16 * lane : (lane == 16 ? 8 * C : 0);
         auto issue0 = [&](int n) {
             ScanOps<NB, ND>& op = L.ops[n % GDN_OPS];
@@ -1046,9 +1080,7 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
             }
             const auto vrs = vr.rsrc(n);
 #pragma unroll
-            for (int jj = 0; jj < 2 * GDN_COLS; ++jj)
-                // a column tile past d_v reads as zero (empty resource)
-                dma16(col_ok[jj / 2] ? vrs : make_rsrc(vr.base, 0u), &op.v[jj][0], voff, 16 * jj);
+            for (int jj = 0; jj < NB; ++jj) dma16(vrs, &op.v[jj][0], voff[jj], 0);
             dma16(irs, &op.sc[0], scoff, n * (int)ib + SCAL_OFF);
         };
         auto issue1 = [&](int n) {
@@ -1178,7 +1210,7 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
 #pragma unroll
         for (int mt = 0; mt < NB; ++mt) {
             const int q = r & 3, t = 16 * mt + 4 * g + (r >> 2);
-            const char* vp = reinterpret_cast<const char*>(&op.v[2 * cc + (q >> 1)][0]) + 16 * t + 8 * (q & 1);
+            const char* vp = reinterpret_cast<const char*>(&op.v[0][0]) + 64 * t + 16 * ((2 * cc + (q >> 1)) ^ vswz(t)) + 8 * (q & 1);
             vt[mt] = __builtin_bit_cast(
                 bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)vp));
         }
