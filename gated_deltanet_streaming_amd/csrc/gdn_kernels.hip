@@ -353,53 +353,51 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(6))) v
     const TokMap tok{dir ? N * C - 1 : 0, dir ? -1 : 1};
 
     {
+        // every global load of the step goes out before the first is used: the gates,
+        // then the K and Q rows (16-byte chunks, NLD per thread)
+        float av = 1.f, bt = 0.f;
+        bool gv = false;
+        if (tid < C) {
+            const int tk = tok(n, C, tid);
+            gv = tk >= 0 && tk < T;
+            if (gv) {
+                const int64_t gq = (int64_t)b * p.gs[0] + (int64_t)tk * p.gs[1] + (int64_t)h * p.gs[2];
+                av = p.a[gq];
+                bt = p.beta[gq];
+            }
+        }
         const bf16* kb = reinterpret_cast<const bf16*>(p.k) + (int64_t)b * p.ks[0] + (int64_t)h * p.ks[2];
         const bf16* qb = reinterpret_cast<const bf16*>(p.q) + (int64_t)b * p.qs[0] + (int64_t)h * p.qs[2];
         const auto kr = make_rsrc(kb, (uint32_t)(((int64_t)(T - 1) * p.ks[1] + D) * 2));
         const auto qr = make_rsrc(qb, (uint32_t)(((int64_t)(T - 1) * p.qs[1] + D) * 2));
         const int ksb = (int)p.ks[1] * 2, qsb = (int)p.qs[1] * 2;
-        for (int idx = tid; idx < C * CH; idx += NT) {
-            const int t = idx / CH, c = idx - t * CH;
-            const int tk = tok(n, C, t);
-            const uint4 kv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, tk * ksb + 16 * c, 0, 0));
-            const uint4 qv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(qr, tk * qsb + 16 * c, 0, 0));
-            *reinterpret_cast<uint4*>(Ks + t * LDR + 8 * c) = kv;
-            *reinterpret_cast<uint4*>(Qs + t * LDR + 8 * c) = qv;
+        constexpr int NLD = (C * CH + NT - 1) / NT;
+        uint4 kv[NLD], qv[NLD];
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int idx = tid + i * NT;
+            if (idx < C * CH) {
+                const int t = idx / CH, c = idx - t * CH;
+                const int tk = tok(n, C, t);
+                kv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, tk * ksb + 16 * c, 0, 0));
+                qv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(qr, tk * qsb + 16 * c, 0, 0));
+            }
         }
-    }
-    if (tid < C) {
-        const int tk = tok(n, C, tid);
-        float la = 0.f, bt = 0.f;
-        if (tk >= 0 && tk < T) {
-            const int64_t gq = (int64_t)b * p.gs[0] + (int64_t)tk * p.gs[1] + (int64_t)h * p.gs[2];
-            la = fmaxf(logf(p.a[gq]), GDN_MIN_LOG_DECAY);
-            bt = p.beta[gq];
+        if (tid < C) {
+            sc[0][tid] = gv ? fmaxf(logf(av), GDN_MIN_LOG_DECAY) : 0.f;
+            sc[1][tid] = bt;
         }
-        sc[0][tid] = la;
-        sc[1][tid] = bt;
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int idx = tid + i * NT;
+            if (idx < C * CH) {
+                const int t = idx / CH, c = idx - t * CH;
+                *reinterpret_cast<uint4*>(Ks + t * LDR + 8 * c) = kv[i];
+                *reinterpret_cast<uint4*>(Qs + t * LDR + 8 * c) = qv[i];
+            }
+        }
     }
     __syncthreads();
-
-    // the operand fragments of this step's token tiles (written by one direction only)
-    if (dir == p.dir0) {
-        constexpr int NKD = (ND + 1) / 2, NKF = ND / 2;
-        const int ntile = (T + 15) / 16;
-        for (int job = w; job < 2 * NB * NKD; job += NW) {
-            const int kind = job / (NB * NKD), mt = (job / NKD) % NB, ks = job % NKD;
-            const int tile = frag_tile(dir, N, NB, n, mt);
-            if (tile >= ntile) continue;
-            const bf16* row = (kind ? Qs : Ks) + (16 * mt + (dir ? 15 - r : r)) * LDR;
-            uint4 v;
-            if (ks < NKF) {
-                v = *reinterpret_cast<const uint4*>(row + 32 * ks + 8 * g);
-            } else {
-                const uint2 hv = *reinterpret_cast<const uint2*>(row + 16 * (ND - 1) + 4 * g);
-                v = uint4{hv.x, hv.y, 0u, 0u};
-            }
-            char* dst = const_cast<char*>(frag_base(p, kind, b, h, NKD)) + ((int64_t)tile * NKD + ks) * 1024;
-            reinterpret_cast<uint4*>(dst)[lane] = v;
-        }
-    }
 
     // per-token inverse norms: 4 lanes per row, 16 rows per wavefront; waves < NB take the
     // K rows, the others the Q rows
@@ -434,8 +432,11 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(6))) v
 
     // Gram tiles on MFMA: K K^T -> L (strictly lower, stored transposed), Q K^T -> A (lower incl. diagonal)
     {
-        constexpr int NTILE = NB * (NB + 1) / 2;
-        for (int tt = w; tt < 2 * NTILE; tt += NW) {
+        constexpr int NTILE = NB * (NB + 1) / 2, NGT = 2 * NTILE, TPW = (NGT + NW - 1) / NW;
+#pragma unroll
+        for (int it = 0; it < TPW; ++it) {
+            const int tt = w + it * NW;
+            if (tt >= NGT) break;
             const bool isq = tt >= NTILE;
             const int ti = isq ? tt - NTILE : tt;
             int mt = 0;
@@ -473,15 +474,27 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(6))) v
                 else
                     Am[LB::at(t, s)] = (f16)((s <= t) ? p.scale * dec * rt[i] * rs * acc[i] : 0.f);
             }
-#pragma unroll
-            for (int ks = 0; ks < ND / 2; ++ks) {
-                keep_alive(aop[ks]);
-                keep_alive(bop[ks]);
+        }
+    }
+    // the operand fragments of this step's token tiles (written by one direction only; Q before
+    // its rows are overwritten by T)
+    if (dir == p.dir0) {
+        constexpr int NKD = (ND + 1) / 2, NKF = ND / 2;
+        const int ntile = (T + 15) / 16;
+        for (int job = w; job < 2 * NB * NKD; job += NW) {
+            const int kind = job / (NB * NKD), mt = (job / NKD) % NB, ks = job % NKD;
+            const int tile = frag_tile(dir, N, NB, n, mt);
+            if (tile >= ntile) continue;
+            const bf16* row = (kind ? Qs : Ks) + (16 * mt + (dir ? 15 - r : r)) * LDR;
+            uint4 v;
+            if (ks < NKF) {
+                v = *reinterpret_cast<const uint4*>(row + 32 * ks + 8 * g);
+            } else {
+                const uint2 hv = *reinterpret_cast<const uint2*>(row + 16 * (ND - 1) + 4 * g);
+                v = uint4{hv.x, hv.y, 0u, 0u};
             }
-            if constexpr (ND % 2) {
-                keep_alive(aoh);
-                keep_alive(boh);
-            }
+            char* dst = const_cast<char*>(frag_base(p, kind, b, h, NKD)) + ((int64_t)tile * NKD + ks) * 1024;
+            reinterpret_cast<uint4*>(dst)[lane] = v;
         }
     }
     __syncthreads();
@@ -529,13 +542,6 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(6))) v
                 }
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) z = __builtin_amdgcn_mfma_f32_16x16x4f32(la[kk], tb[kk], z, 0, 0, 0);
-                const float zs = z[0];
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    keep_alive(la[kk]);
-                    keep_alive(tb[kk]);
-                }
-                keep_alive(zs);
             }
             // z: lane (column r, group g) holds Z[4g + e][r]; B operand with k = 4g + kk
             float ta[4];
@@ -546,8 +552,6 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(6))) v
             for (int kk = 0; kk < 4; ++kk) t4 = __builtin_amdgcn_mfma_f32_16x16x4f32(ta[kk], z[kk], t4, 0, 0, 0);
             // T[16 ib + 4g + e][16 jb + r] -> Tt[16 jb + r][16 ib + 4g + e]
             *reinterpret_cast<f32x4*>(Tt + UB::at(16 * jb + r, 16 * ib + 4 * g)) = -t4;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) keep_alive(ta[kk]);
         }
         __syncthreads();
     }
@@ -588,10 +592,6 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(6))) v
                         for (int e = 0; e < 8; ++e) ao[e] = bo[e] = (f16)0.f;
                     }
                     acc = mma_f16_k32(ao, bo, acc);
-                    const float accs = acc[0];
-                    keep_alive(ao);
-                    keep_alive(bo);
-                    keep_alive(accs);
                 }
             }
             // column beta_u of T diag(beta): rows u = 16 ut + 4 g + i of this E^T tile
@@ -651,11 +651,6 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(6))) v
                     const bf16x8 bk = cat(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi4));
                     acc = mma_bf16_k32(ahi, bk, acc);
                     acc = mma_bf16_k32(alo, bk, acc);
-                    const float accs = acc[0];
-                    keep_alive(ahi);
-                    keep_alive(alo);
-                    keep_alive(bk);
-                    keep_alive(accs);
                 }
             }
             const f32x4 bt4 = (mt < NB) ? *reinterpret_cast<const f32x4*>(&sc[1][16 * mt + 4 * g])
