@@ -297,11 +297,20 @@ struct UpperF32 {   // fp32 blocks (a, b) with a <= b (L^T and T^T), rows of LD_
     }
 };
 template <int NB>
-struct LowerF16 {   // fp16 blocks (a, b) with a >= b (A), rows of 24 halves
-    static constexpr int LD = 24, COUNT = NB * (NB + 1) / 2, HALVES = COUNT * 16 * LD;
+struct UpperF16 {   // fp16 blocks (a, b) with a <= b (L^T), rows of 16 halves
+    static constexpr int COUNT = NB * (NB + 1) / 2, HALVES = COUNT * 256;
     __device__ static int at(int row, int col) {
         const int a = row >> 4, b = col >> 4;
-        return ((a * (a + 1)) / 2 + b) * (16 * LD) + (row & 15) * LD + (col & 15);
+        return (a * NB - (a * (a - 1)) / 2 + (b - a)) * 256 + (row & 15) * 16 + (col & 15);
+    }
+};
+template <int NB>
+struct LowerF16 {   // fp16 blocks (a, b) with a >= b (A), rows of 16 halves; the two 8-half
+                    // chunks of rows 8..15 swapped (16-byte row reads free of bank conflicts)
+    static constexpr int COUNT = NB * (NB + 1) / 2, HALVES = COUNT * 256;
+    __device__ static int at(int row, int col) {
+        const int a = row >> 4, b = col >> 4;
+        return ((a * (a + 1)) / 2 + b) * 256 + (row & 15) * 16 + ((((col & 15) >> 3) ^ ((row >> 3) & 1)) << 3) + (col & 7);
     }
 };
 
@@ -319,10 +328,9 @@ struct LowerF16 {   // fp16 blocks (a, b) with a >= b (A), rows of 24 halves
 // d of Z^T follows the scan's state order (see dperm).
 // ---------------------------------------------------------------------------
 template <int NB, int ND>
-__global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(6))) void gdn_prep_kernel(Params p) {
+__global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) void gdn_prep_kernel(Params p) {
     constexpr int C = 16 * NB, D = 16 * ND;
-    constexpr int LDR = D + 8;   // bf16 row stride of the staged K and Q rows (8-byte aligned rows)
-    using UL = UpperF32<NB, 16>; // L^T (read by rows or 64 consecutive floats)
+    using UL = UpperF16<NB>;     // L^T (fp16: its rounding is below that of the fp16 E and Z it feeds)
     using UB = UpperF32<NB, 20>; // T^T (also read down columns: padded rows)
     using LB = LowerF16<NB>;     // A
     constexpr int NW = 2 * NB;   // wavefronts
@@ -335,10 +343,13 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(6))) v
     typedef short s16x4 __attribute__((ext_vector_type(4)));
 
     // Q rows (bf16) share storage with T^T (fp32), which is built after the Gram products
-    constexpr int Q_BYTES = C * LDR * 2, T_BYTES = UB::FLOATS * 4;
-    __shared__ __align__(16) bf16 Ks[C * LDR];
+    // K and Q rows (bf16, D per row); row t holds its 16-byte chunk c at position c ^ ((t >> 3) & 1),
+    // so that 16 rows read at one column are free of bank conflicts
+    auto kq = [](int t, int d) { return t * D + (((d >> 3) ^ ((t >> 3) & 1)) << 3) + (d & 7); };
+    constexpr int Q_BYTES = C * D * 2, T_BYTES = UB::FLOATS * 4;
+    __shared__ __align__(16) bf16 Ks[C * D];
     __shared__ __align__(16) char QT[Q_BYTES > T_BYTES ? Q_BYTES : T_BYTES];
-    __shared__ __align__(16) float Lt[UL::FLOATS];   // L transposed: Lt[s][t] = L[t][s], s < t
+    __shared__ __align__(16) f16 Lt[UL::HALVES];     // L transposed: Lt[s][t] = L[t][s], s < t
     __shared__ __align__(16) f16 Am[LB::HALVES];     // A[t][s], s <= t (an fp16 operand of E only)
     __shared__ __align__(16) float sc[5][C];      // 0: log a then g, 1: beta, 2: 1/|k|, 3: 1/|q|, 4: e^{g_C-g}/|k|
     bf16* Qs = reinterpret_cast<bf16*>(QT);
@@ -392,8 +403,8 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(6))) v
             const int idx = tid + i * NT;
             if (idx < C * CH) {
                 const int t = idx / CH, c = idx - t * CH;
-                *reinterpret_cast<uint4*>(Ks + t * LDR + 8 * c) = kv[i];
-                *reinterpret_cast<uint4*>(Qs + t * LDR + 8 * c) = qv[i];
+                *reinterpret_cast<uint4*>(Ks + kq(t, 8 * c)) = kv[i];
+                *reinterpret_cast<uint4*>(Qs + kq(t, 8 * c)) = qv[i];
             }
         }
     }
@@ -404,10 +415,10 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(6))) v
     {
         const bool isk = w < NB;
         const int t = 16 * (isk ? w : w - NB) + (lane >> 2), part = lane & 3;
-        const bf16* rowp = (isk ? Ks : Qs) + t * LDR;
+        const bf16* rows = isk ? Ks : Qs;
         float ss = 0.f;
         for (int c = part; c < CH; c += 4) {
-            const bf16x8 xv = ld_bf16x8(rowp + 8 * c);
+            const bf16x8 xv = ld_bf16x8(rows + kq(t, 8 * c));
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float xf = (float)xv[e];
@@ -442,18 +453,18 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(6))) v
             int mt = 0;
             while ((mt + 1) * (mt + 2) / 2 <= ti) ++mt;
             const int nt = ti - mt * (mt + 1) / 2;
-            const bf16* arow = (isq ? Qs : Ks) + (16 * mt + r) * LDR;
-            const bf16* brow = Ks + (16 * nt + r) * LDR;
+            const bf16* arows = isq ? Qs : Ks;
+            const int ar = 16 * mt + r, br = 16 * nt + r;
             bf16x8 aop[ND / 2 > 0 ? ND / 2 : 1], bop[ND / 2 > 0 ? ND / 2 : 1];
             bf16x4 aoh, boh;
 #pragma unroll
             for (int ks = 0; ks < ND / 2; ++ks) {
-                aop[ks] = ld_bf16x8(arow + 32 * ks + 8 * g);
-                bop[ks] = ld_bf16x8(brow + 32 * ks + 8 * g);
+                aop[ks] = ld_bf16x8(arows + kq(ar, 32 * ks + 8 * g));
+                bop[ks] = ld_bf16x8(Ks + kq(br, 32 * ks + 8 * g));
             }
             if constexpr (ND % 2) {
-                aoh = ld_bf16x4(arow + 32 * (ND / 2) + 4 * g);
-                boh = ld_bf16x4(brow + 32 * (ND / 2) + 4 * g);
+                aoh = ld_bf16x4(arows + kq(ar, 32 * (ND / 2) + 4 * g));
+                boh = ld_bf16x4(Ks + kq(br, 32 * (ND / 2) + 4 * g));
             }
             // per-row (t = 16 mt + 4 g + i) and per-column (s = 16 nt + r) scalars
             const int s = 16 * nt + r, t0 = 16 * mt + 4 * g;
@@ -470,7 +481,7 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(6))) v
                 const int t = t0 + i;
                 const float dec = (s <= t) ? __expf(gt[i] - gs) : 0.f;
                 if (!isq)
-                    Lt[UL::at(s, t)] = (s < t) ? bt[i] * dec * rt[i] * rs * acc[i] : 0.f;
+                    Lt[UL::at(s, t)] = (f16)((s < t) ? bt[i] * dec * rt[i] * rs * acc[i] : 0.f);
                 else
                     Am[LB::at(t, s)] = (f16)((s <= t) ? p.scale * dec * rt[i] * rs * acc[i] : 0.f);
             }
@@ -485,12 +496,13 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(6))) v
             const int kind = job / (NB * NKD), mt = (job / NKD) % NB, ks = job % NKD;
             const int tile = frag_tile(dir, N, NB, n, mt);
             if (tile >= ntile) continue;
-            const bf16* row = (kind ? Qs : Ks) + (16 * mt + (dir ? 15 - r : r)) * LDR;
+            const bf16* rows = kind ? Qs : Ks;
+            const int rr = 16 * mt + (dir ? 15 - r : r);
             uint4 v;
             if (ks < NKF) {
-                v = *reinterpret_cast<const uint4*>(row + 32 * ks + 8 * g);
+                v = *reinterpret_cast<const uint4*>(rows + kq(rr, 32 * ks + 8 * g));
             } else {
-                const uint2 hv = *reinterpret_cast<const uint2*>(row + 16 * (ND - 1) + 4 * g);
+                const uint2 hv = *reinterpret_cast<const uint2*>(rows + kq(rr, 16 * (ND - 1) + 4 * g));
                 v = uint4{hv.x, hv.y, 0u, 0u};
             }
             char* dst = const_cast<char*>(frag_base(p, kind, b, h, NKD)) + ((int64_t)tile * NKD + ks) * 1024;
@@ -509,13 +521,13 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(6))) v
         for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
 #pragma unroll
         for (int k = 0; k < 15; ++k) {
-            const float* lcol = Lt + UL::at(o + k, o);   // L[o + i][o + k] for i > k
+            const f16* lcol = Lt + UL::at(o + k, o);   // L[o + i][o + k] for i > k
             float lv[16];
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const f32x4 v4 = *reinterpret_cast<const f32x4*>(lcol + 4 * i4);
+            for (int i8 = 0; i8 < 2; ++i8) {
+                const f16x8 v8 = *reinterpret_cast<const f16x8*>(lcol + 8 * i8);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) lv[4 * i4 + e] = v4[e];
+                for (int e = 0; e < 8; ++e) lv[8 * i8 + e] = (float)v8[e];
             }
 #pragma unroll
             for (int i = k + 1; i < 16; ++i) x[i] -= lv[i] * x[k];
@@ -537,7 +549,7 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(6))) v
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
                     const int k = 16 * kb + 4 * kk + g;
-                    la[kk] = Lt[UL::at(k, 16 * ib + r)];      // L[16 ib + r][k]
+                    la[kk] = (float)Lt[UL::at(k, 16 * ib + r)];   // L[16 ib + r][k]
                     tb[kk] = Tt[UB::at(16 * jb + r, k)];      // T[k][16 jb + r]
                 }
 #pragma unroll
@@ -644,10 +656,10 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(6))) v
                     const int d0 = dperm<ND>(m, 4 * (r & 3));   // 4 consecutive d per lane quad
                     s16x4 lo = {0, 0, 0, 0}, hi4 = {0, 0, 0, 0};
                     if (32 * ss < C)
-                        lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(Ks + t0 * LDR + d0));
+                        lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(Ks + kq(t0, d0)));
                     if (32 * ss + 16 < C)
                         hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) s16x4*)(Ks + (t0 + 16) * LDR + d0));
+                            (__attribute__((address_space(3))) s16x4*)(Ks + kq(t0 + 16, d0)));
                     const bf16x8 bk = cat(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi4));
                     acc = mma_bf16_k32(ahi, bk, acc);
                     acc = mma_bf16_k32(alo, bk, acc);
