@@ -305,6 +305,14 @@ struct UpperF16 {   // fp16 blocks (a, b) with a <= b (L^T), rows of 16 halves
     }
 };
 template <int NB>
+struct UpperF16S {  // fp16 blocks (a, b) with a <= b (T^T), rows of 16 halves, chunks of rows 8..15 swapped
+    static constexpr int COUNT = NB * (NB + 1) / 2, HALVES = COUNT * 256;
+    __device__ static int at(int row, int col) {
+        const int a = row >> 4, b = col >> 4;
+        return (a * NB - (a * (a - 1)) / 2 + (b - a)) * 256 + (row & 15) * 16 + ((((col & 15) >> 3) ^ ((row >> 3) & 1)) << 3) + (col & 7);
+    }
+};
+template <int NB>
 struct LowerF16 {   // fp16 blocks (a, b) with a >= b (A), rows of 16 halves; the two 8-half
                     // chunks of rows 8..15 swapped (16-byte row reads free of bank conflicts)
     static constexpr int COUNT = NB * (NB + 1) / 2, HALVES = COUNT * 256;
@@ -332,6 +340,7 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
     constexpr int C = 16 * NB, D = 16 * ND;
     using UL = UpperF16<NB>;     // L^T (fp16: its rounding is below that of the fp16 E and Z it feeds)
     using UB = UpperF32<NB, 20>; // T^T (also read down columns: padded rows)
+    using US = UpperF16S<NB>;    // T^T in fp16 (E's operand; stored over L)
     using LB = LowerF16<NB>;     // A
     constexpr int NW = 2 * NB;   // wavefronts
     constexpr int NT = 64 * NW;
@@ -346,9 +355,14 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
     // K and Q rows (bf16, D per row); row t holds its 16-byte chunk c at position c ^ ((t >> 3) & 1),
     // so that 16 rows read at one column are free of bank conflicts
     auto kq = [](int t, int d) { return t * D + (((d >> 3) ^ ((t >> 3) & 1)) << 3) + (d & 7); };
-    constexpr int Q_BYTES = C * D * 2, T_BYTES = UB::FLOATS * 4;
+    // Z's A fragments: one per (row tile mt, 32-wide step ss >= mt/2), as a high/low pair
+    constexpr int NKT_ = Blocks<NB>::NFULL + (Blocks<NB>::HALF ? 1 : 0);
+    constexpr auto zoff = [](int mt) { int o = 0; for (int m2 = 0; m2 < mt; ++m2) o += NKT_ - m2 / 2; return o; };
+    constexpr int NZB = zoff(NB);
+    constexpr int Q_BYTES = C * D * 2, T_BYTES = UB::FLOATS * 4, ZW_BYTES = NZB * 2048;
+    constexpr int QT_BYTES = Q_BYTES > T_BYTES ? (Q_BYTES > ZW_BYTES ? Q_BYTES : ZW_BYTES) : (T_BYTES > ZW_BYTES ? T_BYTES : ZW_BYTES);
     __shared__ __align__(16) bf16 Ks[C * D];
-    __shared__ __align__(16) char QT[Q_BYTES > T_BYTES ? Q_BYTES : T_BYTES];
+    __shared__ __align__(16) char QT[QT_BYTES];
     __shared__ __align__(16) f16 Lt[UL::HALVES];     // L transposed: Lt[s][t] = L[t][s], s < t
     __shared__ __align__(16) f16 Am[LB::HALVES];     // A[t][s], s <= t (an fp16 operand of E only)
     __shared__ __align__(16) float sc[5][C];      // 0: log a then g, 1: beta, 2: 1/|k|, 3: 1/|q|, 4: e^{g_C-g}/|k|
@@ -428,7 +442,8 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
         ss = sum4(ss);
         if (part == 0) sc[isk ? 2 : 3][t] = p.l2norm ? 1.f / sqrtf(ss + p.eps) : 1.f;
     }
-    // inclusive prefix of log a along the processing order (C <= 64: one wavefront)
+    // inclusive prefix of log a along the processing order (C <= 64: one wavefront), kept in
+    // base-2 units (every decay below is an exp2 of a difference of these)
     if (w == 0) {
         float x = (lane < C) ? sc[0][lane] : 0.f;
 #pragma unroll
@@ -436,10 +451,10 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
             const float y = __shfl_up(x, off);
             if (lane >= off) x += y;
         }
-        if (lane < C) sc[0][lane] = x;
+        if (lane < C) sc[0][lane] = x * 1.4426950408889634f;
     }
     __syncthreads();
-    if (tid < C) sc[4][tid] = __expf(sc[0][C - 1] - sc[0][tid]) * sc[2][tid];
+    if (tid < C) sc[4][tid] = __builtin_amdgcn_exp2f(sc[0][C - 1] - sc[0][tid]) * sc[2][tid];
 
     // Gram tiles on MFMA: K K^T -> L (strictly lower, stored transposed), Q K^T -> A (lower incl. diagonal)
     {
@@ -466,24 +481,29 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
                 aoh = ld_bf16x4(arows + kq(ar, 32 * (ND / 2) + 4 * g));
                 boh = ld_bf16x4(Ks + kq(br, 32 * (ND / 2) + 4 * g));
             }
-            // per-row (t = 16 mt + 4 g + i) and per-column (s = 16 nt + r) scalars
-            const int s = 16 * nt + r, t0 = 16 * mt + 4 * g;
-            const f32x4 gt = *reinterpret_cast<const f32x4*>(&sc[0][t0]);
-            const f32x4 bt = *reinterpret_cast<const f32x4*>(&sc[1][t0]);
-            const f32x4 rt = *reinterpret_cast<const f32x4*>(&sc[isq ? 3 : 2][t0]);
-            const float gs = sc[0][s], rs = sc[2][s];
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < ND / 2; ++ks) acc = mma_bf16_k32(aop[ks], bop[ks], acc);
             if constexpr (ND % 2) acc = mma_bf16_k16(aoh, boh, acc);
+            // rows t = 16 mt + 4 g + i, column s = 16 nt + r:
+            //   L: beta_t e^{g_t-g_s} k^_t.k^_s (s < t),  A: scale e^{g_t-g_s} q^_t.k^_s (s <= t)
+            const int s = 16 * nt + r, t0 = 16 * mt + 4 * g;
+            const f32x4 gt = *reinterpret_cast<const f32x4*>(&sc[0][t0]);
+            f32x4 rt = *reinterpret_cast<const f32x4*>(&sc[isq ? 3 : 2][t0]);
+            rt = isq ? rt * p.scale : rt * *reinterpret_cast<const f32x4*>(&sc[1][t0]);
+            const float gs = sc[0][s], rs = sc[2][s];
+            f32x4 v;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = t0 + i;
-                const float dec = (s <= t) ? __expf(gt[i] - gs) : 0.f;
-                if (!isq)
-                    Lt[UL::at(s, t)] = (f16)((s < t) ? bt[i] * dec * rt[i] * rs * acc[i] : 0.f);
-                else
-                    Am[LB::at(t, s)] = (f16)((s <= t) ? p.scale * dec * rt[i] * rs * acc[i] : 0.f);
+            for (int i = 0; i < 4; ++i) v[i] = acc[i] * (rt[i] * rs) * __builtin_amdgcn_exp2f(gt[i] - gs);
+            if (mt == nt) {   // the diagonal tile: only s < t (L) or s <= t (A)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = (isq ? s <= t0 + i : s < t0 + i) ? v[i] : 0.f;
+            }
+            if (!isq) {
+                *reinterpret_cast<f16x4*>(Lt + UL::at(s, t0)) = f16x4{(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Am[LB::at(t0 + i, s)] = (f16)v[i];
             }
         }
     }
@@ -568,6 +588,68 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
         __syncthreads();
     }
 
+    // T^T once more, in the two forms its products take, from the fp32 blocks (read by every
+    // thread before the sync, then overwritten):
+    //   T16: fp16 blocks in L's storage (E's operand);
+    //   Zw:  for row tile mt and 32-wide step ss >= mt/2, the A fragment of Z, T[s][t] w[s] with
+    //        w = e^{g_C-g}/|k| (slots 16 (i/4) + 4 g + i%4 of the step), as a bf16 high/low pair
+    constexpr int NBLK = NB * (NB + 1) / 2;
+    f16* T16 = Lt;
+    uint4* Zw = reinterpret_cast<uint4*>(QT);
+    f16x8 t16v;
+    uint4 zwhi, zwlo;
+    int t16blk_a = 0, t16blk_b = 0, t16row = 0, t16c = 0, zb_ss = 0;
+    const bool do_t16 = tid < NBLK * 32, do_zw = tid < NZB * 64;
+    if (do_t16) {
+        const int q = tid >> 5;
+        t16row = (tid >> 1) & 15;
+        t16c = tid & 1;
+        int a = 0, rem = q;
+        while (rem >= NB - a) { rem -= NB - a; ++a; }
+        t16blk_a = a;
+        t16blk_b = a + rem;
+        const float* src = Tt + UB::at(16 * a + t16row, 16 * t16blk_b + 8 * t16c);
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(src), x1 = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            t16v[e] = (f16)x0[e];
+            t16v[4 + e] = (f16)x1[e];
+        }
+    }
+    if (do_zw) {
+        const int zb = tid >> 6;
+        int mt = 0;
+        while (zoff(mt + 1) <= zb) ++mt;
+        zb_ss = mt / 2 + (zb - zoff(mt));
+        bf16x8 hi8, lo8;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int s0 = 32 * zb_ss + 16 * hf + 4 * g;
+            f32x4 tv = {0.f, 0.f, 0.f, 0.f}, wv = {0.f, 0.f, 0.f, 0.f};
+            if (s0 < C && 2 * zb_ss + hf >= mt) {   // T[s][t] = 0 for s < t
+                tv = *reinterpret_cast<const f32x4*>(Tt + UB::at(16 * mt + r, s0));
+                wv = *reinterpret_cast<const f32x4*>(&sc[4][s0]);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float v = tv[e] * wv[e];
+                const bf16 hv = (bf16)v;
+                hi8[4 * hf + e] = hv;
+                lo8[4 * hf + e] = (bf16)(v - (float)hv);
+            }
+        }
+        zwhi = __builtin_bit_cast(uint4, hi8);
+        zwlo = __builtin_bit_cast(uint4, lo8);
+    }
+    __syncthreads();
+    if (do_t16) *reinterpret_cast<f16x8*>(T16 + US::at(16 * t16blk_a + t16row, 16 * t16blk_b + 8 * t16c)) = t16v;
+    if (do_zw) {
+        const int zb = tid >> 6;
+        Zw[(2 * zb) * 64 + lane] = zwhi;
+        Zw[(2 * zb + 1) * 64 + lane] = zwlo;
+    }
+    __syncthreads();
+
     char* item = p.ws + ((((int64_t)dir * p.B + b) * p.H + h) * p.nsub_max + n) * p.ws_item_bytes;
     uint4* Efr = reinterpret_cast<uint4*>(item);                          // BK::TOTAL blocks
     uint4* Zfr = Efr + BK::TOTAL * 64;                                    // ND x NKT blocks
@@ -587,18 +669,11 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
             if (ut <= mt) {
                 // contraction over s in 32-wide steps (zero outside the triangle)
                 for (int ss = (16 * ut) / 32; ss * 32 < 16 * (mt + 1); ++ss) {
-                    const float* ta = Tt + UB::at(16 * ut + r, 32 * ss + 8 * g);
-                    const f16* aa = Am + LB::at(16 * mt + r, 32 * ss + 8 * g);
                     f16x8 ao, bo;
                     const int sb = 2 * ss + (g >> 1);   // 16-wide block of this lane's s
                     if (32 * ss + 8 * g < C && sb >= ut && sb <= mt) {
-                        const f32x4 t0v = *reinterpret_cast<const f32x4*>(ta), t1v = *reinterpret_cast<const f32x4*>(ta + 4);
-                        bo = *reinterpret_cast<const f16x8*>(aa);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            ao[e] = (f16)t0v[e];
-                            ao[4 + e] = (f16)t1v[e];
-                        }
+                        ao = *reinterpret_cast<const f16x8*>(T16 + US::at(16 * ut + r, 32 * ss + 8 * g));
+                        bo = *reinterpret_cast<const f16x8*>(Am + LB::at(16 * mt + r, 32 * ss + 8 * g));
                     } else {
 #pragma unroll
                         for (int e = 0; e < 8; ++e) ao[e] = bo[e] = (f16)0.f;
@@ -620,71 +695,65 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
         Efr[blk * 64 + lane] = __builtin_bit_cast(uint4, fr);
     }
 
-    // Z = diag(beta) T^T diag(e^{g_C-g}/|k|) K: A operand rows t, k = s (slots 16 (i/4) + 4g
-    // + i%4 of each 32-wide step) as a bf16 high/low pair; B operand = raw K rows read
-    // transposed, column r of tile m being state index dperm(m, r).  Output tiles (2ks, m)
-    // and (2ks + 1, m) form the state-update fragment (m, ks).
-    for (int job = w; job < ND * NKT; job += NW) {
-        const int m = job / NKT, ks = job - m * NKT;
-        f32x4 zt[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
+    // Z = diag(beta) T^T diag(e^{g_C-g}/|k|) K: A operand = the Zw fragments (k = s in slots
+    // 16 (i/4) + 4 g + i%4 of each 32-wide step); B operand = raw K rows read transposed, column r
+    // of tile m being state index dperm(m, r).  A job takes row tile mt = 2 ks + hh and a group of
+    // d tiles, sharing the A fragments; output tiles (2ks, m) and (2ks + 1, m) form the
+    // state-update fragment (m, ks), as its lower and upper 8 bytes.
+    {
+        constexpr int MG = NW / (2 * NKT) > 0 ? NW / (2 * NKT) : 1;   // groups of d tiles
+        constexpr int MPG = (ND + MG - 1) / MG;                        // d tiles per group
+        for (int job = w; job < 2 * NKT * MG; job += NW) {
+            const int mg = job % MG, kh = job / MG, ks = kh >> 1, hh = kh & 1;
             const int mt = 2 * ks + hh;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            f32x4 acc[MPG];
+#pragma unroll
+            for (int mi = 0; mi < MPG; ++mi) acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (mt < NB) {
                 for (int ss = mt / 2; ss < NKT; ++ss) {
-                    // A: Tt[t][s] * wk[s], s = 32 ss + 16 (i/4) + 4 g + i%4
-                    bf16x8 ahi, alo;
+                    const int zb = zoff(mt) + ss - mt / 2;
+                    const bf16x8 ahi = __builtin_bit_cast(bf16x8, Zw[(2 * zb) * 64 + lane]);
+                    const bf16x8 alo = __builtin_bit_cast(bf16x8, Zw[(2 * zb + 1) * 64 + lane]);
+                    const int t0 = 32 * ss + 4 * g + (r >> 2);
 #pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        const int s0 = 32 * ss + 16 * hf + 4 * g;
-                        f32x4 tv = {0.f, 0.f, 0.f, 0.f}, wv = {0.f, 0.f, 0.f, 0.f};
-                        if (s0 < C && 2 * ss + hf >= mt) {   // T[s][t] = 0 for s < t
-                            tv = *reinterpret_cast<const f32x4*>(Tt + UB::at(16 * mt + r, s0));
-                            wv = *reinterpret_cast<const f32x4*>(&sc[4][s0]);
-                        }
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float v = tv[e] * wv[e];
-                            const bf16 hi = (bf16)v;
-                            ahi[4 * hf + e] = hi;
-                            alo[4 * hf + e] = (bf16)(v - (float)hi);
+                    for (int mi = 0; mi < MPG; ++mi) {
+                        const int m = mg * MPG + mi;
+                        if (m < ND) {
+                            const int d0 = dperm<ND>(m, 4 * (r & 3));   // 4 consecutive d per lane quad
+                            s16x4 lo = {0, 0, 0, 0}, hi4 = {0, 0, 0, 0};
+                            if (32 * ss < C)
+                                lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(Ks + kq(t0, d0)));
+                            if (32 * ss + 16 < C)
+                                hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                    (__attribute__((address_space(3))) s16x4*)(Ks + kq(t0 + 16, d0)));
+                            const bf16x8 bk = cat(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi4));
+                            acc[mi] = mma_bf16_k32(ahi, bk, acc[mi]);
+                            acc[mi] = mma_bf16_k32(alo, bk, acc[mi]);
                         }
                     }
-                    // B: K[s][16 m + r] with the same slot -> s map, via transposing LDS reads
-                    const int t0 = 32 * ss + 4 * g + (r >> 2);
-                    const int d0 = dperm<ND>(m, 4 * (r & 3));   // 4 consecutive d per lane quad
-                    s16x4 lo = {0, 0, 0, 0}, hi4 = {0, 0, 0, 0};
-                    if (32 * ss < C)
-                        lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(Ks + kq(t0, d0)));
-                    if (32 * ss + 16 < C)
-                        hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) s16x4*)(Ks + kq(t0 + 16, d0)));
-                    const bf16x8 bk = cat(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi4));
-                    acc = mma_bf16_k32(ahi, bk, acc);
-                    acc = mma_bf16_k32(alo, bk, acc);
                 }
             }
             const f32x4 bt4 = (mt < NB) ? *reinterpret_cast<const f32x4*>(&sc[1][16 * mt + 4 * g])
                                         : f32x4{0.f, 0.f, 0.f, 0.f};
-            zt[hh] = acc * bt4;
-        }
-        f16x8 fr;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            fr[e] = (f16)zt[0][e];
-            fr[4 + e] = (f16)zt[1][e];
+            for (int mi = 0; mi < MPG; ++mi) {
+                const int m = mg * MPG + mi;
+                if (m < ND) {
+                    const f32x4 z = acc[mi] * bt4;
+                    const f16x4 z4 = {(f16)z[0], (f16)z[1], (f16)z[2], (f16)z[3]};
+                    reinterpret_cast<uint2*>(Zfr + (m * NKT + ks) * 64 + lane)[hh] = __builtin_bit_cast(uint2, z4);
+                }
+            }
         }
-        Zfr[job * 64 + lane] = __builtin_bit_cast(uint4, fr);
     }
 
     // scalars: c1 in token order; c2 with token 16 mt + r at r * NB + mt (one vector load
     // per lane of the scan's output wavefront); gamma_C
     if (tid < C) {
-        const float gam = __expf(sc[0][tid]);
+        const float gam = __builtin_amdgcn_exp2f(sc[0][tid]);
         scw[tid] = gam * sc[2][tid];
         scw[C + (tid & 15) * NB + (tid >> 4)] = p.scale * gam * sc[3][tid];
-        if (tid == 0) scw[2 * C] = __expf(sc[0][C - 1]);
+        if (tid == 0) scw[2 * C] = __builtin_amdgcn_exp2f(sc[0][C - 1]);
     }
 }
 
