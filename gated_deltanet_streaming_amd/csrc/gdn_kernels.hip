@@ -697,19 +697,23 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
 
     // Z = diag(beta) T^T diag(e^{g_C-g}/|k|) K: A operand = the Zw fragments (k = s in slots
     // 16 (i/4) + 4 g + i%4 of each 32-wide step); B operand = raw K rows read transposed, column r
-    // of tile m being state index dperm(m, r).  A job takes row tile mt = 2 ks + hh and a group of
-    // d tiles, sharing the A fragments; output tiles (2ks, m) and (2ks + 1, m) form the
-    // state-update fragment (m, ks), as its lower and upper 8 bytes.
+    // of tile m being state index dperm(m, r).  A job takes the row tiles mt = 2 ks, 2 ks + 1 and a
+    // group of d tiles; output tiles (2ks, m) and (2ks + 1, m) form the state-update fragment
+    // (m, ks), written whole.
     {
-        constexpr int MG = NW / (2 * NKT) > 0 ? NW / (2 * NKT) : 1;   // groups of d tiles
-        constexpr int MPG = (ND + MG - 1) / MG;                        // d tiles per group
-        for (int job = w; job < 2 * NKT * MG; job += NW) {
-            const int mg = job % MG, kh = job / MG, ks = kh >> 1, hh = kh & 1;
-            const int mt = 2 * ks + hh;
-            f32x4 acc[MPG];
+        constexpr int MG = NW / NKT > 0 ? NW / NKT : 1;     // groups of d tiles
+        constexpr int MPG = (ND + MG - 1) / MG;             // d tiles per group
+        for (int job = w; job < NKT * MG; job += NW) {
+            const int mg = job % MG, ks = job / MG;
+            f32x4 acc[2][MPG];
 #pragma unroll
-            for (int mi = 0; mi < MPG; ++mi) acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (mt < NB) {
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int mi = 0; mi < MPG; ++mi) acc[hh][mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int mt = 2 * ks + hh;
+                if (mt >= NB) continue;
                 for (int ss = mt / 2; ss < NKT; ++ss) {
                     const int zb = zoff(mt) + ss - mt / 2;
                     const bf16x8 ahi = __builtin_bit_cast(bf16x8, Zw[(2 * zb) * 64 + lane]);
@@ -727,21 +731,25 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
                                 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                     (__attribute__((address_space(3))) s16x4*)(Ks + kq(t0 + 16, d0)));
                             const bf16x8 bk = cat(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi4));
-                            acc[mi] = mma_bf16_k32(ahi, bk, acc[mi]);
-                            acc[mi] = mma_bf16_k32(alo, bk, acc[mi]);
+                            acc[hh][mi] = mma_bf16_k32(ahi, bk, acc[hh][mi]);
+                            acc[hh][mi] = mma_bf16_k32(alo, bk, acc[hh][mi]);
                         }
                     }
                 }
             }
-            const f32x4 bt4 = (mt < NB) ? *reinterpret_cast<const f32x4*>(&sc[1][16 * mt + 4 * g])
-                                        : f32x4{0.f, 0.f, 0.f, 0.f};
+            f32x4 bt4[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int mt = 2 * ks + hh;
+                bt4[hh] = (mt < NB) ? *reinterpret_cast<const f32x4*>(&sc[1][16 * mt + 4 * g]) : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
 #pragma unroll
             for (int mi = 0; mi < MPG; ++mi) {
                 const int m = mg * MPG + mi;
                 if (m < ND) {
-                    const f32x4 z = acc[mi] * bt4;
-                    const f16x4 z4 = {(f16)z[0], (f16)z[1], (f16)z[2], (f16)z[3]};
-                    reinterpret_cast<uint2*>(Zfr + (m * NKT + ks) * 64 + lane)[hh] = __builtin_bit_cast(uint2, z4);
+                    const f32x4 z0 = acc[0][mi] * bt4[0], z1 = acc[1][mi] * bt4[1];
+                    const f16x8 fr = {(f16)z0[0], (f16)z0[1], (f16)z0[2], (f16)z0[3], (f16)z1[0], (f16)z1[1], (f16)z1[2], (f16)z1[3]};
+                    Zfr[(m * NKT + ks) * 64 + lane] = __builtin_bit_cast(uint4, fr);
                 }
             }
         }
