@@ -835,10 +835,14 @@ __device__ __forceinline__ void wait_counter(int* cnt, int target) {
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
-// Make this wavefront's LDS writes (or completed LDS reads) visible, then set the counter.
+// Set a counter once this wavefront's earlier LDS writes (or reads) are done.  The LDS
+// performs the operations of one wavefront in the order they were issued, so a counter
+// store issued after them is seen by another wavefront only once they have taken effect:
+// the store needs to stay behind them in the instruction stream (an instruction of its own
+// with a memory clobber), not to wait for them.
 __device__ __forceinline__ void signal_counter(int* cnt, int value) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __hip_atomic_store(cnt, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const unsigned addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) int*)cnt;
+    asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(value) : "memory");
 }
 
 template <int NB>
@@ -1238,18 +1242,20 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
     // K fragments of a step, read one step ahead (while the state update runs); a trailing
     // half k-step (odd ND) has zero upper slots
     uint4 kf[NB][NKD];
-    auto read_k = [&](const ScanOps<NB, ND>& op) {
+    auto read_k = [&](const ScanOps<NB, ND>& op, int dep) {
 #pragma unroll
         for (int ks = 0; ks < NKD; ++ks)
 #pragma unroll
-            for (int mt = 0; mt < NB; ++mt) kf[mt][ks] = op.k[mt][ks][lane];
+            for (int mt = 0; mt < NB; ++mt) kf[mt][ks] = op.k[mt][ks][lane + dep];
     };
     wait_counter(&K.loaded[1], 1);
-    read_k(L.ops[0]);
+    read_k(L.ops[0], 0);
 #pragma unroll 1
     for (int n = 0; n < N; ++n) {
         const int sl = n % GDN_RING;
         const ScanOps<NB, ND>& op = L.ops[n % GDN_OPS];
+        // the loaders' count, read now so that it is back before the next step's K is read
+        const int ldc = __hip_atomic_load(&K.loaded[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         // the output ring slot of this step must have been released by every output
         // wavefront (the last counts seen are kept, so the counters are read only when needed)
 #pragma unroll
@@ -1336,16 +1342,22 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
         signal_counter(&K.ready[cc], n + 1);
-        // the next step's operands must have landed before its K is read below
-        if (n + 1 < N) wait_counter(&K.loaded[1], n + 2);
-        __builtin_amdgcn_sched_barrier(0);
+        // the next step's operands must have landed before its K is read (the addresses of
+        // the reads depend on the count, through an empty asm, so they follow it)
+        if (n + 1 < N) {
+            int kdep = 0;
+            if (ldc < n + 2) {
+                wait_counter(&K.loaded[1], n + 2);
+            }
+            asm volatile("" : "+v"(kdep) : "v"(ldc));
+            read_k(L.ops[(n + 1) % GDN_OPS], kdep);
+        }
         // S^T <- gamma_C S^T + Z^T R  (rows d, columns: state rows); a trailing 16-token
-        // step has zero upper slots in both operands.  The next step's K is read meanwhile.
+        // step has zero upper slots in both operands
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
             for (int m = 0; m < ND; ++m) P[m] = mma_f16_k32(__builtin_bit_cast(f16x8, zfr[m][kt]), Rb[kt], P[m]);
-        if (n + 1 < N) read_k(L.ops[(n + 1) % GDN_OPS]);
     }
     float* Sout = p.S_out[dir];
     if (Sout && tile_ok) {
