@@ -264,15 +264,6 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Token of local row t of processing step n: forward runs 0..N*C-1, reverse
-// runs N*C-1 down to 0 (the padding of a ragged sequence then lands beyond
-// T-1 in both directions).
-struct TokMap {
-    int base, sgn;
-    __device__ __forceinline__ int operator()(int n, int C, int t) const { return base + sgn * (n * C + t); }
-};
-
-
 // K and Q operand fragments by 16-token tile (token order).  Block (tile, ks) holds, for
 // lane r + 16 g, row 16 tile + r at d = 32 ks + 8 g .. +7 (16 bytes); a trailing single
 // tile of d (odd D/16) holds d = 16 (ND-1) + 4 g .. +3 and 8 zero bytes.  Processing tile mt
@@ -288,14 +279,6 @@ __device__ __forceinline__ const char* frag_base(const Params& p, int kind, int 
 
 // Compact LDS storage of the C x C matrices of a step by 16x16 blocks: only the
 // blocks on one side of the diagonal are kept (rows padded to 16-byte multiples).
-template <int NB, int LD_>
-struct UpperF32 {   // fp32 blocks (a, b) with a <= b (L^T and T^T), rows of LD_ floats
-    static constexpr int LD = LD_, COUNT = NB * (NB + 1) / 2, FLOATS = COUNT * 16 * LD;
-    __device__ static int at(int row, int col) {
-        const int a = row >> 4, b = col >> 4;
-        return (a * NB - (a * (a - 1)) / 2 + (b - a)) * (16 * LD) + (row & 15) * LD + (col & 15);
-    }
-};
 template <int NB>
 struct UpperF16 {   // fp16 blocks (a, b) with a <= b (L^T), rows of 16 halves
     static constexpr int COUNT = NB * (NB + 1) / 2, HALVES = COUNT * 256;
@@ -323,68 +306,78 @@ struct LowerF16 {   // fp16 blocks (a, b) with a >= b (A), rows of 16 halves; th
 };
 
 // ---------------------------------------------------------------------------
-// Chunk preparation: one workgroup (2 NB wavefronts) per (direction, b, h,
-// processing step n).  Rows are in processing order.  For the C tokens of the
-// step, with k^ = k/|k|, q^ = q/|q|, g = prefix of log a, gamma = e^g:
+// Chunk preparation: one workgroup (2 NB wavefronts) per (b, h, block j of C
+// tokens), for every requested direction at once.  The forward direction
+// processes block j as its step j, the reverse direction as its step N-1-j
+// (the blocks of the two directions coincide; the padding of a ragged sequence
+// lies beyond T-1 in both).  Shared by the directions: the K and Q rows, their
+// norms, the in-block log-gate prefix and the Gram products K K^T and Q K^T
+// (the forward direction takes their lower triangles, the reverse direction
+// the upper ones).  Per direction, in its processing order p (token j C + p
+// forward, j C + C-1-p reverse), with k^ = k/|k|, q^ = q/|q|, g = prefix of
+// log a along p and gamma = e^g:
 //   L[t,s] = beta_t e^{g_t-g_s} k^_t.k^_s (s < t),   T = (I + L)^{-1}
 //   A[t,s] = scale e^{g_t-g_s} q^_t.k^_s (s <= t)
 //   E = A T diag(beta)                  (output:  O = diag(c2) Q S^T + E R)
 //   Z = diag(beta) T^T diag(e^{g_C-g}/|k|) K  (state: S^T <- gamma_C S^T + Z^T R)
 // with R = V - diag(c1) K S^T, c1 = gamma/|k|, c2 = scale gamma/|q|.  (The gate
 // beta is folded into E and Z, so the serial scan needs one scale per token.)
-// E and Z^T are stored as fp16 MFMA fragments for the scan; the state dimension
-// d of Z^T follows the scan's state order (see dperm).
+// L, A and T are held in fp16 (T is built in fp32 arithmetic from fp16 blocks);
+// E and Z^T are stored as fp16 MFMA fragments for the scan, the state dimension
+// d of Z^T in the scan's state order (see dperm).
 // ---------------------------------------------------------------------------
 template <int NB, int ND>
 __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) void gdn_prep_kernel(Params p) {
     constexpr int C = 16 * NB, D = 16 * ND;
-    using UL = UpperF16<NB>;     // L^T (fp16: its rounding is below that of the fp16 E and Z it feeds)
-    using UB = UpperF32<NB, 20>; // T^T (also read down columns: padded rows)
-    using US = UpperF16S<NB>;    // T^T in fp16 (E's operand; stored over L)
-    using LB = LowerF16<NB>;     // A
+    using UL = UpperF16<NB>;     // L^T per direction
+    using US = UpperF16S<NB>;    // T^T per direction
+    using LB = LowerF16<NB>;     // A per direction (over L^T once T is built)
+    static_assert(UL::HALVES == LB::HALVES, "A reuses the storage of L^T");
     constexpr int NW = 2 * NB;   // wavefronts
     constexpr int NT = 64 * NW;
     constexpr int CH = D / 8;    // 16-byte chunks per row
     using BK = Blocks<NB>;
-    constexpr int NFT = BK::NFULL;
-    constexpr bool HT = BK::HALF;
-    constexpr int NKT = NFT + (HT ? 1 : 0);
+    constexpr int NKT = BK::NFULL + (BK::HALF ? 1 : 0);
     typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-    // Q rows (bf16) share storage with T^T (fp32), which is built after the Gram products
-    // K and Q rows (bf16, D per row); row t holds its 16-byte chunk c at position c ^ ((t >> 3) & 1),
-    // so that 16 rows read at one column are free of bank conflicts
+    // K and Q rows (bf16, D per row, token order); row t holds its 16-byte chunk c at position
+    // c ^ ((t >> 3) & 1), so that 16 rows read at one column are free of bank conflicts.  The Q
+    // rows are dead after the Gram products; T^T of both directions then takes their storage.
     auto kq = [](int t, int d) { return t * D + (((d >> 3) ^ ((t >> 3) & 1)) << 3) + (d & 7); };
-    // Z's A fragments: one per (row tile mt, 32-wide step ss >= mt/2), as a high/low pair
-    constexpr int NKT_ = Blocks<NB>::NFULL + (Blocks<NB>::HALF ? 1 : 0);
-    constexpr auto zoff = [](int mt) { int o = 0; for (int m2 = 0; m2 < mt; ++m2) o += NKT_ - m2 / 2; return o; };
-    constexpr int NZB = zoff(NB);
-    constexpr int Q_BYTES = C * D * 2, T_BYTES = UB::FLOATS * 4, ZW_BYTES = NZB * 2048;
-    constexpr int QT_BYTES = Q_BYTES > T_BYTES ? (Q_BYTES > ZW_BYTES ? Q_BYTES : ZW_BYTES) : (T_BYTES > ZW_BYTES ? T_BYTES : ZW_BYTES);
+    constexpr int Q_BYTES = C * D * 2, T2_BYTES = 2 * US::HALVES * 2;
+    constexpr int QT_BYTES = Q_BYTES > T2_BYTES ? Q_BYTES : T2_BYTES;
     __shared__ __align__(16) bf16 Ks[C * D];
     __shared__ __align__(16) char QT[QT_BYTES];
-    __shared__ __align__(16) f16 Lt[UL::HALVES];     // L transposed: Lt[s][t] = L[t][s], s < t
-    __shared__ __align__(16) f16 Am[LB::HALVES];     // A[t][s], s <= t (an fp16 operand of E only)
-    __shared__ __align__(16) float sc[5][C];      // 0: log a then g, 1: beta, 2: 1/|k|, 3: 1/|q|, 4: e^{g_C-g}/|k|
+    __shared__ __align__(16) f16 LA[2 * UL::HALVES];  // L^T per direction, then A per direction
+    __shared__ __align__(16) float sg[2][C];          // by token: forward, reverse inclusive log2-gate prefix
+    __shared__ __align__(16) float rk[C], rq[C];      // by token: 1/|k|, 1/|q|
+    __shared__ __align__(16) float bp[2][C];          // beta by processing row (forward = token order)
+    __shared__ __align__(16) f16 w16[2][C];           // e^{g_C-g}/|k| by processing row
     bf16* Qs = reinterpret_cast<bf16*>(QT);
-    float* Tt = reinterpret_cast<float*>(QT);     // T transposed: Tt[u][s] = T[s][u]
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, r = lane & 15;
-    const int n = blockIdx.x, bh = blockIdx.y, dir = p.dir0 + blockIdx.z;
+    const int j = blockIdx.x, bh = blockIdx.y;
     const int b = bh / p.H, h = bh - b * p.H;
     const int T = (int)p.T;
     const int N = (T + C - 1) / C;
-    const TokMap tok{dir ? N * C - 1 : 0, dir ? -1 : 1};
+    const int dlo = p.dir0, dhi = p.dir0 + p.ndirs - 1;
+    auto active = [&](int dir) { return dir >= dlo && dir <= dhi; };
+    // token row (within the block) of processing row t
+    auto mrow = [](int dir, int t) { return dir ? C - 1 - t : t; };
+    auto item_of = [&](int dir) {
+        const int n = dir ? N - 1 - j : j;
+        return p.ws + ((((int64_t)dir * p.B + b) * p.H + h) * p.nsub_max + n) * p.ws_item_bytes;
+    };
 
     {
-        // every global load of the step goes out before the first is used: the gates,
+        // every global load of the block goes out before the first is used: the gates,
         // then the K and Q rows (16-byte chunks, NLD per thread)
         float av = 1.f, bt = 0.f;
         bool gv = false;
         if (tid < C) {
-            const int tk = tok(n, C, tid);
-            gv = tk >= 0 && tk < T;
+            const int tk = j * C + tid;
+            gv = tk < T;
             if (gv) {
                 const int64_t gq = (int64_t)b * p.gs[0] + (int64_t)tk * p.gs[1] + (int64_t)h * p.gs[2];
                 av = p.a[gq];
@@ -403,14 +396,14 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
             const int idx = tid + i * NT;
             if (idx < C * CH) {
                 const int t = idx / CH, c = idx - t * CH;
-                const int tk = tok(n, C, t);
+                const int tk = j * C + t;
                 kv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, tk * ksb + 16 * c, 0, 0));
                 qv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(qr, tk * qsb + 16 * c, 0, 0));
             }
         }
         if (tid < C) {
-            sc[0][tid] = gv ? fmaxf(logf(av), GDN_MIN_LOG_DECAY) : 0.f;
-            sc[1][tid] = bt;
+            sg[0][tid] = gv ? fmaxf(logf(av), GDN_MIN_LOG_DECAY) : 0.f;   // log a until the prefix
+            bp[0][tid] = bt;
         }
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
@@ -440,84 +433,145 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
             }
         }
         ss = sum4(ss);
-        if (part == 0) sc[isk ? 2 : 3][t] = p.l2norm ? 1.f / sqrtf(ss + p.eps) : 1.f;
+        if (part == 0) (isk ? rk : rq)[t] = p.l2norm ? 1.f / sqrtf(ss + p.eps) : 1.f;
     }
-    // inclusive prefix of log a along the processing order (C <= 64: one wavefront), kept in
-    // base-2 units (every decay below is an exp2 of a difference of these)
+    // inclusive prefixes of log a within the block (C <= 64: one wavefront), in base-2 units
+    // (every decay below is an exp2 of a difference of these): forward over tokens <= t,
+    // reverse over tokens >= t
     if (w == 0) {
-        float x = (lane < C) ? sc[0][lane] : 0.f;
+        const float la = (lane < C) ? sg[0][lane] * 1.4426950408889634f : 0.f;
+        float x = la;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const float y = __shfl_up(x, off);
             if (lane >= off) x += y;
         }
-        if (lane < C) sc[0][lane] = x * 1.4426950408889634f;
+        const float tot = __shfl(x, C - 1);
+        if (lane < C) {
+            sg[0][lane] = x;
+            sg[1][lane] = tot - x + la;
+        }
     }
     __syncthreads();
-    if (tid < C) sc[4][tid] = __builtin_amdgcn_exp2f(sc[0][C - 1] - sc[0][tid]) * sc[2][tid];
 
-    // Gram tiles on MFMA: K K^T -> L (strictly lower, stored transposed), Q K^T -> A (lower incl. diagonal)
-    {
-        constexpr int NTILE = NB * (NB + 1) / 2, NGT = 2 * NTILE, TPW = (NGT + NW - 1) / NW;
+    // per direction and processing row: beta, e^{g_C-g}/|k|, and the step's scalars c1 (token
+    // order), c2 (token 16 mt + r at r * NB + mt: one vector load per lane of the scan's output
+    // wavefront) and gamma_C
+    if (tid < 2 * C) {
+        const int dir = tid / C, pr = tid - dir * C;
+        if (active(dir)) {
+            const int t = mrow(dir, pr);
+            const float g2 = sg[dir][t], gtot = sg[0][C - 1];
+            const float gam = __builtin_amdgcn_exp2f(g2);
+            if (dir) bp[1][pr] = bp[0][t];
+            w16[dir][pr] = (f16)(__builtin_amdgcn_exp2f(gtot - g2) * rk[t]);
+            float* scw = reinterpret_cast<float*>(item_of(dir) + 1024 * (BK::TOTAL + ND * NKT));
+            scw[pr] = gam * rk[t];
+            scw[C + (pr & 15) * NB + (pr >> 4)] = p.scale * gam * rq[t];
+            if (pr == 0) scw[2 * C] = __builtin_amdgcn_exp2f(gtot);
+        }
+    }
+
+    // Gram tiles on MFMA (token-order tiles: rows t = 16 mt + 4 g + i, column s = 16 nt + r).
+    //   Q K^T, all tiles a direction needs (forward s <= t, reverse s >= t): scale e^{g_t-g_s}
+    //     q^_t.k^_s with the direction's prefix, computed transposed (lane: column t, rows
+    //     s = 16 nt + 4 g + i) and kept in registers until L is no longer needed.
+    //   K K^T, tiles mt >= nt: forward L[t][s] = beta_t e^{g_t-g_s} k^_t.k^_s (s < t), stored
+    //     transposed; the reverse direction takes the mirror entry (processing rows C-1-s >
+    //     C-1-t) with its own prefix.
+    constexpr int NQ = NB * NB, TPQ = (NQ + NW - 1) / NW;
+    constexpr int NKK = NB * (NB + 1) / 2, TPK = (NKK + NW - 1) / NW;
+    auto q_needed = [&](int mt, int nt) { return (mt >= nt && active(0)) || (mt <= nt && active(1)); };
+    f16x4 qa[TPQ];
+    // operands of one Gram tile: A = rows arow of `arows`, B = K rows brow; chunk 4 ks + g of a
+    // row sits at (4 ks + g) ^ x = 4 ks + (g ^ x) with x = (row >> 3) & 1
+    auto gram = [&](int arow, int brow, const bf16* arows, const bf16* brows) {
+        bf16x8 aop[ND / 2 > 0 ? ND / 2 : 1], bop[ND / 2 > 0 ? ND / 2 : 1];
+        bf16x4 aoh, boh;
+        const bf16* ap = arows + arow * D + ((g ^ ((arow >> 3) & 1)) << 3);
+        const bf16* bpp = brows + brow * D + ((g ^ ((brow >> 3) & 1)) << 3);
 #pragma unroll
-        for (int it = 0; it < TPW; ++it) {
-            const int tt = w + it * NW;
-            if (tt >= NGT) break;
-            const bool isq = tt >= NTILE;
-            const int ti = isq ? tt - NTILE : tt;
-            int mt = 0;
-            while ((mt + 1) * (mt + 2) / 2 <= ti) ++mt;
-            const int nt = ti - mt * (mt + 1) / 2;
-            const bf16* arows = isq ? Qs : Ks;
-            const int ar = 16 * mt + r, br = 16 * nt + r;
-            bf16x8 aop[ND / 2 > 0 ? ND / 2 : 1], bop[ND / 2 > 0 ? ND / 2 : 1];
-            bf16x4 aoh, boh;
+        for (int ks = 0; ks < ND / 2; ++ks) {
+            aop[ks] = ld_bf16x8(ap + 32 * ks);
+            bop[ks] = ld_bf16x8(bpp + 32 * ks);
+        }
+        if constexpr (ND % 2) {
+            aoh = ld_bf16x4(arows + kq(arow, 32 * (ND / 2) + 4 * g));
+            boh = ld_bf16x4(brows + kq(brow, 32 * (ND / 2) + 4 * g));
+        }
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < ND / 2; ++ks) {
-                aop[ks] = ld_bf16x8(arows + kq(ar, 32 * ks + 8 * g));
-                bop[ks] = ld_bf16x8(Ks + kq(br, 32 * ks + 8 * g));
-            }
-            if constexpr (ND % 2) {
-                aoh = ld_bf16x4(arows + kq(ar, 32 * (ND / 2) + 4 * g));
-                boh = ld_bf16x4(Ks + kq(br, 32 * (ND / 2) + 4 * g));
-            }
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < ND / 2; ++ks) acc = mma_bf16_k32(aop[ks], bop[ks], acc);
+        if constexpr (ND % 2) acc = mma_bf16_k16(aoh, boh, acc);
+        return acc;
+    };
 #pragma unroll
-            for (int ks = 0; ks < ND / 2; ++ks) acc = mma_bf16_k32(aop[ks], bop[ks], acc);
-            if constexpr (ND % 2) acc = mma_bf16_k16(aoh, boh, acc);
-            // rows t = 16 mt + 4 g + i, column s = 16 nt + r:
-            //   L: beta_t e^{g_t-g_s} k^_t.k^_s (s < t),  A: scale e^{g_t-g_s} q^_t.k^_s (s <= t)
-            const int s = 16 * nt + r, t0 = 16 * mt + 4 * g;
-            const f32x4 gt = *reinterpret_cast<const f32x4*>(&sc[0][t0]);
-            f32x4 rt = *reinterpret_cast<const f32x4*>(&sc[isq ? 3 : 2][t0]);
-            rt = isq ? rt * p.scale : rt * *reinterpret_cast<const f32x4*>(&sc[1][t0]);
-            const float gs = sc[0][s], rs = sc[2][s];
-            f32x4 v;
+    for (int it = 0; it < TPQ; ++it) {
+        const int qi = w + it * NW;
+        qa[it] = f16x4{(f16)0.f, (f16)0.f, (f16)0.f, (f16)0.f};
+        if (qi < NQ) {
+            const int mt = qi / NB, nt = qi - mt * NB;
+            if (q_needed(mt, nt)) {
+                const f32x4 acc = gram(16 * nt + r, 16 * mt + r, Ks, Qs);
+                const int t = 16 * mt + r, s0 = 16 * nt + 4 * g;
+                const f32x4 gf = *reinterpret_cast<const f32x4*>(&sg[0][s0]);
+                const f32x4 gr = *reinterpret_cast<const f32x4*>(&sg[1][s0]);
+                const f32x4 rs = *reinterpret_cast<const f32x4*>(&rk[s0]);
+                const float gft = sg[0][t], grt = sg[1][t], rt = rq[t] * p.scale;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = acc[i] * (rt[i] * rs) * __builtin_amdgcn_exp2f(gt[i] - gs);
-            if (mt == nt) {   // the diagonal tile: only s < t (L) or s <= t (A)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = (isq ? s <= t0 + i : s < t0 + i) ? v[i] : 0.f;
-            }
-            if (!isq) {
-                *reinterpret_cast<f16x4*>(Lt + UL::at(s, t0)) = f16x4{(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Am[LB::at(t0 + i, s)] = (f16)v[i];
+                for (int i = 0; i < 4; ++i) {
+                    const int s = s0 + i;
+                    const bool fw = s <= t;   // forward prefix (on the diagonal both give e^0)
+                    const bool ok = s == t || (fw ? active(0) : active(1));
+                    const float v = acc[i] * (rt * rs[i]) * __builtin_amdgcn_exp2f(fw ? gft - gf[i] : grt - gr[i]);
+                    qa[it][i] = (f16)(ok ? v : 0.f);
+                }
             }
         }
     }
-    // the operand fragments of this step's token tiles (written by one direction only; Q before
-    // its rows are overwritten by T)
-    if (dir == p.dir0) {
+#pragma unroll
+    for (int it = 0; it < TPK; ++it) {
+        const int kt = (NW - 1 - w) + it * NW;
+        if (kt < NKK) {
+            int mt = 0;
+            while ((mt + 1) * (mt + 2) / 2 <= kt) ++mt;
+            const int nt = kt - mt * (mt + 1) / 2;
+            const f32x4 acc = gram(16 * mt + r, 16 * nt + r, Ks, Ks);
+            const int s = 16 * nt + r, t0 = 16 * mt + 4 * g;
+            const f32x4 rt = *reinterpret_cast<const f32x4*>(&rk[t0]);
+            const float rs = rk[s];
+            if (active(0)) {
+                const f32x4 gt = *reinterpret_cast<const f32x4*>(&sg[0][t0]);
+                const f32x4 bt = *reinterpret_cast<const f32x4*>(&bp[0][t0]);
+                const float gs = sg[0][s];
+                f16x4 v;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    v[i] = (f16)((s < t0 + i) ? acc[i] * (rt[i] * rs * bt[i]) * __builtin_amdgcn_exp2f(gt[i] - gs) : 0.f);
+                *reinterpret_cast<f16x4*>(LA + UL::at(s, t0)) = v;
+            }
+            if (active(1)) {
+                const f32x4 gt = *reinterpret_cast<const f32x4*>(&sg[1][t0]);
+                const float gs = sg[1][s], bs = bp[0][s];
+                f16* Lr = LA + UL::HALVES;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (s < t0 + i)
+                        Lr[UL::at(C - 1 - (t0 + i), C - 1 - s)] =
+                            (f16)(acc[i] * (rt[i] * rs * bs) * __builtin_amdgcn_exp2f(gs - gt[i]));
+            }
+        }
+    }
+    // the K and Q operand fragments of the block's token tiles (shared by both directions)
+    {
         constexpr int NKD = (ND + 1) / 2, NKF = ND / 2;
         const int ntile = (T + 15) / 16;
         for (int job = w; job < 2 * NB * NKD; job += NW) {
             const int kind = job / (NB * NKD), mt = (job / NKD) % NB, ks = job % NKD;
-            const int tile = frag_tile(dir, N, NB, n, mt);
+            const int tile = NB * j + mt;
             if (tile >= ntile) continue;
             const bf16* rows = kind ? Qs : Ks;
-            const int rr = 16 * mt + (dir ? 15 - r : r);
+            const int rr = 16 * mt + r;
             uint4 v;
             if (ks < NKF) {
                 v = *reinterpret_cast<const uint4*>(rows + kq(rr, 32 * ks + 8 * g));
@@ -531,209 +585,221 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
     }
     __syncthreads();
 
-    // T = (I + L)^{-1}, built transposed.  16x16 diagonal blocks: one lane per
-    // (block, column j), right-looking forward substitution; column j of T_bb is
-    // row j of Tt.
-    if (tid < C) {
-        const int o = 16 * (tid >> 4), j = tid & 15;
-        float x[16];
+    // T = (I + L)^{-1} per direction, built transposed in processing order.  16x16 diagonal
+    // blocks: one lane per (direction, block, column j), right-looking forward substitution in
+    // fp32; column j of T_bb is row j of T^T.
+    if (tid < 2 * C) {
+        const int dir = tid / C, tl = tid - dir * C;
+        if (active(dir)) {
+            const f16* Lt = LA + dir * UL::HALVES;
+            f16* T16 = reinterpret_cast<f16*>(QT) + dir * US::HALVES;
+            const int o = 16 * (tl >> 4), jc = tl & 15;
+            float x[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
+            for (int i = 0; i < 16; ++i) x[i] = (i == jc) ? 1.f : 0.f;
 #pragma unroll
-        for (int k = 0; k < 15; ++k) {
-            const f16* lcol = Lt + UL::at(o + k, o);   // L[o + i][o + k] for i > k
-            float lv[16];
+            for (int k = 0; k < 15; ++k) {
+                const f16* lcol = Lt + UL::at(o + k, o);   // L[o + i][o + k] for i > k
+                float lv[16];
 #pragma unroll
-            for (int i8 = 0; i8 < 2; ++i8) {
-                const f16x8 v8 = *reinterpret_cast<const f16x8*>(lcol + 8 * i8);
+                for (int i8 = 0; i8 < 2; ++i8) {
+                    const f16x8 v8 = *reinterpret_cast<const f16x8*>(lcol + 8 * i8);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) lv[8 * i8 + e] = (float)v8[e];
-            }
-#pragma unroll
-            for (int i = k + 1; i < 16; ++i) x[i] -= lv[i] * x[k];
-        }
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4)
-            *reinterpret_cast<f32x4*>(Tt + UB::at(o + j, o) + 4 * i4) =
-                f32x4{x[4 * i4], x[4 * i4 + 1], x[4 * i4 + 2], x[4 * i4 + 3]};
-    }
-    __syncthreads();
-    // off-diagonal blocks, by distance d from the diagonal, on fp32 MFMA (one wavefront per block):
-    //   T_ij = -T_ii sum_{k=j}^{i-1} L_ik T_kj
-    for (int d = 1; d < NB; ++d) {
-        if (w < NB - d) {
-            const int ib = w + d, jb = w;
-            f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            for (int kb = jb; kb < ib; ++kb) {
-                float la[4], tb[4];
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const int k = 16 * kb + 4 * kk + g;
-                    la[kk] = (float)Lt[UL::at(k, 16 * ib + r)];   // L[16 ib + r][k]
-                    tb[kk] = Tt[UB::at(16 * jb + r, k)];      // T[k][16 jb + r]
+                    for (int e = 0; e < 8; ++e) lv[8 * i8 + e] = (float)v8[e];
                 }
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) z = __builtin_amdgcn_mfma_f32_16x16x4f32(la[kk], tb[kk], z, 0, 0, 0);
+                for (int i = k + 1; i < 16; ++i) x[i] -= lv[i] * x[k];
             }
-            // z: lane (column r, group g) holds Z[4g + e][r]; B operand with k = 4g + kk
-            float ta[4];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) ta[kk] = Tt[UB::at(16 * ib + 4 * g + kk, 16 * ib + r)];   // T[16 ib + r][16 ib + 4g + kk]
-            f32x4 t4 = {0.f, 0.f, 0.f, 0.f};
+            for (int i8 = 0; i8 < 2; ++i8) {
+                f16x8 v8;
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) t4 = __builtin_amdgcn_mfma_f32_16x16x4f32(ta[kk], z[kk], t4, 0, 0, 0);
-            // T[16 ib + 4g + e][16 jb + r] -> Tt[16 jb + r][16 ib + 4g + e]
-            *reinterpret_cast<f32x4*>(Tt + UB::at(16 * jb + r, 16 * ib + 4 * g)) = -t4;
+                for (int e = 0; e < 8; ++e) v8[e] = (f16)x[8 * i8 + e];
+                *reinterpret_cast<f16x8*>(T16 + US::at(o + jc, o + 8 * i8)) = v8;
+            }
+        }
+    } else {
+        // the other wavefronts turn the K rows into fp16 in place (the operand form Z takes;
+        // exact for |k| entries in fp16's normal range)
+        for (int idx = tid - 2 * C; idx < C * CH; idx += NT - 2 * C) {
+            const int t = idx / CH, c = idx - t * CH;
+            uint4* pp = reinterpret_cast<uint4*>(Ks + kq(t, 8 * c));
+            const bf16x8 xv = __builtin_bit_cast(bf16x8, *pp);
+            f16x8 hv;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) hv[e] = (f16)(float)xv[e];
+            *pp = __builtin_bit_cast(uint4, hv);
+        }
+    }
+    __syncthreads();
+    // off-diagonal blocks, by distance d from the diagonal (one wavefront per direction and
+    // block), on fp16 MFMA: z = sum_{k=j}^{i-1} L_ik T_kj with two 16-blocks of k per product,
+    // then T_ij = -T_ii z.  L_ik and T_ii are read transposed from their transposed storage
+    // (lane r of a group supplies row r/4 and columns 4 (r%4) .. +3 of a 4x16 block and
+    // receives column r).
+    for (int d = 1; d < NB; ++d) {
+        const int dir = w / NB, wl = w - dir * NB;
+        if (active(dir) && wl < NB - d) {
+            const f16* Lt = LA + dir * UL::HALVES;
+            f16* T16 = reinterpret_cast<f16*>(QT) + dir * US::HALVES;
+            const int ib = wl + d, jb = wl;
+            f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            for (int kb0 = jb; kb0 < ib; kb0 += 2) {
+                // k-slots of group g: block kb0 + g/2, rows 8 (g%2) .. +7
+                const int kb = kb0 + (g >> 1), k0 = 16 * kb + 8 * (g & 1);
+                f16x8 ao, bo;
+                if (kb < ib) {
+                    const s16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4*)(Lt + UL::at(k0 + (r >> 2), 16 * ib + 4 * (r & 3))));
+                    const s16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4*)(Lt + UL::at(k0 + 4 + (r >> 2), 16 * ib + 4 * (r & 3))));
+                    const f16x4 a0h = __builtin_bit_cast(f16x4, a0), a1h = __builtin_bit_cast(f16x4, a1);
+                    ao = f16x8{a0h[0], a0h[1], a0h[2], a0h[3], a1h[0], a1h[1], a1h[2], a1h[3]};   // L[16 ib + r][k0 ..]
+                    bo = *reinterpret_cast<const f16x8*>(T16 + US::at(16 * jb + r, k0));            // T[k0 ..][16 jb + r]
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) ao[e] = bo[e] = (f16)0.f;
+                }
+                z = mma_f16_k32(ao, bo, z);
+            }
+            // z: lane (column r, group g) holds z[4g + e][16 jb + r], the B operand of
+            // T_ii z with k = 4g + e (upper slots zero); A = T[16 ib + r][16 ib + 4g + e]
+            const s16x4 ta = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(T16 + US::at(16 * ib + 4 * g + (r >> 2), 16 * ib + 4 * (r & 3))));
+            const f16x4 tah = __builtin_bit_cast(f16x4, ta);
+            const f16 z0 = (f16)0.f;
+            const f16x8 a2 = {tah[0], tah[1], tah[2], tah[3], z0, z0, z0, z0};
+            const f16x8 b2 = {(f16)z[0], (f16)z[1], (f16)z[2], (f16)z[3], z0, z0, z0, z0};
+            const f32x4 t4 = mma_f16_k32(a2, b2, f32x4{0.f, 0.f, 0.f, 0.f});
+            // T[16 ib + 4g + e][16 jb + r] -> T^T[16 jb + r][16 ib + 4g + e]
+            *reinterpret_cast<f16x4*>(T16 + US::at(16 * jb + r, 16 * ib + 4 * g)) =
+                f16x4{(f16)-t4[0], (f16)-t4[1], (f16)-t4[2], (f16)-t4[3]};
         }
         __syncthreads();
     }
 
-    // T^T once more, in the two forms its products take, from the fp32 blocks (read by every
-    // thread before the sync, then overwritten):
-    //   T16: fp16 blocks in L's storage (E's operand);
-    //   Zw:  for row tile mt and 32-wide step ss >= mt/2, the A fragment of Z, T[s][t] w[s] with
-    //        w = e^{g_C-g}/|k| (slots 16 (i/4) + 4 g + i%4 of the step), as a bf16 high/low pair
-    constexpr int NBLK = NB * (NB + 1) / 2;
-    f16* T16 = Lt;
-    uint4* Zw = reinterpret_cast<uint4*>(QT);
-    f16x8 t16v;
-    uint4 zwhi, zwlo;
-    int t16blk_a = 0, t16blk_b = 0, t16row = 0, t16c = 0, zb_ss = 0;
-    const bool do_t16 = tid < NBLK * 32, do_zw = tid < NZB * 64;
-    if (do_t16) {
-        const int q = tid >> 5;
-        t16row = (tid >> 1) & 15;
-        t16c = tid & 1;
-        int a = 0, rem = q;
-        while (rem >= NB - a) { rem -= NB - a; ++a; }
-        t16blk_a = a;
-        t16blk_b = a + rem;
-        const float* src = Tt + UB::at(16 * a + t16row, 16 * t16blk_b + 8 * t16c);
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(src), x1 = *reinterpret_cast<const f32x4*>(src + 4);
+    // A per direction in processing order (lower incl. the diagonal) over the dead L^T: the
+    // forward direction's entries in place, the reverse direction's mirrored; the diagonal
+    // blocks are written whole (zero above the diagonal)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            t16v[e] = (f16)x0[e];
-            t16v[4 + e] = (f16)x1[e];
+    for (int it = 0; it < TPQ; ++it) {
+        const int qi = w + it * NW;
+        if (qi < NQ) {
+            const int mt = qi / NB, nt = qi - mt * NB;
+            const int t = 16 * mt + r, s0 = 16 * nt + 4 * g;
+            if (mt >= nt && active(0)) {
+                f16x4 v;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = (s0 + i <= t) ? qa[it][i] : (f16)0.f;
+                *reinterpret_cast<f16x4*>(LA + LB::at(t, s0)) = v;
+            }
+            if (mt <= nt && active(1)) {
+                f16x4 v;   // processing columns C-4-s0 .. C-1-s0 hold tokens s0+3 .. s0
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = (s0 + 3 - i >= t) ? qa[it][3 - i] : (f16)0.f;
+                *reinterpret_cast<f16x4*>(LA + LB::HALVES + LB::at(C - 1 - t, C - 4 - s0)) = v;
+            }
         }
     }
-    if (do_zw) {
-        const int zb = tid >> 6;
-        int mt = 0;
-        while (zoff(mt + 1) <= zb) ++mt;
-        zb_ss = mt / 2 + (zb - zoff(mt));
-        bf16x8 hi8, lo8;
+    __syncthreads();
+
+    // E and Z per direction, as independent jobs over the wavefronts
+    constexpr int MG = NW / NKT > 0 ? NW / NKT : 1;     // groups of d tiles in a Z job
+    constexpr int MPG = (ND + MG - 1) / MG;             // d tiles per group
+    constexpr int NEJ = BK::TOTAL, NZJ = NKT * MG, NJ = NEJ + NZJ;
+    for (int job = w; job < p.ndirs * NJ; job += NW) {
+        const int dir = dlo + job / NJ, jj = job % NJ;
+        const f16* T16 = reinterpret_cast<const f16*>(QT) + dir * US::HALVES;
+        const f16* Am = LA + dir * LB::HALVES;
+        uint4* Efr = reinterpret_cast<uint4*>(item_of(dir));    // BK::TOTAL blocks
+        uint4* Zfr = Efr + BK::TOTAL * 64;                      // ND x NKT blocks
+        if (jj < NEJ) {
+            // E^T = T^T A^T, tile (ut, tt) = sum_s T^T[u][s] A[t][s] over s in [16 ut, 16 tt + 16);
+            // the output tiles (2ks, mt) and (2ks + 1, mt) form the O-product A fragment (mt, ks).
+            const int blk = jj;
+            int mt = 0;
+            while (BK::offset(mt + 1) <= blk) ++mt;
+            const int ks = blk - BK::offset(mt);
+            f32x4 et[2];
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const int s0 = 32 * zb_ss + 16 * hf + 4 * g;
-            f32x4 tv = {0.f, 0.f, 0.f, 0.f}, wv = {0.f, 0.f, 0.f, 0.f};
-            if (s0 < C && 2 * zb_ss + hf >= mt) {   // T[s][t] = 0 for s < t
-                tv = *reinterpret_cast<const f32x4*>(Tt + UB::at(16 * mt + r, s0));
-                wv = *reinterpret_cast<const f32x4*>(&sc[4][s0]);
+            for (int hh = 0; hh < 2; ++hh) {
+                const int ut = 2 * ks + hh;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                if (ut <= mt) {
+                    // contraction over s in 32-wide steps (zero outside the triangle)
+                    for (int ss = (16 * ut) / 32; ss * 32 < 16 * (mt + 1); ++ss) {
+                        f16x8 ao, bo;
+                        const int sb = 2 * ss + (g >> 1);   // 16-wide block of this lane's s
+                        if (32 * ss + 8 * g < C && sb >= ut && sb <= mt) {
+                            ao = *reinterpret_cast<const f16x8*>(T16 + US::at(16 * ut + r, 32 * ss + 8 * g));
+                            bo = *reinterpret_cast<const f16x8*>(Am + LB::at(16 * mt + r, 32 * ss + 8 * g));
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) ao[e] = bo[e] = (f16)0.f;
+                        }
+                        acc = mma_f16_k32(ao, bo, acc);
+                    }
+                }
+                // column beta_u of T diag(beta): rows u = 16 ut + 4 g + i of this E^T tile
+                const f32x4 bu = (ut < NB) ? *reinterpret_cast<const f32x4*>(&bp[dir][16 * ut + 4 * g])
+                                           : f32x4{0.f, 0.f, 0.f, 0.f};
+                et[hh] = acc * bu;
             }
+            f16x8 fr;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float v = tv[e] * wv[e];
-                const bf16 hv = (bf16)v;
-                hi8[4 * hf + e] = hv;
-                lo8[4 * hf + e] = (bf16)(v - (float)hv);
+                fr[e] = (f16)et[0][e];
+                fr[4 + e] = (f16)et[1][e];
             }
-        }
-        zwhi = __builtin_bit_cast(uint4, hi8);
-        zwlo = __builtin_bit_cast(uint4, lo8);
-    }
-    __syncthreads();
-    if (do_t16) *reinterpret_cast<f16x8*>(T16 + US::at(16 * t16blk_a + t16row, 16 * t16blk_b + 8 * t16c)) = t16v;
-    if (do_zw) {
-        const int zb = tid >> 6;
-        Zw[(2 * zb) * 64 + lane] = zwhi;
-        Zw[(2 * zb + 1) * 64 + lane] = zwlo;
-    }
-    __syncthreads();
-
-    char* item = p.ws + ((((int64_t)dir * p.B + b) * p.H + h) * p.nsub_max + n) * p.ws_item_bytes;
-    uint4* Efr = reinterpret_cast<uint4*>(item);                          // BK::TOTAL blocks
-    uint4* Zfr = Efr + BK::TOTAL * 64;                                    // ND x NKT blocks
-    float* scw = reinterpret_cast<float*>(item + 1024 * (BK::TOTAL + ND * NKT));
-
-    // E^T = T^T A^T, tile (ut, tt) = sum_s Tt[u][s] A[t][s] over s in [16 ut, 16 tt + 16); the
-    // output tiles (2ks, mt) and (2ks + 1, mt) form the O-product A fragment (mt, ks) directly.
-    for (int blk = w; blk < BK::TOTAL; blk += NW) {
-        int mt = 0;
-        while (BK::offset(mt + 1) <= blk) ++mt;
-        const int ks = blk - BK::offset(mt);
-        f32x4 et[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const int ut = 2 * ks + hh;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            if (ut <= mt) {
-                // contraction over s in 32-wide steps (zero outside the triangle)
-                for (int ss = (16 * ut) / 32; ss * 32 < 16 * (mt + 1); ++ss) {
-                    f16x8 ao, bo;
-                    const int sb = 2 * ss + (g >> 1);   // 16-wide block of this lane's s
-                    if (32 * ss + 8 * g < C && sb >= ut && sb <= mt) {
-                        ao = *reinterpret_cast<const f16x8*>(T16 + US::at(16 * ut + r, 32 * ss + 8 * g));
-                        bo = *reinterpret_cast<const f16x8*>(Am + LB::at(16 * mt + r, 32 * ss + 8 * g));
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) ao[e] = bo[e] = (f16)0.f;
-                    }
-                    acc = mma_f16_k32(ao, bo, acc);
-                }
-            }
-            // column beta_u of T diag(beta): rows u = 16 ut + 4 g + i of this E^T tile
-            const f32x4 bu = (ut < NB) ? *reinterpret_cast<const f32x4*>(&sc[1][16 * ut + 4 * g])
-                                       : f32x4{0.f, 0.f, 0.f, 0.f};
-            et[hh] = acc * bu;
-        }
-        f16x8 fr;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            fr[e] = (f16)et[0][e];
-            fr[4 + e] = (f16)et[1][e];
-        }
-        Efr[blk * 64 + lane] = __builtin_bit_cast(uint4, fr);
-    }
-
-    // Z = diag(beta) T^T diag(e^{g_C-g}/|k|) K: A operand = the Zw fragments (k = s in slots
-    // 16 (i/4) + 4 g + i%4 of each 32-wide step); B operand = raw K rows read transposed, column r
-    // of tile m being state index dperm(m, r).  A job takes the row tiles mt = 2 ks, 2 ks + 1 and a
-    // group of d tiles; output tiles (2ks, m) and (2ks + 1, m) form the state-update fragment
-    // (m, ks), written whole.
-    {
-        constexpr int MG = NW / NKT > 0 ? NW / NKT : 1;     // groups of d tiles
-        constexpr int MPG = (ND + MG - 1) / MG;             // d tiles per group
-        for (int job = w; job < NKT * MG; job += NW) {
-            const int mg = job % MG, ks = job / MG;
+            Efr[blk * 64 + lane] = __builtin_bit_cast(uint4, fr);
+        } else {
+            // Z = diag(beta) T^T diag(w) K on fp16 MFMA, w = e^{g_C-g}/|k|: A operand T[s][t] w_s
+            // (row t, k = s in slots 16 (i/4) + 4 g + i%4 of each 32-wide step), B operand the fp16 K
+            // rows read transposed (token row of processing row s; column r of tile m is state
+            // index dperm(m, r)).  A job takes the row tiles mt = 2 ks, 2 ks + 1 and a group of d
+            // tiles; output tiles (2ks, m) and (2ks + 1, m) form the state-update fragment
+            // (m, ks), written whole.
+            const int zj = jj - NEJ, mg = zj % MG, ks = zj / MG;
             f32x4 acc[2][MPG];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
                 for (int mi = 0; mi < MPG; ++mi) acc[hh][mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int ss = ks; ss < NKT; ++ss) {
+                f16x8 aw[2];
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const int mt = 2 * ks + hh;
-                if (mt >= NB) continue;
-                for (int ss = mt / 2; ss < NKT; ++ss) {
-                    const int zb = zoff(mt) + ss - mt / 2;
-                    const bf16x8 ahi = __builtin_bit_cast(bf16x8, Zw[(2 * zb) * 64 + lane]);
-                    const bf16x8 alo = __builtin_bit_cast(bf16x8, Zw[(2 * zb + 1) * 64 + lane]);
-                    const int t0 = 32 * ss + 4 * g + (r >> 2);
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int mt = 2 * ks + hh;
 #pragma unroll
-                    for (int mi = 0; mi < MPG; ++mi) {
-                        const int m = mg * MPG + mi;
-                        if (m < ND) {
-                            const int d0 = dperm<ND>(m, 4 * (r & 3));   // 4 consecutive d per lane quad
-                            s16x4 lo = {0, 0, 0, 0}, hi4 = {0, 0, 0, 0};
-                            if (32 * ss < C)
-                                lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(Ks + kq(t0, d0)));
-                            if (32 * ss + 16 < C)
-                                hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                    (__attribute__((address_space(3))) s16x4*)(Ks + kq(t0 + 16, d0)));
-                            const bf16x8 bk = cat(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi4));
-                            acc[hh][mi] = mma_bf16_k32(ahi, bk, acc[hh][mi]);
-                            acc[hh][mi] = mma_bf16_k32(alo, bk, acc[hh][mi]);
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const int s0 = 32 * ss + 16 * hf + 4 * g;
+                        f16x4 tv = {(f16)0.f, (f16)0.f, (f16)0.f, (f16)0.f};
+                        if (mt < NB && s0 < C && 2 * ss + hf >= mt) {   // T[s][t] = 0 for s < t
+                            tv = *reinterpret_cast<const f16x4*>(T16 + US::at(16 * mt + r, s0));
+                            tv = tv * *reinterpret_cast<const f16x4*>(&w16[dir][s0]);
                         }
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) aw[hh][4 * hf + e] = tv[e];
+                    }
+                }
+                const int t0 = 32 * ss + 4 * g + (r >> 2);
+#pragma unroll
+                for (int mi = 0; mi < MPG; ++mi) {
+                    const int m = mg * MPG + mi;
+                    if (m < ND) {
+                        const int d0 = dperm<ND>(m, 4 * (r & 3));   // 4 consecutive d per lane quad
+                        s16x4 lo = {0, 0, 0, 0}, hi4 = {0, 0, 0, 0};
+                        if (32 * ss < C)
+                            lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                (__attribute__((address_space(3))) s16x4*)(Ks + kq(mrow(dir, t0), d0)));
+                        if (32 * ss + 16 < C)
+                            hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                (__attribute__((address_space(3))) s16x4*)(Ks + kq(mrow(dir, t0 + 16), d0)));
+                        const f16x4 lh = __builtin_bit_cast(f16x4, lo), hh4 = __builtin_bit_cast(f16x4, hi4);
+                        const f16x8 bh16 = {lh[0], lh[1], lh[2], lh[3], hh4[0], hh4[1], hh4[2], hh4[3]};
+#pragma unroll
+                        for (int hh = 0; hh < 2; ++hh)
+                            if (2 * ks + hh < NB) acc[hh][mi] = mma_f16_k32(aw[hh], bh16, acc[hh][mi]);
                     }
                 }
             }
@@ -741,7 +807,7 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 const int mt = 2 * ks + hh;
-                bt4[hh] = (mt < NB) ? *reinterpret_cast<const f32x4*>(&sc[1][16 * mt + 4 * g]) : f32x4{0.f, 0.f, 0.f, 0.f};
+                bt4[hh] = (mt < NB) ? *reinterpret_cast<const f32x4*>(&bp[dir][16 * mt + 4 * g]) : f32x4{0.f, 0.f, 0.f, 0.f};
             }
 #pragma unroll
             for (int mi = 0; mi < MPG; ++mi) {
@@ -753,15 +819,6 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
                 }
             }
         }
-    }
-
-    // scalars: c1 in token order; c2 with token 16 mt + r at r * NB + mt (one vector load
-    // per lane of the scan's output wavefront); gamma_C
-    if (tid < C) {
-        const float gam = __builtin_amdgcn_exp2f(sc[0][tid]);
-        scw[tid] = gam * sc[2][tid];
-        scw[C + (tid & 15) * NB + (tid >> 4)] = p.scale * gam * sc[3][tid];
-        if (tid == 0) scw[2 * C] = __builtin_amdgcn_exp2f(sc[0][C - 1]);
     }
 }
 
@@ -1423,7 +1480,7 @@ template <int NB, int ND>
 static hipError_t run_chunked(const Params& p, hipStream_t s, Timing* tm) {
     const int nsub = (int)((p.T + 16 * NB - 1) / (16 * NB));
     tm_begin(tm, s, KPREP);
-    hipLaunchKernelGGL((gdn_prep_kernel<NB, ND>), dim3(nsub, p.B * p.H, p.ndirs), dim3(128 * NB), 0, s, p);
+    hipLaunchKernelGGL((gdn_prep_kernel<NB, ND>), dim3(nsub, p.B * p.H), dim3(128 * NB), 0, s, p);
     tm_end(tm, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
