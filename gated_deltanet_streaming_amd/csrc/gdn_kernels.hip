@@ -39,6 +39,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -175,9 +177,32 @@ __device__ __forceinline__ void st_elem(void* base, int64_t idx, float v) {
     else reinterpret_cast<bf16*>(base)[idx] = (bf16)v;
 }
 
+// Lane exchange within a row of 16 lanes (DPP).  Lanes whose source is out of range, or
+// whose row is masked off, read 0.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWS, 0xf, true));
+}
+// out[n] = x of lane n of the lane's row of 16, n = 0..15 (row broadcasts)
+template <int... Is>
+__device__ __forceinline__ void row_broadcasts(float x, float* out, std::integer_sequence<int, Is...>) {
+    ((out[Is] = dpp<0x150 + Is>(x)), ...);
+}
+// sum over the 4 lanes of a quad (quad permutations [1,0,3,2] and [2,3,0,1])
 __device__ __forceinline__ float sum4(float x) {
-    x += __shfl_xor(x, 1);
-    x += __shfl_xor(x, 2);
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    return x;
+}
+// inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 within each row of 16, then
+// the last lane of row 0 into row 1 and of row 2 into row 3, then lane 31 into rows 2 and 3
+__device__ __forceinline__ float wave_prefix(float x) {
+    x += dpp<0x111>(x);
+    x += dpp<0x112>(x);
+    x += dpp<0x114>(x);
+    x += dpp<0x118>(x);
+    x += dpp<0x142, 0xa>(x);
+    x += dpp<0x143, 0xc>(x);
     return x;
 }
 
@@ -353,6 +378,7 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
     __shared__ __align__(16) float rk[C], rq[C];      // by token: 1/|k|, 1/|q|
     __shared__ __align__(16) float bp[2][C];          // beta by processing row (forward = token order)
     __shared__ __align__(16) f16 w16[2][C];           // e^{g_C-g}/|k| by processing row
+    __shared__ int jobctr;                            // next E/Z job
     bf16* Qs = reinterpret_cast<bf16*>(QT);
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -405,6 +431,7 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
             sg[0][tid] = gv ? fmaxf(logf(av), GDN_MIN_LOG_DECAY) : 0.f;   // log a until the prefix
             bp[0][tid] = bt;
         }
+        if (tid == 0) jobctr = 0;
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
             const int idx = tid + i * NT;
@@ -415,7 +442,7 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // per-token inverse norms: 4 lanes per row, 16 rows per wavefront; waves < NB take the
     // K rows, the others the Q rows
@@ -440,19 +467,14 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
     // reverse over tokens >= t
     if (w == 0) {
         const float la = (lane < C) ? sg[0][lane] * 1.4426950408889634f : 0.f;
-        float x = la;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(x, off);
-            if (lane >= off) x += y;
-        }
-        const float tot = __shfl(x, C - 1);
+        const float x = wave_prefix(la);
+        const float tot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), C - 1));
         if (lane < C) {
             sg[0][lane] = x;
             sg[1][lane] = tot - x + la;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // per direction and processing row: beta, e^{g_C-g}/|k|, and the step's scalars c1 (token
     // order), c2 (token 16 mt + r at r * NB + mt: one vector load per lane of the scan's output
@@ -583,7 +605,7 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
             reinterpret_cast<uint4*>(dst)[lane] = v;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // T = (I + L)^{-1} per direction, built transposed in processing order.  16x16 diagonal
     // blocks: one lane per (direction, block, column j), right-looking forward substitution in
@@ -631,7 +653,7 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
             *pp = __builtin_bit_cast(uint4, hv);
         }
     }
-    __syncthreads();
+    lds_barrier();
     // off-diagonal blocks, by distance d from the diagonal (one wavefront per direction and
     // block), on fp16 MFMA: z = sum_{k=j}^{i-1} L_ik T_kj with two 16-blocks of k per product,
     // then T_ij = -T_ii z.  L_ik and T_ii are read transposed from their transposed storage
@@ -675,7 +697,7 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
             *reinterpret_cast<f16x4*>(T16 + US::at(16 * jb + r, 16 * ib + 4 * g)) =
                 f16x4{(f16)-t4[0], (f16)-t4[1], (f16)-t4[2], (f16)-t4[3]};
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     // A per direction in processing order (lower incl. the diagonal) over the dead L^T: the
@@ -701,14 +723,21 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
-    // E and Z per direction, as independent jobs over the wavefronts
+    // E and Z per direction, as independent jobs that the wavefronts take in turn from an LDS
+    // counter (the longer Z jobs first, then the E blocks of the lower rows first)
     constexpr int MG = NW / NKT > 0 ? NW / NKT : 1;     // groups of d tiles in a Z job
     constexpr int MPG = (ND + MG - 1) / MG;             // d tiles per group
-    constexpr int NEJ = BK::TOTAL, NZJ = NKT * MG, NJ = NEJ + NZJ;
-    for (int job = w; job < p.ndirs * NJ; job += NW) {
-        const int dir = dlo + job / NJ, jj = job % NJ;
+    constexpr int NEJ = BK::TOTAL, NZJ = NKT * MG;
+    for (;;) {
+        int q = 0;
+        if (lane == 0) q = atomicAdd(&jobctr, 1);
+        q = __builtin_amdgcn_readfirstlane(q);
+        if (q >= p.ndirs * (NEJ + NZJ)) break;
+        const int nz = p.ndirs * NZJ;
+        const int dir = dlo + (q < nz ? q : q - nz) % p.ndirs;
+        const int jj = q < nz ? NEJ + q / p.ndirs : NEJ - 1 - (q - nz) / p.ndirs;
         const f16* T16 = reinterpret_cast<const f16*>(QT) + dir * US::HALVES;
         const f16* Am = LA + dir * LB::HALVES;
         uint4* Efr = reinterpret_cast<uint4*>(item_of(dir));    // BK::TOTAL blocks
@@ -946,7 +975,7 @@ struct ScanCtr {
     int ready[GDN_COLS];                 // steps each chain wavefront has published to the output
                                          // ring (and so finished reading from the operand slots)
     int done[ScanShape<NB>::NOUT];       // steps each output wavefront has taken from the ring
-    int loaded[2];                       // steps whose operands loader 0 / both loaders have landed
+    int loaded[2];                       // steps whose operands loader 0 / loader 1 has landed
 };
 
 // Direct global-to-LDS load of 16 bytes per lane into a wave-uniform LDS block.
@@ -1145,9 +1174,9 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
     constexpr int NKT = NFT + (HT ? 1 : 0);
     constexpr int SCAL_OFF = 1024 * (BK::TOTAL + ND * NKT);   // scalars of an item
     constexpr int NOUT = ScanShape<NB>::NOUT;
-    // loads the loader wavefronts issue per step: K, V and the scales; Z
-    constexpr int NDMA0 = NB * NKD + NB + 1;
-    constexpr int NDMA1 = ND * NKT;
+    // loads the loader wavefronts issue per step: K and the scales; Z and V
+    constexpr int NDMA0 = NB * NKD + 1;
+    constexpr int NDMA1 = ND * NKT + NB;
     typedef short s16x4 __attribute__((ext_vector_type(4)));
 
     __shared__ __align__(16) ScanLds<NB, ND> L;
@@ -1198,8 +1227,8 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
         // Deposit the chain's operands of step n in slot n % GDN_OPS once both chain
         // wavefronts are done with that slot, with direct global-to-LDS loads, and publish
         // a step once its loads have landed (each keeps the next step's loads in flight).
-        // Loader 0 moves K, V and the scales, loader 1 the state-update fragments Z;
-        // loader 1 publishes a step for the chain only once loader 0 has landed it too.
+        // Loader 0 moves K and the scales, loader 1 the state-update fragments Z and V;
+        // each publishes its own count.
         const int part = wave - (GDN_COLS + NOUT);
         // K fragments: 16 bytes per lane, the rows of a tile reversed for the reverse direction
         const auto kfr = make_rsrc(frag_base(p, 0, b, h, NKD), (uint32_t)(((T + 15) / 16) * NKD * 1024));
@@ -1223,9 +1252,6 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
 #pragma unroll
                 for (int ks = 0; ks < NKD; ++ks) dma16(kfr, &op.k[mt][ks][0], kfl, (tile * NKD + ks) * 1024);
             }
-            const auto vrs = vr.rsrc(n);
-#pragma unroll
-            for (int jj = 0; jj < NB; ++jj) dma16(vrs, &op.v[jj][0], voff[jj], 0);
             dma16(irs, &op.sc[0], scoff, n * (int)ib + SCAL_OFF);
         };
         auto issue1 = [&](int n) {
@@ -1236,6 +1262,9 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
 #pragma unroll
                 for (int kt = 0; kt < NKT; ++kt)
                     dma16(irs, &op.z[m][kt][0], 16 * lane, ioff + 1024 * (BK::TOTAL + m * NKT + kt));
+            const auto vrs = vr.rsrc(n);
+#pragma unroll
+            for (int jj = 0; jj < NB; ++jj) dma16(vrs, &op.v[jj][0], voff[jj], 0);
         };
         // The direct loads complete in order and count on the vector memory counter;
         // once it has dropped to this step's count, the previous step's data is in LDS.
@@ -1252,13 +1281,11 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
                 issue1(n);
                 if (n > 0) {
                     wait_vmcnt<(NDMA1 < 63 ? NDMA1 : 63)>();
-                    wait_counter(&K.loaded[0], n);
                     publish_loaded(&K.loaded[1], n);
                 }
             }
         }
         wait_vmcnt<0>();
-        if (part == 1) wait_counter(&K.loaded[0], N);
         publish_loaded(&K.loaded[part], N);
         return;
     }
@@ -1305,14 +1332,17 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
 #pragma unroll
             for (int mt = 0; mt < NB; ++mt) kf[mt][ks] = op.k[mt][ks][lane + dep];
     };
+    wait_counter(&K.loaded[0], 1);
     wait_counter(&K.loaded[1], 1);
     read_k(L.ops[0], 0);
 #pragma unroll 1
     for (int n = 0; n < N; ++n) {
         const int sl = n % GDN_RING;
         const ScanOps<NB, ND>& op = L.ops[n % GDN_OPS];
-        // the loaders' count, read now so that it is back before the next step's K is read
-        const int ldc = __hip_atomic_load(&K.loaded[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        // the loaders' counts, read now so that they are back before the next step's K is read
+        const int ld0 = __hip_atomic_load(&K.loaded[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const int ld1 = __hip_atomic_load(&K.loaded[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const int ldc = ld0 < ld1 ? ld0 : ld1;
         // the output ring slot of this step must have been released by every output
         // wavefront (the last counts seen are kept, so the counters are read only when needed)
 #pragma unroll
@@ -1348,11 +1378,11 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
         for (int ks = 0; ks < NKD; ++ks) L.ringP[sl][ks][cc][lane] = __builtin_bit_cast(uint4, Pb[ks]);
         // the step's remaining operands, in order of use: the scales and V (read back
         // transposed: lane quad q of group g supplies row 16 mt + 4 g + i, columns
-        // 16 cc + 4 q .. +3 of the deposited rows), then Z
-        f32x4 c1[NB];
-#pragma unroll
-        for (int mt = 0; mt < NB; ++mt) c1[mt] = __builtin_bit_cast(f32x4, op.sc[4 * mt + g]);
-        const float gC = __builtin_bit_cast(f32x4, op.sc[16]).x;
+        // 16 cc + 4 q .. +3 of the deposited rows), then Z.  c1 of the tokens 16 mt + 4 g + i
+        // this lane scales is read once per row of 16 lanes (lane 4 mt + i holds it) and
+        // handed round the row by broadcasts.
+        const float c1l = reinterpret_cast<const float*>(&op.sc[0])[16 * (r >> 2) + 4 * g + (r & 3)];
+        const float gC = reinterpret_cast<const float*>(&op.sc[16])[0];
         bf16x4 vt[NB];
 #pragma unroll
         for (int mt = 0; mt < NB; ++mt) {
@@ -1378,11 +1408,13 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
 #pragma unroll
         for (int m = 0; m < ND; ++m) P[m] = P[m] * gC;
         // R = V - diag(e^g / |k|) X, as fp16 B operand (k = token)
+        float c1[16];
+        row_broadcasts(c1l, c1, std::make_integer_sequence<int, 16>{});
         f16x8 Rb[NKT];
 #pragma unroll
         for (int mt = 0; mt < NB; ++mt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Rb[mt >> 1][4 * (mt & 1) + i] = (f16)((float)vt[mt][i] - c1[mt][i] * X[mt][i]);
+            for (int i = 0; i < 4; ++i) Rb[mt >> 1][4 * (mt & 1) + i] = (f16)((float)vt[mt][i] - c1[4 * mt + i] * X[mt][i]);
         if constexpr (HT) {
 #pragma unroll
             for (int i = 4; i < 8; ++i) Rb[NFT][i] = (f16)0.f;
@@ -1404,6 +1436,7 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
         if (n + 1 < N) {
             int kdep = 0;
             if (ldc < n + 2) {
+                wait_counter(&K.loaded[0], n + 2);
                 wait_counter(&K.loaded[1], n + 2);
             }
             asm volatile("" : "+v"(kdep) : "v"(ldc));
