@@ -882,7 +882,8 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
 // ---------------------------------------------------------------------------
 #define GDN_COLS 2       // 16-row column tiles of the state per workgroup
 #define GDN_RING 3        // output ring slots
-#define GDN_OPS 3         // operand ring slots (the loader runs up to two steps ahead)
+#define GDN_OPS 3         // operand ring slots
+#define GDN_STAGES 2      // register stages of each loader (its loads run up to GDN_STAGES steps ahead of the ring)
 #define GDN_SPIN_LIMIT (1 << 22)
 
 template <int NT, int ND>
@@ -938,9 +939,9 @@ struct ScanShape {
     static constexpr int THREADS = 64 * (GDN_COLS + NOUT + 2);   // + chain wavefronts + two loaders
 };
 
-// One step's chain operands as the loader wavefront deposits them (direct
-// global-to-LDS loads: lane l of a 16-byte load lands at byte 16 l of its block),
-// so each block is one MFMA operand fragment read back with one 16-byte LDS read.
+// One step's chain operands as the loader wavefronts deposit them (lane l's 16 bytes of a
+// block at byte 16 l), so each block is one MFMA operand fragment read back with one
+// 16-byte LDS read.
 template <int NB, int ND>
 struct ScanOps {
     static constexpr int NKD = (ND + 1) / 2;   // 32-wide k-steps over d (the last half-filled for odd ND)
@@ -967,9 +968,7 @@ struct ScanLds {
 __device__ __forceinline__ int vswz(int t) { return 2 * ((t >> 2) & 1); }
 __device__ __forceinline__ int oswz(int t) { return (t >> 2) & 3; }
 
-// Progress counters of the scan's wavefronts.  A separate LDS object from the
-// operand slots, so that the compiler need not order the counters behind the
-// direct global-to-LDS loads in flight.
+// Progress counters of the scan's wavefronts (an LDS object of their own).
 template <int NB>
 struct ScanCtr {
     int ready[GDN_COLS];                 // steps each chain wavefront has published to the output
@@ -978,14 +977,9 @@ struct ScanCtr {
     int loaded[2];                       // steps whose operands loader 0 / loader 1 has landed
 };
 
-// Direct global-to-LDS load of 16 bytes per lane into a wave-uniform LDS block.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void* lds, int voff, int soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
-}
-// Store a progress counter to LDS.  Written as an instruction of its own so that the
-// compiler does not hold it behind every direct global-to-LDS load in flight (it
-// cannot tell the counter from the loads' destinations); the caller orders it
-// after the loads it publishes with wait_vmcnt.
+// Store a progress counter to LDS as an instruction of its own: it takes effect after the
+// wavefront's earlier LDS stores (one wavefront's LDS operations complete in issue order),
+// and the memory clobber keeps the compiler from moving those stores past it.
 __device__ __forceinline__ void publish_loaded(int* cnt, int value) {
     const unsigned addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) int*)cnt;
     asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(value) : "memory");
@@ -1225,8 +1219,9 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
     if (wave >= GDN_COLS + NOUT) {
         // ------------------------------ loader wavefronts ------------------------------
         // Deposit the chain's operands of step n in slot n % GDN_OPS once both chain
-        // wavefronts are done with that slot, with direct global-to-LDS loads, and publish
-        // a step once its loads have landed (each keeps the next step's loads in flight).
+        // wavefronts are done with that slot, and publish the step.  The operands are
+        // loaded into registers GDN_STAGES steps before they are deposited, so each step's
+        // loads are in flight while the chain works ~GDN_STAGES + 2 steps behind them.
         // Loader 0 moves K and the scales, loader 1 the state-update fragments Z and V;
         // each publishes its own count.
         const int part = wave - (GDN_COLS + NOUT);
@@ -1243,50 +1238,74 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
             voff[jj] = (row0 + 16 * (j >> 1) < p.Dv) ? vr.row(t) + 2 * row0 + 16 * j : (int)0x80000000;
         }
         const int scoff = lane < 16 ? 16 * lane : (lane == 16 ? 8 * C : 0);
-        auto issue0 = [&](int n) {
-            ScanOps<NB, ND>& op = L.ops[n % GDN_OPS];
+        static_assert(GDN_STAGES * NDMA0 <= 63 && GDN_STAGES * NDMA1 <= 63, "loads in flight per loader");
+        auto ld16 = [](__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+            return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0));
+        };
+        // loader 0: K fragments (NB x NKD blocks), then the scalars; loader 1: Z (ND x NKT), then V (NB)
+        auto load0 = [&](uint4* st, int n) {
 #pragma unroll
             for (int mt = 0; mt < NB; ++mt) {
                 // tiles past the last token read as zero (outside the resource)
                 const int tile = frag_tile(dir, N, NB, n, mt);
 #pragma unroll
-                for (int ks = 0; ks < NKD; ++ks) dma16(kfr, &op.k[mt][ks][0], kfl, (tile * NKD + ks) * 1024);
+                for (int ks = 0; ks < NKD; ++ks) st[mt * NKD + ks] = ld16(kfr, kfl, (tile * NKD + ks) * 1024);
             }
-            dma16(irs, &op.sc[0], scoff, n * (int)ib + SCAL_OFF);
+            st[NB * NKD] = ld16(irs, scoff, n * (int)ib + SCAL_OFF);
         };
-        auto issue1 = [&](int n) {
+        auto put0 = [&](const uint4* st, int n) {
             ScanOps<NB, ND>& op = L.ops[n % GDN_OPS];
+#pragma unroll
+            for (int mt = 0; mt < NB; ++mt)
+#pragma unroll
+                for (int ks = 0; ks < NKD; ++ks) op.k[mt][ks][lane] = st[mt * NKD + ks];
+            op.sc[lane] = st[NB * NKD];
+        };
+        auto load1 = [&](uint4* st, int n) {
             const int ioff = n * (int)ib;
 #pragma unroll
             for (int m = 0; m < ND; ++m)
 #pragma unroll
-                for (int kt = 0; kt < NKT; ++kt)
-                    dma16(irs, &op.z[m][kt][0], 16 * lane, ioff + 1024 * (BK::TOTAL + m * NKT + kt));
+                for (int kt = 0; kt < NKT; ++kt) st[m * NKT + kt] = ld16(irs, 16 * lane, ioff + 1024 * (BK::TOTAL + m * NKT + kt));
             const auto vrs = vr.rsrc(n);
 #pragma unroll
-            for (int jj = 0; jj < NB; ++jj) dma16(vrs, &op.v[jj][0], voff[jj], 0);
+            for (int jj = 0; jj < NB; ++jj) st[ND * NKT + jj] = ld16(vrs, voff[jj], 0);
         };
-        // The direct loads complete in order and count on the vector memory counter;
-        // once it has dropped to this step's count, the previous step's data is in LDS.
-        for (int n = 0; n < N; ++n) {
+        auto put1 = [&](const uint4* st, int n) {
+            ScanOps<NB, ND>& op = L.ops[n % GDN_OPS];
 #pragma unroll
-            for (int c = 0; c < GDN_COLS; ++c) wait_counter(&K.ready[c], n + 1 - GDN_OPS);
-            if (part == 0) {
-                issue0(n);
-                if (n > 0) {
-                    wait_vmcnt<(NDMA0 < 63 ? NDMA0 : 63)>();   // step n - 1 has landed
-                    publish_loaded(&K.loaded[0], n);
-                }
-            } else {
-                issue1(n);
-                if (n > 0) {
-                    wait_vmcnt<(NDMA1 < 63 ? NDMA1 : 63)>();
-                    publish_loaded(&K.loaded[1], n);
+            for (int m = 0; m < ND; ++m)
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt) op.z[m][kt][lane] = st[m * NKT + kt];
+#pragma unroll
+            for (int jj = 0; jj < NB; ++jj) op.v[jj][lane] = st[ND * NKT + jj];
+        };
+        // Per step n: wait for slot n % GDN_OPS, wait for stage n % GDN_STAGES (the loads of the
+        // other stages may still be in flight: the loads of a wavefront complete in order), write
+        // it to the slot, publish, and reload the stage with step n + GDN_STAGES.
+        auto run = [&](auto load, auto put, auto wait_stage) {
+            constexpr int NL = NDMA1 > NDMA0 ? NDMA1 : NDMA0;
+            uint4 st[GDN_STAGES][NL];
+#pragma unroll
+            for (int i = 0; i < GDN_STAGES; ++i) load(st[i], i < N ? i : N - 1);
+            for (int n = 0; n < N; n += GDN_STAGES) {
+#pragma unroll
+                for (int i = 0; i < GDN_STAGES; ++i) {
+                    const int m = n + i;
+                    if (m >= N) break;
+#pragma unroll
+                    for (int c = 0; c < GDN_COLS; ++c) wait_counter(&K.ready[c], m + 1 - GDN_OPS);
+                    wait_stage();
+                    put(st[i], m);
+                    publish_loaded(&K.loaded[part], m + 1);
+                    load(st[i], m + GDN_STAGES < N ? m + GDN_STAGES : N - 1);
                 }
             }
-        }
-        wait_vmcnt<0>();
-        publish_loaded(&K.loaded[part], N);
+            wait_vmcnt<0>();
+        };
+        // the other stages' loads may still be in flight
+        if (part == 0) run(load0, put0, [] { wait_vmcnt<(GDN_STAGES - 1) * NDMA0>(); });
+        else run(load1, put1, [] { wait_vmcnt<(GDN_STAGES - 1) * NDMA1>(); });
         return;
     }
     if (wave == GDN_COLS) {
