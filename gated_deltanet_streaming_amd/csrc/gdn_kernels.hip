@@ -854,23 +854,20 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
 // ---------------------------------------------------------------------------
 // Chunk scan: one workgroup per (direction, b, h, slice of 32 state rows),
 // serial over the processing steps.  Rows of S evolve independently, so the
-// slices of a head need no exchange.  Each MFMA operand fragment loaded for a
-// step (K, Z, Q, E) feeds the two 16-row column tiles of the slice.
-//   wave 0 (chain):   X = K S^T, R = V - diag(c1) X; publishes the step's state
-//                     (bf16) and R (fp16) to an LDS ring, then
-//                     S^T <- gamma_C S^T + Z^T R.  The state slice lives in its
-//                     MFMA accumulators for the whole call.
-//   waves 1.. (output, one per half of the step's token tiles):
-//                     O^T = S Q^T diag(c2) + R^T E^T from the published
-//                     fragments (each lane stores 4 consecutive state rows of
-//                     one token).
-// The wavefronts are coupled only through the ring (GDN_RING slots, LDS
-// counters with bounded spins), so the output wavefronts may trail the chain
-// by up to GDN_RING - 1 steps.  Operands are prefetched with 16-byte loads as
-// soon as their registers are free (K two steps ahead, V and the scales one
-// step ahead, Z at the start of its step); the register file and the 63
-// vector memory instructions the hardware tracks per wavefront bound the
-// buffering.  An
+// slices of a head need no exchange.  Six wavefronts with fixed roles:
+//   chain (2, one per 16-row column tile of the slice): per step X = K S^T,
+//                     R = V - diag(c1) X; the step's state (bf16) and R (fp16)
+//                     go to an LDS ring, then S^T <- gamma_C S^T + Z^T R.  The
+//                     state tile lives in MFMA accumulators for the whole call.
+//   output (2, one per half of the step's token tiles): O^T = S Q^T diag(c2) +
+//                     R^T E^T from the ring and their own Q, E and c2 (loaded
+//                     two steps ahead); bf16 tiles leave through LDS staging.
+//   loader (2): deposit each step's K, scalars (loader 0) and Z, V (loader 1)
+//                     in a 3-slot operand ring, loaded into registers two steps
+//                     before.
+// The wavefronts are coupled only through the rings and LDS counters with
+// bounded spins: the output wavefronts may trail the chain by up to
+// ring_slots() - 1 steps, the loaders run ahead of it by up to two slots.  An
 // operand register of an MFMA is refilled only after a result depending on
 // that MFMA has been consumed.
 //
@@ -881,7 +878,9 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
 // multiple of 32) are computed from zero inputs and never stored.
 // ---------------------------------------------------------------------------
 #define GDN_COLS 2       // 16-row column tiles of the state per workgroup
-#define GDN_RING 3        // output ring slots
+// output ring slots
+template <int ND>
+__host__ __device__ constexpr int ring_slots() { return 3; }
 #define GDN_OPS 3         // operand ring slots
 #define GDN_STAGES 2      // register stages of each loader (its loads run up to GDN_STAGES steps ahead of the ring)
 #define GDN_SPIN_LIMIT (1 << 22)
@@ -956,8 +955,8 @@ template <int NB, int ND>
 struct ScanLds {
     static constexpr int NKD = (ND + 1) / 2;
     static constexpr int NKT = Blocks<NB>::NFULL + (Blocks<NB>::HALF ? 1 : 0);
-    uint4 ringP[GDN_RING][NKD][GDN_COLS][64];
-    uint4 ringR[GDN_RING][NKT][GDN_COLS][64];
+    uint4 ringP[ring_slots<ND>()][NKD][GDN_COLS][64];
+    uint4 ringR[ring_slots<ND>()][NKT][GDN_COLS][64];
     ScanOps<NB, ND> ops[GDN_OPS];
     uint4 ostage[ScanShape<NB>::NOUT][ScanShape<NB>::TPO][64];   // bf16 output tiles on their way out
 };
@@ -1055,7 +1054,7 @@ __device__ __forceinline__ void scan_output(const Params& p, ScanLds<NB, ND>& L,
     load_out(oA, 0);
     load_out(oB, N > 1 ? 1 : 0);
     auto out_step = [&](OutIn& o, int n) {
-        const int sl = n % GDN_RING;
+        const int sl = n % ring_slots<ND>();
 #pragma unroll
         for (int c = 0; c < GDN_COLS; ++c) wait_counter(&K.ready[c], n + 1);
         bf16x8 Pb[NKD][GDN_COLS];
@@ -1356,7 +1355,7 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
     read_k(L.ops[0], 0);
 #pragma unroll 1
     for (int n = 0; n < N; ++n) {
-        const int sl = n % GDN_RING;
+        const int sl = n % ring_slots<ND>();
         const ScanOps<NB, ND>& op = L.ops[n % GDN_OPS];
         // the loaders' counts, read now so that they are back before the next step's K is read
         const int ld0 = __hip_atomic_load(&K.loaded[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -1366,8 +1365,8 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
         // wavefront (the last counts seen are kept, so the counters are read only when needed)
 #pragma unroll
         for (int o = 0; o < NOUT; ++o)
-            if (done_seen[o] < n + 1 - GDN_RING) {
-                wait_counter(&K.done[o], n + 1 - GDN_RING);
+            if (done_seen[o] < n + 1 - ring_slots<ND>()) {
+                wait_counter(&K.done[o], n + 1 - ring_slots<ND>());
                 done_seen[o] = __hip_atomic_load(&K.done[o], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
         // state as bf16 operand: k-slot e of lane group g <-> d = dperm(2 ks + e/4, 4 g + e%4)
