@@ -990,7 +990,13 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((V & 15) | (7 << 4) | (15 << 8) | ((V >> 4) << 14));
 }
 
-// Output wavefront `O`: token tiles [O * TPO, (O + 1) * TPO) of every step.
+// Output wavefront `O`: token tiles out_tile(O, 0 .. TPO-1) of every step.  With two tiles each,
+// wavefront O takes tiles O and NB-1-O, so both carry the same number of E blocks (a tile's
+// E blocks grow with its distance from the start of the step).
+template <int NB>
+__host__ __device__ constexpr int out_tile(int O, int tt) {
+    return ScanShape<NB>::TPO == 2 ? (tt == 0 ? O : NB - 1 - O) : O * ScanShape<NB>::TPO + tt;
+}
 template <int NB, int ND, int O>
 __device__ __forceinline__ void scan_output(const Params& p, ScanLds<NB, ND>& L, ScanCtr<NB>& K, int lane, int b, int h, int dir, int T,
                                             int N, int row0, const char* item0, int64_t ib) {
@@ -999,8 +1005,9 @@ __device__ __forceinline__ void scan_output(const Params& p, ScanLds<NB, ND>& L,
     using BK = Blocks<NB>;
     constexpr int NKT = BK::NFULL + (BK::HALF ? 1 : 0);
     constexpr int TPO = ScanShape<NB>::TPO;
-    constexpr int MT0 = O * TPO;
-    constexpr int EB0 = BK::offset(MT0), EB = BK::offset(MT0 + TPO) - EB0;   // E blocks of these tiles
+    // E blocks of this wavefront's tiles, tile after tile
+    constexpr auto eoff = [](int tt) { int o = 0; for (int t2 = 0; t2 < tt; ++t2) o += BK::count(out_tile<NB>(O, t2)); return o; };
+    constexpr int EB = eoff(TPO);
     constexpr int SCAL_OFF = 1024 * (BK::TOTAL + ND * NKT);
     const int r = lane & 15, g = lane >> 4;
     struct OutIn {
@@ -1018,14 +1025,14 @@ __device__ __forceinline__ void scan_output(const Params& p, ScanLds<NB, ND>& L,
                         p.os[1] * oesz, T, C, N, dir, oesz * D};
     int ooff[TPO];
 #pragma unroll
-    for (int tt = 0; tt < TPO; ++tt) ooff[tt] = orow.row(16 * (MT0 + tt) + r) + oesz * (row0 + 4 * g);   // token, state rows row0 + 4g ..
+    for (int tt = 0; tt < TPO; ++tt) ooff[tt] = orow.row(16 * out_tile<NB>(O, tt) + r) + oesz * (row0 + 4 * g);   // token, state rows row0 + 4g ..
     // bf16: the tiles go out through LDS, lane quad l/4 storing token l/4's 64-byte slice
     // (chunks past d_v are stored outside the resource, i.e. dropped)
     const int st = lane >> 2, sj = (lane & 3) ^ oswz(lane >> 2);
     int soff[TPO];
 #pragma unroll
     for (int tt = 0; tt < TPO; ++tt)
-        soff[tt] = (row0 + 16 * (sj >> 1) < p.Dv) ? orow.row(16 * (MT0 + tt) + st) + 2 * row0 + 16 * sj : (int)0x80000000;
+        soff[tt] = (row0 + 16 * (sj >> 1) < p.Dv) ? orow.row(16 * out_tile<NB>(O, tt) + st) + 2 * row0 + 16 * sj : (int)0x80000000;
     bool col_ok[GDN_COLS];
 #pragma unroll
     for (int c = 0; c < GDN_COLS; ++c) col_ok[c] = row0 + 16 * c < p.Dv;
@@ -1035,19 +1042,22 @@ __device__ __forceinline__ void scan_output(const Params& p, ScanLds<NB, ND>& L,
     auto load_out = [&](OutIn& o, int n) {
 #pragma unroll
         for (int tt = 0; tt < TPO; ++tt) {
-            const int tile = frag_tile(dir, N, NB, n, MT0 + tt);   // past the last token: zero
+            const int tile = frag_tile(dir, N, NB, n, out_tile<NB>(O, tt));   // past the last token: zero
 #pragma unroll
             for (int ks = 0; ks < NKD; ++ks)
                 o.q.op[tt][ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(qfr, qfl, (tile * NKD + ks) * 1024, 0));
         }
         const int ioff = n * (int)ib;
 #pragma unroll
-        for (int e = 0; e < EB; ++e)
-            o.efr[e] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(irs, 16 * lane, ioff + 1024 * (EB0 + e), 0));
-        // c2 of tokens 16 mt + r, mt = MT0 .. MT0 + TPO - 1 (lane-major scalars)
+        for (int tt = 0; tt < TPO; ++tt)
+#pragma unroll
+            for (int kt = 0; kt < BK::count(out_tile<NB>(O, tt)); ++kt)
+                o.efr[eoff(tt) + kt] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(irs, 16 * lane, ioff + 1024 * (BK::offset(out_tile<NB>(O, tt)) + kt), 0));
+        // c2 of tokens 16 mt + r of this wavefront's tiles mt (lane-major scalars)
 #pragma unroll
         for (int tt = 0; tt < TPO; ++tt)
-            o.c2[tt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(irs, 4 * (NB * r + MT0 + tt),
+            o.c2[tt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(irs, 4 * (NB * r + out_tile<NB>(O, tt)),
                                                                                       ioff + SCAL_OFF + 4 * C, 0));
     };
 
@@ -1100,8 +1110,8 @@ __device__ __forceinline__ void scan_output(const Params& p, ScanLds<NB, ND>& L,
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
             for (int tt = 0; tt < TPO; ++tt) {
-                if (kt >= BK::count(MT0 + tt)) continue;
-                const f16x8 ef = __builtin_bit_cast(f16x8, o.efr[BK::offset(MT0 + tt) - EB0 + kt]);
+                if (kt >= BK::count(out_tile<NB>(O, tt))) continue;
+                const f16x8 ef = __builtin_bit_cast(f16x8, o.efr[eoff(tt) + kt]);
 #pragma unroll
                 for (int c = 0; c < GDN_COLS; ++c) Ot[tt][c] = mma_f16_k32(Rb[kt][c], ef, Ot[tt][c]);
             }
