@@ -381,7 +381,9 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
     __shared__ int jobctr;                            // next E/Z job
     bf16* Qs = reinterpret_cast<bf16*>(QT);
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // the wavefront index is uniform: in a scalar register, so that everything derived from
+    // it (tile and job assignment, addresses) is scalar work
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, r = lane & 15;
     const int j = blockIdx.x, bh = blockIdx.y;
     const int b = bh / p.H, h = bh - b * p.H;
