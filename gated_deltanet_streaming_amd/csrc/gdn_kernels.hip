@@ -393,10 +393,12 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
     auto active = [&](int dir) { return dir >= dlo && dir <= dhi; };
     // token row (within the block) of processing row t
     auto mrow = [](int dir, int t) { return dir ? C - 1 - t : t; };
-    auto item_of = [&](int dir) {
+    auto item_addr = [&](int dir) {
         const int n = dir ? N - 1 - j : j;
         return p.ws + ((((int64_t)dir * p.B + b) * p.H + h) * p.nsub_max + n) * p.ws_item_bytes;
     };
+    char* const items[2] = {item_addr(0), item_addr(1)};   // this block's item in either direction
+    auto item_of = [&](int dir) { return items[dir]; };
 
     {
         // every global load of the block goes out before the first is used: the gates,
@@ -590,10 +592,11 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
     {
         constexpr int NKD = (ND + 1) / 2, NKF = ND / 2;
         const int ntile = (T + 15) / 16;
+        char* const fragb[2] = {const_cast<char*>(frag_base(p, 0, b, h, NKD)) + (int64_t)NB * j * NKD * 1024,
+                                const_cast<char*>(frag_base(p, 1, b, h, NKD)) + (int64_t)NB * j * NKD * 1024};
         for (int job = w; job < 2 * NB * NKD; job += NW) {
             const int kind = job / (NB * NKD), mt = (job / NKD) % NB, ks = job % NKD;
-            const int tile = NB * j + mt;
-            if (tile >= ntile) continue;
+            if (NB * j + mt >= ntile) continue;
             const bf16* rows = kind ? Qs : Ks;
             const int rr = 16 * mt + r;
             uint4 v;
@@ -603,8 +606,7 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
                 const uint2 hv = *reinterpret_cast<const uint2*>(rows + kq(rr, 16 * (ND - 1) + 4 * g));
                 v = uint4{hv.x, hv.y, 0u, 0u};
             }
-            char* dst = const_cast<char*>(frag_base(p, kind, b, h, NKD)) + ((int64_t)tile * NKD + ks) * 1024;
-            reinterpret_cast<uint4*>(dst)[lane] = v;
+            reinterpret_cast<uint4*>(fragb[kind] + (mt * NKD + ks) * 1024)[lane] = v;
         }
     }
     lds_barrier();
@@ -732,14 +734,24 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
     constexpr int MG = NW / NKT > 0 ? NW / NKT : 1;     // groups of d tiles in a Z job
     constexpr int MPG = (ND + MG - 1) / MG;             // d tiles per group
     constexpr int NEJ = BK::TOTAL, NZJ = NKT * MG;
+    // E block -> (row tile, 32-wide step)
+    struct EBlocks { int mt[NEJ], ks[NEJ]; };
+    constexpr EBlocks eblk = [] {
+        EBlocks e{};
+        int k = 0;
+        for (int m = 0; m < NB; ++m)
+            for (int s2 = 0; s2 < BK::count(m); ++s2) { e.mt[k] = m; e.ks[k] = s2; ++k; }
+        return e;
+    }();
+    const int dsh = p.ndirs - 1;   // 0 or 1: job index -> direction by a shift, not a division
+    const int nz = NZJ << dsh;
     for (;;) {
         int q = 0;
         if (lane == 0) q = atomicAdd(&jobctr, 1);
         q = __builtin_amdgcn_readfirstlane(q);
-        if (q >= p.ndirs * (NEJ + NZJ)) break;
-        const int nz = p.ndirs * NZJ;
-        const int dir = dlo + (q < nz ? q : q - nz) % p.ndirs;
-        const int jj = q < nz ? NEJ + q / p.ndirs : NEJ - 1 - (q - nz) / p.ndirs;
+        if (q >= ((NEJ + NZJ) << dsh)) break;
+        const int dir = dlo + ((q < nz ? q : q - nz) & dsh);
+        const int jj = q < nz ? NEJ + (q >> dsh) : NEJ - 1 - ((q - nz) >> dsh);
         const f16* T16 = reinterpret_cast<const f16*>(QT) + dir * US::HALVES;
         const f16* Am = LA + dir * LB::HALVES;
         uint4* Efr = reinterpret_cast<uint4*>(item_of(dir));    // BK::TOTAL blocks
@@ -748,9 +760,7 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
             // E^T = T^T A^T, tile (ut, tt) = sum_s T^T[u][s] A[t][s] over s in [16 ut, 16 tt + 16);
             // the output tiles (2ks, mt) and (2ks + 1, mt) form the O-product A fragment (mt, ks).
             const int blk = jj;
-            int mt = 0;
-            while (BK::offset(mt + 1) <= blk) ++mt;
-            const int ks = blk - BK::offset(mt);
+            const int mt = eblk.mt[blk], ks = eblk.ks[blk];
             f32x4 et[2];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
@@ -791,6 +801,19 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
             // tiles; output tiles (2ks, m) and (2ks + 1, m) form the state-update fragment
             // (m, ks), written whole.
             const int zj = jj - NEJ, mg = zj % MG, ks = zj / MG;
+            // K (fp16) read transposed: lane r of group g supplies processing row t + 4 g + r/4 at
+            // state indices dperm(m, 4 (r%4)) .. +3.  Its address is kq(mrow(dir, row), d): the
+            // row part is a lane constant plus a scalar step, and the chunk swizzle bit of the row
+            // ((row >> 3) & 1) depends on the lane only.
+            const int u = 4 * g + (r >> 2);
+            const int xs = dir ? 1 - ((u >> 3) & 1) : ((u >> 3) & 1);
+            const int kl = (dir ? C - 1 - u : u) * D;
+            const int rstep = dir ? -D : D;
+            const int cb = 8 * ((r & 3) ^ xs), cbs = 8 * (((r & 3) >> 1) ^ xs) + 4 * (r & 1);
+            auto kaddr = [&](int trow, int m) {
+                const int col = (m < (ND & ~1)) ? 32 * (m >> 1) + 4 * (m & 1) + cb : 16 * m + cbs;
+                return Ks + kl + trow * rstep + col;
+            };
             f32x4 acc[2][MPG];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh)
@@ -813,19 +836,15 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
                         for (int e = 0; e < 4; ++e) aw[hh][4 * hf + e] = tv[e];
                     }
                 }
-                const int t0 = 32 * ss + 4 * g + (r >> 2);
 #pragma unroll
                 for (int mi = 0; mi < MPG; ++mi) {
                     const int m = mg * MPG + mi;
                     if (m < ND) {
-                        const int d0 = dperm<ND>(m, 4 * (r & 3));   // 4 consecutive d per lane quad
                         s16x4 lo = {0, 0, 0, 0}, hi4 = {0, 0, 0, 0};
                         if (32 * ss < C)
-                            lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                (__attribute__((address_space(3))) s16x4*)(Ks + kq(mrow(dir, t0), d0)));
+                            lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)kaddr(32 * ss, m));
                         if (32 * ss + 16 < C)
-                            hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                (__attribute__((address_space(3))) s16x4*)(Ks + kq(mrow(dir, t0 + 16), d0)));
+                            hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)kaddr(32 * ss + 16, m));
                         const f16x4 lh = __builtin_bit_cast(f16x4, lo), hh4 = __builtin_bit_cast(f16x4, hi4);
                         const f16x8 bh16 = {lh[0], lh[1], lh[2], lh[3], hh4[0], hh4[1], hh4[2], hh4[3]};
 #pragma unroll
