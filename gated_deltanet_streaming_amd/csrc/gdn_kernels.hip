@@ -577,14 +577,15 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
                 *reinterpret_cast<f16x4*>(LA + UL::at(s, t0)) = v;
             }
             if (active(1)) {
+                // entries with s >= t (diagonal tiles only) land at row >= column of the mirrored
+                // diagonal block, a part nothing reads: stored without a branch; the mirrored
+                // rows C-1-t0-i of one lane are consecutive rows of one 16x16 block
                 const f32x4 gt = *reinterpret_cast<const f32x4*>(&sg[1][t0]);
                 const float gs = sg[1][s], bs = bp[0][s];
-                f16* Lr = LA + UL::HALVES;
+                f16* Lr = LA + UL::HALVES + UL::at(C - 1 - t0, C - 1 - s);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (s < t0 + i)
-                        Lr[UL::at(C - 1 - (t0 + i), C - 1 - s)] =
-                            (f16)(acc[i] * (rt[i] * rs * bs) * __builtin_amdgcn_exp2f(gs - gt[i]));
+                    Lr[-16 * i] = (f16)(acc[i] * (rt[i] * rs * bs) * __builtin_amdgcn_exp2f(fminf(gs - gt[i], 0.f)));
             }
         }
     }
