@@ -544,13 +544,20 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
                 const f32x4 gr = *reinterpret_cast<const f32x4*>(&sg[1][s0]);
                 const f32x4 rs = *reinterpret_cast<const f32x4*>(&rk[s0]);
                 const float gft = sg[0][t], grt = sg[1][t], rt = rq[t] * p.scale;
+                if (mt != nt) {
+                    // the whole tile belongs to one direction (forward below the diagonal)
+                    const f32x4 gd = mt > nt ? gft - gf : grt - gr;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int s = s0 + i;
-                    const bool fw = s <= t;   // forward prefix (on the diagonal both give e^0)
-                    const bool ok = s == t || (fw ? active(0) : active(1));
-                    const float v = acc[i] * (rt * rs[i]) * __builtin_amdgcn_exp2f(fw ? gft - gf[i] : grt - gr[i]);
-                    qa[it][i] = (f16)(ok ? v : 0.f);
+                    for (int i = 0; i < 4; ++i) qa[it][i] = (f16)(acc[i] * (rt * rs[i]) * __builtin_amdgcn_exp2f(gd[i]));
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int s = s0 + i;
+                        const bool fw = s <= t;   // forward prefix (on the diagonal both give e^0)
+                        const bool ok = s == t || (fw ? active(0) : active(1));
+                        const float v = acc[i] * (rt * rs[i]) * __builtin_amdgcn_exp2f(fw ? gft - gf[i] : grt - gr[i]);
+                        qa[it][i] = (f16)(ok ? v : 0.f);
+                    }
                 }
             }
         }
@@ -715,15 +722,19 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
             const int mt = qi / NB, nt = qi - mt * NB;
             const int t = 16 * mt + r, s0 = 16 * nt + 4 * g;
             if (mt >= nt && active(0)) {
-                f16x4 v;
+                f16x4 v = qa[it];
+                if (mt == nt) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = (s0 + i <= t) ? qa[it][i] : (f16)0.f;
+                    for (int i = 0; i < 4; ++i) v[i] = (s0 + i <= t) ? v[i] : (f16)0.f;
+                }
                 *reinterpret_cast<f16x4*>(LA + LB::at(t, s0)) = v;
             }
             if (mt <= nt && active(1)) {
-                f16x4 v;   // processing columns C-4-s0 .. C-1-s0 hold tokens s0+3 .. s0
+                f16x4 v = {qa[it][3], qa[it][2], qa[it][1], qa[it][0]};   // processing columns C-4-s0 .. C-1-s0
+                if (mt == nt) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = (s0 + 3 - i >= t) ? qa[it][3 - i] : (f16)0.f;
+                    for (int i = 0; i < 4; ++i) v[i] = (s0 + 3 - i >= t) ? v[i] : (f16)0.f;
+                }
                 *reinterpret_cast<f16x4*>(LA + LB::HALVES + LB::at(C - 1 - t, C - 4 - s0)) = v;
             }
         }
