@@ -16,7 +16,11 @@ written (224 B each in bf16) plus the two fp32 gates; a bidirectional call also
 writes o_rev; the forward scan reads and writes the 112x112 fp32 state of each
 head once.
 `cpu_baseline` times the fp64 CPU oracle on the host cores over the same
-workload (the oracle is a test reference, not a tuned CPU implementation).
+workload (the oracle is a test reference, not a tuned CPU implementation), and
+once more on one core.
+`measured_peaks` states what this machine reaches with plain kernels of our own
+(a 1 GiB device copy, a dense bf16 MFMA loop) beside the vendor peaks the
+fractions are quoted against.
 """
 from __future__ import annotations
 
@@ -71,15 +75,60 @@ def load_traffic():
 def cpu_baseline(d, threads):
     import oracle
     oracle.build(force=False)
-    reps, t0 = 0, time.perf_counter()
-    while reps < 500 and (reps < 2 or time.perf_counter() - t0 < 12.0):
-        oracle.forward(d["q"], d["k"], d["v"], d["a"], d["beta"], d["S0"], threads=threads)
-        oracle.reverse(d["q"], d["k"], d["v"], d["a"], d["beta"], threads=threads)
-        reps += 1
-    dt = (time.perf_counter() - t0) / reps
+
+    def rate(nthreads, budget_s, max_reps):
+        reps, t0 = 0, time.perf_counter()
+        while reps < max_reps and (reps < 1 or time.perf_counter() - t0 < budget_s):
+            oracle.forward(d["q"], d["k"], d["v"], d["a"], d["beta"], d["S0"], threads=nthreads)
+            oracle.reverse(d["q"], d["k"], d["v"], d["a"], d["beta"], threads=nthreads)
+            reps += 1
+        return reps, (time.perf_counter() - t0) / reps
+
+    reps, dt = rate(threads, 12.0, 500)
+    reps1, dt1 = rate(1, 3.0, 4)
     return {"value": round(T / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"the full workload, {reps} repeats: forward + reverse fp64 scans of B={B} H={H} "
-                      f"d={D} T={T} ({dt:.3f} s per step)"}
+                      f"d={D} T={T} ({dt:.3f} s per step)",
+            "single_core": {"value": round(T / dt1, 1), "cores": 1,
+                            "sample": f"the same step on one thread, {reps1} repeats ({dt1:.3f} s per step)"}}
+
+
+def measured_peaks(torch, dev):
+    """A 1 GiB device-to-device copy (512 MiB read + 512 MiB written, beyond the 256 MB MALL) and a
+    dense bf16 MFMA loop (two wavefronts per SIMD), both hand-written HIP in libgdn_peaks.so."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "gated_deltanet_streaming_amd", "libgdn_peaks.so"))
+    lib.gdn_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]
+    lib.gdn_peak_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double)]
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    half = 512 * 1024 * 1024
+    src = torch.empty(half, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    copy_gbs = {}
+    for form, name in ((0, "grid_stride"), (1, "one_vector_per_thread")):
+        ms = ctypes.c_float()
+        if lib.gdn_peak_copy(src.data_ptr(), dst.data_ptr(), half, 20, form, stream, ctypes.byref(ms)) != 0:
+            raise RuntimeError("copy probe failed")
+        copy_gbs[name] = round(2 * half / (ms.value * 1e-3) / 1e9, 1)
+    best = max(copy_gbs.values())
+    del src, dst
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks = 2 * cus
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    mms, flops = ctypes.c_float(), ctypes.c_double()
+    if lib.gdn_peak_mfma_bf16(blocks, 2000, 10, out.data_ptr(), stream, ctypes.byref(mms), ctypes.byref(flops)) != 0:
+        raise RuntimeError("MFMA probe failed")
+    torch.cuda.synchronize()
+    tflops = flops.value / (mms.value * 1e-3) / 1e12
+    return {"hbm_copy_GBs": best, "hbm_copy_frac_of_vendor": round(best / HBM_PEAK_GBS, 4), "hbm_copy_forms": copy_gbs,
+            "mfma_bf16_TFLOPs": round(tflops, 1), "mfma_bf16_frac_of_vendor": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "compute_units": cus,
+            "how": "copy: 1 GiB moved per launch (read + write), average of 20, the better of two kernel forms; "
+                   "MFMA: 16x16x32 bf16, 8 independent "
+                   "chains per wavefront, 2 wavefronts per SIMD, average of 10 launches"}
 
 
 def main():
@@ -91,6 +140,7 @@ def main():
                     help="bidir: one gdn_chunk_bidir call per step; separate: forward then reverse calls")
     ap.add_argument("--sets", type=int, default=6, help="rotating input/output buffer sets (1 = warm)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the copy / MFMA peak probes")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 256 MiB device copy (reference for counter scaling)")
     args = ap.parse_args()
@@ -243,6 +293,8 @@ def main():
             "target_tokens_per_s": 108e6,
         },
     }
+    if not args.no_peaks:
+        out["measured_peaks"] = measured_peaks(torch, dev)
     if not args.no_cpu:
         # the host share of one GPU: OMP_NUM_THREADS when set (16 on the GPU machines), else the affinity mask
         threads = min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS", "0")) or 1 << 30)

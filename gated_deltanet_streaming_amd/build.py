@@ -1,4 +1,6 @@
-"""Build the gfx950 library ``libgdn_stream.so`` in-tree with hipcc."""
+"""Build the gfx950 libraries in-tree with hipcc: ``libgdn_stream.so`` (the GDN path and its
+C ABI) and ``libgdn_peaks.so`` (copy and MFMA probes that measure the machine's peaks for the
+roofline; measurement support, not part of the path)."""
 from __future__ import annotations
 
 import os
@@ -10,6 +12,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgdn_stream.so")
 SOURCES = [os.path.join(CSRC, "gdn_kernels.hip"), os.path.join(CSRC, "gdn_api.cpp")]
+PEAKS_LIB = os.path.join(PKG, "libgdn_peaks.so")
+PEAKS_SOURCES = [os.path.join(CSRC, "gdn_peaks.hip")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
@@ -22,20 +26,26 @@ HIPCC_FLAGS = [
 ]
 
 
-def command(out: str = LIB) -> list:
+def command(out: str = LIB, sources=None) -> list:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    return [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", out, *SOURCES]
+    return [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", out, *(sources or SOURCES)]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    res = subprocess.run(command(tmp), capture_output=True, text=True)
+def _build_one(lib: str, sources, verbose: bool) -> str:
+    tmp = lib + ".tmp"
+    res = subprocess.run(command(tmp, sources), capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
     if verbose:
         print(res.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Builds both libraries; returns the path of the GDN library."""
+    _build_one(PEAKS_LIB, PEAKS_SOURCES, verbose)
+    return _build_one(LIB, SOURCES, verbose)
 
 
 if __name__ == "__main__":

@@ -78,3 +78,21 @@ def test_null_arguments_are_rejected(lib):
     assert lib.gdn_state_get(None, None, None) == binding.GDN_E_INVAL
     assert lib.gdn_state_set(None, None, None) == binding.GDN_E_INVAL
     assert lib.gdn_stream_destroy(None) == binding.GDN_OK
+
+
+def test_peaks_library_exports_its_probes():
+    """The measurement-support library (copy and MFMA probes behind the roofline peaks) is
+    built beside the GDN library and exports exactly its two entry points."""
+    path = os.path.join(os.path.dirname(binding.library_path()), "libgdn_peaks.so")
+    if not os.path.exists(path):
+        pytest.skip("libgdn_peaks.so not built (run __graft_entry__.build())")
+    out = os.popen(f"nm -D --defined-only {path}").read()
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert exported == {"gdn_peak_copy", "gdn_peak_mfma_bf16"}
+    lib = ctypes.CDLL(path)
+    lib.gdn_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]
+    ms = ctypes.c_float()
+    # argument checks only (no device work): null buffers and a size that is not a multiple of 16
+    assert lib.gdn_peak_copy(None, None, 1024, 1, 0, None, ctypes.byref(ms)) == -1
+    assert lib.gdn_peak_copy(1, 1, 1000, 1, 0, None, ctypes.byref(ms)) == -1
