@@ -365,10 +365,18 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
     constexpr int NKT = BK::NFULL + (BK::HALF ? 1 : 0);
     typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-    // K and Q rows (bf16, D per row, token order); row t holds its 16-byte chunk c at position
-    // c ^ ((t >> 3) & 1), so that 16 rows read at one column are free of bank conflicts.  The Q
-    // rows are dead after the Gram products; T^T of both directions then takes their storage.
-    auto kq = [](int t, int d) { return t * D + (((d >> 3) ^ ((t >> 3) & 1)) << 3) + (d & 7); };
+    // K and Q rows (bf16, D per row, token order).  Row t holds its 16-byte chunk c at position
+    // c ^ sw(t, c): the chunks of the 32-wide k-steps are permuted within their group of four by
+    // (t >> 2) & 3, the two chunks of a trailing 16-wide step swap for rows with bit 3 set.  With
+    // this layout the MFMA operand reads (16 consecutive rows at one column, 16- and 8-byte) are
+    // free of LDS bank conflicts on gfx950 (measured; a swap by bit 3 alone leaves the 16-byte
+    // reads two-way conflicted).  The Q rows are dead after the Gram products; T^T of both
+    // directions then takes their storage.
+    constexpr int CHF = 4 * (ND / 2);   // chunks of the 32-wide k-steps
+    auto kq = [](int t, int d) {
+        const int c = d >> 3, sw = c < CHF ? ((t >> 2) & 3) : ((t >> 3) & 1);
+        return t * D + ((c ^ sw) << 3) + (d & 7);
+    };
     constexpr int Q_BYTES = C * D * 2, T2_BYTES = 2 * US::HALVES * 2;
     constexpr int QT_BYTES = Q_BYTES > T2_BYTES ? Q_BYTES : T2_BYTES;
     __shared__ __align__(16) bf16 Ks[C * D];
@@ -510,12 +518,12 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
     auto q_needed = [&](int mt, int nt) { return (mt >= nt && active(0)) || (mt <= nt && active(1)); };
     f16x4 qa[TPQ];
     // operands of one Gram tile: A = rows arow of `arows`, B = K rows brow; chunk 4 ks + g of a
-    // row sits at (4 ks + g) ^ x = 4 ks + (g ^ x) with x = (row >> 3) & 1
+    // row sits at 4 ks + (g ^ ((row >> 2) & 3))
     auto gram = [&](int arow, int brow, const bf16* arows, const bf16* brows) {
         bf16x8 aop[ND / 2 > 0 ? ND / 2 : 1], bop[ND / 2 > 0 ? ND / 2 : 1];
         bf16x4 aoh, boh;
-        const bf16* ap = arows + arow * D + ((g ^ ((arow >> 3) & 1)) << 3);
-        const bf16* bpp = brows + brow * D + ((g ^ ((brow >> 3) & 1)) << 3);
+        const bf16* ap = arows + arow * D + ((g ^ ((arow >> 2) & 3)) << 3);
+        const bf16* bpp = brows + brow * D + ((g ^ ((brow >> 2) & 3)) << 3);
 #pragma unroll
         for (int ks = 0; ks < ND / 2; ++ks) {
             aop[ks] = ld_bf16x8(ap + 32 * ks);
@@ -815,13 +823,15 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
             const int zj = jj - NEJ, mg = zj % MG, ks = zj / MG;
             // K (fp16) read transposed: lane r of group g supplies processing row t + 4 g + r/4 at
             // state indices dperm(m, 4 (r%4)) .. +3.  Its address is kq(mrow(dir, row), d): the
-            // row part is a lane constant plus a scalar step, and the chunk swizzle bit of the row
-            // ((row >> 3) & 1) depends on the lane only.
+            // row part is a lane constant plus a scalar step (a multiple of 16 rows), so the chunk
+            // permutation of the row ((row >> 2) & 3, and bit 3 for a trailing step) depends on
+            // the lane only.
             const int u = 4 * g + (r >> 2);
             const int xs = dir ? 1 - ((u >> 3) & 1) : ((u >> 3) & 1);
+            const int s4 = dir ? 3 - g : g;   // ((row >> 2) & 3) of token row mrow(dir, 16 k + u)
             const int kl = (dir ? C - 1 - u : u) * D;
             const int rstep = dir ? -D : D;
-            const int cb = 8 * ((r & 3) ^ xs), cbs = 8 * (((r & 3) >> 1) ^ xs) + 4 * (r & 1);
+            const int cb = 8 * ((r & 3) ^ s4), cbs = 8 * (((r & 3) >> 1) ^ xs) + 4 * (r & 1);
             auto kaddr = [&](int trow, int m) {
                 const int col = (m < (ND & ~1)) ? 32 * (m >> 1) + 4 * (m & 1) + cb : 16 * m + cbs;
                 return Ks + kl + trow * rstep + col;
