@@ -281,6 +281,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// A 16-byte store through the global address space.  A store through a generic pointer is
+// a flat store, which also counts against the LDS wait counter: every later wait for an LDS
+// read would then wait for the store to reach memory as well.
+__device__ __forceinline__ void gstore16(void* p, uint4 v) {
+    *(__attribute__((address_space(1))) u32x4*)p = __builtin_bit_cast(u32x4, v);
+}
+
 // LDS-only barrier: orders LDS traffic between the wavefronts of a workgroup
 // without waiting for global loads that are still in flight.
 __device__ __forceinline__ void lds_barrier() {
@@ -373,6 +380,8 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
     // reads two-way conflicted).  The Q rows are dead after the Gram products; T^T of both
     // directions then takes their storage.
     constexpr int CHF = 4 * (ND / 2);   // chunks of the 32-wide k-steps
+    auto kq_full = [](int t, int d) { return t * D + (((d >> 3) ^ ((t >> 2) & 3)) << 3) + (d & 7); };   // d < 8 CHF
+    auto kq_tail = [](int t, int d) { return t * D + (((d >> 3) ^ ((t >> 3) & 1)) << 3) + (d & 7); };   // d >= 8 CHF
     auto kq = [](int t, int d) {
         const int c = d >> 3, sw = c < CHF ? ((t >> 2) & 3) : ((t >> 3) & 1);
         return t * D + ((c ^ sw) << 3) + (d & 7);
@@ -530,8 +539,8 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
             bop[ks] = ld_bf16x8(bpp + 32 * ks);
         }
         if constexpr (ND % 2) {
-            aoh = ld_bf16x4(arows + kq(arow, 32 * (ND / 2) + 4 * g));
-            boh = ld_bf16x4(brows + kq(brow, 32 * (ND / 2) + 4 * g));
+            aoh = ld_bf16x4(arows + kq_tail(arow, 32 * (ND / 2) + 4 * g));
+            boh = ld_bf16x4(brows + kq_tail(brow, 32 * (ND / 2) + 4 * g));
         }
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -617,12 +626,12 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
             const int rr = 16 * mt + r;
             uint4 v;
             if (ks < NKF) {
-                v = *reinterpret_cast<const uint4*>(rows + kq(rr, 32 * ks + 8 * g));
+                v = *reinterpret_cast<const uint4*>(rows + kq_full(rr, 32 * ks + 8 * g));
             } else {
-                const uint2 hv = *reinterpret_cast<const uint2*>(rows + kq(rr, 16 * (ND - 1) + 4 * g));
+                const uint2 hv = *reinterpret_cast<const uint2*>(rows + kq_tail(rr, 16 * (ND - 1) + 4 * g));
                 v = uint4{hv.x, hv.y, 0u, 0u};
             }
-            reinterpret_cast<uint4*>(fragb[kind] + (mt * NKD + ks) * 1024)[lane] = v;
+            gstore16(fragb[kind] + (mt * NKD + ks) * 1024 + 16 * lane, v);
         }
     }
     lds_barrier();
@@ -774,8 +783,8 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
         const int jj = q < nz ? NEJ + (q >> dsh) : NEJ - 1 - ((q - nz) >> dsh);
         const f16* T16 = reinterpret_cast<const f16*>(QT) + dir * US::HALVES;
         const f16* Am = LA + dir * LB::HALVES;
-        uint4* Efr = reinterpret_cast<uint4*>(item_of(dir));    // BK::TOTAL blocks
-        uint4* Zfr = Efr + BK::TOTAL * 64;                      // ND x NKT blocks
+        // the item: BK::TOTAL E blocks, then ND x NKT Z blocks (1 KB each)
+        char* const itm = item_of(dir);
         if (jj < NEJ) {
             // E^T = T^T A^T, tile (ut, tt) = sum_s T^T[u][s] A[t][s] over s in [16 ut, 16 tt + 16);
             // the output tiles (2ks, mt) and (2ks + 1, mt) form the O-product A fragment (mt, ks).
@@ -812,7 +821,7 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
                 fr[e] = (f16)et[0][e];
                 fr[4 + e] = (f16)et[1][e];
             }
-            Efr[blk * 64 + lane] = __builtin_bit_cast(uint4, fr);
+            gstore16(itm + blk * 1024 + 16 * lane, __builtin_bit_cast(uint4, fr));
         } else {
             // Z = diag(beta) T^T diag(w) K on fp16 MFMA, w = e^{g_C-g}/|k|: A operand T[s][t] w_s
             // (row t, k = s in slots 16 (i/4) + 4 g + i%4 of each 32-wide step), B operand the fp16 K
@@ -887,7 +896,7 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
                 if (m < ND) {
                     const f32x4 z0 = acc[0][mi] * bt4[0], z1 = acc[1][mi] * bt4[1];
                     const f16x8 fr = {(f16)z0[0], (f16)z0[1], (f16)z0[2], (f16)z0[3], (f16)z1[0], (f16)z1[1], (f16)z1[2], (f16)z1[3]};
-                    Zfr[(m * NKT + ks) * 64 + lane] = __builtin_bit_cast(uint4, fr);
+                    gstore16(itm + (BK::TOTAL + m * NKT + ks) * 1024 + 16 * lane, __builtin_bit_cast(uint4, fr));
                 }
             }
         }

@@ -119,6 +119,20 @@ def test_fp32_io_chunked(C):
     assert_close("state", S, Sf)
 
 
+@pytest.mark.parametrize("C", [16, 32, 64])
+def test_repeated_bidir_calls_are_bitwise_identical(C):
+    """Fresh handles (fresh workspace memory) and the same inputs give the same bits every time:
+    the kernels read nothing they have not written and reduce in a fixed order."""
+    d = gdn_inputs.batch(63, 2, 700, 3, 112, io="f32", with_state=True)
+    first = _run_pair(d, 112, 700, C=C, io="f32", bidir=True)
+    for x in first:
+        assert torch.isfinite(x).all()
+    for _ in range(5):
+        again = _run_pair(d, 112, 700, C=C, io="f32", bidir=True)
+        for x, y in zip(first, again):
+            assert torch.equal(x, y)
+
+
 def test_bidir_equals_separate_calls_bitwise():
     d = gdn_inputs.batch(61, 2, 300, 4, 112, with_state=True)
     a = _run_pair(d, 112, 300)
