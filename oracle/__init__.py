@@ -50,6 +50,11 @@ def _bind(path):
                                     ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double,
                                     dp, dp, ctypes.c_int, i64]
     lib.gdn_oracle_scan.restype = ctypes.c_int
+    lib.gdn_oracle_backward.argtypes = [i64, i64, i64, i64, i64,
+                                        dp, dp, dp, dp, dp, dp, dp, dp,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+                                        dp, dp, dp, dp, dp, dp, ctypes.c_int]
+    lib.gdn_oracle_backward.restype = ctypes.c_int
     return lib
 
 
@@ -120,3 +125,35 @@ def forward(q, k, v, a, beta, S0=None, **kw):
 def reverse(q, k, v, a, beta, **kw):
     """Intra-chunk backward scan: starts from a zero state at the chunk end."""
     return scan(q, k, v, a, beta, None, reverse=True, **kw)
+
+
+def backward(q, k, v, a, beta, dO, S0=None, dS_final=None, *, reverse=False, l2norm=True,
+             eps=DEFAULT_EPS, scale=1.0, threads=None, lib=None):
+    """Gradients of ``scan`` (reverse-mode through the per-token rule, fp64).
+
+    dO: gradient of the loss with respect to o [B, T, H, Dv]; dS_final: with respect to the
+    final state [B, H, Dv, Dk] (None = zero).  Returns a dict with dq, dk [B, T, H, Dk],
+    dv [B, T, H, Dv], da, dbeta [B, T, H] and dS0 [B, H, Dv, Dk].  Training over streaming
+    chunks (the Chinese summary, "Method steps") needs this pass; the pages print no
+    formula for it, so it is the derivative of the recurrence itself.
+    """
+    q, k, v, a, beta, dO = (_f64(x) for x in (q, k, v, a, beta, dO))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    assert k.shape == (B, T, H, Dk) and v.shape == (B, T, H, Dv) and dO.shape == (B, T, H, Dv)
+    assert a.shape == (B, T, H) and beta.shape == (B, T, H)
+    S0 = None if S0 is None else _f64(S0)
+    dS_final = None if dS_final is None else _f64(dS_final)
+    for x in (S0, dS_final):
+        if x is not None:
+            assert x.shape == (B, H, Dv, Dk)
+    out = {"dq": np.zeros((B, T, H, Dk)), "dk": np.zeros((B, T, H, Dk)), "dv": np.zeros((B, T, H, Dv)),
+           "da": np.zeros((B, T, H)), "dbeta": np.zeros((B, T, H)), "dS0": np.zeros((B, H, Dv, Dk))}
+    rc = _load(lib).gdn_oracle_backward(B, T, H, Dk, Dv, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta),
+                                     _ptr(S0), _ptr(dO), _ptr(dS_final), int(bool(reverse)),
+                                     int(bool(l2norm)), float(eps), float(scale),
+                                     _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["da"]),
+                                     _ptr(out["dbeta"]), _ptr(out["dS0"]), int(threads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"gdn_oracle_backward failed with code {rc}")
+    return out
