@@ -228,8 +228,9 @@ static int run_bitem(const bjob_t* J, int64_t b, int64_t h) {
         const int64_t tok = (b * T + t) * H + h;
         const double at = J->a[tok], bt = J->beta[tok];
         const double* vt = J->v + tok * Dv;
-        normalise(J->k + tok * Dk, Dk, J->l2norm, J->eps, kh + p * Dk);
-        normalise(J->q + tok * Dk, Dk, J->l2norm, J->eps, qh + p * Dk);
+        const double *kt = J->k + tok * Dk, *qt = J->q + tok * Dk;
+        normalise(kt, Dk, J->l2norm, J->eps, kh + p * Dk);
+        normalise(qt, Dk, J->l2norm, J->eps, qh + p * Dk);
         const double* Sp = S + p * DD;
         double* Sn = S + (p + 1) * DD;
         const double* kp = kh + p * Dk;
@@ -256,7 +257,7 @@ static int run_bitem(const bjob_t* J, int64_t b, int64_t h) {
         for (int64_t c = 0; c < Dk; ++c) {
             double s = 0.0;
             for (int64_t r = 0; r < Dv; ++r) s += Sc[r * Dk + c] * dot[r];
-            gq[c] = J->scale * s;
+            gq[c] = s * J->scale;
         }
         for (int64_t r = 0; r < Dv; ++r)
             for (int64_t c = 0; c < Dk; ++c) G[r * Dk + c] += J->scale * dot[r] * qp[c];
