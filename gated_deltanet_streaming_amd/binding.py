@@ -19,8 +19,8 @@ GDN_BF16, GDN_F32 = 0, 1
 GDN_L2NORM_QK = 1 << 0
 GDN_NO_COMMIT = 1 << 0
 GDN_SEQUENTIAL = 1 << 1
-GDN_KERNEL_PREP, GDN_KERNEL_SCAN, GDN_KERNEL_SEQ, GDN_KERNEL_COUNT = 0, 1, 2, 3
-KERNEL_NAMES = ("prep", "scan", "sequential")
+GDN_KERNEL_PREP, GDN_KERNEL_SCAN, GDN_KERNEL_SEQ, GDN_KERNEL_BWD, GDN_KERNEL_COUNT = 0, 1, 2, 3, 4
+KERNEL_NAMES = ("prep", "scan", "sequential", "backward")
 
 
 class GdnConfig(ctypes.Structure):
@@ -38,6 +38,12 @@ class GdnIo(ctypes.Structure):
                 ("o", ctypes.c_void_p), ("a", ctypes.c_void_p), ("beta", ctypes.c_void_p),
                 ("q_strides", _Strides), ("k_strides", _Strides), ("v_strides", _Strides),
                 ("o_strides", _Strides), ("g_strides", _Strides)]
+
+
+class GdnGrad(ctypes.Structure):
+    _fields_ = [("d_o", ctypes.c_void_p), ("d_state", ctypes.c_void_p), ("state0", ctypes.c_void_p),
+                ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+                ("da", ctypes.c_void_p), ("dbeta", ctypes.c_void_p), ("d_state0", ctypes.c_void_p)]
 
 
 class GdnError(RuntimeError):
@@ -68,6 +74,7 @@ def load_library():
         "gdn_chunk_forward": ([vp, ctypes.POINTER(GdnIo), i64, u32, vp, vp], i32),
         "gdn_chunk_reverse": ([vp, ctypes.POINTER(GdnIo), i64, u32, vp, vp], i32),
         "gdn_chunk_bidir": ([vp, ctypes.POINTER(GdnIo), vp, i64, u32, vp, vp], i32),
+        "gdn_chunk_backward": ([vp, ctypes.POINTER(GdnIo), ctypes.POINTER(GdnGrad), i64, i32, vp], i32),
         "gdn_state_get": ([vp, vp, vp], i32),
         "gdn_state_set": ([vp, vp, vp], i32),
         "gdn_profile": ([vp, i32], i32),
@@ -180,6 +187,27 @@ def gdn_profile_read(handle, reset=True):
     return {KERNEL_NAMES[i]: (ms[i], n[i]) for i in range(GDN_KERNEL_COUNT)}
 
 
+def gdn_chunk_backward(handle, q, k, v, a, beta, d_o, grads, *, reverse=False, d_state=None, state0=None,
+                       stream=None):
+    """Gradients of one scan.  ``grads`` maps dq, dk, dv (fp32 [B, T, H, D], contiguous), da,
+    dbeta (fp32 [B, T, H], contiguous) and optionally d_state0 (fp32 [B, H, d_v, d_k]) to
+    the tensors to write."""
+    io = _make_io(q, k, v, d_o, a, beta)
+    for name in ("dq", "dk", "dv", "da", "dbeta"):
+        t = grads[name]
+        if not t.is_contiguous() or t.dtype.itemsize != 4:
+            raise ValueError(f"{name} must be a contiguous fp32 tensor")
+    g = GdnGrad()
+    g.d_o = d_o.data_ptr()
+    g.d_state = None if d_state is None else d_state.data_ptr()
+    g.state0 = None if state0 is None else state0.data_ptr()
+    g.dq, g.dk, g.dv = grads["dq"].data_ptr(), grads["dk"].data_ptr(), grads["dv"].data_ptr()
+    g.da, g.dbeta = grads["da"].data_ptr(), grads["dbeta"].data_ptr()
+    g.d_state0 = None if grads.get("d_state0") is None else grads["d_state0"].data_ptr()
+    _check(load_library().gdn_chunk_backward(ctypes.c_void_p(handle), ctypes.byref(io), ctypes.byref(g), q.shape[1],
+                                             int(bool(reverse)), _stream_ptr(stream, q.device)))
+
+
 class Stream:
     """One handle: B streams x H heads of carried state on one device."""
 
@@ -199,6 +227,21 @@ class Stream:
 
     def bidir(self, q, k, v, a, beta, o, o_rev, **kw):
         gdn_chunk_bidir(self.handle, q, k, v, a, beta, o, o_rev, **kw)
+
+    def backward(self, q, k, v, a, beta, d_o, *, reverse=False, d_state=None, state0=None, **kw):
+        """Gradients of one scan; returns a dict of fp32 tensors dq, dk, dv, da, dbeta, d_state0."""
+        import torch
+        B, T, H, Dk = q.shape
+        Dv = v.shape[-1]
+        dev = q.device
+        g = {"dq": torch.empty((B, T, H, Dk), dtype=torch.float32, device=dev),
+             "dk": torch.empty((B, T, H, Dk), dtype=torch.float32, device=dev),
+             "dv": torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev),
+             "da": torch.empty((B, T, H), dtype=torch.float32, device=dev),
+             "dbeta": torch.empty((B, T, H), dtype=torch.float32, device=dev),
+             "d_state0": torch.empty(self.shape, dtype=torch.float32, device=dev)}
+        gdn_chunk_backward(self.handle, q, k, v, a, beta, d_o, g, reverse=reverse, d_state=d_state, state0=state0, **kw)
+        return g
 
     def state_get(self, dst=None, **kw):
         import torch

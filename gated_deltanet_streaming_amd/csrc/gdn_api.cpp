@@ -34,6 +34,7 @@ struct gdn_stream {
     int nsub_max;
     int64_t items_total;  // bytes of the items (the fragment area follows)
     int ntile_max;
+    float* bwd_ws;        // backward workspace (states, partial sums), allocated on first use
     // optional per-kernel timing
     bool profile;
     std::vector<std::pair<hipEvent_t, hipEvent_t>> pend;
@@ -267,6 +268,7 @@ GDN_API int gdn_stream_init(const gdn_config* cfg, int device, gdn_stream** out)
     e = hipMemset(s->state, 0, s->state_elems * sizeof(float));
     s->ws = nullptr;
     s->conv = nullptr;
+    s->bwd_ws = nullptr;
     s->item_bytes = 0;
     s->nsub_max = 0;
     s->items_total = 0;
@@ -322,6 +324,7 @@ GDN_API int gdn_stream_destroy(gdn_stream* s) {
     (void)hipFree(s->state);
     if (s->ws) (void)hipFree(s->ws);
     if (s->conv) (void)hipFree(s->conv);
+    if (s->bwd_ws) (void)hipFree(s->bwd_ws);
     delete s;
     if (e != hipSuccess) return fail(GDN_E_HIP, "destroy: %s", hipGetErrorString(e));
     return ok();
@@ -433,6 +436,95 @@ GDN_API int gdn_profile_read(gdn_stream* s, double* ms, int64_t* launches, int r
             s->acc_n[i] = 0;
         }
     }
+    return ok();
+}
+
+GDN_API int gdn_chunk_backward(gdn_stream* s, const gdn_io* io, const gdn_grad* g, int64_t T, int reverse,
+                               void* hip_stream) {
+    if (!s) return fail(GDN_E_INVAL, "handle is NULL");
+    if (!io) return fail(GDN_E_INVAL, "io is NULL");
+    if (!g) return fail(GDN_E_INVAL, "grad is NULL");
+    if (reverse != 0 && reverse != 1) return fail(GDN_E_INVAL, "reverse must be 0 or 1");
+    if (reverse && g->state0) return fail(GDN_E_INVAL, "the reverse scan starts from zero: state0 must be NULL");
+    if (T < 0 || T > s->cfg.max_tokens)
+        return fail(GDN_E_SHAPE, "T = %lld outside [0, max_tokens = %lld]", (long long)T, (long long)s->cfg.max_tokens);
+    const int64_t sbytes = s->state_elems * (int64_t)sizeof(float);
+    DeviceGuard dg(s->device);
+    if (dg.err != hipSuccess) return fail(GDN_E_HIP, "hipSetDevice(%d): %s", s->device, hipGetErrorString(dg.err));
+    const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    if (T == 0) {
+        if (!g->d_state0) return ok();
+        hipError_t e = g->d_state ? hipMemcpyAsync(g->d_state0, g->d_state, sbytes, hipMemcpyDeviceToDevice, st)
+                                  : gdn::launch_zero(g->d_state0, s->state_elems, st);
+        return e == hipSuccess ? ok() : fail(GDN_E_HIP, "d_state0: %s", hipGetErrorString(e));
+    }
+    const int esz = elem_size(s->cfg);
+    const int dk = s->cfg.d_k, dv = s->cfg.d_v;
+    int rc;
+    if ((rc = check_tensor("q", io->q, io->q_strides, esz, dk, T)) != GDN_OK) return rc;
+    if ((rc = check_tensor("k", io->k, io->k_strides, esz, dk, T)) != GDN_OK) return rc;
+    if ((rc = check_tensor("v", io->v, io->v_strides, esz, dv, T)) != GDN_OK) return rc;
+    if ((rc = check_tensor("d_o", g->d_o, io->o_strides, esz, dv, T)) != GDN_OK) return rc;
+    if (!io->a) return fail(GDN_E_INVAL, "a is NULL");
+    if (!io->beta) return fail(GDN_E_INVAL, "beta is NULL");
+    for (int i = 0; i < 3; ++i)
+        if (io->g_strides[i] < 0) return fail(GDN_E_INVAL, "gate stride %d is negative", i);
+    if (!g->dq || !g->dk || !g->dv || !g->da || !g->dbeta) return fail(GDN_E_INVAL, "a gradient output is NULL");
+    if (!s->bwd_ws) {
+        const int64_t bytes = gdn::backward_ws_bytes(s->cfg.batch, s->cfg.heads, dk, dv, s->cfg.max_tokens);
+        hipError_t e = hipMalloc(&s->bwd_ws, bytes);
+        if (e != hipSuccess) {
+            s->bwd_ws = nullptr;
+            (void)hipGetLastError();
+            return fail(GDN_E_NOMEM, "backward workspace (%lld bytes): %s", (long long)bytes, hipGetErrorString(e));
+        }
+    }
+    gdn::Params p = base_params(s, io, T);
+    p.dir0 = reverse;
+    p.ndirs = 1;
+    gdn::BwdParams b;
+    b.d_o = g->d_o;
+    b.d_state = g->d_state;
+    b.state0 = g->state0;
+    b.dq = g->dq;
+    b.dk = g->dk;
+    b.dv = g->dv;
+    b.da = g->da;
+    b.dbeta = g->dbeta;
+    b.d_state0 = g->d_state0;
+    b.states = s->bwd_ws;
+    b.partials = s->bwd_ws + (int64_t)s->cfg.batch * s->cfg.heads * (dv / 16) * (s->cfg.max_tokens + 1) * 16 * dk;
+    b.reverse = reverse;
+    hipError_t prior = hipPeekAtLastError();
+    if (prior != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(GDN_E_HIP, "earlier HIP error: %s", hipGetErrorString(prior));
+    }
+    hipEvent_t evs[2];
+    int kinds[1];
+    gdn::Timing tm{nullptr, kinds, 1, 0};
+    std::pair<hipEvent_t, hipEvent_t> pr;
+    if (s->profile) {
+        if (!s->spare.empty()) {
+            pr = s->spare.back();
+            s->spare.pop_back();
+        } else if (hipEventCreate(&pr.first) != hipSuccess || hipEventCreate(&pr.second) != hipSuccess) {
+            return fail(GDN_E_HIP, "hipEventCreate failed");
+        }
+        evs[0] = pr.first;
+        evs[1] = pr.second;
+        tm.ev = evs;
+    }
+    hipError_t e = gdn::launch_backward(p, b, st, &tm);
+    if (s->profile) {
+        if (tm.n > 0) {
+            s->pend.push_back(pr);
+            s->pend_kind.push_back(kinds[0]);
+        } else {
+            s->spare.push_back(pr);
+        }
+    }
+    if (e != hipSuccess) return fail(GDN_E_HIP, "kernel launch: %s", hipGetErrorString(e));
     return ok();
 }
 

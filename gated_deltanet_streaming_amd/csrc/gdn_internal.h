@@ -7,7 +7,7 @@
 
 namespace gdn {
 
-enum KernelKind { KPREP = 0, KSCAN = 1, KSEQ = 2, KCOUNT = 3 };
+enum KernelKind { KPREP = 0, KSCAN = 1, KSEQ = 2, KBWD = 3, KCOUNT = 4 };
 
 // Everything one launch needs.  Directions: 0 = forward (t ascending, starts
 // from S_in), 1 = reverse (t descending, starts from zero).
@@ -44,6 +44,25 @@ int64_t chunk_item_bytes(int C, int D);
 // Bytes of the fragment area for B streams, H heads and up to max_tokens tokens.
 int64_t chunk_frag_bytes(int D, int64_t max_tokens, int B, int H);
 
+// Gradient of one token-sequential scan (fp32).  Workspace (owned by the handle):
+// states [B][H][Dv/16][T+1][16][Dk] and partial sums [B][T][H][Dv/16][2 Dk + 2].
+struct BwdParams {
+    const void* d_o;       // dL/do, io dtype, o's strides (Params::os)
+    const float* d_state;  // dL/d(final state) [B, H, Dv, Dk], or null
+    const float* state0;   // start state of the scan [B, H, Dv, Dk], or null (zero)
+    float* dq;             // [B, T, H, Dk]
+    float* dk;             // [B, T, H, Dk]
+    float* dv;             // [B, T, H, Dv]
+    float* da;             // [B, T, H]
+    float* dbeta;          // [B, T, H]
+    float* d_state0;       // [B, H, Dv, Dk], or null
+    float* states;
+    float* partials;
+    int reverse;           // 0: the forward scan (t ascending), 1: the reverse scan
+};
+// Bytes of the backward workspace for max_tokens tokens.
+int64_t backward_ws_bytes(int B, int H, int Dk, int Dv, int64_t max_tokens);
+
 // Which (C, D) pairs the chunked kernels are built for.
 bool chunked_supported(int C, int Dk, int Dv, int io_f32);
 
@@ -59,5 +78,6 @@ struct Timing {
 hipError_t launch_zero(float* x, int64_t n, hipStream_t s);
 hipError_t launch_sequential(const Params& p, hipStream_t s, Timing* tm);
 hipError_t launch_chunked(const Params& p, hipStream_t s, Timing* tm);
+hipError_t launch_backward(const Params& p, const BwdParams& g, hipStream_t s, Timing* tm);
 
 }  // namespace gdn

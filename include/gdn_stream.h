@@ -144,9 +144,41 @@ GDN_API int gdn_state_set(gdn_stream* s, const float* src, void* hip_stream);
 #define GDN_KERNEL_PREP  0   /* chunk preparation (norms, gates, Gram, UT inverse) */
 #define GDN_KERNEL_SCAN  1   /* chunk scan (state recurrence and outputs)          */
 #define GDN_KERNEL_SEQ   2   /* token-sequential kernel                            */
-#define GDN_KERNEL_COUNT 3
+#define GDN_KERNEL_BWD   3   /* gradient of one scan (both of its kernels)         */
+#define GDN_KERNEL_COUNT 4
 GDN_API int gdn_profile(gdn_stream* s, int enable);
 GDN_API int gdn_profile_read(gdn_stream* s, double* ms, int64_t* launches, int reset);
+
+/* Gradients of one scan, for training over streaming chunks (the Chinese summary,
+ * "Method steps": bidirectional training on short clips and streaming training on
+ * long ones).  The pages print no formula for this pass; it is the reverse-mode
+ * derivative of the per-token rule, computed by a token-sequential fp32 path.
+ * All pointers are device memory on the handle's device; gradients are written
+ * in fp32, contiguous. */
+typedef struct gdn_grad {
+    const void* d_o;        /* [B, T, H, d_v] io_dtype, io->o_strides: dL/do of the scan   */
+    const float* d_state;   /* [B, H, d_v, d_k] fp32: dL/d(final state), or NULL (zero)     */
+    const float* state0;    /* [B, H, d_v, d_k] fp32: start state of a forward scan, or NULL
+                               (zero); must be NULL for the reverse scan (it starts at zero) */
+    float* dq;              /* [B, T, H, d_k] written                                       */
+    float* dk;              /* [B, T, H, d_k] written                                       */
+    float* dv;              /* [B, T, H, d_v] written                                       */
+    float* da;              /* [B, T, H] written (gradient with respect to a_t)             */
+    float* dbeta;           /* [B, T, H] written                                            */
+    float* d_state0;        /* [B, H, d_v, d_k] written when non-NULL                       */
+} gdn_grad;
+
+/* Gradient of the forward scan (reverse = 0: t ascending from g->state0) or of the
+ * reverse scan (reverse = 1: t descending from zero) over T tokens of io->q, k, v,
+ * a, beta (io->o is not used; its strides give d_o's layout).  Never reads or
+ * writes the cache.  Asynchronous on hip_stream.  The first call on a handle
+ * allocates a backward workspace of 4 (B H (d_v/16)(max_tokens+1) 16 d_k +
+ * B max_tokens H (d_v/16)(2 d_k + 2)) bytes, kept until gdn_stream_destroy
+ * (GDN_E_NOMEM if that fails).  Errors: GDN_E_INVAL (NULL handle/io/g/output,
+ * bad strides, state0 given with reverse), GDN_E_SHAPE (T outside [0, max_tokens]),
+ * GDN_E_HIP; on error nothing is enqueued.  T = 0 writes d_state0 = d_state. */
+GDN_API int gdn_chunk_backward(gdn_stream* s, const gdn_io* io, const gdn_grad* g, int64_t T, int reverse,
+                               void* hip_stream);
 
 /* Message for the last failing call on this thread ("" when none). */
 GDN_API const char* gdn_last_error(void);
