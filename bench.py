@@ -136,8 +136,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--mode", choices=["bidir", "separate"], default="bidir",
-                    help="bidir: one gdn_chunk_bidir call per step; separate: forward then reverse calls")
+    ap.add_argument("--mode", choices=["bidir", "separate", "backward"], default="bidir",
+                    help="bidir: one gdn_chunk_bidir call per step; separate: forward then reverse calls; "
+                         "backward: the gradients of both scans of the pair (gdn_chunk_backward)")
     ap.add_argument("--sets", type=int, default=6, help="rotating input/output buffer sets (1 = warm)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-peaks", action="store_true", help="skip the copy / MFMA peak probes")
@@ -149,6 +150,9 @@ def main():
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path needs no "
               "multi-GPU exchange; see the sharding notes).", file=sys.stderr)
         sys.exit(2)
+
+    if args.mode == "backward":
+        return main_backward(args)
 
     import numpy as np
     import torch
@@ -299,6 +303,93 @@ def main():
         # the host share of one GPU: OMP_NUM_THREADS when set (16 on the GPU machines), else the affinity mask
         threads = min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS", "0")) or 1 << 30)
         out["cpu_baseline"] = cpu_baseline(d, threads)
+    s.close()
+    print(json.dumps(out), flush=True)
+
+
+def main_backward(args):
+    """Gradients of both scans of the 720p pair (forward from the carried state, reverse from
+    zero) through gdn_chunk_backward: a token-sequential fp32 path, bound by its serial chain
+    of T steps per (head, row block), reported against the HBM roofline of its bytes."""
+    import numpy as np
+    import torch
+
+    import gdn_inputs
+    from gated_deltanet_streaming_amd import binding as gb
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = gdn_inputs.batch(1, B, T, H, D, with_state=True)
+    rng = np.random.default_rng(2)
+    x = {k: torch.from_numpy(d[k]).to(dev, torch.bfloat16) for k in ("q", "k", "v")}
+    a = torch.from_numpy(d["a"]).to(dev)
+    beta = torch.from_numpy(d["beta"]).to(dev)
+    S0 = torch.from_numpy(d["S0"]).to(dev)
+    dO = [torch.from_numpy(rng.standard_normal((B, T, H, D)).astype(np.float32)).to(dev, torch.bfloat16) for _ in range(2)]
+    dSf = torch.from_numpy(rng.standard_normal((B, H, D, D)).astype(np.float32)).to(dev)
+    s = gb.Stream(B, H, D, D, T, device=0)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        s.backward(x["q"], x["k"], x["v"], a, beta, dO[0], d_state=dSf, state0=S0, stream=stream)
+        s.backward(x["q"], x["k"], x["v"], a, beta, dO[1], reverse=True, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - w0) * 1e3 / args.steps
+    gb.gdn_profile(s.handle, True)
+    gb.gdn_profile_read(s.handle, reset=True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    prof = gb.gdn_profile_read(s.handle, reset=True)
+    gb.gdn_profile(s.handle, False)
+    bwd_ms, bwd_n = prof["backward"]
+    launch_ms = bwd_ms / max(bwd_n, 1)
+    # per scan and token-head: q, k, v, d_o read (bf16), a and beta read, dq, dk, dv written (fp32),
+    # da and dbeta written; per scan and head: start state, final-state gradient and start-state
+    # gradient (fp32) for the forward scan, the start-state gradient for the reverse one
+    per_tok = 4 * D * 2 + 2 * 4 + 3 * D * 4 + 2 * 4
+    alg_bytes = 2 * B * T * H * per_tok + 4 * B * H * D * D * 4
+    achieved = alg_bytes / 2 / (launch_ms * 1e-3) / 1e9
+    out = {
+        "metric": "GDN backward (gradients of the forward and reverse scans) tokens/s per layer at 2640-token 720p chunk",
+        "value": round(T / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "720p streaming chunk, one GDN layer: gradients of the forward scan (carried "
+                               "state) and of the intra-chunk reverse scan", "B": B, "H": H, "d_k": D, "d_v": D,
+                   "T": T, "call": "gdn_chunk_backward x 2", "path": "token-sequential fp32"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": None, "kernel": "gdn_bwd_rows_kernel + "
+                     "gdn_bwd_reduce_kernel", "kernel_avg_us": round(launch_ms * 1e3, 1),
+                     "algorithmic_bytes_per_launch": int(alg_bytes / 2),
+                     "note": "latency-bound by the serial chain of T tokens per (head, 16-row block)"},
+    }
+    if not args.no_cpu:
+        import oracle
+        oracle.build(force=False)
+        hs = 2   # bounded sample: 2 of the H heads, the full 2640 tokens, both scans
+        sl = {k: d[k][:, :, :hs] for k in ("q", "k", "v", "a", "beta")}
+        dOs = [t[:, :, :hs].float().cpu().numpy() for t in dO]
+        threads = min(len(os.sched_getaffinity(0)), hs)
+        t0 = time.perf_counter()
+        oracle.backward(sl["q"], sl["k"], sl["v"], sl["a"], sl["beta"], dOs[0], d["S0"][:, :hs],
+                        dSf[:, :hs].cpu().numpy(), threads=threads)
+        oracle.backward(sl["q"], sl["k"], sl["v"], sl["a"], sl["beta"], dOs[1], None, None, reverse=True,
+                        threads=threads)
+        dt = (time.perf_counter() - t0) * H / hs
+        out["cpu_baseline"] = {"value": round(T / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                               "sample": f"{hs} of {H} heads, full {T} tokens, both scans' gradients, scaled "
+                                         f"to {H} heads ({dt:.1f} s per step)"}
     s.close()
     print(json.dumps(out), flush=True)
 
