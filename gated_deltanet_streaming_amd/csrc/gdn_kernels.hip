@@ -965,11 +965,12 @@ struct StepRows {
 };
 
 // Wait until an LDS counter written by another wavefront reaches `target`.
-// Bounded, so a wavefront can never hang here.
+// Bounded, so a wavefront can never hang here.  The poll does not sleep between
+// reads: a hand-off is seen one LDS round trip after it happens (with a 64-cycle
+// sleep per poll the scan measured 0.6 us slower per 720p call).
 __device__ __forceinline__ void wait_counter(int* cnt, int target) {
     for (int it = 0; it < GDN_SPIN_LIMIT; ++it) {
         if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
-        __builtin_amdgcn_s_sleep(1);
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
