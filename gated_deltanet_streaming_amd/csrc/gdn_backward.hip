@@ -20,10 +20,15 @@ __device__ __forceinline__ float ld_elem(const void* base, int64_t idx) {
     else return (float)reinterpret_cast<const bf16*>(base)[idx];
 }
 
-// sum over the 4 lanes of a lane quad (one state row)
+// lane data movement within rows of 16 lanes (DPP; every source lane is valid for these controls)
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+// sum over the 4 lanes of a lane quad (one state row): quad permutations [1,0,3,2] and [2,3,0,1]
 __device__ __forceinline__ float sum4(float x) {
-    x += __shfl_xor(x, 1);
-    x += __shfl_xor(x, 2);
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
     return x;
 }
 
@@ -65,10 +70,11 @@ int64_t backward_ws_bytes(int B, int H, int Dk, int Dv, int64_t max_tokens) {
     return 4 * (states + partials);
 }
 
-// sum over the 16 rows of the workgroup (lane bits 2..5)
+// sum over the 16 rows of the workgroup (lane bits 2..5): within each row of 16 lanes by two
+// rotations (by 4, then by 8: lanes j, j-4, j-8, j-12), then across the four rows
 __device__ __forceinline__ float sum_rows(float x) {
-    x += __shfl_xor(x, 4);
-    x += __shfl_xor(x, 8);
+    x += dpp<0x124>(x);   // row_ror:4
+    x += dpp<0x128>(x);   // row_ror:8
     x += __shfl_xor(x, 16);
     x += __shfl_xor(x, 32);
     return x;
