@@ -1,4 +1,4 @@
-"""ctypes binding of ``libgdn_stream.so`` (C ABI in include/gdn_stream.h).
+"""ctypes binding of ``libgdn_stream.so`` (C ABI in include/gdn_stream.h and include/gdn_attn.h).
 
 Argument marshalling only: torch supplies device memory and the current HIP
 stream; every step of the computation runs in the library's kernels.  The
@@ -46,6 +46,17 @@ class GdnGrad(ctypes.Structure):
                 ("da", ctypes.c_void_p), ("dbeta", ctypes.c_void_p), ("d_state0", ctypes.c_void_p)]
 
 
+class GdnAttnConfig(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("sink_tokens", ctypes.c_int32), ("window_tokens", ctypes.c_int32), ("max_tokens", ctypes.c_int64),
+                ("scale", ctypes.c_float)]
+
+
+class GdnAttnIo(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("o", ctypes.c_void_p),
+                ("q_strides", _Strides), ("k_strides", _Strides), ("v_strides", _Strides), ("o_strides", _Strides)]
+
+
 class GdnError(RuntimeError):
     def __init__(self, code, msg):
         super().__init__(f"gdn error {code}: {msg}")
@@ -80,6 +91,13 @@ def load_library():
         "gdn_profile": ([vp, i32], i32),
         "gdn_profile_read": ([vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), i32], i32),
         "gdn_last_error": ([], ctypes.c_char_p),
+        "gdn_attn_init": ([ctypes.POINTER(GdnAttnConfig), i32, ctypes.POINTER(vp)], i32),
+        "gdn_attn_destroy": ([vp], i32),
+        "gdn_attn_chunk": ([vp, ctypes.POINTER(GdnAttnIo), i64, u32, vp], i32),
+        "gdn_attn_reset": ([vp], i32),
+        "gdn_attn_cache_len": ([vp, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)], i32),
+        "gdn_attn_profile": ([vp, i32], i32),
+        "gdn_attn_profile_read": ([vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), i32], i32),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -256,6 +274,85 @@ class Stream:
     def close(self):
         if self.handle:
             gdn_stream_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ---- softmax-block attention over the sink + window cache ----------------------------------
+
+def gdn_attn_init(batch, heads, head_dim, sink_tokens, window_tokens, max_tokens, *, scale=0.0, device=0):
+    """Create an attention handle (scale 0 selects 1/sqrt(head_dim)); returns the opaque pointer."""
+    cfg = GdnAttnConfig(batch, heads, head_dim, sink_tokens, window_tokens, max_tokens, scale)
+    h = ctypes.c_void_p()
+    _check(load_library().gdn_attn_init(ctypes.byref(cfg), int(device), ctypes.byref(h)))
+    return h.value
+
+
+def gdn_attn_destroy(handle):
+    _check(load_library().gdn_attn_destroy(ctypes.c_void_p(handle)))
+
+
+def gdn_attn_chunk(handle, q, k, v, o, *, flags=0, stream=None):
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        if t.dim() != 4 or t.stride(-1) != 1:
+            raise ValueError(f"{name} must be [B, T, H, D] with a contiguous last dimension")
+    io = GdnAttnIo()
+    io.q, io.k, io.v, io.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()
+    io.q_strides, io.k_strides, io.v_strides, io.o_strides = _strides3(q), _strides3(k), _strides3(v), _strides3(o)
+    _check(load_library().gdn_attn_chunk(ctypes.c_void_p(handle), ctypes.byref(io), q.shape[1], flags,
+                                         _stream_ptr(stream, q.device)))
+
+
+def gdn_attn_reset(handle):
+    _check(load_library().gdn_attn_reset(ctypes.c_void_p(handle)))
+
+
+def gdn_attn_cache_len(handle):
+    s, w = ctypes.c_int64(), ctypes.c_int64()
+    _check(load_library().gdn_attn_cache_len(ctypes.c_void_p(handle), ctypes.byref(s), ctypes.byref(w)))
+    return s.value, w.value
+
+
+def gdn_attn_profile(handle, enable=True):
+    _check(load_library().gdn_attn_profile(ctypes.c_void_p(handle), int(bool(enable))))
+
+
+def gdn_attn_profile_read(handle, reset=True):
+    """(total ms, launches) of the attention kernel since the last reset."""
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    _check(load_library().gdn_attn_profile_read(ctypes.c_void_p(handle), ctypes.byref(ms), ctypes.byref(n),
+                                                int(bool(reset))))
+    return ms.value, n.value
+
+
+class WindowAttention:
+    """One softmax block: B streams x H heads of sink + window cache on one device."""
+
+    def __init__(self, batch, heads, head_dim, sink_tokens, window_tokens, max_tokens, *, scale=0.0, device=0):
+        self.handle = gdn_attn_init(batch, heads, head_dim, sink_tokens, window_tokens, max_tokens, scale=scale,
+                                    device=device)
+
+    def chunk(self, q, k, v, o=None, *, commit=True, stream=None):
+        import torch
+        if o is None:
+            o = torch.empty_like(v)
+        gdn_attn_chunk(self.handle, q, k, v, o, flags=0 if commit else GDN_NO_COMMIT, stream=stream)
+        return o
+
+    def reset(self):
+        gdn_attn_reset(self.handle)
+
+    def cache_len(self):
+        return gdn_attn_cache_len(self.handle)
+
+    def close(self):
+        if self.handle:
+            gdn_attn_destroy(self.handle)
             self.handle = None
 
     def __del__(self):

@@ -11,7 +11,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgdn_stream.so")
-SOURCES = [os.path.join(CSRC, "gdn_kernels.hip"), os.path.join(CSRC, "gdn_backward.hip"), os.path.join(CSRC, "gdn_api.cpp")]
+SOURCES = [os.path.join(CSRC, "gdn_kernels.hip"), os.path.join(CSRC, "gdn_backward.hip"),
+           os.path.join(CSRC, "gdn_attention.hip"), os.path.join(CSRC, "gdn_api.cpp")]
 PEAKS_LIB = os.path.join(PKG, "libgdn_peaks.so")
 PEAKS_SOURCES = [os.path.join(CSRC, "gdn_peaks.hip")]
 

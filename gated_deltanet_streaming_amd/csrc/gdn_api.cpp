@@ -18,6 +18,7 @@
 #include <vector>
 
 #include "gdn_internal.h"
+#include "gdn_attn.h"
 #include "gdn_stream.h"
 
 struct gdn_stream {
@@ -42,6 +43,21 @@ struct gdn_stream {
     std::vector<std::pair<hipEvent_t, hipEvent_t>> spare;
     double acc_ms[gdn::KCOUNT];
     int64_t acc_n[gdn::KCOUNT];
+};
+
+// Softmax-block attention handle: the sink and window cache of every (stream, head), with
+// the fill counters kept on the host (they follow from the sequence of committed calls).
+struct gdn_attn {
+    gdn_attn_config cfg;
+    int device;
+    float scale;
+    __bf16* cache;        // k_sink | v_sink | k_win | v_win, each [B][H][capacity][d]
+    int64_t sink_fill;    // tokens in the sink
+    int64_t win_total;    // tokens ever written to the window (the ring head is win_total mod window)
+    bool profile;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> pend, spare;
+    double acc_ms;
+    int64_t acc_n;
 };
 
 namespace {
@@ -525,6 +541,201 @@ GDN_API int gdn_chunk_backward(gdn_stream* s, const gdn_io* io, const gdn_grad* 
         }
     }
     if (e != hipSuccess) return fail(GDN_E_HIP, "kernel launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+// ---- softmax-block attention over the sink + window cache (gdn_attn.h) ----------------------
+
+GDN_API int gdn_attn_init(const gdn_attn_config* cfg, int device, gdn_attn** out) {
+    if (!cfg || !out) return fail(GDN_E_INVAL, "cfg or out is NULL");
+    *out = nullptr;
+    const gdn_attn_config& c = *cfg;
+    if (c.batch < 1 || c.heads < 1) return fail(GDN_E_SHAPE, "batch and heads must be >= 1");
+    if (!gdn::attn_dim_supported(c.head_dim)) return fail(GDN_E_SHAPE, "head_dim %d: 64, 112 or 128", c.head_dim);
+    if (c.sink_tokens < 0 || c.window_tokens < 0) return fail(GDN_E_SHAPE, "negative cache size");
+    if (c.max_tokens < 1 || c.max_tokens > (1 << 30)) return fail(GDN_E_SHAPE, "max_tokens must be in [1, 2^30]");
+    if (!(c.scale >= 0.f) || !std::isfinite(c.scale)) return fail(GDN_E_INVAL, "scale must be finite and >= 0");
+    const int64_t slots = (int64_t)c.batch * c.heads * ((int64_t)c.sink_tokens + c.window_tokens) * c.head_dim;
+    if ((int64_t)c.sink_tokens + c.window_tokens > (1 << 30)) return fail(GDN_E_SHAPE, "cache too large");
+    DeviceGuard dg(device);
+    if (dg.err != hipSuccess) return fail(GDN_E_HIP, "hipSetDevice(%d): %s", device, hipGetErrorString(dg.err));
+    gdn_attn* a = new (std::nothrow) gdn_attn();
+    if (!a) return fail(GDN_E_NOMEM, "host allocation failed");
+    a->cfg = c;
+    a->device = device;
+    a->scale = c.scale > 0.f ? c.scale : 1.0f / std::sqrt((float)c.head_dim);
+    a->cache = nullptr;
+    if (slots > 0) {
+        hipError_t e = hipMalloc(&a->cache, 2 * slots * sizeof(__bf16));
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            delete a;
+            return fail(GDN_E_NOMEM, "cache (%lld bytes): %s", (long long)(4 * slots), hipGetErrorString(e));
+        }
+    }
+    a->sink_fill = a->win_total = 0;
+    a->profile = false;
+    a->acc_ms = 0.0;
+    a->acc_n = 0;
+    *out = a;
+    return ok();
+}
+
+GDN_API int gdn_attn_destroy(gdn_attn* a) {
+    if (!a) return ok();
+    DeviceGuard dg(a->device);
+    (void)hipDeviceSynchronize();
+    if (a->cache) (void)hipFree(a->cache);
+    for (auto& pr : a->pend) { (void)hipEventDestroy(pr.first); (void)hipEventDestroy(pr.second); }
+    for (auto& pr : a->spare) { (void)hipEventDestroy(pr.first); (void)hipEventDestroy(pr.second); }
+    delete a;
+    return ok();
+}
+
+GDN_API int gdn_attn_chunk(gdn_attn* a, const gdn_attn_io* io, int64_t T, uint32_t flags, void* hip_stream) {
+    if (!a) return fail(GDN_E_INVAL, "handle is NULL");
+    if (!io) return fail(GDN_E_INVAL, "io is NULL");
+    if (flags & ~(uint32_t)GDN_NO_COMMIT) return fail(GDN_E_INVAL, "unknown flag bits 0x%x", flags);
+    if (T < 0 || T > a->cfg.max_tokens)
+        return fail(GDN_E_SHAPE, "T = %lld outside [0, max_tokens = %lld]", (long long)T, (long long)a->cfg.max_tokens);
+    if (T == 0) return ok();
+    const int d = a->cfg.head_dim;
+    int rc;
+    if ((rc = check_tensor("q", io->q, io->q_strides, 2, d, T)) != GDN_OK) return rc;
+    if ((rc = check_tensor("k", io->k, io->k_strides, 2, d, T)) != GDN_OK) return rc;
+    if ((rc = check_tensor("v", io->v, io->v_strides, 2, d, T)) != GDN_OK) return rc;
+    if ((rc = check_tensor("o", io->o, io->o_strides, 2, d, T)) != GDN_OK) return rc;
+    DeviceGuard dg(a->device);
+    if (dg.err != hipSuccess) return fail(GDN_E_HIP, "hipSetDevice(%d): %s", a->device, hipGetErrorString(dg.err));
+    hipError_t prior = hipPeekAtLastError();
+    if (prior != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(GDN_E_HIP, "earlier HIP error: %s", hipGetErrorString(prior));
+    }
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    const gdn_attn_config& c = a->cfg;
+    const int64_t per = (int64_t)c.batch * c.heads * d;
+    __bf16* k_sink = a->cache;
+    __bf16* v_sink = k_sink + per * c.sink_tokens;
+    __bf16* k_win = v_sink + per * c.sink_tokens;
+    __bf16* v_win = k_win + per * c.window_tokens;
+
+    gdn::AttnParams p;
+    std::memset(&p, 0, sizeof p);
+    p.q = io->q;
+    p.k = io->k;
+    p.v = io->v;
+    p.o = io->o;
+    for (int i = 0; i < 3; ++i) {
+        p.qs[i] = io->q_strides[i];
+        p.ks[i] = io->k_strides[i];
+        p.vs[i] = io->v_strides[i];
+        p.os[i] = io->o_strides[i];
+    }
+    p.k_sink = k_sink;
+    p.v_sink = v_sink;
+    p.k_win = k_win;
+    p.v_win = v_win;
+    p.sink_cap = c.sink_tokens;
+    p.win_cap = c.window_tokens;
+    p.n_sink = (int)a->sink_fill;
+    p.n_win = (int)std::min<int64_t>(a->win_total, c.window_tokens);
+    p.T = (int)T;
+    p.B = c.batch;
+    p.H = c.heads;
+    p.D = d;
+    p.scale_log2 = a->scale * 1.4426950408889634f;
+
+    std::pair<hipEvent_t, hipEvent_t> pr;
+    if (a->profile) {
+        if (!a->spare.empty()) {
+            pr = a->spare.back();
+            a->spare.pop_back();
+        } else if (hipEventCreate(&pr.first) != hipSuccess || hipEventCreate(&pr.second) != hipSuccess) {
+            return fail(GDN_E_HIP, "hipEventCreate failed");
+        }
+        (void)hipEventRecord(pr.first, st);
+    }
+    hipError_t e = gdn::launch_attention(p, st);
+    if (a->profile) {
+        (void)hipEventRecord(pr.second, st);
+        a->pend.push_back(pr);
+    }
+    if (e != hipSuccess) return fail(GDN_E_HIP, "attention launch: %s", hipGetErrorString(e));
+
+    if (!(flags & GDN_NO_COMMIT)) {
+        const int64_t taken = std::min<int64_t>(T, c.sink_tokens - a->sink_fill);
+        const int64_t rest = T - taken;
+        const int64_t skip = c.window_tokens > 0 ? std::max<int64_t>(0, rest - c.window_tokens) : rest;
+        if (taken + (rest - skip) > 0) {
+            gdn::AppendParams ap;
+            std::memset(&ap, 0, sizeof ap);
+            ap.k = io->k;
+            ap.v = io->v;
+            for (int i = 0; i < 3; ++i) {
+                ap.ks[i] = io->k_strides[i];
+                ap.vs[i] = io->v_strides[i];
+            }
+            ap.k_sink = k_sink;
+            ap.v_sink = v_sink;
+            ap.k_win = k_win;
+            ap.v_win = v_win;
+            ap.sink_cap = c.sink_tokens;
+            ap.win_cap = c.window_tokens;
+            ap.T = (int)T;
+            ap.B = c.batch;
+            ap.H = c.heads;
+            ap.D = d;
+            ap.sink_fill = (int)a->sink_fill;
+            ap.taken = (int)taken;
+            ap.skip = (int)skip;
+            ap.win_base = c.window_tokens > 0 ? (int)(a->win_total % c.window_tokens) : 0;
+            e = gdn::launch_attn_append(ap, st);
+            if (e != hipSuccess) return fail(GDN_E_HIP, "cache append launch: %s", hipGetErrorString(e));
+        }
+        a->sink_fill += taken;
+        a->win_total += rest;
+    }
+    return ok();
+}
+
+GDN_API int gdn_attn_reset(gdn_attn* a) {
+    if (!a) return fail(GDN_E_INVAL, "handle is NULL");
+    a->sink_fill = a->win_total = 0;
+    return ok();
+}
+
+GDN_API int gdn_attn_cache_len(const gdn_attn* a, int64_t* sink, int64_t* window) {
+    if (!a) return fail(GDN_E_INVAL, "handle is NULL");
+    if (sink) *sink = a->sink_fill;
+    if (window) *window = std::min<int64_t>(a->win_total, a->cfg.window_tokens);
+    return ok();
+}
+
+GDN_API int gdn_attn_profile(gdn_attn* a, int enable) {
+    if (!a) return fail(GDN_E_INVAL, "handle is NULL");
+    a->profile = enable != 0;
+    return ok();
+}
+
+GDN_API int gdn_attn_profile_read(gdn_attn* a, double* ms, int64_t* launches, int reset) {
+    if (!a) return fail(GDN_E_INVAL, "handle is NULL");
+    DeviceGuard dg(a->device);
+    for (auto& pr : a->pend) {
+        float t = 0.f;
+        if (hipEventSynchronize(pr.second) == hipSuccess && hipEventElapsedTime(&t, pr.first, pr.second) == hipSuccess) {
+            a->acc_ms += t;
+            a->acc_n += 1;
+        }
+        a->spare.push_back(pr);
+    }
+    a->pend.clear();
+    if (ms) *ms = a->acc_ms;
+    if (launches) *launches = a->acc_n;
+    if (reset) {
+        a->acc_ms = 0.0;
+        a->acc_n = 0;
+    }
     return ok();
 }
 

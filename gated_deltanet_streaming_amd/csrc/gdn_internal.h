@@ -75,6 +75,31 @@ struct Timing {
     int n;
 };
 
+// Softmax attention of a chunk over the sink + window cache (gdn_attention.hip).  Cache
+// buffers are [B][H][capacity][D] bf16; n_sink / n_win of their slots are valid.
+struct AttnParams {
+    const void *q, *k, *v;
+    void* o;
+    int64_t qs[3], ks[3], vs[3], os[3];
+    const void *k_sink, *v_sink, *k_win, *v_win;
+    int sink_cap, win_cap, n_sink, n_win;
+    int T, B, H, D;
+    float scale_log2;   // logit scale times log2(e)
+};
+// Cache append after a committed call: the first `taken` tokens fill sink slots from
+// sink_fill on, the rest go to the window ring from slot win_base, the first `skip` of them
+// (already older than the window) not at all.
+struct AppendParams {
+    const void *k, *v;
+    int64_t ks[3], vs[3];
+    void *k_sink, *v_sink, *k_win, *v_win;
+    int sink_cap, win_cap, T, B, H, D;
+    int sink_fill, taken, skip, win_base;
+};
+bool attn_dim_supported(int d);
+hipError_t launch_attention(const AttnParams& p, hipStream_t s);
+hipError_t launch_attn_append(const AppendParams& p, hipStream_t s);
+
 hipError_t launch_zero(float* x, int64_t n, hipStream_t s);
 hipError_t launch_sequential(const Params& p, hipStream_t s, Timing* tm);
 hipError_t launch_chunked(const Params& p, hipStream_t s, Timing* tm);

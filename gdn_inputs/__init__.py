@@ -122,3 +122,19 @@ def stream_chunk_torch(cfg: int, chunk: int, B: int, T: int, H: int, D: int, *, 
     if with_state:
         out["S0"] = 0.1 * torch.randn((B, H, D, D), generator=gen, device=device)
     return out
+
+
+ATTN_CFG = 10   # seed tag of the softmax-block attention inputs
+
+
+def attn_chunk(chunk: int, B: int, T: int, H: int, D: int, *, stream: int = 0, step: int = 0,
+               q_scale: float = 1.0) -> dict:
+    """q, k, v [B, T, H, D] of one chunk for the softmax block's attention: N(0, 1) entries
+    (q times ``q_scale``: the logits scale*q.k then have standard deviation q_scale at the
+    default scale 1/sqrt(D)), rounded to bf16, returned as float32.
+    Seed: SeedSequence([10, stream, 0, chunk, step]); draw order q, k, v."""
+    rng = rng_for(ATTN_CFG, stream=stream, chunk=chunk, step=step)
+    q = round_bf16(q_scale * rng.standard_normal((B, T, H, D), dtype=np.float32))
+    k = round_bf16(rng.standard_normal((B, T, H, D), dtype=np.float32))
+    v = round_bf16(rng.standard_normal((B, T, H, D), dtype=np.float32))
+    return {"q": q, "k": k, "v": v}

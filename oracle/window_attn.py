@@ -66,14 +66,15 @@ class SinkWindowAttention:
         return 0 if self.k_hist is None else self.k_hist.shape[1]
 
     def chunk(self, q, k, v, commit: bool = True) -> np.ndarray:
-        """Attention of a chunk of T tokens: q, k [B, T, H, d], v [B, T, H, dv] -> o [B, T, H, dv]."""
+        """Attention of a chunk of T tokens: k [B, T, H, d], v [B, T, H, dv] -> o [B, Tq, H, dv] for
+        the queries q [B, Tq, H, d] (Tq = T for the whole chunk; fewer rows give those rows' outputs)."""
         q = np.asarray(q, np.float64)
         k = np.asarray(k, np.float64)
         v = np.asarray(v, np.float64)
-        B, T, H, d = q.shape
+        B, Tq, H, d = q.shape
         scale = self.scale if self.scale is not None else 1.0 / np.sqrt(d)
         idx = visible_tokens(self.history, self.n_sink, self.n_window)
-        o = np.empty(v.shape, np.float64)
+        o = np.empty((B, Tq, H, v.shape[-1]), np.float64)
         for b in range(B):
             for h in range(H):
                 if idx:

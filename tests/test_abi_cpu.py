@@ -8,11 +8,12 @@ import pytest
 
 from gated_deltanet_streaming_amd import binding
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "gdn_stream.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADERS = [os.path.join(INCLUDE, "gdn_stream.h"), os.path.join(INCLUDE, "gdn_attn.h")]
 
 
 def declared_symbols():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"GDN_API\s+[\w\s\*]+?\b(gdn_\w+)\s*\(", text)))
 
 
@@ -24,7 +25,8 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_symbols()
     for required in ("gdn_stream_init", "gdn_stream_destroy", "gdn_chunk_forward", "gdn_chunk_reverse",
-                     "gdn_state_get", "gdn_state_set", "gdn_last_error"):
+                     "gdn_state_get", "gdn_state_set", "gdn_last_error", "gdn_attn_init", "gdn_attn_chunk",
+                     "gdn_attn_destroy"):
         assert required in names
 
 
@@ -96,3 +98,41 @@ def test_peaks_library_exports_its_probes():
     # argument checks only (no device work): null buffers and a size that is not a multiple of 16
     assert lib.gdn_peak_copy(None, None, 1024, 1, 0, None, ctypes.byref(ms)) == -1
     assert lib.gdn_peak_copy(1, 1, 1000, 1, 0, None, ctypes.byref(ms)) == -1
+
+
+def _attn_cfg(**kw):
+    base = dict(batch=1, heads=20, head_dim=112, sink_tokens=880, window_tokens=2640, max_tokens=2640, scale=0.0)
+    base.update(kw)
+    return binding.GdnAttnConfig(**base)
+
+
+@pytest.mark.parametrize("bad, code", [
+    (dict(batch=0), binding.GDN_E_SHAPE),
+    (dict(heads=0), binding.GDN_E_SHAPE),
+    (dict(head_dim=96), binding.GDN_E_SHAPE),
+    (dict(head_dim=32), binding.GDN_E_SHAPE),
+    (dict(sink_tokens=-1), binding.GDN_E_SHAPE),
+    (dict(window_tokens=-5), binding.GDN_E_SHAPE),
+    (dict(max_tokens=0), binding.GDN_E_SHAPE),
+    (dict(scale=-1.0), binding.GDN_E_INVAL),
+    (dict(scale=float("inf")), binding.GDN_E_INVAL),
+])
+def test_attn_init_rejects_bad_config(lib, bad, code):
+    h = ctypes.c_void_p(123)
+    rc = lib.gdn_attn_init(ctypes.byref(_attn_cfg(**bad)), 0, ctypes.byref(h))
+    assert rc == code
+    assert h.value is None
+    assert binding.gdn_last_error()
+
+
+def test_attn_null_arguments_are_rejected(lib):
+    h = ctypes.c_void_p()
+    assert lib.gdn_attn_init(None, 0, ctypes.byref(h)) == binding.GDN_E_INVAL
+    io = binding.GdnAttnIo()
+    assert lib.gdn_attn_chunk(None, ctypes.byref(io), 1, 0, None) == binding.GDN_E_INVAL
+    assert "handle" in binding.gdn_last_error()
+    assert lib.gdn_attn_reset(None) == binding.GDN_E_INVAL
+    assert lib.gdn_attn_cache_len(None, None, None) == binding.GDN_E_INVAL
+    assert lib.gdn_attn_profile(None, 1) == binding.GDN_E_INVAL
+    assert lib.gdn_attn_profile_read(None, None, None, 0) == binding.GDN_E_INVAL
+    assert lib.gdn_attn_destroy(None) == binding.GDN_OK
