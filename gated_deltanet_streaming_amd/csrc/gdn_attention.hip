@@ -19,9 +19,9 @@
 // of the second product once its key index becomes the contraction index: slot i of group g
 // in a 32-key step c stands for key 32c + 4g + i (i < 4) or 32c + 16 + 4g + (i - 4) (i >= 4).
 // V is written to LDS transposed, in exactly that key order, so that each A operand is one
-// 16-byte LDS read.  The softmax is online in the log2 domain (running maximum m and partial
-// sum l per lane; O^T rescaled by 2^(m_old - m_new) when the maximum grows); p enters the
-// second product rounded to bf16, l sums the fp32 values.
+// 16-byte LDS read.  The softmax is online in the log2 domain (reference maximum m and partial
+// sum l per lane; O^T and l rescaled by 2^(m_old - m_new) when m moves); p enters the second
+// product rounded to bf16, l sums the fp32 values.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -66,13 +66,19 @@ __device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
                                                    bf16x8{b[0], b[1], b[2], b[3], z, z, z, z}, c, 0, 0, 0);
 }
 
-struct Seg {
-    const bf16* k;
-    const bf16* v;
-    int64_t ks, vs;  // token strides, elements
-    int n;           // tokens
-    int nt;          // tiles
-};
+// loads through the global address space (flat loads would also hold the LDS counter)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 gload16(const void* p) {
+    return __builtin_bit_cast(uint4, *(__attribute__((address_space(1))) const u32x4*)p);
+}
+__device__ __forceinline__ uint2 gload8(const void* p) {
+    return __builtin_bit_cast(uint2, *(__attribute__((address_space(1))) const u32x2*)p);
+}
+// raw buffer resource over [base, base + bytes); loads beyond it return zero
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
 
 template <int D>
 __global__ __launch_bounds__(NTHR, 2) void attn_kernel(AttnParams p) {
@@ -83,6 +89,10 @@ __global__ __launch_bounds__(NTHR, 2) void attn_kernel(AttnParams p) {
     const int b = blockIdx.z, h = blockIdx.y;
     const int64_t bh = (int64_t)b * p.H + h;
     const int64_t q0 = (int64_t)blockIdx.x * QT + wave * (QB * 16);
+    // launch arguments as plain locals (the lambdas below must not take the argument block's address)
+    const int T = p.T, n_sink = p.n_sink, n_win = p.n_win;
+    const int64_t ks_chunk = p.ks[1], vs_chunk = p.vs[1];
+    const float scale_log2 = p.scale_log2;
 
     // Q fragments: lane holds query q0 + 16 qb + r, d = 32 s + 8 g .. +7 (tail: d = 32 NS + 4 g .. +3)
     bf16x8 qf[QB][TL::NS > 0 ? TL::NS : 1];
@@ -91,41 +101,35 @@ __global__ __launch_bounds__(NTHR, 2) void attn_kernel(AttnParams p) {
         const bf16* qbase = static_cast<const bf16*>(p.q) + b * p.qs[0] + h * p.qs[2];
         for (int qb = 0; qb < QB; ++qb) {
             const int64_t t = q0 + 16 * qb + r;
-            const bool in = t < p.T;
+            const bool in = t < T;
             const bf16* row = qbase + (in ? t : 0) * p.qs[1];
 #pragma unroll
             for (int s = 0; s < TL::NS; ++s) {
-                uint4 x = in ? *reinterpret_cast<const uint4*>(row + 32 * s + 8 * g) : uint4{0, 0, 0, 0};
+                uint4 x = in ? gload16(row + 32 * s + 8 * g) : uint4{0, 0, 0, 0};
                 qf[qb][s] = __builtin_bit_cast(bf16x8, x);
             }
             if constexpr (TL::TAIL) {
-                uint2 x = in ? *reinterpret_cast<const uint2*>(row + 32 * TL::NS + 4 * g) : uint2{0, 0};
+                uint2 x = in ? gload8(row + 32 * TL::NS + 4 * g) : uint2{0, 0};
                 qt[qb] = __builtin_bit_cast(bf16x4, x);
             }
         }
     }
 
-    Seg seg[3];
-    seg[0] = Seg{static_cast<const bf16*>(p.k_sink) + bh * p.sink_cap * D,
-                 static_cast<const bf16*>(p.v_sink) + bh * p.sink_cap * D, D, D, p.n_sink, 0};
-    seg[1] = Seg{static_cast<const bf16*>(p.k_win) + bh * p.win_cap * D,
-                 static_cast<const bf16*>(p.v_win) + bh * p.win_cap * D, D, D, p.n_win, 0};
-    seg[2] = Seg{static_cast<const bf16*>(p.k) + b * p.ks[0] + h * p.ks[2],
-                 static_cast<const bf16*>(p.v) + b * p.vs[0] + h * p.vs[2], p.ks[1], p.vs[1], p.T, 0};
-    for (int i = 0; i < 3; ++i) seg[i].nt = (seg[i].n + KT - 1) / KT;
-    const int ntiles = seg[0].nt + seg[1].nt + seg[2].nt;
+    // the three key/value segments: sink, window (cache, [B][H][capacity][D]) and the chunk
+    const bf16* k0 = static_cast<const bf16*>(p.k_sink) + bh * p.sink_cap * D;
+    const bf16* v0 = static_cast<const bf16*>(p.v_sink) + bh * p.sink_cap * D;
+    const bf16* k1 = static_cast<const bf16*>(p.k_win) + bh * p.win_cap * D;
+    const bf16* v1 = static_cast<const bf16*>(p.v_win) + bh * p.win_cap * D;
+    const bf16* k2 = static_cast<const bf16*>(p.k) + b * p.ks[0] + h * p.ks[2];
+    const bf16* v2 = static_cast<const bf16*>(p.v) + b * p.vs[0] + h * p.vs[2];
+    const int nt0 = (n_sink + KT - 1) / KT, nt1 = (n_win + KT - 1) / KT, nt2 = (T + KT - 1) / KT;
+    const int ntiles = nt0 + nt1 + nt2;
 
-    // tile t -> its rows: key pointer, value pointer, strides, valid rows
-    auto locate = [&](int t, const bf16*& kp, const bf16*& vp, int64_t& ks, int64_t& vs, int& cnt) {
-        int i = 0;
-        if (t >= seg[0].nt) { t -= seg[0].nt; i = 1; }
-        if (i == 1 && t >= seg[1].nt) { t -= seg[1].nt; i = 2; }
-        const Seg& sg = seg[i];
-        kp = sg.k + (int64_t)t * KT * sg.ks;
-        vp = sg.v + (int64_t)t * KT * sg.vs;
-        ks = sg.ks;
-        vs = sg.vs;
-        cnt = min(KT, sg.n - t * KT);
+    // valid rows of tile t (uniform)
+    auto tile_rows = [&](int t) __attribute__((always_inline)) {
+        if (t < nt0) return min(KT, n_sink - t * KT);
+        if (t < nt0 + nt1) return min(KT, n_win - (t - nt0) * KT);
+        return min(KT, T - (t - nt0 - nt1) * KT);
     };
 
     // V task of this thread: key quad vq (keys 4 vq .. 4 vq + 3), 16-byte d-chunk vu
@@ -136,26 +140,43 @@ __global__ __launch_bounds__(NTHR, 2) void attn_kernel(AttnParams p) {
 
     uint4 kreg[TL::KLOADS];
     uint4 vreg[4];
-    auto fetch = [&](int t) {
-        const bf16 *kp, *vp;
-        int64_t ks, vs;
-        int cnt;
-        locate(t, kp, vp, ks, vs, cnt);
+    // global -> registers through buffer loads: one resource per segment and tensor, bounded
+    // by the segment's valid rows, so rows past the end read as zero without a test; per tile
+    // only the scalar offset changes.  Thread offsets: K chunk (row, u) of load i, V chunk vu
+    // of rows 4 vq + j.
+    const auto rk0 = rsrc(k0, (int64_t)n_sink * D * 2), rv0 = rsrc(v0, (int64_t)n_sink * D * 2);
+    const auto rk1 = rsrc(k1, (int64_t)n_win * D * 2), rv1 = rsrc(v1, (int64_t)n_win * D * 2);
+    const auto rk2 = rsrc(k2, T > 0 ? ((int64_t)(T - 1) * ks_chunk + D) * 2 : 0);
+    const auto rv2 = rsrc(v2, T > 0 ? ((int64_t)(T - 1) * vs_chunk + D) * 2 : 0);
+    int krow[TL::KLOADS], kcol[TL::KLOADS];
 #pragma unroll
-        for (int i = 0; i < TL::KLOADS; ++i) {
-            const int idx = tid + NTHR * i;
-            const int row = idx / TL::KCH, u = idx % TL::KCH;
-            kreg[i] = (idx < KT * TL::KCH && row < cnt) ? *reinterpret_cast<const uint4*>(kp + row * ks + 8 * u)
-                                                        : uint4{0, 0, 0, 0};
-        }
+    for (int i = 0; i < TL::KLOADS; ++i) {
+        const int idx = min(tid + NTHR * i, KT * TL::KCH - 1);
+        krow[i] = idx / TL::KCH;
+        kcol[i] = 16 * (idx % TL::KCH);
+    }
+    const int vcol = vtask ? 16 * vu : 0;
+    auto fetch_rows = [&](__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int kstride, int vstride, int tt)
+                          __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = 4 * vq + j;
-            vreg[j] = (vtask && row < cnt) ? *reinterpret_cast<const uint4*>(vp + row * vs + 8 * vu)
-                                           : uint4{0, 0, 0, 0};
-        }
+        for (int i = 0; i < TL::KLOADS; ++i)
+            kreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    rk, krow[i] * kstride + kcol[i], tt * KT * kstride, 0));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            vreg[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    rv, (4 * vq + j) * vstride + vcol, tt * KT * vstride, 0));
     };
-    auto deposit = [&](int buf) {
+    // tile t of the sequence sink, window, chunk
+    auto fetch = [&](int t) __attribute__((always_inline)) {
+        if (t < nt0)
+            fetch_rows(rk0, rv0, 2 * D, 2 * D, t);
+        else if (t < nt0 + nt1)
+            fetch_rows(rk1, rv1, 2 * D, 2 * D, t - nt0);
+        else
+            fetch_rows(rk2, rv2, (int)(2 * ks_chunk), (int)(2 * vs_chunk), t - nt0 - nt1);
+    };
+    auto deposit = [&](int buf) __attribute__((always_inline)) {
         char* kb = lds + buf * TL::BUF;
 #pragma unroll
         for (int i = 0; i < TL::KLOADS; ++i) {
@@ -194,16 +215,14 @@ __global__ __launch_bounds__(NTHR, 2) void attn_kernel(AttnParams p) {
         fetch(0);
         deposit(0);
     }
+    // every load issued so far (Q fragments, tile 0) has landed: without this the waits inside
+    // the loop cannot tell the Q loads from the prefetch and wait for both every tile
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
     __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1;
         if (t + 1 < ntiles) fetch(t + 1);
-        int cnt;
-        {
-            const bf16 *kp, *vp;
-            int64_t ks, vs;
-            locate(t, kp, vp, ks, vs, cnt);
-        }
+        const int cnt = tile_rows(t);
         const char* kb = lds + buf * TL::BUF;
         const char* vb = kb + TL::K_BYTES;
 
@@ -226,36 +245,50 @@ __global__ __launch_bounds__(NTHR, 2) void attn_kernel(AttnParams p) {
             }
         }
 
-        // online softmax (log2 domain) and P^T fragments
-        bf16x8 pf[QB][KT / 32];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            float mx = -__builtin_inff();
+        // online softmax (log2 domain) and P^T fragments.  Only a segment's last tile is
+        // masked.  The reference maximum m of a query moves only when a tile's maximum exceeds
+        // it by more than 8 (p then stays below 2^8, exact enough in fp32 and in bf16); the
+        // rescale of O^T and l is skipped when no query of the wavefront needs it.
+        if (cnt < KT) {
 #pragma unroll
             for (int kk = 0; kk < KT / 16; ++kk)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bool valid = kk * 16 + 4 * g + i < cnt;
-                    st[kk][qb][i] = valid ? st[kk][qb][i] * p.scale_log2 : -__builtin_inff();
-                    mx = fmaxf(mx, st[kk][qb][i]);
-                }
+                for (int i = 0; i < 4; ++i)
+                    if (kk * 16 + 4 * g + i >= cnt)
+#pragma unroll
+                        for (int qb = 0; qb < QB; ++qb) st[kk][qb][i] = -__builtin_inff();
+        }
+        bf16x8 pf[QB][KT / 32];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            float mx = st[0][qb][0];
+#pragma unroll
+            for (int e = 1; e < 4 * (KT / 16); e += 2) {
+                const int e1 = e + 1 < 4 * (KT / 16) ? e + 1 : e;
+                mx = fmaxf(fmaxf(mx, st[e / 4][qb][e % 4]), st[e1 / 4][qb][e1 % 4]);
+            }
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mnew = fmaxf(m[qb], mx);
-            const float alpha = __builtin_amdgcn_exp2f(m[qb] - mnew);
-            m[qb] = mnew;
+            const float ms = mx * scale_log2;
+            if (__any(ms > m[qb] + 8.0f)) {
+                const float mnew = fmaxf(m[qb], ms);
+                const float alpha = __builtin_amdgcn_exp2f(m[qb] - mnew);
+                m[qb] = mnew;
+                l[qb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < TL::ND; ++db) o[db][qb] *= alpha;
+            }
+            const float nm = -m[qb];
             float ls = 0.f;
             float pv[KT / 16][4];
 #pragma unroll
             for (int kk = 0; kk < KT / 16; ++kk)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    pv[kk][i] = __builtin_amdgcn_exp2f(st[kk][qb][i] - mnew);
+                    pv[kk][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kk][qb][i], scale_log2, nm));
                     ls += pv[kk][i];
                 }
-            l[qb] = l[qb] * alpha + ls;
-#pragma unroll
-            for (int db = 0; db < TL::ND; ++db) o[db][qb] *= alpha;
+            l[qb] += ls;
 #pragma unroll
             for (int c = 0; c < KT / 32; ++c)
                 pf[qb][c] = bf16x8{(bf16)pv[2 * c][0], (bf16)pv[2 * c][1], (bf16)pv[2 * c][2], (bf16)pv[2 * c][3],
@@ -288,7 +321,7 @@ __global__ __launch_bounds__(NTHR, 2) void attn_kernel(AttnParams p) {
         lt += __shfl_xor(lt, 32);
         const float inv = 1.0f / lt;
         const int64_t t = q0 + 16 * qb + r;
-        if (t < p.T) {
+        if (t < T) {
             bf16* row = obase + t * p.os[1];
 #pragma unroll
             for (int db = 0; db < TL::ND; ++db) {
