@@ -75,6 +75,26 @@ __device__ __forceinline__ uint4 gload16(const void* p) {
 __device__ __forceinline__ uint2 gload8(const void* p) {
     return __builtin_bit_cast(uint2, *(__attribute__((address_space(1))) const u32x2*)p);
 }
+// Reductions over the 4 lanes that share a query (lanes l, l ^ 16, l ^ 32, l ^ 48) with the
+// gfx950 lane swaps: with both operands the same value, the pair returned by
+// permlane16_swap holds, in every lane, its own and its l ^ 16 partner's value (in some
+// order), and permlane32_swap likewise for l ^ 32.
+__device__ __forceinline__ float max4q(float x) {
+    const unsigned u = __float_as_uint(x);
+    auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const unsigned w = __float_as_uint(x);
+    auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum4q(float x) {
+    const unsigned u = __float_as_uint(x);
+    auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const unsigned w = __float_as_uint(x);
+    auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 // raw buffer resource over [base, base + bytes); loads beyond it return zero
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -226,23 +246,34 @@ __global__ __launch_bounds__(NTHR, 2) void attn_kernel(AttnParams p) {
         const char* kb = lds + buf * TL::BUF;
         const char* vb = kb + TL::K_BYTES;
 
-        // S^T = K Q^T: 4 key blocks x QB query blocks
+        // S^T = K Q^T: 4 key blocks x QB query blocks, d-steps outermost so that 4 * QB
+        // independent accumulations separate the dependent ones
         f32x4 st[KT / 16][QB];
 #pragma unroll
-        for (int kk = 0; kk < KT / 16; ++kk) {
+        for (int kk = 0; kk < KT / 16; ++kk)
+#pragma unroll
             for (int qb = 0; qb < QB; ++qb) st[kk][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const char* krow = kb + (kk * 16 + r) * TL::KS;
+        const char* krow = kb + r * TL::KS;
 #pragma unroll
-            for (int s = 0; s < TL::NS; ++s) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 64 * s + 16 * g);
+        for (int s = 0; s < TL::NS; ++s) {
+            bf16x8 a[KT / 16];
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) st[kk][qb] = mma32(a, qf[qb][s], st[kk][qb]);
-            }
-            if constexpr (TL::TAIL) {
-                const bf16x4 a = *reinterpret_cast<const bf16x4*>(krow + 64 * TL::NS + 8 * g);
+            for (int kk = 0; kk < KT / 16; ++kk)
+                a[kk] = *reinterpret_cast<const bf16x8*>(krow + kk * 16 * TL::KS + 64 * s + 16 * g);
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) st[kk][qb] = mma16(a, qt[qb], st[kk][qb]);
-            }
+            for (int kk = 0; kk < KT / 16; ++kk)
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) st[kk][qb] = mma32(a[kk], qf[qb][s], st[kk][qb]);
+        }
+        if constexpr (TL::TAIL) {
+            bf16x4 a[KT / 16];
+#pragma unroll
+            for (int kk = 0; kk < KT / 16; ++kk)
+                a[kk] = *reinterpret_cast<const bf16x4*>(krow + kk * 16 * TL::KS + 64 * TL::NS + 8 * g);
+#pragma unroll
+            for (int kk = 0; kk < KT / 16; ++kk)
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) st[kk][qb] = mma16(a[kk], qt[qb], st[kk][qb]);
         }
 
         // online softmax (log2 domain) and P^T fragments.  Only a segment's last tile is
@@ -267,8 +298,7 @@ __global__ __launch_bounds__(NTHR, 2) void attn_kernel(AttnParams p) {
                 const int e1 = e + 1 < 4 * (KT / 16) ? e + 1 : e;
                 mx = fmaxf(fmaxf(mx, st[e / 4][qb][e % 4]), st[e1 / 4][qb][e1 % 4]);
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = max4q(mx);
             const float ms = mx * scale_log2;
             if (__any(ms > m[qb] + 8.0f)) {
                 const float mnew = fmaxf(m[qb], ms);
@@ -296,17 +326,15 @@ __global__ __launch_bounds__(NTHR, 2) void attn_kernel(AttnParams p) {
                                    (bf16)pv[2 * c + 1][3]};
         }
 
-        // O^T += V^T P^T
+        // O^T += V^T P^T, 32-key steps outermost (2 * ND * QB accumulations in between)
 #pragma unroll
-        for (int db = 0; db < TL::ND; ++db) {
-            const char* vrow = vb + (db * 16 + r) * VT_STRIDE;
+        for (int c = 0; c < KT / 32; ++c)
 #pragma unroll
-            for (int c = 0; c < KT / 32; ++c) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(vrow + 64 * c + 16 * g);
+            for (int db = 0; db < TL::ND; ++db) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(vb + (db * 16 + r) * VT_STRIDE + 64 * c + 16 * g);
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) o[db][qb] = mma32(a, pf[qb][c], o[db][qb]);
             }
-        }
 
         if (t + 1 < ntiles) deposit(buf ^ 1);
         __syncthreads();
@@ -316,9 +344,7 @@ __global__ __launch_bounds__(NTHR, 2) void attn_kernel(AttnParams p) {
     bf16* obase = static_cast<bf16*>(p.o) + b * p.os[0] + h * p.os[2];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        float lt = l[qb];
-        lt += __shfl_xor(lt, 16);
-        lt += __shfl_xor(lt, 32);
+        const float lt = sum4q(l[qb]);
         const float inv = 1.0f / lt;
         const int64_t t = q0 + 16 * qb + r;
         if (t < T) {
