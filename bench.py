@@ -136,9 +136,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--mode", choices=["bidir", "separate", "backward"], default="bidir",
+    ap.add_argument("--mode", choices=["bidir", "separate", "backward", "attention"], default="bidir",
                     help="bidir: one gdn_chunk_bidir call per step; separate: forward then reverse calls; "
-                         "backward: the gradients of both scans of the pair (gdn_chunk_backward)")
+                         "backward: the gradients of both scans of the pair (gdn_chunk_backward); "
+                         "attention: the softmax block's sink + window attention (gdn_attn_chunk)")
     ap.add_argument("--sets", type=int, default=6, help="rotating input/output buffer sets (1 = warm)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-peaks", action="store_true", help="skip the copy / MFMA peak probes")
@@ -153,6 +154,8 @@ def main():
 
     if args.mode == "backward":
         return main_backward(args)
+    if args.mode == "attention":
+        return main_attention(args)
 
     import numpy as np
     import torch
@@ -391,6 +394,102 @@ def main_backward(args):
                                "sample": f"{hs} of {H} heads, full {T} tokens, both scans' gradients, scaled "
                                          f"to {H} heads ({dt:.1f} s per step)"}
     s.close()
+    print(json.dumps(out), flush=True)
+
+
+ATTN_SINK, ATTN_WINDOW = 880, 2640   # one latent frame of sink, one chunk of window
+
+
+def main_attention(args):
+    """The softmax block of the hybrid DiT at the 720p layer shape in steady state: every step
+    is one committed gdn_attn_chunk call on a 2640-token chunk whose queries attend over
+    880 sink + 2640 window + 2640 chunk = 6160 keys (attention kernel plus cache append),
+    reported against the bf16 MFMA roofline of its algorithmic flops."""
+    import numpy as np
+    import torch
+
+    import gdn_inputs
+    from gated_deltanet_streaming_amd import binding as gb
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    nsets = max(1, args.sets)
+    sets = []
+    for i in range(nsets):
+        d = gdn_inputs.attn_chunk(i, B, T, H, D)
+        sets.append([torch.from_numpy(d[k]).to(dev, torch.bfloat16) for k in ("q", "k", "v")])
+    outs = [torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev) for _ in range(nsets)]
+    att = gb.WindowAttention(B, H, D, ATTN_SINK, ATTN_WINDOW, T, device=0)
+    stream = torch.cuda.current_stream(dev)
+    for i in range(2):                       # fill the sink and the window
+        att.chunk(*sets[i % nsets], outs[0], stream=stream)
+    L = ATTN_SINK + ATTN_WINDOW + T
+    n = [0]
+
+    def step():
+        i = n[0] % nsets
+        n[0] += 1
+        att.chunk(*sets[i], outs[i], stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert att.cache_len() == (ATTN_SINK, ATTN_WINDOW)
+    w0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - w0) * 1e3 / args.steps
+    gb.gdn_attn_profile(att.handle, True)
+    gb.gdn_attn_profile_read(att.handle, reset=True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    k_ms, k_n = gb.gdn_attn_profile_read(att.handle, reset=True)
+    gb.gdn_attn_profile(att.handle, False)
+    if args.copy_probe:   # a 256 MiB device copy: the reference that scales the byte counters
+        src = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+    launch_ms = k_ms / max(k_n, 1)
+    flops = 4.0 * B * H * T * L * D          # q.k and p.v, 2 flops per multiply-add
+    achieved = flops / (launch_ms * 1e-3) / 1e12
+    out = {
+        "metric": "softmax-block (sink + window attention) tokens/s per layer at 2640-token 720p chunk",
+        "value": round(T / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "720p streaming chunk, one softmax block in steady state: 2640 queries over "
+                               "880 sink + 2640 window + 2640 chunk keys", "B": B, "H": H, "d": D, "T": T,
+                   "sink": ATTN_SINK, "window": ATTN_WINDOW, "keys": L, "call": "gdn_attn_chunk (commit)"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_kernel", "kernel_avg_us": round(launch_ms * 1e3, 1),
+                     "algorithmic_flops_per_launch": flops},
+    }
+    if not args.no_cpu:
+        from oracle.window_attn import SinkWindowAttention
+        import threadpoolctl
+        hs = H   # the whole steady-state chunk (about 73 GFLOP in fp64: seconds on the host)
+        ref = SinkWindowAttention(ATTN_SINK, ATTN_WINDOW)
+        for i in range(2):
+            d = gdn_inputs.attn_chunk(i, B, T, H, D)
+            ref.chunk(d["q"][:, :1, :hs], d["k"][:, :, :hs], d["v"][:, :, :hs])
+        d = gdn_inputs.attn_chunk(2, B, T, H, D)
+        t0 = time.perf_counter()
+        ref.chunk(d["q"][:, :, :hs], d["k"][:, :, :hs], d["v"][:, :, :hs])
+        dt = (time.perf_counter() - t0) * H / hs
+        blas = [p["num_threads"] for p in threadpoolctl.threadpool_info() if p.get("user_api") == "blas"]
+        out["cpu_baseline"] = {"value": round(T / dt, 1), "unit": "tokens/s",
+                               "cores": max(blas) if blas else 1, "kind": "oracle",
+                               "sample": f"{hs} of {H} heads of one steady-state chunk ({L} keys), numpy fp64 "
+                                         f"matmuls ({dt:.2f} s per step)"}
+    att.close()
     print(json.dumps(out), flush=True)
 
 

@@ -106,9 +106,16 @@ __global__ __launch_bounds__(NTHR, 2) void attn_kernel(AttnParams p) {
     __shared__ __align__(16) char lds[2 * TL::BUF];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
-    const int b = blockIdx.z, h = blockIdx.y;
+    // Work item of this workgroup.  Consecutive workgroups are dispatched to the 8 XCDs in
+    // turn, and each XCD has its own L2: the k-th workgroup of XCD x takes item
+    // start(x) + k, so that an XCD works through a contiguous band of items, i.e. through the
+    // query tiles of a few heads, whose keys and values then stay in its L2.
+    const int nwg = gridDim.x, xcd = blockIdx.x % 8, k8 = blockIdx.x / 8;
+    const int item = xcd * (nwg / 8) + min(xcd, nwg % 8) + k8;
+    const int nqt = (p.T + QT - 1) / QT;
+    const int qtile = item % nqt, h = (item / nqt) % p.H, b = item / (nqt * p.H);
     const int64_t bh = (int64_t)b * p.H + h;
-    const int64_t q0 = (int64_t)blockIdx.x * QT + wave * (QB * 16);
+    const int64_t q0 = (int64_t)qtile * QT + wave * (QB * 16);
     // launch arguments as plain locals (the lambdas below must not take the argument block's address)
     const int T = p.T, n_sink = p.n_sink, n_win = p.n_win;
     const int64_t ks_chunk = p.ks[1], vs_chunk = p.vs[1];
@@ -361,46 +368,51 @@ __global__ __launch_bounds__(NTHR, 2) void attn_kernel(AttnParams p) {
 
 // Copies the chunk's k, v rows into the cache: token i < taken fills sink slot sink_fill + i;
 // the rest go to the window ring (slot (win_base + j) mod win_cap), where the first `skip`
-// of them are already older than the window and are not written.  One 64-lane workgroup per
-// (token, head, stream).
+// of them are already older than the window and are not written.  One thread per 16-byte
+// chunk of a k or v row; items ordered (token, stream, head, k/v, chunk).
 template <int D>
-__global__ __launch_bounds__(64) void attn_append_kernel(AppendParams p) {
+__global__ __launch_bounds__(256) void attn_append_kernel(AppendParams p) {
     constexpr int KCH = D / 8;
-    const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= (int64_t)p.T * p.B * p.H * 2 * KCH) return;
+    const int c = (int)(gid % (2 * KCH));
+    int64_t rest = gid / (2 * KCH);
+    const int h = (int)(rest % p.H);
+    rest /= p.H;
+    const int b = (int)(rest % p.B);
+    const int i = (int)(rest / p.B);
     const int64_t bh = (int64_t)b * p.H + h;
-    bf16 *kd, *vd;
+    const bool isv = c >= KCH;
+    const int u = isv ? c - KCH : c;
+    int64_t slot;
+    bf16* dst;
     if (i < p.taken) {
-        const int64_t slot = bh * p.sink_cap + p.sink_fill + i;
-        kd = static_cast<bf16*>(p.k_sink) + slot * D;
-        vd = static_cast<bf16*>(p.v_sink) + slot * D;
+        slot = bh * p.sink_cap + p.sink_fill + i;
+        dst = static_cast<bf16*>(isv ? p.v_sink : p.k_sink);
     } else {
         const int j = i - p.taken;
         if (j < p.skip) return;
-        const int64_t slot = bh * p.win_cap + (int)(((int64_t)p.win_base + j) % p.win_cap);
-        kd = static_cast<bf16*>(p.k_win) + slot * D;
-        vd = static_cast<bf16*>(p.v_win) + slot * D;
+        slot = bh * p.win_cap + (int)(((int64_t)p.win_base + j) % p.win_cap);
+        dst = static_cast<bf16*>(isv ? p.v_win : p.k_win);
     }
-    if (lane < KCH) {
-        const bf16* ks = static_cast<const bf16*>(p.k) + b * p.ks[0] + (int64_t)i * p.ks[1] + h * p.ks[2];
-        *reinterpret_cast<uint4*>(kd + 8 * lane) = *reinterpret_cast<const uint4*>(ks + 8 * lane);
-    } else if (lane < 2 * KCH) {
-        const int u = lane - KCH;
-        const bf16* vs = static_cast<const bf16*>(p.v) + b * p.vs[0] + (int64_t)i * p.vs[1] + h * p.vs[2];
-        *reinterpret_cast<uint4*>(vd + 8 * u) = *reinterpret_cast<const uint4*>(vs + 8 * u);
-    }
+    const bf16* src = isv ? static_cast<const bf16*>(p.v) + b * p.vs[0] + (int64_t)i * p.vs[1] + h * p.vs[2]
+                          : static_cast<const bf16*>(p.k) + b * p.ks[0] + (int64_t)i * p.ks[1] + h * p.ks[2];
+    *reinterpret_cast<uint4*>(dst + slot * D + 8 * u) = gload16(src + 8 * u);
 }
 
 template <int D>
 hipError_t launch_attn_d(const AttnParams& p, hipStream_t s) {
-    dim3 grid((unsigned)((p.T + QT - 1) / QT), (unsigned)p.H, (unsigned)p.B);
-    hipLaunchKernelGGL(attn_kernel<D>, grid, dim3(NTHR), 0, s, p);
+    const int64_t nwg = (int64_t)((p.T + QT - 1) / QT) * p.H * p.B;
+    if (nwg >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(attn_kernel<D>, dim3((unsigned)nwg), dim3(NTHR), 0, s, p);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_append_d(const AppendParams& p, hipStream_t s) {
-    dim3 grid((unsigned)p.T, (unsigned)p.H, (unsigned)p.B);
-    hipLaunchKernelGGL(attn_append_kernel<D>, grid, dim3(64), 0, s, p);
+    const int64_t n = (int64_t)p.T * p.B * p.H * 2 * (D / 8);
+    if ((n + 255) / 256 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(attn_append_kernel<D>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
