@@ -44,10 +44,12 @@ STATE_BYTES = B * H * D * D * 4
 FLOPS_PER_TOKEN_HEAD = 6 * D * D             # S k, rank-1 update, S q
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_scan_720p.json")
 KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_streaming_amd", "csrc", "gdn_kernels.hip")
+ATTN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_720p.json")
+ATTN_KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_streaming_amd", "csrc", "gdn_attention.hip")
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_source_hash(src: str = KERNEL_SRC) -> str:
+    with open(src, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
@@ -59,15 +61,15 @@ def algorithmic_bytes(mode: str) -> int:
     return 2 * per_scan + 2 * STATE_BYTES
 
 
-def load_traffic():
-    """HBM bytes per scan launch from the committed rocprofv3 counter runs, if they
-    were taken on the current kernel source; else None."""
+def load_traffic(path: str = TRAFFIC_FILE, src: str = KERNEL_SRC):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter runs,
+    if they were taken on the current kernel source; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash(src):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -468,7 +470,8 @@ def main_attention(args):
                                "880 sink + 2640 window + 2640 chunk keys", "B": B, "H": H, "d": D, "T": T,
                    "sink": ATTN_SINK, "window": ATTN_WINDOW, "keys": L, "call": "gdn_attn_chunk (commit)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": load_traffic(ATTN_TRAFFIC_FILE, ATTN_KERNEL_SRC),
                      "kernel": "attn_kernel", "kernel_avg_us": round(launch_ms * 1e3, 1),
                      "algorithmic_flops_per_launch": flops},
     }

@@ -37,7 +37,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int KT = 64;                 // keys per tile
 constexpr int QB = 2;                  // 16-query blocks per wavefront
-constexpr int NWAVE = 4;               // wavefronts per workgroup
+constexpr int NWAVE = 8;               // wavefronts per workgroup
 constexpr int NTHR = NWAVE * 64;
 constexpr int QT = NWAVE * QB * 16;    // queries per workgroup
 constexpr int VT_STRIDE = KT * 2 + 16; // bytes per d-row of the transposed V tile
