@@ -8,6 +8,7 @@
 // enqueued; on error the cache is untouched and nothing runs.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -556,7 +557,11 @@ GDN_API int gdn_attn_init(const gdn_attn_config* cfg, int device, gdn_attn** out
     if (c.max_tokens < 1 || c.max_tokens > (1 << 30)) return fail(GDN_E_SHAPE, "max_tokens must be in [1, 2^30]");
     if (!(c.scale >= 0.f) || !std::isfinite(c.scale)) return fail(GDN_E_INVAL, "scale must be finite and >= 0");
     const int64_t slots = (int64_t)c.batch * c.heads * ((int64_t)c.sink_tokens + c.window_tokens) * c.head_dim;
-    if ((int64_t)c.sink_tokens + c.window_tokens > (1 << 30)) return fail(GDN_E_SHAPE, "cache too large");
+    // the kernels address a (stream, head)'s sink or window, and a chunk, with 32-bit byte offsets
+    if ((int64_t)std::max(std::max(c.sink_tokens, c.window_tokens), (int32_t)std::min<int64_t>(c.max_tokens, 1 << 30)) *
+            c.head_dim * 2 >= ((int64_t)1 << 31))
+        return fail(GDN_E_SHAPE, "sink, window or max_tokens too large: %d x %d bf16 values exceed 2 GiB per (stream, head)",
+                    std::max(c.sink_tokens, c.window_tokens), c.head_dim);
     DeviceGuard dg(device);
     if (dg.err != hipSuccess) return fail(GDN_E_HIP, "hipSetDevice(%d): %s", device, hipGetErrorString(dg.err));
     gdn_attn* a = new (std::nothrow) gdn_attn();

@@ -39,7 +39,8 @@ typedef struct gdn_attn_config {
     int32_t head_dim;       /* d of q, k and v: 64, 112 or 128                           */
     int32_t sink_tokens;    /* sink capacity per (stream, head), >= 0                    */
     int32_t window_tokens;  /* window capacity per (stream, head), >= 0                  */
-    int64_t max_tokens;     /* largest T of any call, >= 1                               */
+    int64_t max_tokens;     /* largest T of any call, >= 1; sink_tokens, window_tokens   */
+                            /* and max_tokens times head_dim * 2 bytes stay below 2 GiB */
     float scale;            /* logit scale; 0 selects 1/sqrt(head_dim)                   */
 } gdn_attn_config;
 

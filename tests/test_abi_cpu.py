@@ -114,6 +114,9 @@ def _attn_cfg(**kw):
     (dict(sink_tokens=-1), binding.GDN_E_SHAPE),
     (dict(window_tokens=-5), binding.GDN_E_SHAPE),
     (dict(max_tokens=0), binding.GDN_E_SHAPE),
+    (dict(sink_tokens=1 << 24), binding.GDN_E_SHAPE),       # 2^24 x 112 x 2 bytes > 2 GiB
+    (dict(window_tokens=(1 << 30) - 1), binding.GDN_E_SHAPE),
+    (dict(max_tokens=1 << 24), binding.GDN_E_SHAPE),
     (dict(scale=-1.0), binding.GDN_E_INVAL),
     (dict(scale=float("inf")), binding.GDN_E_INVAL),
 ])
