@@ -8,8 +8,8 @@
 //
 // One workgroup of NWAVE wavefronts takes QT consecutive queries of one (stream, head); each
 // wavefront keeps its QB x 16 queries' Q fragments in registers for the whole call.  Keys and
-// values stream through LDS in tiles of KT keys (double-buffered, one barrier per tile), tile
-// after tile over the three segments (sink, window, chunk); a segment's last tile is masked.
+// values stream through LDS in tiles of KT keys (four buffers, one barrier per pair of tiles),
+// tile after tile over the three segments (sink, window, chunk); a segment's last tile is masked.
 // Products run on 16x16x32 bf16 MFMAs in transposed form:
 //
 //     S^T = K Q^T      (A = K rows from LDS, B = Q fragments in registers)
@@ -103,7 +103,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
 template <int D>
 __global__ __launch_bounds__(NTHR, 2) void attn_kernel(AttnParams p) {
     using TL = Tile<D>;
-    __shared__ __align__(16) char lds[2 * TL::BUF];
+    __shared__ __align__(16) char lds[4 * TL::BUF];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
     // Work item of this workgroup.  Consecutive workgroups are dispatched to the 8 XCDs in
@@ -242,108 +242,117 @@ __global__ __launch_bounds__(NTHR, 2) void attn_kernel(AttnParams p) {
         fetch(0);
         deposit(0);
     }
-    // every load issued so far (Q fragments, tile 0) has landed: without this the waits inside
-    // the loop cannot tell the Q loads from the prefetch and wait for both every tile
+    // Four LDS buffers and one barrier per pair of tiles: tile t + 2 is fetched before tile t is
+    // computed and deposited into buffer (t + 2) mod 4 right after it; that buffer was last read
+    // before the previous barrier.
+    if (ntiles > 1) {
+        fetch(1);
+        deposit(1);
+    }
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
     __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < ntiles) fetch(t + 1);
-        const int cnt = tile_rows(t);
-        const char* kb = lds + buf * TL::BUF;
-        const char* vb = kb + TL::K_BYTES;
+    for (int t0 = 0; t0 < ntiles; t0 += 2) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int t = t0 + half;
+            if (t < ntiles) {
+                if (t + 2 < ntiles) fetch(t + 2);
+                const int cnt = tile_rows(t);
+                const char* kb = lds + (t & 3) * TL::BUF;
+                const char* vb = kb + TL::K_BYTES;
 
-        // S^T = K Q^T: 4 key blocks x QB query blocks, d-steps outermost so that 4 * QB
-        // independent accumulations separate the dependent ones
-        f32x4 st[KT / 16][QB];
-#pragma unroll
-        for (int kk = 0; kk < KT / 16; ++kk)
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) st[kk][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const char* krow = kb + r * TL::KS;
-#pragma unroll
-        for (int s = 0; s < TL::NS; ++s) {
-            bf16x8 a[KT / 16];
-#pragma unroll
-            for (int kk = 0; kk < KT / 16; ++kk)
-                a[kk] = *reinterpret_cast<const bf16x8*>(krow + kk * 16 * TL::KS + 64 * s + 16 * g);
-#pragma unroll
-            for (int kk = 0; kk < KT / 16; ++kk)
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) st[kk][qb] = mma32(a[kk], qf[qb][s], st[kk][qb]);
-        }
-        if constexpr (TL::TAIL) {
-            bf16x4 a[KT / 16];
-#pragma unroll
-            for (int kk = 0; kk < KT / 16; ++kk)
-                a[kk] = *reinterpret_cast<const bf16x4*>(krow + kk * 16 * TL::KS + 64 * TL::NS + 8 * g);
-#pragma unroll
-            for (int kk = 0; kk < KT / 16; ++kk)
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) st[kk][qb] = mma16(a[kk], qt[qb], st[kk][qb]);
-        }
-
-        // online softmax (log2 domain) and P^T fragments.  Only a segment's last tile is
-        // masked.  The reference maximum m of a query moves only when a tile's maximum exceeds
-        // it by more than 8 (p then stays below 2^8, exact enough in fp32 and in bf16); the
-        // rescale of O^T and l is skipped when no query of the wavefront needs it.
-        if (cnt < KT) {
-#pragma unroll
-            for (int kk = 0; kk < KT / 16; ++kk)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (kk * 16 + 4 * g + i >= cnt)
-#pragma unroll
-                        for (int qb = 0; qb < QB; ++qb) st[kk][qb][i] = -__builtin_inff();
-        }
-        bf16x8 pf[QB][KT / 32];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            float mx = st[0][qb][0];
-#pragma unroll
-            for (int e = 1; e < 4 * (KT / 16); e += 2) {
-                const int e1 = e + 1 < 4 * (KT / 16) ? e + 1 : e;
-                mx = fmaxf(fmaxf(mx, st[e / 4][qb][e % 4]), st[e1 / 4][qb][e1 % 4]);
-            }
-            mx = max4q(mx);
-            const float ms = mx * scale_log2;
-            if (__any(ms > m[qb] + 8.0f)) {
-                const float mnew = fmaxf(m[qb], ms);
-                const float alpha = __builtin_amdgcn_exp2f(m[qb] - mnew);
-                m[qb] = mnew;
-                l[qb] *= alpha;
-#pragma unroll
-                for (int db = 0; db < TL::ND; ++db) o[db][qb] *= alpha;
-            }
-            const float nm = -m[qb];
-            float ls = 0.f;
-            float pv[KT / 16][4];
-#pragma unroll
-            for (int kk = 0; kk < KT / 16; ++kk)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pv[kk][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kk][qb][i], scale_log2, nm));
-                    ls += pv[kk][i];
+                // S^T = K Q^T: 4 key blocks x QB query blocks, d-steps outermost so that 4 * QB
+                // independent accumulations separate the dependent ones
+                f32x4 st[KT / 16][QB];
+        #pragma unroll
+                for (int kk = 0; kk < KT / 16; ++kk)
+        #pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) st[kk][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                const char* krow = kb + r * TL::KS;
+        #pragma unroll
+                for (int s = 0; s < TL::NS; ++s) {
+                    bf16x8 a[KT / 16];
+        #pragma unroll
+                    for (int kk = 0; kk < KT / 16; ++kk)
+                        a[kk] = *reinterpret_cast<const bf16x8*>(krow + kk * 16 * TL::KS + 64 * s + 16 * g);
+        #pragma unroll
+                    for (int kk = 0; kk < KT / 16; ++kk)
+        #pragma unroll
+                        for (int qb = 0; qb < QB; ++qb) st[kk][qb] = mma32(a[kk], qf[qb][s], st[kk][qb]);
                 }
-            l[qb] += ls;
-#pragma unroll
-            for (int c = 0; c < KT / 32; ++c)
-                pf[qb][c] = bf16x8{(bf16)pv[2 * c][0], (bf16)pv[2 * c][1], (bf16)pv[2 * c][2], (bf16)pv[2 * c][3],
-                                   (bf16)pv[2 * c + 1][0], (bf16)pv[2 * c + 1][1], (bf16)pv[2 * c + 1][2],
-                                   (bf16)pv[2 * c + 1][3]};
-        }
+                if constexpr (TL::TAIL) {
+                    bf16x4 a[KT / 16];
+        #pragma unroll
+                    for (int kk = 0; kk < KT / 16; ++kk)
+                        a[kk] = *reinterpret_cast<const bf16x4*>(krow + kk * 16 * TL::KS + 64 * TL::NS + 8 * g);
+        #pragma unroll
+                    for (int kk = 0; kk < KT / 16; ++kk)
+        #pragma unroll
+                        for (int qb = 0; qb < QB; ++qb) st[kk][qb] = mma16(a[kk], qt[qb], st[kk][qb]);
+                }
 
-        // O^T += V^T P^T, 32-key steps outermost (2 * ND * QB accumulations in between)
-#pragma unroll
-        for (int c = 0; c < KT / 32; ++c)
-#pragma unroll
-            for (int db = 0; db < TL::ND; ++db) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(vb + (db * 16 + r) * VT_STRIDE + 64 * c + 16 * g);
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) o[db][qb] = mma32(a, pf[qb][c], o[db][qb]);
+                // online softmax (log2 domain) and P^T fragments.  Only a segment's last tile is
+                // masked.  The reference maximum m of a query moves only when a tile's maximum exceeds
+                // it by more than 8 (p then stays below 2^8, exact enough in fp32 and in bf16); the
+                // rescale of O^T and l is skipped when no query of the wavefront needs it.
+                if (cnt < KT) {
+        #pragma unroll
+                    for (int kk = 0; kk < KT / 16; ++kk)
+        #pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (kk * 16 + 4 * g + i >= cnt)
+        #pragma unroll
+                                for (int qb = 0; qb < QB; ++qb) st[kk][qb][i] = -__builtin_inff();
+                }
+                bf16x8 pf[QB][KT / 32];
+        #pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    float mx = st[0][qb][0];
+        #pragma unroll
+                    for (int e = 1; e < 4 * (KT / 16); e += 2) {
+                        const int e1 = e + 1 < 4 * (KT / 16) ? e + 1 : e;
+                        mx = fmaxf(fmaxf(mx, st[e / 4][qb][e % 4]), st[e1 / 4][qb][e1 % 4]);
+                    }
+                    mx = max4q(mx);
+                    const float ms = mx * scale_log2;
+                    if (__any(ms > m[qb] + 8.0f)) {
+                        const float mnew = fmaxf(m[qb], ms);
+                        const float alpha = __builtin_amdgcn_exp2f(m[qb] - mnew);
+                        m[qb] = mnew;
+                        l[qb] *= alpha;
+        #pragma unroll
+                        for (int db = 0; db < TL::ND; ++db) o[db][qb] *= alpha;
+                    }
+                    const float nm = -m[qb];
+                    float ls = 0.f;
+                    float pv[KT / 16][4];
+        #pragma unroll
+                    for (int kk = 0; kk < KT / 16; ++kk)
+        #pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            pv[kk][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kk][qb][i], scale_log2, nm));
+                            ls += pv[kk][i];
+                        }
+                    l[qb] += ls;
+        #pragma unroll
+                    for (int c = 0; c < KT / 32; ++c)
+                        pf[qb][c] = bf16x8{(bf16)pv[2 * c][0], (bf16)pv[2 * c][1], (bf16)pv[2 * c][2], (bf16)pv[2 * c][3],
+                                           (bf16)pv[2 * c + 1][0], (bf16)pv[2 * c + 1][1], (bf16)pv[2 * c + 1][2],
+                                           (bf16)pv[2 * c + 1][3]};
+                }
+
+                // O^T += V^T P^T, 32-key steps outermost (2 * ND * QB accumulations in between)
+        #pragma unroll
+                for (int c = 0; c < KT / 32; ++c)
+        #pragma unroll
+                    for (int db = 0; db < TL::ND; ++db) {
+                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vb + (db * 16 + r) * VT_STRIDE + 64 * c + 16 * g);
+        #pragma unroll
+                        for (int qb = 0; qb < QB; ++qb) o[db][qb] = mma32(a, pf[qb][c], o[db][qb]);
+                    }
+                if (t + 2 < ntiles) deposit((t + 2) & 3);
             }
-
-        if (t + 1 < ntiles) deposit(buf ^ 1);
+        }
         __syncthreads();
     }
 
