@@ -96,6 +96,9 @@ def load_library():
         "gdn_attn_chunk": ([vp, ctypes.POINTER(GdnAttnIo), i64, u32, vp], i32),
         "gdn_attn_reset": ([vp], i32),
         "gdn_attn_cache_len": ([vp, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)], i32),
+        "gdn_attn_cache_bytes": ([vp, ctypes.POINTER(ctypes.c_int64)], i32),
+        "gdn_attn_cache_get": ([vp, vp, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64), vp], i32),
+        "gdn_attn_cache_set": ([vp, vp, i64, i64, vp], i32),
         "gdn_attn_profile": ([vp, i32], i32),
         "gdn_attn_profile_read": ([vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), i32], i32),
     }
@@ -318,6 +321,25 @@ def gdn_attn_cache_len(handle):
     return s.value, w.value
 
 
+def gdn_attn_cache_bytes(handle):
+    n = ctypes.c_int64()
+    _check(load_library().gdn_attn_cache_bytes(ctypes.c_void_p(handle), ctypes.byref(n)))
+    return n.value
+
+
+def gdn_attn_cache_get(handle, dst, *, stream=None):
+    """Copy the cache into the uint8 device tensor ``dst``; returns (sink_len, window_total)."""
+    s, w = ctypes.c_int64(), ctypes.c_int64()
+    _check(load_library().gdn_attn_cache_get(ctypes.c_void_p(handle), _ptr(dst), ctypes.byref(s), ctypes.byref(w),
+                                             _stream_ptr(stream, dst.device)))
+    return s.value, w.value
+
+
+def gdn_attn_cache_set(handle, src, sink_len, window_total, *, stream=None):
+    _check(load_library().gdn_attn_cache_set(ctypes.c_void_p(handle), _ptr(src), int(sink_len), int(window_total),
+                                             _stream_ptr(stream, src.device)))
+
+
 def gdn_attn_profile(handle, enable=True):
     _check(load_library().gdn_attn_profile(ctypes.c_void_p(handle), int(bool(enable))))
 
@@ -349,6 +371,16 @@ class WindowAttention:
 
     def cache_len(self):
         return gdn_attn_cache_len(self.handle)
+
+    def checkpoint(self, device="cuda"):
+        """(snapshot tensor, sink_len, window_total) of the cache."""
+        import torch
+        snap = torch.empty(gdn_attn_cache_bytes(self.handle), dtype=torch.uint8, device=device)
+        s, w = gdn_attn_cache_get(self.handle, snap)
+        return snap, s, w
+
+    def restore(self, snap, sink_len, window_total):
+        gdn_attn_cache_set(self.handle, snap, sink_len, window_total)
 
     def close(self):
         if self.handle:

@@ -717,6 +717,50 @@ GDN_API int gdn_attn_cache_len(const gdn_attn* a, int64_t* sink, int64_t* window
     return ok();
 }
 
+GDN_API int gdn_attn_cache_bytes(const gdn_attn* a, int64_t* bytes) {
+    if (!a || !bytes) return fail(GDN_E_INVAL, "handle or bytes is NULL");
+    *bytes = 4 * (int64_t)a->cfg.batch * a->cfg.heads * ((int64_t)a->cfg.sink_tokens + a->cfg.window_tokens) *
+             a->cfg.head_dim;
+    return ok();
+}
+
+GDN_API int gdn_attn_cache_get(gdn_attn* a, void* dst, int64_t* sink_len, int64_t* window_total, void* hip_stream) {
+    if (!a) return fail(GDN_E_INVAL, "handle is NULL");
+    int64_t bytes = 0;
+    (void)gdn_attn_cache_bytes(a, &bytes);
+    if (bytes > 0 && (!dst || !aligned16(dst))) return fail(GDN_E_INVAL, "dst is NULL or not 16-byte aligned");
+    DeviceGuard dg(a->device);
+    if (dg.err != hipSuccess) return fail(GDN_E_HIP, "hipSetDevice(%d): %s", a->device, hipGetErrorString(dg.err));
+    if (bytes > 0) {
+        hipError_t e = hipMemcpyAsync(dst, a->cache, bytes, hipMemcpyDeviceToDevice, static_cast<hipStream_t>(hip_stream));
+        if (e != hipSuccess) return fail(GDN_E_HIP, "cache copy: %s", hipGetErrorString(e));
+    }
+    if (sink_len) *sink_len = a->sink_fill;
+    if (window_total) *window_total = a->win_total;
+    return ok();
+}
+
+GDN_API int gdn_attn_cache_set(gdn_attn* a, const void* src, int64_t sink_len, int64_t window_total,
+                               void* hip_stream) {
+    if (!a) return fail(GDN_E_INVAL, "handle is NULL");
+    if (sink_len < 0 || sink_len > a->cfg.sink_tokens || window_total < 0 ||
+        (window_total > 0 && sink_len < a->cfg.sink_tokens))
+        return fail(GDN_E_INVAL, "counters (sink %lld, window %lld) do not describe a cache of sink %d", (long long)sink_len,
+                    (long long)window_total, a->cfg.sink_tokens);
+    int64_t bytes = 0;
+    (void)gdn_attn_cache_bytes(a, &bytes);
+    if (bytes > 0 && (!src || !aligned16(src))) return fail(GDN_E_INVAL, "src is NULL or not 16-byte aligned");
+    DeviceGuard dg(a->device);
+    if (dg.err != hipSuccess) return fail(GDN_E_HIP, "hipSetDevice(%d): %s", a->device, hipGetErrorString(dg.err));
+    if (bytes > 0) {
+        hipError_t e = hipMemcpyAsync(a->cache, src, bytes, hipMemcpyDeviceToDevice, static_cast<hipStream_t>(hip_stream));
+        if (e != hipSuccess) return fail(GDN_E_HIP, "cache copy: %s", hipGetErrorString(e));
+    }
+    a->sink_fill = sink_len;
+    a->win_total = window_total;
+    return ok();
+}
+
 GDN_API int gdn_attn_profile(gdn_attn* a, int enable) {
     if (!a) return fail(GDN_E_INVAL, "handle is NULL");
     a->profile = enable != 0;

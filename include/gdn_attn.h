@@ -78,6 +78,19 @@ GDN_API int gdn_attn_reset(gdn_attn* a);
 /* Tokens the cache holds now, per (stream, head): in the sink and in the window. */
 GDN_API int gdn_attn_cache_len(const gdn_attn* a, int64_t* sink, int64_t* window);
 
+/* Checkpoint and resume of the cache (the softmax block's counterpart of gdn_state_get/set).
+ * The snapshot is the library's cache memory as it stands: k of the sink, v of the sink, k of
+ * the window, v of the window, each bf16 [B, H, capacity, d] (gdn_attn_cache_bytes bytes in
+ * all, device memory on the handle's device, 16-byte aligned), plus two counters: the tokens
+ * in the sink and the tokens ever written to the window (its ring position).  Copies are
+ * enqueued asynchronously on `hip_stream`; get takes the state after every call enqueued
+ * before it.  set checks 0 <= sink_len <= sink_tokens, window_total >= 0 and window_total = 0
+ * unless the sink is full (GDN_E_INVAL otherwise; nothing enqueued). */
+GDN_API int gdn_attn_cache_bytes(const gdn_attn* a, int64_t* bytes);
+GDN_API int gdn_attn_cache_get(gdn_attn* a, void* dst, int64_t* sink_len, int64_t* window_total, void* hip_stream);
+GDN_API int gdn_attn_cache_set(gdn_attn* a, const void* src, int64_t sink_len, int64_t window_total,
+                               void* hip_stream);
+
 /* Optional timing of the attention kernel (not the cache append): with profiling on, every
  * launch is bracketed by hipEvents on the launch stream; gdn_attn_profile_read waits for them
  * and returns the summed milliseconds and the launch count, clearing them when `reset` != 0. */

@@ -137,5 +137,8 @@ def test_attn_null_arguments_are_rejected(lib):
     assert lib.gdn_attn_reset(None) == binding.GDN_E_INVAL
     assert lib.gdn_attn_cache_len(None, None, None) == binding.GDN_E_INVAL
     assert lib.gdn_attn_profile(None, 1) == binding.GDN_E_INVAL
+    assert lib.gdn_attn_cache_bytes(None, None) == binding.GDN_E_INVAL
+    assert lib.gdn_attn_cache_get(None, None, None, None, None) == binding.GDN_E_INVAL
+    assert lib.gdn_attn_cache_set(None, None, 0, 0, None) == binding.GDN_E_INVAL
     assert lib.gdn_attn_profile_read(None, None, None, 0) == binding.GDN_E_INVAL
     assert lib.gdn_attn_destroy(None) == binding.GDN_OK

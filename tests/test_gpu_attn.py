@@ -3,11 +3,12 @@ fp64 oracle (oracle/window_attn.py), through the C ABI.
 
 Every call of a stream is compared element by element with the oracle on the same seeded
 bf16 inputs, at max-abs <= 2e-2 and relative Frobenius <= 5e-3 over the call's output.  Cases:
-ragged chunks that cross the 64-key tile and the 128-query workgroup boundaries, a sink that
+ragged chunks that cross the 64-key tile and 32-query wavefront boundaries, a sink that
 fills over two calls, chunks longer than the window, no sink, no window, no cache at all,
 uncommitted replays (bitwise repeatable, cache unchanged), peaked logits, strided [B, H, T, D]
 buffers, and the 720p layer shape (20 heads x 112, one latent frame of sink, one chunk of
-window) through three chunks to the steady state, checked on sampled query rows.
+window) through three chunks to the steady state, checked on sampled query rows; and a cache
+checkpoint restored into a second handle, which then continues bitwise identically.
 """
 import numpy as np
 import pytest
@@ -121,3 +122,32 @@ def test_720p_layer_steady_state_sampled_rows():
         assert_close(f"o[{c}] rows", o[:, torch.from_numpy(rows).cuda()], want)
     assert att.cache_len() == (880, 2640)
     att.close()
+
+
+def test_checkpoint_resume_is_bitwise():
+    """A handle resumed from another's cache snapshot continues bitwise identically; bad
+    counters are refused."""
+    import torch
+    from gated_deltanet_streaming_amd.binding import GdnError, WindowAttention
+    B, H, D = 2, 3, 112
+    a = WindowAttention(B, H, D, 40, 100, 130)
+    for c, T in enumerate((30, 130, 64)):
+        d = gdn_inputs.attn_chunk(c, B, T, H, D)
+        a.chunk(*(_dev(d[x]) for x in ("q", "k", "v")))
+    snap, s_len, w_tot = a.checkpoint()
+    assert (s_len, w_tot) == (40, 184)
+    b = WindowAttention(B, H, D, 40, 100, 130)
+    with pytest.raises(GdnError):
+        b.restore(snap, 10, 5)          # a window cannot fill before the sink
+    b.restore(snap, s_len, w_tot)
+    assert b.cache_len() == a.cache_len()
+    d = gdn_inputs.attn_chunk(3, B, 120, H, D)
+    x = [_dev(d[k]) for k in ("q", "k", "v")]
+    oa, ob = a.chunk(*x), b.chunk(*x)
+    d = gdn_inputs.attn_chunk(4, B, 50, H, D)
+    x = [_dev(d[k]) for k in ("q", "k", "v")]
+    oa2, ob2 = a.chunk(*x), b.chunk(*x)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob) and torch.equal(oa2, ob2)
+    a.close()
+    b.close()
