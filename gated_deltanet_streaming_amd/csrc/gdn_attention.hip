@@ -37,7 +37,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int KT = 64;                 // keys per tile
 constexpr int QB = 2;                  // 16-query blocks per wavefront
-constexpr int NWAVE = 8;               // wavefronts per workgroup
+constexpr int NWAVE = 7;               // wavefronts per workgroup (224 queries: 240 workgroups at the
+                                       // 720p layer, one per CU, against 220 with 8)
 constexpr int NTHR = NWAVE * 64;
 constexpr int QT = NWAVE * QB * 16;    // queries per workgroup
 constexpr int VT_STRIDE = KT * 2 + 16; // bytes per d-row of the transposed V tile
