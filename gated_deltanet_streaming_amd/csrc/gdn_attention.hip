@@ -45,7 +45,10 @@ constexpr int VT_STRIDE = KT * 2 + 16; // bytes per d-row of the transposed V ti
 
 template <int D>
 struct Tile {
-    static constexpr int KS = (D * 2) % 128 == 0 ? D * 2 + 16 : D * 2;  // bytes per K row
+    // bytes per K row: 16 more than a row, so that the 16 rows a 16-lane group of a 16-byte
+    // read touches fall on 16 different 16-byte bank groups (with 224-byte rows, rows r and
+    // r + 8 shared banks)
+    static constexpr int KS = D * 2 + 16;
     static constexpr int K_BYTES = KT * KS;
     static constexpr int V_BYTES = D * VT_STRIDE;
     static constexpr int BUF = K_BYTES + V_BYTES;
