@@ -9,9 +9,11 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -29,13 +31,13 @@ struct gdn_stream {
     bool chunked_ok;      // chunked kernels exist for this shape and dtype
     float* state;         // [B, H, d_v, d_k]
     int64_t state_elems;
-    char* ws;             // chunked workspace: [2 directions][B][H][nsub_max] items, then the
-                          // K / Q fragment area
+    char* ws;             // chunked workspace: [2 directions][B][H][nsub_max] items
     __bf16* conv;         // fp32 I/O with the chunked kernels: bf16 staging of q, k, v
     int64_t item_bytes;
     int nsub_max;
-    int64_t items_total;  // bytes of the items (the fragment area follows)
-    int ntile_max;
+    int64_t items_total;  // bytes of the items
+    int* err;             // error word in pinned host memory: a kernel wait gave up
+    int spin_limit;       // polls before a wait gives up
     float* bwd_ws;        // backward workspace (states, partial sums), allocated on first use
     // optional per-kernel timing
     bool profile;
@@ -77,6 +79,16 @@ int fail(int code, const char* fmt, ...) {
 
 int ok() {
     g_err.clear();
+    return GDN_OK;
+}
+
+// A wait inside an earlier call's kernels gave up: its outputs are not valid.  Reported once.
+int check_err_word(gdn_stream* s) {
+    if (s->err && __atomic_load_n(s->err, __ATOMIC_ACQUIRE) != 0) {
+        __atomic_store_n(s->err, 0, __ATOMIC_RELEASE);
+        return fail(GDN_E_HIP, "a wait inside an earlier call's kernels gave up (spin limit %d): that call's "
+                               "outputs and state are not valid", s->spin_limit);
+    }
     return GDN_OK;
 }
 
@@ -125,6 +137,7 @@ int check_tensor(const char* name, const void* ptr, const int64_t* st, int esz, 
 int check_call(gdn_stream* s, const gdn_io* io, int64_t T, uint32_t flags, const void* o_rev, bool need_rev) {
     if (!s) return fail(GDN_E_INVAL, "handle is NULL");
     if (!io) return fail(GDN_E_INVAL, "io is NULL");
+    if (check_err_word(s) != GDN_OK) return GDN_E_HIP;
     if (flags & ~(uint32_t)(GDN_NO_COMMIT | GDN_SEQUENTIAL)) return fail(GDN_E_INVAL, "unknown flag bits 0x%x", flags);
     if (T < 0 || T > s->cfg.max_tokens)
         return fail(GDN_E_SHAPE, "T = %lld outside [0, max_tokens = %lld]", (long long)T, (long long)s->cfg.max_tokens);
@@ -178,8 +191,9 @@ gdn::Params base_params(gdn_stream* s, const gdn_io* io, int64_t T) {
     p.nsub_max = s->nsub_max;
     p.C = s->C;
     p.conv = s->conv;
-    p.frag = s->ws ? s->ws + s->items_total : nullptr;
-    p.ntile_max = s->ntile_max;
+    p.gate_log = (s->cfg.flags & GDN_GATE_IS_LOG) != 0;
+    p.spin_limit = s->spin_limit;
+    p.err = s->err;
     return p;
 }
 
@@ -254,7 +268,8 @@ GDN_API int gdn_stream_init(const gdn_config* cfg, int device, gdn_stream** out)
     const int C = c.subchunk == 0 ? 64 : c.subchunk;
     if (!(C == 16 || C == 32 || C == 64)) return fail(GDN_E_SHAPE, "subchunk %d not in {0, 16, 32, 64}", c.subchunk);
     if (c.io_dtype != GDN_BF16 && c.io_dtype != GDN_F32) return fail(GDN_E_DTYPE, "unknown io_dtype %d", c.io_dtype);
-    if (c.flags & ~(uint32_t)GDN_L2NORM_QK) return fail(GDN_E_INVAL, "unknown config flag bits 0x%x", c.flags);
+    if (c.flags & ~(uint32_t)(GDN_L2NORM_QK | GDN_GATE_IS_LOG | GDN_POISON_WS))
+        return fail(GDN_E_INVAL, "unknown config flag bits 0x%x", c.flags);
     if (!std::isfinite(c.l2_eps) || c.l2_eps < 0.f) return fail(GDN_E_INVAL, "l2_eps must be finite and >= 0");
     if (!std::isfinite(c.scale)) return fail(GDN_E_INVAL, "scale must be finite");
 
@@ -289,25 +304,42 @@ GDN_API int gdn_stream_init(const gdn_config* cfg, int device, gdn_stream** out)
     s->item_bytes = 0;
     s->nsub_max = 0;
     s->items_total = 0;
-    s->ntile_max = 0;
+    s->err = nullptr;
+    s->spin_limit = 1 << 22;
+    if (const char* sl = std::getenv("GDN_SPIN_LIMIT")) {
+        const long v = std::strtol(sl, nullptr, 10);
+        if (v >= 1 && v <= INT_MAX) s->spin_limit = (int)v;
+    }
+    if (e == hipSuccess) {
+        e = hipHostMalloc(reinterpret_cast<void**>(&s->err), sizeof(int), hipHostMallocCoherent | hipHostMallocMapped);
+        if (e != hipSuccess) {
+            s->err = nullptr;
+            (void)hipFree(s->state);
+            delete s;
+            return fail(GDN_E_NOMEM, "error word allocation: %s", hipGetErrorString(e));
+        }
+        *s->err = 0;
+    }
     if (e == hipSuccess && s->chunked_ok) {
         s->item_bytes = gdn::chunk_item_bytes(C, c.d_k);
         s->nsub_max = (int)((c.max_tokens + C - 1) / C);
-        s->ntile_max = (int)((c.max_tokens + 15) / 16);
         s->items_total = 2 * (int64_t)c.batch * c.heads * s->nsub_max * s->item_bytes;
-        const int64_t bytes = s->items_total + gdn::chunk_frag_bytes(c.d_k, c.max_tokens, c.batch, c.heads);
+        const int64_t bytes = s->items_total;
         e = hipMalloc(&s->ws, bytes);
         if (e != hipSuccess) {
             (void)hipFree(s->state);
+            (void)hipHostFree(s->err);
             delete s;
             return fail(GDN_E_NOMEM, "workspace allocation (%lld bytes): %s", (long long)bytes, hipGetErrorString(e));
         }
+        if (c.flags & GDN_POISON_WS) e = hipMemset(s->ws, 0xff, bytes);
         if (c.io_dtype == GDN_F32) {
             const int64_t cb = 3 * (int64_t)c.batch * c.max_tokens * c.heads * c.d_k * 2;
             e = hipMalloc(&s->conv, cb);
             if (e != hipSuccess) {
                 (void)hipFree(s->state);
                 (void)hipFree(s->ws);
+                (void)hipHostFree(s->err);
                 delete s;
                 return fail(GDN_E_NOMEM, "bf16 staging allocation (%lld bytes): %s", (long long)cb,
                             hipGetErrorString(e));
@@ -319,6 +351,7 @@ GDN_API int gdn_stream_init(const gdn_config* cfg, int device, gdn_stream** out)
         (void)hipFree(s->state);
         if (s->ws) (void)hipFree(s->ws);
         if (s->conv) (void)hipFree(s->conv);
+        if (s->err) (void)hipHostFree(s->err);
         delete s;
         return fail(GDN_E_HIP, "init: %s", hipGetErrorString(e));
     }
@@ -342,6 +375,7 @@ GDN_API int gdn_stream_destroy(gdn_stream* s) {
     if (s->ws) (void)hipFree(s->ws);
     if (s->conv) (void)hipFree(s->conv);
     if (s->bwd_ws) (void)hipFree(s->bwd_ws);
+    if (s->err) (void)hipHostFree(s->err);
     delete s;
     if (e != hipSuccess) return fail(GDN_E_HIP, "destroy: %s", hipGetErrorString(e));
     return ok();
@@ -418,6 +452,7 @@ GDN_API int gdn_chunk_bidir(gdn_stream* s, const gdn_io* io, void* o_rev, int64_
 
 GDN_API int gdn_state_get(gdn_stream* s, float* dst, void* hip_stream) {
     if (!s || !dst) return fail(GDN_E_INVAL, "handle and dst must be non-NULL");
+    if (check_err_word(s) != GDN_OK) return GDN_E_HIP;
     DeviceGuard dg(s->device);
     hipError_t e = hipMemcpyAsync(dst, s->state, s->state_elems * sizeof(float), hipMemcpyDeviceToDevice,
                                   reinterpret_cast<hipStream_t>(hip_stream));
@@ -427,6 +462,7 @@ GDN_API int gdn_state_get(gdn_stream* s, float* dst, void* hip_stream) {
 
 GDN_API int gdn_state_set(gdn_stream* s, const float* src, void* hip_stream) {
     if (!s) return fail(GDN_E_INVAL, "handle is NULL");
+    if (check_err_word(s) != GDN_OK) return GDN_E_HIP;
     DeviceGuard dg(s->device);
     hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
     hipError_t e = src ? hipMemcpyAsync(s->state, src, s->state_elems * sizeof(float), hipMemcpyDeviceToDevice, st)
@@ -461,6 +497,7 @@ GDN_API int gdn_chunk_backward(gdn_stream* s, const gdn_io* io, const gdn_grad* 
     if (!s) return fail(GDN_E_INVAL, "handle is NULL");
     if (!io) return fail(GDN_E_INVAL, "io is NULL");
     if (!g) return fail(GDN_E_INVAL, "grad is NULL");
+    if (check_err_word(s) != GDN_OK) return GDN_E_HIP;
     if (reverse != 0 && reverse != 1) return fail(GDN_E_INVAL, "reverse must be 0 or 1");
     if (reverse && g->state0) return fail(GDN_E_INVAL, "the reverse scan starts from zero: state0 must be NULL");
     if (T < 0 || T > s->cfg.max_tokens)

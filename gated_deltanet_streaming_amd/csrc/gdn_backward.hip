@@ -117,7 +117,7 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g)
 #pragma unroll
             for (int i = 0; i < MAXC; ++i) { kv[i] *= rk; qv[i] *= rq; }
         }
-        at = p.a[gq];
+        at = p.gate_log ? expf(p.a[gq]) : p.a[gq];
         bt = p.beta[gq];
         vr = ld_elem<F32>(p.v, vq + row);
     };
@@ -276,7 +276,9 @@ __global__ __launch_bounds__(64) void gdn_bwd_reduce_kernel(Params p, BwdParams 
         }
     }
     if (lane == 0) {
-        g.da[out] = da;
+        // with a given as log a, dL/d(log a) = a dL/da
+        const int64_t gq = (int64_t)b * p.gs[0] + t * p.gs[1] + (int64_t)h * p.gs[2];
+        g.da[out] = p.gate_log ? da * expf(p.a[gq]) : da;
         g.dbeta[out] = db;
     }
 }

@@ -33,16 +33,13 @@ struct Params {
     int nsub_max;
     int C;                 // sub-chunk length
     __bf16* conv;          // fp32 I/O only: bf16 copies of q, k, v ([3][B][T][H][D])
-    // K and Q rows as MFMA operand fragments, by 16-token tile in token order (shared by
-    // both directions): [2 (K, Q)][B][H][ntile_max][(D/16 + 1)/2 k-steps][64 lanes][16 B]
-    char* frag;
-    int ntile_max;
+    int gate_log;          // a holds log a_t instead of a_t
+    int spin_limit;        // polls before a wavefront gives up waiting for another
+    int* err;              // error word (host memory): set to 1 when a wait gives up
 };
 
 // Bytes of one workspace item for sub-chunk C (multiple of 16, 16..64).
 int64_t chunk_item_bytes(int C, int D);
-// Bytes of the fragment area for B streams, H heads and up to max_tokens tokens.
-int64_t chunk_frag_bytes(int D, int64_t max_tokens, int B, int H);
 
 // Gradient of one token-sequential scan (fp32).  Workspace (owned by the handle):
 // states [B][H][Dv/16][T+1][16][Dk] and partial sums [B][T][H][Dv/16][2 Dk + 2].

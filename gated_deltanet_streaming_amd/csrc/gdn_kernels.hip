@@ -126,40 +126,22 @@ __host__ __device__ constexpr int dperm(int m, int j) {
     return (m < (ND & ~1)) ? 32 * (m >> 1) + 8 * (j >> 2) + 4 * (m & 1) + (j & 3) : 16 * m + j;
 }
 
-// workspace item of one processing step: [E fragments: TOTAL blocks][Z^T fragments:
-// ND x NKT blocks][scalars: c1, c2 (C floats each), gamma_C], 1 KB per fragment
-// block (64 lanes x 16 bytes)
-template <int NB, int ND>
-__host__ __device__ constexpr int64_t item_bytes_t() {
-    constexpr int NKT = Blocks<NB>::NFULL + (Blocks<NB>::HALF ? 1 : 0);
-    int64_t b = 1024 * (int64_t)(Blocks<NB>::TOTAL + ND * NKT) + 4 * (2 * 16 * NB + 4);
-    return (b + 255) / 256 * 256;
-}
-
+// workspace item of one processing step (written by the prep, read by the scan): [T~ fragments:
+// TOTAL blocks][A^T fragments: TOTAL blocks][scalars c1[C], w[C], c2[C], gamma_C], 1 KB per
+// fragment block (64 lanes x 16 bytes), the scalars in a 1 KB block of their own
 template <int NB>
-static int64_t item_bytes_d(int D) {
-    switch (D) {
-        case 16: return item_bytes_t<NB, 1>();
-        case 32: return item_bytes_t<NB, 2>();
-        case 64: return item_bytes_t<NB, 4>();
-        case 112: return item_bytes_t<NB, 7>();
-        case 128: return item_bytes_t<NB, 8>();
-        default: return -1;
-    }
+__host__ __device__ constexpr int64_t item_bytes_t() {
+    return 1024 * (int64_t)(2 * Blocks<NB>::TOTAL + 1);
 }
 
 int64_t chunk_item_bytes(int C, int D) {
+    if (!(D == 16 || D == 32 || D == 64 || D == 112 || D == 128)) return -1;
     switch (C) {
-        case 16: return item_bytes_d<1>(D);
-        case 32: return item_bytes_d<2>(D);
-        case 64: return item_bytes_d<4>(D);
+        case 16: return item_bytes_t<1>();
+        case 32: return item_bytes_t<2>();
+        case 64: return item_bytes_t<4>();
         default: return -1;
     }
-}
-
-int64_t chunk_frag_bytes(int D, int64_t max_tokens, int B, int H) {
-    const int64_t nkd = (D / 16 + 1) / 2;
-    return 2 * (int64_t)B * H * ((max_tokens + 15) / 16) * nkd * 1024;
 }
 
 // ---------------------------------------------------------------------------
@@ -243,7 +225,7 @@ __global__ __launch_bounds__(64) void gdn_seq_kernel(Params p) {
             sk += kv[i] * kv[i];
             sq += qv[i] * qv[i];
         }
-        const float at = p.a[gq], bt = p.beta[gq];
+        const float at = p.gate_log ? expf(p.a[gq]) : p.a[gq], bt = p.beta[gq];
         const float vr = ld_elem<F32>(p.v, vq + row);
         if (p.l2norm) {
             const float rk = 1.f / sqrtf(sum4(sk) + p.eps);
@@ -296,19 +278,6 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// K and Q operand fragments by 16-token tile (token order).  Block (tile, ks) holds, for
-// lane r + 16 g, row 16 tile + r at d = 32 ks + 8 g .. +7 (16 bytes); a trailing single
-// tile of d (odd D/16) holds d = 16 (ND-1) + 4 g .. +3 and 8 zero bytes.  Processing tile mt
-// of step n is token tile frag_tile(); the reverse direction takes the tile's rows in
-// reverse order (processing row r is the tile's row 15 - r).
-__device__ __forceinline__ int frag_tile(int dir, int N, int NB, int n, int mt) {
-    return dir ? N * NB - 1 - NB * n - mt : NB * n + mt;
-}
-// fragments of (kind 0 = K / 1 = Q, b, h): base and bytes of the tiles that hold tokens
-__device__ __forceinline__ const char* frag_base(const Params& p, int kind, int b, int h, int nkd) {
-    return p.frag + (((int64_t)kind * p.B + b) * p.H + h) * p.ntile_max * nkd * 1024;
-}
-
 // Compact LDS storage of the C x C matrices of a step by 16x16 blocks: only the
 // blocks on one side of the diagonal are kept (rows padded to 16-byte multiples).
 template <int NB>
@@ -350,13 +319,12 @@ struct LowerF16 {   // fp16 blocks (a, b) with a >= b (A), rows of 16 halves; th
 // log a along p and gamma = e^g:
 //   L[t,s] = beta_t e^{g_t-g_s} k^_t.k^_s (s < t),   T = (I + L)^{-1}
 //   A[t,s] = scale e^{g_t-g_s} q^_t.k^_s (s <= t)
-//   E = A T diag(beta)                  (output:  O = diag(c2) Q S^T + E R)
-//   Z = diag(beta) T^T diag(e^{g_C-g}/|k|) K  (state: S^T <- gamma_C S^T + Z^T R)
-// with R = V - diag(c1) K S^T, c1 = gamma/|k|, c2 = scale gamma/|q|.  (The gate
-// beta is folded into E and Z, so the serial scan needs one scale per token.)
+// and it stores, per direction and step, the step operators the scan needs:
+//   T~ = T diag(beta)       (the UT transform: U = T~ R for the step's R)
+//   A                        (the decay-masked in-step attention: O += A U)
+//   c1 = gamma/|k|, w = e^{g_C-g}/|k|, c2 = scale gamma/|q|, gamma_C.
 // L, A and T are held in fp16 (T is built in fp32 arithmetic from fp16 blocks);
-// E and Z^T are stored as fp16 MFMA fragments for the scan, the state dimension
-// d of Z^T in the scan's state order (see dperm).
+// T~ and A leave as fp16 MFMA fragments, the scalars in fp32.
 // ---------------------------------------------------------------------------
 template <int NB, int ND>
 __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) void gdn_prep_kernel(Params p) {
@@ -369,7 +337,6 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
     constexpr int NT = 64 * NW;
     constexpr int CH = D / 8;    // 16-byte chunks per row
     using BK = Blocks<NB>;
-    constexpr int NKT = BK::NFULL + (BK::HALF ? 1 : 0);
     typedef short s16x4 __attribute__((ext_vector_type(4)));
 
     // K and Q rows (bf16, D per row, token order).  Row t holds its 16-byte chunk c at position
@@ -380,7 +347,6 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
     // reads two-way conflicted).  The Q rows are dead after the Gram products; T^T of both
     // directions then takes their storage.
     constexpr int CHF = 4 * (ND / 2);   // chunks of the 32-wide k-steps
-    auto kq_full = [](int t, int d) { return t * D + (((d >> 3) ^ ((t >> 2) & 3)) << 3) + (d & 7); };   // d < 8 CHF
     auto kq_tail = [](int t, int d) { return t * D + (((d >> 3) ^ ((t >> 3) & 1)) << 3) + (d & 7); };   // d >= 8 CHF
     auto kq = [](int t, int d) {
         const int c = d >> 3, sw = c < CHF ? ((t >> 2) & 3) : ((t >> 3) & 1);
@@ -394,15 +360,19 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
     __shared__ __align__(16) float sg[2][C];          // by token: forward, reverse inclusive log2-gate prefix
     __shared__ __align__(16) float rk[C], rq[C];      // by token: 1/|k|, 1/|q|
     __shared__ __align__(16) float bp[2][C];          // beta by processing row (forward = token order)
-    __shared__ __align__(16) f16 w16[2][C];           // e^{g_C-g}/|k| by processing row
-    __shared__ int jobctr;                            // next E/Z job
     bf16* Qs = reinterpret_cast<bf16*>(QT);
 
     // the wavefront index is uniform: in a scalar register, so that everything derived from
     // it (tile and job assignment, addresses) is scalar work
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, r = lane & 15;
-    const int j = blockIdx.x, bh = blockIdx.y;
+    // XCD-aware order: workgroup id % 8 is the XCD it runs on; the blocks of stream-head bh run
+    // on XCD bh % 8, where the scan workgroups of both directions of that head run, so that the
+    // items land in the L2 they are read from
+    const int nsub = (int)((p.T + C - 1) / C);
+    const int xcd = blockIdx.x & 7, kk = blockIdx.x >> 3;
+    const int j = kk % nsub, bh = xcd + 8 * (kk / nsub);
+    if (bh >= p.B * p.H) return;
     const int b = bh / p.H, h = bh - b * p.H;
     const int T = (int)p.T;
     const int N = (T + C - 1) / C;
@@ -449,10 +419,9 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
             }
         }
         if (tid < C) {
-            sg[0][tid] = gv ? fmaxf(logf(av), GDN_MIN_LOG_DECAY) : 0.f;   // log a until the prefix
+            sg[0][tid] = gv ? fmaxf(p.gate_log ? av : logf(av), GDN_MIN_LOG_DECAY) : 0.f;   // log a until the prefix
             bp[0][tid] = bt;
         }
-        if (tid == 0) jobctr = 0;
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
             const int idx = tid + i * NT;
@@ -481,7 +450,10 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
             }
         }
         ss = sum4(ss);
-        if (part == 0) (isk ? rk : rq)[t] = p.l2norm ? 1.f / sqrtf(ss + p.eps) : 1.f;
+        // rows past the end of the sequence (zero k and q) get zero scales: nothing of them
+        // reaches a product, whatever eps is
+        const bool tv = j * C + t < T;
+        if (part == 0) (isk ? rk : rq)[t] = !tv ? 0.f : p.l2norm ? 1.f / sqrtf(ss + p.eps) : 1.f;
     }
     // inclusive prefixes of log a within the block (C <= 64: one wavefront), in base-2 units
     // (every decay below is an exp2 of a difference of these): forward over tokens <= t,
@@ -497,9 +469,9 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
     }
     lds_barrier();
 
-    // per direction and processing row: beta, e^{g_C-g}/|k|, and the step's scalars c1 (token
-    // order), c2 (token 16 mt + r at r * NB + mt: one vector load per lane of the scan's output
-    // wavefront) and gamma_C
+    // per direction and processing row: beta, and the step's scalars c1 = gamma/|k| and
+    // w = e^{g_C-g}/|k| (processing order), c2 = scale gamma/|q| (token 16 mt + r at r * NB + mt:
+    // one vector load per lane of the scan's output wavefront) and gamma_C
     if (tid < 2 * C) {
         const int dir = tid / C, pr = tid - dir * C;
         if (active(dir)) {
@@ -507,11 +479,11 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
             const float g2 = sg[dir][t], gtot = sg[0][C - 1];
             const float gam = __builtin_amdgcn_exp2f(g2);
             if (dir) bp[1][pr] = bp[0][t];
-            w16[dir][pr] = (f16)(__builtin_amdgcn_exp2f(gtot - g2) * rk[t]);
-            float* scw = reinterpret_cast<float*>(item_of(dir) + 1024 * (BK::TOTAL + ND * NKT));
+            float* scw = reinterpret_cast<float*>(item_of(dir) + 1024 * 2 * BK::TOTAL);
             scw[pr] = gam * rk[t];
-            scw[C + (pr & 15) * NB + (pr >> 4)] = p.scale * gam * rq[t];
-            if (pr == 0) scw[2 * C] = __builtin_amdgcn_exp2f(gtot);
+            scw[C + pr] = __builtin_amdgcn_exp2f(gtot - g2) * rk[t];
+            scw[2 * C + (pr & 15) * NB + (pr >> 4)] = p.scale * gam * rq[t];
+            if (pr == 0) scw[3 * C] = __builtin_amdgcn_exp2f(gtot);
         }
     }
 
@@ -613,27 +585,6 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
             }
         }
     }
-    // the K and Q operand fragments of the block's token tiles (shared by both directions)
-    {
-        constexpr int NKD = (ND + 1) / 2, NKF = ND / 2;
-        const int ntile = (T + 15) / 16;
-        char* const fragb[2] = {const_cast<char*>(frag_base(p, 0, b, h, NKD)) + (int64_t)NB * j * NKD * 1024,
-                                const_cast<char*>(frag_base(p, 1, b, h, NKD)) + (int64_t)NB * j * NKD * 1024};
-        for (int job = w; job < 2 * NB * NKD; job += NW) {
-            const int kind = job / (NB * NKD), mt = (job / NKD) % NB, ks = job % NKD;
-            if (NB * j + mt >= ntile) continue;
-            const bf16* rows = kind ? Qs : Ks;
-            const int rr = 16 * mt + r;
-            uint4 v;
-            if (ks < NKF) {
-                v = *reinterpret_cast<const uint4*>(rows + kq_full(rr, 32 * ks + 8 * g));
-            } else {
-                const uint2 hv = *reinterpret_cast<const uint2*>(rows + kq_tail(rr, 16 * (ND - 1) + 4 * g));
-                v = uint4{hv.x, hv.y, 0u, 0u};
-            }
-            gstore16(fragb[kind] + (mt * NKD + ks) * 1024 + 16 * lane, v);
-        }
-    }
     lds_barrier();
 
     // T = (I + L)^{-1} per direction, built transposed in processing order.  16x16 diagonal
@@ -668,18 +619,6 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
                 for (int e = 0; e < 8; ++e) v8[e] = (f16)x[8 * i8 + e];
                 *reinterpret_cast<f16x8*>(T16 + US::at(o + jc, o + 8 * i8)) = v8;
             }
-        }
-    } else {
-        // the other wavefronts turn the K rows into fp16 in place (the operand form Z takes;
-        // exact for |k| entries in fp16's normal range)
-        for (int idx = tid - 2 * C; idx < C * CH; idx += NT - 2 * C) {
-            const int t = idx / CH, c = idx - t * CH;
-            uint4* pp = reinterpret_cast<uint4*>(Ks + kq(t, 8 * c));
-            const bf16x8 xv = __builtin_bit_cast(bf16x8, *pp);
-            f16x8 hv;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) hv[e] = (f16)(float)xv[e];
-            *pp = __builtin_bit_cast(uint4, hv);
         }
     }
     lds_barrier();
@@ -758,147 +697,50 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
     }
     lds_barrier();
 
-    // E and Z per direction, as independent jobs that the wavefronts take in turn from an LDS
-    // counter (the longer Z jobs first, then the E blocks of the lower rows first)
-    constexpr int MG = NW / NKT > 0 ? NW / NKT : 1;     // groups of d tiles in a Z job
-    constexpr int MPG = (ND + MG - 1) / MG;             // d tiles per group
-    constexpr int NEJ = BK::TOTAL, NZJ = NKT * MG;
-    // E block -> (row tile, 32-wide step)
-    struct EBlocks { int mt[NEJ], ks[NEJ]; };
-    constexpr EBlocks eblk = [] {
-        EBlocks e{};
-        int k = 0;
-        for (int m = 0; m < NB; ++m)
-            for (int s2 = 0; s2 < BK::count(m); ++s2) { e.mt[k] = m; e.ks[k] = s2; ++k; }
-        return e;
-    }();
-    const int dsh = p.ndirs - 1;   // 0 or 1: job index -> direction by a shift, not a division
-    const int nz = NZJ << dsh;
-    for (;;) {
-        int q = 0;
-        if (lane == 0) q = atomicAdd(&jobctr, 1);
-        q = __builtin_amdgcn_readfirstlane(q);
-        if (q >= ((NEJ + NZJ) << dsh)) break;
-        const int dir = dlo + ((q < nz ? q : q - nz) & dsh);
-        const int jj = q < nz ? NEJ + (q >> dsh) : NEJ - 1 - ((q - nz) >> dsh);
-        const f16* T16 = reinterpret_cast<const f16*>(QT) + dir * US::HALVES;
-        const f16* Am = LA + dir * LB::HALVES;
-        // the item: BK::TOTAL E blocks, then ND x NKT Z blocks (1 KB each)
-        char* const itm = item_of(dir);
-        if (jj < NEJ) {
-            // E^T = T^T A^T, tile (ut, tt) = sum_s T^T[u][s] A[t][s] over s in [16 ut, 16 tt + 16);
-            // the output tiles (2ks, mt) and (2ks + 1, mt) form the O-product A fragment (mt, ks).
-            const int blk = jj;
-            const int mt = eblk.mt[blk], ks = eblk.ks[blk];
-            f32x4 et[2];
+    // T~ = T diag(beta) (A operand of U = T~ R) and A^T (B operand of O^T += U^T A^T) of each
+    // direction as fp16 MFMA fragments.  Fragment (mt, ks) holds in lane r + 16 g row (T~) or
+    // column (A^T) t = 16 mt + r and the k-slots e = 0..7 of group g, s = 32 ks + 16 (e / 4) +
+    // 4 g + e % 4: the slot order of MFMA output tiles, so that the scan's U tiles meet them
+    // without a shuffle.  Blocks of s past the diagonal block of t (or past C) are zero.
+    {
+        constexpr int NF = BK::TOTAL;
+        struct FBlocks { int mt[NF], ks[NF]; };
+        constexpr FBlocks fb = [] {
+            FBlocks e{};
+            int k = 0;
+            for (int m = 0; m < NB; ++m)
+                for (int s2 = 0; s2 < BK::count(m); ++s2) { e.mt[k] = m; e.ks[k] = s2; ++k; }
+            return e;
+        }();
+        for (int job = w; job < 4 * NF; job += NW) {
+            const int dir = job / (2 * NF), kind = (job / NF) & 1, f = job - (job / NF) * NF;
+            if (!active(dir)) continue;
+            const int mt = fb.mt[f], ks = fb.ks[f];
+            const f16* T16 = reinterpret_cast<const f16*>(QT) + dir * US::HALVES;
+            const f16* Am = LA + dir * LB::HALVES;
+            f16x8 v;
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const int ut = 2 * ks + hh;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                if (ut <= mt) {
-                    // contraction over s in 32-wide steps (zero outside the triangle)
-                    for (int ss = (16 * ut) / 32; ss * 32 < 16 * (mt + 1); ++ss) {
-                        f16x8 ao, bo;
-                        const int sb = 2 * ss + (g >> 1);   // 16-wide block of this lane's s
-                        if (32 * ss + 8 * g < C && sb >= ut && sb <= mt) {
-                            ao = *reinterpret_cast<const f16x8*>(T16 + US::at(16 * ut + r, 32 * ss + 8 * g));
-                            bo = *reinterpret_cast<const f16x8*>(Am + LB::at(16 * mt + r, 32 * ss + 8 * g));
-                        } else {
+            for (int hf = 0; hf < 2; ++hf) {
+                const int sb = 2 * ks + hf;   // 16-block of s
+                f16x4 x = {(f16)0.f, (f16)0.f, (f16)0.f, (f16)0.f};
+                if (sb <= mt) {
+                    if (kind == 0) {
+                        // T[t][s] for s = 16 sb + 4 g + i: column t of T^T, rows s (transposing read;
+                        // lane r of the group supplies row 16 sb + 4 g + r/4, columns 16 mt + 4 (r%4) ..)
+                        const s16x4 tv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) s16x4*)(T16 + US::at(16 * sb + 4 * g + (r >> 2), 16 * mt + 4 * (r & 3))));
+                        const f16x4 th = __builtin_bit_cast(f16x4, tv);
+                        const f32x4 bs = *reinterpret_cast<const f32x4*>(&bp[dir][16 * sb + 4 * g]);
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) ao[e] = bo[e] = (f16)0.f;
-                        }
-                        acc = mma_f16_k32(ao, bo, acc);
-                    }
-                }
-                // column beta_u of T diag(beta): rows u = 16 ut + 4 g + i of this E^T tile
-                const f32x4 bu = (ut < NB) ? *reinterpret_cast<const f32x4*>(&bp[dir][16 * ut + 4 * g])
-                                           : f32x4{0.f, 0.f, 0.f, 0.f};
-                et[hh] = acc * bu;
-            }
-            f16x8 fr;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                fr[e] = (f16)et[0][e];
-                fr[4 + e] = (f16)et[1][e];
-            }
-            gstore16(itm + blk * 1024 + 16 * lane, __builtin_bit_cast(uint4, fr));
-        } else {
-            // Z = diag(beta) T^T diag(w) K on fp16 MFMA, w = e^{g_C-g}/|k|: A operand T[s][t] w_s
-            // (row t, k = s in slots 16 (i/4) + 4 g + i%4 of each 32-wide step), B operand the fp16 K
-            // rows read transposed (token row of processing row s; column r of tile m is state
-            // index dperm(m, r)).  A job takes the row tiles mt = 2 ks, 2 ks + 1 and a group of d
-            // tiles; output tiles (2ks, m) and (2ks + 1, m) form the state-update fragment
-            // (m, ks), written whole.
-            const int zj = jj - NEJ, mg = zj % MG, ks = zj / MG;
-            // K (fp16) read transposed: lane r of group g supplies processing row t + 4 g + r/4 at
-            // state indices dperm(m, 4 (r%4)) .. +3.  Its address is kq(mrow(dir, row), d): the
-            // row part is a lane constant plus a scalar step (a multiple of 16 rows), so the chunk
-            // permutation of the row ((row >> 2) & 3, and bit 3 for a trailing step) depends on
-            // the lane only.
-            const int u = 4 * g + (r >> 2);
-            const int xs = dir ? 1 - ((u >> 3) & 1) : ((u >> 3) & 1);
-            const int s4 = dir ? 3 - g : g;   // ((row >> 2) & 3) of token row mrow(dir, 16 k + u)
-            const int kl = (dir ? C - 1 - u : u) * D;
-            const int rstep = dir ? -D : D;
-            const int cb = 8 * ((r & 3) ^ s4), cbs = 8 * (((r & 3) >> 1) ^ xs) + 4 * (r & 1);
-            auto kaddr = [&](int trow, int m) {
-                const int col = (m < (ND & ~1)) ? 32 * (m >> 1) + 4 * (m & 1) + cb : 16 * m + cbs;
-                return Ks + kl + trow * rstep + col;
-            };
-            f32x4 acc[2][MPG];
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                for (int mi = 0; mi < MPG; ++mi) acc[hh][mi] = f32x4{0.f, 0.f, 0.f, 0.f};
-            for (int ss = ks; ss < NKT; ++ss) {
-                f16x8 aw[2];
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int mt = 2 * ks + hh;
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        const int s0 = 32 * ss + 16 * hf + 4 * g;
-                        f16x4 tv = {(f16)0.f, (f16)0.f, (f16)0.f, (f16)0.f};
-                        if (mt < NB && s0 < C && 2 * ss + hf >= mt) {   // T[s][t] = 0 for s < t
-                            tv = *reinterpret_cast<const f16x4*>(T16 + US::at(16 * mt + r, s0));
-                            tv = tv * *reinterpret_cast<const f16x4*>(&w16[dir][s0]);
-                        }
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) aw[hh][4 * hf + e] = tv[e];
+                        for (int i = 0; i < 4; ++i) x[i] = (f16)((float)th[i] * bs[i]);
+                    } else {
+                        x = *reinterpret_cast<const f16x4*>(Am + LB::at(16 * mt + r, 16 * sb + 4 * g));
                     }
                 }
 #pragma unroll
-                for (int mi = 0; mi < MPG; ++mi) {
-                    const int m = mg * MPG + mi;
-                    if (m < ND) {
-                        s16x4 lo = {0, 0, 0, 0}, hi4 = {0, 0, 0, 0};
-                        if (32 * ss < C)
-                            lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)kaddr(32 * ss, m));
-                        if (32 * ss + 16 < C)
-                            hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)kaddr(32 * ss + 16, m));
-                        const f16x4 lh = __builtin_bit_cast(f16x4, lo), hh4 = __builtin_bit_cast(f16x4, hi4);
-                        const f16x8 bh16 = {lh[0], lh[1], lh[2], lh[3], hh4[0], hh4[1], hh4[2], hh4[3]};
-#pragma unroll
-                        for (int hh = 0; hh < 2; ++hh)
-                            if (2 * ks + hh < NB) acc[hh][mi] = mma_f16_k32(aw[hh], bh16, acc[hh][mi]);
-                    }
-                }
+                for (int i = 0; i < 4; ++i) v[4 * hf + i] = x[i];
             }
-            f32x4 bt4[2];
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const int mt = 2 * ks + hh;
-                bt4[hh] = (mt < NB) ? *reinterpret_cast<const f32x4*>(&bp[dir][16 * mt + 4 * g]) : f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-#pragma unroll
-            for (int mi = 0; mi < MPG; ++mi) {
-                const int m = mg * MPG + mi;
-                if (m < ND) {
-                    const f32x4 z0 = acc[0][mi] * bt4[0], z1 = acc[1][mi] * bt4[1];
-                    const f16x8 fr = {(f16)z0[0], (f16)z0[1], (f16)z0[2], (f16)z0[3], (f16)z1[0], (f16)z1[1], (f16)z1[2], (f16)z1[3]};
-                    gstore16(itm + (BK::TOTAL + m * NKT + ks) * 1024 + 16 * lane, __builtin_bit_cast(uint4, fr));
-                }
-            }
+            gstore16(item_of(dir) + (kind * NF + f) * 1024 + 16 * lane, __builtin_bit_cast(uint4, v));
         }
     }
 }
@@ -906,21 +748,25 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
 // ---------------------------------------------------------------------------
 // Chunk scan: one workgroup per (direction, b, h, slice of 32 state rows),
 // serial over the processing steps.  Rows of S evolve independently, so the
-// slices of a head need no exchange.  Six wavefronts with fixed roles:
-//   chain (2, one per 16-row column tile of the slice): per step X = K S^T,
-//                     R = V - diag(c1) X; the step's state (bf16) and R (fp16)
-//                     go to an LDS ring, then S^T <- gamma_C S^T + Z^T R.  The
+// slices of a head need no exchange.  Per step n with state S (its slice):
+//   X = K S^T,  R = V - diag(c1) X,  U = T~ R            (U: the step's u_t rows)
+//   O = diag(c2) Q S^T + A U,        S^T <- gamma_C S^T + K^T diag(w) U
+// Six wavefronts with fixed roles:
+//   chain (2, one per 16-row column tile of the slice): the recurrence; the
 //                     state tile lives in MFMA accumulators for the whole call.
-//   output (2, one per half of the step's token tiles): O^T = S Q^T diag(c2) +
-//                     R^T E^T from the ring and their own Q, E and c2 (loaded
-//                     two steps ahead); bf16 tiles leave through LDS staging.
-//   loader (2): deposit each step's K, scalars (loader 0) and Z, V (loader 1)
-//                     in a 3-slot operand ring, loaded into registers two steps
-//                     before.
+//                     Each step's state (bf16) and U (fp16) go to an LDS ring.
+//   output (2, one per half of the step's token tiles): O from the ring, the
+//                     step's Q rows, and A and c2 (loaded two steps ahead);
+//                     bf16 tiles leave through LDS staging.
+//   loader (2): copy each step's operands from memory straight into a 3-slot
+//                     operand ring (loads that write LDS, no registers):
+//                     loader 0 the K rows, the V slice, T~ and the scalars,
+//                     loader 1 the Q rows.
 // The wavefronts are coupled only through the rings and LDS counters with
-// bounded spins: the output wavefronts may trail the chain by up to
-// ring_slots() - 1 steps, the loaders run ahead of it by up to two slots.  An
-// operand register of an MFMA is refilled only after a result depending on
+// bounded spins.  K and Q rows are stored in processing order with the chunk
+// permutation of the prep (conflict-free 16-byte row reads and transposing
+// 8-byte reads); the loaders realise it by the source address each lane loads.
+// An operand register of an MFMA is refilled only after a result depending on
 // that MFMA has been consumed.
 //
 // Row addressing: the buffer resource of a step starts at the lowest token of
@@ -930,24 +776,68 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
 // multiple of 32) are computed from zero inputs and never stored.
 // ---------------------------------------------------------------------------
 #define GDN_COLS 2       // 16-row column tiles of the state per workgroup
-// output ring slots
-template <int ND>
-__host__ __device__ constexpr int ring_slots() { return 3; }
-#define GDN_OPS 3         // operand ring slots
-#define GDN_STAGES 2      // register stages of each loader (its loads run up to GDN_STAGES steps ahead of the ring)
-#define GDN_SPIN_LIMIT (1 << 22)
+#define GDN_OPS 3        // operand ring slots
+#define GDN_RING 2       // output ring slots
 
-template <int NT, int ND>
-struct Rows {                    // NT row tiles of Q (lane = row) as MFMA operands
-    uint4 op[NT][(ND + 1) / 2];  // [tile][ks]: 8 consecutive d; a trailing single tile holds 4 and zeros
+template <int NB, int ND>
+struct ScanGeom {
+    static constexpr int C = 16 * NB, D = 16 * ND;
+    static constexpr int CH = 2 * ND;                        // 16-byte chunks of a K or Q row
+    static constexpr int CHF = 4 * (ND / 2);                 // chunks of the 32-wide k-steps
+    static constexpr int NKD = (ND + 1) / 2, NKF = ND / 2;   // k-steps over d (the last half for odd ND)
+    using BK = Blocks<NB>;
+    static constexpr int NKT = BK::NFULL + (BK::HALF ? 1 : 0);   // 32-wide k-steps over tokens
+    static constexpr int NF = BK::TOTAL;                     // T~ (A) fragments of a step
+    static constexpr int NLK = (C * CH + 63) / 64;           // loads of one block of K (Q) rows
+    static constexpr int NLV = (C * 4 + 63) / 64;            // loads of one V slice
+    static constexpr int ITEM_SC = 2 * NF * 1024;            // scalars in an item: c1[C], w[C], c2[C], gamma_C
+    static constexpr int NOUT = NB >= 2 ? 2 : 1;             // output wavefronts
+    static constexpr int TPO = NB / NOUT;                    // token tiles per output wavefront
+    static constexpr int THREADS = 64 * (GDN_COLS + NOUT + 2);
+    static constexpr int NLD0 = NLK + NLV + NF + 1;          // loads per step, loader 0
+    static constexpr int NLD1 = NLK;                         // loads per step, loader 1
+    // byte offset of (row t, state index d) in a block of K or Q rows: chunk c of row t sits at
+    // c ^ sw(t, c) (the prep's permutation)
+    __host__ __device__ static constexpr int sw(int t, int c) { return c < CHF ? ((t >> 2) & 3) : ((t >> 3) & 1); }
+    __host__ __device__ static constexpr int kq(int t, int d) {
+        return t * 2 * D + 16 * ((d >> 3) ^ sw(t, d >> 3)) + 2 * (d & 7);
+    }
 };
 
-template <int NB>
-struct VIn {                     // chain operands of one step used right after X
-    uint4 v[GDN_COLS][2];        // V row of one token, columns row0 + 16c .. +15 (bf16)
-    f32x4 c1[NB];
-    float gC;
+// One step's operands in LDS (16-byte aligned areas; K, Q and V rounded up to whole loads).
+template <int NB, int ND>
+struct ScanSlot {
+    using G = ScanGeom<NB, ND>;
+    uint4 k[G::NLK][64];        // K rows
+    uint4 q[G::NLK][64];        // Q rows
+    uint4 v[G::NLV][64];        // V slice: token t's 64 bytes at 64 t, chunk j at j ^ vswz(t)
+    uint4 tt[G::NF][64];        // T~ fragments
+    uint4 sc[64];               // c1[C], w[C], c2[C] (lane-major), gamma_C
 };
+
+template <int NB, int ND>
+struct ScanLds {
+    using G = ScanGeom<NB, ND>;
+    ScanSlot<NB, ND> ops[GDN_OPS];
+    uint4 ringS[GDN_RING][G::NKD][GDN_COLS][64];   // state slice, bf16 A-operand fragments of S Q^T
+    uint4 ringU[GDN_RING][G::NKT][GDN_COLS][64];   // U, fp16 A-operand fragments of U^T A^T
+    uint4 ostage[G::NOUT][G::TPO][64];             // bf16 output tiles on their way out
+};
+
+// Progress counters of the scan's wavefronts (an LDS object of their own).
+struct ScanCtr {
+    int ready[GDN_COLS];   // steps each chain wavefront has published to the output ring
+    int cdone[GDN_COLS];   // steps each chain wavefront has finished reading from the operand ring
+    int rdone[2];          // steps each output wavefront has taken from the output ring
+    int odone[2];          // steps each output wavefront has finished reading from the operand ring
+    int loaded[2];         // steps whose operands loader 0 / loader 1 has landed
+};
+
+// A token's 64-byte slice (32 state rows, bf16) in LDS holds its 16-byte chunk j at position
+// j ^ vswz(t): tokens 4 apart land on different banks for the chain's transposing reads
+// and the output tiles' writes, while each lane quad moves one token's 64 contiguous bytes.
+__device__ __forceinline__ int vswz(int t) { return 2 * ((t >> 2) & 1); }
+__device__ __forceinline__ int oswz(int t) { return (t >> 2) & 3; }
 
 // Buffer resource over the rows of processing step n: base at the step's lowest
 // token, num_records ending after the last real token.
@@ -964,75 +854,28 @@ struct StepRows {
     __device__ __forceinline__ int row(int t) const { return (dir ? (C - 1 - t) : t) * (int)tstride; }
 };
 
-// Wait until an LDS counter written by another wavefront reaches `target`.
-// Bounded, so a wavefront can never hang here.  The poll does not sleep between
-// reads: a hand-off is seen one LDS round trip after it happens (with a 64-cycle
-// sleep per poll the scan measured 0.6 us slower per 720p call).
-__device__ __forceinline__ void wait_counter(int* cnt, int target) {
-    for (int it = 0; it < GDN_SPIN_LIMIT; ++it) {
+// Wait until an LDS counter written by another wavefront reaches `target`.  Bounded, so a
+// wavefront can never hang here: after `limit` polls it records the give-up in the error word
+// (host memory the library reads on the handle's next call) and goes on.  The chain wavefronts
+// poll without sleeping (a hand-off is seen one LDS round trip after it happens); the others
+// sleep ~64 cycles between polls, so that their polls do not take LDS issue slots from a chain
+// wavefront on the same SIMD.
+template <bool SLEEP>
+__device__ __forceinline__ void wait_counter(int* cnt, int target, int limit, int* err) {
+    int it = 0;
+    for (; it < limit; ++it) {
         if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+        if constexpr (SLEEP) __builtin_amdgcn_s_sleep(1);
     }
+    if (it == limit && err) __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
-// Set a counter once this wavefront's earlier LDS writes (or reads) are done.  The LDS
-// performs the operations of one wavefront in the order they were issued, so a counter
-// store issued after them is seen by another wavefront only once they have taken effect:
-// the store needs to stay behind them in the instruction stream (an instruction of its own
-// with a memory clobber), not to wait for them.
+// Set a counter once this wavefront's earlier LDS reads and writes have taken effect.  The LDS
+// performs the operations of one wavefront in the order they were issued, so a counter store
+// issued after them is seen by another wavefront only once they are done: the store needs to
+// stay behind them in the instruction stream (an instruction of its own with a memory
+// clobber), not to wait for them.
 __device__ __forceinline__ void signal_counter(int* cnt, int value) {
-    const unsigned addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) int*)cnt;
-    asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(value) : "memory");
-}
-
-template <int NB>
-struct ScanShape {
-    static constexpr int NOUT = NB >= 2 ? 2 : 1;   // output wavefronts
-    static constexpr int TPO = NB / NOUT;          // token tiles per output wavefront
-    static constexpr int THREADS = 64 * (GDN_COLS + NOUT + 2);   // + chain wavefronts + two loaders
-};
-
-// One step's chain operands as the loader wavefronts deposit them (lane l's 16 bytes of a
-// block at byte 16 l), so each block is one MFMA operand fragment read back with one
-// 16-byte LDS read.
-template <int NB, int ND>
-struct ScanOps {
-    static constexpr int NKD = (ND + 1) / 2;   // 32-wide k-steps over d (the last half-filled for odd ND)
-    static constexpr int NKT = Blocks<NB>::NFULL + (Blocks<NB>::HALF ? 1 : 0);
-    uint4 k[NB][NKD][64];                // K fragments of processing tile mt (as stored by the prep)
-    uint4 z[ND][NKT][64];                // state-update fragments of the item
-    uint4 v[NB][64];                     // V row slices, [token][4 chunks of 16 bytes] (see vslot)
-    uint4 sc[64];                        // lanes 0..15: c1 (64 floats); lane 16: gamma_C
-};
-
-template <int NB, int ND>
-struct ScanLds {
-    static constexpr int NKD = (ND + 1) / 2;
-    static constexpr int NKT = Blocks<NB>::NFULL + (Blocks<NB>::HALF ? 1 : 0);
-    uint4 ringP[ring_slots<ND>()][NKD][GDN_COLS][64];
-    uint4 ringR[ring_slots<ND>()][NKT][GDN_COLS][64];
-    ScanOps<NB, ND> ops[GDN_OPS];
-    uint4 ostage[ScanShape<NB>::NOUT][ScanShape<NB>::TPO][64];   // bf16 output tiles on their way out
-};
-
-// A token's 64-byte slice (32 state rows, bf16) in LDS holds its 16-byte chunk j at position
-// j ^ vswz(t): tokens 4 apart land on different banks for the chain's transposing reads
-// and the output tiles' writes, while each lane quad moves one token's 64 contiguous bytes.
-__device__ __forceinline__ int vswz(int t) { return 2 * ((t >> 2) & 1); }
-__device__ __forceinline__ int oswz(int t) { return (t >> 2) & 3; }
-
-// Progress counters of the scan's wavefronts (an LDS object of their own).
-template <int NB>
-struct ScanCtr {
-    int ready[GDN_COLS];                 // steps each chain wavefront has published to the output
-                                         // ring (and so finished reading from the operand slots)
-    int done[ScanShape<NB>::NOUT];       // steps each output wavefront has taken from the ring
-    int loaded[2];                       // steps whose operands loader 0 / loader 1 has landed
-};
-
-// Store a progress counter to LDS as an instruction of its own: it takes effect after the
-// wavefront's earlier LDS stores (one wavefront's LDS operations complete in issue order),
-// and the memory clobber keeps the compiler from moving those stores past it.
-__device__ __forceinline__ void publish_loaded(int* cnt, int value) {
     const unsigned addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) int*)cnt;
     asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(value) : "memory");
 }
@@ -1042,36 +885,34 @@ __device__ __forceinline__ void wait_vmcnt() {
     static_assert(V >= 0 && V < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((V & 15) | (7 << 4) | (15 << 8) | ((V >> 4) << 14));
 }
+// 16 bytes per lane from a buffer resource straight into LDS: lane l's bytes land at dst + 16 l
+// (dst wave-uniform).  Loads past the resource's end write zeros.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, void* dst, int voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
+}
 
 // Output wavefront `O`: token tiles out_tile(O, 0 .. TPO-1) of every step.  With two tiles each,
-// wavefront O takes tiles O and NB-1-O, so both carry the same number of E blocks (a tile's
-// E blocks grow with its distance from the start of the step).
+// wavefront O takes tiles O and NB-1-O, so both carry the same number of A fragments (a tile's
+// fragments grow with its distance from the start of the step).
 template <int NB>
 __host__ __device__ constexpr int out_tile(int O, int tt) {
-    return ScanShape<NB>::TPO == 2 ? (tt == 0 ? O : NB - 1 - O) : O * ScanShape<NB>::TPO + tt;
+    return ScanGeom<NB, 1>::TPO == 2 ? (tt == 0 ? O : NB - 1 - O) : O * ScanGeom<NB, 1>::TPO + tt;
 }
+
 template <int NB, int ND, int O>
-__device__ __forceinline__ void scan_output(const Params& p, ScanLds<NB, ND>& L, ScanCtr<NB>& K, int lane, int b, int h, int dir, int T,
+__device__ __forceinline__ void scan_output(const Params& p, ScanLds<NB, ND>& L, ScanCtr& K, int lane, int b, int h, int dir, int T,
                                             int N, int row0, const char* item0, int64_t ib) {
-    constexpr int C = 16 * NB, D = 16 * ND;
-    constexpr int NKD = (ND + 1) / 2;
+    using G = ScanGeom<NB, ND>;
+    constexpr int C = G::C, D = G::D, NKD = G::NKD, NKF = G::NKF, NKT = G::NKT, NF = G::NF, TPO = G::TPO;
     using BK = Blocks<NB>;
-    constexpr int NKT = BK::NFULL + (BK::HALF ? 1 : 0);
-    constexpr int TPO = ScanShape<NB>::TPO;
-    // E blocks of this wavefront's tiles, tile after tile
-    constexpr auto eoff = [](int tt) { int o = 0; for (int t2 = 0; t2 < tt; ++t2) o += BK::count(out_tile<NB>(O, t2)); return o; };
-    constexpr int EB = eoff(TPO);
-    constexpr int SCAL_OFF = 1024 * (BK::TOTAL + ND * NKT);
     const int r = lane & 15, g = lane >> 4;
+    // A fragments of this wavefront's tiles, tile after tile
+    constexpr auto aoff = [](int tt) { int o = 0; for (int t2 = 0; t2 < tt; ++t2) o += BK::count(out_tile<NB>(O, t2)); return o; };
+    constexpr int AB = aoff(TPO);
     struct OutIn {
-        Rows<TPO, ND> q;
-        uint4 efr[EB];
+        uint4 afr[AB];
         float c2[TPO];
     };
-
-    // Q fragments (16 bytes per lane, the rows of a tile reversed for the reverse direction)
-    const auto qfr = make_rsrc(frag_base(p, 1, b, h, NKD), (uint32_t)(((T + 15) / 16) * NKD * 1024));
-    const int qfl = 16 * ((dir ? 15 - r : r) + 16 * g);
     // o is bf16, or fp32 when the call's I/O is fp32 (its q, k, v were staged as bf16)
     const int oesz = p.io_f32 ? 4 : 2;
     const StepRows orow{reinterpret_cast<const char*>(p.o[dir]) + ((int64_t)b * p.os[0] + (int64_t)h * p.os[2]) * oesz,
@@ -1089,48 +930,51 @@ __device__ __forceinline__ void scan_output(const Params& p, ScanLds<NB, ND>& L,
     bool col_ok[GDN_COLS];
 #pragma unroll
     for (int c = 0; c < GDN_COLS; ++c) col_ok[c] = row0 + 16 * c < p.Dv;
+    // Q operand reads: row 16 tile + r, state indices 32 ks + 8 g .. (a trailing 16-wide step:
+    // 16 (ND-1) + 4 g .., 8 bytes)
+    int qoff[TPO][NKD];
+#pragma unroll
+    for (int tt = 0; tt < TPO; ++tt)
+#pragma unroll
+        for (int ks = 0; ks < NKD; ++ks)
+            qoff[tt][ks] = ks < NKF ? G::kq(16 * out_tile<NB>(O, tt) + r, 32 * ks + 8 * g)
+                                    : G::kq(16 * out_tile<NB>(O, tt) + r, 32 * NKF + 4 * g);
 
     OutIn oA, oB;
     const auto irs = make_rsrc(item0, (uint32_t)(N * ib));
     auto load_out = [&](OutIn& o, int n) {
-#pragma unroll
-        for (int tt = 0; tt < TPO; ++tt) {
-            const int tile = frag_tile(dir, N, NB, n, out_tile<NB>(O, tt));   // past the last token: zero
-#pragma unroll
-            for (int ks = 0; ks < NKD; ++ks)
-                o.q.op[tt][ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(qfr, qfl, (tile * NKD + ks) * 1024, 0));
-        }
         const int ioff = n * (int)ib;
 #pragma unroll
         for (int tt = 0; tt < TPO; ++tt)
 #pragma unroll
             for (int kt = 0; kt < BK::count(out_tile<NB>(O, tt)); ++kt)
-                o.efr[eoff(tt) + kt] = __builtin_bit_cast(
-                    uint4, __builtin_amdgcn_raw_buffer_load_b128(irs, 16 * lane, ioff + 1024 * (BK::offset(out_tile<NB>(O, tt)) + kt), 0));
+                o.afr[aoff(tt) + kt] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(irs, 16 * lane, ioff + 1024 * (NF + BK::offset(out_tile<NB>(O, tt)) + kt), 0));
         // c2 of tokens 16 mt + r of this wavefront's tiles mt (lane-major scalars)
 #pragma unroll
         for (int tt = 0; tt < TPO; ++tt)
             o.c2[tt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(irs, 4 * (NB * r + out_tile<NB>(O, tt)),
-                                                                                      ioff + SCAL_OFF + 4 * C, 0));
+                                                                                      ioff + G::ITEM_SC + 8 * C, 0));
     };
 
     load_out(oA, 0);
     load_out(oB, N > 1 ? 1 : 0);
     auto out_step = [&](OutIn& o, int n) {
-        const int sl = n % ring_slots<ND>();
+        const int sl = n % GDN_RING;
+        const ScanSlot<NB, ND>& op = L.ops[n % GDN_OPS];
 #pragma unroll
-        for (int c = 0; c < GDN_COLS; ++c) wait_counter(&K.ready[c], n + 1);
+        for (int c = 0; c < GDN_COLS; ++c) wait_counter<true>(&K.ready[c], n + 1, p.spin_limit, p.err);
         bf16x8 Pb[NKD][GDN_COLS];
-        f16x8 Rb[NKT][GDN_COLS];
+        f16x8 Ub[NKT][GDN_COLS];
 #pragma unroll
         for (int ks = 0; ks < NKD; ++ks)
 #pragma unroll
-            for (int c = 0; c < GDN_COLS; ++c) Pb[ks][c] = __builtin_bit_cast(bf16x8, L.ringP[sl][ks][c][lane]);
+            for (int c = 0; c < GDN_COLS; ++c) Pb[ks][c] = __builtin_bit_cast(bf16x8, L.ringS[sl][ks][c][lane]);
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-            for (int c = 0; c < GDN_COLS; ++c) Rb[kt][c] = __builtin_bit_cast(f16x8, L.ringR[sl][kt][c][lane]);
-        // the slot is free once its fragments are in registers
+            for (int c = 0; c < GDN_COLS; ++c) Ub[kt][c] = __builtin_bit_cast(f16x8, L.ringU[sl][kt][c][lane]);
+        // the ring slot is free once its fragments are in registers
 #pragma unroll
         for (int ks = 0; ks < NKD; ++ks)
 #pragma unroll
@@ -1138,8 +982,29 @@ __device__ __forceinline__ void scan_output(const Params& p, ScanLds<NB, ND>& L,
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-            for (int c = 0; c < GDN_COLS; ++c) keep_alive(Rb[kt][c]);
-        signal_counter(&K.done[O], n + 1);
+            for (int c = 0; c < GDN_COLS; ++c) keep_alive(Ub[kt][c]);
+        signal_counter(&K.rdone[O], n + 1);
+        // the step's Q rows
+        wait_counter<true>(&K.loaded[1], n + 1, p.spin_limit, p.err);
+        bf16x8 Qf[TPO][NKD];
+#pragma unroll
+        for (int tt = 0; tt < TPO; ++tt)
+#pragma unroll
+            for (int ks = 0; ks < NKD; ++ks) {
+                const char* qp = reinterpret_cast<const char*>(&op.q[0][0]) + qoff[tt][ks];
+                if (ks < NKF) {
+                    Qf[tt][ks] = ld_bf16x8(reinterpret_cast<const bf16*>(qp));
+                } else {
+                    const bf16x4 h4 = ld_bf16x4(reinterpret_cast<const bf16*>(qp));
+                    const bf16 z = (bf16)0.f;
+                    Qf[tt][ks] = bf16x8{h4[0], h4[1], h4[2], h4[3], z, z, z, z};
+                }
+            }
+#pragma unroll
+        for (int tt = 0; tt < TPO; ++tt)
+#pragma unroll
+            for (int ks = 0; ks < NKD; ++ks) keep_alive(Qf[tt][ks]);
+        signal_counter(&K.odone[O], n + 1);
         __builtin_amdgcn_sched_barrier(0);
         // Y^T = S Q^T: rows = state rows 16 c + 4 g + i, column = token 16 mt + r
         f32x4 Ot[TPO][GDN_COLS];
@@ -1152,21 +1017,20 @@ __device__ __forceinline__ void scan_output(const Params& p, ScanLds<NB, ND>& L,
 #pragma unroll
             for (int tt = 0; tt < TPO; ++tt)
 #pragma unroll
-                for (int c = 0; c < GDN_COLS; ++c)
-                    Ot[tt][c] = mma_bf16_k32(Pb[ks][c], __builtin_bit_cast(bf16x8, o.q.op[tt][ks]), Ot[tt][c]);
+                for (int c = 0; c < GDN_COLS; ++c) Ot[tt][c] = mma_bf16_k32(Pb[ks][c], Qf[tt][ks], Ot[tt][c]);
 #pragma unroll
         for (int tt = 0; tt < TPO; ++tt)
 #pragma unroll
             for (int c = 0; c < GDN_COLS; ++c) Ot[tt][c] = Ot[tt][c] * o.c2[tt];
-        // + R^T E^T (a trailing 16-token step has zero upper slots in both operands)
+        // + U^T A^T (a trailing 16-token step has zero upper slots in both operands)
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
             for (int tt = 0; tt < TPO; ++tt) {
                 if (kt >= BK::count(out_tile<NB>(O, tt))) continue;
-                const f16x8 ef = __builtin_bit_cast(f16x8, o.efr[eoff(tt) + kt]);
+                const f16x8 af = __builtin_bit_cast(f16x8, o.afr[aoff(tt) + kt]);
 #pragma unroll
-                for (int c = 0; c < GDN_COLS; ++c) Ot[tt][c] = mma_f16_k32(Rb[kt][c], ef, Ot[tt][c]);
+                for (int c = 0; c < GDN_COLS; ++c) Ot[tt][c] = mma_f16_k32(Ub[kt][c], af, Ot[tt][c]);
             }
         uint2 ov[TPO][GDN_COLS];
 #pragma unroll
@@ -1219,155 +1083,124 @@ __device__ __forceinline__ void scan_output(const Params& p, ScanLds<NB, ND>& L,
 }
 
 template <int NB, int ND>
-__global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params p, int ngroups) {
-    constexpr int C = 16 * NB, D = 16 * ND;
-    constexpr int NKD = (ND + 1) / 2;      // k-steps over d (the last one half-filled for odd ND)
-    constexpr int NKF = ND / 2;            // full k-steps over d
+__global__ __launch_bounds__((ScanGeom<NB, ND>::THREADS)) void gdn_scan_kernel(Params p, int ngroups) {
+    using G = ScanGeom<NB, ND>;
+    constexpr int C = G::C, D = G::D;
+    constexpr int NKD = G::NKD, NKF = G::NKF, NKT = G::NKT, NF = G::NF;
     constexpr int NS = (ND + GDN_COLS - 1) / GDN_COLS;   // slices per head
+    constexpr int NOUT = G::NOUT;
     using BK = Blocks<NB>;
-    constexpr int NFT = BK::NFULL;         // 32-wide steps over tokens
-    constexpr bool HT = BK::HALF;
-    constexpr int NKT = NFT + (HT ? 1 : 0);
-    constexpr int SCAL_OFF = 1024 * (BK::TOTAL + ND * NKT);   // scalars of an item
-    constexpr int NOUT = ScanShape<NB>::NOUT;
-    // loads the loader wavefronts issue per step: K and the scales; Z and V
-    constexpr int NDMA0 = NB * NKD + 1;
-    constexpr int NDMA1 = ND * NKT + NB;
     typedef short s16x4 __attribute__((ext_vector_type(4)));
 
     __shared__ __align__(16) ScanLds<NB, ND> L;
-    __shared__ ScanCtr<NB> K;
+    __shared__ ScanCtr K;
 
     const int lane = threadIdx.x & 63;
     // the role of a wavefront is wave-uniform: keep it in a scalar register so every
     // role is a whole-wavefront branch
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, g = lane >> 4;
-    // Workgroups are spread over the 8 XCDs round-robin (id % 8); keep the NS
-    // slices of one (direction, b, h) on one XCD so they share its L2.
+    // Workgroup id % 8 is the XCD it runs on.  Both directions and all NS slices of stream-head
+    // bh run on XCD bh % 8 (with the prep workgroups of that head), so that they share its L2.
     const int id = blockIdx.x, xcd = id & 7, slot = id >> 3;
-    const int group = (slot / NS) * 8 + xcd, j = slot - (slot / NS) * NS;
-    if (group >= ngroups) return;
-    int gg = group;
-    const int h = gg % p.H; gg /= p.H;
-    const int b = gg % p.B; gg /= p.B;
-    const int dir = p.dir0 + gg;
+    const int j = slot % NS, rest = slot / NS;
+    const int bh = xcd + 8 * (rest / p.ndirs);
+    if (bh >= ngroups) return;
+    const int dir = p.dir0 + rest % p.ndirs;
+    const int h = bh % p.H, b = bh / p.H;
     const int T = (int)p.T;
     const int N = (T + C - 1) / C;
     const int row0 = 16 * GDN_COLS * j;
     const char* item0 = p.ws + (((int64_t)dir * p.B + b) * p.H + h) * p.nsub_max * p.ws_item_bytes;
     const int64_t ib = p.ws_item_bytes;
-    bool col_ok[GDN_COLS];
-#pragma unroll
-    for (int c = 0; c < GDN_COLS; ++c) col_ok[c] = row0 + 16 * c < p.Dv;
 
     if (threadIdx.x == 0) {
 #pragma unroll
-        for (int c = 0; c < GDN_COLS; ++c) K.ready[c] = 0;
-#pragma unroll
-        for (int o = 0; o < NOUT; ++o) K.done[o] = 0;
+        for (int c = 0; c < GDN_COLS; ++c) K.ready[c] = K.cdone[c] = 0;
+        K.rdone[0] = K.rdone[1] = K.odone[0] = K.odone[1] = 0;
         K.loaded[0] = K.loaded[1] = 0;
+        // a single output wavefront (C = 16) leaves the second pair of counts open
+        if (NOUT == 1) K.rdone[1] = K.odone[1] = 1 << 30;
     }
     __syncthreads();
 
-    const StepRows vr{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.v) + (int64_t)b * p.vs[0] +
-                                                    (int64_t)h * p.vs[2]),
-                      p.vs[1] * 2, T, C, N, dir, 2 * D};
-    // the items of this (direction, b, h), addressed with lane-constant offsets
-    const auto irs = make_rsrc(item0, (uint32_t)(N * ib));
-
-    // roles: waves 0 .. GDN_COLS-1 chain, then the output wavefronts, then the two
-    // loaders (which share SIMDs with the chain wavefronts and move data without VGPRs)
     if (wave >= GDN_COLS + NOUT) {
         // ------------------------------ loader wavefronts ------------------------------
-        // Deposit the chain's operands of step n in slot n % GDN_OPS once both chain
-        // wavefronts are done with that slot, and publish the step.  The operands are
-        // loaded into registers GDN_STAGES steps before they are deposited, so each step's
-        // loads are in flight while the chain works ~GDN_STAGES + 2 steps behind them.
-        // Loader 0 moves K and the scales, loader 1 the state-update fragments Z and V;
-        // each publishes its own count.
+        // Step m goes to operand slot m % GDN_OPS once every wavefront that reads that part of
+        // the slot is done with step m - GDN_OPS.  Two steps are in flight: the loads of step
+        // m + 1 are issued before those of step m are waited for (the loads of a wavefront
+        // complete in order).
         const int part = wave - (GDN_COLS + NOUT);
-        // K fragments: 16 bytes per lane, the rows of a tile reversed for the reverse direction
-        const auto kfr = make_rsrc(frag_base(p, 0, b, h, NKD), (uint32_t)(((T + 15) / 16) * NKD * 1024));
-        const int kfl = 16 * ((dir ? 15 - r : r) + 16 * g);
-        // V: lane quad l/4 moves token 16 jj + l/4's slice, lane l%4 its chunk at position l%4;
-        // chunks of column tiles past d_v are read from outside the resource (zero)
-        static_assert(GDN_COLS == 2, "V slices are 64 bytes");
-        int voff[NB];
+        const StepRows krow{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.k) + (int64_t)b * p.ks[0] + (int64_t)h * p.ks[2]),
+                            p.ks[1] * 2, T, C, N, dir, 2 * D};
+        const StepRows qrow{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.q) + (int64_t)b * p.qs[0] + (int64_t)h * p.qs[2]),
+                            p.qs[1] * 2, T, C, N, dir, 2 * D};
+        const StepRows vrow{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.v) + (int64_t)b * p.vs[0] + (int64_t)h * p.vs[2]),
+                            p.vs[1] * 2, T, C, N, dir, 2 * D};
+        const StepRows& rows = part == 0 ? krow : qrow;
+        // destination chunk 64 i + lane of a block of rows: row t, position pos; the source chunk
+        // is pos ^ sw(t, pos) (the permutation is an involution within its group of chunks)
+        int roff[G::NLK];
 #pragma unroll
-        for (int jj = 0; jj < NB; ++jj) {
-            const int t = 16 * jj + (lane >> 2), j = (lane & 3) ^ vswz(t);
-            voff[jj] = (row0 + 16 * (j >> 1) < p.Dv) ? vr.row(t) + 2 * row0 + 16 * j : (int)0x80000000;
+        for (int i = 0; i < G::NLK; ++i) {
+            const int pc = 64 * i + lane;
+            const int t = pc < C * G::CH ? pc / G::CH : 0, pos = pc < C * G::CH ? pc - t * G::CH : 0;
+            roff[i] = rows.row(t) + 16 * (pos ^ G::sw(t, pos));
         }
-        const int scoff = lane < 16 ? 16 * lane : (lane == 16 ? 8 * C : 0);
-        static_assert(GDN_STAGES * NDMA0 <= 63 && GDN_STAGES * NDMA1 <= 63, "loads in flight per loader");
-        auto ld16 = [](__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
-            return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0));
-        };
-        // loader 0: K fragments (NB x NKD blocks), then the scalars; loader 1: Z (ND x NKT), then V (NB)
-        auto load0 = [&](uint4* st, int n) {
+        // V slice: token t = p / 4 of the step, chunk position p % 4 holds source chunk
+        // (p % 4) ^ vswz(t); chunks of column tiles past d_v are read from outside the resource
+        int voff[G::NLV];
 #pragma unroll
-            for (int mt = 0; mt < NB; ++mt) {
-                // tiles past the last token read as zero (outside the resource)
-                const int tile = frag_tile(dir, N, NB, n, mt);
+        for (int i = 0; i < G::NLV; ++i) {
+            const int pc = 64 * i + lane, t = pc >> 2, jj = (pc & 3) ^ vswz(t);
+            voff[i] = (row0 + 16 * (jj >> 1) < p.Dv) ? vrow.row(t) + 2 * row0 + 16 * jj : (int)0x80000000;
+        }
+        const auto irs = make_rsrc(item0, (uint32_t)(N * ib));
+        auto issue = [&](int m) {
+            ScanSlot<NB, ND>& op = L.ops[m % GDN_OPS];
+            if (part == 0) {
+                const auto krs = krow.rsrc(m);
 #pragma unroll
-                for (int ks = 0; ks < NKD; ++ks) st[mt * NKD + ks] = ld16(kfr, kfl, (tile * NKD + ks) * 1024);
+                for (int i = 0; i < G::NLK; ++i) lds_load16(krs, &op.k[i][0], roff[i], 0);
+                const auto vrs = vrow.rsrc(m);
+#pragma unroll
+                for (int i = 0; i < G::NLV; ++i) lds_load16(vrs, &op.v[i][0], voff[i], 0);
+#pragma unroll
+                for (int f = 0; f < NF; ++f) lds_load16(irs, &op.tt[f][0], 1024 * f + 16 * lane, m * (int)ib);
+                lds_load16(irs, &op.sc[0], G::ITEM_SC + 16 * lane, m * (int)ib);
+            } else {
+                const auto qrs = qrow.rsrc(m);
+#pragma unroll
+                for (int i = 0; i < G::NLK; ++i) lds_load16(qrs, &op.q[i][0], roff[i], 0);
             }
-            st[NB * NKD] = ld16(irs, scoff, n * (int)ib + SCAL_OFF);
         };
-        auto put0 = [&](const uint4* st, int n) {
-            ScanOps<NB, ND>& op = L.ops[n % GDN_OPS];
+        auto slot_free = [&](int m) {   // readers done with step m - GDN_OPS
+            const int need = m + 1 - GDN_OPS;
+            if (need <= 0) return;
+            if (part == 0) {
 #pragma unroll
-            for (int mt = 0; mt < NB; ++mt)
-#pragma unroll
-                for (int ks = 0; ks < NKD; ++ks) op.k[mt][ks][lane] = st[mt * NKD + ks];
-            op.sc[lane] = st[NB * NKD];
-        };
-        auto load1 = [&](uint4* st, int n) {
-            const int ioff = n * (int)ib;
-#pragma unroll
-            for (int m = 0; m < ND; ++m)
-#pragma unroll
-                for (int kt = 0; kt < NKT; ++kt) st[m * NKT + kt] = ld16(irs, 16 * lane, ioff + 1024 * (BK::TOTAL + m * NKT + kt));
-            const auto vrs = vr.rsrc(n);
-#pragma unroll
-            for (int jj = 0; jj < NB; ++jj) st[ND * NKT + jj] = ld16(vrs, voff[jj], 0);
-        };
-        auto put1 = [&](const uint4* st, int n) {
-            ScanOps<NB, ND>& op = L.ops[n % GDN_OPS];
-#pragma unroll
-            for (int m = 0; m < ND; ++m)
-#pragma unroll
-                for (int kt = 0; kt < NKT; ++kt) op.z[m][kt][lane] = st[m * NKT + kt];
-#pragma unroll
-            for (int jj = 0; jj < NB; ++jj) op.v[jj][lane] = st[ND * NKT + jj];
-        };
-        // Per step n: wait for slot n % GDN_OPS, wait for stage n % GDN_STAGES (the loads of the
-        // other stages may still be in flight: the loads of a wavefront complete in order), write
-        // it to the slot, publish, and reload the stage with step n + GDN_STAGES.
-        auto run = [&](auto load, auto put, auto wait_stage) {
-            constexpr int NL = NDMA1 > NDMA0 ? NDMA1 : NDMA0;
-            uint4 st[GDN_STAGES][NL];
-#pragma unroll
-            for (int i = 0; i < GDN_STAGES; ++i) load(st[i], i < N ? i : N - 1);
-            for (int n = 0; n < N; n += GDN_STAGES) {
-#pragma unroll
-                for (int i = 0; i < GDN_STAGES; ++i) {
-                    const int m = n + i;
-                    if (m >= N) break;
-#pragma unroll
-                    for (int c = 0; c < GDN_COLS; ++c) wait_counter(&K.ready[c], m + 1 - GDN_OPS);
-                    wait_stage();
-                    put(st[i], m);
-                    publish_loaded(&K.loaded[part], m + 1);
-                    load(st[i], m + GDN_STAGES < N ? m + GDN_STAGES : N - 1);
-                }
+                for (int c = 0; c < GDN_COLS; ++c) wait_counter<true>(&K.cdone[c], need, p.spin_limit, p.err);
+            } else {
+                wait_counter<true>(&K.odone[0], need, p.spin_limit, p.err);
+                wait_counter<true>(&K.odone[1], need, p.spin_limit, p.err);
             }
-            wait_vmcnt<0>();
         };
-        // the other stages' loads may still be in flight
-        if (part == 0) run(load0, put0, [] { wait_vmcnt<(GDN_STAGES - 1) * NDMA0>(); });
-        else run(load1, put1, [] { wait_vmcnt<(GDN_STAGES - 1) * NDMA1>(); });
+        issue(0);
+        if (N > 1) issue(1);
+        for (int m = 0; m < N; ++m) {
+            if (m + 1 < N) {
+                if (part == 0) wait_vmcnt<G::NLD0>();
+                else wait_vmcnt<G::NLD1>();
+            } else {
+                wait_vmcnt<0>();
+            }
+            signal_counter(&K.loaded[part], m + 1);
+            if (m + 2 < N) {
+                slot_free(m + 2);
+                issue(m + 2);
+            }
+        }
+        wait_vmcnt<0>();
         return;
     }
     if (wave == GDN_COLS) {
@@ -1383,10 +1216,8 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
 
     // ------------------------------ chain wavefronts ------------------------------
     // Chain wavefront cc owns state rows row0 + 16 cc .. +15.  Per step n: wait for the
-    // step's operands; Pb = bf16(S); read K, the scales and Z from the operand slot;
-    // X = K S^T on MFMA while the VALU decays the state and reads V back transposed;
-    // R = V - c1 X; release the slot; publish the state and R to the output ring;
-    // S^T += Z^T R on MFMA.
+    // step's operands and a free output-ring slot; Pb = bf16(S) to the ring; X = K S^T on MFMA;
+    // R = V - c1 X; U = T~ R (fp16 MFMA) to the ring; S^T <- gamma_C S^T + K^T (w U).
     const int cc = wave;
     const bool tile_ok = row0 + 16 * cc < p.Dv;
     f32x4 P[ND];   // P[m][i] = S[row0 + 16 cc + r][dperm(m, 4 g + i)]
@@ -1400,37 +1231,65 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
         else
             P[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-
-    int done_seen[NOUT];
+    // operand read offsets within a slot (bytes):
+    //   K rows for X: row 16 mt + r, state indices 32 ks + 8 g .. (trailing half step: 16 (ND-1) + 4 g ..)
+    //   K^T for the update (transposing 8-byte reads): lane r of group g supplies row
+    //     32 kt + 16 hh + 4 g + r/4 at state indices dperm(m, 4 (r%4)) .. +3, and receives
+    //     column dperm(m, r) at rows 32 kt + 16 hh + 4 g .. +3
+    int kxo[NB][NKD];
 #pragma unroll
-    for (int o = 0; o < NOUT; ++o) done_seen[o] = 0;
-    // K fragments of a step, read one step ahead (while the state update runs); a trailing
-    // half k-step (odd ND) has zero upper slots
-    uint4 kf[NB][NKD];
-    auto read_k = [&](const ScanOps<NB, ND>& op, int dep) {
+    for (int mt = 0; mt < NB; ++mt)
 #pragma unroll
         for (int ks = 0; ks < NKD; ++ks)
-#pragma unroll
-            for (int mt = 0; mt < NB; ++mt) kf[mt][ks] = op.k[mt][ks][lane + dep];
+            kxo[mt][ks] = ks < NKF ? G::kq(16 * mt + r, 32 * ks + 8 * g) : G::kq(16 * mt + r, 32 * NKF + 4 * g);
+    auto kto = [&](int m, int trow) { return G::kq(trow + 4 * g + (r >> 2), dperm<ND>(m, 4 * (r & 3))); };
+    // V read back transposed: lane quad q of group g supplies token 16 mt + 4 g + i (i = r/4), columns
+    // 16 cc + 4 q .. +3 of the slice; lane (r, g) receives state row 16 cc + r at tokens 16 mt + 4 g ..
+    auto vto = [&](int mt) {
+        const int q = r & 3, t = 16 * mt + 4 * g + (r >> 2);
+        return 64 * t + 16 * ((2 * cc + (q >> 1)) ^ vswz(t)) + 8 * (q & 1);
     };
-    wait_counter(&K.loaded[0], 1);
-    wait_counter(&K.loaded[1], 1);
-    read_k(L.ops[0], 0);
+
+    int rdone_seen[2] = {0, 0};
+    // K rows of a step as X operands (read one step ahead, during the previous update)
+    auto read_kf = [&](const char* kb, bf16x8 (&kf)[NB][NKD]) {
+#pragma unroll
+        for (int mt = 0; mt < NB; ++mt)
+#pragma unroll
+            for (int ks = 0; ks < NKD; ++ks) {
+                const bf16* kp = reinterpret_cast<const bf16*>(kb + kxo[mt][ks]);
+                if (ks < NKF) {
+                    kf[mt][ks] = ld_bf16x8(kp);
+                } else {
+                    const bf16x4 h4 = ld_bf16x4(kp);
+                    const bf16 z = (bf16)0.f;
+                    kf[mt][ks] = bf16x8{h4[0], h4[1], h4[2], h4[3], z, z, z, z};
+                }
+            }
+    };
+    bf16x8 kf[NB][NKD];
+    wait_counter<false>(&K.loaded[0], 1, p.spin_limit, p.err);
+    read_kf(reinterpret_cast<const char*>(&L.ops[0].k[0][0]), kf);
+    bf16x8 kT[ND][NKT];
+    bf16x8 Ub[NKT];
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) Ub[kt] = bf16x8{};
+#pragma unroll
+    for (int m = 0; m < ND; ++m)
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) kT[m][kt] = bf16x8{};
 #pragma unroll 1
     for (int n = 0; n < N; ++n) {
-        const int sl = n % ring_slots<ND>();
-        const ScanOps<NB, ND>& op = L.ops[n % GDN_OPS];
-        // the loaders' counts, read now so that they are back before the next step's K is read
-        const int ld0 = __hip_atomic_load(&K.loaded[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        const int ld1 = __hip_atomic_load(&K.loaded[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        const int ldc = ld0 < ld1 ? ld0 : ld1;
-        // the output ring slot of this step must have been released by every output
-        // wavefront (the last counts seen are kept, so the counters are read only when needed)
+        const int sl = n % GDN_RING;
+        const ScanSlot<NB, ND>& op = L.ops[n % GDN_OPS];
+        const char* kb = reinterpret_cast<const char*>(&op.k[0][0]);
+        // the output ring slot of this step must have been released by every output wavefront
+        // (the counts were read early in the previous step; a poll here only when they were short)
 #pragma unroll
-        for (int o = 0; o < NOUT; ++o)
-            if (done_seen[o] < n + 1 - ring_slots<ND>()) {
-                wait_counter(&K.done[o], n + 1 - ring_slots<ND>());
-                done_seen[o] = __hip_atomic_load(&K.done[o], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        for (int o = 0; o < 2; ++o)
+            if (rdone_seen[o] < n + 1 - GDN_RING) {
+                wait_counter<false>(&K.rdone[o], n + 1 - GDN_RING, p.spin_limit, p.err);
+                rdone_seen[o] = n + 1 - GDN_RING;
             }
         // state as bf16 operand: k-slot e of lane group g <-> d = dperm(2 ks + e/4, 4 g + e%4)
         bf16x8 Pb[NKD];
@@ -1448,35 +1307,16 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
                 Pb[NKD - 1][4 + i] = (bf16)0.f;
             }
         }
-        // The Z fragments are read into the registers the previous state update took its
-        // operands from: their LDS addresses depend on Pb (through an empty asm), and Pb
-        // on every result of that update, so the reads issue only once it has finished.
-        int zdep = 0;
-#pragma unroll
-        for (int ks = 0; ks < NKD; ++ks) asm volatile("" : "+v"(zdep) : "v"(Pb[ks]));
-        // publish the state to the output ring right away
-#pragma unroll
-        for (int ks = 0; ks < NKD; ++ks) L.ringP[sl][ks][cc][lane] = __builtin_bit_cast(uint4, Pb[ks]);
-        // the step's remaining operands, in order of use: the scales and V (read back
-        // transposed: lane quad q of group g supplies row 16 mt + 4 g + i, columns
-        // 16 cc + 4 q .. +3 of the deposited rows), then Z.  c1 of the tokens 16 mt + 4 g + i
-        // this lane scales is read once per row of 16 lanes (lane 4 mt + i holds it) and
-        // handed round the row by broadcasts.
-        const float c1l = reinterpret_cast<const float*>(&op.sc[0])[16 * (r >> 2) + 4 * g + (r & 3)];
-        const float gC = reinterpret_cast<const float*>(&op.sc[16])[0];
-        bf16x4 vt[NB];
-#pragma unroll
-        for (int mt = 0; mt < NB; ++mt) {
-            const int q = r & 3, t = 16 * mt + 4 * g + (r >> 2);
-            const char* vp = reinterpret_cast<const char*>(&op.v[0][0]) + 64 * t + 16 * ((2 * cc + (q >> 1)) ^ vswz(t)) + 8 * (q & 1);
-            vt[mt] = __builtin_bit_cast(
-                bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)vp));
-        }
-        uint4 zfr[ND][NKT];
+        // Pb holds the previous update's results: that update's operands may be released now
 #pragma unroll
         for (int m = 0; m < ND; ++m)
 #pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) zfr[m][kt] = op.z[m][kt][lane + zdep];
+            for (int kt = 0; kt < NKT; ++kt) keep_alive(kT[m][kt]);
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) keep_alive(Ub[kt]);
+        // publish the state to the output ring right away
+#pragma unroll
+        for (int ks = 0; ks < NKD; ++ks) L.ringS[sl][ks][cc][lane] = __builtin_bit_cast(uint4, Pb[ks]);
         // X = K S^T (rows: tokens 16 mt + 4 g + i, column: state row 16 cc + r)
         f32x4 X[NB];
 #pragma unroll
@@ -1484,51 +1324,111 @@ __global__ __launch_bounds__(ScanShape<NB>::THREADS) void gdn_scan_kernel(Params
 #pragma unroll
         for (int ks = 0; ks < NKD; ++ks)
 #pragma unroll
-            for (int mt = 0; mt < NB; ++mt) X[mt] = mma_bf16_k32(__builtin_bit_cast(bf16x8, kf[mt][ks]), Pb[ks], X[mt]);
-        // meanwhile: decay the state
+            for (int mt = 0; mt < NB; ++mt) X[mt] = mma_bf16_k32(kf[mt][ks], Pb[ks], X[mt]);
+        // The counters this wavefront waits on next are read now, ahead of the step's other LDS
+        // reads: LDS reads complete in order, so checking a count read after them would wait for
+        // all of them.
+        const int ld_early = __hip_atomic_load(&K.loaded[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        int rd_early[2];
+#pragma unroll
+        for (int o = 0; o < 2; ++o) rd_early[o] = __hip_atomic_load(&K.rdone[o], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __builtin_amdgcn_sched_barrier(0);
+        // meanwhile: the step's other operands -- c1 and w of tokens 16 mt + 4 g .. +3, gamma_C,
+        // V (transposed) and the T~ fragments -- and the decay of the state
+        const float* scf = reinterpret_cast<const float*>(&op.sc[0]);
+        f32x4 c1v[NB], wv[NB];
+#pragma unroll
+        for (int mt = 0; mt < NB; ++mt) {
+            c1v[mt] = *reinterpret_cast<const f32x4*>(scf + 16 * mt + 4 * g);
+            wv[mt] = *reinterpret_cast<const f32x4*>(scf + C + 16 * mt + 4 * g);
+        }
+        const float gC = scf[3 * C];
+        bf16x4 vt[NB];
+#pragma unroll
+        for (int mt = 0; mt < NB; ++mt)
+            vt[mt] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(reinterpret_cast<const char*>(&op.v[0][0]) + vto(mt))));
+        f16x8 tf[NF];
+#pragma unroll
+        for (int f = 0; f < NF; ++f) tf[f] = __builtin_bit_cast(f16x8, op.tt[f][lane]);
 #pragma unroll
         for (int m = 0; m < ND; ++m) P[m] = P[m] * gC;
-        // R = V - diag(e^g / |k|) X, as fp16 B operand (k = token)
-        float c1[16];
-        row_broadcasts(c1l, c1, std::make_integer_sequence<int, 16>{});
+        // R = V - diag(c1) X, as fp16 B operand (k = token, slot order of the output tiles)
         f16x8 Rb[NKT];
 #pragma unroll
         for (int mt = 0; mt < NB; ++mt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Rb[mt >> 1][4 * (mt & 1) + i] = (f16)((float)vt[mt][i] - c1[4 * mt + i] * X[mt][i]);
-        if constexpr (HT) {
+            for (int i = 0; i < 4; ++i) Rb[mt >> 1][4 * (mt & 1) + i] = (f16)((float)vt[mt][i] - c1v[mt][i] * X[mt][i]);
+        if constexpr (BK::HALF) {
 #pragma unroll
-            for (int i = 4; i < 8; ++i) Rb[NFT][i] = (f16)0.f;
+            for (int i = 4; i < 8; ++i) Rb[NKT - 1][i] = (f16)0.f;
         }
+        // X is consumed: its K operands may be released
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) L.ringR[sl][kt][cc][lane] = __builtin_bit_cast(uint4, Rb[kt]);
-        // issue order of the step: the conversions and ring writes of Pb, then each X
-        // MFMA followed by two of the operand reads, then the arithmetic of R
-        __builtin_amdgcn_sched_group_barrier(0x002, 2 * NKD, 0);
-        __builtin_amdgcn_sched_group_barrier(0x200, NKD, 0);
+        for (int mt = 0; mt < NB; ++mt)
 #pragma unroll
-        for (int i = 0; i < NB * NKD; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-        signal_counter(&K.ready[cc], n + 1);
-        // the next step's operands must have landed before its K is read (the addresses of
-        // the reads depend on the count, through an empty asm, so they follow it)
-        if (n + 1 < N) {
-            int kdep = 0;
-            if (ldc < n + 2) {
-                wait_counter(&K.loaded[0], n + 2);
-                wait_counter(&K.loaded[1], n + 2);
+            for (int ks = 0; ks < NKD; ++ks) keep_alive(kf[mt][ks]);
+        // K^T fragments for the update (state index rows, token k-slots)
+#pragma unroll
+        for (int m = 0; m < ND; ++m)
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) {
+                s16x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+                if (32 * kt < C)
+                    lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(kb + kto(m, 32 * kt)));
+                if (32 * kt + 16 < C)
+                    hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(kb + kto(m, 32 * kt + 16)));
+                const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo), h4 = __builtin_bit_cast(bf16x4, hi);
+                kT[m][kt] = bf16x8{l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
             }
-            asm volatile("" : "+v"(kdep) : "v"(ldc));
-            read_k(L.ops[(n + 1) % GDN_OPS], kdep);
+        // U = T~ R (rows: tokens 16 mt + 4 g + i, column: state row 16 cc + r)
+        f32x4 U[NB];
+#pragma unroll
+        for (int mt = 0; mt < NB; ++mt) {
+            U[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kt = 0; kt < BK::count(mt); ++kt) U[mt] = mma_f16_k32(tf[BK::offset(mt) + kt], Rb[kt], U[mt]);
         }
-        // S^T <- gamma_C S^T + Z^T R  (rows d, columns: state rows); a trailing 16-token
+        // U to the output ring (fp16, A operand of U^T A^T) and w U as bf16 B operand of the update
+        f16x8 Uh[NKT];
+#pragma unroll
+        for (int mt = 0; mt < NB; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                Uh[mt >> 1][4 * (mt & 1) + i] = (f16)U[mt][i];
+                Ub[mt >> 1][4 * (mt & 1) + i] = (bf16)(wv[mt][i] * U[mt][i]);
+            }
+        if constexpr (BK::HALF) {
+#pragma unroll
+            for (int i = 4; i < 8; ++i) {
+                Uh[NKT - 1][i] = (f16)0.f;
+                Ub[NKT - 1][i] = (bf16)0.f;
+            }
+        }
+#pragma unroll
+        for (int f = 0; f < NF; ++f) keep_alive(tf[f]);
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) keep_alive(Rb[kt]);
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) L.ringU[sl][kt][cc][lane] = __builtin_bit_cast(uint4, Uh[kt]);
+        signal_counter(&K.ready[cc], n + 1);
+        // the next step's K rows, read while the update runs (into registers of their own: the
+        // update's operands stay live until its results have been read)
+#pragma unroll
+        for (int o = 0; o < 2; ++o) rdone_seen[o] = rd_early[o] > rdone_seen[o] ? rd_early[o] : rdone_seen[o];
+        if (n + 1 < N) {
+            if (ld_early < n + 2) wait_counter<false>(&K.loaded[0], n + 2, p.spin_limit, p.err);
+            read_kf(reinterpret_cast<const char*>(&L.ops[(n + 1) % GDN_OPS].k[0][0]), kf);
+        }
+        // S^T <- gamma_C S^T + K^T (w U)  (rows d, columns: state rows); a trailing 16-token
         // step has zero upper slots in both operands
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-            for (int m = 0; m < ND; ++m) P[m] = mma_f16_k32(__builtin_bit_cast(f16x8, zfr[m][kt]), Rb[kt], P[m]);
+            for (int m = 0; m < ND; ++m) P[m] = mma_bf16_k32(kT[m][kt], Ub[kt], P[m]);
+        // every read of the operand slot of step n has been issued (and, the LDS being in order,
+        // takes effect before this count)
+        signal_counter(&K.cdone[cc], n + 1);
     }
     float* Sout = p.S_out[dir];
     if (Sout && tile_ok) {
@@ -1594,14 +1494,14 @@ template <int NB, int ND>
 static hipError_t run_chunked(const Params& p, hipStream_t s, Timing* tm) {
     const int nsub = (int)((p.T + 16 * NB - 1) / (16 * NB));
     tm_begin(tm, s, KPREP);
-    hipLaunchKernelGGL((gdn_prep_kernel<NB, ND>), dim3(nsub, p.B * p.H), dim3(128 * NB), 0, s, p);
+    hipLaunchKernelGGL((gdn_prep_kernel<NB, ND>), dim3(8 * ((p.B * p.H + 7) / 8) * nsub), dim3(128 * NB), 0, s, p);
     tm_end(tm, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int ngroups = p.ndirs * p.B * p.H;
-    const int grid = (ngroups + 7) / 8 * 8 * ((ND + GDN_COLS - 1) / GDN_COLS);
+    const int ngroups = p.B * p.H;   // stream-heads; each has p.ndirs directions
+    const int grid = (ngroups + 7) / 8 * 8 * p.ndirs * ((ND + GDN_COLS - 1) / GDN_COLS);
     tm_begin(tm, s, KSCAN);
-    hipLaunchKernelGGL((gdn_scan_kernel<NB, ND>), dim3(grid), dim3(ScanShape<NB>::THREADS), 0, s, p, ngroups);
+    hipLaunchKernelGGL((gdn_scan_kernel<NB, ND>), dim3(grid), dim3(ScanGeom<NB, ND>::THREADS), 0, s, p, ngroups);
     tm_end(tm, s);
     return hipGetLastError();
 }

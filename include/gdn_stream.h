@@ -24,6 +24,12 @@
  *  - Return GDN_OK (0) or a negative GDN_E_* code.  On any error nothing has
  *    been enqueued and the cache is unchanged; gdn_last_error() gives a message
  *    (thread-local, valid until the next call from the same thread).
+ *  - The kernels hand work between their wavefronts through bounded waits.  A
+ *    wait that gives up (it never should) marks the handle's error word; the
+ *    next call on the handle then returns GDN_E_HIP without enqueueing anything
+ *    (the outputs of the earlier call are not valid) and clears the mark.  The
+ *    bound is 2^22 polls, or the value of the environment variable
+ *    GDN_SPIN_LIMIT when the handle was created.
  *  - Device pointers are caller-owned, must live on the handle's device, and
  *    are not retained after the call returns.  Work is enqueued asynchronously
  *    on `hip_stream` (a hipStream_t; NULL = the null stream); the caller
@@ -58,7 +64,12 @@ extern "C" {
 #define GDN_F32  1
 
 /* gdn_config.flags */
-#define GDN_L2NORM_QK (1u << 0)   /* normalise q and k per token (default on) */
+#define GDN_L2NORM_QK   (1u << 0) /* normalise q and k per token (default on)     */
+#define GDN_GATE_IS_LOG (1u << 1) /* io->a holds log a_t (<= 0) instead of a_t;
+                                     the gradient da is then dL/d(log a_t)        */
+#define GDN_POISON_WS   (1u << 2) /* debugging: fill the workspace with NaN bytes at
+                                     init, so that a read of a workspace byte the
+                                     kernels did not write shows up in the output */
 
 /* per-call flags */
 #define GDN_NO_COMMIT  (1u << 0)  /* forward: leave the cache unchanged; the final
@@ -79,7 +90,7 @@ typedef struct gdn_config {
                          /* even; a workspace of 3*B*max_tokens*H*d_k*2 bytes   */
                          /* is added at init) and store o in fp32; the          */
                          /* sequential kernel stays in fp32 throughout          */
-    uint32_t flags;      /* GDN_L2NORM_QK                                        */
+    uint32_t flags;      /* GDN_L2NORM_QK | GDN_GATE_IS_LOG | GDN_POISON_WS      */
     float l2_eps;        /* eps inside the L2 norm (1e-6 is the usual value)     */
     float scale;         /* output scale (1.0 when q is unit-norm)               */
 } gdn_config;
@@ -89,7 +100,8 @@ typedef struct gdn_io {
     const void* k;        /* [B, T, H, d_k] io_dtype                           */
     const void* v;        /* [B, T, H, d_v] io_dtype                           */
     void* o;              /* [B, T, H, d_v] io_dtype, written                  */
-    const float* a;       /* [B, T, H] decay a_t in (0, 1]; log-domain inside  */
+    const float* a;       /* [B, T, H] decay a_t in (0, 1] (log a_t with       */
+                          /* GDN_GATE_IS_LOG); log-domain inside, clamped at -80 */
     const float* beta;    /* [B, T, H] write strength beta_t                    */
     int64_t q_strides[3]; /* (b, t, h) strides of q, in elements                */
     int64_t k_strides[3];
