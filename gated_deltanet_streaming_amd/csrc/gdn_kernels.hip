@@ -306,6 +306,15 @@ struct LowerF16 {   // fp16 blocks (a, b) with a >= b (A), rows of 16 halves; th
     }
 };
 
+// Stream-heads bh = b H + h are spread over the 8 XCDs in contiguous ranges (workgroup id % 8 is
+// the XCD a workgroup runs on): XCD x takes bh in [first(x), first(x + 1)), first(x) =
+// ceil(x BH / 8).  Neighbouring heads share the cache lines of a token's row, so a contiguous
+// range reads each line into one L2.  Returns the k-th stream-head of XCD x, or -1.
+__device__ __forceinline__ int xcd_head(int x, int k, int BH) {
+    const int first = (x * BH + 7) / 8, next = ((x + 1) * BH + 7) / 8;
+    return k < next - first ? first + k : -1;
+}
+
 // ---------------------------------------------------------------------------
 // Chunk preparation: one workgroup (2 NB wavefronts) per (b, h, block j of C
 // tokens), for every requested direction at once.  The forward direction
@@ -366,13 +375,13 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
     // it (tile and job assignment, addresses) is scalar work
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, r = lane & 15;
-    // XCD-aware order: workgroup id % 8 is the XCD it runs on; the blocks of stream-head bh run
-    // on XCD bh % 8, where the scan workgroups of both directions of that head run, so that the
-    // items land in the L2 they are read from
+    // XCD-aware order: the blocks of stream-head bh run on its XCD (xcd_head), where the scan
+    // workgroups of both directions of that head run, so that the items land in the L2 they are
+    // read from
     const int nsub = (int)((p.T + C - 1) / C);
     const int xcd = blockIdx.x & 7, kk = blockIdx.x >> 3;
-    const int j = kk % nsub, bh = xcd + 8 * (kk / nsub);
-    if (bh >= p.B * p.H) return;
+    const int j = kk % nsub, bh = xcd_head(xcd, kk / nsub, p.B * p.H);
+    if (bh < 0) return;
     const int b = bh / p.H, h = bh - b * p.H;
     const int T = (int)p.T;
     const int N = (T + C - 1) / C;
@@ -1101,11 +1110,12 @@ __global__ __launch_bounds__((ScanGeom<NB, ND>::THREADS)) void gdn_scan_kernel(P
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, g = lane >> 4;
     // Workgroup id % 8 is the XCD it runs on.  Both directions and all NS slices of stream-head
-    // bh run on XCD bh % 8 (with the prep workgroups of that head), so that they share its L2.
+    // bh run on its XCD (xcd_head, with the prep workgroups of that head), so that they share
+    // its L2.
     const int id = blockIdx.x, xcd = id & 7, slot = id >> 3;
     const int j = slot % NS, rest = slot / NS;
-    const int bh = xcd + 8 * (rest / p.ndirs);
-    if (bh >= ngroups) return;
+    const int bh = xcd_head(xcd, rest / p.ndirs, ngroups);
+    if (bh < 0) return;
     const int dir = p.dir0 + rest % p.ndirs;
     const int h = bh % p.H, b = bh / p.H;
     const int T = (int)p.T;
