@@ -17,6 +17,9 @@ GDN_OK = 0
 GDN_E_INVAL, GDN_E_SHAPE, GDN_E_DTYPE, GDN_E_NOMEM, GDN_E_HIP = -1, -2, -3, -4, -5
 GDN_BF16, GDN_F32 = 0, 1
 GDN_L2NORM_QK = 1 << 0
+GDN_GATE_IS_LOG = 1 << 1
+GDN_POISON_WS = 1 << 2
+GDN_NOALLOC_SCRATCH_BYTES = 64 << 20
 GDN_NO_COMMIT = 1 << 0
 GDN_SEQUENTIAL = 1 << 1
 GDN_KERNEL_PREP, GDN_KERNEL_SCAN, GDN_KERNEL_SEQ, GDN_KERNEL_BWD, GDN_KERNEL_COUNT = 0, 1, 2, 3, 4
@@ -85,6 +88,7 @@ def load_library():
         "gdn_chunk_forward": ([vp, ctypes.POINTER(GdnIo), i64, u32, vp, vp], i32),
         "gdn_chunk_reverse": ([vp, ctypes.POINTER(GdnIo), i64, u32, vp, vp], i32),
         "gdn_chunk_bidir": ([vp, ctypes.POINTER(GdnIo), vp, i64, u32, vp, vp], i32),
+        "gdn_chunk_bidir_noalloc": ([ctypes.POINTER(GdnConfig), ctypes.POINTER(GdnIo), vp, i64, vp, vp, vp, vp], i32),
         "gdn_chunk_backward": ([vp, ctypes.POINTER(GdnIo), ctypes.POINTER(GdnGrad), i64, i32, vp], i32),
         "gdn_state_get": ([vp, vp, vp], i32),
         "gdn_state_set": ([vp, vp, vp], i32),
@@ -153,11 +157,12 @@ def _make_io(q, k, v, o, a, beta):
 
 
 def gdn_stream_init(batch, heads, d_k, d_v, max_tokens, *, subchunk=0, io_dtype=GDN_BF16,
-                    l2norm=True, l2_eps=1e-6, scale=1.0, device=0):
+                    l2norm=True, l2_eps=1e-6, scale=1.0, gate_is_log=False, poison_ws=False, device=0):
     """Create a handle; returns the opaque pointer (int)."""
     lib = load_library()
-    cfg = GdnConfig(batch, heads, d_k, d_v, max_tokens, subchunk, io_dtype,
-                    GDN_L2NORM_QK if l2norm else 0, l2_eps, scale)
+    flags = ((GDN_L2NORM_QK if l2norm else 0) | (GDN_GATE_IS_LOG if gate_is_log else 0)
+             | (GDN_POISON_WS if poison_ws else 0))
+    cfg = GdnConfig(batch, heads, d_k, d_v, max_tokens, subchunk, io_dtype, flags, l2_eps, scale)
     h = ctypes.c_void_p()
     _check(lib.gdn_stream_init(ctypes.byref(cfg), int(device), ctypes.byref(h)))
     return h.value
@@ -185,6 +190,24 @@ def gdn_chunk_bidir(handle, q, k, v, a, beta, o, o_rev, *, flags=0, state_out=No
     io = _make_io(q, k, v, o, a, beta)
     _check(load_library().gdn_chunk_bidir(ctypes.c_void_p(handle), ctypes.byref(io), _ptr(o_rev), q.shape[1],
                                           flags, _ptr(state_out), _stream_ptr(stream, q.device)))
+
+
+def gdn_chunk_bidir_noalloc(q, k, v, a, beta, o, o_rev, status, *, state_in=None, state_out=None, subchunk=0,
+                            l2norm=True, l2_eps=1e-6, scale=1.0, gate_is_log=False, stream=None):
+    """Both scans of one chunk without a handle and without any device allocation: the
+    workspace is the library's static scratch.  ``status`` is an int32 device tensor of one
+    element that the kernels set to 1 if a wait gives up."""
+    if o_rev.stride() != o.stride():
+        raise ValueError("o_rev must have o's strides")
+    if status.dtype.itemsize != 4 or status.numel() < 1:
+        raise ValueError("status must be an int32 tensor")
+    B, T, H, Dk = q.shape
+    flags = (GDN_L2NORM_QK if l2norm else 0) | (GDN_GATE_IS_LOG if gate_is_log else 0)
+    cfg = GdnConfig(B, H, Dk, v.shape[-1], max(T, 1), subchunk, GDN_BF16, flags, l2_eps, scale)
+    io = _make_io(q, k, v, o, a, beta)
+    _check(load_library().gdn_chunk_bidir_noalloc(ctypes.byref(cfg), ctypes.byref(io), _ptr(o_rev), T,
+                                                  _ptr(state_in), _ptr(state_out), _ptr(status),
+                                                  _stream_ptr(stream, q.device)))
 
 
 def gdn_state_get(handle, dst, *, stream=None):
@@ -233,12 +256,13 @@ class Stream:
     """One handle: B streams x H heads of carried state on one device."""
 
     def __init__(self, batch, heads, d_k, d_v, max_tokens, *, subchunk=0, io_dtype="bf16", l2norm=True,
-                 l2_eps=1e-6, scale=1.0, device=0):
+                 l2_eps=1e-6, scale=1.0, gate_is_log=False, poison_ws=False, device=0):
         self.shape = (batch, heads, d_v, d_k)
         self.device = device
         self.handle = gdn_stream_init(batch, heads, d_k, d_v, max_tokens, subchunk=subchunk,
                                       io_dtype=GDN_F32 if io_dtype == "f32" else GDN_BF16, l2norm=l2norm,
-                                      l2_eps=l2_eps, scale=scale, device=device)
+                                      l2_eps=l2_eps, scale=scale, gate_is_log=gate_is_log, poison_ws=poison_ws,
+                                      device=device)
 
     def forward(self, q, k, v, a, beta, o, **kw):
         gdn_chunk_forward(self.handle, q, k, v, a, beta, o, **kw)

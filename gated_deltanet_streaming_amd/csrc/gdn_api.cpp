@@ -134,17 +134,27 @@ int check_tensor(const char* name, const void* ptr, const int64_t* st, int esz, 
     return GDN_OK;
 }
 
-int check_call(gdn_stream* s, const gdn_io* io, int64_t T, uint32_t flags, const void* o_rev, bool need_rev) {
-    if (!s) return fail(GDN_E_INVAL, "handle is NULL");
-    if (!io) return fail(GDN_E_INVAL, "io is NULL");
-    if (check_err_word(s) != GDN_OK) return GDN_E_HIP;
-    if (flags & ~(uint32_t)(GDN_NO_COMMIT | GDN_SEQUENTIAL)) return fail(GDN_E_INVAL, "unknown flag bits 0x%x", flags);
-    if (T < 0 || T > s->cfg.max_tokens)
-        return fail(GDN_E_SHAPE, "T = %lld outside [0, max_tokens = %lld]", (long long)T, (long long)s->cfg.max_tokens);
-    if (T == 0) return GDN_OK;
-    const int esz = elem_size(s->cfg);
+// Validation of a configuration shared by gdn_stream_init and gdn_chunk_bidir_noalloc; on success
+// *C receives the sub-chunk length.
+int check_config(const gdn_config& c, uint32_t allowed_flags, int* C) {
+    if (c.batch < 1 || c.heads < 1) return fail(GDN_E_SHAPE, "batch and heads must be >= 1");
+    if (!is_mult16(c.d_k) || !is_mult16(c.d_v))
+        return fail(GDN_E_SHAPE, "d_k=%d d_v=%d must be multiples of 16 in [16, 128]", c.d_k, c.d_v);
+    if (c.max_tokens < 1) return fail(GDN_E_SHAPE, "max_tokens must be >= 1");
+    *C = c.subchunk == 0 ? 64 : c.subchunk;
+    if (!(*C == 16 || *C == 32 || *C == 64)) return fail(GDN_E_SHAPE, "subchunk %d not in {0, 16, 32, 64}", c.subchunk);
+    if (c.io_dtype != GDN_BF16 && c.io_dtype != GDN_F32) return fail(GDN_E_DTYPE, "unknown io_dtype %d", c.io_dtype);
+    if (c.flags & ~allowed_flags) return fail(GDN_E_INVAL, "unknown config flag bits 0x%x", c.flags & ~allowed_flags);
+    if (!std::isfinite(c.l2_eps) || c.l2_eps < 0.f) return fail(GDN_E_INVAL, "l2_eps must be finite and >= 0");
+    if (!std::isfinite(c.scale)) return fail(GDN_E_INVAL, "scale must be finite");
+    return GDN_OK;
+}
+
+// q, k, v, o (and o_rev when given), a and beta of a call of T > 0 tokens.
+int check_io(const gdn_config& c, const gdn_io* io, int64_t T, const void* o_rev, bool need_rev) {
+    const int esz = elem_size(c);
     int rc;
-    const int dk = s->cfg.d_k, dv = s->cfg.d_v;
+    const int dk = c.d_k, dv = c.d_v;
     if ((rc = check_tensor("q", io->q, io->q_strides, esz, dk, T)) != GDN_OK) return rc;
     if ((rc = check_tensor("k", io->k, io->k_strides, esz, dk, T)) != GDN_OK) return rc;
     if ((rc = check_tensor("v", io->v, io->v_strides, esz, dv, T)) != GDN_OK) return rc;
@@ -154,6 +164,19 @@ int check_call(gdn_stream* s, const gdn_io* io, int64_t T, uint32_t flags, const
     if (!io->beta) return fail(GDN_E_INVAL, "beta is NULL");
     for (int i = 0; i < 3; ++i)
         if (io->g_strides[i] < 0) return fail(GDN_E_INVAL, "gate stride %d is negative", i);
+    return GDN_OK;
+}
+
+int check_call(gdn_stream* s, const gdn_io* io, int64_t T, uint32_t flags, const void* o_rev, bool need_rev) {
+    if (!s) return fail(GDN_E_INVAL, "handle is NULL");
+    if (!io) return fail(GDN_E_INVAL, "io is NULL");
+    if (check_err_word(s) != GDN_OK) return GDN_E_HIP;
+    if (flags & ~(uint32_t)(GDN_NO_COMMIT | GDN_SEQUENTIAL)) return fail(GDN_E_INVAL, "unknown flag bits 0x%x", flags);
+    if (T < 0 || T > s->cfg.max_tokens)
+        return fail(GDN_E_SHAPE, "T = %lld outside [0, max_tokens = %lld]", (long long)T, (long long)s->cfg.max_tokens);
+    if (T == 0) return GDN_OK;
+    const int rc = check_io(s->cfg, io, T, o_rev, need_rev);
+    if (rc != GDN_OK) return rc;
     if (!(flags & GDN_SEQUENTIAL) && !s->chunked_ok)
         return fail(GDN_E_SHAPE,
                     "no chunked kernel for d_k=%d d_v=%d subchunk=%d io_dtype=%d; pass GDN_SEQUENTIAL",
@@ -161,7 +184,8 @@ int check_call(gdn_stream* s, const gdn_io* io, int64_t T, uint32_t flags, const
     return GDN_OK;
 }
 
-gdn::Params base_params(gdn_stream* s, const gdn_io* io, int64_t T) {
+// The parts of a launch's parameters that follow from the configuration and the call.
+gdn::Params call_params(const gdn_config& c, int C, const gdn_io* io, int64_t T) {
     gdn::Params p;
     std::memset(&p, 0, sizeof p);
     p.q = io->q;
@@ -178,23 +202,38 @@ gdn::Params base_params(gdn_stream* s, const gdn_io* io, int64_t T) {
         p.gs[i] = io->g_strides[i];
     }
     p.T = T;
-    p.B = s->cfg.batch;
-    p.H = s->cfg.heads;
-    p.Dk = s->cfg.d_k;
-    p.Dv = s->cfg.d_v;
-    p.io_f32 = s->cfg.io_dtype == GDN_F32;
-    p.l2norm = (s->cfg.flags & GDN_L2NORM_QK) != 0;
-    p.eps = s->cfg.l2_eps;
-    p.scale = s->cfg.scale;
+    p.B = c.batch;
+    p.H = c.heads;
+    p.Dk = c.d_k;
+    p.Dv = c.d_v;
+    p.io_f32 = c.io_dtype == GDN_F32;
+    p.l2norm = (c.flags & GDN_L2NORM_QK) != 0;
+    p.eps = c.l2_eps;
+    p.scale = c.scale;
+    p.C = C;
+    p.gate_log = (c.flags & GDN_GATE_IS_LOG) != 0;
+    return p;
+}
+
+gdn::Params base_params(gdn_stream* s, const gdn_io* io, int64_t T) {
+    gdn::Params p = call_params(s->cfg, s->C, io, T);
     p.ws = s->ws;
     p.ws_item_bytes = s->item_bytes;
     p.nsub_max = s->nsub_max;
-    p.C = s->C;
     p.conv = s->conv;
-    p.gate_log = (s->cfg.flags & GDN_GATE_IS_LOG) != 0;
     p.spin_limit = s->spin_limit;
     p.err = s->err;
     return p;
+}
+
+// Polls before a kernel wait gives up: 2^22, or GDN_SPIN_LIMIT from the environment.
+int env_spin_limit() {
+    int lim = 1 << 22;
+    if (const char* sl = std::getenv("GDN_SPIN_LIMIT")) {
+        const long v = std::strtol(sl, nullptr, 10);
+        if (v >= 1 && v <= INT_MAX) lim = (int)v;
+    }
+    return lim;
 }
 
 // Fold finished timing events into the per-kernel totals.
@@ -261,17 +300,9 @@ GDN_API int gdn_stream_init(const gdn_config* cfg, int device, gdn_stream** out)
     if (!cfg || !out) return fail(GDN_E_INVAL, "cfg and out must be non-NULL");
     *out = nullptr;
     const gdn_config c = *cfg;
-    if (c.batch < 1 || c.heads < 1) return fail(GDN_E_SHAPE, "batch and heads must be >= 1");
-    if (!is_mult16(c.d_k) || !is_mult16(c.d_v))
-        return fail(GDN_E_SHAPE, "d_k=%d d_v=%d must be multiples of 16 in [16, 128]", c.d_k, c.d_v);
-    if (c.max_tokens < 1) return fail(GDN_E_SHAPE, "max_tokens must be >= 1");
-    const int C = c.subchunk == 0 ? 64 : c.subchunk;
-    if (!(C == 16 || C == 32 || C == 64)) return fail(GDN_E_SHAPE, "subchunk %d not in {0, 16, 32, 64}", c.subchunk);
-    if (c.io_dtype != GDN_BF16 && c.io_dtype != GDN_F32) return fail(GDN_E_DTYPE, "unknown io_dtype %d", c.io_dtype);
-    if (c.flags & ~(uint32_t)(GDN_L2NORM_QK | GDN_GATE_IS_LOG | GDN_POISON_WS))
-        return fail(GDN_E_INVAL, "unknown config flag bits 0x%x", c.flags);
-    if (!std::isfinite(c.l2_eps) || c.l2_eps < 0.f) return fail(GDN_E_INVAL, "l2_eps must be finite and >= 0");
-    if (!std::isfinite(c.scale)) return fail(GDN_E_INVAL, "scale must be finite");
+    int C = 0;
+    const int rc = check_config(c, GDN_L2NORM_QK | GDN_GATE_IS_LOG | GDN_POISON_WS, &C);
+    if (rc != GDN_OK) return rc;
 
     int ndev = 0;
     hipError_t e = hipGetDeviceCount(&ndev);
@@ -305,11 +336,7 @@ GDN_API int gdn_stream_init(const gdn_config* cfg, int device, gdn_stream** out)
     s->nsub_max = 0;
     s->items_total = 0;
     s->err = nullptr;
-    s->spin_limit = 1 << 22;
-    if (const char* sl = std::getenv("GDN_SPIN_LIMIT")) {
-        const long v = std::strtol(sl, nullptr, 10);
-        if (v >= 1 && v <= INT_MAX) s->spin_limit = (int)v;
-    }
+    s->spin_limit = env_spin_limit();
     if (e == hipSuccess) {
         e = hipHostMalloc(reinterpret_cast<void**>(&s->err), sizeof(int), hipHostMallocCoherent | hipHostMallocMapped);
         if (e != hipSuccess) {
@@ -448,6 +475,66 @@ GDN_API int gdn_chunk_bidir(gdn_stream* s, const gdn_io* io, void* o_rev, int64_
     p.dir0 = 0;
     p.ndirs = 2;
     return run(s, p, flags, st);
+}
+
+GDN_API int gdn_chunk_bidir_noalloc(const gdn_config* cfg, const gdn_io* io, void* o_rev, int64_t T,
+                                    const float* state_in, float* state_out, int* status, void* hip_stream) {
+    static_assert(gdn::kScratchBytes == GDN_NOALLOC_SCRATCH_BYTES, "scratch size");
+    if (!cfg || !io) return fail(GDN_E_INVAL, "cfg and io must be non-NULL");
+    if (!status) return fail(GDN_E_INVAL, "status is NULL");
+    const gdn_config c = *cfg;
+    int C = 0;
+    int rc = check_config(c, GDN_L2NORM_QK | GDN_GATE_IS_LOG, &C);
+    if (rc != GDN_OK) return rc;
+    if (c.io_dtype != GDN_BF16) return fail(GDN_E_DTYPE, "the allocation-free call takes bf16 q, k, v, o only");
+    if (!gdn::chunked_supported(C, c.d_k, c.d_v, 0))
+        return fail(GDN_E_SHAPE, "no chunked kernel for d_k=%d d_v=%d subchunk=%d", c.d_k, c.d_v, C);
+    if (T < 0) return fail(GDN_E_SHAPE, "T = %lld is negative", (long long)T);
+    const int64_t item = gdn::chunk_item_bytes(C, c.d_k);
+    const int64_t nsub = (T + C - 1) / C;
+    const int64_t need = 2 * (int64_t)c.batch * c.heads * nsub * item;
+    if (need > gdn::kScratchBytes)
+        return fail(GDN_E_SHAPE, "B=%d H=%d T=%lld needs %lld bytes of workspace, more than the %lld of the static scratch",
+                    c.batch, c.heads, (long long)T, (long long)need, (long long)gdn::kScratchBytes);
+    if (T > 0 && (rc = check_io(c, io, T, o_rev, true)) != GDN_OK) return rc;
+
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(GDN_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    char* ws = nullptr;
+    e = gdn::scratch_address(dev, &ws);
+    if (e != hipSuccess) return fail(GDN_E_HIP, "static scratch on device %d: %s", dev, hipGetErrorString(e));
+    hipError_t prior = hipPeekAtLastError();
+    if (prior != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(GDN_E_HIP, "earlier HIP error: %s", hipGetErrorString(prior));
+    }
+    const hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+    if (T == 0) {
+        if (!state_out || state_out == state_in) return ok();
+        const int64_t n = (int64_t)c.batch * c.heads * c.d_v * c.d_k;
+        e = state_in ? hipMemcpyAsync(state_out, state_in, n * sizeof(float), hipMemcpyDeviceToDevice, st)
+                     : gdn::launch_zero(state_out, n, st);
+        return e == hipSuccess ? ok() : fail(GDN_E_HIP, "state copy: %s", hipGetErrorString(e));
+    }
+    static const int spin_limit = env_spin_limit();
+    gdn::Params p = call_params(c, C, io, T);
+    p.ws = ws;
+    p.ws_item_bytes = item;
+    p.nsub_max = (int)nsub;
+    p.conv = nullptr;
+    p.spin_limit = spin_limit;
+    p.err = status;
+    p.o[1] = o_rev;
+    p.S_in = state_in;
+    p.S_out[0] = state_out;
+    p.S_out[1] = nullptr;
+    p.dir0 = 0;
+    p.ndirs = 2;
+    gdn::Timing tm{nullptr, nullptr, 0, 0};
+    e = gdn::launch_chunked(p, st, &tm);
+    if (e != hipSuccess) return fail(GDN_E_HIP, "kernel launch: %s", hipGetErrorString(e));
+    return ok();
 }
 
 GDN_API int gdn_state_get(gdn_stream* s, float* dst, void* hip_stream) {

@@ -63,6 +63,13 @@ int64_t backward_ws_bytes(int B, int H, int Dk, int Dv, int64_t max_tokens);
 // Which (C, D) pairs the chunked kernels are built for.
 bool chunked_supported(int C, int Dk, int Dv, int io_f32);
 
+// Static workspace of the allocation-free entry point: a file-scope device array in
+// gdn_kernels.hip, one copy per device, loaded with the library's code object and kept until
+// the process ends.  scratch_address gives its device address on `device`, which must be the
+// current device; the address is looked up once per device (hipGetSymbolAddress) and kept.
+constexpr int64_t kScratchBytes = (int64_t)64 << 20;
+hipError_t scratch_address(int device, char** out);
+
 // Optional per-kernel timing: when `ev` is non-null, ev[2*i] / ev[2*i+1] are
 // recorded around launch i and *nlaunch receives the count (<= 4).
 struct Timing {

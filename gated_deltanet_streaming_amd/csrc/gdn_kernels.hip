@@ -39,9 +39,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <utility>
 
 #include "gdn_internal.h"
+
+// Workspace of the allocation-free entry point (gdn_chunk_bidir_noalloc): the prep/scan items of
+// both directions, 2 B H ceil(T / C) of them.  Nothing in it has to start at zero: every item the
+// scan reads is written by the prep launch before it on the same stream.
+static __device__ __align__(256) unsigned char scratch[gdn::kScratchBytes];
 
 namespace gdn {
 
@@ -1533,6 +1539,25 @@ bool chunked_supported(int C, int Dk, int Dv, int io_f32) {
     if (Dk != Dv) return false;
     if (!(Dk == 16 || Dk == 32 || Dk == 64 || Dk == 112 || Dk == 128)) return false;
     return C == 16 || C == 32 || C == 64;
+}
+
+// Device address of the static workspace on `device` (current), looked up on the first call for
+// that device.  Host code never passes the array's own name to a kernel: on the host that name
+// stands for a host-side shadow, not for device memory.
+hipError_t scratch_address(int device, char** out) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static char* addr[kMaxDevices] = {};
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[device]) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[device] = static_cast<char*>(ptr);
+    }
+    *out = addr[device];
+    return hipSuccess;
 }
 
 hipError_t launch_chunked(const Params& p0, hipStream_t s, Timing* tm) {

@@ -143,6 +143,37 @@ GDN_API int gdn_chunk_reverse(gdn_stream* s, const gdn_io* io, int64_t T, uint32
 GDN_API int gdn_chunk_bidir(gdn_stream* s, const gdn_io* io, void* o_rev, int64_t T,
                             uint32_t flags, float* state_out, void* hip_stream);
 
+/* Allocation-free variant of gdn_chunk_bidir, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  It needs no handle and calls no hipMalloc, hipFree or
+ * allocating library routine.  Runs on the current HIP device (the one that
+ * hip_stream belongs to).
+ *  - cfg: as for gdn_stream_init, except that io_dtype must be GDN_BF16
+ *    (GDN_E_DTYPE otherwise), flags may hold GDN_L2NORM_QK and GDN_GATE_IS_LOG
+ *    only, and max_tokens is not used (T bounds the call).
+ *  - The forward scan starts from state_in ([B, H, d_v, d_k] fp32 device memory,
+ *    NULL = zero) and writes o (io->o); its final state goes to state_out (same
+ *    layout, may be NULL, may equal state_in).  The reverse scan starts from zero
+ *    and writes o_rev (io->o's strides).  T = 0 copies state_in to state_out.
+ *  - status: device-visible int (device memory or mapped host memory), not
+ *    NULL.  The kernels set it to 1 when a wait gives up (spin limit as for a
+ *    handle, read from GDN_SPIN_LIMIT at the first call); the outputs of that
+ *    call are then not valid.  The library never clears it.
+ *  - Workspace: the prep and scan items, 2 B H ceil(T / C) of chunk_item bytes
+ *    (13312 bytes for C = 64 and d_k = 112: the 2640-token, 20-head chunk
+ *    takes 22.4 MB),
+ *    live in a static device array of GDN_NOALLOC_SCRATCH_BYTES, one per
+ *    device, created when the library's code is loaded on that device and held
+ *    until the process ends.  A call that needs more returns GDN_E_SHAPE.
+ *  - Every call on a device uses that device's one array: calls that overlap
+ *    in time on one device (different streams, no ordering between them) race
+ *    and produce wrong outputs.  Calls on one stream are ordered and safe.
+ * Errors: GDN_E_INVAL (NULL cfg, io or status, bad flags, alignment or
+ * strides), GDN_E_SHAPE, GDN_E_DTYPE, GDN_E_HIP; on error nothing is enqueued. */
+#define GDN_NOALLOC_SCRATCH_BYTES ((int64_t)64 << 20)
+GDN_API int gdn_chunk_bidir_noalloc(const gdn_config* cfg, const gdn_io* io, void* o_rev, int64_t T,
+                                    const float* state_in, float* state_out, int* status, void* hip_stream);
+
 /* Asynchronous device-to-device copy of the cache [B, H, d_v, d_k] fp32 into
  * dst / from src (src NULL = zero the cache).  Checkpoint, resume and replay. */
 GDN_API int gdn_state_get(gdn_stream* s, float* dst, void* hip_stream);

@@ -82,6 +82,42 @@ def test_null_arguments_are_rejected(lib):
     assert lib.gdn_stream_destroy(None) == binding.GDN_OK
 
 
+@pytest.mark.parametrize("bad, code, word", [
+    (dict(io_dtype=binding.GDN_F32), binding.GDN_E_DTYPE, "bf16"),
+    (dict(flags=binding.GDN_POISON_WS), binding.GDN_E_INVAL, "flag"),
+    (dict(d_k=48, d_v=48), binding.GDN_E_SHAPE, "chunked"),
+    (dict(subchunk=8), binding.GDN_E_SHAPE, "subchunk"),
+    (dict(heads=20, max_tokens=8200), binding.GDN_E_SHAPE, "scratch"),
+])
+def test_noalloc_rejects_bad_calls_before_any_device_work(lib, bad, code, word):
+    """Argument checks of the allocation-free call come before any HIP call, so they hold here.
+    The scratch bound: B=1 H=20 d=112 T=8200 needs 2*20*129*13312 bytes > 64 MiB."""
+    io = binding.GdnIo()
+    status = ctypes.c_int(0)
+    cfg = _cfg(**bad)
+    rc = lib.gdn_chunk_bidir_noalloc(ctypes.byref(cfg), ctypes.byref(io), None, cfg.max_tokens, None, None,
+                                     ctypes.byref(status), None)
+    assert rc == code
+    assert word in binding.gdn_last_error()
+
+
+def test_noalloc_null_arguments_are_rejected(lib):
+    io = binding.GdnIo()
+    cfg = _cfg()
+    status = ctypes.c_int(0)
+    assert lib.gdn_chunk_bidir_noalloc(None, ctypes.byref(io), None, 1, None, None, ctypes.byref(status),
+                                       None) == binding.GDN_E_INVAL
+    assert lib.gdn_chunk_bidir_noalloc(ctypes.byref(cfg), ctypes.byref(io), None, 1, None, None, None,
+                                       None) == binding.GDN_E_INVAL
+    assert "status" in binding.gdn_last_error()
+    # T > 0 with NULL tensors is refused before the device is touched
+    assert lib.gdn_chunk_bidir_noalloc(ctypes.byref(cfg), ctypes.byref(io), None, 64, None, None,
+                                       ctypes.byref(status), None) == binding.GDN_E_INVAL
+    assert "q is NULL" in binding.gdn_last_error()
+    assert lib.gdn_chunk_bidir_noalloc(ctypes.byref(cfg), ctypes.byref(io), None, -1, None, None,
+                                       ctypes.byref(status), None) == binding.GDN_E_SHAPE
+
+
 def test_peaks_library_exports_its_probes():
     """The measurement-support library (copy and MFMA probes behind the roofline peaks) is
     built beside the GDN library and exports exactly its two entry points."""
