@@ -9,12 +9,19 @@ rotate over enough buffer sets that the live set exceeds the 256 MB MALL, so
 every step streams from HBM.
 
 Prints one JSON line.  `value` is tokens per second per layer (T / step time).
-`roofline` is for the dominant kernel (the chunk scan): the algorithmic bytes of
-the call it serves over its average duration from HIP events recorded on its
-launch stream.  Algorithmic bytes per token-head: q, k, v read once and o
+`roofline` is for the step, the launch pair gdn_prep_kernel + gdn_scan_kernel
+that one gdn_chunk_bidir call runs: the algorithmic bytes of the step over
+`ms_per_step`.  Algorithmic bytes per token-head: q, k, v read once and o
 written (224 B each in bf16) plus the two fp32 gates; a bidirectional call also
 writes o_rev; the forward scan reads and writes the 112x112 fp32 state of each
-head once.
+head once.  `roofline.kernels` splits those bytes between the two kernels (the
+prep reads q, k, a, beta; the scan reads v and the state and writes o, o_rev and
+the state) and gives each kernel's average duration from HIP events on its
+launch stream, its duration in the committed rocprofv3 trace, and its HBM
+traffic from the committed FETCH_SIZE / WRITE_SIZE counter runs (null once the
+kernel source has changed since they were taken).
+`--mode long` times the same call on a 21-frame clip (T = 18480 tokens: 289
+dependent sub-chunk steps per head), a secondary line beside the headline.
 `cpu_baseline` times the fp64 CPU oracle on the host cores over the same
 workload (the oracle is a test reference, not a tuned CPU implementation), and
 once more on one core.
@@ -42,9 +49,12 @@ BYTES_PER_TOKEN_HEAD = 4 * D * 2 + 2 * 4     # one scan: q, k, v, o in bf16 + a,
 BIDIR_BYTES_PER_TOKEN_HEAD = 5 * D * 2 + 2 * 4   # both scans in one call: q, k, v once, o and o_rev
 STATE_BYTES = B * H * D * D * 4
 FLOPS_PER_TOKEN_HEAD = 6 * D * D             # S k, rank-1 update, S q
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_scan_720p.json")
+T_LONG = 21 * 880                            # 21 latent frames of 22 x 40 tokens
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gdn_step_720p.json")
+TRACE_FILE = os.path.join(ROOT, "profiles", "trace_gdn_step_720p.json")
 KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_streaming_amd", "csrc", "gdn_kernels.hip")
 ATTN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_720p.json")
+ATTN_TRACE_FILE = os.path.join(ROOT, "profiles", "trace_attn_720p.json")
 ATTN_KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_streaming_amd", "csrc", "gdn_attention.hip")
 
 
@@ -53,17 +63,25 @@ def kernel_source_hash(src: str = KERNEL_SRC) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def algorithmic_bytes(mode: str) -> int:
+def algorithmic_bytes(mode: str, t: int = T) -> int:
     """Bytes a whole step (forward with carried state + reverse) must move at least."""
-    if mode == "bidir":
-        return B * T * H * BIDIR_BYTES_PER_TOKEN_HEAD + 2 * STATE_BYTES
-    per_scan = B * T * H * BYTES_PER_TOKEN_HEAD
+    if mode in ("bidir", "long"):
+        return B * t * H * BIDIR_BYTES_PER_TOKEN_HEAD + 2 * STATE_BYTES
+    per_scan = B * t * H * BYTES_PER_TOKEN_HEAD
     return 2 * per_scan + 2 * STATE_BYTES
 
 
-def load_traffic(path: str = TRAFFIC_FILE, src: str = KERNEL_SRC):
-    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter runs,
-    if they were taken on the current kernel source; else None."""
+def kernel_byte_shares(t: int = T) -> dict:
+    """The algorithmic bytes of one bidirectional call split between its two kernels: the prep
+    reads q, k (bf16) and a, beta (fp32); the scan reads v and the carried state and writes o,
+    o_rev and the state.  The shares add up to algorithmic_bytes("bidir", t)."""
+    prep = B * t * H * (2 * D * 2 + 2 * 4)
+    scan = B * t * H * (3 * D * 2) + 2 * STATE_BYTES
+    return {"gdn_prep_kernel": prep, "gdn_scan_kernel": scan}
+
+
+def _load_record(path: str, src: str = KERNEL_SRC):
+    """A committed rocprofv3 summary record, if it was taken on the current kernel source."""
     try:
         with open(path) as f:
             rec = json.load(f)
@@ -71,10 +89,98 @@ def load_traffic(path: str = TRAFFIC_FILE, src: str = KERNEL_SRC):
         return None
     if rec.get("kernel_source_sha256_16") != kernel_source_hash(src):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
 
 
-def cpu_baseline(d, threads):
+def load_traffic(path: str = TRAFFIC_FILE, src: str = KERNEL_SRC):
+    """HBM bytes per dispatch of each kernel from the committed FETCH_SIZE / WRITE_SIZE runs,
+    {kernel: bytes}, if they were taken on the current kernel source; else None."""
+    rec = _load_record(path, src)
+    if rec is None:
+        return None
+    return {k: v["bytes_per_dispatch"] for k, v in rec["kernels"].items()}
+
+
+def load_trace(path: str = TRACE_FILE, src: str = KERNEL_SRC):
+    """Average duration (us) of each kernel in the committed kernel trace, if it was taken on the
+    current kernel source; else None."""
+    rec = _load_record(path, src)
+    if rec is None:
+        return None
+    return {k: v["average_us"] for k, v in rec["kernels"].items()}
+
+
+def _short_kernel_name(name: str) -> str:
+    for k in ("gdn_prep_kernel", "gdn_scan_kernel", "attn_kernel", "attn_append_kernel"):
+        if k in name:
+            return k
+    return name
+
+
+def summarize_rocprof(kind: str, dirs, out_path: str, src: str) -> None:
+    """Write the committed summary record of rocprofv3 csv output.
+
+    kind "traffic": dirs = (FETCH_SIZE run, WRITE_SIZE run) of a bench run with --copy-probe; the
+    counters of each kernel (median over its dispatches, KiB) are scaled by what the same counter
+    reads for the 256 MiB device copy (bytes read, bytes written).  kind "trace": dirs = (trace
+    run,); the kernel_stats average of each kernel."""
+    import csv
+    import glob
+    import statistics
+
+    def rows(d, pattern):
+        files = glob.glob(os.path.join(d, "**", pattern), recursive=True)
+        if not files:
+            raise SystemExit(f"no {pattern} under {d}")
+        out = []
+        for fn in files:
+            with open(fn) as f:
+                out.extend(csv.DictReader(f))
+        return out
+
+    rec = {"kernel_source_sha256_16": kernel_source_hash(src), "kernels": {}}
+    if kind == "trace":
+        for r in rows(dirs[0], "*kernel_stats.csv"):
+            k = _short_kernel_name(r["Name"])
+            if k.startswith(("gdn_", "attn_")):
+                rec["kernels"][k] = {"calls": int(r["Calls"]), "average_us": round(float(r["AverageNs"]) / 1e3, 3),
+                                     "min_us": round(float(r["MinNs"]) / 1e3, 3),
+                                     "max_us": round(float(r["MaxNs"]) / 1e3, 3)}
+    else:
+        per = {}
+        copy_bytes = 256 * 1024 * 1024
+        for d, counter in zip(dirs, ("FETCH_SIZE", "WRITE_SIZE")):
+            vals = {}
+            for r in rows(d, "*counter_collection.csv"):
+                if r["Counter_Name"] != counter:
+                    continue
+                vals.setdefault((r["Kernel_Name"], r["Dispatch_Id"]), 0.0)
+                vals[(r["Kernel_Name"], r["Dispatch_Id"])] += float(r["Counter_Value"])
+            by_kernel = {}
+            for (name, _), v in vals.items():
+                by_kernel.setdefault(name, []).append(v)
+            copy = [statistics.median(v) for n, v in by_kernel.items() if "copyBuffer" in n]
+            if not copy:
+                raise SystemExit(f"{counter}: no copy-probe dispatch in {d} (run the bench with --copy-probe)")
+            # the copy reads and writes copy_bytes: scale = bytes per counter unit (KiB)
+            rec[f"{counter.lower()}_scale_bytes_per_unit"] = copy_bytes / copy[0]
+            rec[f"copy_probe_{counter}_KiB"] = copy[0]
+            for n, v in by_kernel.items():
+                k = _short_kernel_name(n)
+                if k.startswith(("gdn_", "attn_")):
+                    per.setdefault(k, {})[counter] = (statistics.median(v), len(v))
+        for k, c in per.items():
+            f_kib, n = c.get("FETCH_SIZE", (0.0, 0))
+            w_kib, _ = c.get("WRITE_SIZE", (0.0, 0))
+            rec["kernels"][k] = {"dispatches": n, "fetch_KiB": f_kib, "write_KiB": w_kib,
+                                 "bytes_per_dispatch": int(f_kib * rec["fetch_size_scale_bytes_per_unit"]
+                                                           + w_kib * rec["write_size_scale_bytes_per_unit"])}
+    with open(out_path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
+def cpu_baseline(d, threads, t=T):
     import oracle
     oracle.build(force=False)
 
@@ -88,10 +194,10 @@ def cpu_baseline(d, threads):
 
     reps, dt = rate(threads, 12.0, 500)
     reps1, dt1 = rate(1, 3.0, 4)
-    return {"value": round(T / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": round(t / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"the full workload, {reps} repeats: forward + reverse fp64 scans of B={B} H={H} "
-                      f"d={D} T={T} ({dt:.3f} s per step)",
-            "single_core": {"value": round(T / dt1, 1), "cores": 1,
+                      f"d={D} T={t} ({dt:.3f} s per step)",
+            "single_core": {"value": round(t / dt1, 1), "cores": 1,
                             "sample": f"the same step on one thread, {reps1} repeats ({dt1:.3f} s per step)"}}
 
 
@@ -138,8 +244,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--mode", choices=["bidir", "separate", "backward", "attention"], default="bidir",
+    ap.add_argument("--mode", choices=["bidir", "separate", "long", "backward", "attention"], default="bidir",
                     help="bidir: one gdn_chunk_bidir call per step; separate: forward then reverse calls; "
+                         "long: gdn_chunk_bidir on a 21-frame clip (T = 18480); "
                          "backward: the gradients of both scans of the pair (gdn_chunk_backward); "
                          "attention: the softmax block's sink + window attention (gdn_attn_chunk)")
     ap.add_argument("--sets", type=int, default=6, help="rotating input/output buffer sets (1 = warm)")
@@ -147,7 +254,23 @@ def main():
     ap.add_argument("--no-peaks", action="store_true", help="skip the copy / MFMA peak probes")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 256 MiB device copy (reference for counter scaling)")
+    ap.add_argument("--summarize", nargs="+", metavar=("KIND", "DIR"),
+                    help="no GPU run: write the committed summary record of rocprofv3 csv output; "
+                         "'traffic FETCH_DIR WRITE_DIR [attn]' or 'trace TRACE_DIR [attn]'")
     args = ap.parse_args()
+
+    if args.summarize:
+        kind, rest = args.summarize[0], args.summarize[1:]
+        attn = rest and rest[-1] == "attn"
+        dirs = rest[:-1] if attn else rest
+        if kind not in ("traffic", "trace") or len(dirs) != (2 if kind == "traffic" else 1):
+            raise SystemExit("--summarize traffic FETCH_DIR WRITE_DIR [attn] | trace TRACE_DIR [attn]")
+        if attn:
+            out = ATTN_TRAFFIC_FILE if kind == "traffic" else ATTN_TRACE_FILE
+            src = ATTN_KERNEL_SRC
+        else:
+            out, src = (TRAFFIC_FILE if kind == "traffic" else TRACE_FILE), KERNEL_SRC
+        return summarize_rocprof(kind, dirs, out, src)
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path needs no "
@@ -167,12 +290,14 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    d = gdn_inputs.batch(1, B, T, H, D, with_state=True)
+    t_run = T_LONG if args.mode == "long" else T
+    nsets = min(args.sets, 3) if args.mode == "long" else args.sets   # 3 long sets: 620 MB live
+    d = gdn_inputs.batch(1, B, t_run, H, D, with_state=True)
 
     sets = []
-    for i in range(args.sets):
+    for i in range(nsets):
         # distinct values per set (the first set is the seeded workload itself)
-        di = d if i == 0 else gdn_inputs.batch(1, B, T, H, D, chunk=i)
+        di = d if i == 0 else gdn_inputs.batch(1, B, t_run, H, D, chunk=i)
         qi = {k: torch.from_numpy(di[k]).to(dev, torch.bfloat16) for k in ("q", "k", "v")}
         qi["a"] = torch.from_numpy(di["a"]).to(dev)
         qi["beta"] = torch.from_numpy(di["beta"]).to(dev)
@@ -180,13 +305,13 @@ def main():
         qi["o_rev"] = torch.empty_like(qi["v"])
         sets.append(qi)
 
-    s = gb.Stream(B, H, D, D, T, device=0)
+    s = gb.Stream(B, H, D, D, t_run, device=0)
     s.state_set(torch.from_numpy(d["S0"]).to(dev))
     stream = torch.cuda.current_stream(dev)
 
     def step(i):
         x = sets[i % len(sets)]
-        if args.mode == "bidir":
+        if args.mode in ("bidir", "long"):
             s.bidir(x["q"], x["k"], x["v"], x["a"], x["beta"], x["o"], x["o_rev"], stream=stream)
         else:
             s.forward(x["q"], x["k"], x["v"], x["a"], x["beta"], x["o"], stream=stream)
@@ -250,17 +375,30 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    alg_bytes = algorithmic_bytes(args.mode)
+    alg_bytes = algorithmic_bytes(args.mode, t_run)
     launches_per_step = scan_n / args.steps
-    bytes_per_scan_launch = alg_bytes / launches_per_step
-    achieved_gbs = bytes_per_scan_launch / (scan_avg_ms * 1e-3) / 1e9
     step_gbs = alg_bytes / (ms_per_step * 1e-3) / 1e9
-    flops = 2 * B * T * H * FLOPS_PER_TOKEN_HEAD
-    traffic = load_traffic()
+    flops = 2 * B * t_run * H * FLOPS_PER_TOKEN_HEAD
+    headline = args.mode == "bidir" and args.sets >= 6
+    # the committed trace and counter records describe the headline run only
+    traffic = load_traffic() if headline else None
+    trace = load_trace() if headline else None
+    kernels = {}
+    if args.mode in ("bidir", "long"):
+        for k, share in kernel_byte_shares(t_run).items():
+            ev_ms = prep_avg_ms if k == "gdn_prep_kernel" else scan_avg_ms
+            kernels[k] = {
+                "algorithmic_bytes": share,
+                "avg_us_events": round(ev_ms * 1e3, 3),
+                "achieved_GBs_events": round(share / (ev_ms * 1e-3) / 1e9, 1),
+                "avg_us_trace": trace.get(k) if trace else None,
+                "traffic": traffic.get(k) if traffic else None,
+            }
+    step_traffic = sum(v["traffic"] for v in kernels.values()) if traffic and kernels else None
 
     out = {
         "metric": METRIC,
-        "value": round(T / (ms_per_step * 1e-3), 1),
+        "value": round(t_run / (ms_per_step * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -272,34 +410,34 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "720p streaming chunk, one GDN layer: forward scan from the carried state + "
-                        "intra-chunk reverse scan",
-            "B": B, "H": H, "d_k": D, "d_v": D, "T": T, "subchunk": 64,
-            "call": "gdn_chunk_bidir" if args.mode == "bidir" else "gdn_chunk_forward + gdn_chunk_reverse",
-            "buffers": f"{args.sets} rotating sets ({'cold: live set > 256 MB MALL' if args.sets >= 6 else 'warm'})",
+            "workload": ("21-frame clip (18480 tokens), one GDN layer: forward scan from the carried state + "
+                         "reverse scan" if args.mode == "long" else
+                         "720p streaming chunk, one GDN layer: forward scan from the carried state + "
+                         "intra-chunk reverse scan"),
+            "B": B, "H": H, "d_k": D, "d_v": D, "T": t_run, "subchunk": 64,
+            "call": "gdn_chunk_forward + gdn_chunk_reverse" if args.mode == "separate" else "gdn_chunk_bidir",
+            "buffers": f"{nsets} rotating sets ({'cold: live set > 256 MB MALL' if nsets * t_run >= 6 * T else 'warm'})",
         },
         "roofline": {
             "bound": "hbm",
-            "achieved": round(achieved_gbs, 1),
+            "achieved": round(step_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "kernel": "gdn_scan_kernel",
-            "kernel_avg_us": round(scan_avg_ms * 1e3, 3),
-            "algorithmic_bytes_per_launch": int(bytes_per_scan_launch),
-        },
-        "step_roofline": {
+            "frac": round(step_gbs / HBM_PEAK_GBS, 4),
+            "traffic": step_traffic,
+            "kernel": "step: gdn_prep_kernel + gdn_scan_kernel",
             "algorithmic_bytes_per_step": alg_bytes,
-            "achieved_GBs": round(step_gbs, 1),
-            "hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+            "kernels": kernels,
+            "note": "achieved = algorithmic bytes of the step / ms_per_step; traffic = the kernels' scaled "
+                    "FETCH_SIZE + WRITE_SIZE per dispatch from the committed counter runs",
+        },
+        "step_detail": {
             "mfma_bf16_frac": round(flops / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
-            "prep_avg_us": round(prep_avg_ms * 1e3, 3),
-            "scan_avg_us": round(scan_avg_ms * 1e3, 3),
+            "launches_per_step": launches_per_step,
             "event_ms_per_step": round(ms_events / args.steps, 5),
             "per_call_ms_p10_p50_p90": [round(p10, 5), round(p50, 5), round(p90, 5)],
             "warm_ms_per_step": round(warm_ms, 5),
-            "target_tokens_per_s": 108e6,
+            "target_tokens_per_s": 108e6 if args.mode == "bidir" else None,
         },
     }
     if not args.no_peaks:
@@ -307,7 +445,7 @@ def main():
     if not args.no_cpu:
         # the host share of one GPU: OMP_NUM_THREADS when set (16 on the GPU machines), else the affinity mask
         threads = min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS", "0")) or 1 << 30)
-        out["cpu_baseline"] = cpu_baseline(d, threads)
+        out["cpu_baseline"] = cpu_baseline(d, threads, t_run)
     s.close()
     print(json.dumps(out), flush=True)
 
@@ -471,7 +609,7 @@ def main_attention(args):
                    "sink": ATTN_SINK, "window": ATTN_WINDOW, "keys": L, "call": "gdn_attn_chunk (commit)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": load_traffic(ATTN_TRAFFIC_FILE, ATTN_KERNEL_SRC),
+                     "traffic": (load_traffic(ATTN_TRAFFIC_FILE, ATTN_KERNEL_SRC) or {}).get("attn_kernel"),
                      "kernel": "attn_kernel", "kernel_avg_us": round(launch_ms * 1e3, 1),
                      "algorithmic_flops_per_launch": flops},
     }

@@ -124,6 +124,27 @@ def test_720p_layer_steady_state_sampled_rows():
     att.close()
 
 
+def test_720p_layer_steady_state_every_row_of_two_heads():
+    """The same 720p steady state (third chunk: 6160 keys), every one of the 2640 query rows of
+    heads 0 and 13 against the reference fed those heads' q, k, v for all three chunks (heads
+    are independent)."""
+    import torch
+    from gated_deltanet_streaming_amd.binding import WindowAttention
+    B, H, D, T = 1, 20, 112, 2640
+    heads = [0, 13]
+    att = WindowAttention(B, H, D, 880, 2640, T)
+    ref = SinkWindowAttention(880, 2640)
+    for c in range(3):
+        d = gdn_inputs.attn_chunk(c, B, T, H, D)
+        q, k, v = (_dev(d[x]) for x in ("q", "k", "v"))
+        print(f"case 720p every row, heads {heads}, call={c}", flush=True)
+        o = att.chunk(q, k, v)
+        torch.cuda.synchronize()
+        want = ref.chunk(d["q"][:, :, heads], d["k"][:, :, heads], d["v"][:, :, heads])
+        assert_close(f"o[{c}] heads {heads}", o[:, :, heads], want)
+    att.close()
+
+
 def test_checkpoint_resume_is_bitwise():
     """A handle resumed from another's cache snapshot continues bitwise identically; bad
     counters are refused."""

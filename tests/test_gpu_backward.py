@@ -87,6 +87,14 @@ def test_backward_720p_width_long(reverse):
     _check_all(g, ref)
 
 
+@pytest.mark.parametrize("reverse", [False, True])
+def test_backward_720p_chunk_two_heads(reverse):
+    """The benchmarked shape along time: d = 112, T = 2640 (the whole 720p chunk), 2 heads."""
+    d = gdn_inputs.batch(76, 1, 2640, 2, 112, with_state=True)
+    g, ref = _grads(d, 112, 112, 2640, reverse=reverse, seed=76)
+    _check_all(g, ref)
+
+
 def test_backward_without_final_gradient_or_start():
     d = gdn_inputs.batch(78, 1, 64, 2, 32, with_state=True)
     g, ref = _grads(d, 32, 32, 64, with_state=False, with_final=False, seed=78)

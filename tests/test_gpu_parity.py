@@ -20,7 +20,8 @@ from gated_deltanet_streaming_amd import binding as gb  # noqa: E402
 
 def _run_pair(d, D, T, *, C=0, flags=0, io="bf16", layout="bthd", state=True, bidir=False):
     B, H = d["q"].shape[0], d["q"].shape[2]
-    s = gb.Stream(B, H, D, D, max(T, 1), subchunk=C, io_dtype=io)
+    # NaN-filled workspace: a read of a workspace byte the kernels did not write shows up
+    s = gb.Stream(B, H, D, D, max(T, 1), subchunk=C, io_dtype=io, poison_ws=True)
     try:
         if state:
             s.state_set(torch.from_numpy(d["S0"]).cuda())
