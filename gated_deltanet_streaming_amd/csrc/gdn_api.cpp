@@ -15,6 +15,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 #include <new>
 #include <string>
 #include <utility>
@@ -115,6 +116,18 @@ int elem_size(const gdn_config& c) { return c.io_dtype == GDN_F32 ? 4 : 2; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The product of non-negative sizes in int64; false if a factor is negative or it overflows.
+bool size_product(std::initializer_list<int64_t> factors, int64_t* out) {
+    int64_t r = 1;
+    for (const int64_t x : factors)
+        if (x < 0 || __builtin_mul_overflow(r, x, &r)) return false;
+    *out = r;
+    return true;
+}
+
+constexpr int64_t kMaxTokens = (int64_t)1 << 30;   // the kernels count tokens in 32-bit integers
+constexpr int64_t kMaxStride = (int64_t)1 << 40;   // elements; larger strides cannot address a real tensor
+
 // Rows of one (stream, head) are addressed with 32-bit byte offsets from a
 // per-(b, h) base, and rows past the end of the sequence must not overlap real
 // rows (they read as zero): token stride >= row width, extent < 2 GiB.
@@ -123,13 +136,15 @@ int check_tensor(const char* name, const void* ptr, const int64_t* st, int esz, 
     if (!aligned16(ptr)) return fail(GDN_E_INVAL, "%s is not 16-byte aligned", name);
     for (int i = 0; i < 3; ++i) {
         if (st[i] < 0) return fail(GDN_E_INVAL, "%s stride %d is negative", name, i);
+        if (st[i] > kMaxStride) return fail(GDN_E_SHAPE, "%s stride %d (%lld elements) is too large", name, i, (long long)st[i]);
         if ((st[i] * esz) % 16 != 0)
             return fail(GDN_E_INVAL, "%s stride %d (%lld elements) is not a multiple of 16 bytes", name, i,
                         (long long)st[i]);
     }
     if (st[1] < width)
         return fail(GDN_E_INVAL, "%s token stride %lld is smaller than the row width %d", name, (long long)st[1], width);
-    if ((T + 64) * st[1] * esz >= ((int64_t)1 << 31))
+    // (T + 64) st[1] esz < 2^31, with T <= kMaxTokens checked by every caller
+    if (st[1] > (((int64_t)1 << 31) - 1) / ((T + 64) * esz))
         return fail(GDN_E_SHAPE, "%s: T * token stride exceeds the 2 GiB per-(stream, head) extent", name);
     return GDN_OK;
 }
@@ -140,7 +155,7 @@ int check_config(const gdn_config& c, uint32_t allowed_flags, int* C) {
     if (c.batch < 1 || c.heads < 1) return fail(GDN_E_SHAPE, "batch and heads must be >= 1");
     if (!is_mult16(c.d_k) || !is_mult16(c.d_v))
         return fail(GDN_E_SHAPE, "d_k=%d d_v=%d must be multiples of 16 in [16, 128]", c.d_k, c.d_v);
-    if (c.max_tokens < 1) return fail(GDN_E_SHAPE, "max_tokens must be >= 1");
+    if (c.max_tokens < 1 || c.max_tokens > kMaxTokens) return fail(GDN_E_SHAPE, "max_tokens must be in [1, 2^30]");
     *C = c.subchunk == 0 ? 64 : c.subchunk;
     if (!(*C == 16 || *C == 32 || *C == 64)) return fail(GDN_E_SHAPE, "subchunk %d not in {0, 16, 32, 64}", c.subchunk);
     if (c.io_dtype != GDN_BF16 && c.io_dtype != GDN_F32) return fail(GDN_E_DTYPE, "unknown io_dtype %d", c.io_dtype);
@@ -303,6 +318,17 @@ GDN_API int gdn_stream_init(const gdn_config* cfg, int device, gdn_stream** out)
     int C = 0;
     const int rc = check_config(c, GDN_L2NORM_QK | GDN_GATE_IS_LOG | GDN_POISON_WS, &C);
     if (rc != GDN_OK) return rc;
+    // every size the handle allocates, checked for overflow before anything is allocated
+    const bool chunked = gdn::chunked_supported(C, c.d_k, c.d_v, c.io_dtype == GDN_F32);
+    const int64_t item_bytes = chunked ? gdn::chunk_item_bytes(C, c.d_k) : 0;
+    const int64_t nsub_max = (c.max_tokens + C - 1) / C;
+    int64_t state_elems = 0, items_total = 0, conv_bytes = 0;
+    if (!size_product({c.batch, c.heads, c.d_v, c.d_k, (int64_t)sizeof(float)}, &state_elems) ||
+        !size_product({2, c.batch, c.heads, nsub_max, item_bytes}, &items_total) ||
+        !size_product({3, c.batch, c.max_tokens, c.heads, c.d_k, 2}, &conv_bytes))
+        return fail(GDN_E_SHAPE, "batch %d x heads %d x max_tokens %lld: the state or workspace size overflows",
+                    c.batch, c.heads, (long long)c.max_tokens);
+    state_elems /= (int64_t)sizeof(float);
 
     int ndev = 0;
     hipError_t e = hipGetDeviceCount(&ndev);
@@ -316,8 +342,8 @@ GDN_API int gdn_stream_init(const gdn_config* cfg, int device, gdn_stream** out)
     s->cfg = c;
     s->device = device;
     s->C = C;
-    s->chunked_ok = gdn::chunked_supported(C, c.d_k, c.d_v, c.io_dtype == GDN_F32);
-    s->state_elems = (int64_t)c.batch * c.heads * c.d_v * c.d_k;
+    s->chunked_ok = chunked;
+    s->state_elems = state_elems;
     s->profile = false;
     for (int i = 0; i < gdn::KCOUNT; ++i) {
         s->acc_ms[i] = 0.0;
@@ -348,9 +374,9 @@ GDN_API int gdn_stream_init(const gdn_config* cfg, int device, gdn_stream** out)
         *s->err = 0;
     }
     if (e == hipSuccess && s->chunked_ok) {
-        s->item_bytes = gdn::chunk_item_bytes(C, c.d_k);
-        s->nsub_max = (int)((c.max_tokens + C - 1) / C);
-        s->items_total = 2 * (int64_t)c.batch * c.heads * s->nsub_max * s->item_bytes;
+        s->item_bytes = item_bytes;
+        s->nsub_max = (int)nsub_max;
+        s->items_total = items_total;
         const int64_t bytes = s->items_total;
         e = hipMalloc(&s->ws, bytes);
         if (e != hipSuccess) {
@@ -361,7 +387,7 @@ GDN_API int gdn_stream_init(const gdn_config* cfg, int device, gdn_stream** out)
         }
         if (c.flags & GDN_POISON_WS) e = hipMemset(s->ws, 0xff, bytes);
         if (c.io_dtype == GDN_F32) {
-            const int64_t cb = 3 * (int64_t)c.batch * c.max_tokens * c.heads * c.d_k * 2;
+            const int64_t cb = conv_bytes;
             e = hipMalloc(&s->conv, cb);
             if (e != hipSuccess) {
                 (void)hipFree(s->state);
@@ -482,18 +508,19 @@ GDN_API int gdn_chunk_bidir_noalloc(const gdn_config* cfg, const gdn_io* io, voi
     static_assert(gdn::kScratchBytes == GDN_NOALLOC_SCRATCH_BYTES, "scratch size");
     if (!cfg || !io) return fail(GDN_E_INVAL, "cfg and io must be non-NULL");
     if (!status) return fail(GDN_E_INVAL, "status is NULL");
-    const gdn_config c = *cfg;
+    gdn_config c = *cfg;
+    c.max_tokens = 1;   // not used by this call
     int C = 0;
     int rc = check_config(c, GDN_L2NORM_QK | GDN_GATE_IS_LOG, &C);
     if (rc != GDN_OK) return rc;
     if (c.io_dtype != GDN_BF16) return fail(GDN_E_DTYPE, "the allocation-free call takes bf16 q, k, v, o only");
     if (!gdn::chunked_supported(C, c.d_k, c.d_v, 0))
         return fail(GDN_E_SHAPE, "no chunked kernel for d_k=%d d_v=%d subchunk=%d", c.d_k, c.d_v, C);
-    if (T < 0) return fail(GDN_E_SHAPE, "T = %lld is negative", (long long)T);
+    if (T < 0 || T > kMaxTokens) return fail(GDN_E_SHAPE, "T = %lld outside [0, 2^30]", (long long)T);
     const int64_t item = gdn::chunk_item_bytes(C, c.d_k);
     const int64_t nsub = (T + C - 1) / C;
-    const int64_t need = 2 * (int64_t)c.batch * c.heads * nsub * item;
-    if (need > gdn::kScratchBytes)
+    int64_t need = 0;
+    if (!size_product({2, c.batch, c.heads, nsub, item}, &need) || need > gdn::kScratchBytes)
         return fail(GDN_E_SHAPE, "B=%d H=%d T=%lld needs %lld bytes of workspace, more than the %lld of the static scratch",
                     c.batch, c.heads, (long long)T, (long long)need, (long long)gdn::kScratchBytes);
     if (T > 0 && (rc = check_io(c, io, T, o_rev, true)) != GDN_OK) return rc;
@@ -613,6 +640,7 @@ GDN_API int gdn_chunk_backward(gdn_stream* s, const gdn_io* io, const gdn_grad* 
     if (!g->dq || !g->dk || !g->dv || !g->da || !g->dbeta) return fail(GDN_E_INVAL, "a gradient output is NULL");
     if (!s->bwd_ws) {
         const int64_t bytes = gdn::backward_ws_bytes(s->cfg.batch, s->cfg.heads, dk, dv, s->cfg.max_tokens);
+        if (bytes < 0) return fail(GDN_E_SHAPE, "the backward workspace size overflows");
         hipError_t e = hipMalloc(&s->bwd_ws, bytes);
         if (e != hipSuccess) {
             s->bwd_ws = nullptr;
@@ -680,7 +708,11 @@ GDN_API int gdn_attn_init(const gdn_attn_config* cfg, int device, gdn_attn** out
     if (c.sink_tokens < 0 || c.window_tokens < 0) return fail(GDN_E_SHAPE, "negative cache size");
     if (c.max_tokens < 1 || c.max_tokens > (1 << 30)) return fail(GDN_E_SHAPE, "max_tokens must be in [1, 2^30]");
     if (!(c.scale >= 0.f) || !std::isfinite(c.scale)) return fail(GDN_E_INVAL, "scale must be finite and >= 0");
-    const int64_t slots = (int64_t)c.batch * c.heads * ((int64_t)c.sink_tokens + c.window_tokens) * c.head_dim;
+    int64_t slots = 0;
+    if (!size_product({c.batch, c.heads, (int64_t)c.sink_tokens + c.window_tokens, c.head_dim, 4}, &slots))
+        return fail(GDN_E_SHAPE, "batch %d x heads %d x (sink + window) %lld: the cache size overflows", c.batch,
+                    c.heads, (long long)c.sink_tokens + c.window_tokens);
+    slots /= 4;
     // the kernels address a (stream, head)'s sink or window, and a chunk, with 32-bit byte offsets
     if ((int64_t)std::max(std::max(c.sink_tokens, c.window_tokens), (int32_t)std::min<int64_t>(c.max_tokens, 1 << 30)) *
             c.head_dim * 2 >= ((int64_t)1 << 31))

@@ -65,9 +65,14 @@ void tm_end(Timing* tm, hipStream_t s) {
 // ---------------------------------------------------------------------------
 int64_t backward_ws_bytes(int B, int H, int Dk, int Dv, int64_t max_tokens) {
     const int64_t nrb = Dv / 16;
-    const int64_t states = (int64_t)B * H * nrb * (max_tokens + 1) * 16 * Dk;
-    const int64_t partials = (int64_t)B * max_tokens * H * nrb * (2 * Dk + 2);
-    return 4 * (states + partials);
+    int64_t states = 0, partials = 0, total = 0;
+    if (__builtin_mul_overflow((int64_t)B * H, nrb * 16 * Dk, &states) ||
+        __builtin_mul_overflow(states, max_tokens + 1, &states) ||
+        __builtin_mul_overflow((int64_t)B * H, nrb * (2 * Dk + 2), &partials) ||
+        __builtin_mul_overflow(partials, max_tokens, &partials) || __builtin_add_overflow(states, partials, &total) ||
+        __builtin_mul_overflow(total, (int64_t)4, &total))
+        return -1;
+    return total;
 }
 
 // sum over the 16 rows of the workgroup (lane bits 2..5): within each row of 16 lanes by two

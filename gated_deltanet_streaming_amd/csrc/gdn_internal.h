@@ -57,7 +57,7 @@ struct BwdParams {
     float* partials;
     int reverse;           // 0: the forward scan (t ascending), 1: the reverse scan
 };
-// Bytes of the backward workspace for max_tokens tokens.
+// Bytes of the backward workspace for max_tokens tokens, or -1 if the size overflows int64.
 int64_t backward_ws_bytes(int B, int H, int Dk, int Dv, int64_t max_tokens);
 
 // Which (C, D) pairs the chunked kernels are built for.

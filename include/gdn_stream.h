@@ -54,7 +54,8 @@ extern "C" {
 /* return codes */
 #define GDN_OK        0
 #define GDN_E_INVAL  -1   /* NULL handle/pointer, bad flag, bad alignment      */
-#define GDN_E_SHAPE  -2   /* unsupported sizes, T outside [0, max_tokens]       */
+#define GDN_E_SHAPE  -2   /* unsupported sizes, T outside [0, max_tokens], sizes
+                             or strides whose products overflow                 */
 #define GDN_E_DTYPE  -3   /* unknown io_dtype                                   */
 #define GDN_E_NOMEM  -4   /* device allocation failed at init                   */
 #define GDN_E_HIP    -5   /* a HIP runtime call failed (incl. earlier faults)   */
@@ -83,7 +84,8 @@ typedef struct gdn_config {
     int32_t d_k;         /* key/query width: multiple of 16, 16..128             */
     int32_t d_v;         /* value width (state rows): multiple of 16, 16..128;   */
                          /* the chunked kernels need d_v == d_k (16, 32, 64, 112, 128) */
-    int64_t max_tokens;  /* largest T of any call; sizes the fixed workspace     */
+    int64_t max_tokens;  /* largest T of any call, 1 .. 2^30; sizes the fixed    */
+                         /* workspace                                          */
     int32_t subchunk;    /* chunked-kernel sub-chunk C: 0 (= 64), 16, 32 or 64  */
     int32_t io_dtype;    /* GDN_BF16 or GDN_F32.  With GDN_F32 the chunked       */
                          /* kernels stage q, k, v as bf16 (round to nearest    */
