@@ -63,6 +63,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // decays below e^-80 are treated as e^-80 (the state is forgotten either way)
 #define GDN_MIN_LOG_DECAY (-80.0f)
+#define GDN_PREP_BLOCKS 1   // consecutive sub-chunk blocks per prep workgroup
 
 __device__ __forceinline__ f32x4 mma_bf16_k32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -385,8 +386,9 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
     // workgroups of both directions of that head run, so that the items land in the L2 they are
     // read from
     const int nsub = (int)((p.T + C - 1) / C);
+    const int ngrp = (nsub + GDN_PREP_BLOCKS - 1) / GDN_PREP_BLOCKS;   // block groups per stream-head
     const int xcd = blockIdx.x & 7, kk = blockIdx.x >> 3;
-    const int j = kk % nsub, bh = xcd_head(xcd, kk / nsub, p.B * p.H);
+    const int jg = kk % ngrp, bh = xcd_head(xcd, kk / ngrp, p.B * p.H);
     if (bh < 0) return;
     const int b = bh / p.H, h = bh - b * p.H;
     const int T = (int)p.T;
@@ -395,20 +397,25 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
     auto active = [&](int dir) { return dir >= dlo && dir <= dhi; };
     // token row (within the block) of processing row t
     auto mrow = [](int dir, int t) { return dir ? C - 1 - t : t; };
-    auto item_addr = [&](int dir) {
-        const int n = dir ? N - 1 - j : j;
-        return p.ws + ((((int64_t)dir * p.B + b) * p.H + h) * p.nsub_max + n) * p.ws_item_bytes;
-    };
-    char* const items[2] = {item_addr(0), item_addr(1)};   // this block's item in either direction
-    auto item_of = [&](int dir) { return items[dir]; };
-
-    {
-        // every global load of the block goes out before the first is used: the gates,
-        // then the K and Q rows (16-byte chunks, NLD per thread)
-        float av = 1.f, bt = 0.f;
-        bool gv = false;
+    // The global loads of a block: its gates (threads < C) and its K and Q rows (16-byte chunks,
+    // NLD per thread), into registers.  A workgroup takes GDN_PREP_BLOCKS consecutive blocks; the
+    // loads of the next block go out before the work on the current one starts, so that their
+    // latency hides behind it.
+    const bf16* kb = reinterpret_cast<const bf16*>(p.k) + (int64_t)b * p.ks[0] + (int64_t)h * p.ks[2];
+    const bf16* qb = reinterpret_cast<const bf16*>(p.q) + (int64_t)b * p.qs[0] + (int64_t)h * p.qs[2];
+    const auto kr = make_rsrc(kb, (uint32_t)(((int64_t)(T - 1) * p.ks[1] + D) * 2));
+    const auto qr = make_rsrc(qb, (uint32_t)(((int64_t)(T - 1) * p.qs[1] + D) * 2));
+    const int ksb = (int)p.ks[1] * 2, qsb = (int)p.qs[1] * 2;
+    constexpr int NLD = (C * CH + NT - 1) / NT;
+    float av = 1.f, bt = 0.f;
+    bool gv = false;
+    uint4 kv[NLD], qv[NLD];
+    auto load_block = [&](int jb) {
+        av = 1.f;
+        bt = 0.f;
+        gv = false;
         if (tid < C) {
-            const int tk = j * C + tid;
+            const int tk = jb * C + tid;
             gv = tk < T;
             if (gv) {
                 const int64_t gq = (int64_t)b * p.gs[0] + (int64_t)tk * p.gs[1] + (int64_t)h * p.gs[2];
@@ -416,37 +423,43 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
                 bt = p.beta[gq];
             }
         }
-        const bf16* kb = reinterpret_cast<const bf16*>(p.k) + (int64_t)b * p.ks[0] + (int64_t)h * p.ks[2];
-        const bf16* qb = reinterpret_cast<const bf16*>(p.q) + (int64_t)b * p.qs[0] + (int64_t)h * p.qs[2];
-        const auto kr = make_rsrc(kb, (uint32_t)(((int64_t)(T - 1) * p.ks[1] + D) * 2));
-        const auto qr = make_rsrc(qb, (uint32_t)(((int64_t)(T - 1) * p.qs[1] + D) * 2));
-        const int ksb = (int)p.ks[1] * 2, qsb = (int)p.qs[1] * 2;
-        constexpr int NLD = (C * CH + NT - 1) / NT;
-        uint4 kv[NLD], qv[NLD];
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
             const int idx = tid + i * NT;
             if (idx < C * CH) {
                 const int t = idx / CH, c = idx - t * CH;
-                const int tk = j * C + t;
+                const int tk = jb * C + t;
                 kv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, tk * ksb + 16 * c, 0, 0));
                 qv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(qr, tk * qsb + 16 * c, 0, 0));
             }
         }
-        if (tid < C) {
-            sg[0][tid] = gv ? fmaxf(p.gate_log ? av : logf(av), GDN_MIN_LOG_DECAY) : 0.f;   // log a until the prefix
-            bp[0][tid] = bt;
-        }
+    };
+    load_block(jg * GDN_PREP_BLOCKS);
+
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int idx = tid + i * NT;
-            if (idx < C * CH) {
-                const int t = idx / CH, c = idx - t * CH;
-                *reinterpret_cast<uint4*>(Ks + kq(t, 8 * c)) = kv[i];
-                *reinterpret_cast<uint4*>(Qs + kq(t, 8 * c)) = qv[i];
-            }
+    for (int it = 0; it < GDN_PREP_BLOCKS; ++it) {
+    const int j = jg * GDN_PREP_BLOCKS + it;
+    if (j >= nsub) break;
+    if (it > 0) lds_barrier();   // every read of the previous block's LDS data is done
+    // this block's item in either direction
+    char* const item_f = p.ws + ((((int64_t)0 * p.B + b) * p.H + h) * p.nsub_max + j) * p.ws_item_bytes;
+    char* const item_r = p.ws + ((((int64_t)1 * p.B + b) * p.H + h) * p.nsub_max + (N - 1 - j)) * p.ws_item_bytes;
+    auto item_of = [&](int dir) { return dir ? item_r : item_f; };
+
+    if (tid < C) {
+        sg[0][tid] = gv ? fmaxf(p.gate_log ? av : logf(av), GDN_MIN_LOG_DECAY) : 0.f;   // log a until the prefix
+        bp[0][tid] = bt;
+    }
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+        const int idx = tid + i * NT;
+        if (idx < C * CH) {
+            const int t = idx / CH, c = idx - t * CH;
+            *reinterpret_cast<uint4*>(Ks + kq(t, 8 * c)) = kv[i];
+            *reinterpret_cast<uint4*>(Qs + kq(t, 8 * c)) = qv[i];
         }
     }
+    if (it + 1 < GDN_PREP_BLOCKS && j + 1 < nsub) load_block(j + 1);
     lds_barrier();
 
     // per-token inverse norms: 4 lanes per row, 16 rows per wavefront; waves < NB take the
@@ -758,6 +771,7 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
             gstore16(item_of(dir) + (kind * NF + f) * 1024 + 16 * lane, __builtin_bit_cast(uint4, v));
         }
     }
+    }   // blocks of the workgroup
 }
 
 // ---------------------------------------------------------------------------
@@ -1510,7 +1524,8 @@ template <int NB, int ND>
 static hipError_t run_chunked(const Params& p, hipStream_t s, Timing* tm) {
     const int nsub = (int)((p.T + 16 * NB - 1) / (16 * NB));
     tm_begin(tm, s, KPREP);
-    hipLaunchKernelGGL((gdn_prep_kernel<NB, ND>), dim3(8 * ((p.B * p.H + 7) / 8) * nsub), dim3(128 * NB), 0, s, p);
+    const int ngrp = (nsub + GDN_PREP_BLOCKS - 1) / GDN_PREP_BLOCKS;
+    hipLaunchKernelGGL((gdn_prep_kernel<NB, ND>), dim3(8 * ((p.B * p.H + 7) / 8) * ngrp), dim3(128 * NB), 0, s, p);
     tm_end(tm, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
