@@ -662,7 +662,8 @@ GDN_API int gdn_chunk_backward(gdn_stream* s, const gdn_io* io, const gdn_grad* 
     b.dbeta = g->dbeta;
     b.d_state0 = g->d_state0;
     b.states = s->bwd_ws;
-    b.partials = s->bwd_ws + (int64_t)s->cfg.batch * s->cfg.heads * (dv / 16) * (s->cfg.max_tokens + 1) * 16 * dk;
+    b.partials = s->bwd_ws + gdn::backward_ckpt_floats(s->cfg.batch, s->cfg.heads, dk, dv, s->cfg.max_tokens);
+    b.ck_per = gdn::backward_ckpt_per(s->cfg.max_tokens);
     b.reverse = reverse;
     hipError_t prior = hipPeekAtLastError();
     if (prior != hipSuccess) {

@@ -50,172 +50,361 @@ void tm_end(Timing* tm, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // Gradient of one scan (reverse-mode through the per-token rule), fp32 and
 // token-sequential: a reference-grade path for training over streaming chunks.
-// gdn_bwd_rows_kernel: one 64-lane workgroup per (b, h, block of 16 state rows),
-// lane l owns row 16 rb + l/4 and columns l%4 + 4i, as in gdn_seq_kernel.  It
-// runs the scan forward storing the state before every token, then walks the
-// tokens backward with G = dL/dS:
+// With G = dL/dS, walking the tokens backward (q_t, k_t normalised):
 //     G += scale do_t q_t^T,  x = S_{t-1} k_t,  gk = G k_t
 //     dv_t = beta_t gk,  da_t = <G, S_{t-1}> - beta_t gk.x,  dbeta_t = gk.(v_t - a_t x)
-//     dk_t = beta_t G^T v_t - a_t beta_t (S_{t-1}^T gk + G^T x),  dq_t = scale S_t^T do_t
+//     dk_t = beta_t G^T (v_t - a_t x) - a_t beta_t S_{t-1}^T gk,  dq_t = scale S_t^T do_t
 //     G <- a_t (G - beta_t gk k_t^T)
-// (q_t, k_t normalised).  dv and the start-state gradient are row-local; the
-// other gradients sum over all rows, so each workgroup writes its rows' partial
-// sums, and gdn_bwd_reduce_kernel adds them in a fixed order and maps the
-// normalised-vector gradients back through the L2 normalisation.
+// gdn_bwd_rows_kernel: one 64-lane workgroup per (b, h, block of 16 state rows);
+// lane l owns row 16 rb + l/4 and the columns 16 j + 4 (l%4) + e (e < 4) of every
+// 16-column group j, one float4 per group.  Tokens are staged through LDS in
+// blocks of TB (k and q normalised once per block; the next block's global loads
+// go out before the current block is worked on).  A forward pass keeps only the
+// state before every block (a checkpoint); the backward pass walks the blocks in
+// reverse, recomputes the states inside a block from its checkpoint into LDS and
+// then walks its tokens backward.  dv and the start-state gradient are row-local;
+// the other gradients sum over all rows: per token the rows' terms go through an
+// LDS buffer and each lane adds one float4 column group over the 16 rows in row
+// order, then the workgroup writes its rows' partial sums, and gdn_bwd_reduce_kernel
+// adds the row blocks in a fixed order and maps the normalised-vector gradients
+// back through the L2 normalisation.
 // ---------------------------------------------------------------------------
+constexpr int kMinTB = 14;   // smallest token block of any instance (sizes the checkpoints)
+
+int64_t backward_ckpt_per(int64_t max_tokens) { return (max_tokens + kMinTB - 1) / kMinTB + 1; }
+
+int64_t backward_ckpt_floats(int B, int H, int Dk, int Dv, int64_t max_tokens) {
+    return (int64_t)B * H * (Dv / 16) * backward_ckpt_per(max_tokens) * 16 * Dk;
+}
+
 int64_t backward_ws_bytes(int B, int H, int Dk, int Dv, int64_t max_tokens) {
     const int64_t nrb = Dv / 16;
     int64_t states = 0, partials = 0, total = 0;
     if (__builtin_mul_overflow((int64_t)B * H, nrb * 16 * Dk, &states) ||
-        __builtin_mul_overflow(states, max_tokens + 1, &states) ||
-        __builtin_mul_overflow((int64_t)B * H, nrb * (2 * Dk + 2), &partials) ||
+        __builtin_mul_overflow(states, backward_ckpt_per(max_tokens), &states) ||
+        __builtin_mul_overflow((int64_t)B * H, nrb * (2 * Dk + 4), &partials) ||
         __builtin_mul_overflow(partials, max_tokens, &partials) || __builtin_add_overflow(states, partials, &total) ||
         __builtin_mul_overflow(total, (int64_t)4, &total))
         return -1;
     return total;
 }
 
-// sum over the 16 rows of the workgroup (lane bits 2..5): within each row of 16 lanes by two
-// rotations (by 4, then by 8: lanes j, j-4, j-8, j-12), then across the four rows
+namespace {
+
+// sum over the 16 rows of the workgroup (lane bits 2..5): the four rows of each 16-lane DPP row
+// by two rotations (lanes j, j-4, j-8, j-12), then across the four DPP rows with lane swaps
 __device__ __forceinline__ float sum_rows(float x) {
     x += dpp<0x124>(x);   // row_ror:4
     x += dpp<0x128>(x);   // row_ror:8
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
+    const unsigned u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const unsigned w = __float_as_uint(x);
+    const auto c = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
-template <bool F32>
+__device__ __forceinline__ float dot4(const float4& a, const float4& b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; }
+// acc += a * b componentwise: four independent chains for a dot product over many float4
+__device__ __forceinline__ void fma4(float4& acc, const float4& a, const float4& b) {
+    acc.x += a.x * b.x;
+    acc.y += a.y * b.y;
+    acc.z += a.z * b.z;
+    acc.w += a.w * b.w;
+}
+__device__ __forceinline__ float hsum4(const float4& a) { return (a.x + a.y) + (a.z + a.w); }
+
+// raw buffer resource over [base, base + bytes); loads beyond it return zero
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Orders LDS accesses of the (single) wavefront around this point in the compiled code: lanes read
+// what other lanes wrote before it, and the LDS performs one wavefront's operations in order.
+__device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
+
+}  // namespace
+
+template <int NG, bool F32>
 __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g) {
-    constexpr int MAXC = 32;  // d_k <= 128
+    constexpr int DK = 16 * NG;               // d_k
+    constexpr int TB = NG == 8 ? 14 : 16;     // tokens per staged block (LDS: states of a block)
+    constexpr int NLQ = (TB * DK + 255) / 256;   // staged elements of k (and of q) per lane, 4 at a time
+    static_assert(TB >= kMinTB, "checkpoint sizing");
     const int lane = threadIdx.x, part = lane & 3, rl = lane >> 2;
     const int nrb = p.Dv / 16;
     int id = blockIdx.x;
-    const int rb = id % nrb; id /= nrb;
-    const int h = id % p.H; id /= p.H;
+    const int rb = id % nrb;
+    id /= nrb;
+    const int h = id % p.H;
+    id /= p.H;
     const int b = id;
     const int row = 16 * rb + rl;
-    const int nc = p.Dk / 4;
-    const int64_t T = p.T;
-    const int Dk = p.Dk;
-    float* st = g.states + (((int64_t)b * p.H + h) * nrb + rb) * (T + 1) * 16 * Dk;
-    auto sidx = [&](int64_t pi, int i) { return (pi * 16 + rl) * Dk + part + 4 * i; };
-    const int64_t srow = (((int64_t)b * p.H + h) * p.Dv + row) * Dk;
+    const int T = (int)p.T;
+    const int nblk = (T + TB - 1) / TB;
+    const int wid = 2 * DK + 4;
 
-    // token loads: the normalised k_t, q_t columns of this lane, a_t, beta_t, v_t[row]
-    auto load_token = [&](int64_t t, float* kv, float* qv, float& at, float& bt, float& vr) {
-        const int64_t kq = (int64_t)b * p.ks[0] + t * p.ks[1] + (int64_t)h * p.ks[2];
-        const int64_t qq = (int64_t)b * p.qs[0] + t * p.qs[1] + (int64_t)h * p.qs[2];
-        const int64_t vq = (int64_t)b * p.vs[0] + t * p.vs[1] + (int64_t)h * p.vs[2];
-        const int64_t gq = (int64_t)b * p.gs[0] + t * p.gs[1] + (int64_t)h * p.gs[2];
-        float sk = 0.f, sq = 0.f;
+    __shared__ __align__(16) float4 sst[TB][NG][64];   // S_{t-1} of the block's tokens, lane-major
+    __shared__ __align__(16) float skn[TB][DK];        // normalised k of the block's tokens
+    __shared__ __align__(16) float sqn[TB][DK];        // normalised q
+    __shared__ __align__(16) float scol[2][16][DK];    // per-row terms of dq and dk of one token
+    __shared__ float sv[TB][16], sdo[TB][16], sx[TB][16], sa[TB], sb[TB];
+
+    float* ck = g.states + (((int64_t)b * p.H + h) * nrb + rb) * g.ck_per * 16 * DK;
+    auto tok = [&](int pi) { return g.reverse ? T - 1 - pi : pi; };
+
+    // ---- staging: raw loads of a block into registers, then fp32 (normalised) into LDS ----
+    // Rows are read in 16-byte chunks through buffer resources over the (b, h) rows; chunks of
+    // tokens past the block or past T use an offset beyond the resource and read as zero.
+    constexpr int ESZ = F32 ? 4 : 2, EPC = 16 / ESZ;   // bytes per element, elements per chunk
+    constexpr int CPR = DK / EPC, NCH = TB * CPR;        // chunks per k/q row, per block
+    constexpr int NLC = (NCH + 63) / 64;                 // k (q) chunks per lane
+    constexpr int VCPR = 16 / EPC, NVC = TB * VCPR;      // chunks of a token's 16 v (d_o) values, per block
+    static_assert(NVC <= 64, "one v chunk per lane");
+    const char* kb = static_cast<const char*>(p.k) + ((int64_t)b * p.ks[0] + (int64_t)h * p.ks[2]) * ESZ;
+    const char* qb = static_cast<const char*>(p.q) + ((int64_t)b * p.qs[0] + (int64_t)h * p.qs[2]) * ESZ;
+    const char* vb = static_cast<const char*>(p.v) + ((int64_t)b * p.vs[0] + (int64_t)h * p.vs[2] + 16 * rb) * ESZ;
+    const char* ob = static_cast<const char*>(g.d_o) + ((int64_t)b * p.os[0] + (int64_t)h * p.os[2] + 16 * rb) * ESZ;
+    const auto krs = make_rsrc(kb, ((int64_t)(T - 1) * p.ks[1] + DK) * ESZ);
+    const auto qrs = make_rsrc(qb, ((int64_t)(T - 1) * p.qs[1] + DK) * ESZ);
+    const auto vrs = make_rsrc(vb, ((int64_t)(T - 1) * p.vs[1] + 16) * ESZ);
+    const auto ors = make_rsrc(ob, ((int64_t)(T - 1) * p.os[1] + 16) * ESZ);
+    const int ksb = (int)(p.ks[1] * ESZ), qsb = (int)(p.qs[1] * ESZ), vsb = (int)(p.vs[1] * ESZ), osb = (int)(p.os[1] * ESZ);
+    constexpr int OUT = (int)0x80000000;   // beyond every resource
+    uint4 rk[NLC], rq[NLC], rv = {0u, 0u, 0u, 0u}, rdo = {0u, 0u, 0u, 0u};
+    float ra = 1.f, rbt = 0.f;
+    auto load_block = [&](int blk, bool with_q) {
+        const int pi0 = blk * TB;
 #pragma unroll
-        for (int i = 0; i < MAXC; ++i) {
-            kv[i] = (i < nc) ? ld_elem<F32>(p.k, kq + part + 4 * i) : 0.f;
-            qv[i] = (i < nc) ? ld_elem<F32>(p.q, qq + part + 4 * i) : 0.f;
-            sk += kv[i] * kv[i];
-            sq += qv[i] * qv[i];
+        for (int i = 0; i < NLC; ++i) {
+            const int e = lane + 64 * i, ti = e / CPR, c = e - ti * CPR;
+            const bool ok = e < NCH && pi0 + ti < T;
+            const int t = ok ? tok(pi0 + ti) : 0;
+            rk[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, ok ? t * ksb + 16 * c : OUT, 0, 0));
+            if (with_q)
+                rq[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(qrs, ok ? t * qsb + 16 * c : OUT, 0, 0));
         }
-        if (p.l2norm) {
-            const float rk = 1.f / sqrtf(sum4(sk) + p.eps);
-            const float rq = 1.f / sqrtf(sum4(sq) + p.eps);
-#pragma unroll
-            for (int i = 0; i < MAXC; ++i) { kv[i] *= rk; qv[i] *= rq; }
+        {
+            const int ti = lane / VCPR, c = lane - ti * VCPR;
+            const bool ok = lane < NVC && pi0 + ti < T;
+            const int t = ok ? tok(pi0 + ti) : 0;
+            rv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, ok ? t * vsb + 16 * c : OUT, 0, 0));
+            if (with_q)
+                rdo = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ors, ok ? t * osb + 16 * c : OUT, 0, 0));
         }
-        at = p.gate_log ? expf(p.a[gq]) : p.a[gq];
-        bt = p.beta[gq];
-        vr = ld_elem<F32>(p.v, vq + row);
+        ra = 1.f;
+        rbt = 0.f;
+        if (lane < TB && pi0 + lane < T) {
+            const int64_t t = tok(pi0 + lane);
+            const int64_t gq = (int64_t)b * p.gs[0] + t * p.gs[1] + (int64_t)h * p.gs[2];
+            ra = p.gate_log ? expf(p.a[gq]) : p.a[gq];
+            rbt = p.beta[gq];
+        }
     };
-
-    // forward, keeping the state before every step (and the final one)
-    float S[MAXC];
+    // a 16-byte chunk of EPC elements as fp32, to dst (16-byte aligned)
+    auto put_chunk = [&](float* dst, const uint4& raw) {
+        if constexpr (F32) {
+            *reinterpret_cast<float4*>(dst) = __builtin_bit_cast(float4, raw);
+        } else {
+            const unsigned w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-    for (int i = 0; i < MAXC; ++i) S[i] = (i < nc && g.state0) ? g.state0[srow + part + 4 * i] : 0.f;
-    for (int64_t pi = 0; pi < T; ++pi) {
-#pragma unroll
-        for (int i = 0; i < MAXC; ++i)
-            if (i < nc) st[sidx(pi, i)] = S[i];
-        const int64_t t = g.reverse ? (T - 1 - pi) : pi;
-        float kv[MAXC], qv[MAXC], at, bt, vr;
-        load_token(t, kv, qv, at, bt, vr);
-        float x = 0.f;
-#pragma unroll
-        for (int i = 0; i < MAXC; ++i) x += S[i] * kv[i];
-        x = sum4(x);
-#pragma unroll
-        for (int i = 0; i < MAXC; ++i) S[i] = at * (S[i] - bt * x * kv[i]) + bt * vr * kv[i];
-    }
-#pragma unroll
-    for (int i = 0; i < MAXC; ++i)
-        if (i < nc) st[sidx(T, i)] = S[i];
-
-    // backward
-    float G[MAXC];
-#pragma unroll
-    for (int i = 0; i < MAXC; ++i) G[i] = (i < nc && g.d_state) ? g.d_state[srow + part + 4 * i] : 0.f;
-    const int wid = 2 * Dk + 2;
-    for (int64_t pi = T - 1; pi >= 0; --pi) {
-        const int64_t t = g.reverse ? (T - 1 - pi) : pi;
-        float kv[MAXC], qv[MAXC], at, bt, vr;
-        load_token(t, kv, qv, at, bt, vr);
-        const int64_t oq = (int64_t)b * p.os[0] + t * p.os[1] + (int64_t)h * p.os[2];
-        const float dor = p.scale * ld_elem<F32>(g.d_o, oq + row);
-        float Sp[MAXC], pq[MAXC], pk[MAXC];
-#pragma unroll
-        for (int i = 0; i < MAXC; ++i) {
-            Sp[i] = (i < nc) ? st[sidx(pi, i)] : 0.f;
-            pq[i] = (i < nc) ? dor * st[sidx(pi + 1, i)] : 0.f;   // scale do_t[row] S_t[row, c]
-            G[i] += dor * qv[i];
+            for (int k2 = 0; k2 < 2; ++k2)
+                *reinterpret_cast<float4*>(dst + 4 * k2) =
+                    float4{__uint_as_float(w[2 * k2] << 16), __uint_as_float(w[2 * k2] & 0xffff0000u),
+                           __uint_as_float(w[2 * k2 + 1] << 16), __uint_as_float(w[2 * k2 + 1] & 0xffff0000u)};
         }
-        float x = 0.f, gk = 0.f, gs = 0.f;
+    };
+    auto store_block = [&](bool with_q) {
 #pragma unroll
-        for (int i = 0; i < MAXC; ++i) {
-            x += Sp[i] * kv[i];
-            gk += G[i] * kv[i];
-            gs += G[i] * Sp[i];
-        }
-        x = sum4(x);
-        gk = sum4(gk);
-        gs = sum4(gs);
-        if (part == 0) g.dv[(((int64_t)b * T + t) * p.H + h) * p.Dv + row] = bt * gk;
-#pragma unroll
-        for (int i = 0; i < MAXC; ++i) {
-            pk[i] = bt * G[i] * vr - at * bt * (Sp[i] * gk + G[i] * x);
-            G[i] = at * (G[i] - bt * gk * kv[i]);
-        }
-        // per-row scalars: every lane of a row holds them; count each row once
-        float da = (part == 0) ? gs - bt * gk * x : 0.f;
-        float db = (part == 0) ? gk * (vr - at * x) : 0.f;
-        da = sum4(da);
-        db = sum4(db);
-        da = sum_rows(da);
-        db = sum_rows(db);
-#pragma unroll
-        for (int i = 0; i < MAXC; ++i) {
-            if (i < nc) {
-                pq[i] = sum_rows(pq[i]);
-                pk[i] = sum_rows(pk[i]);
+        for (int i = 0; i < NLC; ++i) {
+            const int e = lane + 64 * i, ti = e / CPR, c = e - ti * CPR;
+            if (e < NCH) {
+                put_chunk(&skn[ti][EPC * c], rk[i]);
+                if (with_q) put_chunk(&sqn[ti][EPC * c], rq[i]);
             }
         }
-        float* pw = g.partials + ((((int64_t)b * T + t) * p.H + h) * nrb + rb) * wid;
-        if (rl == 0) {
+        if (lane < NVC) {
+            const int ti = lane / VCPR, c = lane - ti * VCPR;
+            put_chunk(&sv[ti][EPC * c], rv);
+            if (with_q) put_chunk(&sdo[ti][EPC * c], rdo);
+        }
+        if (lane < TB) {
+            sa[lane] = ra;
+            sb[lane] = rbt;
+        }
+        lds_order();
+        // normalise the rows in place: lanes 4 r + q (r < TB) sum row r of k (q = 0, 1) or of q
+        // (q = 2, 3) over half the columns each, combined across the lane pair
+        if (p.l2norm) {
+            const int r = lane >> 2, which = (lane >> 1) & 1, half = lane & 1;
+            float* rowp = (which ? &sqn[0][0] : &skn[0][0]) + r * DK + half * (DK / 2);
+            float ss = 0.f;
+            if (r < TB && (with_q || !which)) {
 #pragma unroll
-            for (int i = 0; i < MAXC; ++i) {
-                if (i < nc) {
-                    pw[part + 4 * i] = pq[i];
-                    pw[Dk + part + 4 * i] = pk[i];
+                for (int c = 0; c < DK / 2; c += 4) {
+                    const float4 x = *reinterpret_cast<const float4*>(rowp + c);
+                    ss += dot4(x, x);
                 }
             }
-            if (part == 0) {
-                pw[2 * Dk] = da;
-                pw[2 * Dk + 1] = db;
+            ss += dpp<0xB1>(ss);   // lane pair: quad permutation [1,0,3,2]
+            // rows past the end of the sequence are zero and stay zero
+            const float sc = ss + p.eps > 0.f ? 1.f / sqrtf(ss + p.eps) : 0.f;
+            if (r < TB && (with_q || !which)) {
+#pragma unroll
+                for (int c = 0; c < DK / 2; c += 4) {
+                    float4 x = *reinterpret_cast<const float4*>(rowp + c);
+                    x.x *= sc; x.y *= sc; x.z *= sc; x.w *= sc;
+                    *reinterpret_cast<float4*>(rowp + c) = x;
+                }
             }
+        }
+        lds_order();
+    };
+    // columns of this lane in staged row r: 16 j + 4 part .. +3
+    auto krow = [&](int r, int j) { return *reinterpret_cast<const float4*>(&skn[r][16 * j + 4 * part]); };
+    auto qrow = [&](int r, int j) { return *reinterpret_cast<const float4*>(&sqn[r][16 * j + 4 * part]); };
+    auto ckp = [&](int blk, int j) { return reinterpret_cast<float4*>(ck + ((int64_t)blk * 16 + rl) * DK + 16 * j + 4 * part); };
+
+    // one token of the forward recurrence on S (row dot and update); returns x = S k
+    float4 S[NG];
+    auto fwd_token = [&](int r) {
+        float4 kr[NG];
+#pragma unroll
+        for (int j = 0; j < NG; ++j) kr[j] = krow(r, j);
+        const float at = sa[r], bt = sb[r], vr = sv[r][rl];
+        float4 xa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < NG; ++j) fma4(xa, S[j], kr[j]);
+        const float x = sum4(hsum4(xa));
+        const float c0 = bt * x, c1 = bt * vr;
+#pragma unroll
+        for (int j = 0; j < NG; ++j) {
+            const float4 kk = kr[j];
+            S[j].x = at * (S[j].x - c0 * kk.x) + c1 * kk.x;
+            S[j].y = at * (S[j].y - c0 * kk.y) + c1 * kk.y;
+            S[j].z = at * (S[j].z - c0 * kk.z) + c1 * kk.z;
+            S[j].w = at * (S[j].w - c0 * kk.w) + c1 * kk.w;
+        }
+        return x;
+    };
+
+    // ---- forward: checkpoints before every block ----
+#pragma unroll
+    for (int j = 0; j < NG; ++j)
+        S[j] = g.state0 ? *reinterpret_cast<const float4*>(g.state0 + (((int64_t)b * p.H + h) * p.Dv + row) * DK + 16 * j + 4 * part)
+                        : float4{0.f, 0.f, 0.f, 0.f};
+    if (nblk > 0) load_block(0, false);
+    for (int blk = 0; blk < nblk; ++blk) {
+        store_block(false);
+        if (blk + 1 < nblk) load_block(blk + 1, false);
+#pragma unroll
+        for (int j = 0; j < NG; ++j) *ckp(blk, j) = S[j];
+        const int n = min(TB, T - blk * TB);
+        for (int r = 0; r < n; ++r) (void)fwd_token(r);
+    }
+
+    // ---- backward over the blocks in reverse ----
+    float4 G[NG];
+#pragma unroll
+    for (int j = 0; j < NG; ++j)
+        G[j] = g.d_state ? *reinterpret_cast<const float4*>(g.d_state + (((int64_t)b * p.H + h) * p.Dv + row) * DK + 16 * j + 4 * part)
+                         : float4{0.f, 0.f, 0.f, 0.f};
+    if (nblk > 0) load_block(nblk - 1, true);
+    for (int blk = nblk - 1; blk >= 0; --blk) {
+        store_block(true);
+        if (blk > 0) load_block(blk - 1, true);
+        const int n = min(TB, T - blk * TB);
+        // recompute the block's states from its checkpoint: S_{t-1} of each token into LDS
+#pragma unroll
+        for (int j = 0; j < NG; ++j) S[j] = *ckp(blk, j);
+        for (int r = 0; r < n; ++r) {
+#pragma unroll
+            for (int j = 0; j < NG; ++j) sst[r][j][lane] = S[j];
+            const float x = fwd_token(r);
+            if (part == 0) sx[r][rl] = x;
+        }
+        // S is the state after the block's last token; walk the block's tokens backward
+        for (int r = n - 1; r >= 0; --r) {
+            const int64_t t = tok(blk * TB + r);
+            // every LDS operand of the token first, then the arithmetic
+            float4 Sp[NG], kr[NG], qr[NG];
+#pragma unroll
+            for (int j = 0; j < NG; ++j) {
+                Sp[j] = sst[r][j][lane];
+                kr[j] = krow(r, j);
+                qr[j] = qrow(r, j);
+            }
+            const float dor = p.scale * sdo[r][rl];
+            const float at = sa[r], bt = sb[r], vr = sv[r][rl], x = sx[r][rl];
+#pragma unroll
+            for (int j = 0; j < NG; ++j) {
+                const float4 qq = qr[j];
+                G[j].x += dor * qq.x;
+                G[j].y += dor * qq.y;
+                G[j].z += dor * qq.z;
+                G[j].w += dor * qq.w;
+            }
+            float4 gka = {0.f, 0.f, 0.f, 0.f}, gsa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < NG; ++j) {
+                fma4(gka, G[j], kr[j]);
+                fma4(gsa, G[j], Sp[j]);
+            }
+            const float gk = sum4(hsum4(gka)), gs = sum4(hsum4(gsa));
+            if (part == 0) g.dv[(((int64_t)b * T + t) * p.H + h) * p.Dv + row] = bt * gk;
+            // this row's terms of dq_t = scale S_t^T do_t and dk_t = beta G^T (v - a x) - a beta S_{t-1}^T gk
+            const float wv = bt * (vr - at * x), ws = at * bt * gk;
+#pragma unroll
+            for (int j = 0; j < NG; ++j) {
+                *reinterpret_cast<float4*>(&scol[0][rl][16 * j + 4 * part]) =
+                    float4{dor * S[j].x, dor * S[j].y, dor * S[j].z, dor * S[j].w};
+                *reinterpret_cast<float4*>(&scol[1][rl][16 * j + 4 * part]) =
+                    float4{wv * G[j].x - ws * Sp[j].x, wv * G[j].y - ws * Sp[j].y, wv * G[j].z - ws * Sp[j].z,
+                           wv * G[j].w - ws * Sp[j].w};
+            }
+            lds_order();
+            const float cg = bt * gk;
+#pragma unroll
+            for (int j = 0; j < NG; ++j) {
+                const float4 kk = kr[j];
+                G[j].x = at * (G[j].x - cg * kk.x);
+                G[j].y = at * (G[j].y - cg * kk.y);
+                G[j].z = at * (G[j].z - cg * kk.z);
+                G[j].w = at * (G[j].w - cg * kk.w);
+            }
+            // per-row scalars (identical in the 4 lanes of a row; counted once)
+            float da = (part == 0) ? gs - bt * gk * x : 0.f;
+            float db = (part == 0) ? gk * (vr - at * x) : 0.f;
+            da = sum_rows(da);
+            db = sum_rows(db);
+            float* pw = g.partials + ((((int64_t)b * T + t) * p.H + h) * nrb + rb) * wid;
+            // column sums over the 16 rows, in row order: lane l adds float4 group l
+            if (lane < DK / 2) {
+                const int a = lane / (DK / 4), c4 = 4 * (lane - a * (DK / 4));
+                float4 acc = *reinterpret_cast<const float4*>(&scol[a][0][c4]);
+#pragma unroll
+                for (int rr = 1; rr < 16; ++rr) {
+                    const float4 v4 = *reinterpret_cast<const float4*>(&scol[a][rr][c4]);
+                    acc.x += v4.x;
+                    acc.y += v4.y;
+                    acc.z += v4.z;
+                    acc.w += v4.w;
+                }
+                *reinterpret_cast<float4*>(pw + a * DK + c4) = acc;
+            }
+            if (lane == 0) {
+                pw[2 * DK] = da;
+                pw[2 * DK + 1] = db;
+            }
+            lds_order();
+#pragma unroll
+            for (int j = 0; j < NG; ++j) S[j] = Sp[j];
         }
     }
     if (g.d_state0) {
 #pragma unroll
-        for (int i = 0; i < MAXC; ++i)
-            if (i < nc) g.d_state0[srow + part + 4 * i] = G[i];
+        for (int j = 0; j < NG; ++j)
+            *reinterpret_cast<float4*>(g.d_state0 + (((int64_t)b * p.H + h) * p.Dv + row) * DK + 16 * j + 4 * part) = G[j];
     }
 }
 
@@ -235,7 +424,7 @@ __global__ __launch_bounds__(64) void gdn_bwd_reduce_kernel(Params p, BwdParams 
     const int h = (int)(id % p.H); id /= p.H;
     const int64_t t = id % p.T; id /= p.T;
     const int b = (int)id;
-    const int Dk = p.Dk, nrb = p.Dv / 16, wid = 2 * Dk + 2;
+    const int Dk = p.Dk, nrb = p.Dv / 16, wid = 2 * Dk + 4;
     const float* pw = g.partials + (((int64_t)b * p.T + t) * p.H + h) * nrb * wid;
     float gq[2] = {0.f, 0.f}, gkk[2] = {0.f, 0.f}, da = 0.f, db = 0.f;
     for (int r = 0; r < nrb; ++r) {
@@ -288,13 +477,32 @@ __global__ __launch_bounds__(64) void gdn_bwd_reduce_kernel(Params p, BwdParams 
     }
 }
 
+template <int NG>
+static void launch_rows_ng(const Params& p, const BwdParams& g, hipStream_t s, int grid) {
+    if (p.io_f32) hipLaunchKernelGGL((gdn_bwd_rows_kernel<NG, true>), dim3(grid), dim3(64), 0, s, p, g);
+    else hipLaunchKernelGGL((gdn_bwd_rows_kernel<NG, false>), dim3(grid), dim3(64), 0, s, p, g);
+}
+
+static hipError_t launch_rows(const Params& p, const BwdParams& g, hipStream_t s, int grid) {
+    switch (p.Dk) {
+        case 16: launch_rows_ng<1>(p, g, s, grid); break;
+        case 32: launch_rows_ng<2>(p, g, s, grid); break;
+        case 48: launch_rows_ng<3>(p, g, s, grid); break;
+        case 64: launch_rows_ng<4>(p, g, s, grid); break;
+        case 80: launch_rows_ng<5>(p, g, s, grid); break;
+        case 96: launch_rows_ng<6>(p, g, s, grid); break;
+        case 112: launch_rows_ng<7>(p, g, s, grid); break;
+        case 128: launch_rows_ng<8>(p, g, s, grid); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_backward(const Params& p, const BwdParams& g, hipStream_t s, Timing* tm) {
     const int rows_grid = p.B * p.H * (p.Dv / 16);
     const int64_t red_grid = (int64_t)p.B * p.T * p.H;
     tm_begin(tm, s, KBWD);
-    if (p.io_f32) hipLaunchKernelGGL(gdn_bwd_rows_kernel<true>, dim3(rows_grid), dim3(64), 0, s, p, g);
-    else hipLaunchKernelGGL(gdn_bwd_rows_kernel<false>, dim3(rows_grid), dim3(64), 0, s, p, g);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_rows(p, g, s, rows_grid);
     if (e == hipSuccess && red_grid > 0) {
         if (p.io_f32) hipLaunchKernelGGL(gdn_bwd_reduce_kernel<true>, dim3((unsigned)red_grid), dim3(64), 0, s, p, g);
         else hipLaunchKernelGGL(gdn_bwd_reduce_kernel<false>, dim3((unsigned)red_grid), dim3(64), 0, s, p, g);

@@ -41,8 +41,9 @@ struct Params {
 // Bytes of one workspace item for sub-chunk C (multiple of 16, 16..64).
 int64_t chunk_item_bytes(int C, int D);
 
-// Gradient of one token-sequential scan (fp32).  Workspace (owned by the handle):
-// states [B][H][Dv/16][T+1][16][Dk] and partial sums [B][T][H][Dv/16][2 Dk + 2].
+// Gradient of one token-sequential scan (fp32).  Workspace (owned by the handle): state
+// checkpoints [B][H][Dv/16][ck_per][16][Dk] (the state before every staged block of tokens)
+// and partial sums [B][T][H][Dv/16][2 Dk + 4].
 struct BwdParams {
     const void* d_o;       // dL/do, io dtype, o's strides (Params::os)
     const float* d_state;  // dL/d(final state) [B, H, Dv, Dk], or null
@@ -53,12 +54,17 @@ struct BwdParams {
     float* da;             // [B, T, H]
     float* dbeta;          // [B, T, H]
     float* d_state0;       // [B, H, Dv, Dk], or null
-    float* states;
+    float* states;         // checkpoints
     float* partials;
+    int64_t ck_per;        // checkpoints per (b, h, row block) in `states`
     int reverse;           // 0: the forward scan (t ascending), 1: the reverse scan
 };
 // Bytes of the backward workspace for max_tokens tokens, or -1 if the size overflows int64.
 int64_t backward_ws_bytes(int B, int H, int Dk, int Dv, int64_t max_tokens);
+// Checkpoints per (b, h, row block) for max_tokens tokens, and the floats they take in all
+// (where the partial sums start in the workspace).
+int64_t backward_ckpt_per(int64_t max_tokens);
+int64_t backward_ckpt_floats(int B, int H, int Dk, int Dv, int64_t max_tokens);
 
 // Which (C, D) pairs the chunked kernels are built for.
 bool chunked_supported(int C, int Dk, int Dv, int io_f32);
