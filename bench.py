@@ -56,6 +56,12 @@ KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_streaming_amd", "csrc", "gdn_ker
 ATTN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_720p.json")
 ATTN_TRACE_FILE = os.path.join(ROOT, "profiles", "trace_attn_720p.json")
 ATTN_KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_streaming_amd", "csrc", "gdn_attention.hip")
+LOWP_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_e4m3_720p.json")
+LOWP_TRACE_FILE = os.path.join(ROOT, "profiles", "trace_gemm_e4m3_720p.json")
+LOWP_KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_streaming_amd", "csrc", "gdn_lowp.hip")
+MFMA_FP8_PEAK_TFLOPS = 5000.0    # dense fp8
+KERNEL_NAMES = ("gdn_prep_kernel", "gdn_scan_kernel", "attn_kernel", "attn_append_kernel", "gemm_e4m3_kernel",
+                "quantize_rows_vec_kernel", "quantize_rows_kernel")
 
 
 def kernel_source_hash(src: str = KERNEL_SRC) -> str:
@@ -111,7 +117,7 @@ def load_trace(path: str = TRACE_FILE, src: str = KERNEL_SRC):
 
 
 def _short_kernel_name(name: str) -> str:
-    for k in ("gdn_prep_kernel", "gdn_scan_kernel", "attn_kernel", "attn_append_kernel"):
+    for k in KERNEL_NAMES:
         if k in name:
             return k
     return name
@@ -142,7 +148,7 @@ def summarize_rocprof(kind: str, dirs, out_path: str, src: str) -> None:
     if kind == "trace":
         for r in rows(dirs[0], "*kernel_stats.csv"):
             k = _short_kernel_name(r["Name"])
-            if k.startswith(("gdn_", "attn_")):
+            if k in KERNEL_NAMES:
                 rec["kernels"][k] = {"calls": int(r["Calls"]), "average_us": round(float(r["AverageNs"]) / 1e3, 3),
                                      "min_us": round(float(r["MinNs"]) / 1e3, 3),
                                      "max_us": round(float(r["MaxNs"]) / 1e3, 3)}
@@ -167,7 +173,7 @@ def summarize_rocprof(kind: str, dirs, out_path: str, src: str) -> None:
             rec[f"copy_probe_{counter}_KiB"] = copy[0]
             for n, v in by_kernel.items():
                 k = _short_kernel_name(n)
-                if k.startswith(("gdn_", "attn_")):
+                if k in KERNEL_NAMES:
                     per.setdefault(k, {})[counter] = (statistics.median(v), len(v))
         for k, c in per.items():
             f_kib, n = c.get("FETCH_SIZE", (0.0, 0))
@@ -239,16 +245,45 @@ def measured_peaks(torch, dev):
                    "chains per wavefront, 2 wavefronts per SIMD, average of 10 launches"}
 
 
+def measured_peaks_lowp(torch, dev):
+    """A dense fp8 (E4M3) MFMA loop (two wavefronts per SIMD) and the LDS read rate of 16-byte reads (eight
+    wavefronts per CU, no bank conflicts), both hand-written HIP in libgdn_peaks.so: the MFMA rate the fp8
+    GEMM is quoted against, and the LDS rate that bounds it."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "gated_deltanet_streaming_amd", "libgdn_peaks.so"))
+    for fn in (lib.gdn_peak_mfma_fp8, lib.gdn_peak_lds_read):
+        fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                       ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double)]
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(2 * cus * 512, dtype=torch.float32, device=dev)
+    ms, amount = ctypes.c_float(), ctypes.c_double()
+    if lib.gdn_peak_mfma_fp8(2 * cus, 2000, 10, out.data_ptr(), stream, ctypes.byref(ms), ctypes.byref(amount)) != 0:
+        raise RuntimeError("fp8 MFMA probe failed")
+    fp8 = amount.value / (ms.value * 1e-3) / 1e12
+    if lib.gdn_peak_lds_read(cus, 2000, 10, out.data_ptr(), stream, ctypes.byref(ms), ctypes.byref(amount)) != 0:
+        raise RuntimeError("LDS probe failed")
+    torch.cuda.synchronize()
+    lds = amount.value / (ms.value * 1e-3)
+    return {"mfma_fp8_TFLOPs": round(fp8, 1), "mfma_fp8_frac_of_vendor": round(fp8 / MFMA_FP8_PEAK_TFLOPS, 4),
+            "lds_read_GBs_per_cu": round(lds / cus / 1e9, 1),
+            "lds_read_bytes_per_clock_per_cu_at_2400MHz": round(lds / cus / 2.4e9, 1), "compute_units": cus,
+            "how": "fp8: 16x16x128 E4M3 MFMAs, 8 independent chains per wavefront, 2 wavefronts per SIMD; LDS: 16-byte "
+                   "reads of 1 KB contiguous per wavefront instruction, 8 wavefronts per CU, one workgroup per CU"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--mode", choices=["bidir", "separate", "long", "backward", "attention"], default="bidir",
+    ap.add_argument("--mode", choices=["bidir", "separate", "long", "backward", "attention", "lowp"], default="bidir",
                     help="bidir: one gdn_chunk_bidir call per step; separate: forward then reverse calls; "
                          "long: gdn_chunk_bidir on a 21-frame clip (T = 18480); "
                          "backward: the gradients of both scans of the pair (gdn_chunk_backward); "
-                         "attention: the softmax block's sink + window attention (gdn_attn_chunk)")
+                         "attention: the softmax block's sink + window attention (gdn_attn_chunk); "
+                         "lowp: the GDN block's fused q/k/v projection as an E4M3 GEMM (gdn_quantize_rows_e4m3 + "
+                         "gdn_gemm_e4m3)")
     ap.add_argument("--sets", type=int, default=6, help="rotating input/output buffer sets (1 = warm)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-peaks", action="store_true", help="skip the copy / MFMA peak probes")
@@ -256,18 +291,21 @@ def main():
                     help="also run a 256 MiB device copy (reference for counter scaling)")
     ap.add_argument("--summarize", nargs="+", metavar=("KIND", "DIR"),
                     help="no GPU run: write the committed summary record of rocprofv3 csv output; "
-                         "'traffic FETCH_DIR WRITE_DIR [attn]' or 'trace TRACE_DIR [attn]'")
+                         "'traffic FETCH_DIR WRITE_DIR [attn|lowp]' or 'trace TRACE_DIR [attn|lowp]'")
     args = ap.parse_args()
 
     if args.summarize:
         kind, rest = args.summarize[0], args.summarize[1:]
-        attn = rest and rest[-1] == "attn"
-        dirs = rest[:-1] if attn else rest
+        tag = rest[-1] if rest and rest[-1] in ("attn", "lowp") else None
+        dirs = rest[:-1] if tag else rest
         if kind not in ("traffic", "trace") or len(dirs) != (2 if kind == "traffic" else 1):
-            raise SystemExit("--summarize traffic FETCH_DIR WRITE_DIR [attn] | trace TRACE_DIR [attn]")
-        if attn:
+            raise SystemExit("--summarize traffic FETCH_DIR WRITE_DIR [attn|lowp] | trace TRACE_DIR [attn|lowp]")
+        if tag == "attn":
             out = ATTN_TRAFFIC_FILE if kind == "traffic" else ATTN_TRACE_FILE
             src = ATTN_KERNEL_SRC
+        elif tag == "lowp":
+            out = LOWP_TRAFFIC_FILE if kind == "traffic" else LOWP_TRACE_FILE
+            src = LOWP_KERNEL_SRC
         else:
             out, src = (TRAFFIC_FILE if kind == "traffic" else TRACE_FILE), KERNEL_SRC
         return summarize_rocprof(kind, dirs, out, src)
@@ -281,6 +319,8 @@ def main():
         return main_backward(args)
     if args.mode == "attention":
         return main_attention(args)
+    if args.mode == "lowp":
+        return main_lowp(args)
 
     import numpy as np
     import torch
@@ -633,6 +673,118 @@ def main_attention(args):
                                "sample": f"{hs} of {H} heads of one steady-state chunk ({L} keys), numpy fp64 "
                                          f"matmuls, {reps} repetitions ({dt:.2f} s per step)"}
     att.close()
+    print(json.dumps(out), flush=True)
+
+
+def main_lowp(args):
+    """The GDN block's fused q/k/v projection at the 720p layer shape as an FP8 (E4M3) GEMM: X [2640 tokens x
+    2240] bf16 times W [6720 = 3 x 2240 features x 2240]^T, weights quantised once beforehand (as a deployed model
+    stores them).  One step = per-token quantisation of X (gdn_quantize_rows_e4m3) + the GEMM (gdn_gemm_e4m3),
+    bf16 out.  The roofline is the GEMM kernel's: 2 M N K flops per launch against the dense fp8 peak."""
+    import numpy as np
+    import torch
+
+    import gdn_inputs
+    from gated_deltanet_streaming_amd import binding as gb
+
+    M, K, N = T, H * D, 3 * H * D
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    nsets = max(1, args.sets)
+    xs, ys = [], []
+    x0, w = gdn_inputs.proj_inputs(0, M, K, N)
+    for i in range(nsets):
+        xi = x0 if i == 0 else gdn_inputs.proj_inputs(i, M, K, N)[0]
+        xs.append(torch.from_numpy(xi.astype(np.float32)).to(dev, torch.bfloat16))
+        ys.append(torch.empty((M, N), dtype=torch.bfloat16, device=dev))
+    wq, ws = gb.quantize_rows_e4m3(torch.from_numpy(w.astype(np.float32)).to(dev, torch.bfloat16))
+    xq = [gb.e4m3_codes_empty(M, K, dev) for _ in range(nsets)]
+    xsc = [torch.empty(M, dtype=torch.float32, device=dev) for _ in range(nsets)]
+    stream = torch.cuda.current_stream(dev)
+    n = [0]
+
+    def step():
+        i = n[0] % nsets
+        n[0] += 1
+        gb.quantize_rows_e4m3(xs[i], codes=xq[i], scales=xsc[i], stream=stream)
+        gb.gemm_e4m3(xq[i], xsc[i], wq, ws, ys[i], stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - w0) * 1e3 / args.steps
+    # the GEMM kernel alone, HIP events on its launch stream (the current stream)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for j in range(args.steps):
+        gb.gemm_e4m3(xq[j % nsets], xsc[j % nsets], wq, ws, ys[j % nsets], stream=stream)
+    ev1.record(stream)
+    ev1.synchronize()
+    gemm_ms = ev0.elapsed_time(ev1) / args.steps
+    ev0.record(stream)
+    for j in range(args.steps):
+        gb.quantize_rows_e4m3(xs[j % nsets], codes=xq[j % nsets], scales=xsc[j % nsets], stream=stream)
+    ev1.record(stream)
+    ev1.synchronize()
+    quant_ms = ev0.elapsed_time(ev1) / args.steps
+    if args.copy_probe:   # a 256 MiB device copy: the reference that scales the byte counters
+        src = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+    flops = 2.0 * M * N * K
+    achieved = flops / (gemm_ms * 1e-3) / 1e12
+    quant_bytes = M * K * 2 + M * K + M * 4            # bf16 X read, codes and scales written
+    gemm_bytes = M * K + N * K + (M + N) * 4 + M * N * 2   # codes and scales read once, bf16 Y written
+    traffic = load_traffic(LOWP_TRAFFIC_FILE, LOWP_KERNEL_SRC) or {}
+    trace = load_trace(LOWP_TRACE_FILE, LOWP_KERNEL_SRC) or {}
+    out = {
+        "metric": "GDN block q/k/v projection tokens/s at 2640-token 720p chunk (E4M3 GEMM); % of fp8 MFMA roofline",
+        "value": round(M / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8-e4m3 (fp32 accumulate, bf16 out)", "data": "synthetic",
+        "config": {"workload": "720p streaming chunk, the GDN block's fused q/k/v projection: 2640 tokens x 2240 "
+                               "in, 6720 out", "M": M, "K": K, "N": N,
+                   "call": "gdn_quantize_rows_e4m3 (activations) + gdn_gemm_e4m3; weights quantised once"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_FP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4),
+                     "traffic": traffic.get("gemm_e4m3_kernel"),
+                     "kernel": "gemm_e4m3_kernel", "kernel_avg_us": round(gemm_ms * 1e3, 2),
+                     "trace_avg_us": trace.get("gemm_e4m3_kernel"),
+                     "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": gemm_bytes,
+                     "quantize": {"kernel": "quantize_rows_vec_kernel", "kernel_avg_us": round(quant_ms * 1e3, 2),
+                                  "trace_avg_us": trace.get("quantize_rows_vec_kernel"),
+                                  "algorithmic_bytes_per_launch": quant_bytes, "bound": "hbm",
+                                  "achieved_GBs": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
+                                  "traffic": traffic.get("quantize_rows_vec_kernel")}},
+    }
+    if not args.no_peaks:
+        out["measured_peaks"] = measured_peaks_lowp(torch, dev)
+    if not args.no_cpu:
+        from oracle import lowp_gemm
+        import threadpoolctl
+        rows = 512   # a bounded sample: 512 of the 2640 tokens against the whole weight
+        xr = x0[:rows].astype(np.float32)
+        wcodes, wscales = lowp_gemm.quantize_rows(w.astype(np.float32))
+        reps, t0 = 0, time.perf_counter()
+        while reps == 0 or time.perf_counter() - t0 < 10.0:
+            c, sc = lowp_gemm.quantize_rows(xr)
+            lowp_gemm.bf16_round(lowp_gemm.gemm_e4m3(c, sc, wcodes, wscales))
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+        blas = [p["num_threads"] for p in threadpoolctl.threadpool_info() if p.get("user_api") == "blas"]
+        out["cpu_baseline"] = {"value": round(rows / dt, 1), "unit": "tokens/s",
+                               "cores": max(blas) if blas else 1, "kind": "oracle",
+                               "sample": f"{rows} of {M} tokens: per-row quantisation + fp64 GEMM of the decoded "
+                                         f"codes against all {N} features, {reps} repetitions ({dt:.2f} s each)"}
     print(json.dumps(out), flush=True)
 
 

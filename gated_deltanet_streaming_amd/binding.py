@@ -105,6 +105,8 @@ def load_library():
         "gdn_attn_cache_set": ([vp, vp, i64, i64, vp], i32),
         "gdn_attn_profile": ([vp, i32], i32),
         "gdn_attn_profile_read": ([vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), i32], i32),
+        "gdn_quantize_rows_e4m3": ([vp, i32, i64, i64, i64, vp, i64, vp, vp], i32),
+        "gdn_gemm_e4m3": ([vp, i64, vp, vp, i64, vp, i64, i64, i64, vp, i64, vp], i32),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -416,3 +418,48 @@ class WindowAttention:
             self.close()
         except Exception:
             pass
+
+
+# ---- FP8 (E4M3) projection GEMMs ---------------------------------------------------------------------
+
+def e4m3_codes_empty(rows, cols, device):
+    """An uninitialised uint8 [rows, cols] code matrix whose row stride is cols rounded up to a multiple of 128
+    bytes: the GEMM reads each row in 128-byte k steps, and rows that start on a 128-byte boundary take one
+    cache line per step instead of two."""
+    import torch
+    return torch.empty((rows, (cols + 127) // 128 * 128), dtype=torch.uint8, device=device)[:, :cols]
+
+
+def quantize_rows_e4m3(x, codes=None, scales=None, *, stream=None):
+    """Per-row E4M3 quantisation of a 2-D bf16 or fp32 tensor with a contiguous last dimension; returns
+    (codes uint8 [rows, cols], scales fp32 [rows]).  New code matrices come from e4m3_codes_empty."""
+    import torch
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with a contiguous last dimension")
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("x must be bf16 or fp32")
+    rows, cols = x.shape
+    if codes is None:
+        codes = e4m3_codes_empty(rows, cols, x.device)
+    if scales is None:
+        scales = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _check(load_library().gdn_quantize_rows_e4m3(_ptr(x), GDN_F32 if x.dtype == torch.float32 else GDN_BF16, rows, cols,
+                                                 x.stride(0), _ptr(codes), codes.stride(0), _ptr(scales),
+                                                 _stream_ptr(stream, x.device)))
+    return codes, scales
+
+
+def gemm_e4m3(x_codes, x_scales, w_codes, w_scales, y=None, *, stream=None):
+    """y [M, N] bf16 = diag(x_scales) dec(x_codes) dec(w_codes)^T diag(w_scales) for E4M3 codes x [M, K] and
+    w [N, K] (uint8, contiguous last dimension)."""
+    import torch
+    M, K = x_codes.shape
+    N = w_codes.shape[0]
+    if w_codes.shape[1] != K:
+        raise ValueError("x and w must share K")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x_codes.device)
+    _check(load_library().gdn_gemm_e4m3(_ptr(x_codes), x_codes.stride(0), _ptr(x_scales), _ptr(w_codes),
+                                        w_codes.stride(0), _ptr(w_scales), M, N, K, _ptr(y), y.stride(0),
+                                        _stream_ptr(stream, x_codes.device)))
+    return y

@@ -12,34 +12,63 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgdn_stream.so")
 SOURCES = [os.path.join(CSRC, "gdn_kernels.hip"), os.path.join(CSRC, "gdn_backward.hip"),
-           os.path.join(CSRC, "gdn_attention.hip"), os.path.join(CSRC, "gdn_api.cpp")]
+           os.path.join(CSRC, "gdn_attention.hip"), os.path.join(CSRC, "gdn_lowp.hip"), os.path.join(CSRC, "gdn_api.cpp")]
 PEAKS_LIB = os.path.join(PKG, "libgdn_peaks.so")
 PEAKS_SOURCES = [os.path.join(CSRC, "gdn_peaks.hip")]
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     # keep the compiler from forming packed fp32 ops (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA results and accumulators in ordinary VGPRs: the scan scales and converts its
-    # accumulators every step, which with accumulation registers costs a copy per value
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-result",
 ]
+# MFMA results and accumulators in ordinary VGPRs: the scan scales and converts its accumulators every step,
+# which with accumulation registers costs a copy per value.  Not for the FP8 GEMM, whose 144 accumulators per
+# wavefront live in the accumulation registers (one wavefront per SIMD, 512 registers).
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+NO_VGPR_FORM = {"gdn_lowp.hip"}
+
+
+def _flags(src: str) -> list:
+    return HIPCC_FLAGS + ([] if os.path.basename(src) in NO_VGPR_FORM else VGPR_FORM)
+
+
+def _hipcc() -> str:
+    return os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
 def command(out: str = LIB, sources=None) -> list:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    return [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", out, *(sources or SOURCES)]
+    """The link command of a library from its sources' objects (object of s: out + '.' + basename(s) + '.o')."""
+    objs = [out + "." + os.path.basename(s) + ".o" for s in (sources or SOURCES)]
+    return [_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", out, *objs]
 
 
 def _build_one(lib: str, sources, verbose: bool) -> str:
     tmp = lib + ".tmp"
-    res = subprocess.run(command(tmp, sources), capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
-    if verbose:
-        print(res.stderr)
-    os.replace(tmp, lib)
+    procs = []
+    for src in sources:
+        obj = tmp + "." + os.path.basename(src) + ".o"
+        cmd = [_hipcc(), *_flags(src), "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+        procs.append((src, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+    errors, objs = [], []
+    for src, obj, p in procs:
+        out, err = p.communicate()
+        if p.returncode != 0:
+            errors.append(f"{src}:\n{out}{err}")
+        elif verbose:
+            print(err)
+        objs.append(obj)
+    try:
+        if errors:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(errors))
+        res = subprocess.run(command(tmp, sources), capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("hipcc link failed:\n" + res.stdout + res.stderr)
+        os.replace(tmp, lib)
+    finally:
+        for obj in objs:
+            if os.path.exists(obj):
+                os.remove(obj)
     return lib
 
 

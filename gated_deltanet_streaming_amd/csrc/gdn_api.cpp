@@ -23,6 +23,7 @@
 
 #include "gdn_internal.h"
 #include "gdn_attn.h"
+#include "gdn_lowp.h"
 #include "gdn_stream.h"
 
 struct gdn_stream {
@@ -943,6 +944,76 @@ GDN_API int gdn_attn_profile_read(gdn_attn* a, double* ms, int64_t* launches, in
         a->acc_n = 0;
     }
     return ok();
+}
+
+// ---- FP8 projection GEMMs (gdn_lowp.h) -------------------------------------------------------------
+
+GDN_API int gdn_quantize_rows_e4m3(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t x_stride,
+                                   uint8_t* codes, int64_t codes_stride, float* scales, void* hip_stream) {
+    if (x_dtype != GDN_BF16 && x_dtype != GDN_F32) return fail(GDN_E_DTYPE, "x_dtype %d: GDN_BF16 or GDN_F32", x_dtype);
+    if (rows < 0 || cols < 0) return fail(GDN_E_SHAPE, "negative rows or cols");
+    if (rows == 0) return ok();
+    if (!x || !codes || !scales) return fail(GDN_E_INVAL, "x, codes and scales must be non-NULL");
+    if (x_stride < cols || codes_stride < cols) return fail(GDN_E_INVAL, "a row stride is below cols");
+    const int esz = x_dtype == GDN_F32 ? 4 : 2;
+    int64_t ext = 0;
+    if (!size_product({rows, std::max<int64_t>(x_stride, codes_stride), esz}, &ext) || ext >= ((int64_t)1 << 40))
+        return fail(GDN_E_SHAPE, "rows x stride reaches 2^40 bytes");
+    gdn::QuantParams p;
+    p.x = x;
+    p.rows = rows;
+    p.cols = cols;
+    p.x_stride = x_stride;
+    p.x_f32 = x_dtype == GDN_F32;
+    p.codes = codes;
+    p.codes_stride = codes_stride;
+    p.scales = scales;
+    hipError_t prior = hipPeekAtLastError();
+    if (prior != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(GDN_E_HIP, "earlier HIP error: %s", hipGetErrorString(prior));
+    }
+    const hipError_t e = gdn::launch_quantize_rows(p, reinterpret_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? ok() : fail(GDN_E_HIP, "kernel launch: %s", hipGetErrorString(e));
+}
+
+GDN_API int gdn_gemm_e4m3(const uint8_t* x, int64_t x_stride, const float* x_scales, const uint8_t* w,
+                          int64_t w_stride, const float* w_scales, int64_t M, int64_t N, int64_t K, void* y,
+                          int64_t y_stride, void* hip_stream) {
+    if (M < 0 || N < 0 || K < 0) return fail(GDN_E_SHAPE, "negative M, N or K");
+    if (K % 16 != 0) return fail(GDN_E_SHAPE, "K = %lld is not a multiple of 16", (long long)K);
+    if (N % 4 != 0) return fail(GDN_E_SHAPE, "N = %lld is not a multiple of 4", (long long)N);
+    if (M == 0 || N == 0) return ok();
+    // with K = 0 nothing of x or w is read (an empty view may carry no address)
+    if ((K > 0 && (!x || !w)) || !x_scales || !w_scales || !y) return fail(GDN_E_INVAL, "a pointer is NULL");
+    if (!aligned16(x) || !aligned16(w) || !aligned16(w_scales) || reinterpret_cast<uintptr_t>(y) % 8)
+        return fail(GDN_E_INVAL, "x, w and w_scales must be 16-byte aligned, y 8-byte aligned");
+    if (x_stride < K || w_stride < K || x_stride % 16 || w_stride % 16)
+        return fail(GDN_E_INVAL, "x_stride and w_stride must be multiples of 16 and >= K");
+    if (y_stride < N || y_stride % 4) return fail(GDN_E_INVAL, "y_stride must be a multiple of 4 and >= N");
+    const int64_t lim = (int64_t)1 << 31;
+    if (M > lim || N > lim || K > lim || (M - 1) * x_stride + K >= lim || (N - 1) * w_stride + K >= lim ||
+        M * y_stride >= ((int64_t)1 << 40))
+        return fail(GDN_E_SHAPE, "an operand reaches the 2 GiB extent of its 32-bit offsets");
+    gdn::GemmParams p;
+    p.x = x;
+    p.x_stride = x_stride;
+    p.x_scales = x_scales;
+    p.w = w;
+    p.w_stride = w_stride;
+    p.w_scales = w_scales;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.y = y;
+    p.y_stride = y_stride;
+    hipError_t prior = hipPeekAtLastError();
+    if (prior != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(GDN_E_HIP, "earlier HIP error: %s", hipGetErrorString(prior));
+    }
+    const hipError_t e = gdn::launch_gemm_e4m3(p, reinterpret_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? ok() : fail(GDN_E_HIP, "kernel launch: %s", hipGetErrorString(e));
 }
 
 GDN_API const char* gdn_last_error(void) { return g_err.c_str(); }

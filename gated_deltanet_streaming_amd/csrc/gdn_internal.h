@@ -110,6 +110,34 @@ bool attn_dim_supported(int d);
 hipError_t launch_attention(const AttnParams& p, hipStream_t s);
 hipError_t launch_attn_append(const AppendParams& p, hipStream_t s);
 
+// Low-precision projection GEMMs (gdn_lowp.hip).  Per-row E4M3 quantisation of x [rows][cols] (bf16 or
+// fp32, row stride in elements) into codes [rows][codes_stride] and fp32 scales [rows].
+struct QuantParams {
+    const void* x;
+    int64_t rows, cols, x_stride;
+    int x_f32;
+    unsigned char* codes;
+    int64_t codes_stride;
+    float* scales;
+};
+// y[m][n] (bf16, row stride y_stride elements) = x_scales[m] w_scales[n] sum_k x[m][k] w[n][k] over E4M3 codes
+// (row strides in bytes); K a multiple of 16, N a multiple of 4.
+struct GemmParams {
+    const unsigned char* x;
+    int64_t x_stride;
+    const float* x_scales;
+    const unsigned char* w;
+    int64_t w_stride;
+    const float* w_scales;
+    int64_t M, N, K;
+    void* y;
+    int64_t y_stride;
+};
+hipError_t launch_quantize_rows(const QuantParams& p, hipStream_t s);
+hipError_t launch_gemm_e4m3(const GemmParams& p, hipStream_t s);
+// index of the workgroup tile configuration that launch_gemm_e4m3 picks for M x N on cus compute units
+int gemm_e4m3_tile_features(int64_t M, int64_t N, int cus);
+
 hipError_t launch_zero(float* x, int64_t n, hipStream_t s);
 hipError_t launch_sequential(const Params& p, hipStream_t s, Timing* tm);
 hipError_t launch_chunked(const Params& p, hipStream_t s, Timing* tm);

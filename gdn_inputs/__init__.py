@@ -138,3 +138,13 @@ def attn_chunk(chunk: int, B: int, T: int, H: int, D: int, *, stream: int = 0, s
     k = round_bf16(rng.standard_normal((B, T, H, D), dtype=np.float32))
     v = round_bf16(rng.standard_normal((B, T, H, D), dtype=np.float32))
     return {"q": q, "k": k, "v": v}
+
+
+def proj_inputs(cfg: int, M: int, K: int, N: int):
+    """Inputs of a projection GEMM of the GDN block: activations x [M, K] ~ N(0, 1) and weights w [N, K] ~
+    N(0, 1/K), both rounded to bf16 (float32 arrays of bf16 values).  SeedSequence([cfg, 0, 0, 0, 0]) -> PCG64,
+    drawn in that order."""
+    rng = rng_for(cfg)
+    x = round_bf16(rng.standard_normal((M, K)).astype(np.float32))
+    w = round_bf16((rng.standard_normal((N, K)) / np.sqrt(max(K, 1))).astype(np.float32))
+    return x, w

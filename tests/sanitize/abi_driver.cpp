@@ -10,6 +10,7 @@
 #include <vector>
 
 #include "gdn_attn.h"
+#include "gdn_lowp.h"
 #include "gdn_stream.h"
 
 static int failures = 0;
@@ -155,6 +156,25 @@ static void run_all() {
     expect("attn max_tokens", gdn_attn_init(&abad, 0, &a), GDN_E_SHAPE);
     expect("attn NULL", gdn_attn_init(nullptr, 0, &a), GDN_E_INVAL);
     expect("attn chunk NULL", gdn_attn_chunk(nullptr, nullptr, 1, 0, nullptr), GDN_E_INVAL);
+
+    // FP8 GEMM and quantisation: refused before any device work
+    const uint8_t* fx = reinterpret_cast<const uint8_t*>((uintptr_t)1 << 40);
+    const float* fs = reinterpret_cast<const float*>(((uintptr_t)1 << 40) + (1 << 24));
+    void* fy = reinterpret_cast<void*>(((uintptr_t)1 << 40) + (2 << 24));
+    expect("gemm K not a multiple of 16", gdn_gemm_e4m3(fx, 64, fs, fx, 64, fs, 8, 8, 40, fy, 8, nullptr), GDN_E_SHAPE);
+    expect("gemm N not a multiple of 4", gdn_gemm_e4m3(fx, 64, fs, fx, 64, fs, 8, 6, 64, fy, 8, nullptr), GDN_E_SHAPE);
+    expect("gemm NULL w", gdn_gemm_e4m3(fx, 64, fs, nullptr, 64, fs, 8, 8, 64, fy, 8, nullptr), GDN_E_INVAL);
+    expect("gemm misaligned y", gdn_gemm_e4m3(fx, 64, fs, fx, 64, fs, 8, 8, 64, (char*)fy + 2, 8, nullptr), GDN_E_INVAL);
+    expect("gemm stride below K", gdn_gemm_e4m3(fx, 48, fs, fx, 64, fs, 8, 8, 64, fy, 8, nullptr), GDN_E_INVAL);
+    expect("gemm extent", gdn_gemm_e4m3(fx, (int64_t)1 << 20, fs, fx, 64, fs, 1 << 12, 8, 64, fy, 8, nullptr), GDN_E_SHAPE);
+    expect("gemm huge sizes", gdn_gemm_e4m3(fx, 64, fs, fx, 64, fs, INT64_MAX, 8, 64, fy, 8, nullptr), GDN_E_SHAPE);
+    expect("gemm y_stride not a multiple of 4", gdn_gemm_e4m3(fx, 64, fs, fx, 64, fs, 8, 8, 64, fy, 10, nullptr), GDN_E_INVAL);
+    expect("gemm NULL x with K > 0", gdn_gemm_e4m3(nullptr, 64, fs, fx, 64, fs, 8, 8, 64, fy, 8, nullptr), GDN_E_INVAL);
+    expect("gemm empty", gdn_gemm_e4m3(nullptr, 0, nullptr, nullptr, 0, nullptr, 0, 8, 64, nullptr, 8, nullptr), GDN_OK);
+    expect("quantize dtype", gdn_quantize_rows_e4m3(fx, 7, 4, 64, 64, (uint8_t*)fy, 64, (float*)fs, nullptr), GDN_E_DTYPE);
+    expect("quantize NULL", gdn_quantize_rows_e4m3(nullptr, GDN_BF16, 4, 64, 64, (uint8_t*)fy, 64, (float*)fs, nullptr), GDN_E_INVAL);
+    expect("quantize stride", gdn_quantize_rows_e4m3(fx, GDN_BF16, 4, 64, 32, (uint8_t*)fy, 64, (float*)fs, nullptr), GDN_E_INVAL);
+    expect("quantize overflow", gdn_quantize_rows_e4m3(fx, GDN_BF16, INT64_MAX / 2, 64, 64, (uint8_t*)fy, 64, (float*)fs, nullptr), GDN_E_SHAPE);
 }
 
 int main() {

@@ -9,7 +9,7 @@ import pytest
 from gated_deltanet_streaming_amd import binding
 
 INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
-HEADERS = [os.path.join(INCLUDE, "gdn_stream.h"), os.path.join(INCLUDE, "gdn_attn.h")]
+HEADERS = [os.path.join(INCLUDE, "gdn_stream.h"), os.path.join(INCLUDE, "gdn_attn.h"), os.path.join(INCLUDE, "gdn_lowp.h")]
 
 
 def declared_symbols():
@@ -126,7 +126,7 @@ def test_peaks_library_exports_its_probes():
         pytest.skip("libgdn_peaks.so not built (run __graft_entry__.build())")
     out = os.popen(f"nm -D --defined-only {path}").read()
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
-    assert exported == {"gdn_peak_copy", "gdn_peak_mfma_bf16"}
+    assert exported == {"gdn_peak_copy", "gdn_peak_mfma_bf16", "gdn_peak_mfma_fp8", "gdn_peak_lds_read"}
     lib = ctypes.CDLL(path)
     lib.gdn_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                   ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]

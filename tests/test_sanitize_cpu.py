@@ -55,7 +55,7 @@ def test_abi_host_code_under_asan_ubsan(tmp_path):
     common = ["--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,
               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
     objs, procs = [], []
-    for src in ("gdn_kernels.hip", "gdn_backward.hip", "gdn_attention.hip", "gdn_api.cpp"):
+    for src in ("gdn_kernels.hip", "gdn_backward.hip", "gdn_attention.hip", "gdn_lowp.hip", "gdn_api.cpp"):
         obj = str(tmp_path / (src + ".o"))
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
         procs.append((src, subprocess.Popen([HIPCC, *common, *host_san, *lang, "-c", os.path.join(CSRC, src), "-o", obj],
