@@ -19,7 +19,11 @@
 // of the second product once its key index becomes the contraction index: slot i of group g
 // in a 32-key step c stands for key 32c + 4g + i (i < 4) or 32c + 16 + 4g + (i - 4) (i >= 4).
 // V is written to LDS transposed, in exactly that key order, so that each A operand is one
-// 16-byte LDS read.  The softmax is online in the log2 domain (reference maximum m and partial
+// 16-byte LDS read.  Both LDS tiles are k-major in blocks of 16 rows (key rows of K, d rows of
+// V^T), with the row index XOR-ed by the 16-byte chunk: chunk u of row r at block + 256 u +
+// 16 ((r % 16) ^ u).  A 16-byte operand read (16 rows, one chunk per 16-lane group) then covers
+// one aligned 256-byte run of LDS, which this chip serves without bank conflicts, and the
+// deposits of a row's consecutive chunks fall on different bank groups.  The softmax is online in the log2 domain (reference maximum m and partial
 // sum l per lane; O^T and l rescaled by 2^(m_old - m_new) when m moves); p enters the second
 // product rounded to bf16, l sums the fp32 values.
 #include <hip/hip_runtime.h>
@@ -41,24 +45,22 @@ constexpr int NWAVE = 7;               // wavefronts per workgroup (224 queries:
                                        // 720p layer, one per CU, against 220 with 8)
 constexpr int NTHR = NWAVE * 64;
 constexpr int QT = NWAVE * QB * 16;    // queries per workgroup
-constexpr int VT_STRIDE = KT * 2 + 16; // bytes per d-row of the transposed V tile
 
 template <int D>
 struct Tile {
-    // bytes per K row: 16 more than a row, so that the 16 rows a 16-lane group of a 16-byte
-    // read touches fall on 16 different 16-byte bank groups (with 224-byte rows, rows r and
-    // r + 8 shared banks)
-    static constexpr int KS = D * 2 + 16;
-    static constexpr int K_BYTES = KT * KS;
-    static constexpr int V_BYTES = D * VT_STRIDE;
+    static constexpr int KBLK = (D / 8) * 256;    // one 16-key block of the K tile (D / 8 chunks)
+    static constexpr int K_BYTES = (KT / 16) * KBLK;
+    static constexpr int V_BYTES = (D / 16) * 2048;   // D / 16 blocks of 16 d rows x 8 chunks (64 keys)
     static constexpr int BUF = K_BYTES + V_BYTES;
     static constexpr int NS = D / 32;             // full 32-wide steps over d
     static constexpr bool TAIL = (D % 32) != 0;   // plus one 16-wide step
     static constexpr int ND = D / 16;             // 16-row blocks of d in O^T
     static constexpr int KCH = D / 8;             // 16-byte chunks per row
     static constexpr int KLOADS = (KT * KCH + NTHR - 1) / NTHR;
-    static_assert(16 * KCH <= NTHR, "one V task per thread");
+    static_assert(16 * KCH <= NTHR && KCH <= 16, "one V task per thread; chunk index within a 16-row block");
 };
+// byte offset of 16-byte chunk u of row r in a k-major XOR-ed tile whose 16-row blocks are blk bytes
+__device__ __forceinline__ int kmaj(int r, int u, int blk) { return (r >> 4) * blk + 256 * u + 16 * ((r & 15) ^ u); }
 
 __device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -214,11 +216,14 @@ __global__ __launch_bounds__(NTHR, 2) void attn_kernel(AttnParams p) {
             const int idx = tid + NTHR * i;
             if (idx < KT * TL::KCH) {
                 const int row = idx / TL::KCH, u = idx % TL::KCH;
-                *reinterpret_cast<uint4*>(kb + row * TL::KS + 16 * u) = kreg[i];
+                *reinterpret_cast<uint4*>(kb + kmaj(row, u, TL::KBLK)) = kreg[i];
             }
         }
         if (vtask) {
-            char* vb = kb + TL::K_BYTES + vpos * 2;
+            // keys 4 vq .. 4 vq + 3 sit at positions vpos .. vpos + 3 of a d row: chunk vpos / 8,
+            // bytes 2 (vpos % 8) .. of it
+            char* vb = kb + TL::K_BYTES + 2 * (vpos & 7);
+            const int vj = vpos >> 3;
             const unsigned* w0 = reinterpret_cast<const unsigned*>(&vreg[0]);
             const unsigned* w1 = reinterpret_cast<const unsigned*>(&vreg[1]);
             const unsigned* w2 = reinterpret_cast<const unsigned*>(&vreg[2]);
@@ -228,8 +233,8 @@ __global__ __launch_bounds__(NTHR, 2) void attn_kernel(AttnParams p) {
                 // d = 8 vu + 2m (low halves) and 8 vu + 2m + 1 (high halves) of the four keys
                 const uint2 lo = {(w0[m] & 0xffffu) | (w1[m] << 16), (w2[m] & 0xffffu) | (w3[m] << 16)};
                 const uint2 hi = {(w0[m] >> 16) | (w1[m] & 0xffff0000u), (w2[m] >> 16) | (w3[m] & 0xffff0000u)};
-                *reinterpret_cast<uint2*>(vb + (8 * vu + 2 * m) * VT_STRIDE) = lo;
-                *reinterpret_cast<uint2*>(vb + (8 * vu + 2 * m + 1) * VT_STRIDE) = hi;
+                *reinterpret_cast<uint2*>(vb + kmaj(8 * vu + 2 * m, vj, 2048)) = lo;
+                *reinterpret_cast<uint2*>(vb + kmaj(8 * vu + 2 * m + 1, vj, 2048)) = hi;
             }
         }
     };
@@ -272,13 +277,12 @@ __global__ __launch_bounds__(NTHR, 2) void attn_kernel(AttnParams p) {
                 for (int kk = 0; kk < KT / 16; ++kk)
         #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) st[kk][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                const char* krow = kb + r * TL::KS;
         #pragma unroll
                 for (int s = 0; s < TL::NS; ++s) {
                     bf16x8 a[KT / 16];
         #pragma unroll
                     for (int kk = 0; kk < KT / 16; ++kk)
-                        a[kk] = *reinterpret_cast<const bf16x8*>(krow + kk * 16 * TL::KS + 64 * s + 16 * g);
+                        a[kk] = *reinterpret_cast<const bf16x8*>(kb + kmaj(16 * kk + r, 4 * s + g, TL::KBLK));
         #pragma unroll
                     for (int kk = 0; kk < KT / 16; ++kk)
         #pragma unroll
@@ -288,7 +292,8 @@ __global__ __launch_bounds__(NTHR, 2) void attn_kernel(AttnParams p) {
                     bf16x4 a[KT / 16];
         #pragma unroll
                     for (int kk = 0; kk < KT / 16; ++kk)
-                        a[kk] = *reinterpret_cast<const bf16x4*>(krow + kk * 16 * TL::KS + 64 * TL::NS + 8 * g);
+                        a[kk] = *reinterpret_cast<const bf16x4*>(kb + kmaj(16 * kk + r, 4 * TL::NS + (g >> 1), TL::KBLK) +
+                                                                 8 * (g & 1));
         #pragma unroll
                     for (int kk = 0; kk < KT / 16; ++kk)
         #pragma unroll
@@ -350,7 +355,7 @@ __global__ __launch_bounds__(NTHR, 2) void attn_kernel(AttnParams p) {
                 for (int c = 0; c < KT / 32; ++c)
         #pragma unroll
                     for (int db = 0; db < TL::ND; ++db) {
-                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vb + (db * 16 + r) * VT_STRIDE + 64 * c + 16 * g);
+                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vb + kmaj(db * 16 + r, 4 * c + g, 2048));
         #pragma unroll
                         for (int qb = 0; qb < QB; ++qb) o[db][qb] = mma32(a, pf[qb][c], o[db][qb]);
                     }

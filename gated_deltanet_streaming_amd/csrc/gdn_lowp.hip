@@ -4,7 +4,7 @@
 // The pages run the block's projections in mixed precision (the Chinese summary, "Results", Table 2 and
 // Figure 6; the Korean review, section 1 "Key Terms", MPQ) without printing the formats or the scaling
 // policy.  Here: E4M3 codes with one float32 scale per row of the activations (per token) and per row of
-// the weights (per output feature), s = amax / 448, code = E4M3(x / s) rounded to nearest even and
+// the weights (per output feature), s = amax / 448, code = E4M3(x * (448 / amax)) rounded to nearest even and
 // saturated at 448; C[m][n] = s_x[m] s_w[n] sum_k E4M3^-1(X[m][k]) E4M3^-1(W[n][k]), accumulated in fp32
 // (every product of two E4M3 values is exact in fp32), stored as bf16.
 #include <hip/hip_runtime.h>
@@ -71,10 +71,10 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantParams p) {
     float amax = 0.f;
     for (int64_t c = lane; c < p.cols; c += 64) amax = fmaxf(amax, fabsf(elem(c)));
     amax = wave_max(amax);
-    const float s = amax / 448.f;
-    if (lane == 0) p.scales[row] = s;
+    if (lane == 0) p.scales[row] = amax / 448.f;
+    const float r = amax > 0.f ? 448.f / amax : 0.f;   // codes of a zero row: e4m3_code(0) = 0
     unsigned char* qr = p.codes + row * p.codes_stride;
-    for (int64_t c = lane; c < p.cols; c += 64) qr[c] = (unsigned char)(s > 0.f ? e4m3_code(elem(c) / s) : 0u);
+    for (int64_t c = lane; c < p.cols; c += 64) qr[c] = (unsigned char)e4m3_code(elem(c) * r);
 }
 
 // Vector form for rows of at most 64 x 8 x QV elements in groups of 8 (16-byte aligned input rows, 8-byte
@@ -119,8 +119,8 @@ __global__ __launch_bounds__(256) void quantize_rows_vec_kernel(QuantParams p) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[j][i]));
     amax = wave_max(amax);
-    const float s = amax / 448.f;
-    if (lane == 0) p.scales[row] = s;
+    if (lane == 0) p.scales[row] = amax / 448.f;
+    const float r = amax > 0.f ? 448.f / amax : 0.f;
     uint2* qr = reinterpret_cast<uint2*>(p.codes + row * p.codes_stride);
 #pragma unroll
     for (int j = 0; j < QV; ++j) {
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256) void quantize_rows_vec_kernel(QuantParams p) {
         if (g < ng) {
             unsigned c[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) c[i] = s > 0.f ? e4m3_code(v[j][i] / s) : 0u;
+            for (int i = 0; i < 8; ++i) c[i] = e4m3_code(v[j][i] * r);
             qr[g] = uint2{c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
         }
     }

@@ -5,8 +5,9 @@
  * "Results", Table 2 and Figure 6: projections that keep quality in low precision; the Korean review,
  * section 1 "Key Terms", MPQ).  They print neither the formats' details nor a scaling policy; this interface
  * takes E4M3 with one float32 scale per row:
- *     quantise:  s[r] = max_c |x[r][c]| / 448,  code[r][c] = E4M3(x[r][c] / s[r])
- *                (both in float32; round to nearest, ties to even; saturating at +-448; s = 0 gives codes 0)
+ *     quantise:  s[r] = max_c |x[r][c]| / 448,  code[r][c] = E4M3(x[r][c] * (448 / max_c |x[r][c]|))
+ *                (all in float32; round to nearest, ties to even; saturating at +-448; a zero row gives s = 0
+ *                and codes 0)
  *     GEMM:      y[m][n] = s_x[m] s_w[n] sum_k E4M3^-1(x[m][k]) E4M3^-1(w[n][k])
  *                (float32 accumulation, bf16 result rounded to nearest even)
  * Activations are quantised per token (rows of x), weights per output feature (rows of w), so a projection is

@@ -7,9 +7,10 @@ nor the scaling policy.  Readings taken here:
 - FP8 is OCP E4M3: sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 holds the subnormals
   m * 2^-9; S.1111.111 is NaN and there is no infinity, so the largest finite magnitude is 1.75 * 2^8 = 448.
   Conversion rounds to nearest with ties to even and saturates at +-448 (the "satfinite" conversion).
-- Activations are scaled per row (token) and weights per row (output feature): s = amax / 448 computed in float32,
-  code = E4M3(x / s) with x / s computed in float32 (an IEEE division, correctly rounded), so the integer codes are
-  a float32 decision taken identically on both sides; a row of zeros gets s = 0 and codes 0.
+- Activations are scaled per row (token) and weights per row (output feature).  The stored dequantisation scale is
+  s = amax / 448 and the codes are E4M3(x * r) with r = 448 / amax, both divisions IEEE float32 (correctly rounded)
+  and the product a float32 multiply, so the integer codes are a float32 decision taken identically on both sides
+  (one division per row rather than per element); a row of zeros gets s = 0 and codes 0.
 - The GEMM: C[i][j] = sa[i] * sw[j] * sum_k E4M3^-1(A[i][k]) * E4M3^-1(W[j][k]), accumulated in float32 by the
   kernel (every product of two E4M3 values is exact in float32) and stored as bfloat16 (round to nearest even); here
   the sum is exact in float64.
@@ -67,14 +68,15 @@ def e4m3_decode(codes) -> np.ndarray:
 
 
 def quantize_rows(x) -> tuple[np.ndarray, np.ndarray]:
-    """Per-row E4M3 quantisation of a 2-D array: (codes uint8 [rows, cols], scales float32 [rows]).  The scale and
-    the scaled values are float32 computations, as the kernel does them."""
+    """Per-row E4M3 quantisation of a 2-D array: (codes uint8 [rows, cols], scales float32 [rows]).  The scale s,
+    the code multiplier r and the scaled values are float32 computations, as the kernel does them."""
     x32 = np.asarray(x, dtype=np.float32)
     amax = np.max(np.abs(x32), axis=1) if x32.shape[1] else np.zeros(x32.shape[0], np.float32)
     s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
-    with np.errstate(divide="ignore", invalid="ignore"):
-        y = np.where(s[:, None] > 0, x32 / np.where(s[:, None] > 0, s[:, None], np.float32(1)), np.float32(0))
-    return e4m3_encode(y.astype(np.float32)), s
+    nz = amax > 0
+    r = np.where(nz, np.float32(E4M3_MAX) / np.where(nz, amax, np.float32(1)), np.float32(0)).astype(np.float32)
+    y = (x32 * r[:, None]).astype(np.float32)
+    return e4m3_encode(y), s
 
 
 def gemm_e4m3(a_codes, a_scales, w_codes, w_scales) -> np.ndarray:
