@@ -50,6 +50,8 @@
 static __device__ __align__(256) unsigned char scratch[gdn::kScratchBytes];
 
 namespace gdn {
+// a compile-time int as a value (selects a code path of a generic lambda)
+template <int V> struct IConst { static constexpr int value = V; };
 
 typedef __bf16 bf16;
 typedef _Float16 f16;
@@ -787,8 +789,9 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
 //   output (2, one per half of the step's token tiles): O from the ring, the
 //                     step's Q rows, and A and c2 (loaded two steps ahead);
 //                     bf16 tiles leave through LDS staging.
-//   loader (2): copy each step's operands from memory straight into a 3-slot
-//                     operand ring (loads that write LDS, no registers):
+//   loader (2): copy each step's operands from memory into a 3-slot operand
+//                     ring through registers (16-byte buffer loads, then
+//                     16-byte LDS stores; two steps in flight):
 //                     loader 0 the K rows, the V slice, T~ and the scalars,
 //                     loader 1 the Q rows.
 // The wavefronts are coupled only through the rings and LDS counters with
@@ -913,11 +916,6 @@ template <int V>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(V >= 0 && V < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((V & 15) | (7 << 4) | (15 << 8) | ((V >> 4) << 14));
-}
-// 16 bytes per lane from a buffer resource straight into LDS: lane l's bytes land at dst + 16 l
-// (dst wave-uniform).  Loads past the resource's end write zeros.
-__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, void* dst, int voff, int soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
 }
 
 // Output wavefront `O`: token tiles out_tile(O, 0 .. TPO-1) of every step.  With two tiles each,
@@ -1157,9 +1155,11 @@ __global__ __launch_bounds__((ScanGeom<NB, ND>::THREADS)) void gdn_scan_kernel(P
     if (wave >= GDN_COLS + NOUT) {
         // ------------------------------ loader wavefronts ------------------------------
         // Step m goes to operand slot m % GDN_OPS once every wavefront that reads that part of
-        // the slot is done with step m - GDN_OPS.  Two steps are in flight: the loads of step
-        // m + 1 are issued before those of step m are waited for (the loads of a wavefront
-        // complete in order).
+        // the slot is done with step m - GDN_OPS.  The loads go into registers and from there to
+        // LDS with 16-byte stores: the LDS takes them at its full store rate, while loads that write
+        // LDS directly held its other traffic back (the scan ran 2 us longer with them).  Two steps
+        // are in flight in two register sets: the loads of step m + 1 are issued before those of
+        // step m are waited for (the loads of a wavefront complete in order).
         const int part = wave - (GDN_COLS + NOUT);
         const StepRows krow{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.k) + (int64_t)b * p.ks[0] + (int64_t)h * p.ks[2]),
                             p.ks[1] * 2, T, C, N, dir, 2 * D};
@@ -1186,24 +1186,6 @@ __global__ __launch_bounds__((ScanGeom<NB, ND>::THREADS)) void gdn_scan_kernel(P
             voff[i] = (row0 + 16 * (jj >> 1) < p.Dv) ? vrow.row(t) + 2 * row0 + 16 * jj : (int)0x80000000;
         }
         const auto irs = make_rsrc(item0, (uint32_t)(N * ib));
-        auto issue = [&](int m) {
-            ScanSlot<NB, ND>& op = L.ops[m % GDN_OPS];
-            if (part == 0) {
-                const auto krs = krow.rsrc(m);
-#pragma unroll
-                for (int i = 0; i < G::NLK; ++i) lds_load16(krs, &op.k[i][0], roff[i], 0);
-                const auto vrs = vrow.rsrc(m);
-#pragma unroll
-                for (int i = 0; i < G::NLV; ++i) lds_load16(vrs, &op.v[i][0], voff[i], 0);
-#pragma unroll
-                for (int f = 0; f < NF; ++f) lds_load16(irs, &op.tt[f][0], 1024 * f + 16 * lane, m * (int)ib);
-                lds_load16(irs, &op.sc[0], G::ITEM_SC + 16 * lane, m * (int)ib);
-            } else {
-                const auto qrs = qrow.rsrc(m);
-#pragma unroll
-                for (int i = 0; i < G::NLK; ++i) lds_load16(qrs, &op.q[i][0], roff[i], 0);
-            }
-        };
         auto slot_free = [&](int m) {   // readers done with step m - GDN_OPS
             const int need = m + 1 - GDN_OPS;
             if (need <= 0) return;
@@ -1215,22 +1197,61 @@ __global__ __launch_bounds__((ScanGeom<NB, ND>::THREADS)) void gdn_scan_kernel(P
                 wait_counter<true>(&K.odone[1], need, p.spin_limit, p.err);
             }
         };
-        issue(0);
-        if (N > 1) issue(1);
-        for (int m = 0; m < N; ++m) {
-            if (m + 1 < N) {
-                if (part == 0) wait_vmcnt<G::NLD0>();
-                else wait_vmcnt<G::NLD1>();
-            } else {
-                wait_vmcnt<0>();
+        // one code path per loader, so that its register sets have a compile-time size
+        auto run = [&](auto PART) __attribute__((always_inline)) {
+            constexpr int P = decltype(PART)::value;
+            constexpr int NL = P == 0 ? G::NLD0 : G::NLD1;
+            auto issue = [&](int m, u32x4 (&R)[NL]) __attribute__((always_inline)) {
+                if constexpr (P == 0) {
+                    const auto krs = krow.rsrc(m);
+#pragma unroll
+                    for (int i = 0; i < G::NLK; ++i) R[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, roff[i], 0, 0));
+                    const auto vrs = vrow.rsrc(m);
+#pragma unroll
+                    for (int i = 0; i < G::NLV; ++i) R[G::NLK + i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, voff[i], 0, 0));
+#pragma unroll
+                    for (int f = 0; f < NF; ++f)
+                        R[G::NLK + G::NLV + f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(irs, 1024 * f + 16 * lane, m * (int)ib, 0));
+                    R[G::NLK + G::NLV + NF] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(irs, G::ITEM_SC + 16 * lane, m * (int)ib, 0));
+                } else {
+                    const auto qrs = qrow.rsrc(m);
+#pragma unroll
+                    for (int i = 0; i < G::NLK; ++i) R[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs, roff[i], 0, 0));
+                }
+            };
+            auto step = [&](int m, u32x4 (&R)[NL]) __attribute__((always_inline)) {
+                if (m + 1 < N) wait_vmcnt<NL>();
+                else wait_vmcnt<0>();
+                slot_free(m);
+                ScanSlot<NB, ND>& op = L.ops[m % GDN_OPS];
+                if constexpr (P == 0) {
+#pragma unroll
+                    for (int i = 0; i < G::NLK; ++i) *reinterpret_cast<u32x4*>(&op.k[i][lane]) = R[i];
+#pragma unroll
+                    for (int i = 0; i < G::NLV; ++i) *reinterpret_cast<u32x4*>(&op.v[i][lane]) = R[G::NLK + i];
+#pragma unroll
+                    for (int f = 0; f < NF; ++f) *reinterpret_cast<u32x4*>(&op.tt[f][lane]) = R[G::NLK + G::NLV + f];
+                    *reinterpret_cast<u32x4*>(&op.sc[lane]) = R[G::NLK + G::NLV + NF];
+                } else {
+#pragma unroll
+                    for (int i = 0; i < G::NLK; ++i) *reinterpret_cast<u32x4*>(&op.q[i][lane]) = R[i];
+                }
+                signal_counter(&K.loaded[P], m + 1);
+                if (m + 2 < N) issue(m + 2, R);
+            };
+            u32x4 ra[NL], rb[NL];
+            issue(0, ra);
+            if (N > 1) issue(1, rb);
+            int m = 0;
+            for (; m + 1 < N; m += 2) {
+                step(m, ra);
+                step(m + 1, rb);
             }
-            signal_counter(&K.loaded[part], m + 1);
-            if (m + 2 < N) {
-                slot_free(m + 2);
-                issue(m + 2);
-            }
-        }
-        wait_vmcnt<0>();
+            if (m < N) step(m, ra);
+            wait_vmcnt<0>();
+        };
+        if (part == 0) run(IConst<0>{});
+        else run(IConst<1>{});
         return;
     }
     if (wave == GDN_COLS) {
@@ -1281,25 +1302,24 @@ __global__ __launch_bounds__((ScanGeom<NB, ND>::THREADS)) void gdn_scan_kernel(P
     };
 
     int rdone_seen[2] = {0, 0};
-    // K rows of a step as X operands (read one step ahead, during the previous update)
-    auto read_kf = [&](const char* kb, bf16x8 (&kf)[NB][NKD]) {
+    // K rows of a step as X operands; the trailing half k-step's rows are kept as read (kh) and widened
+    // with zero slots just before their use, so that no wait for them sits ahead of the update
+    constexpr bool HALFK = NKF < NKD;
+    constexpr int NKH = HALFK ? NB : 1;
+    auto read_kf = [&](const char* kb, bf16x8 (&kf)[NB][NKD], bf16x4 (&kh)[NKH]) {
 #pragma unroll
         for (int mt = 0; mt < NB; ++mt)
 #pragma unroll
             for (int ks = 0; ks < NKD; ++ks) {
                 const bf16* kp = reinterpret_cast<const bf16*>(kb + kxo[mt][ks]);
-                if (ks < NKF) {
-                    kf[mt][ks] = ld_bf16x8(kp);
-                } else {
-                    const bf16x4 h4 = ld_bf16x4(kp);
-                    const bf16 z = (bf16)0.f;
-                    kf[mt][ks] = bf16x8{h4[0], h4[1], h4[2], h4[3], z, z, z, z};
-                }
+                if (ks < NKF) kf[mt][ks] = ld_bf16x8(kp);
+                else kh[mt] = ld_bf16x4(kp);
             }
     };
     bf16x8 kf[NB][NKD];
+    bf16x4 kh[NKH];
     wait_counter<false>(&K.loaded[0], 1, p.spin_limit, p.err);
-    read_kf(reinterpret_cast<const char*>(&L.ops[0].k[0][0]), kf);
+    read_kf(reinterpret_cast<const char*>(&L.ops[0].k[0][0]), kf, kh);
     bf16x8 kT[ND][NKT];
     bf16x8 Ub[NKT];
 #pragma unroll
@@ -1314,13 +1334,35 @@ __global__ __launch_bounds__((ScanGeom<NB, ND>::THREADS)) void gdn_scan_kernel(P
         const ScanSlot<NB, ND>& op = L.ops[n % GDN_OPS];
         const char* kb = reinterpret_cast<const char*>(&op.k[0][0]);
         // the output ring slot of this step must have been released by every output wavefront
-        // (the counts were read early in the previous step; a poll here only when they were short)
+        // (the counts were read in the previous step; a poll here only when they were short)
 #pragma unroll
         for (int o = 0; o < 2; ++o)
             if (rdone_seen[o] < n + 1 - GDN_RING) {
                 wait_counter<false>(&K.rdone[o], n + 1 - GDN_RING, p.spin_limit, p.err);
                 rdone_seen[o] = n + 1 - GDN_RING;
             }
+        // The step's other operands do not depend on the state: they are read now, so that they have
+        // arrived by the time X does.  c1 and w of tokens 16 mt + 4 g .. +3, gamma_C, V (transposed)
+        // and the T~ fragments.
+        const float* scf = reinterpret_cast<const float*>(&op.sc[0]);
+        f32x4 c1v[NB], wv[NB];
+#pragma unroll
+        for (int mt = 0; mt < NB; ++mt) {
+            c1v[mt] = *reinterpret_cast<const f32x4*>(scf + 16 * mt + 4 * g);
+            wv[mt] = *reinterpret_cast<const f32x4*>(scf + C + 16 * mt + 4 * g);
+        }
+        const float gC = scf[3 * C];
+        bf16x4 vt[NB];
+#pragma unroll
+        for (int mt = 0; mt < NB; ++mt)
+            vt[mt] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(reinterpret_cast<const char*>(&op.v[0][0]) + vto(mt))));
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (HALFK) {
+            const bf16 z = (bf16)0.f;
+#pragma unroll
+            for (int mt = 0; mt < NB; ++mt) kf[mt][NKD - 1] = bf16x8{kh[mt][0], kh[mt][1], kh[mt][2], kh[mt][3], z, z, z, z};
+        }
         // state as bf16 operand: k-slot e of lane group g <-> d = dperm(2 ks + e/4, 4 g + e%4)
         bf16x8 Pb[NKD];
 #pragma unroll
@@ -1347,7 +1389,8 @@ __global__ __launch_bounds__((ScanGeom<NB, ND>::THREADS)) void gdn_scan_kernel(P
         // publish the state to the output ring right away
 #pragma unroll
         for (int ks = 0; ks < NKD; ++ks) L.ringS[sl][ks][cc][lane] = __builtin_bit_cast(uint4, Pb[ks]);
-        // X = K S^T (rows: tokens 16 mt + 4 g + i, column: state row 16 cc + r)
+        // X = K S^T (rows: tokens 16 mt + 4 g + i, column: state row 16 cc + r); the decay of the state
+        // for the update is applied in the shadow of these products
         f32x4 X[NB];
 #pragma unroll
         for (int mt = 0; mt < NB; ++mt) X[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1355,34 +1398,19 @@ __global__ __launch_bounds__((ScanGeom<NB, ND>::THREADS)) void gdn_scan_kernel(P
         for (int ks = 0; ks < NKD; ++ks)
 #pragma unroll
             for (int mt = 0; mt < NB; ++mt) X[mt] = mma_bf16_k32(kf[mt][ks], Pb[ks], X[mt]);
-        // The counters this wavefront waits on next are read now, ahead of the step's other LDS
-        // reads: LDS reads complete in order, so checking a count read after them would wait for
-        // all of them.
+#pragma unroll
+        for (int m = 0; m < ND; ++m) P[m] = P[m] * gC;
+        __builtin_amdgcn_sched_barrier(0);
+        // the counters this wavefront checks next, read ahead of its further LDS reads (LDS reads
+        // complete in order: a count read after them would wait for all of them)
         const int ld_early = __hip_atomic_load(&K.loaded[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         int rd_early[2];
 #pragma unroll
         for (int o = 0; o < 2; ++o) rd_early[o] = __hip_atomic_load(&K.rdone[o], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        __builtin_amdgcn_sched_barrier(0);
-        // meanwhile: the step's other operands -- c1 and w of tokens 16 mt + 4 g .. +3, gamma_C,
-        // V (transposed) and the T~ fragments -- and the decay of the state
-        const float* scf = reinterpret_cast<const float*>(&op.sc[0]);
-        f32x4 c1v[NB], wv[NB];
-#pragma unroll
-        for (int mt = 0; mt < NB; ++mt) {
-            c1v[mt] = *reinterpret_cast<const f32x4*>(scf + 16 * mt + 4 * g);
-            wv[mt] = *reinterpret_cast<const f32x4*>(scf + C + 16 * mt + 4 * g);
-        }
-        const float gC = scf[3 * C];
-        bf16x4 vt[NB];
-#pragma unroll
-        for (int mt = 0; mt < NB; ++mt)
-            vt[mt] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(reinterpret_cast<const char*>(&op.v[0][0]) + vto(mt))));
         f16x8 tf[NF];
 #pragma unroll
         for (int f = 0; f < NF; ++f) tf[f] = __builtin_bit_cast(f16x8, op.tt[f][lane]);
-#pragma unroll
-        for (int m = 0; m < ND; ++m) P[m] = P[m] * gC;
+        __builtin_amdgcn_sched_barrier(0);
         // R = V - diag(c1) X, as fp16 B operand (k = token, slot order of the output tiles)
         f16x8 Rb[NKT];
 #pragma unroll
@@ -1442,23 +1470,23 @@ __global__ __launch_bounds__((ScanGeom<NB, ND>::THREADS)) void gdn_scan_kernel(P
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) L.ringU[sl][kt][cc][lane] = __builtin_bit_cast(uint4, Uh[kt]);
         signal_counter(&K.ready[cc], n + 1);
-        // the next step's K rows, read while the update runs (into registers of their own: the
-        // update's operands stay live until its results have been read)
 #pragma unroll
         for (int o = 0; o < 2; ++o) rdone_seen[o] = rd_early[o] > rdone_seen[o] ? rd_early[o] : rdone_seen[o];
-        if (n + 1 < N) {
-            if (ld_early < n + 2) wait_counter<false>(&K.loaded[0], n + 2, p.spin_limit, p.err);
-            read_kf(reinterpret_cast<const char*>(&L.ops[(n + 1) % GDN_OPS].k[0][0]), kf);
-        }
         // S^T <- gamma_C S^T + K^T (w U)  (rows d, columns: state rows); a trailing 16-token
         // step has zero upper slots in both operands
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
             for (int m = 0; m < ND; ++m) P[m] = mma_bf16_k32(kT[m][kt], Ub[kt], P[m]);
+        __builtin_amdgcn_sched_barrier(0);
         // every read of the operand slot of step n has been issued (and, the LDS being in order,
         // takes effect before this count)
         signal_counter(&K.cdone[cc], n + 1);
+        // the next step's K rows, read while the update runs
+        if (n + 1 < N) {
+            if (ld_early < n + 2) wait_counter<false>(&K.loaded[0], n + 2, p.spin_limit, p.err);
+            read_kf(reinterpret_cast<const char*>(&L.ops[(n + 1) % GDN_OPS].k[0][0]), kf, kh);
+        }
     }
     float* Sout = p.S_out[dir];
     if (Sout && tile_ok) {
