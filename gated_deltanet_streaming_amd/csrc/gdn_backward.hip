@@ -25,12 +25,6 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
 }
-// sum over the 4 lanes of a lane quad (one state row): quad permutations [1,0,3,2] and [2,3,0,1]
-__device__ __forceinline__ float sum4(float x) {
-    x += dpp<0xB1>(x);
-    x += dpp<0x4E>(x);
-    return x;
-}
 
 void tm_begin(Timing* tm, hipStream_t s, int kind) {
     if (tm && tm->ev && tm->n < tm->cap) {
@@ -55,32 +49,34 @@ void tm_end(Timing* tm, hipStream_t s) {
 //     dv_t = beta_t gk,  da_t = <G, S_{t-1}> - beta_t gk.x,  dbeta_t = gk.(v_t - a_t x)
 //     dk_t = beta_t G^T (v_t - a_t x) - a_t beta_t S_{t-1}^T gk,  dq_t = scale S_t^T do_t
 //     G <- a_t (G - beta_t gk k_t^T)
-// gdn_bwd_rows_kernel: one 64-lane workgroup per (b, h, block of 16 state rows);
-// lane l owns row 16 rb + l/4 and the columns 16 j + 4 (l%4) + e (e < 4) of every
-// 16-column group j, one float4 per group.  Tokens are staged through LDS in
+// gdn_bwd_rows_kernel: one 64-lane workgroup per (b, h, block of 8 state rows);
+// lane l owns row 8 rb + l/8 and the columns 16 j + 2 (l%8) + e (e < 2) of every
+// 16-column group j, one float2 per group.  Tokens are staged through LDS in
 // blocks of TB (k and q normalised once per block; the next block's global loads
 // go out before the current block is worked on).  A forward pass keeps only the
 // state before every block (a checkpoint); the backward pass walks the blocks in
 // reverse, recomputes the states inside a block from its checkpoint into LDS and
 // then walks its tokens backward.  dv and the start-state gradient are row-local;
 // the other gradients sum over all rows: per token the rows' terms go through an
-// LDS buffer and each lane adds one float4 column group over the 16 rows in row
+// LDS buffer and each lane adds one float4 column group over the 8 rows in row
 // order, then the workgroup writes its rows' partial sums, and gdn_bwd_reduce_kernel
 // adds the row blocks in a fixed order and maps the normalised-vector gradients
 // back through the L2 normalisation.
 // ---------------------------------------------------------------------------
 constexpr int kMinTB = 14;   // smallest token block of any instance (sizes the checkpoints)
+constexpr int kRB = 8;       // state rows per workgroup
+constexpr int kLPR = 64 / kRB;   // lanes per state row
 
 int64_t backward_ckpt_per(int64_t max_tokens) { return (max_tokens + kMinTB - 1) / kMinTB + 1; }
 
 int64_t backward_ckpt_floats(int B, int H, int Dk, int Dv, int64_t max_tokens) {
-    return (int64_t)B * H * (Dv / 16) * backward_ckpt_per(max_tokens) * 16 * Dk;
+    return (int64_t)B * H * (Dv / kRB) * backward_ckpt_per(max_tokens) * kRB * Dk;
 }
 
 int64_t backward_ws_bytes(int B, int H, int Dk, int Dv, int64_t max_tokens) {
-    const int64_t nrb = Dv / 16;
+    const int64_t nrb = Dv / kRB;
     int64_t states = 0, partials = 0, total = 0;
-    if (__builtin_mul_overflow((int64_t)B * H, nrb * 16 * Dk, &states) ||
+    if (__builtin_mul_overflow((int64_t)B * H, nrb * kRB * Dk, &states) ||
         __builtin_mul_overflow(states, backward_ckpt_per(max_tokens), &states) ||
         __builtin_mul_overflow((int64_t)B * H, nrb * (2 * Dk + 4), &partials) ||
         __builtin_mul_overflow(partials, max_tokens, &partials) || __builtin_add_overflow(states, partials, &total) ||
@@ -91,10 +87,17 @@ int64_t backward_ws_bytes(int B, int H, int Dk, int Dv, int64_t max_tokens) {
 
 namespace {
 
-// sum over the 16 rows of the workgroup (lane bits 2..5): the four rows of each 16-lane DPP row
-// by two rotations (lanes j, j-4, j-8, j-12), then across the four DPP rows with lane swaps
+// sum over the 8 lanes of one state row (lane bits 0..2): quad permutations [1,0,3,2] and
+// [2,3,0,1], then the mirror within the 8-lane half row
+__device__ __forceinline__ float sum8(float x) {
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x141>(x);   // row_half_mirror
+    return x;
+}
+// sum over the 8 rows of the workgroup (lane bits 3..5): the two rows of each 16-lane DPP row by
+// one rotation (lanes j, j-8), then across the four DPP rows with lane swaps
 __device__ __forceinline__ float sum_rows(float x) {
-    x += dpp<0x124>(x);   // row_ror:4
     x += dpp<0x128>(x);   // row_ror:8
     const unsigned u = __float_as_uint(x);
     const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
@@ -105,14 +108,12 @@ __device__ __forceinline__ float sum_rows(float x) {
 }
 
 __device__ __forceinline__ float dot4(const float4& a, const float4& b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; }
-// acc += a * b componentwise: four independent chains for a dot product over many float4
-__device__ __forceinline__ void fma4(float4& acc, const float4& a, const float4& b) {
+// acc += a * b componentwise: two independent chains for a dot product over many float2
+__device__ __forceinline__ void fma2(float2& acc, const float2& a, const float2& b) {
     acc.x += a.x * b.x;
     acc.y += a.y * b.y;
-    acc.z += a.z * b.z;
-    acc.w += a.w * b.w;
 }
-__device__ __forceinline__ float hsum4(const float4& a) { return (a.x + a.y) + (a.z + a.w); }
+__device__ __forceinline__ float hsum2(const float2& a) { return a.x + a.y; }
 
 // raw buffer resource over [base, base + bytes); loads beyond it return zero
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
@@ -131,26 +132,27 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g)
     constexpr int TB = NG == 8 ? 14 : 16;     // tokens per staged block (LDS: states of a block)
     constexpr int NLQ = (TB * DK + 255) / 256;   // staged elements of k (and of q) per lane, 4 at a time
     static_assert(TB >= kMinTB, "checkpoint sizing");
-    const int lane = threadIdx.x, part = lane & 3, rl = lane >> 2;
-    const int nrb = p.Dv / 16;
+    const int lane = threadIdx.x, part = lane & (kLPR - 1), rl = lane / kLPR;
+    const int nrb = p.Dv / kRB;
     int id = blockIdx.x;
     const int rb = id % nrb;
     id /= nrb;
     const int h = id % p.H;
     id /= p.H;
     const int b = id;
-    const int row = 16 * rb + rl;
+    const int row = kRB * rb + rl;
     const int T = (int)p.T;
     const int nblk = (T + TB - 1) / TB;
     const int wid = 2 * DK + 4;
 
-    __shared__ __align__(16) float4 sst[TB][NG][64];   // S_{t-1} of the block's tokens, lane-major
+    __shared__ __align__(16) float2 sst[TB][NG][64];   // S_{t-1} of the block's tokens, lane-major
     __shared__ __align__(16) float skn[TB][DK];        // normalised k of the block's tokens
     __shared__ __align__(16) float sqn[TB][DK];        // normalised q
-    __shared__ __align__(16) float scol[2][16][DK];    // per-row terms of dq and dk of one token
-    __shared__ float sv[TB][16], sdo[TB][16], sx[TB][16], sa[TB], sb[TB];
+    __shared__ __align__(16) float scol[2][kRB][DK];   // per-row terms of dq and dk of one token
+    __shared__ __align__(16) float sv[TB][kRB], sdo[TB][kRB];
+    __shared__ float sx[TB][kRB], sa[TB], sb[TB];
 
-    float* ck = g.states + (((int64_t)b * p.H + h) * nrb + rb) * g.ck_per * 16 * DK;
+    float* ck = g.states + (((int64_t)b * p.H + h) * nrb + rb) * g.ck_per * kRB * DK;
     auto tok = [&](int pi) { return g.reverse ? T - 1 - pi : pi; };
 
     // ---- staging: raw loads of a block into registers, then fp32 (normalised) into LDS ----
@@ -159,16 +161,16 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g)
     constexpr int ESZ = F32 ? 4 : 2, EPC = 16 / ESZ;   // bytes per element, elements per chunk
     constexpr int CPR = DK / EPC, NCH = TB * CPR;        // chunks per k/q row, per block
     constexpr int NLC = (NCH + 63) / 64;                 // k (q) chunks per lane
-    constexpr int VCPR = 16 / EPC, NVC = TB * VCPR;      // chunks of a token's 16 v (d_o) values, per block
+    constexpr int VCPR = kRB / EPC, NVC = TB * VCPR;     // chunks of a token's kRB v (d_o) values, per block
     static_assert(NVC <= 64, "one v chunk per lane");
     const char* kb = static_cast<const char*>(p.k) + ((int64_t)b * p.ks[0] + (int64_t)h * p.ks[2]) * ESZ;
     const char* qb = static_cast<const char*>(p.q) + ((int64_t)b * p.qs[0] + (int64_t)h * p.qs[2]) * ESZ;
-    const char* vb = static_cast<const char*>(p.v) + ((int64_t)b * p.vs[0] + (int64_t)h * p.vs[2] + 16 * rb) * ESZ;
-    const char* ob = static_cast<const char*>(g.d_o) + ((int64_t)b * p.os[0] + (int64_t)h * p.os[2] + 16 * rb) * ESZ;
+    const char* vb = static_cast<const char*>(p.v) + ((int64_t)b * p.vs[0] + (int64_t)h * p.vs[2] + kRB * rb) * ESZ;
+    const char* ob = static_cast<const char*>(g.d_o) + ((int64_t)b * p.os[0] + (int64_t)h * p.os[2] + kRB * rb) * ESZ;
     const auto krs = make_rsrc(kb, ((int64_t)(T - 1) * p.ks[1] + DK) * ESZ);
     const auto qrs = make_rsrc(qb, ((int64_t)(T - 1) * p.qs[1] + DK) * ESZ);
-    const auto vrs = make_rsrc(vb, ((int64_t)(T - 1) * p.vs[1] + 16) * ESZ);
-    const auto ors = make_rsrc(ob, ((int64_t)(T - 1) * p.os[1] + 16) * ESZ);
+    const auto vrs = make_rsrc(vb, ((int64_t)(T - 1) * p.vs[1] + kRB) * ESZ);
+    const auto ors = make_rsrc(ob, ((int64_t)(T - 1) * p.os[1] + kRB) * ESZ);
     const int ksb = (int)(p.ks[1] * ESZ), qsb = (int)(p.qs[1] * ESZ), vsb = (int)(p.vs[1] * ESZ), osb = (int)(p.os[1] * ESZ);
     constexpr int OUT = (int)0x80000000;   // beyond every resource
     uint4 rk[NLC], rq[NLC], rv = {0u, 0u, 0u, 0u}, rdo = {0u, 0u, 0u, 0u};
@@ -260,30 +262,28 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g)
         }
         lds_order();
     };
-    // columns of this lane in staged row r: 16 j + 4 part .. +3
-    auto krow = [&](int r, int j) { return *reinterpret_cast<const float4*>(&skn[r][16 * j + 4 * part]); };
-    auto qrow = [&](int r, int j) { return *reinterpret_cast<const float4*>(&sqn[r][16 * j + 4 * part]); };
-    auto ckp = [&](int blk, int j) { return reinterpret_cast<float4*>(ck + ((int64_t)blk * 16 + rl) * DK + 16 * j + 4 * part); };
+    // columns of this lane in staged row r: 16 j + 2 part .. +1
+    auto krow = [&](int r, int j) { return *reinterpret_cast<const float2*>(&skn[r][16 * j + 2 * part]); };
+    auto qrow = [&](int r, int j) { return *reinterpret_cast<const float2*>(&sqn[r][16 * j + 2 * part]); };
+    auto ckp = [&](int blk, int j) { return reinterpret_cast<float2*>(ck + ((int64_t)blk * kRB + rl) * DK + 16 * j + 2 * part); };
 
     // one token of the forward recurrence on S (row dot and update); returns x = S k
-    float4 S[NG];
+    float2 S[NG];
     auto fwd_token = [&](int r) {
-        float4 kr[NG];
+        float2 kr[NG];
 #pragma unroll
         for (int j = 0; j < NG; ++j) kr[j] = krow(r, j);
         const float at = sa[r], bt = sb[r], vr = sv[r][rl];
-        float4 xa = {0.f, 0.f, 0.f, 0.f};
+        float2 xa = {0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < NG; ++j) fma4(xa, S[j], kr[j]);
-        const float x = sum4(hsum4(xa));
+        for (int j = 0; j < NG; ++j) fma2(xa, S[j], kr[j]);
+        const float x = sum8(hsum2(xa));
         const float c0 = bt * x, c1 = bt * vr;
 #pragma unroll
         for (int j = 0; j < NG; ++j) {
-            const float4 kk = kr[j];
+            const float2 kk = kr[j];
             S[j].x = at * (S[j].x - c0 * kk.x) + c1 * kk.x;
             S[j].y = at * (S[j].y - c0 * kk.y) + c1 * kk.y;
-            S[j].z = at * (S[j].z - c0 * kk.z) + c1 * kk.z;
-            S[j].w = at * (S[j].w - c0 * kk.w) + c1 * kk.w;
         }
         return x;
     };
@@ -291,8 +291,8 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g)
     // ---- forward: checkpoints before every block ----
 #pragma unroll
     for (int j = 0; j < NG; ++j)
-        S[j] = g.state0 ? *reinterpret_cast<const float4*>(g.state0 + (((int64_t)b * p.H + h) * p.Dv + row) * DK + 16 * j + 4 * part)
-                        : float4{0.f, 0.f, 0.f, 0.f};
+        S[j] = g.state0 ? *reinterpret_cast<const float2*>(g.state0 + (((int64_t)b * p.H + h) * p.Dv + row) * DK + 16 * j + 2 * part)
+                        : float2{0.f, 0.f};
     if (nblk > 0) load_block(0, false);
     for (int blk = 0; blk < nblk; ++blk) {
         store_block(false);
@@ -304,11 +304,11 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g)
     }
 
     // ---- backward over the blocks in reverse ----
-    float4 G[NG];
+    float2 G[NG];
 #pragma unroll
     for (int j = 0; j < NG; ++j)
-        G[j] = g.d_state ? *reinterpret_cast<const float4*>(g.d_state + (((int64_t)b * p.H + h) * p.Dv + row) * DK + 16 * j + 4 * part)
-                         : float4{0.f, 0.f, 0.f, 0.f};
+        G[j] = g.d_state ? *reinterpret_cast<const float2*>(g.d_state + (((int64_t)b * p.H + h) * p.Dv + row) * DK + 16 * j + 2 * part)
+                         : float2{0.f, 0.f};
     if (nblk > 0) load_block(nblk - 1, true);
     for (int blk = nblk - 1; blk >= 0; --blk) {
         store_block(true);
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g)
         for (int r = n - 1; r >= 0; --r) {
             const int64_t t = tok(blk * TB + r);
             // every LDS operand of the token first, then the arithmetic
-            float4 Sp[NG], kr[NG], qr[NG];
+            float2 Sp[NG], kr[NG], qr[NG];
 #pragma unroll
             for (int j = 0; j < NG; ++j) {
                 Sp[j] = sst[r][j][lane];
@@ -338,52 +338,46 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g)
             const float at = sa[r], bt = sb[r], vr = sv[r][rl], x = sx[r][rl];
 #pragma unroll
             for (int j = 0; j < NG; ++j) {
-                const float4 qq = qr[j];
+                const float2 qq = qr[j];
                 G[j].x += dor * qq.x;
                 G[j].y += dor * qq.y;
-                G[j].z += dor * qq.z;
-                G[j].w += dor * qq.w;
             }
-            float4 gka = {0.f, 0.f, 0.f, 0.f}, gsa = {0.f, 0.f, 0.f, 0.f};
+            float2 gka = {0.f, 0.f}, gsa = {0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < NG; ++j) {
-                fma4(gka, G[j], kr[j]);
-                fma4(gsa, G[j], Sp[j]);
+                fma2(gka, G[j], kr[j]);
+                fma2(gsa, G[j], Sp[j]);
             }
-            const float gk = sum4(hsum4(gka)), gs = sum4(hsum4(gsa));
+            const float gk = sum8(hsum2(gka)), gs = sum8(hsum2(gsa));
             if (part == 0) g.dv[(((int64_t)b * T + t) * p.H + h) * p.Dv + row] = bt * gk;
             // this row's terms of dq_t = scale S_t^T do_t and dk_t = beta G^T (v - a x) - a beta S_{t-1}^T gk
             const float wv = bt * (vr - at * x), ws = at * bt * gk;
 #pragma unroll
             for (int j = 0; j < NG; ++j) {
-                *reinterpret_cast<float4*>(&scol[0][rl][16 * j + 4 * part]) =
-                    float4{dor * S[j].x, dor * S[j].y, dor * S[j].z, dor * S[j].w};
-                *reinterpret_cast<float4*>(&scol[1][rl][16 * j + 4 * part]) =
-                    float4{wv * G[j].x - ws * Sp[j].x, wv * G[j].y - ws * Sp[j].y, wv * G[j].z - ws * Sp[j].z,
-                           wv * G[j].w - ws * Sp[j].w};
+                *reinterpret_cast<float2*>(&scol[0][rl][16 * j + 2 * part]) = float2{dor * S[j].x, dor * S[j].y};
+                *reinterpret_cast<float2*>(&scol[1][rl][16 * j + 2 * part]) =
+                    float2{wv * G[j].x - ws * Sp[j].x, wv * G[j].y - ws * Sp[j].y};
             }
             lds_order();
             const float cg = bt * gk;
 #pragma unroll
             for (int j = 0; j < NG; ++j) {
-                const float4 kk = kr[j];
+                const float2 kk = kr[j];
                 G[j].x = at * (G[j].x - cg * kk.x);
                 G[j].y = at * (G[j].y - cg * kk.y);
-                G[j].z = at * (G[j].z - cg * kk.z);
-                G[j].w = at * (G[j].w - cg * kk.w);
             }
-            // per-row scalars (identical in the 4 lanes of a row; counted once)
+            // per-row scalars (identical in the 8 lanes of a row; counted once)
             float da = (part == 0) ? gs - bt * gk * x : 0.f;
             float db = (part == 0) ? gk * (vr - at * x) : 0.f;
             da = sum_rows(da);
             db = sum_rows(db);
             float* pw = g.partials + ((((int64_t)b * T + t) * p.H + h) * nrb + rb) * wid;
-            // column sums over the 16 rows, in row order: lane l adds float4 group l
+            // column sums over the 8 rows, in row order: lane l adds float4 group l
             if (lane < DK / 2) {
                 const int a = lane / (DK / 4), c4 = 4 * (lane - a * (DK / 4));
                 float4 acc = *reinterpret_cast<const float4*>(&scol[a][0][c4]);
 #pragma unroll
-                for (int rr = 1; rr < 16; ++rr) {
+                for (int rr = 1; rr < kRB; ++rr) {
                     const float4 v4 = *reinterpret_cast<const float4*>(&scol[a][rr][c4]);
                     acc.x += v4.x;
                     acc.y += v4.y;
@@ -404,7 +398,7 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g)
     if (g.d_state0) {
 #pragma unroll
         for (int j = 0; j < NG; ++j)
-            *reinterpret_cast<float4*>(g.d_state0 + (((int64_t)b * p.H + h) * p.Dv + row) * DK + 16 * j + 4 * part) = G[j];
+            *reinterpret_cast<float2*>(g.d_state0 + (((int64_t)b * p.H + h) * p.Dv + row) * DK + 16 * j + 2 * part) = G[j];
     }
 }
 
@@ -424,7 +418,7 @@ __global__ __launch_bounds__(64) void gdn_bwd_reduce_kernel(Params p, BwdParams 
     const int h = (int)(id % p.H); id /= p.H;
     const int64_t t = id % p.T; id /= p.T;
     const int b = (int)id;
-    const int Dk = p.Dk, nrb = p.Dv / 16, wid = 2 * Dk + 4;
+    const int Dk = p.Dk, nrb = p.Dv / kRB, wid = 2 * Dk + 4;
     const float* pw = g.partials + (((int64_t)b * p.T + t) * p.H + h) * nrb * wid;
     float gq[2] = {0.f, 0.f}, gkk[2] = {0.f, 0.f}, da = 0.f, db = 0.f;
     for (int r = 0; r < nrb; ++r) {
@@ -499,7 +493,7 @@ static hipError_t launch_rows(const Params& p, const BwdParams& g, hipStream_t s
 }
 
 hipError_t launch_backward(const Params& p, const BwdParams& g, hipStream_t s, Timing* tm) {
-    const int rows_grid = p.B * p.H * (p.Dv / 16);
+    const int rows_grid = p.B * p.H * (p.Dv / kRB);
     const int64_t red_grid = (int64_t)p.B * p.T * p.H;
     tm_begin(tm, s, KBWD);
     hipError_t e = launch_rows(p, g, s, rows_grid);
