@@ -277,13 +277,16 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--mode", choices=["bidir", "separate", "long", "backward", "attention", "lowp"], default="bidir",
+    ap.add_argument("--mode", choices=["bidir", "separate", "long", "backward", "attention", "lowp", "split"], default="bidir",
                     help="bidir: one gdn_chunk_bidir call per step; separate: forward then reverse calls; "
                          "long: gdn_chunk_bidir on a 21-frame clip (T = 18480); "
                          "backward: the gradients of both scans of the pair (gdn_chunk_backward); "
                          "attention: the softmax block's sink + window attention (gdn_attn_chunk); "
                          "lowp: the GDN block's fused q/k/v projection as an E4M3 GEMM (gdn_quantize_rows_e4m3 + "
-                         "gdn_gemm_e4m3)")
+                         "gdn_gemm_e4m3); "
+                         "split: the forward scan of a 21-frame clip with few stream-heads, plain "
+                         "(gdn_chunk_forward) against the time split (gdn_chunk_forward_split)")
+    ap.add_argument("--split-heads", type=int, default=1, help="heads of the split mode's single stream")
     ap.add_argument("--sets", type=int, default=6, help="rotating input/output buffer sets (1 = warm)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-peaks", action="store_true", help="skip the copy / MFMA peak probes")
@@ -321,6 +324,8 @@ def main():
         return main_attention(args)
     if args.mode == "lowp":
         return main_lowp(args)
+    if args.mode == "split":
+        return main_split(args)
 
     import numpy as np
     import torch
@@ -487,6 +492,78 @@ def main():
         threads = min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS", "0")) or 1 << 30)
         out["cpu_baseline"] = cpu_baseline(d, threads, t_run)
     s.close()
+    print(json.dumps(out), flush=True)
+
+
+def main_split(args):
+    """The causal forward scan of the 21-frame clip (T = 18480, 289 steps of 64 tokens) for one stream
+    of `--split-heads` heads of 112: the plain call against the time split at several segment
+    counts.  Every call starts from the same cached state (GDN_NO_COMMIT); inputs resident in HBM."""
+    import numpy as np
+    import torch
+
+    import gdn_inputs
+    import oracle
+    from gated_deltanet_streaming_amd import binding as gb
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    Hs, t_run = args.split_heads, T_LONG
+    d = gdn_inputs.batch(1, 1, t_run, Hs, D, with_state=True)
+    x = {k: torch.from_numpy(d[k]).to(dev, torch.bfloat16) for k in ("q", "k", "v")}
+    x["a"] = torch.from_numpy(d["a"]).to(dev)
+    x["beta"] = torch.from_numpy(d["beta"]).to(dev)
+    o = torch.empty_like(x["v"])
+    s = gb.Stream(1, Hs, D, D, t_run, device=0)
+    s.state_set(torch.from_numpy(d["S0"]).to(dev))
+    stream = torch.cuda.current_stream(dev)
+
+    def call(seg):
+        if seg == 1:
+            s.forward(x["q"], x["k"], x["v"], x["a"], x["beta"], o, flags=gb.GDN_NO_COMMIT, stream=stream)
+        else:
+            s.forward_split(x["q"], x["k"], x["v"], x["a"], x["beta"], o, seg, flags=gb.GDN_NO_COMMIT, stream=stream)
+
+    steps = max(args.steps // 4, 10)
+    by_seg = {}
+    for seg in (1, 4, 8, 16, 32, 48, 72):
+        for _ in range(max(args.warmup // 4, 3)):
+            call(seg)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            call(seg)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        by_seg[seg] = e0.elapsed_time(e1) / steps
+    best = min((v, k) for k, v in by_seg.items() if k > 1)
+    ms, seg_best = best
+    alg = Hs * (t_run * (3 * 2 * D + 2 * D + 8) + 2 * D * D * 4)
+    out = {
+        "metric": "GDN causal forward scan tokens/s, one stream, few heads, 21-frame clip (time split)",
+        "value": t_run / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": max(args.warmup // 4, 3), "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "21-frame clip, one stream, forward scan from a carried state", "B": 1, "H": Hs,
+                   "d_k": D, "d_v": D, "T": t_run, "subchunk": 64, "call": "gdn_chunk_forward_split",
+                   "segments": seg_best},
+        "plain_ms": by_seg[1], "speedup_vs_plain": by_seg[1] / ms,
+        "ms_by_segments": {str(k): round(v, 4) for k, v in by_seg.items()},
+        "roofline": {"bound": "hbm", "achieved": alg / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "note": "algorithmic bytes of the forward scan (q, k, v, o, gates, the state in and out) / call time"},
+    }
+    if not args.no_cpu:
+        oracle.build(force=False)
+        threads = min(16, os.cpu_count() or 1)
+        reps, t0 = 0, time.perf_counter()
+        while reps < 3 or time.perf_counter() - t0 < 5.0:
+            oracle.forward(d["q"], d["k"], d["v"], d["a"], d["beta"], d["S0"], threads=threads)
+            reps += 1
+        per = (time.perf_counter() - t0) / reps
+        out["cpu_baseline"] = {"value": round(t_run / per, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                               "sample": f"the full workload, {reps} repeats of the fp64 forward scan ({per:.3f} s each)"}
     print(json.dumps(out), flush=True)
 
 

@@ -86,6 +86,7 @@ def load_library():
         "gdn_stream_init": ([ctypes.POINTER(GdnConfig), i32, ctypes.POINTER(vp)], i32),
         "gdn_stream_destroy": ([vp], i32),
         "gdn_chunk_forward": ([vp, ctypes.POINTER(GdnIo), i64, u32, vp, vp], i32),
+        "gdn_chunk_forward_split": ([vp, ctypes.POINTER(GdnIo), i64, i32, u32, vp, vp], i32),
         "gdn_chunk_reverse": ([vp, ctypes.POINTER(GdnIo), i64, u32, vp, vp], i32),
         "gdn_chunk_bidir": ([vp, ctypes.POINTER(GdnIo), vp, i64, u32, vp, vp], i32),
         "gdn_chunk_bidir_noalloc": ([ctypes.POINTER(GdnConfig), ctypes.POINTER(GdnIo), vp, i64, vp, vp, vp, vp], i32),
@@ -180,6 +181,12 @@ def gdn_chunk_forward(handle, q, k, v, a, beta, o, *, flags=0, state_out=None, s
                                             _ptr(state_out), _stream_ptr(stream, q.device)))
 
 
+def gdn_chunk_forward_split(handle, q, k, v, a, beta, o, segments, *, flags=0, state_out=None, stream=None):
+    io = _make_io(q, k, v, o, a, beta)
+    _check(load_library().gdn_chunk_forward_split(ctypes.c_void_p(handle), ctypes.byref(io), q.shape[1], int(segments),
+                                                  flags, _ptr(state_out), _stream_ptr(stream, q.device)))
+
+
 def gdn_chunk_reverse(handle, q, k, v, a, beta, o, *, flags=0, state_out=None, stream=None):
     io = _make_io(q, k, v, o, a, beta)
     _check(load_library().gdn_chunk_reverse(ctypes.c_void_p(handle), ctypes.byref(io), q.shape[1], flags,
@@ -268,6 +275,9 @@ class Stream:
 
     def forward(self, q, k, v, a, beta, o, **kw):
         gdn_chunk_forward(self.handle, q, k, v, a, beta, o, **kw)
+
+    def forward_split(self, q, k, v, a, beta, o, segments, **kw):
+        gdn_chunk_forward_split(self.handle, q, k, v, a, beta, o, segments, **kw)
 
     def reverse(self, q, k, v, a, beta, o, **kw):
         gdn_chunk_reverse(self.handle, q, k, v, a, beta, o, **kw)

@@ -41,6 +41,8 @@ struct gdn_stream {
     int* err;             // error word in pinned host memory: a kernel wait gave up
     int spin_limit;       // polls before a wait gives up
     float* bwd_ws;        // backward workspace (states, partial sums), allocated on first use
+    float* seg_ws;        // time-split workspace (segment states), allocated on first use, grown on demand
+    int64_t seg_elems;
     // optional per-kernel timing
     bool profile;
     std::vector<std::pair<hipEvent_t, hipEvent_t>> pend;
@@ -267,7 +269,7 @@ void drain_profile(gdn_stream* s) {
     s->pend_kind.clear();
 }
 
-int run(gdn_stream* s, gdn::Params& p, uint32_t flags, hipStream_t st) {
+int run(gdn_stream* s, gdn::Params& p, uint32_t flags, hipStream_t st, float* split_in = nullptr) {
     DeviceGuard dg(s->device);
     if (dg.err != hipSuccess) return fail(GDN_E_HIP, "hipSetDevice(%d): %s", s->device, hipGetErrorString(dg.err));
     hipError_t prior = hipPeekAtLastError();
@@ -292,7 +294,9 @@ int run(gdn_stream* s, gdn::Params& p, uint32_t flags, hipStream_t st) {
         }
         tm.ev = evs;
     }
-    hipError_t e = (flags & GDN_SEQUENTIAL) ? gdn::launch_sequential(p, st, &tm) : gdn::launch_chunked(p, st, &tm);
+    hipError_t e = split_in                   ? gdn::launch_split(p, split_in, st, &tm)
+                   : (flags & GDN_SEQUENTIAL) ? gdn::launch_sequential(p, st, &tm)
+                                              : gdn::launch_chunked(p, st, &tm);
     if (s->profile) {
         for (int i = 0; i < 4; ++i) {
             auto pr = std::make_pair(evs[2 * i], evs[2 * i + 1]);
@@ -359,6 +363,8 @@ GDN_API int gdn_stream_init(const gdn_config* cfg, int device, gdn_stream** out)
     s->ws = nullptr;
     s->conv = nullptr;
     s->bwd_ws = nullptr;
+    s->seg_ws = nullptr;
+    s->seg_elems = 0;
     s->item_bytes = 0;
     s->nsub_max = 0;
     s->items_total = 0;
@@ -429,6 +435,7 @@ GDN_API int gdn_stream_destroy(gdn_stream* s) {
     if (s->ws) (void)hipFree(s->ws);
     if (s->conv) (void)hipFree(s->conv);
     if (s->bwd_ws) (void)hipFree(s->bwd_ws);
+    if (s->seg_ws) (void)hipFree(s->seg_ws);
     if (s->err) (void)hipHostFree(s->err);
     delete s;
     if (e != hipSuccess) return fail(GDN_E_HIP, "destroy: %s", hipGetErrorString(e));
@@ -456,6 +463,49 @@ GDN_API int gdn_chunk_forward(gdn_stream* s, const gdn_io* io, int64_t T, uint32
     p.dir0 = 0;
     p.ndirs = 1;
     return run(s, p, flags, st);
+}
+
+GDN_API int gdn_chunk_forward_split(gdn_stream* s, const gdn_io* io, int64_t T, int segments, uint32_t flags,
+                                    float* state_out, void* hip_stream) {
+    int rc = check_call(s, io, T, flags, nullptr, false);
+    if (rc != GDN_OK) return rc;
+    if (flags & GDN_SEQUENTIAL) return fail(GDN_E_INVAL, "the time split runs on the chunked kernels only");
+    if (segments < 1) return fail(GDN_E_INVAL, "segments = %d, must be >= 1", segments);
+    const int64_t N = (T + s->C - 1) / s->C;
+    if (segments == 1 || N < 2) return gdn_chunk_forward(s, io, T, flags, state_out, hip_stream);
+    int nseg = (int)std::min<int64_t>(segments, N);
+    const int seg_steps = (int)((N + nseg - 1) / nseg);
+    nseg = (int)((N + seg_steps - 1) / seg_steps);   // no empty segment
+    int64_t need = 0;
+    if (__builtin_mul_overflow((int64_t)3 * nseg, s->state_elems, &need))
+        return fail(GDN_E_SHAPE, "time-split workspace size overflows");
+    DeviceGuard dg(s->device);
+    if (dg.err != hipSuccess) return fail(GDN_E_HIP, "hipSetDevice(%d): %s", s->device, hipGetErrorString(dg.err));
+    if (s->seg_elems < need) {
+        // a larger split than before: the old workspace may still be in use by enqueued work
+        hipError_t e = hipDeviceSynchronize();
+        if (e == hipSuccess && s->seg_ws) e = hipFree(s->seg_ws);
+        s->seg_ws = nullptr;
+        s->seg_elems = 0;
+        if (e != hipSuccess) return fail(GDN_E_HIP, "time-split workspace release: %s", hipGetErrorString(e));
+        e = hipMalloc(&s->seg_ws, need * sizeof(float));
+        if (e != hipSuccess) {
+            s->seg_ws = nullptr;
+            return fail(GDN_E_NOMEM, "time-split workspace (%lld bytes): %s", (long long)(need * 4), hipGetErrorString(e));
+        }
+        s->seg_elems = need;
+    }
+    hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+    const bool commit = !(flags & GDN_NO_COMMIT);
+    gdn::Params p = base_params(s, io, T);
+    p.S_in = s->state;
+    p.S_out[0] = commit ? s->state : state_out;
+    p.dir0 = 0;
+    p.ndirs = 1;
+    p.nseg = nseg;
+    p.seg_steps = seg_steps;
+    p.seg_out = s->seg_ws + (int64_t)nseg * s->state_elems;
+    return run(s, p, flags, st, s->seg_ws);
 }
 
 GDN_API int gdn_chunk_reverse(gdn_stream* s, const gdn_io* io, int64_t T, uint32_t flags, float* state_out,

@@ -36,7 +36,23 @@ struct Params {
     int gate_log;          // a holds log a_t instead of a_t
     int spin_limit;        // polls before a wavefront gives up waiting for another
     int* err;              // error word (host memory): set to 1 when a wait gives up
+    // Time split of the forward scan (dir0 = 0, ndirs = 1): nseg segments of seg_steps steps (the
+    // last one shorter), states [B, H, Dv, Dk] per entry.
+    //   seg_mode 0: the plain scan (the fields below unused)
+    //   seg_mode 1: every segment twice, from a zero state (variant 0) and from the identity with
+    //               v read as zero (variant 1); outputs dropped; final states to
+    //               seg_out[2 sigma + variant]
+    //   seg_mode 2: segment sigma from S_in (sigma = 0) or seg_in[sigma]; outputs written; the last
+    //               segment's final state to S_out[0]
+    int seg_mode, nseg, seg_steps;
+    const float* seg_in;
+    float* seg_out;
 };
+// Scan workgroups per (stream-head, row slice): directions, or the segments (and variants) of a
+// time split.
+inline int scan_variants(const Params& p) {
+    return p.seg_mode == 1 ? 2 * p.nseg : p.seg_mode == 2 ? p.nseg : p.ndirs;
+}
 
 // Bytes of one workspace item for sub-chunk C (multiple of 16, 16..64).
 int64_t chunk_item_bytes(int C, int D);
@@ -141,6 +157,9 @@ int gemm_e4m3_tile_features(int64_t M, int64_t N, int cus);
 hipError_t launch_zero(float* x, int64_t n, hipStream_t s);
 hipError_t launch_sequential(const Params& p, hipStream_t s, Timing* tm);
 hipError_t launch_chunked(const Params& p, hipStream_t s, Timing* tm);
+// The forward scan as a time split (p.seg_mode 0, p.nseg segments of p.seg_steps steps, p.seg_out
+// set; seg_in: [nseg][B][H][D][D] for the segments' start states).
+hipError_t launch_split(const Params& p, float* seg_in, hipStream_t s, Timing* tm);
 hipError_t launch_backward(const Params& p, const BwdParams& g, hipStream_t s, Timing* tm);
 
 }  // namespace gdn

@@ -389,8 +389,11 @@ __global__ __launch_bounds__(128 * NB) __attribute__((amdgpu_waves_per_eu(8))) v
     // read from
     const int nsub = (int)((p.T + C - 1) / C);
     const int ngrp = (nsub + GDN_PREP_BLOCKS - 1) / GDN_PREP_BLOCKS;   // block groups per stream-head
-    const int xcd = blockIdx.x & 7, kk = blockIdx.x >> 3;
-    const int jg = kk % ngrp, bh = xcd_head(xcd, kk / ngrp, p.B * p.H);
+    // (for a time split, whose point is to use the whole chip when the stream-heads are few, the
+    // blocks are spread over all XCDs instead)
+    const int xcd = blockIdx.x & 7, kk = p.seg_mode ? (int)blockIdx.x : (int)(blockIdx.x >> 3);
+    const int jg = kk % ngrp;
+    const int bh = p.seg_mode ? (kk / ngrp < p.B * p.H ? kk / ngrp : -1) : xcd_head(xcd, kk / ngrp, p.B * p.H);
     if (bh < 0) return;
     const int b = bh / p.H, h = bh - b * p.H;
     const int T = (int)p.T;
@@ -928,7 +931,7 @@ __host__ __device__ constexpr int out_tile(int O, int tt) {
 
 template <int NB, int ND, int O>
 __device__ __forceinline__ void scan_output(const Params& p, ScanLds<NB, ND>& L, ScanCtr& K, int lane, int b, int h, int dir, int T,
-                                            int N, int row0, const char* item0, int64_t ib) {
+                                            int N, int row0, const char* item0, int64_t ib, int t0, int To) {
     using G = ScanGeom<NB, ND>;
     constexpr int C = G::C, D = G::D, NKD = G::NKD, NKF = G::NKF, NKT = G::NKT, NF = G::NF, TPO = G::TPO;
     using BK = Blocks<NB>;
@@ -942,8 +945,9 @@ __device__ __forceinline__ void scan_output(const Params& p, ScanLds<NB, ND>& L,
     };
     // o is bf16, or fp32 when the call's I/O is fp32 (its q, k, v were staged as bf16)
     const int oesz = p.io_f32 ? 4 : 2;
-    const StepRows orow{reinterpret_cast<const char*>(p.o[dir]) + ((int64_t)b * p.os[0] + (int64_t)h * p.os[2]) * oesz,
-                        p.os[1] * oesz, T, C, N, dir, oesz * D};
+    // (To = 0 for the first stage of a time split: a resource of no rows drops every store)
+    const StepRows orow{reinterpret_cast<const char*>(p.o[dir]) + ((int64_t)b * p.os[0] + (int64_t)h * p.os[2] + (int64_t)t0 * p.os[1]) * oesz,
+                        p.os[1] * oesz, To, C, N, dir, oesz * D};
     int ooff[TPO];
 #pragma unroll
     for (int tt = 0; tt < TPO; ++tt) ooff[tt] = orow.row(16 * out_tile<NB>(O, tt) + r) + oesz * (row0 + 4 * g);   // token, state rows row0 + 4g ..
@@ -1130,17 +1134,28 @@ __global__ __launch_bounds__((ScanGeom<NB, ND>::THREADS)) void gdn_scan_kernel(P
     // Workgroup id % 8 is the XCD it runs on.  Both directions and all NS slices of stream-head
     // bh run on its XCD (xcd_head, with the prep workgroups of that head), so that they share
     // its L2.
+    // The workgroups of a stream-head: its directions, or the segments (and, for the first stage
+    // of a time split, their two variants) of its forward scan.
+    // A time split spreads its workgroups over all XCDs instead (its point is to use the whole
+    // chip when the stream-heads are few).
     const int id = blockIdx.x, xcd = id & 7, slot = id >> 3;
-    const int j = slot % NS, rest = slot / NS;
-    const int bh = xcd_head(xcd, rest / p.ndirs, ngroups);
+    const int nv = p.seg_mode == 1 ? 2 * p.nseg : p.seg_mode == 2 ? p.nseg : p.ndirs;
+    const int j = (p.seg_mode ? id : slot) % NS, rest = (p.seg_mode ? id : slot) / NS;
+    const int bh = p.seg_mode ? (rest / nv < ngroups ? rest / nv : -1) : xcd_head(xcd, rest / nv, ngroups);
     if (bh < 0) return;
-    const int dir = p.dir0 + rest % p.ndirs;
+    const int vi = rest % nv;
+    const int dir = p.seg_mode ? 0 : p.dir0 + vi;
+    const int sigma = p.seg_mode == 1 ? (vi >> 1) : p.seg_mode == 2 ? vi : 0;
+    const int variant = p.seg_mode == 1 ? (vi & 1) : 0;   // 0: from a zero state, 1: from the identity with v = 0
     const int h = bh % p.H, b = bh / p.H;
-    const int T = (int)p.T;
-    const int N = (T + C - 1) / C;
+    // a segment is scanned as a sequence of its own: from its first step n0 (token t0), with the
+    // tokens from there on and its own number of steps
+    const int n0 = sigma * p.seg_steps, t0 = n0 * C;
+    const int T = (int)p.T - t0;
+    const int N = p.seg_mode ? min(p.seg_steps, ((int)p.T + C - 1) / C - n0) : (T + C - 1) / C;
     const int row0 = 16 * GDN_COLS * j;
-    const char* item0 = p.ws + (((int64_t)dir * p.B + b) * p.H + h) * p.nsub_max * p.ws_item_bytes;
     const int64_t ib = p.ws_item_bytes;
+    const char* item0 = p.ws + (((int64_t)dir * p.B + b) * p.H + h) * p.nsub_max * ib + (int64_t)n0 * ib;
 
     if (threadIdx.x == 0) {
 #pragma unroll
@@ -1161,12 +1176,16 @@ __global__ __launch_bounds__((ScanGeom<NB, ND>::THREADS)) void gdn_scan_kernel(P
         // are in flight in two register sets: the loads of step m + 1 are issued before those of
         // step m are waited for (the loads of a wavefront complete in order).
         const int part = wave - (GDN_COLS + NOUT);
-        const StepRows krow{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.k) + (int64_t)b * p.ks[0] + (int64_t)h * p.ks[2]),
+        const StepRows krow{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.k) + (int64_t)b * p.ks[0] +
+                                                          (int64_t)h * p.ks[2] + (int64_t)t0 * p.ks[1]),
                             p.ks[1] * 2, T, C, N, dir, 2 * D};
-        const StepRows qrow{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.q) + (int64_t)b * p.qs[0] + (int64_t)h * p.qs[2]),
+        const StepRows qrow{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.q) + (int64_t)b * p.qs[0] +
+                                                          (int64_t)h * p.qs[2] + (int64_t)t0 * p.qs[1]),
                             p.qs[1] * 2, T, C, N, dir, 2 * D};
-        const StepRows vrow{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.v) + (int64_t)b * p.vs[0] + (int64_t)h * p.vs[2]),
-                            p.vs[1] * 2, T, C, N, dir, 2 * D};
+        // the identity variant of a split reads v as zero (a resource of no rows)
+        const StepRows vrow{reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.v) + (int64_t)b * p.vs[0] +
+                                                          (int64_t)h * p.vs[2] + (int64_t)t0 * p.vs[1]),
+                            p.vs[1] * 2, variant ? 0 : T, C, N, dir, 2 * D};
         const StepRows& rows = part == 0 ? krow : qrow;
         // destination chunk 64 i + lane of a block of rows: row t, position pos; the source chunk
         // is pos ^ sw(t, pos) (the permutation is an involution within its group of chunks)
@@ -1255,12 +1274,12 @@ __global__ __launch_bounds__((ScanGeom<NB, ND>::THREADS)) void gdn_scan_kernel(P
         return;
     }
     if (wave == GDN_COLS) {
-        scan_output<NB, ND, 0>(p, L, K, lane, b, h, dir, T, N, row0, item0, ib);
+        scan_output<NB, ND, 0>(p, L, K, lane, b, h, dir, T, N, row0, item0, ib, t0, p.seg_mode == 1 ? 0 : T);
         return;
     }
     if constexpr (NOUT > 1) {
         if (wave == GDN_COLS + 1) {
-            scan_output<NB, ND, 1>(p, L, K, lane, b, h, dir, T, N, row0, item0, ib);
+            scan_output<NB, ND, 1>(p, L, K, lane, b, h, dir, T, N, row0, item0, ib, t0, p.seg_mode == 1 ? 0 : T);
             return;
         }
     }
@@ -1272,12 +1291,21 @@ __global__ __launch_bounds__((ScanGeom<NB, ND>::THREADS)) void gdn_scan_kernel(P
     const int cc = wave;
     const bool tile_ok = row0 + 16 * cc < p.Dv;
     f32x4 P[ND];   // P[m][i] = S[row0 + 16 cc + r][dperm(m, 4 g + i)]
-    const float* Sin = (dir == 0) ? p.S_in : nullptr;
+    // start state: the forward scan's S_in, zero for the reverse scan; for a time split, zero or the
+    // identity (first stage) or the segment's start state (last stage)
+    const int64_t selems = (int64_t)p.B * p.H * D * D;
+    const float* Sin = p.seg_mode == 1 ? nullptr
+                       : p.seg_mode == 2 ? p.seg_in + sigma * selems
+                       : (dir == 0) ? p.S_in : nullptr;
     const int64_t hbase = ((int64_t)b * p.H + h) * D * D;
     const int64_t srow = hbase + (int64_t)(row0 + 16 * cc + r) * D;
 #pragma unroll
     for (int m = 0; m < ND; ++m) {
-        if (Sin && tile_ok)
+        if (variant) {
+            const int srw = row0 + 16 * cc + r;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) P[m][i] = (tile_ok && srw == dperm<ND>(m, 4 * g + i)) ? 1.f : 0.f;
+        } else if (Sin && tile_ok)
             P[m] = *reinterpret_cast<const f32x4*>(Sin + srow + dperm<ND>(m, 4 * g));
         else
             P[m] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1488,7 +1516,9 @@ __global__ __launch_bounds__((ScanGeom<NB, ND>::THREADS)) void gdn_scan_kernel(P
             read_kf(reinterpret_cast<const char*>(&L.ops[(n + 1) % GDN_OPS].k[0][0]), kf, kh);
         }
     }
-    float* Sout = p.S_out[dir];
+    float* Sout = p.seg_mode == 1 ? p.seg_out + (2 * sigma + variant) * selems
+                  : p.seg_mode == 2 ? (sigma == p.nseg - 1 ? p.S_out[0] : nullptr)
+                  : p.S_out[dir];
     if (Sout && tile_ok) {
 #pragma unroll
         for (int m = 0; m < ND; ++m) *reinterpret_cast<f32x4*>(Sout + srow + dperm<ND>(m, 4 * g)) = P[m];
@@ -1523,6 +1553,68 @@ hipError_t launch_zero(float* x, int64_t n, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Second stage of a time split: per (stream-head, 16 state rows), serially over the segments,
+// S_{s+1} = S_s P_s + D_s in fp32 (rows of S evolve independently), from S_0 = S_in (zero if
+// null).  (D_s, P_s) = seg_out[2 s], seg_out[2 s + 1]; S_s goes to seg_in[s] (S_0 too, so that the
+// last stage never reads S_in, which its last segment may overwrite).  P_s is staged in LDS (the
+// next segment's P loaded into registers while this one is applied); thread t owns column t % 128
+// of rows 8 (t / 128) .. +7; the k-sum runs in index order.
+constexpr int SPLIT_PLD = (128 * 128 / 4 + 255) / 256;   // float4 loads of a P per thread (D <= 128)
+__global__ __launch_bounds__(256) void gdn_split_combine_kernel(Params p, float* seg_in) {
+    const int D = p.Dk, nrb = D / 16;
+    const int rb = blockIdx.x % nrb, bh = blockIdx.x / nrb;
+    const int64_t selems = (int64_t)p.B * p.H * D * D, hbase = (int64_t)bh * D * D;
+    __shared__ float srows[16][128];
+    __shared__ __align__(16) float ps[128 * 128];
+    const int tid = threadIdx.x, col = tid & 127, rg = tid >> 7;
+    const int nq = D * D / 4;   // float4 of a P
+    for (int e = tid; e < 16 * D; e += 256) {
+        const int i = e / D, c = e - i * D;
+        const float v = p.S_in ? p.S_in[hbase + (int64_t)(16 * rb + i) * D + c] : 0.f;
+        srows[i][c] = v;
+        seg_in[hbase + (int64_t)(16 * rb + i) * D + c] = v;
+    }
+    float4 pr[SPLIT_PLD];
+    auto load_p = [&](int sg) {
+        const float4* src = reinterpret_cast<const float4*>(p.seg_out + (2 * sg + 1) * selems + hbase);
+#pragma unroll
+        for (int i = 0; i < SPLIT_PLD; ++i) {
+            const int e = tid + 256 * i;
+            pr[i] = e < nq ? src[e] : float4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    if (p.nseg > 1) load_p(0);
+    for (int sg = 0; sg + 1 < p.nseg; ++sg) {
+#pragma unroll
+        for (int i = 0; i < SPLIT_PLD; ++i) {
+            const int e = tid + 256 * i;
+            if (e < nq) reinterpret_cast<float4*>(ps)[e] = pr[i];
+        }
+        __syncthreads();   // P_s and S_s in LDS
+        if (sg + 2 < p.nseg) load_p(sg + 1);
+        const float* Dm = p.seg_out + (2 * sg) * selems + hbase;
+        float acc[8];
+        if (col < D) {
+#pragma unroll
+            for (int ii = 0; ii < 8; ++ii) acc[ii] = Dm[(int64_t)(16 * rb + 8 * rg + ii) * D + col];
+            for (int k = 0; k < D; ++k) {
+                const float pk = ps[k * D + col];
+#pragma unroll
+                for (int ii = 0; ii < 8; ++ii) acc[ii] = fmaf(srows[8 * rg + ii][k], pk, acc[ii]);
+            }
+        }
+        __syncthreads();   // every read of S_s and P_s is done
+        if (col < D) {
+            float* out = seg_in + (sg + 1) * selems + hbase;
+#pragma unroll
+            for (int ii = 0; ii < 8; ++ii) {
+                srows[8 * rg + ii][col] = acc[ii];
+                out[(int64_t)(16 * rb + 8 * rg + ii) * D + col] = acc[ii];
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
@@ -1549,20 +1641,53 @@ hipError_t launch_sequential(const Params& p, hipStream_t s, Timing* tm) {
 }
 
 template <int NB, int ND>
-static hipError_t run_chunked(const Params& p, hipStream_t s, Timing* tm) {
+static hipError_t run_prep(const Params& p, hipStream_t s, Timing* tm) {
     const int nsub = (int)((p.T + 16 * NB - 1) / (16 * NB));
     tm_begin(tm, s, KPREP);
-    const int ngrp = (nsub + GDN_PREP_BLOCKS - 1) / GDN_PREP_BLOCKS;
-    hipLaunchKernelGGL((gdn_prep_kernel<NB, ND>), dim3(8 * ((p.B * p.H + 7) / 8) * ngrp), dim3(128 * NB), 0, s, p);
+    const int ngrp = nsub;
+    const int grid = p.seg_mode ? p.B * p.H * ngrp : 8 * ((p.B * p.H + 7) / 8) * ngrp;
+    hipLaunchKernelGGL((gdn_prep_kernel<NB, ND>), dim3(grid), dim3(128 * NB), 0, s, p);
     tm_end(tm, s);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int ngroups = p.B * p.H;   // stream-heads; each has p.ndirs directions
-    const int grid = (ngroups + 7) / 8 * 8 * p.ndirs * ((ND + GDN_COLS - 1) / GDN_COLS);
+    return hipGetLastError();
+}
+
+template <int NB, int ND>
+static hipError_t run_scan(const Params& p, hipStream_t s, Timing* tm) {
+    const int ngroups = p.B * p.H;   // stream-heads; each has scan_variants(p) workgroups per row slice
+    const int ns = (ND + GDN_COLS - 1) / GDN_COLS;
+    const int grid = p.seg_mode ? ngroups * scan_variants(p) * ns : (ngroups + 7) / 8 * 8 * scan_variants(p) * ns;
     tm_begin(tm, s, KSCAN);
     hipLaunchKernelGGL((gdn_scan_kernel<NB, ND>), dim3(grid), dim3(ScanGeom<NB, ND>::THREADS), 0, s, p, ngroups);
     tm_end(tm, s);
     return hipGetLastError();
+}
+
+template <int NB, int ND>
+static hipError_t run_chunked(const Params& p, hipStream_t s, Timing* tm) {
+    hipError_t e = run_prep<NB, ND>(p, s, tm);
+    if (e != hipSuccess) return e;
+    return run_scan<NB, ND>(p, s, tm);
+}
+
+// The forward scan in p.nseg segments (p.seg_steps steps each): every segment from a zero state and
+// from the identity (v = 0) at once, the segments' start states by the serial combine, then every
+// segment again from its start state, writing o.  seg_in: [nseg][B][H][D][D] (entry 0 unused),
+// p.seg_out: [2 nseg][B][H][D][D].
+template <int NB, int ND>
+static hipError_t run_split(const Params& p, float* seg_in, hipStream_t s, Timing* tm) {
+    Params pa = p;
+    pa.seg_mode = 1;
+    hipError_t e = run_prep<NB, ND>(pa, s, tm);
+    if (e != hipSuccess) return e;
+    e = run_scan<NB, ND>(pa, s, tm);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gdn_split_combine_kernel, dim3((unsigned)(p.B * p.H * (p.Dk / 16))), dim3(256), 0, s, p, seg_in);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    Params pc = p;
+    pc.seg_mode = 2;
+    pc.seg_in = seg_in;
+    return run_scan<NB, ND>(pc, s, tm);
 }
 
 template <int NB>
@@ -1603,21 +1728,54 @@ hipError_t scratch_address(int device, char** out) {
     return hipSuccess;
 }
 
+template <int NB>
+static hipError_t run_split_d(const Params& p, float* seg_in, hipStream_t s, Timing* tm) {
+    switch (p.Dk) {
+        case 16: return run_split<NB, 1>(p, seg_in, s, tm);
+        case 32: return run_split<NB, 2>(p, seg_in, s, tm);
+        case 64: return run_split<NB, 4>(p, seg_in, s, tm);
+        case 112: return run_split<NB, 7>(p, seg_in, s, tm);
+        case 128: return run_split<NB, 8>(p, seg_in, s, tm);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// bf16 staging copies of fp32 q, k, v; p then points at them
+static hipError_t stage_f32(Params& p, const Params& p0, hipStream_t s) {
+    if (!p.conv) return hipErrorInvalidValue;
+    const int64_t per = (int64_t)p.B * p.T * p.H * p.Dk;
+    int64_t blocks = (3 * per + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(gdn_to_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p0, p.conv);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    p.q = p.conv;
+    p.k = p.conv + per;
+    p.v = p.conv + 2 * per;
+    const int64_t st[3] = {p.T * p.H * p.Dk, (int64_t)p.H * p.Dk, p.Dk};
+    for (int i = 0; i < 3; ++i) p.qs[i] = p.ks[i] = p.vs[i] = st[i];
+    return hipSuccess;
+}
+
+hipError_t launch_split(const Params& p0, float* seg_in, hipStream_t s, Timing* tm) {
+    Params p = p0;
+    if (p.io_f32) {
+        const hipError_t e = stage_f32(p, p0, s);
+        if (e != hipSuccess) return e;
+    }
+    switch (p.C) {
+        case 16: return run_split_d<1>(p, seg_in, s, tm);
+        case 32: return run_split_d<2>(p, seg_in, s, tm);
+        case 64: return run_split_d<4>(p, seg_in, s, tm);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_chunked(const Params& p0, hipStream_t s, Timing* tm) {
     Params p = p0;
     if (p.io_f32) {
-        if (!p.conv) return hipErrorInvalidValue;
-        const int64_t per = (int64_t)p.B * p.T * p.H * p.Dk;
-        int64_t blocks = (3 * per + 255) / 256;
-        if (blocks > 8192) blocks = 8192;
-        hipLaunchKernelGGL(gdn_to_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p0, p.conv);
-        hipError_t e = hipGetLastError();
+        const hipError_t e = stage_f32(p, p0, s);
         if (e != hipSuccess) return e;
-        p.q = p.conv;
-        p.k = p.conv + per;
-        p.v = p.conv + 2 * per;
-        const int64_t st[3] = {p.T * p.H * p.Dk, (int64_t)p.H * p.Dk, p.Dk};
-        for (int i = 0; i < 3; ++i) p.qs[i] = p.ks[i] = p.vs[i] = st[i];
     }
     switch (p.C) {
         case 16: return run_chunked_d<1>(p, s, tm);

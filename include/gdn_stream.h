@@ -132,6 +132,26 @@ GDN_API int gdn_stream_destroy(gdn_stream* s);
 GDN_API int gdn_chunk_forward(gdn_stream* s, const gdn_io* io, int64_t T, uint32_t flags,
                               float* state_out, void* hip_stream);
 
+/* The causal forward scan of gdn_chunk_forward, split in time (the three-stage pipeline of
+ * the Chinese summary, "Method steps", step 4, in our reading: segment summaries, a serial
+ * pass over them, then each segment from its start state).  The chunk's ceil(T / C) steps
+ * are cut into `segments` consecutive segments of equal length (the last one shorter;
+ * `segments` is lowered to the number of steps if larger, and to the smallest count of that
+ * length with no empty segment).  Three launches after the prep: every segment from a zero
+ * state (its state contribution D) and from the identity with v read as zero (the product P
+ * of its transitions), all at once; per stream-head the start states S_{s+1} = S_s P_s + D_s
+ * in fp32, serially over the segments from the cached state; every segment again from its
+ * start state, writing o.  Same result as gdn_chunk_forward up to rounding, with about three
+ * times its scan work spread over `segments` times as many workgroups: it pays when the
+ * stream-heads B H are few and the chunk is long (the plain scan then leaves most of the chip
+ * idle).  Arguments, flags (GDN_SEQUENTIAL is rejected with GDN_E_INVAL), cache handling and
+ * state_out as for gdn_chunk_forward.  segments = 1, or a chunk of one step, runs
+ * gdn_chunk_forward.  Workspace: 3 x segments states [B, H, d_v, d_k] fp32, allocated by the
+ * first call that needs it (and again, after waiting for the device, by a call that needs
+ * more).  Errors: as gdn_chunk_forward, GDN_E_INVAL for segments < 1, GDN_E_NOMEM. */
+GDN_API int gdn_chunk_forward_split(gdn_stream* s, const gdn_io* io, int64_t T, int segments, uint32_t flags,
+                                    float* state_out, void* hip_stream);
+
 /* Backward scan inside the chunk: t = T-1 .. 0 from a zero state, each token
  * with its own a_t and beta_t.  Writes o; never reads or writes the cache.
  * state_out (may be NULL) receives the state after absorbing token 0. */

@@ -77,6 +77,7 @@ def test_null_arguments_are_rejected(lib):
         assert fn(None, ctypes.byref(io), 1, 0, None, None) == binding.GDN_E_INVAL
         assert "handle" in binding.gdn_last_error()
     assert lib.gdn_chunk_bidir(None, ctypes.byref(io), None, 1, 0, None, None) == binding.GDN_E_INVAL
+    assert lib.gdn_chunk_forward_split(None, ctypes.byref(io), 1, 2, 0, None, None) == binding.GDN_E_INVAL
     assert lib.gdn_state_get(None, None, None) == binding.GDN_E_INVAL
     assert lib.gdn_state_set(None, None, None) == binding.GDN_E_INVAL
     assert lib.gdn_stream_destroy(None) == binding.GDN_OK
