@@ -1454,6 +1454,11 @@ __global__ __launch_bounds__((ScanGeom<NB, ND>::THREADS)) void gdn_scan_kernel(P
         for (int mt = 0; mt < NB; ++mt)
 #pragma unroll
             for (int ks = 0; ks < NKD; ++ks) keep_alive(kf[mt][ks]);
+        // the next step's K rows, read while U and the update run
+        if (n + 1 < N) {
+            if (ld_early < n + 2) wait_counter<false>(&K.loaded[0], n + 2, p.spin_limit, p.err);
+            read_kf(reinterpret_cast<const char*>(&L.ops[(n + 1) % GDN_OPS].k[0][0]), kf, kh);
+        }
         // K^T fragments for the update (state index rows, token k-slots)
 #pragma unroll
         for (int m = 0; m < ND; ++m)
@@ -1510,11 +1515,6 @@ __global__ __launch_bounds__((ScanGeom<NB, ND>::THREADS)) void gdn_scan_kernel(P
         // every read of the operand slot of step n has been issued (and, the LDS being in order,
         // takes effect before this count)
         signal_counter(&K.cdone[cc], n + 1);
-        // the next step's K rows, read while the update runs
-        if (n + 1 < N) {
-            if (ld_early < n + 2) wait_counter<false>(&K.loaded[0], n + 2, p.spin_limit, p.err);
-            read_kf(reinterpret_cast<const char*>(&L.ops[(n + 1) % GDN_OPS].k[0][0]), kf, kh);
-        }
     }
     float* Sout = p.seg_mode == 1 ? p.seg_out + (2 * sigma + variant) * selems
                   : p.seg_mode == 2 ? (sigma == p.nseg - 1 ? p.S_out[0] : nullptr)
