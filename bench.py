@@ -632,7 +632,7 @@ def main_backward(args):
                      "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": None, "kernel": "gdn_bwd_rows_kernel + "
                      "gdn_bwd_reduce_kernel", "kernel_avg_us": round(launch_ms * 1e3, 1),
                      "algorithmic_bytes_per_launch": int(alg_bytes / 2),
-                     "note": "latency-bound by the serial chain of T tokens per (head, 16-row block)"},
+                     "note": "latency-bound by the serial chain of T tokens per (head, 4-row block)"},
     }
     if not args.no_cpu:
         import oracle

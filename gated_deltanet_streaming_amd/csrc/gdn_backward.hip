@@ -49,22 +49,22 @@ void tm_end(Timing* tm, hipStream_t s) {
 //     dv_t = beta_t gk,  da_t = <G, S_{t-1}> - beta_t gk.x,  dbeta_t = gk.(v_t - a_t x)
 //     dk_t = beta_t G^T (v_t - a_t x) - a_t beta_t S_{t-1}^T gk,  dq_t = scale S_t^T do_t
 //     G <- a_t (G - beta_t gk k_t^T)
-// gdn_bwd_rows_kernel: one 64-lane workgroup per (b, h, block of 8 state rows);
-// lane l owns row 8 rb + l/8 and the columns 16 j + 2 (l%8) + e (e < 2) of every
-// 16-column group j, one float2 per group.  Tokens are staged through LDS in
+// gdn_bwd_rows_kernel: one 64-lane workgroup per (b, h, block of 4 state rows);
+// lane l owns row 4 rb + l/16 and the column 16 j + l%16 of every 16-column
+// group j.  Tokens are staged through LDS in
 // blocks of TB (k and q normalised once per block; the next block's global loads
 // go out before the current block is worked on).  A forward pass keeps only the
 // state before every block (a checkpoint); the backward pass walks the blocks in
 // reverse, recomputes the states inside a block from its checkpoint into LDS and
 // then walks its tokens backward.  dv and the start-state gradient are row-local;
 // the other gradients sum over all rows: per token the rows' terms go through an
-// LDS buffer and each lane adds one float4 column group over the 8 rows in row
+// LDS buffer and each lane adds one float4 column group over the 4 rows in row
 // order, then the workgroup writes its rows' partial sums, and gdn_bwd_reduce_kernel
 // adds the row blocks in a fixed order and maps the normalised-vector gradients
 // back through the L2 normalisation.
 // ---------------------------------------------------------------------------
 constexpr int kMinTB = 14;   // smallest token block of any instance (sizes the checkpoints)
-constexpr int kRB = 8;       // state rows per workgroup
+constexpr int kRB = 4;       // state rows per workgroup
 constexpr int kLPR = 64 / kRB;   // lanes per state row
 
 int64_t backward_ckpt_per(int64_t max_tokens) { return (max_tokens + kMinTB - 1) / kMinTB + 1; }
@@ -87,18 +87,17 @@ int64_t backward_ws_bytes(int B, int H, int Dk, int Dv, int64_t max_tokens) {
 
 namespace {
 
-// sum over the 8 lanes of one state row (lane bits 0..2): quad permutations [1,0,3,2] and
-// [2,3,0,1], then the mirror within the 8-lane half row
-__device__ __forceinline__ float sum8(float x) {
+// sum over the 16 lanes of one state row (lane bits 0..3): quad permutations [1,0,3,2] and
+// [2,3,0,1], then the mirror within each 8-lane half row, then the mirror of the whole row
+__device__ __forceinline__ float sum16(float x) {
     x += dpp<0xB1>(x);
     x += dpp<0x4E>(x);
     x += dpp<0x141>(x);   // row_half_mirror
+    x += dpp<0x140>(x);   // row_mirror
     return x;
 }
-// sum over the 8 rows of the workgroup (lane bits 3..5): the two rows of each 16-lane DPP row by
-// one rotation (lanes j, j-8), then across the four DPP rows with lane swaps
+// sum over the 4 rows of the workgroup (lane bits 4..5): across the four DPP rows with lane swaps
 __device__ __forceinline__ float sum_rows(float x) {
-    x += dpp<0x128>(x);   // row_ror:8
     const unsigned u = __float_as_uint(x);
     const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
     x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
@@ -108,12 +107,6 @@ __device__ __forceinline__ float sum_rows(float x) {
 }
 
 __device__ __forceinline__ float dot4(const float4& a, const float4& b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; }
-// acc += a * b componentwise: two independent chains for a dot product over many float2
-__device__ __forceinline__ void fma2(float2& acc, const float2& a, const float2& b) {
-    acc.x += a.x * b.x;
-    acc.y += a.y * b.y;
-}
-__device__ __forceinline__ float hsum2(const float2& a) { return a.x + a.y; }
 
 // raw buffer resource over [base, base + bytes); loads beyond it return zero
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
@@ -145,7 +138,7 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g)
     const int nblk = (T + TB - 1) / TB;
     const int wid = 2 * DK + 4;
 
-    __shared__ __align__(16) float2 sst[TB][NG][64];   // S_{t-1} of the block's tokens, lane-major
+    __shared__ __align__(16) float sst[TB][NG][64];    // S_{t-1} of the block's tokens, lane-major
     __shared__ __align__(16) float skn[TB][DK];        // normalised k of the block's tokens
     __shared__ __align__(16) float sqn[TB][DK];        // normalised q
     __shared__ __align__(16) float scol[2][kRB][DK];   // per-row terms of dq and dk of one token
@@ -161,8 +154,7 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g)
     constexpr int ESZ = F32 ? 4 : 2, EPC = 16 / ESZ;   // bytes per element, elements per chunk
     constexpr int CPR = DK / EPC, NCH = TB * CPR;        // chunks per k/q row, per block
     constexpr int NLC = (NCH + 63) / 64;                 // k (q) chunks per lane
-    constexpr int VCPR = kRB / EPC, NVC = TB * VCPR;     // chunks of a token's kRB v (d_o) values, per block
-    static_assert(NVC <= 64, "one v chunk per lane");
+    static_assert(TB <= 64 && kRB == 4, "lane ti < TB loads token ti's 4 v (d_o) values");
     const char* kb = static_cast<const char*>(p.k) + ((int64_t)b * p.ks[0] + (int64_t)h * p.ks[2]) * ESZ;
     const char* qb = static_cast<const char*>(p.q) + ((int64_t)b * p.qs[0] + (int64_t)h * p.qs[2]) * ESZ;
     const char* vb = static_cast<const char*>(p.v) + ((int64_t)b * p.vs[0] + (int64_t)h * p.vs[2] + kRB * rb) * ESZ;
@@ -187,12 +179,21 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g)
                 rq[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(qrs, ok ? t * qsb + 16 * c : OUT, 0, 0));
         }
         {
-            const int ti = lane / VCPR, c = lane - ti * VCPR;
-            const bool ok = lane < NVC && pi0 + ti < T;
-            const int t = ok ? tok(pi0 + ti) : 0;
-            rv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, ok ? t * vsb + 16 * c : OUT, 0, 0));
-            if (with_q)
-                rdo = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ors, ok ? t * osb + 16 * c : OUT, 0, 0));
+            // token ti = lane: its 4 v (d_o) values, 16 bytes (fp32) or 8 bytes as two dwords (bf16)
+            const bool ok = lane < TB && pi0 + lane < T;
+            const int t = ok ? tok(pi0 + lane) : 0;
+            const int vo = ok ? t * vsb : OUT, oo = ok ? t * osb : OUT;
+            if constexpr (F32) {
+                rv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, vo, 0, 0));
+                if (with_q) rdo = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ors, oo, 0, 0));
+            } else {
+                rv.x = __builtin_amdgcn_raw_buffer_load_b32(vrs, vo, 0, 0);
+                rv.y = __builtin_amdgcn_raw_buffer_load_b32(vrs, ok ? vo + 4 : OUT, 0, 0);
+                if (with_q) {
+                    rdo.x = __builtin_amdgcn_raw_buffer_load_b32(ors, oo, 0, 0);
+                    rdo.y = __builtin_amdgcn_raw_buffer_load_b32(ors, ok ? oo + 4 : OUT, 0, 0);
+                }
+            }
         }
         ra = 1.f;
         rbt = 0.f;
@@ -216,6 +217,13 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g)
                            __uint_as_float(w[2 * k2 + 1] << 16), __uint_as_float(w[2 * k2 + 1] & 0xffff0000u)};
         }
     };
+    // a token's 4 v (d_o) values as fp32 (fp32: the 16 bytes as loaded; bf16: the two dwords)
+    auto put4 = [&](float* dst, const uint4& raw) {
+        if constexpr (F32) *reinterpret_cast<float4*>(dst) = __builtin_bit_cast(float4, raw);
+        else
+            *reinterpret_cast<float4*>(dst) = float4{__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xffff0000u),
+                                                     __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xffff0000u)};
+    };
     auto store_block = [&](bool with_q) {
 #pragma unroll
         for (int i = 0; i < NLC; ++i) {
@@ -225,10 +233,9 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g)
                 if (with_q) put_chunk(&sqn[ti][EPC * c], rq[i]);
             }
         }
-        if (lane < NVC) {
-            const int ti = lane / VCPR, c = lane - ti * VCPR;
-            put_chunk(&sv[ti][EPC * c], rv);
-            if (with_q) put_chunk(&sdo[ti][EPC * c], rdo);
+        if (lane < TB) {
+            put4(&sv[lane][0], rv);
+            if (with_q) put4(&sdo[lane][0], rdo);
         }
         if (lane < TB) {
             sa[lane] = ra;
@@ -262,37 +269,39 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g)
         }
         lds_order();
     };
-    // columns of this lane in staged row r: 16 j + 2 part .. +1
-    auto krow = [&](int r, int j) { return *reinterpret_cast<const float2*>(&skn[r][16 * j + 2 * part]); };
-    auto qrow = [&](int r, int j) { return *reinterpret_cast<const float2*>(&sqn[r][16 * j + 2 * part]); };
-    auto ckp = [&](int blk, int j) { return reinterpret_cast<float2*>(ck + ((int64_t)blk * kRB + rl) * DK + 16 * j + 2 * part); };
+    // column of this lane in staged row r: 16 j + part
+    auto krow = [&](int r, int j) { return skn[r][16 * j + part]; };
+    auto qrow = [&](int r, int j) { return sqn[r][16 * j + part]; };
+    auto ckp = [&](int blk, int j) { return ck + ((int64_t)blk * kRB + rl) * DK + 16 * j + part; };
+    // a dot product over the lane's NG columns in two independent chains, then over the row's lanes
+    auto rowdot = [&](const float* a, const float* c) {
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int j = 0; j < NG; ++j) {
+            if (j & 1) s1 += a[j] * c[j];
+            else s0 += a[j] * c[j];
+        }
+        return sum16(s0 + s1);
+    };
 
     // one token of the forward recurrence on S (row dot and update); returns x = S k
-    float2 S[NG];
+    float S[NG];
     auto fwd_token = [&](int r) {
-        float2 kr[NG];
+        float kr[NG];
 #pragma unroll
         for (int j = 0; j < NG; ++j) kr[j] = krow(r, j);
         const float at = sa[r], bt = sb[r], vr = sv[r][rl];
-        float2 xa = {0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < NG; ++j) fma2(xa, S[j], kr[j]);
-        const float x = sum8(hsum2(xa));
+        const float x = rowdot(S, kr);
         const float c0 = bt * x, c1 = bt * vr;
 #pragma unroll
-        for (int j = 0; j < NG; ++j) {
-            const float2 kk = kr[j];
-            S[j].x = at * (S[j].x - c0 * kk.x) + c1 * kk.x;
-            S[j].y = at * (S[j].y - c0 * kk.y) + c1 * kk.y;
-        }
+        for (int j = 0; j < NG; ++j) S[j] = at * (S[j] - c0 * kr[j]) + c1 * kr[j];
         return x;
     };
 
     // ---- forward: checkpoints before every block ----
 #pragma unroll
     for (int j = 0; j < NG; ++j)
-        S[j] = g.state0 ? *reinterpret_cast<const float2*>(g.state0 + (((int64_t)b * p.H + h) * p.Dv + row) * DK + 16 * j + 2 * part)
-                        : float2{0.f, 0.f};
+        S[j] = g.state0 ? g.state0[(((int64_t)b * p.H + h) * p.Dv + row) * DK + 16 * j + part] : 0.f;
     if (nblk > 0) load_block(0, false);
     for (int blk = 0; blk < nblk; ++blk) {
         store_block(false);
@@ -304,11 +313,9 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g)
     }
 
     // ---- backward over the blocks in reverse ----
-    float2 G[NG];
+    float G[NG];
 #pragma unroll
-    for (int j = 0; j < NG; ++j)
-        G[j] = g.d_state ? *reinterpret_cast<const float2*>(g.d_state + (((int64_t)b * p.H + h) * p.Dv + row) * DK + 16 * j + 2 * part)
-                         : float2{0.f, 0.f};
+    for (int j = 0; j < NG; ++j) G[j] = g.d_state ? g.d_state[(((int64_t)b * p.H + h) * p.Dv + row) * DK + 16 * j + part] : 0.f;
     if (nblk > 0) load_block(nblk - 1, true);
     for (int blk = nblk - 1; blk >= 0; --blk) {
         store_block(true);
@@ -327,7 +334,7 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g)
         for (int r = n - 1; r >= 0; --r) {
             const int64_t t = tok(blk * TB + r);
             // every LDS operand of the token first, then the arithmetic
-            float2 Sp[NG], kr[NG], qr[NG];
+            float Sp[NG], kr[NG], qr[NG];
 #pragma unroll
             for (int j = 0; j < NG; ++j) {
                 Sp[j] = sst[r][j][lane];
@@ -337,42 +344,27 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g)
             const float dor = p.scale * sdo[r][rl];
             const float at = sa[r], bt = sb[r], vr = sv[r][rl], x = sx[r][rl];
 #pragma unroll
-            for (int j = 0; j < NG; ++j) {
-                const float2 qq = qr[j];
-                G[j].x += dor * qq.x;
-                G[j].y += dor * qq.y;
-            }
-            float2 gka = {0.f, 0.f}, gsa = {0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < NG; ++j) {
-                fma2(gka, G[j], kr[j]);
-                fma2(gsa, G[j], Sp[j]);
-            }
-            const float gk = sum8(hsum2(gka)), gs = sum8(hsum2(gsa));
+            for (int j = 0; j < NG; ++j) G[j] += dor * qr[j];
+            const float gk = rowdot(G, kr), gs = rowdot(G, Sp);
             if (part == 0) g.dv[(((int64_t)b * T + t) * p.H + h) * p.Dv + row] = bt * gk;
             // this row's terms of dq_t = scale S_t^T do_t and dk_t = beta G^T (v - a x) - a beta S_{t-1}^T gk
             const float wv = bt * (vr - at * x), ws = at * bt * gk;
 #pragma unroll
             for (int j = 0; j < NG; ++j) {
-                *reinterpret_cast<float2*>(&scol[0][rl][16 * j + 2 * part]) = float2{dor * S[j].x, dor * S[j].y};
-                *reinterpret_cast<float2*>(&scol[1][rl][16 * j + 2 * part]) =
-                    float2{wv * G[j].x - ws * Sp[j].x, wv * G[j].y - ws * Sp[j].y};
+                scol[0][rl][16 * j + part] = dor * S[j];
+                scol[1][rl][16 * j + part] = wv * G[j] - ws * Sp[j];
             }
             lds_order();
             const float cg = bt * gk;
 #pragma unroll
-            for (int j = 0; j < NG; ++j) {
-                const float2 kk = kr[j];
-                G[j].x = at * (G[j].x - cg * kk.x);
-                G[j].y = at * (G[j].y - cg * kk.y);
-            }
-            // per-row scalars (identical in the 8 lanes of a row; counted once)
+            for (int j = 0; j < NG; ++j) G[j] = at * (G[j] - cg * kr[j]);
+            // per-row scalars (identical in the 16 lanes of a row; counted once)
             float da = (part == 0) ? gs - bt * gk * x : 0.f;
             float db = (part == 0) ? gk * (vr - at * x) : 0.f;
             da = sum_rows(da);
             db = sum_rows(db);
             float* pw = g.partials + ((((int64_t)b * T + t) * p.H + h) * nrb + rb) * wid;
-            // column sums over the 8 rows, in row order: lane l adds float4 group l
+            // column sums over the 4 rows, in row order: lane l adds float4 group l
             if (lane < DK / 2) {
                 const int a = lane / (DK / 4), c4 = 4 * (lane - a * (DK / 4));
                 float4 acc = *reinterpret_cast<const float4*>(&scol[a][0][c4]);
@@ -398,7 +390,7 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g)
     if (g.d_state0) {
 #pragma unroll
         for (int j = 0; j < NG; ++j)
-            *reinterpret_cast<float2*>(g.d_state0 + (((int64_t)b * p.H + h) * p.Dv + row) * DK + 16 * j + 2 * part) = G[j];
+            g.d_state0[(((int64_t)b * p.H + h) * p.Dv + row) * DK + 16 * j + part] = G[j];
     }
 }
 
