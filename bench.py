@@ -569,7 +569,7 @@ def main_split(args):
 
 def main_backward(args):
     """Gradients of both scans of the 720p pair (forward from the carried state, reverse from
-    zero) through gdn_chunk_backward: a token-sequential fp32 path, bound by its serial chain
+    zero) in one gdn_chunk_backward_bidir call: a token-sequential fp32 path, bound by its serial chain
     of T steps per (head, row block), reported against the HBM roofline of its bytes."""
     import numpy as np
     import torch
@@ -590,9 +590,11 @@ def main_backward(args):
     s = gb.Stream(B, H, D, D, T, device=0)
     stream = torch.cuda.current_stream(dev)
 
+    gf, gr = s._grad_buffers(x["q"], x["v"]), s._grad_buffers(x["q"], x["v"])
+
     def step():
-        s.backward(x["q"], x["k"], x["v"], a, beta, dO[0], d_state=dSf, state0=S0, stream=stream)
-        s.backward(x["q"], x["k"], x["v"], a, beta, dO[1], reverse=True, stream=stream)
+        gb.gdn_chunk_backward_bidir(s.handle, x["q"], x["k"], x["v"], a, beta, dO[0], dO[1], gf, gr, d_state=dSf,
+                                    state0=S0, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -616,7 +618,8 @@ def main_backward(args):
     # gradient (fp32) for the forward scan, the start-state gradient for the reverse one
     per_tok = 4 * D * 2 + 2 * 4 + 3 * D * 4 + 2 * 4
     alg_bytes = 2 * B * T * H * per_tok + 4 * B * H * D * D * 4
-    achieved = alg_bytes / 2 / (launch_ms * 1e-3) / 1e9
+    # one timed launch pair (rows + reduce) computes both scans' gradients
+    achieved = alg_bytes / (launch_ms * 1e-3) / 1e9
     out = {
         "metric": "GDN backward (gradients of the forward and reverse scans) tokens/s per layer at 2640-token 720p chunk",
         "value": round(T / (ms_per_step * 1e-3), 1),
@@ -627,11 +630,11 @@ def main_backward(args):
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": "720p streaming chunk, one GDN layer: gradients of the forward scan (carried "
                                "state) and of the intra-chunk reverse scan", "B": B, "H": H, "d_k": D, "d_v": D,
-                   "T": T, "call": "gdn_chunk_backward x 2", "path": "token-sequential fp32"},
+                   "T": T, "call": "gdn_chunk_backward_bidir", "path": "token-sequential fp32"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": None, "kernel": "gdn_bwd_rows_kernel + "
                      "gdn_bwd_reduce_kernel", "kernel_avg_us": round(launch_ms * 1e3, 1),
-                     "algorithmic_bytes_per_launch": int(alg_bytes / 2),
+                     "algorithmic_bytes_per_launch": int(alg_bytes),
                      "note": "latency-bound by the serial chain of T tokens per (head, 4-row block)"},
     }
     if not args.no_cpu:

@@ -91,6 +91,8 @@ def load_library():
         "gdn_chunk_bidir": ([vp, ctypes.POINTER(GdnIo), vp, i64, u32, vp, vp], i32),
         "gdn_chunk_bidir_noalloc": ([ctypes.POINTER(GdnConfig), ctypes.POINTER(GdnIo), vp, i64, vp, vp, vp, vp], i32),
         "gdn_chunk_backward": ([vp, ctypes.POINTER(GdnIo), ctypes.POINTER(GdnGrad), i64, i32, vp], i32),
+        "gdn_chunk_backward_bidir": ([vp, ctypes.POINTER(GdnIo), ctypes.POINTER(GdnGrad), ctypes.POINTER(GdnGrad), i64, vp],
+                                     i32),
         "gdn_state_get": ([vp, vp, vp], i32),
         "gdn_state_set": ([vp, vp, vp], i32),
         "gdn_profile": ([vp, i32], i32),
@@ -240,12 +242,7 @@ def gdn_profile_read(handle, reset=True):
     return {KERNEL_NAMES[i]: (ms[i], n[i]) for i in range(GDN_KERNEL_COUNT)}
 
 
-def gdn_chunk_backward(handle, q, k, v, a, beta, d_o, grads, *, reverse=False, d_state=None, state0=None,
-                       stream=None):
-    """Gradients of one scan.  ``grads`` maps dq, dk, dv (fp32 [B, T, H, D], contiguous), da,
-    dbeta (fp32 [B, T, H], contiguous) and optionally d_state0 (fp32 [B, H, d_v, d_k]) to
-    the tensors to write."""
-    io = _make_io(q, k, v, d_o, a, beta)
+def _make_grad(d_o, grads, d_state, state0):
     for name in ("dq", "dk", "dv", "da", "dbeta"):
         t = grads[name]
         if not t.is_contiguous() or t.dtype.itemsize != 4:
@@ -257,8 +254,32 @@ def gdn_chunk_backward(handle, q, k, v, a, beta, d_o, grads, *, reverse=False, d
     g.dq, g.dk, g.dv = grads["dq"].data_ptr(), grads["dk"].data_ptr(), grads["dv"].data_ptr()
     g.da, g.dbeta = grads["da"].data_ptr(), grads["dbeta"].data_ptr()
     g.d_state0 = None if grads.get("d_state0") is None else grads["d_state0"].data_ptr()
+    return g
+
+
+def gdn_chunk_backward(handle, q, k, v, a, beta, d_o, grads, *, reverse=False, d_state=None, state0=None,
+                       stream=None):
+    """Gradients of one scan.  ``grads`` maps dq, dk, dv (fp32 [B, T, H, D], contiguous), da,
+    dbeta (fp32 [B, T, H], contiguous) and optionally d_state0 (fp32 [B, H, d_v, d_k]) to
+    the tensors to write."""
+    io = _make_io(q, k, v, d_o, a, beta)
+    g = _make_grad(d_o, grads, d_state, state0)
     _check(load_library().gdn_chunk_backward(ctypes.c_void_p(handle), ctypes.byref(io), ctypes.byref(g), q.shape[1],
                                              int(bool(reverse)), _stream_ptr(stream, q.device)))
+
+
+def gdn_chunk_backward_bidir(handle, q, k, v, a, beta, d_o_fwd, d_o_rev, grads_fwd, grads_rev, *, d_state=None,
+                             state0=None, d_state_rev=None, stream=None):
+    """Gradients of both scans of a bidirectional call in one launch pair: the forward scan's
+    (d_o_fwd, d_state, state0) into ``grads_fwd`` and the reverse scan's (d_o_rev, d_state_rev)
+    into ``grads_rev`` (dicts as for gdn_chunk_backward; d_o_rev must have d_o_fwd's strides)."""
+    if tuple(d_o_rev.stride()) != tuple(d_o_fwd.stride()):
+        raise ValueError("d_o_fwd and d_o_rev must have the same strides")
+    io = _make_io(q, k, v, d_o_fwd, a, beta)
+    gf = _make_grad(d_o_fwd, grads_fwd, d_state, state0)
+    gr = _make_grad(d_o_rev, grads_rev, d_state_rev, None)
+    _check(load_library().gdn_chunk_backward_bidir(ctypes.c_void_p(handle), ctypes.byref(io), ctypes.byref(gf),
+                                                   ctypes.byref(gr), q.shape[1], _stream_ptr(stream, q.device)))
 
 
 class Stream:
@@ -285,20 +306,30 @@ class Stream:
     def bidir(self, q, k, v, a, beta, o, o_rev, **kw):
         gdn_chunk_bidir(self.handle, q, k, v, a, beta, o, o_rev, **kw)
 
-    def backward(self, q, k, v, a, beta, d_o, *, reverse=False, d_state=None, state0=None, **kw):
-        """Gradients of one scan; returns a dict of fp32 tensors dq, dk, dv, da, dbeta, d_state0."""
+    def _grad_buffers(self, q, v):
         import torch
         B, T, H, Dk = q.shape
         Dv = v.shape[-1]
         dev = q.device
-        g = {"dq": torch.empty((B, T, H, Dk), dtype=torch.float32, device=dev),
-             "dk": torch.empty((B, T, H, Dk), dtype=torch.float32, device=dev),
-             "dv": torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev),
-             "da": torch.empty((B, T, H), dtype=torch.float32, device=dev),
-             "dbeta": torch.empty((B, T, H), dtype=torch.float32, device=dev),
-             "d_state0": torch.empty(self.shape, dtype=torch.float32, device=dev)}
+        return {"dq": torch.empty((B, T, H, Dk), dtype=torch.float32, device=dev),
+                "dk": torch.empty((B, T, H, Dk), dtype=torch.float32, device=dev),
+                "dv": torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev),
+                "da": torch.empty((B, T, H), dtype=torch.float32, device=dev),
+                "dbeta": torch.empty((B, T, H), dtype=torch.float32, device=dev),
+                "d_state0": torch.empty(self.shape, dtype=torch.float32, device=dev)}
+
+    def backward(self, q, k, v, a, beta, d_o, *, reverse=False, d_state=None, state0=None, **kw):
+        """Gradients of one scan; returns a dict of fp32 tensors dq, dk, dv, da, dbeta, d_state0."""
+        g = self._grad_buffers(q, v)
         gdn_chunk_backward(self.handle, q, k, v, a, beta, d_o, g, reverse=reverse, d_state=d_state, state0=state0, **kw)
         return g
+
+    def backward_bidir(self, q, k, v, a, beta, d_o_fwd, d_o_rev, *, d_state=None, state0=None, d_state_rev=None, **kw):
+        """Gradients of both scans of a bidirectional call; returns (forward scan's dict, reverse scan's dict)."""
+        gf, gr = self._grad_buffers(q, v), self._grad_buffers(q, v)
+        gdn_chunk_backward_bidir(self.handle, q, k, v, a, beta, d_o_fwd, d_o_rev, gf, gr, d_state=d_state,
+                                 state0=state0, d_state_rev=d_state_rev, **kw)
+        return gf, gr
 
     def state_get(self, dst=None, **kw):
         import torch

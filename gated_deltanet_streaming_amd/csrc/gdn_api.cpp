@@ -41,6 +41,7 @@ struct gdn_stream {
     int* err;             // error word in pinned host memory: a kernel wait gave up
     int spin_limit;       // polls before a wait gives up
     float* bwd_ws;        // backward workspace (states, partial sums), allocated on first use
+    float* bwd_ws2;       // the reverse scan's backward workspace of a bidirectional gradient call
     float* seg_ws;        // time-split workspace (segment states), allocated on first use, grown on demand
     int64_t seg_elems;
     // optional per-kernel timing
@@ -363,6 +364,7 @@ GDN_API int gdn_stream_init(const gdn_config* cfg, int device, gdn_stream** out)
     s->ws = nullptr;
     s->conv = nullptr;
     s->bwd_ws = nullptr;
+    s->bwd_ws2 = nullptr;
     s->seg_ws = nullptr;
     s->seg_elems = 0;
     s->item_bytes = 0;
@@ -435,6 +437,7 @@ GDN_API int gdn_stream_destroy(gdn_stream* s) {
     if (s->ws) (void)hipFree(s->ws);
     if (s->conv) (void)hipFree(s->conv);
     if (s->bwd_ws) (void)hipFree(s->bwd_ws);
+    if (s->bwd_ws2) (void)hipFree(s->bwd_ws2);
     if (s->seg_ws) (void)hipFree(s->seg_ws);
     if (s->err) (void)hipHostFree(s->err);
     delete s;
@@ -657,51 +660,32 @@ GDN_API int gdn_profile_read(gdn_stream* s, double* ms, int64_t* launches, int r
     return ok();
 }
 
-GDN_API int gdn_chunk_backward(gdn_stream* s, const gdn_io* io, const gdn_grad* g, int64_t T, int reverse,
-                               void* hip_stream) {
-    if (!s) return fail(GDN_E_INVAL, "handle is NULL");
-    if (!io) return fail(GDN_E_INVAL, "io is NULL");
-    if (!g) return fail(GDN_E_INVAL, "grad is NULL");
-    if (check_err_word(s) != GDN_OK) return GDN_E_HIP;
-    if (reverse != 0 && reverse != 1) return fail(GDN_E_INVAL, "reverse must be 0 or 1");
-    if (reverse && g->state0) return fail(GDN_E_INVAL, "the reverse scan starts from zero: state0 must be NULL");
-    if (T < 0 || T > s->cfg.max_tokens)
-        return fail(GDN_E_SHAPE, "T = %lld outside [0, max_tokens = %lld]", (long long)T, (long long)s->cfg.max_tokens);
-    const int64_t sbytes = s->state_elems * (int64_t)sizeof(float);
-    DeviceGuard dg(s->device);
-    if (dg.err != hipSuccess) return fail(GDN_E_HIP, "hipSetDevice(%d): %s", s->device, hipGetErrorString(dg.err));
-    const hipStream_t st = static_cast<hipStream_t>(hip_stream);
-    if (T == 0) {
-        if (!g->d_state0) return ok();
-        hipError_t e = g->d_state ? hipMemcpyAsync(g->d_state0, g->d_state, sbytes, hipMemcpyDeviceToDevice, st)
-                                  : gdn::launch_zero(g->d_state0, s->state_elems, st);
-        return e == hipSuccess ? ok() : fail(GDN_E_HIP, "d_state0: %s", hipGetErrorString(e));
-    }
-    const int esz = elem_size(s->cfg);
-    const int dk = s->cfg.d_k, dv = s->cfg.d_v;
+// Checks of one scan's gradient arguments (nothing is enqueued here).
+static int check_grad(const gdn_stream* s, const gdn_io* io, const gdn_grad* g, int64_t T, int reverse, const char* which) {
+    if (!g) return fail(GDN_E_INVAL, "%s is NULL", which);
+    if (reverse && g->state0) return fail(GDN_E_INVAL, "the reverse scan starts from zero: %s->state0 must be NULL", which);
+    if (T == 0) return GDN_OK;
     int rc;
-    if ((rc = check_tensor("q", io->q, io->q_strides, esz, dk, T)) != GDN_OK) return rc;
-    if ((rc = check_tensor("k", io->k, io->k_strides, esz, dk, T)) != GDN_OK) return rc;
-    if ((rc = check_tensor("v", io->v, io->v_strides, esz, dv, T)) != GDN_OK) return rc;
-    if ((rc = check_tensor("d_o", g->d_o, io->o_strides, esz, dv, T)) != GDN_OK) return rc;
-    if (!io->a) return fail(GDN_E_INVAL, "a is NULL");
-    if (!io->beta) return fail(GDN_E_INVAL, "beta is NULL");
-    for (int i = 0; i < 3; ++i)
-        if (io->g_strides[i] < 0) return fail(GDN_E_INVAL, "gate stride %d is negative", i);
-    if (!g->dq || !g->dk || !g->dv || !g->da || !g->dbeta) return fail(GDN_E_INVAL, "a gradient output is NULL");
-    if (!s->bwd_ws) {
-        const int64_t bytes = gdn::backward_ws_bytes(s->cfg.batch, s->cfg.heads, dk, dv, s->cfg.max_tokens);
-        if (bytes < 0) return fail(GDN_E_SHAPE, "the backward workspace size overflows");
-        hipError_t e = hipMalloc(&s->bwd_ws, bytes);
-        if (e != hipSuccess) {
-            s->bwd_ws = nullptr;
-            (void)hipGetLastError();
-            return fail(GDN_E_NOMEM, "backward workspace (%lld bytes): %s", (long long)bytes, hipGetErrorString(e));
-        }
+    if ((rc = check_tensor("d_o", g->d_o, io->o_strides, elem_size(s->cfg), s->cfg.d_v, T)) != GDN_OK) return rc;
+    if (!g->dq || !g->dk || !g->dv || !g->da || !g->dbeta) return fail(GDN_E_INVAL, "a gradient output of %s is NULL", which);
+    return GDN_OK;
+}
+
+// A backward workspace, allocated on first use and kept until gdn_stream_destroy.
+static int ensure_bwd_ws(gdn_stream* s, float** ws) {
+    if (*ws) return GDN_OK;
+    const int64_t bytes = gdn::backward_ws_bytes(s->cfg.batch, s->cfg.heads, s->cfg.d_k, s->cfg.d_v, s->cfg.max_tokens);
+    if (bytes < 0) return fail(GDN_E_SHAPE, "the backward workspace size overflows");
+    hipError_t e = hipMalloc(ws, bytes);
+    if (e != hipSuccess) {
+        *ws = nullptr;
+        (void)hipGetLastError();
+        return fail(GDN_E_NOMEM, "backward workspace (%lld bytes): %s", (long long)bytes, hipGetErrorString(e));
     }
-    gdn::Params p = base_params(s, io, T);
-    p.dir0 = reverse;
-    p.ndirs = 1;
+    return GDN_OK;
+}
+
+static gdn::BwdParams bwd_params(const gdn_stream* s, const gdn_grad* g, float* ws, int reverse) {
     gdn::BwdParams b;
     b.d_o = g->d_o;
     b.d_state = g->d_state;
@@ -712,10 +696,57 @@ GDN_API int gdn_chunk_backward(gdn_stream* s, const gdn_io* io, const gdn_grad* 
     b.da = g->da;
     b.dbeta = g->dbeta;
     b.d_state0 = g->d_state0;
-    b.states = s->bwd_ws;
-    b.partials = s->bwd_ws + gdn::backward_ckpt_floats(s->cfg.batch, s->cfg.heads, dk, dv, s->cfg.max_tokens);
+    b.states = ws;
+    b.partials = ws + gdn::backward_ckpt_floats(s->cfg.batch, s->cfg.heads, s->cfg.d_k, s->cfg.d_v, s->cfg.max_tokens);
     b.ck_per = gdn::backward_ckpt_per(s->cfg.max_tokens);
     b.reverse = reverse;
+    return b;
+}
+
+// The gradient of one scan (g1 null: g0's scan is the forward scan when reverse0 = 0, the
+// reverse scan when reverse0 = 1) or of both scans of a bidirectional call (g0: the forward
+// scan, g1: the reverse scan), each with its own workspace, in one launch pair.
+static int backward_impl(gdn_stream* s, const gdn_io* io, const gdn_grad* g0, const gdn_grad* g1, int64_t T,
+                         int reverse0, void* hip_stream) {
+    if (!s) return fail(GDN_E_INVAL, "handle is NULL");
+    if (!io) return fail(GDN_E_INVAL, "io is NULL");
+    if (check_err_word(s) != GDN_OK) return GDN_E_HIP;
+    if (reverse0 != 0 && reverse0 != 1) return fail(GDN_E_INVAL, "reverse must be 0 or 1");
+    const bool both = g1 != nullptr;
+    int rc;
+    if (T < 0 || T > s->cfg.max_tokens)
+        return fail(GDN_E_SHAPE, "T = %lld outside [0, max_tokens = %lld]", (long long)T, (long long)s->cfg.max_tokens);
+    if ((rc = check_grad(s, io, g0, T, reverse0, both ? "g_fwd" : "grad")) != GDN_OK) return rc;
+    if (both && (rc = check_grad(s, io, g1, T, 1, "g_rev")) != GDN_OK) return rc;
+    const int64_t sbytes = s->state_elems * (int64_t)sizeof(float);
+    DeviceGuard dg(s->device);
+    if (dg.err != hipSuccess) return fail(GDN_E_HIP, "hipSetDevice(%d): %s", s->device, hipGetErrorString(dg.err));
+    const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    if (T == 0) {
+        for (const gdn_grad* g : {g0, g1}) {
+            if (!g || !g->d_state0) continue;
+            hipError_t e = g->d_state ? hipMemcpyAsync(g->d_state0, g->d_state, sbytes, hipMemcpyDeviceToDevice, st)
+                                      : gdn::launch_zero(g->d_state0, s->state_elems, st);
+            if (e != hipSuccess) return fail(GDN_E_HIP, "d_state0: %s", hipGetErrorString(e));
+        }
+        return ok();
+    }
+    const int esz = elem_size(s->cfg);
+    const int dk = s->cfg.d_k, dv = s->cfg.d_v;
+    if ((rc = check_tensor("q", io->q, io->q_strides, esz, dk, T)) != GDN_OK) return rc;
+    if ((rc = check_tensor("k", io->k, io->k_strides, esz, dk, T)) != GDN_OK) return rc;
+    if ((rc = check_tensor("v", io->v, io->v_strides, esz, dv, T)) != GDN_OK) return rc;
+    if (!io->a) return fail(GDN_E_INVAL, "a is NULL");
+    if (!io->beta) return fail(GDN_E_INVAL, "beta is NULL");
+    for (int i = 0; i < 3; ++i)
+        if (io->g_strides[i] < 0) return fail(GDN_E_INVAL, "gate stride %d is negative", i);
+    if ((rc = ensure_bwd_ws(s, &s->bwd_ws)) != GDN_OK) return rc;
+    if (both && (rc = ensure_bwd_ws(s, &s->bwd_ws2)) != GDN_OK) return rc;
+    gdn::Params p = base_params(s, io, T);
+    p.dir0 = reverse0;
+    p.ndirs = 1;
+    const gdn::BwdParams b0 = bwd_params(s, g0, s->bwd_ws, reverse0);
+    const gdn::BwdParams b1 = both ? bwd_params(s, g1, s->bwd_ws2, 1) : b0;
     hipError_t prior = hipPeekAtLastError();
     if (prior != hipSuccess) {
         (void)hipGetLastError();
@@ -736,7 +767,7 @@ GDN_API int gdn_chunk_backward(gdn_stream* s, const gdn_io* io, const gdn_grad* 
         evs[1] = pr.second;
         tm.ev = evs;
     }
-    hipError_t e = gdn::launch_backward(p, b, st, &tm);
+    hipError_t e = gdn::launch_backward(p, b0, both ? &b1 : nullptr, st, &tm);
     if (s->profile) {
         if (tm.n > 0) {
             s->pend.push_back(pr);
@@ -747,6 +778,17 @@ GDN_API int gdn_chunk_backward(gdn_stream* s, const gdn_io* io, const gdn_grad* 
     }
     if (e != hipSuccess) return fail(GDN_E_HIP, "kernel launch: %s", hipGetErrorString(e));
     return ok();
+}
+
+GDN_API int gdn_chunk_backward(gdn_stream* s, const gdn_io* io, const gdn_grad* g, int64_t T, int reverse,
+                               void* hip_stream) {
+    return backward_impl(s, io, g, nullptr, T, reverse, hip_stream);
+}
+
+GDN_API int gdn_chunk_backward_bidir(gdn_stream* s, const gdn_io* io, const gdn_grad* g_fwd, const gdn_grad* g_rev,
+                                     int64_t T, void* hip_stream) {
+    if (s && io && g_fwd && !g_rev) return fail(GDN_E_INVAL, "g_rev is NULL");
+    return backward_impl(s, io, g_fwd, g_rev, T, 0, hip_stream);
 }
 
 // ---- softmax-block attention over the sink + window cache (gdn_attn.h) ----------------------

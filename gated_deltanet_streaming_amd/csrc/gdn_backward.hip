@@ -63,7 +63,7 @@ void tm_end(Timing* tm, hipStream_t s) {
 // adds the row blocks in a fixed order and maps the normalised-vector gradients
 // back through the L2 normalisation.
 // ---------------------------------------------------------------------------
-constexpr int kMinTB = 14;   // smallest token block of any instance (sizes the checkpoints)
+constexpr int kMinTB = 8;    // smallest token block of any instance (sizes the checkpoints)
 constexpr int kRB = 4;       // state rows per workgroup
 constexpr int kLPR = 64 / kRB;   // lanes per state row
 
@@ -119,15 +119,19 @@ __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 
 }  // namespace
 
+// Workgroups [0, nwg0) compute the gradient of g0's scan, [nwg0, 2 nwg0) that of g1's (the
+// bidirectional call: both scans' gradients in one launch).
 template <int NG, bool F32>
-__global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g) {
+__global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g0, BwdParams g1, int nwg0) {
     constexpr int DK = 16 * NG;               // d_k
-    constexpr int TB = NG == 8 ? 14 : 16;     // tokens per staged block (LDS: states of a block)
+    constexpr int TB = 8;                     // tokens per staged block (LDS: states of a block)
     constexpr int NLQ = (TB * DK + 255) / 256;   // staged elements of k (and of q) per lane, 4 at a time
     static_assert(TB >= kMinTB, "checkpoint sizing");
     const int lane = threadIdx.x, part = lane & (kLPR - 1), rl = lane / kLPR;
     const int nrb = p.Dv / kRB;
-    int id = blockIdx.x;
+    const bool second = (int)blockIdx.x >= nwg0;
+    const BwdParams g = second ? g1 : g0;
+    int id = (int)blockIdx.x - (second ? nwg0 : 0);
     const int rb = id % nrb;
     id /= nrb;
     const int h = id % p.H;
@@ -404,9 +408,11 @@ __device__ __forceinline__ float sum_wave(float x) {
 // One 64-lane workgroup per (b, t, h): add the row blocks' partial sums (in row-block
 // order) and map the gradients of the normalised q_t, k_t back to q_t, k_t.
 template <bool F32>
-__global__ __launch_bounds__(64) void gdn_bwd_reduce_kernel(Params p, BwdParams g) {
+__global__ __launch_bounds__(64) void gdn_bwd_reduce_kernel(Params p, BwdParams g0, BwdParams g1, int64_t n0) {
     const int lane = threadIdx.x;
-    int64_t id = blockIdx.x;
+    const bool second = (int64_t)blockIdx.x >= n0;
+    const BwdParams g = second ? g1 : g0;
+    int64_t id = (int64_t)blockIdx.x - (second ? n0 : 0);
     const int h = (int)(id % p.H); id /= p.H;
     const int64_t t = id % p.T; id /= p.T;
     const int b = (int)id;
@@ -464,34 +470,38 @@ __global__ __launch_bounds__(64) void gdn_bwd_reduce_kernel(Params p, BwdParams 
 }
 
 template <int NG>
-static void launch_rows_ng(const Params& p, const BwdParams& g, hipStream_t s, int grid) {
-    if (p.io_f32) hipLaunchKernelGGL((gdn_bwd_rows_kernel<NG, true>), dim3(grid), dim3(64), 0, s, p, g);
-    else hipLaunchKernelGGL((gdn_bwd_rows_kernel<NG, false>), dim3(grid), dim3(64), 0, s, p, g);
+static void launch_rows_ng(const Params& p, const BwdParams& g0, const BwdParams& g1, hipStream_t s, int nwg0, int grid) {
+    if (p.io_f32) hipLaunchKernelGGL((gdn_bwd_rows_kernel<NG, true>), dim3(grid), dim3(64), 0, s, p, g0, g1, nwg0);
+    else hipLaunchKernelGGL((gdn_bwd_rows_kernel<NG, false>), dim3(grid), dim3(64), 0, s, p, g0, g1, nwg0);
 }
 
-static hipError_t launch_rows(const Params& p, const BwdParams& g, hipStream_t s, int grid) {
+static hipError_t launch_rows(const Params& p, const BwdParams& g0, const BwdParams& g1, hipStream_t s, int nwg0,
+                              int grid) {
     switch (p.Dk) {
-        case 16: launch_rows_ng<1>(p, g, s, grid); break;
-        case 32: launch_rows_ng<2>(p, g, s, grid); break;
-        case 48: launch_rows_ng<3>(p, g, s, grid); break;
-        case 64: launch_rows_ng<4>(p, g, s, grid); break;
-        case 80: launch_rows_ng<5>(p, g, s, grid); break;
-        case 96: launch_rows_ng<6>(p, g, s, grid); break;
-        case 112: launch_rows_ng<7>(p, g, s, grid); break;
-        case 128: launch_rows_ng<8>(p, g, s, grid); break;
+        case 16: launch_rows_ng<1>(p, g0, g1, s, nwg0, grid); break;
+        case 32: launch_rows_ng<2>(p, g0, g1, s, nwg0, grid); break;
+        case 48: launch_rows_ng<3>(p, g0, g1, s, nwg0, grid); break;
+        case 64: launch_rows_ng<4>(p, g0, g1, s, nwg0, grid); break;
+        case 80: launch_rows_ng<5>(p, g0, g1, s, nwg0, grid); break;
+        case 96: launch_rows_ng<6>(p, g0, g1, s, nwg0, grid); break;
+        case 112: launch_rows_ng<7>(p, g0, g1, s, nwg0, grid); break;
+        case 128: launch_rows_ng<8>(p, g0, g1, s, nwg0, grid); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_backward(const Params& p, const BwdParams& g, hipStream_t s, Timing* tm) {
-    const int rows_grid = p.B * p.H * (p.Dv / kRB);
-    const int64_t red_grid = (int64_t)p.B * p.T * p.H;
+hipError_t launch_backward(const Params& p, const BwdParams& g0, const BwdParams* g1, hipStream_t s, Timing* tm) {
+    const int nscan = g1 ? 2 : 1;
+    const int rows0 = p.B * p.H * (p.Dv / kRB);
+    const int64_t red0 = (int64_t)p.B * p.T * p.H;
+    const BwdParams& gb = g1 ? *g1 : g0;
     tm_begin(tm, s, KBWD);
-    hipError_t e = launch_rows(p, g, s, rows_grid);
-    if (e == hipSuccess && red_grid > 0) {
-        if (p.io_f32) hipLaunchKernelGGL(gdn_bwd_reduce_kernel<true>, dim3((unsigned)red_grid), dim3(64), 0, s, p, g);
-        else hipLaunchKernelGGL(gdn_bwd_reduce_kernel<false>, dim3((unsigned)red_grid), dim3(64), 0, s, p, g);
+    hipError_t e = launch_rows(p, g0, gb, s, rows0, nscan * rows0);
+    if (e == hipSuccess && red0 > 0) {
+        const unsigned grid = (unsigned)(nscan * red0);
+        if (p.io_f32) hipLaunchKernelGGL(gdn_bwd_reduce_kernel<true>, dim3(grid), dim3(64), 0, s, p, g0, gb, red0);
+        else hipLaunchKernelGGL(gdn_bwd_reduce_kernel<false>, dim3(grid), dim3(64), 0, s, p, g0, gb, red0);
         e = hipGetLastError();
     }
     tm_end(tm, s);

@@ -160,6 +160,8 @@ hipError_t launch_chunked(const Params& p, hipStream_t s, Timing* tm);
 // The forward scan as a time split (p.seg_mode 0, p.nseg segments of p.seg_steps steps, p.seg_out
 // set; seg_in: [nseg][B][H][D][D] for the segments' start states).
 hipError_t launch_split(const Params& p, float* seg_in, hipStream_t s, Timing* tm);
-hipError_t launch_backward(const Params& p, const BwdParams& g, hipStream_t s, Timing* tm);
+// Gradient of g0's scan, and of g1's as well in the same launches when g1 is not null (each with
+// its own workspace).
+hipError_t launch_backward(const Params& p, const BwdParams& g0, const BwdParams* g1, hipStream_t s, Timing* tm);
 
 }  // namespace gdn

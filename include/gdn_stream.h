@@ -237,14 +237,28 @@ typedef struct gdn_grad {
  * reverse scan (reverse = 1: t descending from zero) over T tokens of io->q, k, v,
  * a, beta (io->o is not used; its strides give d_o's layout).  Never reads or
  * writes the cache.  Asynchronous on hip_stream.  The first call on a handle
- * allocates a backward workspace of 4 (B H (d_v/4)(ceil(max_tokens/14)+1) 4 d_k
+ * allocates a backward workspace of 4 (B H (d_v/4)(ceil(max_tokens/8)+1) 4 d_k
  * + B max_tokens H (d_v/4)(2 d_k + 4)) bytes (state checkpoints every block of
- * 14 or 16 tokens, and partial sums per block of 4 state rows), kept until gdn_stream_destroy
+ * 8 tokens, and partial sums per block of 4 state rows), kept until gdn_stream_destroy
  * (GDN_E_NOMEM if that fails).  Errors: GDN_E_INVAL (NULL handle/io/g/output,
  * bad strides, state0 given with reverse), GDN_E_SHAPE (T outside [0, max_tokens]),
  * GDN_E_HIP; on error nothing is enqueued.  T = 0 writes d_state0 = d_state. */
 GDN_API int gdn_chunk_backward(gdn_stream* s, const gdn_io* io, const gdn_grad* g, int64_t T, int reverse,
                                void* hip_stream);
+
+/* Gradients of both scans of a gdn_chunk_bidir call, in one launch pair: g_fwd for the
+ * forward scan (as gdn_chunk_backward with reverse = 0: g_fwd->state0 is its start
+ * state) and g_rev for the intra-chunk reverse scan (as reverse = 1: g_rev->state0 must
+ * be NULL).  Training on short clips needs both scans' gradients of every layer (the
+ * Chinese summary, "Method steps", step 2: bidirectional training before streaming
+ * training); the two are independent, so one launch runs them side by side.  The two
+ * d_o tensors share io->o's strides.  Results are bitwise those of the two separate
+ * calls.  The first call on a handle also allocates a second backward workspace of the
+ * size given above (for the reverse scan), kept until gdn_stream_destroy.  Errors as
+ * gdn_chunk_backward (GDN_E_INVAL also for a NULL g_fwd or g_rev); on error nothing is
+ * enqueued.  T = 0 writes each d_state0 from its d_state. */
+GDN_API int gdn_chunk_backward_bidir(gdn_stream* s, const gdn_io* io, const gdn_grad* g_fwd, const gdn_grad* g_rev,
+                                     int64_t T, void* hip_stream);
 
 /* Message for the last failing call on this thread ("" when none). */
 GDN_API const char* gdn_last_error(void);

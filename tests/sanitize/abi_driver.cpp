@@ -102,6 +102,7 @@ static void run_all() {
     expect("reverse NULL handle", gdn_chunk_reverse(nullptr, &io, 64, 0, nullptr, nullptr), GDN_E_INVAL);
     expect("bidir NULL handle", gdn_chunk_bidir(nullptr, &io, nullptr, 64, 0, nullptr, nullptr), GDN_E_INVAL);
     expect("backward NULL handle", gdn_chunk_backward(nullptr, &io, nullptr, 64, 0, nullptr), GDN_E_INVAL);
+    expect("backward_bidir NULL handle", gdn_chunk_backward_bidir(nullptr, &io, nullptr, nullptr, 64, nullptr), GDN_E_INVAL);
     expect("state_get NULL", gdn_state_get(nullptr, nullptr, nullptr), GDN_E_INVAL);
     expect("state_set NULL", gdn_state_set(nullptr, nullptr, nullptr), GDN_E_INVAL);
     expect("profile NULL", gdn_profile(nullptr, 1), GDN_E_INVAL);

@@ -120,3 +120,90 @@ def test_backward_is_bitwise_repeatable():
     g2, _ = _grads(d, 64, 64, 80, seed=79)
     for key in g1:
         assert torch.equal(g1[key], g2[key]), key
+
+
+def _bidir_inputs(d, D, T, seed, io="bf16"):
+    B, H = d["q"].shape[0], d["q"].shape[2]
+    rng = np.random.default_rng(2000 + seed)
+    dt = torch.bfloat16 if io == "bf16" else torch.float32
+    dO = [torch.from_numpy(rng.standard_normal((B, T, H, D)).astype(np.float32)).to(dt) for _ in range(2)]
+    dSf = torch.from_numpy(rng.standard_normal((B, H, D, D)).astype(np.float32))
+    dSr = torch.from_numpy(rng.standard_normal((B, H, D, D)).astype(np.float32))
+    return dO, dSf, dSr
+
+
+def test_backward_bidir_equals_the_two_calls_bitwise():
+    """gdn_chunk_backward_bidir (both scans' gradients in one launch pair) against gdn_chunk_backward
+    called for each scan: the same kernels and order of operations, so the same bits.  T = 300 is
+    not a multiple of the 8-token staging block."""
+    B, T, H, D = 1, 300, 3, 112
+    d = gdn_inputs.batch(81, B, T, H, D, with_state=True)
+    dO, dSf, dSr = _bidir_inputs(d, D, T, 81)
+    s = gb.Stream(B, H, D, D, T)
+    try:
+        t = dev_inputs(d)
+        S0 = torch.from_numpy(np.ascontiguousarray(d["S0"], np.float32)).cuda()
+        args = (t["q"], t["k"], t["v"], t["a"], t["beta"])
+        gf, gr = s.backward_bidir(*args, dO[0].cuda(), dO[1].cuda(), d_state=dSf.cuda(), state0=S0,
+                                  d_state_rev=dSr.cuda())
+        ef = s.backward(*args, dO[0].cuda(), d_state=dSf.cuda(), state0=S0)
+        er = s.backward(*args, dO[1].cuda(), reverse=True, d_state=dSr.cuda())
+        torch.cuda.synchronize()
+    finally:
+        s.close()
+    for key in ef:
+        assert torch.isfinite(gf[key]).all() and torch.isfinite(gr[key]).all(), key
+        assert torch.equal(gf[key], ef[key]), f"forward scan {key}"
+        assert torch.equal(gr[key], er[key]), f"reverse scan {key}"
+
+
+def test_backward_bidir_against_the_oracle():
+    """Both scans' gradients of one bidirectional call at the 720p width, 700 tokens, 2 heads."""
+    B, T, H, D = 1, 700, 2, 112
+    d = gdn_inputs.batch(82, B, T, H, D, with_state=True)
+    dO, dSf, _ = _bidir_inputs(d, D, T, 82)
+    ref_f = oracle.backward(d["q"], d["k"], d["v"], d["a"], d["beta"], dO[0].float().numpy(), d["S0"], dSf.numpy())
+    ref_r = oracle.backward(d["q"], d["k"], d["v"], d["a"], d["beta"], dO[1].float().numpy(), None, None, reverse=True)
+    s = gb.Stream(B, H, D, D, T)
+    try:
+        t = dev_inputs(d)
+        S0 = torch.from_numpy(np.ascontiguousarray(d["S0"], np.float32)).cuda()
+        gf, gr = s.backward_bidir(t["q"], t["k"], t["v"], t["a"], t["beta"], dO[0].cuda(), dO[1].cuda(),
+                                  d_state=dSf.cuda(), state0=S0)
+        torch.cuda.synchronize()
+    finally:
+        s.close()
+    print("forward scan:", flush=True)
+    _check_all(gf, ref_f)
+    print("reverse scan:", flush=True)
+    _check_all(gr, ref_r)
+
+
+def test_backward_bidir_rejects_a_start_state_for_the_reverse_scan():
+    """g_rev->state0 set, or g_rev missing: GDN_E_INVAL and nothing written."""
+    B, T, H, D = 1, 40, 2, 32
+    d = gdn_inputs.batch(83, B, T, H, D, with_state=True)
+    dO, dSf, _ = _bidir_inputs(d, D, T, 83)
+    s = gb.Stream(B, H, D, D, T)
+    try:
+        t = dev_inputs(d)
+        S0 = torch.from_numpy(np.ascontiguousarray(d["S0"], np.float32)).cuda()
+        args = (t["q"], t["k"], t["v"], t["a"], t["beta"])
+        gf, gr = s._grad_buffers(t["q"], t["v"]), s._grad_buffers(t["q"], t["v"])
+        for x in list(gf.values()) + list(gr.values()):
+            x.fill_(7.0)
+        io = gb._make_io(t["q"], t["k"], t["v"], dO[0].cuda(), t["a"], t["beta"])
+        g_f = gb._make_grad(dO[0].cuda(), gf, dSf.cuda(), S0)
+        g_r = gb._make_grad(dO[1].cuda(), gr, None, S0)
+        lib = gb.load_library()
+        import ctypes
+        rc = lib.gdn_chunk_backward_bidir(ctypes.c_void_p(s.handle), ctypes.byref(io), ctypes.byref(g_f),
+                                          ctypes.byref(g_r), T, None)
+        assert rc == gb.GDN_E_INVAL and "state0" in gb.gdn_last_error()
+        rc = lib.gdn_chunk_backward_bidir(ctypes.c_void_p(s.handle), ctypes.byref(io), ctypes.byref(g_f), None, T, None)
+        assert rc == gb.GDN_E_INVAL and "g_rev" in gb.gdn_last_error()
+        torch.cuda.synchronize()
+        for x in list(gf.values()) + list(gr.values()):
+            assert bool((x == 7.0).all())
+    finally:
+        s.close()
