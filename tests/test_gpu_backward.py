@@ -207,3 +207,27 @@ def test_backward_bidir_rejects_a_start_state_for_the_reverse_scan():
             assert bool((x == 7.0).all())
     finally:
         s.close()
+
+
+@pytest.mark.parametrize("T", [1, 7, 8, 9, 17])
+def test_backward_staging_block_edges(T):
+    """Lengths around the 8-token staging block (one token, a short block, exactly one block, one
+    token into the second, two blocks and one), both scans through the bidirectional call, against
+    the oracle."""
+    B, H, D = 1, 2, 32
+    d = gdn_inputs.batch(90 + T, B, T, H, D, with_state=True)
+    dO, dSf, dSr = _bidir_inputs(d, D, T, 90 + T)
+    ref_f = oracle.backward(d["q"], d["k"], d["v"], d["a"], d["beta"], dO[0].float().numpy(), d["S0"], dSf.numpy())
+    ref_r = oracle.backward(d["q"], d["k"], d["v"], d["a"], d["beta"], dO[1].float().numpy(), None, dSr.numpy(),
+                            reverse=True)
+    s = gb.Stream(B, H, D, D, T)
+    try:
+        t = dev_inputs(d)
+        S0 = torch.from_numpy(np.ascontiguousarray(d["S0"], np.float32)).cuda()
+        gf, gr = s.backward_bidir(t["q"], t["k"], t["v"], t["a"], t["beta"], dO[0].cuda(), dO[1].cuda(),
+                                  d_state=dSf.cuda(), state0=S0, d_state_rev=dSr.cuda())
+        torch.cuda.synchronize()
+    finally:
+        s.close()
+    _check_all(gf, ref_f)
+    _check_all(gr, ref_r)
