@@ -334,34 +334,44 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g0
             const float x = fwd_token(r);
             if (part == 0) sx[r][rl] = x;
         }
-        // S is the state after the block's last token; walk the block's tokens backward
-        for (int r = n - 1; r >= 0; --r) {
-            const int64_t t = tok(blk * TB + r);
-            // every LDS operand of the token first, then the arithmetic
+        // S is the state after the block's last token; walk the block's tokens backward.  A token's
+        // LDS operands are read while the previous token finishes (after its column-sum reads, so
+        // that they do not hold those back), alternating between two register sets.
+        struct TokOps {
             float Sp[NG], kr[NG], qr[NG];
+            float dor, at, bt, vr, x;
+        };
+        auto read_ops = [&](TokOps& o, int r) {
 #pragma unroll
             for (int j = 0; j < NG; ++j) {
-                Sp[j] = sst[r][j][lane];
-                kr[j] = krow(r, j);
-                qr[j] = qrow(r, j);
+                o.Sp[j] = sst[r][j][lane];
+                o.kr[j] = krow(r, j);
+                o.qr[j] = qrow(r, j);
             }
-            const float dor = p.scale * sdo[r][rl];
-            const float at = sa[r], bt = sb[r], vr = sv[r][rl], x = sx[r][rl];
+            o.dor = p.scale * sdo[r][rl];
+            o.at = sa[r];
+            o.bt = sb[r];
+            o.vr = sv[r][rl];
+            o.x = sx[r][rl];
+        };
+        auto walk = [&](const TokOps& c, TokOps& nx, int r) __attribute__((always_inline)) {
+            const int64_t t = tok(blk * TB + r);
+            const float dor = c.dor, at = c.at, bt = c.bt, vr = c.vr, x = c.x;
 #pragma unroll
-            for (int j = 0; j < NG; ++j) G[j] += dor * qr[j];
-            const float gk = rowdot(G, kr), gs = rowdot(G, Sp);
+            for (int j = 0; j < NG; ++j) G[j] += dor * c.qr[j];
+            const float gk = rowdot(G, c.kr), gs = rowdot(G, c.Sp);
             if (part == 0) g.dv[(((int64_t)b * T + t) * p.H + h) * p.Dv + row] = bt * gk;
             // this row's terms of dq_t = scale S_t^T do_t and dk_t = beta G^T (v - a x) - a beta S_{t-1}^T gk
             const float wv = bt * (vr - at * x), ws = at * bt * gk;
 #pragma unroll
             for (int j = 0; j < NG; ++j) {
                 scol[0][rl][16 * j + part] = dor * S[j];
-                scol[1][rl][16 * j + part] = wv * G[j] - ws * Sp[j];
+                scol[1][rl][16 * j + part] = wv * G[j] - ws * c.Sp[j];
             }
             lds_order();
             const float cg = bt * gk;
 #pragma unroll
-            for (int j = 0; j < NG; ++j) G[j] = at * (G[j] - cg * kr[j]);
+            for (int j = 0; j < NG; ++j) G[j] = at * (G[j] - cg * c.kr[j]);
             // per-row scalars (identical in the 16 lanes of a row; counted once)
             float da = (part == 0) ? gs - bt * gk * x : 0.f;
             float db = (part == 0) ? gk * (vr - at * x) : 0.f;
@@ -369,9 +379,10 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g0
             db = sum_rows(db);
             float* pw = g.partials + ((((int64_t)b * T + t) * p.H + h) * nrb + rb) * wid;
             // column sums over the 4 rows, in row order: lane l adds float4 group l
+            float4 acc = {0.f, 0.f, 0.f, 0.f};
+            const int a = lane / (DK / 4), c4 = 4 * (lane - a * (DK / 4));
             if (lane < DK / 2) {
-                const int a = lane / (DK / 4), c4 = 4 * (lane - a * (DK / 4));
-                float4 acc = *reinterpret_cast<const float4*>(&scol[a][0][c4]);
+                acc = *reinterpret_cast<const float4*>(&scol[a][0][c4]);
 #pragma unroll
                 for (int rr = 1; rr < kRB; ++rr) {
                     const float4 v4 = *reinterpret_cast<const float4*>(&scol[a][rr][c4]);
@@ -380,16 +391,26 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g0
                     acc.z += v4.z;
                     acc.w += v4.w;
                 }
-                *reinterpret_cast<float4*>(pw + a * DK + c4) = acc;
             }
+            // the next token's operands, behind the column-sum reads
+            if (r > 0) read_ops(nx, r - 1);
+            lds_order();
+            if (lane < DK / 2) *reinterpret_cast<float4*>(pw + a * DK + c4) = acc;
             if (lane == 0) {
                 pw[2 * DK] = da;
                 pw[2 * DK + 1] = db;
             }
-            lds_order();
 #pragma unroll
-            for (int j = 0; j < NG; ++j) S[j] = Sp[j];
+            for (int j = 0; j < NG; ++j) S[j] = c.Sp[j];
+        };
+        TokOps oa, ob;
+        read_ops(oa, n - 1);
+        int r = n - 1;
+        for (; r >= 1; r -= 2) {
+            walk(oa, ob, r);
+            walk(ob, oa, r - 1);
         }
+        if (r == 0) walk(oa, ob, 0);
     }
     if (g.d_state0) {
 #pragma unroll
