@@ -697,8 +697,10 @@ static gdn::BwdParams bwd_params(const gdn_stream* s, const gdn_grad* g, float* 
     b.dbeta = g->dbeta;
     b.d_state0 = g->d_state0;
     b.states = ws;
+    b.gck = ws + gdn::backward_state_ckpt_floats(s->cfg.batch, s->cfg.heads, s->cfg.d_k, s->cfg.d_v, s->cfg.max_tokens);
     b.partials = ws + gdn::backward_ckpt_floats(s->cfg.batch, s->cfg.heads, s->cfg.d_k, s->cfg.d_v, s->cfg.max_tokens);
     b.ck_per = gdn::backward_ckpt_per(s->cfg.max_tokens);
+    b.gck_per = gdn::backward_gck_per(s->cfg.max_tokens);
     b.reverse = reverse;
     return b;
 }

@@ -67,17 +67,25 @@ constexpr int kMinTB = 8;    // smallest token block of any instance (sizes the 
 constexpr int kRB = 4;       // state rows per workgroup
 constexpr int kLPR = 64 / kRB;   // lanes per state row
 
-int64_t backward_ckpt_per(int64_t max_tokens) { return (max_tokens + kMinTB - 1) / kMinTB + 1; }
+constexpr int kSEG = 64;     // tokens per walk segment (a multiple of every token block)
 
-int64_t backward_ckpt_floats(int B, int H, int Dk, int Dv, int64_t max_tokens) {
+int64_t backward_ckpt_per(int64_t max_tokens) { return (max_tokens + kMinTB - 1) / kMinTB + 1; }
+int64_t backward_gck_per(int64_t max_tokens) { return (max_tokens + kSEG - 1) / kSEG; }
+
+// floats of the state checkpoints
+int64_t backward_state_ckpt_floats(int B, int H, int Dk, int Dv, int64_t max_tokens) {
     return (int64_t)B * H * (Dv / kRB) * backward_ckpt_per(max_tokens) * kRB * Dk;
+}
+// floats of the state checkpoints, then of the adjoint checkpoints (the partial sums follow)
+int64_t backward_ckpt_floats(int B, int H, int Dk, int Dv, int64_t max_tokens) {
+    return (int64_t)B * H * (Dv / kRB) * (backward_ckpt_per(max_tokens) + backward_gck_per(max_tokens)) * kRB * Dk;
 }
 
 int64_t backward_ws_bytes(int B, int H, int Dk, int Dv, int64_t max_tokens) {
     const int64_t nrb = Dv / kRB;
     int64_t states = 0, partials = 0, total = 0;
     if (__builtin_mul_overflow((int64_t)B * H, nrb * kRB * Dk, &states) ||
-        __builtin_mul_overflow(states, backward_ckpt_per(max_tokens), &states) ||
+        __builtin_mul_overflow(states, backward_ckpt_per(max_tokens) + backward_gck_per(max_tokens), &states) ||
         __builtin_mul_overflow((int64_t)B * H, nrb * (2 * Dk + 4), &partials) ||
         __builtin_mul_overflow(partials, max_tokens, &partials) || __builtin_add_overflow(states, partials, &total) ||
         __builtin_mul_overflow(total, (int64_t)4, &total))
@@ -119,19 +127,28 @@ __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 
 }  // namespace
 
-// Workgroups [0, nwg0) compute the gradient of g0's scan, [nwg0, 2 nwg0) that of g1's (the
-// bidirectional call: both scans' gradients in one launch).
+// Two launches per gradient.  Phase 0: per (b, h, row block) one workgroup runs the forward
+// recurrence and stores the state before every token block, and another runs the adjoint
+// recurrence alone (it does not involve the state: G <- a (G + scale do q^T)(I - beta k k^T)) and
+// stores dL/dS at the end of every segment of kSEG tokens.  Phase 1: per (b, h, row block,
+// segment) one workgroup walks the segment's tokens backward from its adjoint checkpoint,
+// recomputing each block's states from its state checkpoint; the segments are independent.  The
+// adjoint pass and the walks perform the same operations on G in the same order.
+// Workgroups [0, nunits) work on g0's scan, [nunits, 2 nunits) on g1's (the bidirectional call).
 template <int NG, bool F32>
-__global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g0, BwdParams g1, int nwg0) {
+__global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g0, BwdParams g1, int nunits, int phase) {
     constexpr int DK = 16 * NG;               // d_k
     constexpr int TB = 8;                     // tokens per staged block (LDS: states of a block)
     constexpr int NLQ = (TB * DK + 255) / 256;   // staged elements of k (and of q) per lane, 4 at a time
     static_assert(TB >= kMinTB, "checkpoint sizing");
     const int lane = threadIdx.x, part = lane & (kLPR - 1), rl = lane / kLPR;
     const int nrb = p.Dv / kRB;
-    const bool second = (int)blockIdx.x >= nwg0;
+    const int nwg = p.B * p.H * nrb;
+    const bool second = (int)blockIdx.x >= nunits;
     const BwdParams g = second ? g1 : g0;
-    int id = (int)blockIdx.x - (second ? nwg0 : 0);
+    int id = (int)blockIdx.x - (second ? nunits : 0);
+    const int unit = id / nwg;   // phase 0: 0 state checkpoints, 1 adjoint checkpoints; phase 1: the segment
+    id -= unit * nwg;
     const int rb = id % nrb;
     id /= nrb;
     const int h = id % p.H;
@@ -150,6 +167,9 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g0
     __shared__ float sx[TB][kRB], sa[TB], sb[TB];
 
     float* ck = g.states + (((int64_t)b * p.H + h) * nrb + rb) * g.ck_per * kRB * DK;
+    float* gk0 = g.gck + (((int64_t)b * p.H + h) * nrb + rb) * g.gck_per * kRB * DK;
+    constexpr int BPS = kSEG / TB;   // token blocks per segment
+    static_assert(kSEG % TB == 0, "segments of whole blocks");
     auto tok = [&](int pi) { return g.reverse ? T - 1 - pi : pi; };
 
     // ---- staging: raw loads of a block into registers, then fp32 (normalised) into LDS ----
@@ -169,18 +189,26 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g0
     const auto ors = make_rsrc(ob, ((int64_t)(T - 1) * p.os[1] + kRB) * ESZ);
     const int ksb = (int)(p.ks[1] * ESZ), qsb = (int)(p.qs[1] * ESZ), vsb = (int)(p.vs[1] * ESZ), osb = (int)(p.os[1] * ESZ);
     constexpr int OUT = (int)0x80000000;   // beyond every resource
-    uint4 rk[NLC], rq[NLC], rv = {0u, 0u, 0u, 0u}, rdo = {0u, 0u, 0u, 0u};
-    float ra = 1.f, rbt = 0.f;
-    auto load_block = [&](int blk, bool with_q) {
+    // one block's raw loads (a register set of the staging ring)
+    struct Staged {
+        uint4 rk[NLC], rq[NLC], rv, rdo;
+        float ra, rbt;
+        float ck[NG];   // the block's state checkpoint (walk only)
+    };
+    auto load_block = [&](Staged& st, int blk, bool with_q, bool with_ck) {
         const int pi0 = blk * TB;
+        if (with_ck) {
+#pragma unroll
+            for (int j = 0; j < NG; ++j) st.ck[j] = ck[((int64_t)blk * kRB + rl) * DK + 16 * j + part];
+        }
 #pragma unroll
         for (int i = 0; i < NLC; ++i) {
             const int e = lane + 64 * i, ti = e / CPR, c = e - ti * CPR;
             const bool ok = e < NCH && pi0 + ti < T;
             const int t = ok ? tok(pi0 + ti) : 0;
-            rk[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, ok ? t * ksb + 16 * c : OUT, 0, 0));
+            st.rk[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, ok ? t * ksb + 16 * c : OUT, 0, 0));
             if (with_q)
-                rq[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(qrs, ok ? t * qsb + 16 * c : OUT, 0, 0));
+                st.rq[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(qrs, ok ? t * qsb + 16 * c : OUT, 0, 0));
         }
         {
             // token ti = lane: its 4 v (d_o) values, 16 bytes (fp32) or 8 bytes as two dwords (bf16)
@@ -188,24 +216,26 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g0
             const int t = ok ? tok(pi0 + lane) : 0;
             const int vo = ok ? t * vsb : OUT, oo = ok ? t * osb : OUT;
             if constexpr (F32) {
-                rv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, vo, 0, 0));
-                if (with_q) rdo = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ors, oo, 0, 0));
+                st.rv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, vo, 0, 0));
+                if (with_q) st.rdo = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ors, oo, 0, 0));
             } else {
-                rv.x = __builtin_amdgcn_raw_buffer_load_b32(vrs, vo, 0, 0);
-                rv.y = __builtin_amdgcn_raw_buffer_load_b32(vrs, ok ? vo + 4 : OUT, 0, 0);
+                st.rv.x = __builtin_amdgcn_raw_buffer_load_b32(vrs, vo, 0, 0);
+                st.rv.y = __builtin_amdgcn_raw_buffer_load_b32(vrs, ok ? vo + 4 : OUT, 0, 0);
                 if (with_q) {
-                    rdo.x = __builtin_amdgcn_raw_buffer_load_b32(ors, oo, 0, 0);
-                    rdo.y = __builtin_amdgcn_raw_buffer_load_b32(ors, ok ? oo + 4 : OUT, 0, 0);
+                    st.rdo.x = __builtin_amdgcn_raw_buffer_load_b32(ors, oo, 0, 0);
+                    st.rdo.y = __builtin_amdgcn_raw_buffer_load_b32(ors, ok ? oo + 4 : OUT, 0, 0);
                 }
             }
         }
-        ra = 1.f;
-        rbt = 0.f;
+        // gates of tokens past T: a = 1 (log a = 0), beta = 0; a given as log a is exponentiated
+        // when the block is staged, so that no arithmetic waits for these loads here
+        st.ra = p.gate_log ? 0.f : 1.f;
+        st.rbt = 0.f;
         if (lane < TB && pi0 + lane < T) {
             const int64_t t = tok(pi0 + lane);
             const int64_t gq = (int64_t)b * p.gs[0] + t * p.gs[1] + (int64_t)h * p.gs[2];
-            ra = p.gate_log ? expf(p.a[gq]) : p.a[gq];
-            rbt = p.beta[gq];
+            st.ra = p.a[gq];
+            st.rbt = p.beta[gq];
         }
     };
     // a 16-byte chunk of EPC elements as fp32, to dst (16-byte aligned)
@@ -228,55 +258,84 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g0
             *reinterpret_cast<float4*>(dst) = float4{__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xffff0000u),
                                                      __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xffff0000u)};
     };
-    auto store_block = [&](bool with_q) {
+    auto store_block = [&](const Staged& st, bool with_q) {
 #pragma unroll
         for (int i = 0; i < NLC; ++i) {
             const int e = lane + 64 * i, ti = e / CPR, c = e - ti * CPR;
             if (e < NCH) {
-                put_chunk(&skn[ti][EPC * c], rk[i]);
-                if (with_q) put_chunk(&sqn[ti][EPC * c], rq[i]);
+                put_chunk(&skn[ti][EPC * c], st.rk[i]);
+                if (with_q) put_chunk(&sqn[ti][EPC * c], st.rq[i]);
             }
         }
         if (lane < TB) {
-            put4(&sv[lane][0], rv);
-            if (with_q) put4(&sdo[lane][0], rdo);
+            put4(&sv[lane][0], st.rv);
+            if (with_q) put4(&sdo[lane][0], st.rdo);
         }
         if (lane < TB) {
-            sa[lane] = ra;
-            sb[lane] = rbt;
+            sa[lane] = p.gate_log ? expf(st.ra) : st.ra;
+            sb[lane] = st.rbt;
         }
         lds_order();
-        // normalise the rows in place: lanes 4 r + q (r < TB) sum row r of k (q = 0, 1) or of q
-        // (q = 2, 3) over half the columns each, combined across the lane pair
+        // normalise the rows in place: lane 4 r + u (r < 2 TB = 16) holds quarter u of row r of k
+        // (r < TB) or of q (row r - TB): its DK/4 values are read at once, summed, combined over the
+        // lane quad, scaled and written back (one LDS round trip per block)
+        static_assert(2 * TB * 4 == 64, "four lanes per staged k or q row");
         if (p.l2norm) {
-            const int r = lane >> 2, which = (lane >> 1) & 1, half = lane & 1;
-            float* rowp = (which ? &sqn[0][0] : &skn[0][0]) + r * DK + half * (DK / 2);
+            const int r = lane >> 2, u = lane & 3;
+            const bool isq = r >= TB;
+            float* rowp = (isq ? &sqn[0][0] : &skn[0][0]) + (isq ? r - TB : r) * DK + u * (DK / 4);
+            const bool act = with_q || !isq;
+            float4 xs[DK / 16];
             float ss = 0.f;
-            if (r < TB && (with_q || !which)) {
+            if (act) {
 #pragma unroll
-                for (int c = 0; c < DK / 2; c += 4) {
-                    const float4 x = *reinterpret_cast<const float4*>(rowp + c);
-                    ss += dot4(x, x);
-                }
+                for (int c = 0; c < DK / 16; ++c) xs[c] = *reinterpret_cast<const float4*>(rowp + 4 * c);
+#pragma unroll
+                for (int c = 0; c < DK / 16; ++c) ss += dot4(xs[c], xs[c]);
             }
-            ss += dpp<0xB1>(ss);   // lane pair: quad permutation [1,0,3,2]
+            ss += dpp<0xB1>(ss);   // quad permutations [1,0,3,2] and [2,3,0,1]
+            ss += dpp<0x4E>(ss);
             // rows past the end of the sequence are zero and stay zero
             const float sc = ss + p.eps > 0.f ? 1.f / sqrtf(ss + p.eps) : 0.f;
-            if (r < TB && (with_q || !which)) {
+            if (act) {
 #pragma unroll
-                for (int c = 0; c < DK / 2; c += 4) {
-                    float4 x = *reinterpret_cast<const float4*>(rowp + c);
+                for (int c = 0; c < DK / 16; ++c) {
+                    float4 x = xs[c];
                     x.x *= sc; x.y *= sc; x.z *= sc; x.w *= sc;
-                    *reinterpret_cast<float4*>(rowp + c) = x;
+                    *reinterpret_cast<float4*>(rowp + 4 * c) = x;
                 }
             }
         }
         lds_order();
     };
+    // blocks first, first + dirn, ... (count of them) in turn: each is staged into LDS and handed to
+    // body; its loads were issued three blocks earlier, in a ring of three register sets
+    // (with_ck: the block's state checkpoint is loaded with it and handed to body in registers)
+    auto run_blocks = [&](int first, int count, int dirn, bool with_q, bool with_ck, auto&& body)
+                          __attribute__((always_inline)) {
+        Staged s0, s1, s2;
+        load_block(s0, first, with_q, with_ck);
+        if (count > 1) load_block(s1, first + dirn, with_q, with_ck);
+        if (count > 2) load_block(s2, first + 2 * dirn, with_q, with_ck);
+        auto one = [&](Staged& st, int i) __attribute__((always_inline)) {
+            store_block(st, with_q);
+            float ckv[NG];
+#pragma unroll
+            for (int j = 0; j < NG; ++j) ckv[j] = with_ck ? st.ck[j] : 0.f;
+            if (i + 3 < count) load_block(st, first + (i + 3) * dirn, with_q, with_ck);
+            body(first + i * dirn, ckv);
+        };
+        for (int i = 0; i < count; i += 3) {
+            one(s0, i);
+            if (i + 1 < count) one(s1, i + 1);
+            if (i + 2 < count) one(s2, i + 2);
+        }
+    };
     // column of this lane in staged row r: 16 j + part
     auto krow = [&](int r, int j) { return skn[r][16 * j + part]; };
     auto qrow = [&](int r, int j) { return sqn[r][16 * j + part]; };
     auto ckp = [&](int blk, int j) { return ck + ((int64_t)blk * kRB + rl) * DK + 16 * j + part; };
+    auto gckp = [&](int seg, int j) { return gk0 + ((int64_t)seg * kRB + rl) * DK + 16 * j + part; };
     // a dot product over the lane's NG columns in two independent chains, then over the row's lanes
     auto rowdot = [&](const float* a, const float* c) {
         float s0 = 0.f, s1 = 0.f;
@@ -302,32 +361,56 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g0
         return x;
     };
 
-    // ---- forward: checkpoints before every block ----
+    float G[NG];
+    if (phase == 0 && unit == 0) {
+        // ---- forward: checkpoints before every block ----
 #pragma unroll
-    for (int j = 0; j < NG; ++j)
-        S[j] = g.state0 ? g.state0[(((int64_t)b * p.H + h) * p.Dv + row) * DK + 16 * j + part] : 0.f;
-    if (nblk > 0) load_block(0, false);
-    for (int blk = 0; blk < nblk; ++blk) {
-        store_block(false);
-        if (blk + 1 < nblk) load_block(blk + 1, false);
+        for (int j = 0; j < NG; ++j)
+            S[j] = g.state0 ? g.state0[(((int64_t)b * p.H + h) * p.Dv + row) * DK + 16 * j + part] : 0.f;
+        run_blocks(0, nblk, 1, false, false, [&](int blk, const float*) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < NG; ++j) *ckp(blk, j) = S[j];
-        const int n = min(TB, T - blk * TB);
-        for (int r = 0; r < n; ++r) (void)fwd_token(r);
+            for (int j = 0; j < NG; ++j) *ckp(blk, j) = S[j];
+            const int n = min(TB, T - blk * TB);
+            for (int r = 0; r < n; ++r) (void)fwd_token(r);
+        });
+        return;
+    }
+    if (phase == 0) {
+        // ---- the adjoint recurrence alone, backward: dL/dS at the end of every segment ----
+#pragma unroll
+        for (int j = 0; j < NG; ++j) G[j] = g.d_state ? g.d_state[(((int64_t)b * p.H + h) * p.Dv + row) * DK + 16 * j + part] : 0.f;
+        run_blocks(nblk - 1, nblk, -1, true, false, [&](int blk, const float*) __attribute__((always_inline)) {
+            if (blk == nblk - 1 || (blk + 1) % BPS == 0) {
+#pragma unroll
+                for (int j = 0; j < NG; ++j) *gckp(blk / BPS, j) = G[j];
+            }
+            const int n = min(TB, T - blk * TB);
+            for (int r = n - 1; r >= 0; --r) {
+                float kr[NG];
+                const float dor = p.scale * sdo[r][rl], at = sa[r], bt = sb[r];
+#pragma unroll
+                for (int j = 0; j < NG; ++j) {
+                    kr[j] = krow(r, j);
+                    G[j] += dor * qrow(r, j);
+                }
+                const float gk = rowdot(G, kr);
+                const float cg = bt * gk;
+#pragma unroll
+                for (int j = 0; j < NG; ++j) G[j] = at * (G[j] - cg * kr[j]);
+            }
+        });
+        return;
     }
 
-    // ---- backward over the blocks in reverse ----
-    float G[NG];
+    // ---- phase 1: the walk of segment `unit`, its blocks in reverse, from its adjoint checkpoint ----
+    const int blo = unit * BPS, bhi = min(nblk, blo + BPS) - 1;
 #pragma unroll
-    for (int j = 0; j < NG; ++j) G[j] = g.d_state ? g.d_state[(((int64_t)b * p.H + h) * p.Dv + row) * DK + 16 * j + part] : 0.f;
-    if (nblk > 0) load_block(nblk - 1, true);
-    for (int blk = nblk - 1; blk >= 0; --blk) {
-        store_block(true);
-        if (blk > 0) load_block(blk - 1, true);
+    for (int j = 0; j < NG; ++j) G[j] = *gckp(unit, j);
+    run_blocks(bhi, bhi - blo + 1, -1, true, true, [&](int blk, const float* ckv) __attribute__((always_inline)) {
         const int n = min(TB, T - blk * TB);
         // recompute the block's states from its checkpoint: S_{t-1} of each token into LDS
 #pragma unroll
-        for (int j = 0; j < NG; ++j) S[j] = *ckp(blk, j);
+        for (int j = 0; j < NG; ++j) S[j] = ckv[j];
         for (int r = 0; r < n; ++r) {
 #pragma unroll
             for (int j = 0; j < NG; ++j) sst[r][j][lane] = S[j];
@@ -411,8 +494,8 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g0
             walk(ob, oa, r - 1);
         }
         if (r == 0) walk(oa, ob, 0);
-    }
-    if (g.d_state0) {
+    });
+    if (unit == 0 && g.d_state0) {
 #pragma unroll
         for (int j = 0; j < NG; ++j)
             g.d_state0[(((int64_t)b * p.H + h) * p.Dv + row) * DK + 16 * j + part] = G[j];
@@ -491,22 +574,23 @@ __global__ __launch_bounds__(64) void gdn_bwd_reduce_kernel(Params p, BwdParams 
 }
 
 template <int NG>
-static void launch_rows_ng(const Params& p, const BwdParams& g0, const BwdParams& g1, hipStream_t s, int nwg0, int grid) {
-    if (p.io_f32) hipLaunchKernelGGL((gdn_bwd_rows_kernel<NG, true>), dim3(grid), dim3(64), 0, s, p, g0, g1, nwg0);
-    else hipLaunchKernelGGL((gdn_bwd_rows_kernel<NG, false>), dim3(grid), dim3(64), 0, s, p, g0, g1, nwg0);
+static void launch_rows_ng(const Params& p, const BwdParams& g0, const BwdParams& g1, hipStream_t s, int nunits, int grid,
+                           int phase) {
+    if (p.io_f32) hipLaunchKernelGGL((gdn_bwd_rows_kernel<NG, true>), dim3(grid), dim3(64), 0, s, p, g0, g1, nunits, phase);
+    else hipLaunchKernelGGL((gdn_bwd_rows_kernel<NG, false>), dim3(grid), dim3(64), 0, s, p, g0, g1, nunits, phase);
 }
 
-static hipError_t launch_rows(const Params& p, const BwdParams& g0, const BwdParams& g1, hipStream_t s, int nwg0,
-                              int grid) {
+static hipError_t launch_rows(const Params& p, const BwdParams& g0, const BwdParams& g1, hipStream_t s, int nunits,
+                              int grid, int phase) {
     switch (p.Dk) {
-        case 16: launch_rows_ng<1>(p, g0, g1, s, nwg0, grid); break;
-        case 32: launch_rows_ng<2>(p, g0, g1, s, nwg0, grid); break;
-        case 48: launch_rows_ng<3>(p, g0, g1, s, nwg0, grid); break;
-        case 64: launch_rows_ng<4>(p, g0, g1, s, nwg0, grid); break;
-        case 80: launch_rows_ng<5>(p, g0, g1, s, nwg0, grid); break;
-        case 96: launch_rows_ng<6>(p, g0, g1, s, nwg0, grid); break;
-        case 112: launch_rows_ng<7>(p, g0, g1, s, nwg0, grid); break;
-        case 128: launch_rows_ng<8>(p, g0, g1, s, nwg0, grid); break;
+        case 16: launch_rows_ng<1>(p, g0, g1, s, nunits, grid, phase); break;
+        case 32: launch_rows_ng<2>(p, g0, g1, s, nunits, grid, phase); break;
+        case 48: launch_rows_ng<3>(p, g0, g1, s, nunits, grid, phase); break;
+        case 64: launch_rows_ng<4>(p, g0, g1, s, nunits, grid, phase); break;
+        case 80: launch_rows_ng<5>(p, g0, g1, s, nunits, grid, phase); break;
+        case 96: launch_rows_ng<6>(p, g0, g1, s, nunits, grid, phase); break;
+        case 112: launch_rows_ng<7>(p, g0, g1, s, nunits, grid, phase); break;
+        case 128: launch_rows_ng<8>(p, g0, g1, s, nunits, grid, phase); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -515,10 +599,12 @@ static hipError_t launch_rows(const Params& p, const BwdParams& g0, const BwdPar
 hipError_t launch_backward(const Params& p, const BwdParams& g0, const BwdParams* g1, hipStream_t s, Timing* tm) {
     const int nscan = g1 ? 2 : 1;
     const int rows0 = p.B * p.H * (p.Dv / kRB);
+    const int nseg = (int)((p.T + kSEG - 1) / kSEG);
     const int64_t red0 = (int64_t)p.B * p.T * p.H;
     const BwdParams& gb = g1 ? *g1 : g0;
     tm_begin(tm, s, KBWD);
-    hipError_t e = launch_rows(p, g0, gb, s, rows0, nscan * rows0);
+    hipError_t e = launch_rows(p, g0, gb, s, 2 * rows0, nscan * 2 * rows0, 0);
+    if (e == hipSuccess) e = launch_rows(p, g0, gb, s, nseg * rows0, nscan * nseg * rows0, 1);
     if (e == hipSuccess && red0 > 0) {
         const unsigned grid = (unsigned)(nscan * red0);
         if (p.io_f32) hipLaunchKernelGGL(gdn_bwd_reduce_kernel<true>, dim3(grid), dim3(64), 0, s, p, g0, gb, red0);

@@ -58,7 +58,7 @@ inline int scan_variants(const Params& p) {
 int64_t chunk_item_bytes(int C, int D);
 
 // Gradient of one token-sequential scan (fp32).  Workspace (owned by the handle): state
-// checkpoints [B][H][Dv/16][ck_per][16][Dk] (the state before every staged block of tokens)
+// checkpoints [B][H][Dv/4][ck_per][4][Dk] (the state before every staged block of tokens)
 // and partial sums [B][T][H][Dv/16][2 Dk + 4].
 struct BwdParams {
     const void* d_o;       // dL/do, io dtype, o's strides (Params::os)
@@ -71,8 +71,10 @@ struct BwdParams {
     float* dbeta;          // [B, T, H]
     float* d_state0;       // [B, H, Dv, Dk], or null
     float* states;         // checkpoints
+    float* gck;            // adjoint checkpoints [B][H][Dv/4][gck_per][4][Dk]: dL/dS at the end of every segment
     float* partials;
     int64_t ck_per;        // checkpoints per (b, h, row block) in `states`
+    int64_t gck_per;       // adjoint checkpoints per (b, h, row block) in `gck`
     int reverse;           // 0: the forward scan (t ascending), 1: the reverse scan
 };
 // Bytes of the backward workspace for max_tokens tokens, or -1 if the size overflows int64.
@@ -80,6 +82,8 @@ int64_t backward_ws_bytes(int B, int H, int Dk, int Dv, int64_t max_tokens);
 // Checkpoints per (b, h, row block) for max_tokens tokens, and the floats they take in all
 // (where the partial sums start in the workspace).
 int64_t backward_ckpt_per(int64_t max_tokens);
+int64_t backward_gck_per(int64_t max_tokens);
+int64_t backward_state_ckpt_floats(int B, int H, int Dk, int Dv, int64_t max_tokens);
 int64_t backward_ckpt_floats(int B, int H, int Dk, int Dv, int64_t max_tokens);
 
 // Which (C, D) pairs the chunked kernels are built for.
