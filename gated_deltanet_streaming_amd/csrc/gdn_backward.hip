@@ -331,6 +331,16 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g0
             if (i + 2 < count) one(s2, i + 2);
         }
     };
+    // body(r) for the n tokens of a block in order (backward: r = n-1 .. 0); a full block is unrolled
+    // so that the compiler can issue later tokens' LDS reads ahead of earlier tokens' arithmetic
+    auto for_tokens = [&](int n, bool backward, auto&& body) __attribute__((always_inline)) {
+        if (n == TB) {
+#pragma unroll
+            for (int i = 0; i < TB; ++i) body(backward ? TB - 1 - i : i);
+        } else {
+            for (int i = 0; i < n; ++i) body(backward ? n - 1 - i : i);
+        }
+    };
     // column of this lane in staged row r: 16 j + part
     auto krow = [&](int r, int j) { return skn[r][16 * j + part]; };
     auto qrow = [&](int r, int j) { return sqn[r][16 * j + part]; };
@@ -349,19 +359,30 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g0
 
     // one token of the forward recurrence on S (row dot and update); returns x = S k
     float S[NG];
-    auto fwd_token = [&](int r) {
-        float kr[NG];
-#pragma unroll
-        for (int j = 0; j < NG; ++j) kr[j] = krow(r, j);
-        const float at = sa[r], bt = sb[r], vr = sv[r][rl];
+    auto fwd_step = [&](const float* kr, float at, float bt, float vr) __attribute__((always_inline)) {
         const float x = rowdot(S, kr);
         const float c0 = bt * x, c1 = bt * vr;
 #pragma unroll
         for (int j = 0; j < NG; ++j) S[j] = at * (S[j] - c0 * kr[j]) + c1 * kr[j];
         return x;
     };
-
+    auto fwd_token = [&](int r) {
+        float kr[NG];
+#pragma unroll
+        for (int j = 0; j < NG; ++j) kr[j] = krow(r, j);
+        return fwd_step(kr, sa[r], sb[r], sv[r][rl]);
+    };
+    // one token of the adjoint recurrence: G <- a (G + scale do q^T)(I - beta k k^T)
     float G[NG];
+    auto adj_step = [&](const float* kr, const float* qr, float dor, float at, float bt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < NG; ++j) G[j] += dor * qr[j];
+        const float gk = rowdot(G, kr);
+        const float cg = bt * gk;
+#pragma unroll
+        for (int j = 0; j < NG; ++j) G[j] = at * (G[j] - cg * kr[j]);
+    };
+
     if (phase == 0 && unit == 0) {
         // ---- forward: checkpoints before every block ----
 #pragma unroll
@@ -371,7 +392,22 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g0
 #pragma unroll
             for (int j = 0; j < NG; ++j) *ckp(blk, j) = S[j];
             const int n = min(TB, T - blk * TB);
-            for (int r = 0; r < n; ++r) (void)fwd_token(r);
+            if (n == TB) {
+                // a full block: every operand into registers first, then the chain
+                float kb[TB][NG], ab[TB], bb[TB], vb[TB];
+#pragma unroll
+                for (int r = 0; r < TB; ++r) {
+#pragma unroll
+                    for (int j = 0; j < NG; ++j) kb[r][j] = krow(r, j);
+                    ab[r] = sa[r];
+                    bb[r] = sb[r];
+                    vb[r] = sv[r][rl];
+                }
+#pragma unroll
+                for (int r = 0; r < TB; ++r) (void)fwd_step(kb[r], ab[r], bb[r], vb[r]);
+            } else {
+                for (int r = 0; r < n; ++r) (void)fwd_token(r);
+            }
         });
         return;
     }
@@ -385,18 +421,38 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g0
                 for (int j = 0; j < NG; ++j) *gckp(blk / BPS, j) = G[j];
             }
             const int n = min(TB, T - blk * TB);
-            for (int r = n - 1; r >= 0; --r) {
-                float kr[NG];
-                const float dor = p.scale * sdo[r][rl], at = sa[r], bt = sb[r];
+            auto token = [&](int r) __attribute__((always_inline)) {
+                float kr[NG], qr[NG];
 #pragma unroll
                 for (int j = 0; j < NG; ++j) {
                     kr[j] = krow(r, j);
-                    G[j] += dor * qrow(r, j);
+                    qr[j] = qrow(r, j);
                 }
-                const float gk = rowdot(G, kr);
-                const float cg = bt * gk;
+                adj_step(kr, qr, p.scale * sdo[r][rl], sa[r], sb[r]);
+            };
+            if (n == TB) {
+                // a full block: half the block's operands into registers at a time, then the chain
+                constexpr int HB = TB / 2;
 #pragma unroll
-                for (int j = 0; j < NG; ++j) G[j] = at * (G[j] - cg * kr[j]);
+                for (int hb = 1; hb >= 0; --hb) {
+                    float kb[HB][NG], qb[HB][NG], db[HB], ab[HB], bb[HB];
+#pragma unroll
+                    for (int i = 0; i < HB; ++i) {
+                        const int r = HB * hb + i;
+#pragma unroll
+                        for (int j = 0; j < NG; ++j) {
+                            kb[i][j] = krow(r, j);
+                            qb[i][j] = qrow(r, j);
+                        }
+                        db[i] = p.scale * sdo[r][rl];
+                        ab[i] = sa[r];
+                        bb[i] = sb[r];
+                    }
+#pragma unroll
+                    for (int i = HB - 1; i >= 0; --i) adj_step(kb[i], qb[i], db[i], ab[i], bb[i]);
+                }
+            } else {
+                for (int r = n - 1; r >= 0; --r) token(r);
             }
         });
         return;
@@ -411,12 +467,12 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g0
         // recompute the block's states from its checkpoint: S_{t-1} of each token into LDS
 #pragma unroll
         for (int j = 0; j < NG; ++j) S[j] = ckv[j];
-        for (int r = 0; r < n; ++r) {
+        for_tokens(n, false, [&](int r) __attribute__((always_inline)) {
 #pragma unroll
             for (int j = 0; j < NG; ++j) sst[r][j][lane] = S[j];
             const float x = fwd_token(r);
             if (part == 0) sx[r][rl] = x;
-        }
+        });
         // S is the state after the block's last token; walk the block's tokens backward.  A token's
         // LDS operands are read while the previous token finishes (after its column-sum reads, so
         // that they do not hold those back), alternating between two register sets.
@@ -523,6 +579,9 @@ __global__ __launch_bounds__(64) void gdn_bwd_reduce_kernel(Params p, BwdParams 
     const int Dk = p.Dk, nrb = p.Dv / kRB, wid = 2 * Dk + 4;
     const float* pw = g.partials + (((int64_t)b * p.T + t) * p.H + h) * nrb * wid;
     float gq[2] = {0.f, 0.f}, gkk[2] = {0.f, 0.f}, da = 0.f, db = 0.f;
+    // (unrolled so that the loads of several row blocks are in flight at once; the sums stay in
+    // row-block order)
+#pragma unroll 8
     for (int r = 0; r < nrb; ++r) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
