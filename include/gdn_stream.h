@@ -237,9 +237,10 @@ typedef struct gdn_grad {
  * reverse scan (reverse = 1: t descending from zero) over T tokens of io->q, k, v,
  * a, beta (io->o is not used; its strides give d_o's layout).  Never reads or
  * writes the cache.  Asynchronous on hip_stream.  The first call on a handle
- * allocates a backward workspace of 4 (B H (d_v/4)(ceil(max_tokens/8)+1) 4 d_k
- * + B max_tokens H (d_v/4)(2 d_k + 4)) bytes (state checkpoints every block of
- * 8 tokens, and partial sums per block of 4 state rows), kept until gdn_stream_destroy
+ * allocates a backward workspace of 4 (B H (d_v/4)(ceil(max_tokens/8)+1
+ * + ceil(max_tokens/64)) 4 d_k + B max_tokens H (d_v/4)(2 d_k + 4)) bytes (state
+ * checkpoints every block of 8 tokens, adjoint checkpoints every 64 tokens, and
+ * partial sums per block of 4 state rows), kept until gdn_stream_destroy
  * (GDN_E_NOMEM if that fails).  Errors: GDN_E_INVAL (NULL handle/io/g/output,
  * bad strides, state0 given with reverse), GDN_E_SHAPE (T outside [0, max_tokens]),
  * GDN_E_HIP; on error nothing is enqueued.  T = 0 writes d_state0 = d_state. */

@@ -209,11 +209,12 @@ def test_backward_bidir_rejects_a_start_state_for_the_reverse_scan():
         s.close()
 
 
-@pytest.mark.parametrize("T", [1, 7, 8, 9, 17])
+@pytest.mark.parametrize("T", [1, 7, 8, 9, 17, 63, 65, 129])
 def test_backward_staging_block_edges(T):
     """Lengths around the 8-token staging block (one token, a short block, exactly one block, one
-    token into the second, two blocks and one), both scans through the bidirectional call, against
-    the oracle."""
+    token into the second, two blocks and one) and the 64-token walk segment (one short of a segment,
+    one token into the second, two segments and one), both scans through the bidirectional call,
+    against the oracle."""
     B, H, D = 1, 2, 32
     d = gdn_inputs.batch(90 + T, B, T, H, D, with_state=True)
     dO, dSf, dSr = _bidir_inputs(d, D, T, 90 + T)
