@@ -58,7 +58,7 @@ def _check_all(g, ref):
 
 
 @pytest.mark.parametrize("reverse", [False, True])
-@pytest.mark.parametrize("D", [16, 32, 112])
+@pytest.mark.parametrize("D", [16, 32, 48, 112, 128])
 def test_backward_small(D, reverse):
     d = gdn_inputs.batch(70 + D, 2, 50, 3, D, with_state=True)
     g, ref = _grads(d, D, D, 50, reverse=reverse, seed=D)
