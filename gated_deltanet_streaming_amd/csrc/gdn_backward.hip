@@ -52,11 +52,12 @@ void tm_end(Timing* tm, hipStream_t s) {
 // gdn_bwd_rows_kernel: one 64-lane workgroup per (b, h, block of 4 state rows);
 // lane l owns row 4 rb + l/16 and the column 16 j + l%16 of every 16-column
 // group j.  Tokens are staged through LDS in
-// blocks of TB (k and q normalised once per block; the next block's global loads
-// go out before the current block is worked on).  A forward pass keeps only the
-// state before every block (a checkpoint); the backward pass walks the blocks in
-// reverse, recomputes the states inside a block from its checkpoint into LDS and
-// then walks its tokens backward.  dv and the start-state gradient are row-local;
+// blocks of TB (k and q normalised once per block; a block's global loads go out
+// three blocks before it is worked on, into a ring of register sets).  A forward
+// pass keeps only the state before every block (a checkpoint) and an adjoint pass
+// keeps G at the end of every segment of kSEG tokens; each segment is then walked
+// backward on its own, recomputing the states inside each of its blocks from the
+// block's checkpoint into LDS.  dv and the start-state gradient are row-local;
 // the other gradients sum over all rows: per token the rows' terms go through an
 // LDS buffer and each lane adds one float4 column group over the 4 rows in row
 // order, then the workgroup writes its rows' partial sums, and gdn_bwd_reduce_kernel
