@@ -136,8 +136,12 @@ __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 // recomputing each block's states from its state checkpoint; the segments are independent.  The
 // adjoint pass and the walks perform the same operations on G in the same order.
 // Workgroups [0, nunits) work on g0's scan, [nunits, 2 nunits) on g1's (the bidirectional call).
-template <int NG, bool F32>
-__global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g0, BwdParams g1, int nunits, int phase) {
+// The phases are separate instances: phase 0 uses neither the block-state nor the column-sum
+// buffer, and with them gone (and phase 1's registers) more of its workgroups share a CU: with bf16
+// I/O its registers fit three wavefronts per SIMD, so that the 2 x 2 x (d_v / 4) x H workgroups of a
+// bidirectional call run in one round (fp32 I/O stages twice the bytes and would spill).
+template <int NG, bool F32, int PHASE>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PHASE == 0 && !F32 ? 3 : 1))) void gdn_bwd_rows_kernel(Params p, BwdParams g0, BwdParams g1, int nunits) {
     constexpr int DK = 16 * NG;               // d_k
     constexpr int TB = 8;                     // tokens per staged block (LDS: states of a block)
     constexpr int NLQ = (TB * DK + 255) / 256;   // staged elements of k (and of q) per lane, 4 at a time
@@ -384,7 +388,8 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g0
         for (int j = 0; j < NG; ++j) G[j] = at * (G[j] - cg * kr[j]);
     };
 
-    if (phase == 0 && unit == 0) {
+    if constexpr (PHASE == 0) {
+    if (unit == 0) {
         // ---- forward: checkpoints before every block ----
 #pragma unroll
         for (int j = 0; j < NG; ++j)
@@ -394,25 +399,30 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g0
             for (int j = 0; j < NG; ++j) *ckp(blk, j) = S[j];
             const int n = min(TB, T - blk * TB);
             if (n == TB) {
-                // a full block: every operand into registers first, then the chain
-                float kb[TB][NG], ab[TB], bb[TB], vb[TB];
+                // a full block: half the block's operands into registers at a time, then the chain
+                constexpr int HB = TB / 2;
 #pragma unroll
-                for (int r = 0; r < TB; ++r) {
+                for (int hb = 0; hb < 2; ++hb) {
+                    float kb[HB][NG], ab[HB], bb[HB], vb[HB];
 #pragma unroll
-                    for (int j = 0; j < NG; ++j) kb[r][j] = krow(r, j);
-                    ab[r] = sa[r];
-                    bb[r] = sb[r];
-                    vb[r] = sv[r][rl];
+                    for (int i = 0; i < HB; ++i) {
+                        const int r = HB * hb + i;
+#pragma unroll
+                        for (int j = 0; j < NG; ++j) kb[i][j] = krow(r, j);
+                        ab[i] = sa[r];
+                        bb[i] = sb[r];
+                        vb[i] = sv[r][rl];
+                    }
+#pragma unroll
+                    for (int i = 0; i < HB; ++i) (void)fwd_step(kb[i], ab[i], bb[i], vb[i]);
                 }
-#pragma unroll
-                for (int r = 0; r < TB; ++r) (void)fwd_step(kb[r], ab[r], bb[r], vb[r]);
             } else {
                 for (int r = 0; r < n; ++r) (void)fwd_token(r);
             }
         });
         return;
     }
-    if (phase == 0) {
+    {
         // ---- the adjoint recurrence alone, backward: dL/dS at the end of every segment ----
 #pragma unroll
         for (int j = 0; j < NG; ++j) G[j] = g.d_state ? g.d_state[(((int64_t)b * p.H + h) * p.Dv + row) * DK + 16 * j + part] : 0.f;
@@ -432,10 +442,10 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g0
                 adj_step(kr, qr, p.scale * sdo[r][rl], sa[r], sb[r]);
             };
             if (n == TB) {
-                // a full block: half the block's operands into registers at a time, then the chain
-                constexpr int HB = TB / 2;
+                // a full block: a quarter of the block's operands into registers at a time, then the chain
+                constexpr int HB = TB / 4;
 #pragma unroll
-                for (int hb = 1; hb >= 0; --hb) {
+                for (int hb = TB / HB - 1; hb >= 0; --hb) {
                     float kb[HB][NG], qb[HB][NG], db[HB], ab[HB], bb[HB];
 #pragma unroll
                     for (int i = 0; i < HB; ++i) {
@@ -458,7 +468,7 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g0
         });
         return;
     }
-
+    } else {
     // ---- phase 1: the walk of segment `unit`, its blocks in reverse, from its adjoint checkpoint ----
     const int blo = unit * BPS, bhi = min(nblk, blo + BPS) - 1;
 #pragma unroll
@@ -557,6 +567,7 @@ __global__ __launch_bounds__(64) void gdn_bwd_rows_kernel(Params p, BwdParams g0
         for (int j = 0; j < NG; ++j)
             g.d_state0[(((int64_t)b * p.H + h) * p.Dv + row) * DK + 16 * j + part] = G[j];
     }
+    }
 }
 
 // sum over the 64 lanes
@@ -633,11 +644,16 @@ __global__ __launch_bounds__(64) void gdn_bwd_reduce_kernel(Params p, BwdParams 
     }
 }
 
+template <int NG, int PHASE>
+static void launch_rows_ph(const Params& p, const BwdParams& g0, const BwdParams& g1, hipStream_t s, int nunits, int grid) {
+    if (p.io_f32) hipLaunchKernelGGL((gdn_bwd_rows_kernel<NG, true, PHASE>), dim3(grid), dim3(64), 0, s, p, g0, g1, nunits);
+    else hipLaunchKernelGGL((gdn_bwd_rows_kernel<NG, false, PHASE>), dim3(grid), dim3(64), 0, s, p, g0, g1, nunits);
+}
 template <int NG>
 static void launch_rows_ng(const Params& p, const BwdParams& g0, const BwdParams& g1, hipStream_t s, int nunits, int grid,
                            int phase) {
-    if (p.io_f32) hipLaunchKernelGGL((gdn_bwd_rows_kernel<NG, true>), dim3(grid), dim3(64), 0, s, p, g0, g1, nunits, phase);
-    else hipLaunchKernelGGL((gdn_bwd_rows_kernel<NG, false>), dim3(grid), dim3(64), 0, s, p, g0, g1, nunits, phase);
+    if (phase == 0) launch_rows_ph<NG, 0>(p, g0, g1, s, nunits, grid);
+    else launch_rows_ph<NG, 1>(p, g0, g1, s, nunits, grid);
 }
 
 static hipError_t launch_rows(const Params& p, const BwdParams& g0, const BwdParams& g1, hipStream_t s, int nunits,
