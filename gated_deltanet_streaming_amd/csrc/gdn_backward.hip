@@ -164,12 +164,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PHASE == 0 &
     const int nblk = (T + TB - 1) / TB;
     const int wid = 2 * DK + 4;
 
-    __shared__ __align__(16) float sst[TB][NG][64];    // S_{t-1} of the block's tokens, lane-major
+    constexpr int SH = TB / 2;                         // tokens whose states LDS holds at once (phase 1)
+    __shared__ __align__(16) float sst[SH][NG][64];    // S_{t-1} of half a block's tokens, lane-major
     __shared__ __align__(16) float skn[TB][DK];        // normalised k of the block's tokens
     __shared__ __align__(16) float sqn[TB][DK];        // normalised q
     __shared__ __align__(16) float scol[2][kRB][DK];   // per-row terms of dq and dk of one token
     __shared__ __align__(16) float sv[TB][kRB], sdo[TB][kRB];
-    __shared__ float sx[TB][kRB], sa[TB], sb[TB];
+    __shared__ float sx[SH][kRB], sa[TB], sb[TB];
 
     float* ck = g.states + (((int64_t)b * p.H + h) * nrb + rb) * g.ck_per * kRB * DK;
     float* gk0 = g.gck + (((int64_t)b * p.H + h) * nrb + rb) * g.gck_per * kRB * DK;
@@ -336,16 +337,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PHASE == 0 &
             if (i + 2 < count) one(s2, i + 2);
         }
     };
-    // body(r) for the n tokens of a block in order (backward: r = n-1 .. 0); a full block is unrolled
-    // so that the compiler can issue later tokens' LDS reads ahead of earlier tokens' arithmetic
-    auto for_tokens = [&](int n, bool backward, auto&& body) __attribute__((always_inline)) {
-        if (n == TB) {
-#pragma unroll
-            for (int i = 0; i < TB; ++i) body(backward ? TB - 1 - i : i);
-        } else {
-            for (int i = 0; i < n; ++i) body(backward ? n - 1 - i : i);
-        }
-    };
     // column of this lane in staged row r: 16 j + part
     auto krow = [&](int r, int j) { return skn[r][16 * j + part]; };
     auto qrow = [&](int r, int j) { return sqn[r][16 * j + part]; };
@@ -475,18 +466,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PHASE == 0 &
     for (int j = 0; j < NG; ++j) G[j] = *gckp(unit, j);
     run_blocks(bhi, bhi - blo + 1, -1, true, true, [&](int blk, const float* ckv) __attribute__((always_inline)) {
         const int n = min(TB, T - blk * TB);
-        // recompute the block's states from its checkpoint: S_{t-1} of each token into LDS
+        // The block is walked in two parts of SH tokens, the later part first, so that LDS holds the
+        // states of one part (18 KB instead of 25 KB of LDS at d = 112: eight workgroups per CU
+        // instead of six).  Each part recomputes the states from the block's checkpoint up to its
+        // last token (the same operations in the same order, so the same bits) and keeps S_{t-1} and
+        // x of its own tokens [lo, hi).
+        int lo = 0;
+        auto rec_token = [&](int r) __attribute__((always_inline)) {
+            if (r >= lo) {
 #pragma unroll
-        for (int j = 0; j < NG; ++j) S[j] = ckv[j];
-        for_tokens(n, false, [&](int r) __attribute__((always_inline)) {
-#pragma unroll
-            for (int j = 0; j < NG; ++j) sst[r][j][lane] = S[j];
+                for (int j = 0; j < NG; ++j) sst[r - lo][j][lane] = S[j];
+            }
             const float x = fwd_token(r);
-            if (part == 0) sx[r][rl] = x;
-        });
-        // S is the state after the block's last token; walk the block's tokens backward.  A token's
-        // LDS operands are read while the previous token finishes (after its column-sum reads, so
-        // that they do not hold those back), alternating between two register sets.
+            if (r >= lo && part == 0) sx[r - lo][rl] = x;
+        };
+        // After the recomputation S is the state after the part's last token; the part's tokens are
+        // walked backward.  A token's LDS operands are read while the previous token finishes (after
+        // its column-sum reads, so that they do not hold those back), alternating between two
+        // register sets.
         struct TokOps {
             float Sp[NG], kr[NG], qr[NG];
             float dor, at, bt, vr, x;
@@ -494,7 +491,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PHASE == 0 &
         auto read_ops = [&](TokOps& o, int r) {
 #pragma unroll
             for (int j = 0; j < NG; ++j) {
-                o.Sp[j] = sst[r][j][lane];
+                o.Sp[j] = sst[r - lo][j][lane];
                 o.kr[j] = krow(r, j);
                 o.qr[j] = qrow(r, j);
             }
@@ -502,7 +499,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PHASE == 0 &
             o.at = sa[r];
             o.bt = sb[r];
             o.vr = sv[r][rl];
-            o.x = sx[r][rl];
+            o.x = sx[r - lo][rl];
         };
         auto walk = [&](const TokOps& c, TokOps& nx, int r) __attribute__((always_inline)) {
             const int64_t t = tok(blk * TB + r);
@@ -543,7 +540,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PHASE == 0 &
                 }
             }
             // the next token's operands, behind the column-sum reads
-            if (r > 0) read_ops(nx, r - 1);
+            if (r > lo) read_ops(nx, r - 1);
             lds_order();
             if (lane < DK / 2) *reinterpret_cast<float4*>(pw + a * DK + c4) = acc;
             if (lane == 0) {
@@ -553,14 +550,28 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PHASE == 0 &
 #pragma unroll
             for (int j = 0; j < NG; ++j) S[j] = c.Sp[j];
         };
-        TokOps oa, ob;
-        read_ops(oa, n - 1);
-        int r = n - 1;
-        for (; r >= 1; r -= 2) {
-            walk(oa, ob, r);
-            walk(ob, oa, r - 1);
+#pragma unroll
+        for (int half = 1; half >= 0; --half) {
+            lo = half * SH;
+            const int hi = half ? n : min(n, SH);
+            if (lo >= hi) continue;
+#pragma unroll
+            for (int j = 0; j < NG; ++j) S[j] = ckv[j];
+            if (n == TB) {
+#pragma unroll
+                for (int r = 0; r < (half ? TB : SH); ++r) rec_token(r);
+            } else {
+                for (int r = 0; r < hi; ++r) rec_token(r);
+            }
+            TokOps oa, ob;
+            read_ops(oa, hi - 1);
+            int r = hi - 1;
+            for (; r >= lo + 1; r -= 2) {
+                walk(oa, ob, r);
+                walk(ob, oa, r - 1);
+            }
+            if (r == lo) walk(oa, ob, lo);
         }
-        if (r == 0) walk(oa, ob, 0);
     });
     if (unit == 0 && g.d_state0) {
 #pragma unroll
