@@ -144,7 +144,6 @@ template <int NG, bool F32, int PHASE>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PHASE == 0 && !F32 ? 3 : 1))) void gdn_bwd_rows_kernel(Params p, BwdParams g0, BwdParams g1, int nunits) {
     constexpr int DK = 16 * NG;               // d_k
     constexpr int TB = 8;                     // tokens per staged block (LDS: states of a block)
-    constexpr int NLQ = (TB * DK + 255) / 256;   // staged elements of k (and of q) per lane, 4 at a time
     static_assert(TB >= kMinTB, "checkpoint sizing");
     const int lane = threadIdx.x, part = lane & (kLPR - 1), rl = lane / kLPR;
     const int nrb = p.Dv / kRB;
@@ -599,24 +598,39 @@ __global__ __launch_bounds__(64) void gdn_bwd_reduce_kernel(Params p, BwdParams 
     const int h = (int)(id % p.H); id /= p.H;
     const int64_t t = id % p.T; id /= p.T;
     const int b = (int)id;
-    const int Dk = p.Dk, nrb = p.Dv / kRB, wid = 2 * Dk + 4;
+    const int Dk = p.Dk, nrb = p.Dv / kRB, wid = 2 * Dk + 4, nq = wid / 4;
     const float* pw = g.partials + (((int64_t)b * p.T + t) * p.H + h) * nrb * wid;
-    float gq[2] = {0.f, 0.f}, gkk[2] = {0.f, 0.f}, da = 0.f, db = 0.f;
-    // (unrolled so that the loads of several row blocks are in flight at once; the sums stay in
-    // row-block order)
+    // lane l adds the 16-byte groups l and l + 64 of every row block's partial row (wid floats, a
+    // multiple of 4) in row-block order, unrolled so that several row blocks' loads are in flight;
+    // the sums then go through LDS to the per-column layout below
+    __shared__ __align__(16) float red[2 * 128 + 4];
+    float4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll 8
     for (int r = 0; r < nrb; ++r) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int c = lane + 64 * j;
-            if (c < Dk) {
-                gq[j] += pw[r * wid + c];
-                gkk[j] += pw[r * wid + Dk + c];
+            const int q4 = lane + 64 * j;
+            if (q4 < nq) {
+                const float4 v4 = *reinterpret_cast<const float4*>(pw + (int64_t)r * wid + 4 * q4);
+                acc[j].x += v4.x;
+                acc[j].y += v4.y;
+                acc[j].z += v4.z;
+                acc[j].w += v4.w;
             }
         }
-        da += pw[r * wid + 2 * Dk];
-        db += pw[r * wid + 2 * Dk + 1];
     }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        if (lane + 64 * j < nq) *reinterpret_cast<float4*>(&red[4 * (lane + 64 * j)]) = acc[j];
+    lds_order();
+    float gq[2], gkk[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int c = lane + 64 * j;
+        gq[j] = (c < Dk) ? red[c] : 0.f;
+        gkk[j] = (c < Dk) ? red[Dk + c] : 0.f;
+    }
+    const float da = red[2 * Dk], db = red[2 * Dk + 1];
     const int64_t kq = (int64_t)b * p.ks[0] + t * p.ks[1] + (int64_t)h * p.ks[2];
     const int64_t qq = (int64_t)b * p.qs[0] + t * p.qs[1] + (int64_t)h * p.qs[2];
     float kx[2], qx[2];
