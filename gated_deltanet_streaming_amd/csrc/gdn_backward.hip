@@ -356,9 +356,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PHASE == 0 &
     float S[NG];
     auto fwd_step = [&](const float* kr, float at, float bt, float vr) __attribute__((always_inline)) {
         const float x = rowdot(S, kr);
-        const float c0 = bt * x, c1 = bt * vr;
+        // a (S - beta x k^T) + beta v k^T = a S + beta (v - a x) k^T: a multiply and an FMA per column
+        const float d = bt * (vr - at * x);
 #pragma unroll
-        for (int j = 0; j < NG; ++j) S[j] = at * (S[j] - c0 * kr[j]) + c1 * kr[j];
+        for (int j = 0; j < NG; ++j) S[j] = fmaf(d, kr[j], at * S[j]);
         return x;
     };
     auto fwd_token = [&](int r) {
