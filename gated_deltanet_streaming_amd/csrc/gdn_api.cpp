@@ -682,6 +682,16 @@ static int ensure_bwd_ws(gdn_stream* s, float** ws) {
         (void)hipGetLastError();
         return fail(GDN_E_NOMEM, "backward workspace (%lld bytes): %s", (long long)bytes, hipGetErrorString(e));
     }
+    if (s->cfg.flags & GDN_POISON_WS) {
+        // NaN bytes: a checkpoint or partial sum that the kernels read without writing shows up
+        e = hipMemset(*ws, 0xff, bytes);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            (void)hipFree(*ws);
+            *ws = nullptr;
+            return fail(GDN_E_HIP, "poisoning the backward workspace: %s", hipGetErrorString(e));
+        }
+    }
     return GDN_OK;
 }
 

@@ -69,8 +69,10 @@ extern "C" {
 #define GDN_GATE_IS_LOG (1u << 1) /* io->a holds log a_t (<= 0) instead of a_t;
                                      the gradient da is then dL/d(log a_t)        */
 #define GDN_POISON_WS   (1u << 2) /* debugging: fill the workspace with NaN bytes at
-                                     init, so that a read of a workspace byte the
-                                     kernels did not write shows up in the output */
+                                     init (the gradient workspaces when the first
+                                     gradient call allocates them), so that a read
+                                     of a workspace byte the kernels did not write
+                                     shows up in the output */
 
 /* per-call flags */
 #define GDN_NO_COMMIT  (1u << 0)  /* forward: leave the cache unchanged; the final

@@ -37,7 +37,8 @@ def _grads(d, D, Dv, T, *, io="bf16", reverse=False, seed=0, with_state=True, wi
     dSf = rng.standard_normal((B, H, Dv, D)).astype(np.float32) if with_final else None
     S0 = d["S0"] if (with_state and not reverse) else None
     ref = oracle.backward(d["q"], d["k"], d["v"], d["a"], d["beta"], dO, S0, dSf, reverse=reverse)
-    s = gb.Stream(B, H, D, Dv, max(T, 1), io_dtype=io)
+    # NaN-filled workspaces: a checkpoint or partial sum read before it is written fails the test
+    s = gb.Stream(B, H, D, Dv, max(T, 1), io_dtype=io, poison_ws=True)
     try:
         t = dev_inputs(d, io=io)
         dt = torch.bfloat16 if io == "bf16" else torch.float32
@@ -139,7 +140,7 @@ def test_backward_bidir_equals_the_two_calls_bitwise():
     B, T, H, D = 1, 300, 3, 112
     d = gdn_inputs.batch(81, B, T, H, D, with_state=True)
     dO, dSf, dSr = _bidir_inputs(d, D, T, 81)
-    s = gb.Stream(B, H, D, D, T)
+    s = gb.Stream(B, H, D, D, T, poison_ws=True)
     try:
         t = dev_inputs(d)
         S0 = torch.from_numpy(np.ascontiguousarray(d["S0"], np.float32)).cuda()
@@ -164,7 +165,7 @@ def test_backward_bidir_against_the_oracle():
     dO, dSf, _ = _bidir_inputs(d, D, T, 82)
     ref_f = oracle.backward(d["q"], d["k"], d["v"], d["a"], d["beta"], dO[0].float().numpy(), d["S0"], dSf.numpy())
     ref_r = oracle.backward(d["q"], d["k"], d["v"], d["a"], d["beta"], dO[1].float().numpy(), None, None, reverse=True)
-    s = gb.Stream(B, H, D, D, T)
+    s = gb.Stream(B, H, D, D, T, poison_ws=True)
     try:
         t = dev_inputs(d)
         S0 = torch.from_numpy(np.ascontiguousarray(d["S0"], np.float32)).cuda()
@@ -184,7 +185,7 @@ def test_backward_bidir_rejects_a_start_state_for_the_reverse_scan():
     B, T, H, D = 1, 40, 2, 32
     d = gdn_inputs.batch(83, B, T, H, D, with_state=True)
     dO, dSf, _ = _bidir_inputs(d, D, T, 83)
-    s = gb.Stream(B, H, D, D, T)
+    s = gb.Stream(B, H, D, D, T, poison_ws=True)
     try:
         t = dev_inputs(d)
         S0 = torch.from_numpy(np.ascontiguousarray(d["S0"], np.float32)).cuda()
@@ -221,7 +222,7 @@ def test_backward_staging_block_edges(T):
     ref_f = oracle.backward(d["q"], d["k"], d["v"], d["a"], d["beta"], dO[0].float().numpy(), d["S0"], dSf.numpy())
     ref_r = oracle.backward(d["q"], d["k"], d["v"], d["a"], d["beta"], dO[1].float().numpy(), None, dSr.numpy(),
                             reverse=True)
-    s = gb.Stream(B, H, D, D, T)
+    s = gb.Stream(B, H, D, D, T, poison_ws=True)
     try:
         t = dev_inputs(d)
         S0 = torch.from_numpy(np.ascontiguousarray(d["S0"], np.float32)).cuda()
