@@ -80,6 +80,23 @@ def test_backward_fp32_io_and_unequal_widths():
     _check_all(g, ref)
 
 
+@pytest.mark.parametrize("D", [112, 128])
+def test_backward_fp32_io_wide(D):
+    """fp32 q, k, v, d_o at d = 112 and 128 (four 16-byte chunks of a staged row per lane, the
+    checkpoint passes at their default occupancy), 130 tokens: two whole 64-token segments and a
+    2-token tail."""
+    rng = np.random.default_rng(90 + D)
+    B, T, H = 1, 130, 2
+    d = {"q": rng.standard_normal((B, T, H, D)).astype(np.float32),
+         "k": rng.standard_normal((B, T, H, D)).astype(np.float32),
+         "v": (0.5 * rng.standard_normal((B, T, H, D))).astype(np.float32),
+         "a": np.exp(-0.1 * np.log1p(np.exp(rng.standard_normal((B, T, H))))).astype(np.float32),
+         "beta": (1 / (1 + np.exp(-rng.standard_normal((B, T, H))))).astype(np.float32),
+         "S0": (0.1 * rng.standard_normal((B, H, D, D))).astype(np.float32)}
+    g, ref = _grads(d, D, D, T, io="f32", seed=90 + D)
+    _check_all(g, ref)
+
+
 @pytest.mark.parametrize("reverse", [False, True])
 def test_backward_720p_width_long(reverse):
     """d = 112, 700 tokens (several hundred steps of gradient flow through the state)."""
