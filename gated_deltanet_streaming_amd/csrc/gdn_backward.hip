@@ -57,7 +57,8 @@ void tm_end(Timing* tm, hipStream_t s) {
 // pass keeps only the state before every block (a checkpoint) and an adjoint pass
 // keeps G at the end of every segment of kSEG tokens; each segment is then walked
 // backward on its own, recomputing the states inside each of its blocks from the
-// block's checkpoint into LDS.  dv and the start-state gradient are row-local;
+// block's checkpoint into LDS, half a block at a time.  dv and the start-state
+// gradient are row-local;
 // the other gradients sum over all rows: per token the rows' terms go through an
 // LDS buffer and each lane adds one float4 column group over the 4 rows in row
 // order, then the workgroup writes its rows' partial sums, and gdn_bwd_reduce_kernel
@@ -143,7 +144,7 @@ __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 template <int NG, bool F32, int PHASE>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PHASE == 0 && !F32 ? 3 : 1))) void gdn_bwd_rows_kernel(Params p, BwdParams g0, BwdParams g1, int nunits) {
     constexpr int DK = 16 * NG;               // d_k
-    constexpr int TB = 8;                     // tokens per staged block (LDS: states of a block)
+    constexpr int TB = 8;                     // tokens per staged block
     static_assert(TB >= kMinTB, "checkpoint sizing");
     const int lane = threadIdx.x, part = lane & (kLPR - 1), rl = lane / kLPR;
     const int nrb = p.Dv / kRB;
